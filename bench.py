@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized-weight prefill GEMM on one MI355X.
+
+A step is one pass of the hot path over one 512-token prefill chunk of the FFN:
+the fused gate/up SwiGLU GEMM (Q4_0, 4096 -> 2 x 12288) followed by the down
+projection with residual add (Q8_0, 12288 -> 4096), f16 leg (fp16 inputs, fp32
+accumulation). Inputs are synthetic (seeded N(0, 0.02) weights quantized to
+Q4_0/Q8_0, N(0, 1) activations) and resident in HBM before timing starts; the
+weights rotate over enough copies (> 512 MB) that the 256 MB Infinity Cache does
+not hold them from one step to the next.
+
+Prints one JSON line: value = FLOPs of the step / time (TFLOP/s), a roofline entry
+for the dominant kernel (the gate/up GEMM: its algorithmic FLOPs over its average
+HIP-event duration inside the timed region, against the fp16 dense MFMA peak), and
+the CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "prefill GEMM TFLOP/s at T=512 (Q4_0 4096->12288 gate/up); % MFMA peak"
+
+# MI355X published peaks (dense): 256 CUs at 2.4 GHz.
+PEAK = {
+    "fp16_mfma_tflops": 2516.6,   # 256 CU x 4096 flop/clk x 2.4 GHz
+    "fp32_mfma_tflops": 157.3,
+    "hbm_gbs": 8000.0,
+}
+
+HIDDEN, INTER = 4096, 12288
+Q4_0, Q8_0 = 0, 1
+PLAIN, RESIDUAL, SWIGLU = 0, 1, 2
+BLOCK = {Q4_0: 18, Q8_0: 34}
+
+KERNEL_SOURCES = ["pf_gemm_f16.hip", "pf_gemm_f32.hip", "pf_gemv.hip", "pf_device.h"]
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "quantized_weight_prefill_gguf_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def workloads():
+    """name -> (T, leg, ops). op = (label, qtype, n, k, epilogue, input, output)."""
+    ffn = lambda T: (T, 1, [
+        ("gate_up_swiglu_q4_0", Q4_0, INTER, HIDDEN, SWIGLU, "x", "act"),
+        ("down_residual_q8_0", Q8_0, HIDDEN, INTER, RESIDUAL, "act", "res"),
+    ])
+    return {
+        "ffn_T512_f16": ffn(512),
+        "ffn_T2048_f16": ffn(2048),
+        "ffn_T512_f32": (512, 0, ffn(512)[2]),
+        "plain_q4_0_4096_T512_f16": (512, 1, [("plain_q4_0", Q4_0, HIDDEN, HIDDEN, PLAIN, "x", "out")]),
+        "gemv_q4_0_12288x4096_T1": (1, 0, [("gemv_q4_0", Q4_0, INTER, HIDDEN, PLAIN, "x", "out")]),
+        "gemv_q8_0_4096x12288_T1": (1, 0, [("gemv_q8_0", Q8_0, HIDDEN, INTER, PLAIN, "x12288", "out")]),
+    }
+
+
+def op_rows(op):
+    return 2 * op[2] if op[4] == SWIGLU else op[2]
+
+
+def op_flops(op, T):
+    return 2.0 * T * op_rows(op) * op[3]
+
+
+def op_bytes(op, T):
+    """Algorithmic HBM bytes of one launch: weight blocks once, X read, Y written
+    (and read again for RESIDUAL)."""
+    w = op_rows(op) * (op[3] // 32) * BLOCK[op[1]]
+    x = 4 * T * op[3]
+    y = 4 * T * op[2] * (2 if op[4] == RESIDUAL else 1)
+    return w + x + y
+
+
+def cpu_baseline(T, ops, inputs, target_s=12.0):
+    """The oracle, as it is, on a bounded sample: the same ops over the first t_s
+    token rows (t_s chosen so that the run takes roughly target_s seconds)."""
+    import numpy as np
+    import oracle
+
+    def run(ts):
+        t0 = time.perf_counter()
+        flops = 0.0
+        for op in ops:
+            label, qtype, n, k, epi, src, _ = op
+            X = inputs[src][:ts]
+            R = inputs["res"][:ts] if epi == RESIDUAL else None
+            oracle.gemm(qtype, inputs["w_" + label], n, k, X, epi, R)
+            flops += op_flops(op, ts)
+        return flops, time.perf_counter() - t0
+
+    ts = min(T, 4)
+    flops, dt = run(ts)
+    if dt < target_s / 3 and ts < T:
+        ts = int(min(T, max(ts + 1, ts * target_s / max(dt, 1e-3))))
+        flops, dt = run(ts)
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": "the step's %d ops on the first %d of %d token rows (%.1f GFLOP, %.1f s)"
+                  % (len(ops), ts, T, flops / 1e9, dt),
+    }
+
+
+def load_traffic(workload, label):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(workload, {}).get(label)
+    if not entry or entry.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="ffn_T512_f16", choices=sorted(workloads()))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rotate-mb", type=float, default=640.0,
+                    help="minimum total bytes of rotated weight copies")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this path has no multi-GPU mode "
+              "(each GPU would run its own independent share).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import quantized_weight_prefill_gguf_amd as pf
+    from quantized_weight_prefill_gguf_amd import synth
+
+    pf.load()
+    torch.cuda.set_device(0)
+    T, leg, ops = workloads()[args.workload]
+
+    # ---- inputs (host, seeded), then resident in HBM
+    wid = 3
+    inputs = {}
+    for op in ops:
+        label, qtype, n, k, epi, src, dst = op
+        if epi == SWIGLU:
+            inputs["w_" + label] = synth.gate_up_weight(qtype, n, k, workload_id=wid)
+        else:
+            tid = synth.TENSOR_W_DOWN if label.startswith("down") else synth.TENSOR_W
+            inputs["w_" + label] = synth.quantized_weight(qtype, n, k, workload_id=wid, tensor_id=tid)
+    inputs["x"] = synth.activations(T, HIDDEN, workload_id=wid)
+    inputs["x12288"] = synth.activations(T, INTER, workload_id=wid)
+    inputs["res"] = synth.activations(T, HIDDEN, workload_id=wid, tensor_id=synth.TENSOR_R)
+    inputs["act"] = synth.activations(T, INTER, workload_id=wid, tensor_id=synth.TENSOR_W_UP)
+
+    log("inputs generated for %s" % args.workload)
+    wbytes = sum(inputs["w_" + op[0]].size for op in ops)
+    copies = max(2, int(np.ceil(args.rotate_mb * 1e6 / wbytes)) + 1)
+    dev_w = [{op[0]: torch.from_numpy(inputs["w_" + op[0]]).cuda() for op in ops}]
+    for _ in range(copies - 1):
+        dev_w.append({key: t.clone() for key, t in dev_w[0].items()})
+    bufs = {
+        "x": torch.from_numpy(inputs["x"]).cuda(),
+        "x12288": torch.from_numpy(inputs["x12288"]).cuda(),
+        "act": torch.from_numpy(inputs["act"]).cuda(),
+        "res": torch.from_numpy(inputs["res"]).cuda(),
+        "out": torch.empty((T, max(HIDDEN, INTER)), dtype=torch.float32, device="cuda"),
+    }
+    stream = torch.cuda.current_stream()
+
+    def launch(op, wset):
+        label, qtype, n, k, epi, src, dst = op
+        Y = bufs[dst] if dst != "out" else bufs["out"].view(-1)[: T * n].view(T, n)
+        pf.gemm(qtype, dev_w[wset][label], n, k, bufs[src], Y, epi, leg)
+
+    for i in range(args.warmup):
+        for op in ops:
+            launch(op, i % copies)
+    torch.cuda.synchronize()
+    log("warmup done (%d weight copies)" % copies)
+
+    # ---- timed region: K steps, HIP events around every launch
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in ops] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for j, op in enumerate(ops):
+            ev[s][j][0].record(stream)
+            launch(op, s % copies)
+            ev[s][j][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    step_flops = sum(op_flops(op, T) for op in ops)
+    ms_per_step = elapsed * 1e3 / args.steps
+    kern_ms = [float(np.mean([ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(args.steps)]))
+               for j in range(len(ops))]
+    dom = int(np.argmax(kern_ms))
+    dop = ops[dom]
+    is_gemv = T <= 8
+    if is_gemv:
+        wb = op_rows(dop) * (dop[3] // 32) * BLOCK[dop[1]]
+        achieved = wb / (kern_ms[dom] * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK["hbm_gbs"], "unit": "GB/s",
+                    "frac": achieved / PEAK["hbm_gbs"], "traffic": load_traffic(args.workload, dop[0])}
+    else:
+        achieved = op_flops(dop, T) / (kern_ms[dom] * 1e-3) / 1e12
+        peak = PEAK["fp16_mfma_tflops"] if leg == 1 else PEAK["fp32_mfma_tflops"]
+        roofline = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                    "frac": achieved / peak, "traffic": load_traffic(args.workload, dop[0])}
+    roofline["kernel"] = dop[0]
+    roofline["avg_launch_us"] = kern_ms[dom] * 1e3
+
+    out = {
+        "metric": METRIC,
+        "value": step_flops / (ms_per_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if leg == 1 else "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "T": T, "hidden": HIDDEN, "intermediate": INTER,
+                   "leg": "f16" if leg == 1 else "f32",
+                   "ops": [{"op": op[0], "n": op[2], "k": op[3], "avg_us": kern_ms[j] * 1e3,
+                            "tflops": op_flops(op, T) / (kern_ms[j] * 1e-3) / 1e12,
+                            "gbs": op_bytes(op, T) / (kern_ms[j] * 1e-3) / 1e9}
+                           for j, op in enumerate(ops)],
+                   "weight_copies": copies},
+        "roofline": roofline,
+    }
+    log("timed region done: %.3f ms/step" % ms_per_step)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(T, ops, inputs)
+        log("cpu baseline done")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

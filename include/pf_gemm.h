@@ -1,0 +1,137 @@
+/*
+ * pf_gemm.h - C ABI of the quantized-weight prefill GEMM library for MI355X (gfx950).
+ *
+ * One projection of a batched prompt prefill is one GEMM of T activation rows
+ * against a GGUF block-quantized weight:
+ *
+ *     Y[T][n] = epilogue( X[T][k] . W_hat^T )      W_hat = decode(W_blocks)
+ *
+ * Pages this follows:
+ *  - aprender-serve 0.70.2, src/cuda/executor/gdn_prefill_ops.rs: module doc,
+ *    group 1 "Projections as GEMMs" (an f32 leg, fp32 in and out with no TF32, and
+ *    an f16 leg, fp16 inputs with fp32 accumulation and fp32 output) and
+ *    `qwen35_project_rows` (Y[rows x n] = X[rows x k] . W^T, all row-major).
+ *  - aprender-serve 0.70.2, src/gguf/cuda/forward_qwen35_cuda_prefill.rs: module
+ *    doc (every projection is one GEMM over the chunk's T rows instead of a
+ *    per-token GEMV loop) and `prefill_ffn_rows` (gate, up, SwiGLU, down, residual).
+ *  - oxibonsai-kernels 0.1.4, src/gpu_backend/cuda_q_std_prefill.rs: module doc
+ *    (GGUF AoS blocks, no SoA reformatting), the Q4_0/Q8_0 kernel set
+ *    (`CudaQStdPrefillModules`: GEMM, residual GEMM, fused gate/up SwiGLU GEMM and
+ *    a single-token GEMV per block type), `launch_fused_gate_up_swiglu_q4_0` and
+ *    the weight upload in `try_cuda_prefill_q_std` (gate rows, then up rows, in one
+ *    buffer), and `try_cuda_prefill_q_std` (an empty batch is a no-op).
+ *
+ * Block formats (GGUF, 32 weights per block, rows stored block after block):
+ *  - Q4_0, 18 bytes: fp16 scale d (little-endian, bytes 0-1), 16 bytes qs. Weight
+ *    j < 16 is the low nibble of qs[j], weight j >= 16 the high nibble of
+ *    qs[j-16]; value d * (q - 8).
+ *  - Q8_0, 34 bytes: fp16 scale d, then 32 int8 q; value d * q.
+ *  Block b of weight row r starts at byte (r * (k/32) + b) * block_bytes.
+ *
+ * Memory and ownership: every pointer is a device pointer (HBM) owned by the
+ * caller. The library allocates nothing, frees nothing and keeps no pointer after
+ * a call returns. X and Y are f32, contiguous and row-major ([T][k] and [T][n]).
+ * Calls only enqueue work on `stream` (a hipStream_t; NULL = the default stream)
+ * and never synchronize; a kernel fault shows at the caller's next synchronize.
+ *
+ * Errors: every argument is checked before anything is launched; a call that
+ * returns an error has enqueued nothing and written nothing. Status codes are the
+ * PF_* values below; pf_strerror() names them.
+ */
+#ifndef PF_GEMM_H
+#define PF_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Block types. */
+enum { PF_Q4_0 = 0, PF_Q8_0 = 1 };
+
+/* Epilogues.
+ *  PF_PLAIN          Y = X . W_hat^T                      (W has n rows; Y overwritten)
+ *  PF_RESIDUAL       Y = Y + X . W_hat^T, in place        (W has n rows; Y holds R on entry)
+ *  PF_GATE_UP_SWIGLU Y = silu(X . Wg^T) * (X . Wu^T)      (W has 2n rows: the n gate
+ *                    rows, then the n up rows; silu(g) = g / (1 + e^-g))
+ */
+enum { PF_PLAIN = 0, PF_RESIDUAL = 1, PF_GATE_UP_SWIGLU = 2 };
+
+/* Legs.
+ *  PF_LEG_F32  f32 weights (exact decode) and f32 activations, fp32 accumulation.
+ *  PF_LEG_F16  weights RNE_fp16(d * (q - 8)) or RNE_fp16(d * q), activations
+ *              RNE_fp16(x), fp32 accumulation, f32 output. X stays f32 in memory;
+ *              the rounding happens inside the kernel.
+ *  For T <= PF_GEMV_MAX_T both legs run the f32 GEMV, whose error bound is the
+ *  f32 leg's and therefore also meets the f16 leg's.
+ */
+enum { PF_LEG_F32 = 0, PF_LEG_F16 = 1 };
+
+/* Kernel family. PF_PATH_AUTO picks the GEMV for 1 <= T <= PF_GEMV_MAX_T and the
+ * tiled matrix-core GEMM otherwise. The other two force a family (tests compare
+ * them); PF_PATH_GEMV requires T <= PF_GEMV_MAX_T. */
+enum { PF_PATH_AUTO = 0, PF_PATH_GEMM = 1, PF_PATH_GEMV = 2 };
+#define PF_GEMV_MAX_T 8
+
+/* Status codes. */
+enum {
+    PF_OK = 0,
+    PF_E_NULL = 1,     /* a required pointer is NULL */
+    PF_E_QTYPE = 2,    /* unknown block type */
+    PF_E_EPILOGUE = 3, /* unknown epilogue */
+    PF_E_LEG = 4,      /* unknown leg */
+    PF_E_SHAPE = 5,    /* n < 1, T < 0, k < 256 or k % 256 != 0 (pf_gemm), k % 32 != 0
+                          (pf_dequant_*), or an element count of X, Y or W_hat
+                          reaching 2^31 */
+    PF_E_ALIGN = 6,    /* W, X, Y or out not 16-byte aligned */
+    PF_E_ALIAS = 7,    /* Y (or out) overlaps W or X */
+    PF_E_LAUNCH = 8,   /* the HIP runtime refused the launch */
+    PF_E_PATH = 9      /* unknown path, or PF_PATH_GEMV with T > PF_GEMV_MAX_T */
+};
+
+/* The projection GEMM.
+ *  qtype     PF_Q4_0 or PF_Q8_0.
+ *  W_blocks  device, n_w * (k/32) blocks, n_w = 2n for PF_GATE_UP_SWIGLU, else n.
+ *  n         output width (columns of Y); k reduction length, a multiple of 256.
+ *  X         device, f32 [T][k] row-major. T = 0 is a no-op that returns PF_OK.
+ *  Y         device, f32 [T][n] row-major; read as R by PF_RESIDUAL.
+ *  epilogue  PF_PLAIN, PF_RESIDUAL or PF_GATE_UP_SWIGLU.
+ *  leg       PF_LEG_F32 or PF_LEG_F16.
+ *  stream    hipStream_t to enqueue on (NULL = default stream).
+ * Returns PF_OK or a PF_E_* code. */
+int pf_gemm(int qtype, const void *W_blocks, int64_t n, int64_t k, const float *X, int64_t T,
+            float *Y, int epilogue, int leg, void *stream);
+
+/* pf_gemm with an explicit kernel family (PF_PATH_*); same arguments otherwise. */
+int pf_gemm_path(int qtype, const void *W_blocks, int64_t n, int64_t k, const float *X,
+                 int64_t T, float *Y, int epilogue, int leg, void *stream, int path);
+
+/* Which family pf_gemm would run for these sizes: PF_PATH_GEMM, PF_PATH_GEMV, 0
+ * for T == 0 (nothing runs), or -PF_E_* for arguments pf_gemm would refuse
+ * (pointers are not checked). Host-only; touches no GPU state. */
+int pf_select_path(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int leg);
+
+/* Bit-exact block decode into out[rows][k] (device, f32), out = d * (q - 8) or d * q.
+ * Same block layout as pf_gemm; k a multiple of 32. This is the f32 leg's weight. */
+int pf_dequant_f32(int qtype, const void *W_blocks, int64_t rows, int64_t k, float *out,
+                   void *stream);
+
+/* Block decode into binary16 bit patterns out[rows][k] (device): RNE_fp16 of the f32
+ * decode. This is the f16 leg's weight. */
+int pf_dequant_f16(int qtype, const void *W_blocks, int64_t rows, int64_t k, uint16_t *out,
+                   void *stream);
+
+/* Bytes of a weight of `rows` rows and reduction length k: rows * (k/32) *
+ * block_bytes (18 for Q4_0, 34 for Q8_0). Returns -PF_E_QTYPE or -PF_E_SHAPE (k not
+ * a multiple of 32, rows < 0) on bad arguments. Host-only. */
+int64_t pf_weight_bytes(int qtype, int64_t rows, int64_t k);
+
+/* Static, NUL-terminated name of a status code ("unknown status" otherwise). */
+const char *pf_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PF_GEMM_H */

@@ -32,6 +32,7 @@ def _load():
     lib = ctypes.CDLL(path)
     i64, u16 = ctypes.c_int64, ctypes.c_uint16
     P = ctypes.c_void_p
+    lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_fp16_to_f64.argtypes = [u16]
     lib.oracle_fp16_to_f64.restype = ctypes.c_double
     lib.oracle_f32_to_fp16_rne.argtypes = [ctypes.c_float]
@@ -60,6 +61,11 @@ def _ptr(a):
 def _c(a, dtype):
     a = np.ascontiguousarray(a, dtype=dtype)
     return a
+
+
+def num_threads():
+    """OpenMP threads the oracle runs on."""
+    return int(_load().oracle_num_threads())
 
 
 def fp16_to_f64(h):

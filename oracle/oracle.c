@@ -36,6 +36,9 @@
 #include <stdint.h>
 #include <string.h>
 #include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define ORACLE_Q4_0 0
 #define ORACLE_Q8_0 1
@@ -43,6 +46,16 @@
 #define ORACLE_PLAIN 0
 #define ORACLE_RESIDUAL 1
 #define ORACLE_GATE_UP_SWIGLU 2
+
+/* Threads the OpenMP loops below use (1 without OpenMP). */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* ---------------------------------------------------------------------------
  * IEEE 754 binary16, decoded from its definition (sign, 5-bit biased exponent,

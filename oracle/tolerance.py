@@ -62,15 +62,16 @@ def silu_range(a, b):
     return lo, hi
 
 
-def linear_error(Y, Y_ref, wnorm, xnorm):
-    """Normalised error of a PLAIN/RESIDUAL result.
+def linear_error_elems(Y, Y_ref, den):
+    """Normalised error of PLAIN/RESIDUAL results on matching element arrays.
 
-    Y, Y_ref: [T][n]; wnorm: [n]; xnorm: [T]. Returns (max normalised error over
-    elements with a nonzero denominator, all zero-denominator elements exact?).
+    den = ||w_hat_r|| * ||x_t|| for each element. Returns (max normalised error
+    over elements with den > 0, whether every den == 0 element equals the oracle
+    rounded to f32).
     """
     Y = np.asarray(Y, np.float64)
     Y_ref = np.asarray(Y_ref, np.float64)
-    den = np.outer(np.asarray(xnorm, np.float64), np.asarray(wnorm, np.float64))
+    den = np.broadcast_to(np.asarray(den, np.float64), Y.shape)
     if not np.all(np.isfinite(Y)):
         return np.inf, False
     diff = np.abs(Y - Y_ref)
@@ -80,24 +81,34 @@ def linear_error(Y, Y_ref, wnorm, xnorm):
     return err, exact_ok
 
 
+def linear_error(Y, Y_ref, wnorm, xnorm):
+    """linear_error_elems for full [T][n] results: wnorm [n], xnorm [T]."""
+    den = np.outer(np.asarray(xnorm, np.float64), np.asarray(wnorm, np.float64))
+    return linear_error_elems(Y, Y_ref, den)
+
+
 def check_linear(Y, Y_ref, wnorm, xnorm, leg):
     err, exact_ok = linear_error(Y, Y_ref, wnorm, xnorm)
     return (err <= TOL[leg] and exact_ok), err
 
 
-def swiglu_check(Y, g, u, gnorm, unorm, xnorm, leg):
-    """Interval check for SWIGLU outputs.
+def check_linear_elems(Y, Y_ref, den, leg):
+    err, exact_ok = linear_error_elems(Y, Y_ref, den)
+    return (err <= TOL[leg] and exact_ok), err
 
-    Y: [T][n] result; g, u: [T][n] fp64 oracle gate and up products; gnorm, unorm:
-    [n] weight-row norms; xnorm: [T]. Returns (pass, first-order diagnostic ratio).
+
+def swiglu_check_elems(Y, g, u, gden, uden, leg):
+    """Interval check for SWIGLU outputs on matching element arrays.
+
+    g, u: fp64 oracle gate and up products; gden = ||w_gate_r|| ||x_t||,
+    uden = ||w_up_r|| ||x_t||. Returns (pass, first-order diagnostic ratio).
     """
     tau = TOL[leg]
     Y = np.asarray(Y, np.float64)
     g = np.asarray(g, np.float64)
     u = np.asarray(u, np.float64)
-    xn = np.asarray(xnorm, np.float64)[:, None]
-    G = tau * xn * np.asarray(gnorm, np.float64)[None, :]
-    U = tau * xn * np.asarray(unorm, np.float64)[None, :]
+    G = tau * np.broadcast_to(np.asarray(gden, np.float64), Y.shape)
+    U = tau * np.broadcast_to(np.asarray(uden, np.float64), Y.shape)
     if not np.all(np.isfinite(Y)):
         return False, np.inf
     s_lo, s_hi = silu_range(g - G, g + G)
@@ -108,11 +119,19 @@ def swiglu_check(Y, g, u, gnorm, unorm, xnorm, leg):
     y_ref = _silu(g) * u
     widen = 4.0 * 2.0 ** -24 * np.abs(y_ref)
     ok = bool(np.all((Y >= lo - widen) & (Y <= hi + widen)))
-    # First-order diagnostic: |dY| / (|silu'(g)| |u| G + |silu(g)| U).
-    s = 1.0 / (1.0 + np.exp(-g))
+    # First-order diagnostic: |dY| / (|silu'(g)| |u| G + |silu(g)| U) at tau = 1.
+    with np.errstate(over="ignore"):
+        s = 1.0 / (1.0 + np.exp(-g))
     dsilu = s * (1.0 + g * (1.0 - s))
     den = np.abs(dsilu) * np.abs(u) * G / tau + np.abs(_silu(g)) * U / tau
     diff = np.abs(Y - y_ref)
     nz = den > 0
     ratio = float(np.max(diff[nz] / den[nz])) if np.any(nz) else 0.0
     return ok, ratio
+
+
+def swiglu_check(Y, g, u, gnorm, unorm, xnorm, leg):
+    """swiglu_check_elems for full [T][n] results: gnorm, unorm [n], xnorm [T]."""
+    xn = np.asarray(xnorm, np.float64)[:, None]
+    return swiglu_check_elems(Y, g, u, xn * np.asarray(gnorm, np.float64)[None, :],
+                              xn * np.asarray(unorm, np.float64)[None, :], leg)

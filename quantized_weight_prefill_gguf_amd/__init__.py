@@ -1,0 +1,140 @@
+"""Python binding of libpfgemm (the C ABI in include/pf_gemm.h).
+
+Argument marshalling only: every step of the method runs in the library's gfx950
+kernels. PyTorch supplies device memory and the current stream. The binding has
+no fallback: if the built library is missing it raises.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpfgemm.so")
+
+PF_Q4_0, PF_Q8_0 = 0, 1
+PF_PLAIN, PF_RESIDUAL, PF_GATE_UP_SWIGLU = 0, 1, 2
+PF_LEG_F32, PF_LEG_F16 = 0, 1
+PF_PATH_AUTO, PF_PATH_GEMM, PF_PATH_GEMV = 0, 1, 2
+PF_GEMV_MAX_T = 8
+(PF_OK, PF_E_NULL, PF_E_QTYPE, PF_E_EPILOGUE, PF_E_LEG, PF_E_SHAPE, PF_E_ALIGN,
+ PF_E_ALIAS, PF_E_LAUNCH, PF_E_PATH) = range(10)
+
+BLOCK_BYTES = {PF_Q4_0: 18, PF_Q8_0: 34}
+QTYPES = {"q4_0": PF_Q4_0, "q8_0": PF_Q8_0}
+EPILOGUES = {"plain": PF_PLAIN, "residual": PF_RESIDUAL, "swiglu": PF_GATE_UP_SWIGLU}
+LEGS = {"f32": PF_LEG_F32, "f16": PF_LEG_F16}
+
+# Every symbol include/pf_gemm.h declares.
+EXPORTS = ("pf_gemm", "pf_gemm_path", "pf_select_path", "pf_dequant_f32", "pf_dequant_f16",
+           "pf_weight_bytes", "pf_strerror")
+
+
+class PfError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__("%s: %s" % (what, strerror(status)))
+
+
+_lib = None
+
+
+def load():
+    """Load libpfgemm.so (built in-tree by build.py); raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libpfgemm.so is not built (run quantized_weight_prefill_gguf_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    i32, i64, P = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p
+    lib.pf_gemm.argtypes = [i32, P, i64, i64, P, i64, P, i32, i32, P]
+    lib.pf_gemm.restype = i32
+    lib.pf_gemm_path.argtypes = [i32, P, i64, i64, P, i64, P, i32, i32, P, i32]
+    lib.pf_gemm_path.restype = i32
+    lib.pf_select_path.argtypes = [i32, i64, i64, i64, i32, i32]
+    lib.pf_select_path.restype = i32
+    lib.pf_dequant_f32.argtypes = [i32, P, i64, i64, P, P]
+    lib.pf_dequant_f32.restype = i32
+    lib.pf_dequant_f16.argtypes = [i32, P, i64, i64, P, P]
+    lib.pf_dequant_f16.restype = i32
+    lib.pf_weight_bytes.argtypes = [i32, i64, i64]
+    lib.pf_weight_bytes.restype = i64
+    lib.pf_strerror.argtypes = [i32]
+    lib.pf_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def strerror(status):
+    return load().pf_strerror(status).decode()
+
+
+def weight_bytes(qtype, rows, k):
+    return load().pf_weight_bytes(qtype, rows, k)
+
+
+def select_path(qtype, n, k, T, epilogue, leg):
+    return load().pf_select_path(qtype, n, k, T, epilogue, leg)
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev_ptr(t, name):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def gemm(qtype, W, n, k, X, Y, epilogue, leg, stream=None, path=PF_PATH_AUTO):
+    """Y[T][n] = epilogue(X[T][k] . W_hat^T) on the device (see pf_gemm).
+
+    W: uint8 device tensor of blocks; X, Y: float32 device tensors [T][k], [T][n].
+    """
+    import torch
+    if X.dtype != torch.float32 or Y.dtype != torch.float32 or W.dtype != torch.uint8:
+        raise TypeError("X and Y must be float32 and W uint8")
+    T = X.numel() // k if k > 0 else 0
+    if X.numel() != T * k or Y.numel() != T * n:
+        raise ValueError("X must hold T*k and Y T*n elements")
+    rows = 2 * n if epilogue == PF_GATE_UP_SWIGLU else n
+    need = load().pf_weight_bytes(qtype, rows, k)
+    if need >= 0 and W.numel() < need:
+        raise ValueError("W holds %d bytes, %d needed" % (W.numel(), need))
+    lib = load()
+    st = lib.pf_gemm_path(qtype, _dev_ptr(W, "W"), n, k, _dev_ptr(X, "X"), T, _dev_ptr(Y, "Y"),
+                          epilogue, leg, _stream_handle(stream), path)
+    if st != PF_OK:
+        raise PfError(st, "pf_gemm")
+    return Y
+
+
+def dequant_f32(qtype, W, rows, k, out, stream=None):
+    """out[rows][k] (float32 device tensor) = the exact block decode of W."""
+    import torch
+    if out.dtype != torch.float32 or out.numel() != rows * k:
+        raise ValueError("out must be float32 with rows*k elements")
+    st = load().pf_dequant_f32(qtype, _dev_ptr(W, "W"), rows, k, _dev_ptr(out, "out"),
+                               _stream_handle(stream))
+    if st != PF_OK:
+        raise PfError(st, "pf_dequant_f32")
+    return out
+
+
+def dequant_f16(qtype, W, rows, k, out, stream=None):
+    """out[rows][k] (int16/uint16 device tensor of binary16 bits) = RNE_fp16(decode)."""
+    if out.element_size() != 2 or out.numel() != rows * k:
+        raise ValueError("out must have 2-byte elements, rows*k of them")
+    st = load().pf_dequant_f16(qtype, _dev_ptr(W, "W"), rows, k, _dev_ptr(out, "out"),
+                               _stream_handle(stream))
+    if st != PF_OK:
+        raise PfError(st, "pf_dequant_f16")
+    return out

@@ -1,0 +1,156 @@
+// The C ABI: argument checks, then dispatch to one kernel launch on the caller's
+// stream. Every check runs on the host before any HIP call, so a refused call
+// enqueues nothing and touches no GPU state (the refusal style of the page
+// "aprender-serve 0.70.2 - src/gguf/cuda/forward_qwen35_cuda_prefill.rs",
+// `prefill`: refuse with a reason, leave nothing half applied; null pointers are
+// refused as `qp_launch` on "aprender-serve 0.70.2 -
+// src/cuda/executor/gdn_prefill_ops.rs" does, and an unknown block type as in
+// `qwen35_dequant_f32` there).
+#include <stdint.h>
+
+#include "../../include/pf_gemm.h"
+#include "pf_internal.h"
+
+namespace {
+
+constexpr int64_t kMax31 = (int64_t(1) << 31) - 1;
+
+int block_bytes(int qtype) {
+    if (qtype == PF_Q4_0) return 18;
+    if (qtype == PF_Q8_0) return 34;
+    return -1;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlap(const void *a, int64_t a_bytes, const void *b, int64_t b_bytes) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a_bytes > 0 && b_bytes > 0 && a0 < b0 + (uintptr_t)b_bytes && b0 < a0 + (uintptr_t)a_bytes;
+}
+
+// Checks that need no pointers. On success stores the weight row count.
+int check_sizes(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int leg, int64_t *n_w) {
+    if (block_bytes(qtype) < 0) return PF_E_QTYPE;
+    if (epilogue != PF_PLAIN && epilogue != PF_RESIDUAL && epilogue != PF_GATE_UP_SWIGLU)
+        return PF_E_EPILOGUE;
+    if (leg != PF_LEG_F32 && leg != PF_LEG_F16) return PF_E_LEG;
+    if (n < 1 || T < 0 || k < 256 || k % 256 != 0) return PF_E_SHAPE;
+    const int64_t rows = epilogue == PF_GATE_UP_SWIGLU ? 2 * n : n;
+    // Element counts stay below 2^31 so that 32-bit index arithmetic is exact.
+    if (k > kMax31 / rows || (T > 0 && (k > kMax31 / T || n > kMax31 / T))) return PF_E_SHAPE;
+    if ((rows * (k / 32)) > kMax31 / block_bytes(qtype)) return PF_E_SHAPE;
+    *n_w = rows;
+    return PF_OK;
+}
+
+int gemm_impl(int qtype, const void *W, int64_t n, int64_t k, const float *X, int64_t T, float *Y,
+              int epilogue, int leg, void *stream, int path) {
+    int64_t n_w = 0;
+    int st = check_sizes(qtype, n, k, T, epilogue, leg, &n_w);
+    if (st != PF_OK) return st;
+    if (path != PF_PATH_AUTO && path != PF_PATH_GEMM && path != PF_PATH_GEMV) return PF_E_PATH;
+    if (path == PF_PATH_GEMV && T > PF_GEMV_MAX_T) return PF_E_PATH;
+    if (T == 0) return PF_OK;  // an empty batch is a no-op
+    if (!W || !X || !Y) return PF_E_NULL;
+    if (!aligned16(W) || !aligned16(X) || !aligned16(Y)) return PF_E_ALIGN;
+    const int64_t w_bytes = n_w * (k / 32) * block_bytes(qtype);
+    const int64_t x_bytes = T * k * 4, y_bytes = T * n * 4;
+    if (overlap(Y, y_bytes, X, x_bytes) || overlap(Y, y_bytes, W, w_bytes)) return PF_E_ALIAS;
+
+    pf::GemmArgs a;
+    a.qtype = qtype;
+    a.epilogue = epilogue;
+    a.W = static_cast<const uint8_t *>(W);
+    a.X = X;
+    a.Y = Y;
+    a.n = (int)n;
+    a.k = (int)k;
+    a.T = (int)T;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int use = path == PF_PATH_AUTO ? (T <= PF_GEMV_MAX_T ? PF_PATH_GEMV : PF_PATH_GEMM) : path;
+    hipError_t err;
+    if (use == PF_PATH_GEMV)
+        err = pf::launch_gemv(a, s);
+    else if (leg == PF_LEG_F32)
+        err = pf::launch_gemm_f32(a, s);
+    else
+        err = pf::launch_gemm_f16(a, s);
+    return err == hipSuccess ? PF_OK : PF_E_LAUNCH;
+}
+
+int dequant_check(int qtype, const void *W, int64_t rows, int64_t k, const void *out, int out_elem) {
+    if (block_bytes(qtype) < 0) return PF_E_QTYPE;
+    if (rows < 1 || k < 32 || k % 32 != 0) return PF_E_SHAPE;
+    if (k > kMax31 / rows || (rows * (k / 32)) > kMax31 / block_bytes(qtype)) return PF_E_SHAPE;
+    if (!W || !out) return PF_E_NULL;
+    if (!aligned16(W) || !aligned16(out)) return PF_E_ALIGN;
+    if (overlap(out, rows * k * out_elem, W, rows * (k / 32) * block_bytes(qtype))) return PF_E_ALIAS;
+    return PF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pf_gemm(int qtype, const void *W_blocks, int64_t n, int64_t k, const float *X, int64_t T,
+            float *Y, int epilogue, int leg, void *stream) {
+    return gemm_impl(qtype, W_blocks, n, k, X, T, Y, epilogue, leg, stream, PF_PATH_AUTO);
+}
+
+int pf_gemm_path(int qtype, const void *W_blocks, int64_t n, int64_t k, const float *X,
+                 int64_t T, float *Y, int epilogue, int leg, void *stream, int path) {
+    return gemm_impl(qtype, W_blocks, n, k, X, T, Y, epilogue, leg, stream, path);
+}
+
+int pf_select_path(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int leg) {
+    int64_t n_w = 0;
+    const int st = check_sizes(qtype, n, k, T, epilogue, leg, &n_w);
+    if (st != PF_OK) return -st;
+    if (T == 0) return 0;
+    return T <= PF_GEMV_MAX_T ? PF_PATH_GEMV : PF_PATH_GEMM;
+}
+
+int pf_dequant_f32(int qtype, const void *W_blocks, int64_t rows, int64_t k, float *out,
+                   void *stream) {
+    const int st = dequant_check(qtype, W_blocks, rows, k, out, 4);
+    if (st != PF_OK) return st;
+    const hipError_t err = pf::launch_dequant_f32(qtype, static_cast<const uint8_t *>(W_blocks),
+                                                  (int)rows, (int)k, out,
+                                                  static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? PF_OK : PF_E_LAUNCH;
+}
+
+int pf_dequant_f16(int qtype, const void *W_blocks, int64_t rows, int64_t k, uint16_t *out,
+                   void *stream) {
+    const int st = dequant_check(qtype, W_blocks, rows, k, out, 2);
+    if (st != PF_OK) return st;
+    const hipError_t err = pf::launch_dequant_f16(qtype, static_cast<const uint8_t *>(W_blocks),
+                                                  (int)rows, (int)k, out,
+                                                  static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? PF_OK : PF_E_LAUNCH;
+}
+
+int64_t pf_weight_bytes(int qtype, int64_t rows, int64_t k) {
+    const int bb = block_bytes(qtype);
+    if (bb < 0) return -PF_E_QTYPE;
+    if (rows < 0 || k < 0 || k % 32 != 0) return -PF_E_SHAPE;
+    return rows * (k / 32) * bb;
+}
+
+const char *pf_strerror(int status) {
+    switch (status) {
+    case PF_OK: return "PF_OK: success";
+    case PF_E_NULL: return "PF_E_NULL: a required pointer is NULL";
+    case PF_E_QTYPE: return "PF_E_QTYPE: unknown block type";
+    case PF_E_EPILOGUE: return "PF_E_EPILOGUE: unknown epilogue";
+    case PF_E_LEG: return "PF_E_LEG: unknown leg";
+    case PF_E_SHAPE: return "PF_E_SHAPE: unsupported shape";
+    case PF_E_ALIGN: return "PF_E_ALIGN: pointer not 16-byte aligned";
+    case PF_E_ALIAS: return "PF_E_ALIAS: output overlaps an input";
+    case PF_E_LAUNCH: return "PF_E_LAUNCH: kernel launch failed";
+    case PF_E_PATH: return "PF_E_PATH: unknown path or GEMV with T > 8";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

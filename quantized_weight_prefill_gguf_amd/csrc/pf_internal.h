@@ -1,0 +1,34 @@
+// Internal interface between the C ABI (pf_api.cpp) and the kernel launchers.
+// Host-only types; the launchers live next to their kernels in the .hip files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pf {
+
+// One validated GEMM call. Element counts fit in 31 bits (checked by the API).
+struct GemmArgs {
+    int qtype;      // PF_Q4_0 / PF_Q8_0
+    int epilogue;   // PF_PLAIN / PF_RESIDUAL / PF_GATE_UP_SWIGLU
+    const uint8_t *W;
+    const float *X;
+    float *Y;
+    int n;          // output columns
+    int k;          // reduction length, multiple of 256
+    int T;          // token rows, >= 1
+};
+
+// Tiled matrix-core GEMM, f32 leg (fp32 MFMA).
+hipError_t launch_gemm_f32(const GemmArgs &a, hipStream_t s);
+// Tiled matrix-core GEMM, f16 leg (fp16 MFMA, fp32 accumulation).
+hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t s);
+// Small-T GEMV (T <= 8), f32 arithmetic.
+hipError_t launch_gemv(const GemmArgs &a, hipStream_t s);
+// Block decode to f32 / binary16.
+hipError_t launch_dequant_f32(int qtype, const uint8_t *W, int rows, int k, float *out,
+                              hipStream_t s);
+hipError_t launch_dequant_f16(int qtype, const uint8_t *W, int rows, int k, uint16_t *out,
+                              hipStream_t s);
+
+}  // namespace pf

@@ -1,0 +1,138 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol, and
+refuses bad arguments with the documented codes before touching the GPU.
+
+No call here reaches a kernel launch: each one fails a check (or is the T = 0
+no-op) on the host first, so these run without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_weight_prefill_gguf_amd as pf
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pf_gemm.h")
+
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced by these calls
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return pf.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(pf_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(pf.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_header_enums_match_binding():
+    src = open(HEADER).read()
+    for name in ["PF_Q4_0", "PF_Q8_0", "PF_PLAIN", "PF_RESIDUAL", "PF_GATE_UP_SWIGLU",
+                 "PF_LEG_F32", "PF_LEG_F16", "PF_PATH_AUTO", "PF_PATH_GEMM", "PF_PATH_GEMV",
+                 "PF_OK", "PF_E_NULL", "PF_E_QTYPE", "PF_E_EPILOGUE", "PF_E_LEG", "PF_E_SHAPE",
+                 "PF_E_ALIGN", "PF_E_ALIAS", "PF_E_LAUNCH", "PF_E_PATH"]:
+        m = re.search(r"\b%s\s*=\s*(\d+)" % name, src)
+        assert m and int(m.group(1)) == getattr(pf, name), name
+    assert int(re.search(r"#define PF_GEMV_MAX_T (\d+)", src).group(1)) == pf.PF_GEMV_MAX_T
+
+
+def test_weight_bytes(lib):
+    assert lib.pf_weight_bytes(pf.PF_Q4_0, 4096, 4096) == 4096 * 128 * 18
+    assert lib.pf_weight_bytes(pf.PF_Q8_0, 4096, 12288) == 4096 * 384 * 34
+    assert lib.pf_weight_bytes(pf.PF_Q4_0, 0, 32) == 0
+    assert lib.pf_weight_bytes(7, 1, 32) == -pf.PF_E_QTYPE
+    assert lib.pf_weight_bytes(pf.PF_Q4_0, 1, 33) == -pf.PF_E_SHAPE
+    assert lib.pf_weight_bytes(pf.PF_Q4_0, -1, 32) == -pf.PF_E_SHAPE
+
+
+def test_strerror(lib):
+    for code in range(10):
+        s = lib.pf_strerror(code).decode()
+        assert s.startswith("PF_"), s
+    assert lib.pf_strerror(99).decode() == "unknown status"
+
+
+def test_select_path(lib):
+    sel = lib.pf_select_path
+    assert sel(pf.PF_Q4_0, 4096, 4096, 0, pf.PF_PLAIN, pf.PF_LEG_F32) == 0
+    for T in (1, 2, 8):
+        assert sel(pf.PF_Q4_0, 4096, 4096, T, pf.PF_PLAIN, pf.PF_LEG_F16) == pf.PF_PATH_GEMV
+    for T in (9, 16, 512, 2048):
+        assert sel(pf.PF_Q8_0, 4096, 12288, T, pf.PF_RESIDUAL, pf.PF_LEG_F16) == pf.PF_PATH_GEMM
+    assert sel(5, 1, 256, 1, 0, 0) == -pf.PF_E_QTYPE
+    assert sel(0, 1, 256, 1, 3, 0) == -pf.PF_E_EPILOGUE
+    assert sel(0, 1, 256, 1, 0, 2) == -pf.PF_E_LEG
+    assert sel(0, 1, 128, 1, 0, 0) == -pf.PF_E_SHAPE
+
+
+def _gemm(lib, qtype=0, W=FAKE, n=64, k=256, X=FAKE + 1 << 32, T=16, Y=FAKE + 2 << 32,
+          epi=0, leg=0, path=0):
+    P = ctypes.c_void_p
+    return lib.pf_gemm_path(qtype, P(W), n, k, P(X), T, P(Y), epi, leg, None, path)
+
+
+def test_gemm_argument_checks(lib):
+    W, X, Y = FAKE, FAKE + (1 << 32), FAKE + (2 << 32)
+    g = lambda **kw: _gemm(lib, **{**dict(W=W, X=X, Y=Y), **kw})
+    assert g(qtype=2) == pf.PF_E_QTYPE
+    assert g(qtype=-1) == pf.PF_E_QTYPE
+    assert g(epi=3) == pf.PF_E_EPILOGUE
+    assert g(leg=2) == pf.PF_E_LEG
+    assert g(path=3) == pf.PF_E_PATH
+    assert g(path=pf.PF_PATH_GEMV, T=9) == pf.PF_E_PATH
+    for bad in [dict(n=0), dict(k=0), dict(k=128), dict(k=288), dict(k=4000), dict(T=-1),
+                dict(T=1 << 20, k=4096), dict(n=1 << 30, k=4096, T=1)]:
+        assert g(**bad) == pf.PF_E_SHAPE, bad
+    assert g(W=0) == pf.PF_E_NULL
+    assert g(X=0) == pf.PF_E_NULL
+    assert g(Y=0) == pf.PF_E_NULL
+    assert g(W=W + 2) == pf.PF_E_ALIGN
+    assert g(X=X + 4) == pf.PF_E_ALIGN
+    assert g(Y=Y + 8) == pf.PF_E_ALIGN
+    # Y overlapping X or W
+    assert g(Y=X) == pf.PF_E_ALIAS
+    assert g(Y=X + 16 * 256 * 4 - 16) == pf.PF_E_ALIAS
+    assert g(Y=W + 16) == pf.PF_E_ALIAS
+    assert g(X=Y + 16 * 64 * 4 - 16, Y=Y) == pf.PF_E_ALIAS
+    # T = 0: a no-op that succeeds without looking at the pointers
+    assert g(T=0) == pf.PF_OK
+    assert g(T=0, W=0, X=0, Y=0) == pf.PF_OK
+    # the public pf_gemm performs the same checks
+    P = ctypes.c_void_p
+    assert lib.pf_gemm(0, P(W), 64, 100, P(X), 16, P(Y), 0, 0, None) == pf.PF_E_SHAPE
+    assert lib.pf_gemm(0, P(W), 64, 256, P(X), 0, P(Y), 0, 0, None) == pf.PF_OK
+
+
+def test_dequant_argument_checks(lib):
+    P = ctypes.c_void_p
+    W, out = P(FAKE), P(FAKE + (1 << 32))
+    for fn in (lib.pf_dequant_f32, lib.pf_dequant_f16):
+        assert fn(3, W, 4, 64, out, None) == pf.PF_E_QTYPE
+        assert fn(0, W, 0, 64, out, None) == pf.PF_E_SHAPE
+        assert fn(0, W, 4, 48, out, None) == pf.PF_E_SHAPE
+        assert fn(0, P(0), 4, 64, out, None) == pf.PF_E_NULL
+        assert fn(0, W, 4, 64, P(0), None) == pf.PF_E_NULL
+        assert fn(0, P(FAKE + 2), 4, 64, out, None) == pf.PF_E_ALIGN
+        assert fn(0, W, 4, 64, P(FAKE + 16), None) == pf.PF_E_ALIAS
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    W = torch.zeros(18 * 8, dtype=torch.uint8)
+    X = torch.zeros(1, 256)
+    Y = torch.zeros(1, 1)
+    with pytest.raises(ValueError):
+        pf.gemm(pf.PF_Q4_0, W, 1, 256, X, Y, pf.PF_PLAIN, pf.PF_LEG_F32)
