@@ -31,6 +31,8 @@ template <> struct BlockTraits<Q8_0> {
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float fp16_bits_to_f32(uint32_t bits16) {
     // binary16 -> f32 is exact.

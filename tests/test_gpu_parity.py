@@ -130,8 +130,10 @@ def test_zero_weight_blocks_from_page(gpu, leg):
         rows = 2 * n if epi == SWIGLU else n
         W = np.tile(blk, rows * (kk // 32))
         for path in (1, 2):
-            Y = parity.run_gpu(gpu, Q4_0, W, n, kk, X, epi, leg, R=R, path=path)
-            expect = R if epi == RESIDUAL else np.zeros((T, n), np.float32)
+            # the GEMV takes at most 8 rows: it runs on the first 8 of the 12
+            tt = T if path == 1 else 8
+            Y = parity.run_gpu(gpu, Q4_0, W, n, kk, X[:tt], epi, leg, R=R[:tt], path=path)
+            expect = R[:tt] if epi == RESIDUAL else np.zeros((tt, n), np.float32)
             assert np.array_equal(Y, expect), (epi, path)
 
 
