@@ -4,10 +4,12 @@
 A step is one pass of the hot path over one 512-token prefill chunk of the FFN:
 the fused gate/up SwiGLU GEMM (Q4_0, 4096 -> 2 x 12288) followed by the down
 projection with residual add (Q8_0, 12288 -> 4096), f16 leg (fp16 inputs, fp32
-accumulation). Inputs are synthetic (seeded N(0, 0.02) weights quantized to
-Q4_0/Q8_0, N(0, 1) activations) and resident in HBM before timing starts; the
-weights rotate over enough copies (> 512 MB) that the 256 MB Infinity Cache does
-not hold them from one step to the next.
+accumulation), each through pf_gemm_ws (X rounded to fp16 once into a workspace,
+then the GEMM; both kernels sit inside the op's timing). Inputs are synthetic
+(seeded N(0, 0.02) weights quantized to Q4_0/Q8_0, N(0, 1) activations) and
+resident in HBM before timing starts; the weights rotate over enough copies
+(> 512 MB) that the 256 MB Infinity Cache does not hold them from one step to the
+next.
 
 Prints one JSON line: value = FLOPs of the step / time (TFLOP/s), a roofline entry
 for the dominant kernel (the gate/up GEMM: its algorithmic FLOPs over its average
@@ -15,6 +17,7 @@ HIP-event duration inside the timed region, against the fp16 dense MFMA peak), a
 the CPU oracle timed on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--no-workspace]
 """
 import argparse
 import hashlib
@@ -141,6 +144,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="ffn_T512_f16", choices=sorted(workloads()))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-workspace", action="store_true",
+                    help="call pf_gemm (X rounded inside the GEMM) instead of pf_gemm_ws")
     ap.add_argument("--rotate-mb", type=float, default=640.0,
                     help="minimum total bytes of rotated weight copies")
     args = ap.parse_args()
@@ -188,11 +193,18 @@ def main():
         "out": torch.empty((T, max(HIDDEN, INTER)), dtype=torch.float32, device="cuda"),
     }
     stream = torch.cuda.current_stream()
+    use_ws = not args.no_workspace
+    ws_bytes = max(pf.workspace_bytes(op[1], op[2], op[3], T, op[4], leg) for op in ops)
+    workspace = (torch.empty(((ws_bytes + 15) // 16) * 16, dtype=torch.uint8, device="cuda")
+                 if use_ws and ws_bytes > 0 else None)
 
     def launch(op, wset):
         label, qtype, n, k, epi, src, dst = op
         Y = bufs[dst] if dst != "out" else bufs["out"].view(-1)[: T * n].view(T, n)
-        pf.gemm(qtype, dev_w[wset][label], n, k, bufs[src], Y, epi, leg)
+        if use_ws:
+            pf.gemm_ws(qtype, dev_w[wset][label], n, k, bufs[src], Y, epi, leg, workspace)
+        else:
+            pf.gemm(qtype, dev_w[wset][label], n, k, bufs[src], Y, epi, leg)
 
     for i in range(args.warmup):
         for op in ops:
@@ -252,7 +264,9 @@ def main():
                             "tflops": op_flops(op, T) / (kern_ms[j] * 1e-3) / 1e12,
                             "gbs": op_bytes(op, T) / (kern_ms[j] * 1e-3) / 1e9}
                            for j, op in enumerate(ops)],
-                   "weight_copies": copies},
+                   "weight_copies": copies,
+                   "entry_point": "pf_gemm_ws" if use_ws else "pf_gemm",
+                   "workspace_bytes": ws_bytes if use_ws else 0},
         "roofline": roofline,
     }
     log("timed region done: %.3f ms/step" % ms_per_step)

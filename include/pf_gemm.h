@@ -62,7 +62,8 @@ enum { PF_PLAIN = 0, PF_RESIDUAL = 1, PF_GATE_UP_SWIGLU = 2 };
  *  PF_LEG_F32  f32 weights (exact decode) and f32 activations, fp32 accumulation.
  *  PF_LEG_F16  weights RNE_fp16(d * (q - 8)) or RNE_fp16(d * q), activations
  *              RNE_fp16(x), fp32 accumulation, f32 output. X stays f32 in memory;
- *              the rounding happens inside the kernel.
+ *              pf_gemm rounds it inside the GEMM, pf_gemm_ws once into its
+ *              workspace.
  *  For T <= PF_GEMV_MAX_T both legs run the f32 GEMV, whose error bound is the
  *  f32 leg's and therefore also meets the f16 leg's.
  */
@@ -87,7 +88,9 @@ enum {
     PF_E_ALIGN = 6,    /* W, X, Y or out not 16-byte aligned */
     PF_E_ALIAS = 7,    /* Y (or out) overlaps W or X */
     PF_E_LAUNCH = 8,   /* the HIP runtime refused the launch */
-    PF_E_PATH = 9      /* unknown path, or PF_PATH_GEMV with T > PF_GEMV_MAX_T */
+    PF_E_PATH = 9,     /* unknown path, or PF_PATH_GEMV with T > PF_GEMV_MAX_T */
+    PF_E_WORKSPACE = 10 /* workspace NULL, smaller than pf_workspace_bytes(), not
+                           16-byte aligned, or overlapping W, X or Y */
 };
 
 /* The projection GEMM.
@@ -106,6 +109,30 @@ int pf_gemm(int qtype, const void *W_blocks, int64_t n, int64_t k, const float *
 /* pf_gemm with an explicit kernel family (PF_PATH_*); same arguments otherwise. */
 int pf_gemm_path(int qtype, const void *W_blocks, int64_t n, int64_t k, const float *X,
                  int64_t T, float *Y, int epilogue, int leg, void *stream, int path);
+
+/* Workspace bytes pf_gemm_ws needs for these sizes: T * k * 2 when it runs the f16
+ * leg's matrix-core GEMM (room for X rounded to binary16), 0 when it runs a kernel
+ * that needs none (the f32 leg, the GEMV, T == 0), or -PF_E_* for arguments pf_gemm
+ * would refuse. Host-only; touches no GPU state. */
+int64_t pf_workspace_bytes(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int leg);
+
+/* pf_gemm with a caller workspace. On the f16 leg's matrix-core GEMM, X is first
+ * rounded to binary16 once, into the workspace, and the GEMM then streams that copy
+ * instead of rounding X again in every tile. The operands (RNE_fp16(x) and the
+ * decoded weights) and the accumulation are the same as pf_gemm's, so the result is
+ * pf_gemm's, bit for bit wherever pf_gemm itself is deterministic (it is not where
+ * it splits k across workgroups, whose fp32 atomic adds land in any order).
+ *  workspace        device, owned by the caller, 16-byte aligned, at least
+ *                   pf_workspace_bytes() bytes, not overlapping W, X or Y. Its
+ *                   contents on entry are ignored and undefined on return. May be
+ *                   NULL when pf_workspace_bytes() is 0.
+ *  workspace_bytes  its size in bytes.
+ * Calls that share a workspace must be ordered (same stream, or synchronized).
+ * Returns PF_OK or a PF_E_* code (PF_E_WORKSPACE for a workspace that is missing,
+ * too small, misaligned or overlapping). */
+int pf_gemm_ws(int qtype, const void *W_blocks, int64_t n, int64_t k, const float *X, int64_t T,
+               float *Y, int epilogue, int leg, void *workspace, int64_t workspace_bytes,
+               void *stream);
 
 /* Which family pf_gemm would run for these sizes: PF_PATH_GEMM, PF_PATH_GEMV, 0
  * for T == 0 (nothing runs), or -PF_E_* for arguments pf_gemm would refuse

@@ -16,7 +16,7 @@ PF_LEG_F32, PF_LEG_F16 = 0, 1
 PF_PATH_AUTO, PF_PATH_GEMM, PF_PATH_GEMV = 0, 1, 2
 PF_GEMV_MAX_T = 8
 (PF_OK, PF_E_NULL, PF_E_QTYPE, PF_E_EPILOGUE, PF_E_LEG, PF_E_SHAPE, PF_E_ALIGN,
- PF_E_ALIAS, PF_E_LAUNCH, PF_E_PATH) = range(10)
+ PF_E_ALIAS, PF_E_LAUNCH, PF_E_PATH, PF_E_WORKSPACE) = range(11)
 
 BLOCK_BYTES = {PF_Q4_0: 18, PF_Q8_0: 34}
 QTYPES = {"q4_0": PF_Q4_0, "q8_0": PF_Q8_0}
@@ -24,8 +24,8 @@ EPILOGUES = {"plain": PF_PLAIN, "residual": PF_RESIDUAL, "swiglu": PF_GATE_UP_SW
 LEGS = {"f32": PF_LEG_F32, "f16": PF_LEG_F16}
 
 # Every symbol include/pf_gemm.h declares.
-EXPORTS = ("pf_gemm", "pf_gemm_path", "pf_select_path", "pf_dequant_f32", "pf_dequant_f16",
-           "pf_weight_bytes", "pf_strerror")
+EXPORTS = ("pf_gemm", "pf_gemm_path", "pf_workspace_bytes", "pf_gemm_ws", "pf_select_path",
+           "pf_dequant_f32", "pf_dequant_f16", "pf_weight_bytes", "pf_strerror")
 
 
 class PfError(RuntimeError):
@@ -50,6 +50,10 @@ def load():
     lib.pf_gemm.restype = i32
     lib.pf_gemm_path.argtypes = [i32, P, i64, i64, P, i64, P, i32, i32, P, i32]
     lib.pf_gemm_path.restype = i32
+    lib.pf_workspace_bytes.argtypes = [i32, i64, i64, i64, i32, i32]
+    lib.pf_workspace_bytes.restype = i64
+    lib.pf_gemm_ws.argtypes = [i32, P, i64, i64, P, i64, P, i32, i32, P, i64, P]
+    lib.pf_gemm_ws.restype = i32
     lib.pf_select_path.argtypes = [i32, i64, i64, i64, i32, i32]
     lib.pf_select_path.restype = i32
     lib.pf_dequant_f32.argtypes = [i32, P, i64, i64, P, P]
@@ -94,11 +98,12 @@ def _dev_ptr(t, name):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def gemm(qtype, W, n, k, X, Y, epilogue, leg, stream=None, path=PF_PATH_AUTO):
-    """Y[T][n] = epilogue(X[T][k] . W_hat^T) on the device (see pf_gemm).
+def workspace_bytes(qtype, n, k, T, epilogue, leg):
+    """Bytes of workspace gemm_ws needs (0 if none; negative status on bad sizes)."""
+    return load().pf_workspace_bytes(qtype, n, k, T, epilogue, leg)
 
-    W: uint8 device tensor of blocks; X, Y: float32 device tensors [T][k], [T][n].
-    """
+
+def _check_gemm_args(qtype, W, n, k, X, Y, epilogue):
     import torch
     if X.dtype != torch.float32 or Y.dtype != torch.float32 or W.dtype != torch.uint8:
         raise TypeError("X and Y must be float32 and W uint8")
@@ -109,6 +114,30 @@ def gemm(qtype, W, n, k, X, Y, epilogue, leg, stream=None, path=PF_PATH_AUTO):
     need = load().pf_weight_bytes(qtype, rows, k)
     if need >= 0 and W.numel() < need:
         raise ValueError("W holds %d bytes, %d needed" % (W.numel(), need))
+    return T
+
+
+def gemm_ws(qtype, W, n, k, X, Y, epilogue, leg, workspace, stream=None):
+    """gemm with a caller workspace (a device tensor of at least workspace_bytes()
+    bytes, or None when that is 0); see pf_gemm_ws."""
+    T = _check_gemm_args(qtype, W, n, k, X, Y, epilogue)
+    if workspace is None:
+        ws, ws_bytes = ctypes.c_void_p(0), 0
+    else:
+        ws, ws_bytes = _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    st = load().pf_gemm_ws(qtype, _dev_ptr(W, "W"), n, k, _dev_ptr(X, "X"), T, _dev_ptr(Y, "Y"),
+                           epilogue, leg, ws, ws_bytes, _stream_handle(stream))
+    if st != PF_OK:
+        raise PfError(st, "pf_gemm_ws")
+    return Y
+
+
+def gemm(qtype, W, n, k, X, Y, epilogue, leg, stream=None, path=PF_PATH_AUTO):
+    """Y[T][n] = epilogue(X[T][k] . W_hat^T) on the device (see pf_gemm).
+
+    W: uint8 device tensor of blocks; X, Y: float32 device tensors [T][k], [T][n].
+    """
+    T = _check_gemm_args(qtype, W, n, k, X, Y, epilogue)
     lib = load()
     st = lib.pf_gemm_path(qtype, _dev_ptr(W, "W"), n, k, _dev_ptr(X, "X"), T, _dev_ptr(Y, "Y"),
                           epilogue, leg, _stream_handle(stream), path)

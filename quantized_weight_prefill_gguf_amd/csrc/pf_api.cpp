@@ -43,8 +43,14 @@ int check_sizes(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int le
     return PF_OK;
 }
 
+// Bytes of workspace the f16 leg's GEMM takes (X as binary16), else 0.
+int64_t ws_need(int64_t k, int64_t T, int leg, int use) {
+    return (use == PF_PATH_GEMM && leg == PF_LEG_F16) ? T * k * 2 : 0;
+}
+
 int gemm_impl(int qtype, const void *W, int64_t n, int64_t k, const float *X, int64_t T, float *Y,
-              int epilogue, int leg, void *stream, int path) {
+              int epilogue, int leg, void *stream, int path, bool with_ws, void *ws,
+              int64_t ws_bytes) {
     int64_t n_w = 0;
     int st = check_sizes(qtype, n, k, T, epilogue, leg, &n_w);
     if (st != PF_OK) return st;
@@ -56,6 +62,14 @@ int gemm_impl(int qtype, const void *W, int64_t n, int64_t k, const float *X, in
     const int64_t w_bytes = n_w * (k / 32) * block_bytes(qtype);
     const int64_t x_bytes = T * k * 4, y_bytes = T * n * 4;
     if (overlap(Y, y_bytes, X, x_bytes) || overlap(Y, y_bytes, W, w_bytes)) return PF_E_ALIAS;
+    const int use = path == PF_PATH_AUTO ? (T <= PF_GEMV_MAX_T ? PF_PATH_GEMV : PF_PATH_GEMM) : path;
+    const int64_t need = with_ws ? ws_need(k, T, leg, use) : 0;
+    if (need > 0) {
+        if (!ws || ws_bytes < need || !aligned16(ws)) return PF_E_WORKSPACE;
+        if (overlap(ws, need, W, w_bytes) || overlap(ws, need, X, x_bytes) ||
+            overlap(ws, need, Y, y_bytes))
+            return PF_E_WORKSPACE;
+    }
 
     pf::GemmArgs a;
     a.qtype = qtype;
@@ -67,12 +81,13 @@ int gemm_impl(int qtype, const void *W, int64_t n, int64_t k, const float *X, in
     a.k = (int)k;
     a.T = (int)T;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const int use = path == PF_PATH_AUTO ? (T <= PF_GEMV_MAX_T ? PF_PATH_GEMV : PF_PATH_GEMM) : path;
     hipError_t err;
     if (use == PF_PATH_GEMV)
         err = pf::launch_gemv(a, s);
     else if (leg == PF_LEG_F32)
         err = pf::launch_gemm_f32(a, s);
+    else if (need > 0)
+        err = pf::launch_gemm_f16_ws(a, ws, s);
     else
         err = pf::launch_gemm_f16(a, s);
     return err == hipSuccess ? PF_OK : PF_E_LAUNCH;
@@ -94,12 +109,28 @@ extern "C" {
 
 int pf_gemm(int qtype, const void *W_blocks, int64_t n, int64_t k, const float *X, int64_t T,
             float *Y, int epilogue, int leg, void *stream) {
-    return gemm_impl(qtype, W_blocks, n, k, X, T, Y, epilogue, leg, stream, PF_PATH_AUTO);
+    return gemm_impl(qtype, W_blocks, n, k, X, T, Y, epilogue, leg, stream, PF_PATH_AUTO, false,
+                     nullptr, 0);
+}
+
+int pf_gemm_ws(int qtype, const void *W_blocks, int64_t n, int64_t k, const float *X, int64_t T,
+               float *Y, int epilogue, int leg, void *workspace, int64_t workspace_bytes,
+               void *stream) {
+    return gemm_impl(qtype, W_blocks, n, k, X, T, Y, epilogue, leg, stream, PF_PATH_AUTO, true,
+                     workspace, workspace_bytes);
+}
+
+int64_t pf_workspace_bytes(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int leg) {
+    int64_t n_w = 0;
+    const int st = check_sizes(qtype, n, k, T, epilogue, leg, &n_w);
+    if (st != PF_OK) return -st;
+    if (T == 0) return 0;
+    return ws_need(k, T, leg, T <= PF_GEMV_MAX_T ? PF_PATH_GEMV : PF_PATH_GEMM);
 }
 
 int pf_gemm_path(int qtype, const void *W_blocks, int64_t n, int64_t k, const float *X,
                  int64_t T, float *Y, int epilogue, int leg, void *stream, int path) {
-    return gemm_impl(qtype, W_blocks, n, k, X, T, Y, epilogue, leg, stream, path);
+    return gemm_impl(qtype, W_blocks, n, k, X, T, Y, epilogue, leg, stream, path, false, nullptr, 0);
 }
 
 int pf_select_path(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int leg) {
@@ -149,6 +180,7 @@ const char *pf_strerror(int status) {
     case PF_E_ALIAS: return "PF_E_ALIAS: output overlaps an input";
     case PF_E_LAUNCH: return "PF_E_LAUNCH: kernel launch failed";
     case PF_E_PATH: return "PF_E_PATH: unknown path or GEMV with T > 8";
+    case PF_E_WORKSPACE: return "PF_E_WORKSPACE: workspace missing, too small, misaligned or overlapping";
     default: return "unknown status";
     }
 }

@@ -51,31 +51,49 @@ __device__ __forceinline__ uint32_t h2_bits(h2_t v) { return __builtin_bit_cast(
 // exact f32 product.
 // ---------------------------------------------------------------------------
 
-// Q4_0: w holds qs bytes 4g .. 4g+3 of a block. Returns 4 packed half2 whose 8
-// halves are the weights at k = 4g, 4g+2, 4g+1, 4g+3, 16+4g, 16+4g+2, 16+4g+1,
-// 16+4g+3 (low nibbles, then high nibbles). The activation side stores X in this
-// same order, so the k order inside a block never matters to the dot product.
-__device__ __forceinline__ void q4_word_to_h8(uint32_t w, h2_t d2, uint32_t out[4]) {
-    const h2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
-    uint32_t r0 = (w & 0x000F000Fu) | 0x64006400u;
-    uint32_t r1 = ((w >> 8) & 0x000F000Fu) | 0x64006400u;
-    uint32_t r2 = ((w >> 4) & 0x000F000Fu) | 0x64006400u;
-    uint32_t r3 = ((w >> 12) & 0x000F000Fu) | 0x64006400u;
-    out[0] = h2_bits((as_h2(r0) - off) * d2);
-    out[1] = h2_bits((as_h2(r1) - off) * d2);
-    out[2] = h2_bits((as_h2(r2) - off) * d2);
-    out[3] = h2_bits((as_h2(r3) - off) * d2);
+// v_perm_b32 byte selection: result byte i = byte sel[i] of {src0 (bytes 4-7),
+// src1 (bytes 0-3)}. With src0 = 0x64646464 this builds binary16 patterns
+// 0x64vv = 1024 + v from chosen bytes v of src1.
+constexpr uint32_t MAGIC_BYTES = 0x64646464u;
+constexpr uint32_t SEL_B02 = 0x04020400u;  // (src1.b0, 0x64, src1.b2, 0x64)
+constexpr uint32_t SEL_B13 = 0x04030401u;  // (src1.b1, 0x64, src1.b3, 0x64)
+constexpr uint32_t SEL_B01 = 0x04010400u;  // (src1.b0, 0x64, src1.b1, 0x64)
+constexpr uint32_t SEL_B23 = 0x04030402u;  // (src1.b2, 0x64, src1.b3, 0x64)
+
+__device__ __forceinline__ uint32_t magic_pair(uint32_t bytes, uint32_t sel) {
+    return __builtin_amdgcn_perm(MAGIC_BYTES, bytes, sel);
 }
 
-// Q8_0: w holds 4 int8 q (bytes 4i .. 4i+3). Returns 2 packed half2 = d*q for the
-// 4 bytes in order. x ^ 0x80 turns int8 q into the unsigned byte q + 128.
+// Q4_0: w holds 4 qs bytes b0..b3 (weights j, j+1, j+2, j+3 in their low nibbles
+// and j+16 .. j+19 in their high nibbles). Outputs, each a packed half2 of
+// RNE(d * (q - 8)): lo02 = low nibbles of b0, b2; lo13 = low nibbles of b1, b3;
+// hi02, hi13 likewise for the high nibbles.
+__device__ __forceinline__ void q4_word_decode(uint32_t w, h2_t d2, uint32_t &lo02,
+                                               uint32_t &lo13, uint32_t &hi02,
+                                               uint32_t &hi13) {
+    const h2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const uint32_t lo = w & 0x0F0F0F0Fu;
+    const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
+    lo02 = h2_bits((as_h2(magic_pair(lo, SEL_B02)) - off) * d2);
+    lo13 = h2_bits((as_h2(magic_pair(lo, SEL_B13)) - off) * d2);
+    hi02 = h2_bits((as_h2(magic_pair(hi, SEL_B02)) - off) * d2);
+    hi13 = h2_bits((as_h2(magic_pair(hi, SEL_B13)) - off) * d2);
+}
+
+// Q4_0, 16x16x32 fragment form: the 8 halves of out[0..3] are the weights at
+// k = 4g, 4g+2, 4g+1, 4g+3, 16+4g, 16+4g+2, 16+4g+1, 16+4g+3 when w holds qs
+// bytes 4g .. 4g+3.
+__device__ __forceinline__ void q4_word_to_h8(uint32_t w, h2_t d2, uint32_t out[4]) {
+    q4_word_decode(w, d2, out[0], out[1], out[2], out[3]);
+}
+
+// Q8_0: w holds 4 int8 q (bytes 4i .. 4i+3). Returns 2 packed half2 = RNE(d*q)
+// for the 4 bytes in order. x ^ 0x80 turns int8 q into the unsigned byte q + 128.
 __device__ __forceinline__ void q8_word_to_h4(uint32_t w, h2_t d2, uint32_t out[2]) {
     const h2_t off = {(_Float16)1152.0f, (_Float16)1152.0f};
-    uint32_t x = w ^ 0x80808080u;
-    uint32_t r0 = (x & 0xFFu) | ((x & 0xFF00u) << 8) | 0x64006400u;
-    uint32_t r1 = ((x >> 16) & 0xFFu) | ((x >> 8) & 0xFF0000u) | 0x64006400u;
-    out[0] = h2_bits((as_h2(r0) - off) * d2);
-    out[1] = h2_bits((as_h2(r1) - off) * d2);
+    const uint32_t x = w ^ 0x80808080u;
+    out[0] = h2_bits((as_h2(magic_pair(x, SEL_B01)) - off) * d2);
+    out[1] = h2_bits((as_h2(magic_pair(x, SEL_B23)) - off) * d2);
 }
 
 // ---------------------------------------------------------------------------
@@ -92,5 +110,11 @@ __device__ __forceinline__ float q8_byte_f32(uint32_t w, int byte, float d) {
 // Epilogue helpers. silu(g) = g / (1 + e^-g), evaluated in f32.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
+
+// The same with the hardware exp2 and reciprocal (a few ulp; for the f16 leg,
+// whose tolerance is far above that). g -> -inf gives -0, as the definition does.
+__device__ __forceinline__ float silu_fast(float g) {
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
 
 }  // namespace pf

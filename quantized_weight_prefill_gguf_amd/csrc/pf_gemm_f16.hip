@@ -1,28 +1,38 @@
 // Tiled GEMM, f16 leg: fp16 inputs, fp32 accumulation, f32 output
-// (v_mfma_f32_16x16x32_f16), the f16 leg of the page "aprender-serve 0.70.2 -
+// (v_mfma_f32_32x32x16_f16), the f16 leg of the page "aprender-serve 0.70.2 -
 // src/cuda/executor/gdn_prefill_ops.rs" (module doc, group 1, and
 // `qwen35_project_rows_f16`): weights and activations rounded to fp16,
 // accumulation and output in fp32. Unlike that page nothing is cached or
 // converted in HBM: X is rounded to fp16 while it is staged into LDS, and each
-// weight block is decoded to fp16 in registers right before the MFMA that eats it.
+// weight block is decoded to fp16 in registers right before the MFMAs that eat it.
 //
 // Workgroup: 256 threads = 4 waves in a 2 x 2 grid; tile MT token rows x NW weight
-// rows; each wave owns (MT/2) x (NW/2) of the fp32 accumulators.
-// K loop: one 32-weight block per step (one 16x16x32 MFMA per 16x16 tile).
+// rows; each wave owns (MT/2) x (NW/2) fp32 accumulators as 32 x 32 MFMA tiles.
+// K loop: one 32-weight block per step = two 32x32x16 MFMAs per tile.
 //  - Weight bytes move in chunks of 8 blocks (256 k): a row's chunk is 144 (Q4_0)
 //    or 272 (Q8_0) bytes, 16-byte aligned in HBM when k % 256 == 0, so it is copied
-//    raw, GGUF AoS as it is, with 16-byte loads into a double-buffered LDS chunk.
-//    Each step copies 1/8 of the next chunk.
+//    raw (GGUF AoS as stored) with 16-byte loads into a double-buffered LDS chunk,
+//    1/8 of the next chunk per step.
 //  - X moves one step (32 k) at a time: f32 loads, RNE to fp16, stored in LDS in
-//    the k order the weight decode produces (double-buffered).
-//  - X loads run one step ahead of the step they feed, weight loads two.
-// Lane (c, g) of the B operand decodes 8 weights of its column's block: for Q4_0
-// the low and high nibbles of qs bytes 4g..4g+3, for Q8_0 the int8 bytes
-// 8g..8g+7; X sits in LDS in the same k order, so an A fragment is one 16-byte read.
+//    the k order the weight decode produces, two steps ahead of its use.
+//  - Software pipeline: while step s's MFMAs run, the wave reads step s+1's A
+//    fragments and raw weight words from LDS and decodes the weights, so neither
+//    LDS latency nor the decode sits between barrier and matrix core.
+//  - The 8 steps of a chunk are unrolled, so every LDS offset and the alignment
+//    of every block inside the chunk are compile-time constants.
+// Lane (c, h) of a B fragment (column c, half h) decodes 16 weights of its
+// column's block: Q4_0 qs bytes 8h .. 8h+7 (low nibbles feed the first MFMA, high
+// nibbles the second), Q8_0 int8 bytes 8h .. 8h+7 and 16+8h .. 16+8h+7.
 //
-// Large-n shapes (the gate/up SwiGLU) run one workgroup per output tile; narrow
-// ones (n = 4096 at T = 512) split K over workgroups that add their partial sums
-// into Y with fp32 atomics (PLAIN zero-fills Y first).
+// GATE_UP_SWIGLU: each 32-column tile holds 16 gate rows and the 16 up rows of
+// the same outputs, so g and u of one output sit in lanes c and c+16 of the same
+// register; the epilogue swaps them across the two lane groups.
+//
+// Large-n shapes run one workgroup per output tile; narrow ones (n = 4096 at
+// T = 512) split K over workgroups that add partial sums into Y with fp32 atomics
+// (PLAIN zero-fills Y first).
+#include <type_traits>
+
 #include "pf_device.h"
 #include "pf_internal.h"
 
@@ -30,21 +40,36 @@ namespace pf {
 
 namespace {
 
-constexpr int XS = 40;  // LDS halves per staged X row: 32 + 8 pad (80 bytes)
-
 template <int QT> struct ChunkTraits {
     static constexpr int BB = BlockTraits<QT>::BYTES;
     static constexpr int ROW = 8 * BB;      // bytes of one row's chunk (144 / 272)
     static constexpr int U4 = ROW / 16;     // 16-byte pieces per row chunk (9 / 17)
 };
 
-// Where the float4 holding k = 4*c4 .. 4*c4+3 of a block lands (in halves, within
-// the row's 32-half segment), so that lane group g finds halves 8g .. 8g+7 ready.
-template <int QT> __device__ __forceinline__ int x_half_pos(int c4) {
+typedef float f16v_t __attribute__((ext_vector_type(16)));
+
+// Staged X: within each group of four k, Q4_0 fragments take the order 0, 2, 1, 3
+// (the nibble-pair order of q4_word_decode); Q8_0 takes natural order. Lane half
+// h of MFMA s reads halves 16s + 8h .. 16s + 8h + 7 of the row's block segment.
+template <int QT> __device__ __forceinline__ u2_t x_pack(f4_t v) {
     if constexpr (QT == Q4_0)
-        return 8 * (c4 & 3) + 4 * (c4 >> 2);  // stored as (x0, x2, x1, x3)
+        return u2_t{h2_bits(h2_t{(_Float16)v[0], (_Float16)v[2]}),
+                    h2_bits(h2_t{(_Float16)v[1], (_Float16)v[3]})};
     else
-        return 4 * c4;                         // natural order
+        return u2_t{h2_bits(h2_t{(_Float16)v[0], (_Float16)v[1]}),
+                    h2_bits(h2_t{(_Float16)v[2], (_Float16)v[3]})};
+}
+
+// The 32-bit window starting at byte `addr` of LDS buffer `b`; (addr & 3) == SH
+// is a compile-time constant.
+template <int SH>
+__device__ __forceinline__ uint32_t lds_word(const uint8_t *b, int addr) {
+    if constexpr (SH == 0) {
+        return *reinterpret_cast<const uint32_t *>(b + addr);
+    } else {
+        const uint32_t *al = reinterpret_cast<const uint32_t *>(b + addr - SH);
+        return __builtin_amdgcn_alignbyte(al[1], al[0], SH);
+    }
 }
 
 }  // namespace
@@ -53,43 +78,52 @@ template <int QT> __device__ __forceinline__ int x_half_pos(int c4) {
 template <int EPI, int NW>
 __device__ __forceinline__ int f16_weight_row(int tile_n, int lr, int n) {
     if constexpr (EPI == EPI_SWIGLU) {
-        constexpr int HALF = NW / 2;
-        const int o = tile_n * HALF + (lr % HALF);
+        // 32-row groups: rows 0..15 gate, 16..31 up, for 16 consecutive outputs
+        const int o = tile_n * (NW / 2) + (lr >> 5) * 16 + (lr & 15);
         if (o >= n) return -1;
-        return lr < HALF ? o : n + o;
+        return (lr & 16) ? n + o : o;
     } else {
         const int r = tile_n * NW + lr;
         return r < n ? r : -1;
     }
 }
 
-template <int QT, int EPI, int MT, int NW, bool SPLIT>
+template <int QT, int EPI, int MT, int NW, bool SPLIT, bool XH>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_f16_kernel(const uint8_t *__restrict__ W, const float *__restrict__ X,
+void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
                      float *__restrict__ Y, int n, int k, int T, int tiles_m, int tiles_n,
                      int splits) {
     using CT = ChunkTraits<QT>;
-    constexpr int IT = MT / 32;           // 16-row MFMA tiles per wave
-    constexpr int JT = NW / 32;           // 16-column MFMA tiles per wave
-    constexpr int XF4 = MT / 32;          // X float4 loads per thread per step
-    constexpr int WU = (NW * CT::U4 + 7) / 8;       // 16-byte pieces per step (1/8 chunk)
-    constexpr int WPT = (WU + 255) / 256;           // pieces per thread per step
+    constexpr int BB = CT::BB;
+    constexpr int IT = MT / 64;           // 32-row MFMA tiles per wave
+    constexpr int JT = NW / 64;           // 32-column MFMA tiles per wave
+    constexpr int XF4 = MT / 32;          // f32 X: float4 loads per thread per step
+    constexpr int XH4 = MT / 64;          // fp16 X: 16-byte loads per thread per step
+    constexpr int U4 = CT::U4;                      // 16-byte pieces per row chunk
     constexpr int WROW = CT::ROW;
-    constexpr int WBUF = NW * WROW + 16;            // +16: decode reads one dword past a row
+    constexpr int WBUF = NW * WROW + 16;            // +16: decode reads a dword past a row
+    constexpr int NW32 = (QT == Q4_0) ? 2 : 4;      // qs words per lane per block
 
-    __shared__ __attribute__((aligned(16))) _Float16 xs[2][MT * XS];
-    __shared__ __attribute__((aligned(16))) uint8_t wsm[2][WBUF];
+    // One LDS block: the K loop's two X buffers and two weight chunks; after the
+    // loop, the SwiGLU epilogue reuses its start as 4 per-wave 32 x 36 float slots.
+    constexpr int XBUF_BYTES = MT * 32 * 2;
+    constexpr int LOOP_BYTES = 2 * XBUF_BYTES + 2 * WBUF;
+    constexpr int EPI_BYTES = 4 * 32 * 36 * 4;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[LOOP_BYTES > EPI_BYTES ? LOOP_BYTES : EPI_BYTES];
+    _Float16 (*xs)[MT * 32] = reinterpret_cast<_Float16 (*)[MT * 32]>(smem);
+    uint8_t (*wsm)[WBUF] = reinterpret_cast<uint8_t (*)[WBUF]>(smem + 2 * XBUF_BYTES);
+    static_assert(WBUF % 16 == 0 && XBUF_BYTES % 16 == 0, "LDS carve-up keeps 16-byte alignment");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int c = lane & 15, g = lane >> 4;
+    const int c = lane & 31, h = lane >> 5;
 
-    // Workgroup -> tile. Dispatch spreads consecutive workgroup ids over the 8 XCDs;
-    // remap so that each XCD gets a contiguous run of tiles in which the M tiles of
-    // one weight tile are adjacent (they share the weight chunk in that XCD's L2).
+    // Workgroup -> tile. Dispatch spreads consecutive workgroup ids over the 8
+    // XCDs; remap so that each XCD gets a contiguous run of tiles in which the M
+    // tiles of one weight tile are adjacent (they share its chunks in that L2).
     const int total = tiles_m * tiles_n * splits;
     int logical;
     {
@@ -107,188 +141,290 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const float *__restrict__ X,
     const int nchunks = k >> 8;
     const int c_begin = (int)((long)nchunks * split / splits);
     const int c_end = (int)((long)nchunks * (split + 1) / splits);
-    const int nsteps = 8 * (c_end - c_begin);
-    const int nb = k >> 5;
-    const size_t row_bytes = (size_t)nb * CT::BB;
+    const int nch = c_end - c_begin;
+    if (nch <= 0) return;  // cannot happen (splits <= chunks); keeps the loop simple
+    const int nsteps = 8 * nch;
+    const uint32_t row_bytes = (uint32_t)(k >> 5) * BB;
 
-    // ---- per-thread staging assignments (fixed over the K loop). Every global
-    // load is unconditional so the wait counters stay exact: rows past T (X) or
-    // past the weight read a valid row instead; such rows only feed outputs that
-    // are never stored.
-    const float *xsrc[XF4];
-    int xdst[XF4];
+    // ---- staging assignments (fixed over the K loop), as 32-bit byte offsets
+    // from uniform bases. Global loads are all unconditional so that the wait
+    // counters stay exact: rows past T or past the weight read a valid row
+    // instead; such rows only feed outputs that are never stored.
+    // Staged X rows are 32 halves (4 chunks of 16 bytes); chunk q of row r sits at
+    // chunk q ^ ((r >> 2) & 3), which keeps both the staging writes and the
+    // fragment reads free of LDS bank conflicts.
+    // f32 X (XH false): thread t converts float4 (t & 7) of rows (t >> 3) + 32 i.
+    // fp16 X (XH true, already in fragment k order): thread t copies 16-byte chunk
+    // (t & 3) of rows (t >> 2) + 64 i.
+    constexpr int XN = XH ? XH4 : XF4;
+    const uint8_t *xbase = reinterpret_cast<const uint8_t *>(Xv) + (size_t)c_begin * 256 * (XH ? 2 : 4);
+    uint32_t xoff[XN];
+    int xdst;
+    if constexpr (XH) {
 #pragma unroll
-    for (int i = 0; i < XF4; ++i) {
-        const int row = (tid >> 3) + 32 * i;
-        const int c4 = tid & 7;
-        const int t = min(m0 + row, T - 1);
-        xsrc[i] = X + (size_t)t * k + 4 * c4;
-        xdst[i] = row * XS + x_half_pos<QT>(c4);
-    }
-    // Weight pieces: slice s of a chunk is pieces [s*WU, (s+1)*WU); piece u is row
-    // u / U4, 16-byte piece u % U4. wdst = this thread's index within a slice.
-    int wdst[WPT];
-#pragma unroll
-    for (int i = 0; i < WPT; ++i) wdst[i] = (tid + 256 * i < WU) ? tid + 256 * i : -1;
-
-    // ---- B-operand rows of this wave's column tiles
-    int brow[JT];
-#pragma unroll
-    for (int j = 0; j < JT; ++j) {
-        if constexpr (EPI == EPI_SWIGLU) {
-            constexpr int HALF = NW / 2, PER = JT / 2 * 16;
-            brow[j] = (j < JT / 2) ? wn * PER + j * 16 + c : HALF + wn * PER + (j - JT / 2) * 16 + c;
-        } else {
-            brow[j] = wn * (JT * 16) + j * 16 + c;
+        for (int i = 0; i < XN; ++i) {
+            const int t = min(m0 + (tid >> 2) + 64 * i, T - 1);
+            xoff[i] = ((uint32_t)t * (uint32_t)k + 8 * (tid & 3)) * 2;
         }
+        // rows (tid >> 2) + 64 i share (row >> 2) & 3
+        xdst = (tid >> 2) * 32 + (((tid & 3) ^ ((tid >> 4) & 3)) << 3);
+    } else {
+#pragma unroll
+        for (int i = 0; i < XN; ++i) {
+            const int t = min(m0 + (tid >> 3) + 32 * i, T - 1);
+            xoff[i] = ((uint32_t)t * (uint32_t)k + 4 * (tid & 7)) * 4;
+        }
+        // rows (tid >> 3) + 32 i share (row >> 2) & 3
+        xdst = (tid >> 3) * 32 + ((((tid & 7) >> 1) ^ ((tid >> 5) & 3)) << 3) + 4 * (tid & 1);
     }
+    // Weight staging: thread t < NW copies local row t. Slice s of a chunk is the
+    // row's 16-byte pieces p == s (mod 8); offsets are a per-thread base plus
+    // compile-time immediates.
+    const bool wrow_thread = tid < NW;
+    const uint8_t *wbase = W + (size_t)c_begin * WROW;
+    uint32_t wsrc_row;
+    {
+        int gr = f16_weight_row<EPI, NW>(tn, wrow_thread ? tid : 0, n);
+        gr = gr < 0 ? 0 : gr;
+        wsrc_row = (uint32_t)gr * row_bytes;
+    }
+    const int wdst_row = (wrow_thread ? tid : 0) * WROW;
 
-    f4_t acc[IT][JT];
+    // LDS offsets of this lane's B rows (column c of tile j: bbase + j 32 WROW) and
+    // A fragments.
+    const int bbase = (wn * JT * 32 + c) * WROW;
+    const int sw = (c >> 2) & 3;
+    const int arow = (wm * IT * 32 + c) * 32;
+    const int aoff[2] = {arow + ((h ^ sw) << 3), arow + (((2 + h) ^ sw) << 3)};
+
+    f16v_t acc[IT][JT];
 #pragma unroll
     for (int i = 0; i < IT; ++i)
 #pragma unroll
-        for (int j = 0; j < JT; ++j) acc[i][j] = f4_t{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < JT; ++j) acc[i][j] = f16v_t{};
 
-    f4_t xr[1][XF4];
-    u4_t wr[2][WPT];
+    h8_t afr[2][IT][2];   // A fragments [step parity][tile][MFMA half]
+    h8_t bfr[2][JT][2];   // decoded B fragments [step parity][tile][MFMA half]
+    f4_t xr[XF4];         // f32 X for the staging write of the next step
+    u4_t xh[2][XH4];      // fp16 X for the staging writes of the next two steps
+    constexpr int MAXP = (U4 + 7) / 8;  // pieces in the largest slice (2 / 3)
+    u4_t wr[2][MAXP];     // weight slices for the writes of the next two steps
 
-    auto x_load = [&](int step, f4_t *dst) __attribute__((always_inline)) {
-        const int koff = (c_begin * 8 + step) * 32;
-#pragma unroll
-        for (int i = 0; i < XF4; ++i) dst[i] = *reinterpret_cast<const f4_t *>(xsrc[i] + koff);
-    };
-    auto x_store = [&](const f4_t *src, int buf) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < XF4; ++i) {
-            const f4_t v = src[i];
-            h2_t p0, p1;
-            if constexpr (QT == Q4_0) {
-                p0 = h2_t{(_Float16)v[0], (_Float16)v[2]};
-                p1 = h2_t{(_Float16)v[1], (_Float16)v[3]};
-            } else {
-                p0 = h2_t{(_Float16)v[0], (_Float16)v[1]};
-                p1 = h2_t{(_Float16)v[2], (_Float16)v[3]};
-            }
-            *reinterpret_cast<u2_t *>(&xs[buf][xdst[i]]) = u2_t{h2_bits(p0), h2_bits(p1)};
-        }
-    };
-    const int last_chunk = c_end - c_begin - 1;
-    // Slice `slice` (0..7) of chunk `chunk` (relative to c_begin) into registers.
-    // Out-of-range pieces, rows or chunks load a valid address and are not stored.
-    auto w_load = [&](int chunk, int slice, u4_t *dst) __attribute__((always_inline)) {
-        const int ch = min(chunk, last_chunk);
-#pragma unroll
-        for (int i = 0; i < WPT; ++i) {
-            const int u = min(slice * WU + max(wdst[i], 0), NW * CT::U4 - 1);
-            const int lr = u / CT::U4, piece = u % CT::U4;
-            int gr = f16_weight_row<EPI, NW>(tn, lr, n);
-            gr = gr < 0 ? 0 : gr;
-            dst[i] = *reinterpret_cast<const u4_t *>(W + (size_t)gr * row_bytes +
-                                                      (size_t)(c_begin + ch) * WROW + 16 * piece);
-        }
-    };
-    auto w_store = [&](int chunk, int slice, const u4_t *src) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < WPT; ++i) {
-            const int u = slice * WU + wdst[i];
-            if (wdst[i] >= 0 && u < NW * CT::U4 && chunk <= last_chunk) {
-                const int lr = u / CT::U4, piece = u % CT::U4;
-                *reinterpret_cast<u4_t *>(&wsm[chunk & 1][lr * WROW + 16 * piece]) = src[i];
-            }
-        }
-    };
-
-    // One K step: A fragments from LDS, B fragments decoded from the raw chunk.
-    auto compute = [&](int step) __attribute__((always_inline)) {
-        const int xb = step & 1;
-        const int chunk = step >> 3;
-        const int blk = step & 7;
-        const uint8_t *wb = wsm[chunk & 1];
-        h8_t a[IT];
+    auto load_a = [&](int xb, h8_t (&dst)[IT][2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < IT; ++i)
-            a[i] = *reinterpret_cast<const h8_t *>(&xs[xb][(wm * IT * 16 + i * 16 + c) * XS + 8 * g]);
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                dst[i][s] = *reinterpret_cast<const h8_t *>(&xs[xb][aoff[s] + i * 32 * 32]);
+    };
+    // Read this lane's raw bytes of block `blk` (compile-time) and decode them.
+    auto load_decode_b = [&](const uint8_t *wb, auto blk_c, h8_t (&dst)[JT][2])
+        __attribute__((always_inline)) {
+        constexpr int blk = decltype(blk_c)::value;
+        constexpr int SH = (blk * BB + 2) & 3;
+        uint32_t d16[JT], q[JT][NW32];
 #pragma unroll
         for (int j = 0; j < JT; ++j) {
-            const int base = brow[j] * WROW + blk * CT::BB;
-            const uint32_t d16 = *reinterpret_cast<const uint16_t *>(wb + base);
-            const h2_t d2 = as_h2(d16 | (d16 << 16));
-            uint32_t p[4];
-            if constexpr (QT == Q4_0) {
-                const int addr = base + 2 + 4 * g;  // qs bytes 4g .. 4g+3
-                const uint32_t *al = reinterpret_cast<const uint32_t *>(wb + (addr & ~3));
-                const uint32_t w = (uint32_t)((((uint64_t)al[1] << 32) | al[0]) >> (8 * (addr & 3)));
-                q4_word_to_h8(w, d2, p);
-            } else {
-                const int addr = base + 2 + 8 * g;  // qs bytes 8g .. 8g+7
-                const uint32_t *al = reinterpret_cast<const uint32_t *>(wb + (addr & ~3));
-                const int sh = 8 * (addr & 3);
-                const uint32_t w0 = (uint32_t)((((uint64_t)al[1] << 32) | al[0]) >> sh);
-                const uint32_t w1 = (uint32_t)((((uint64_t)al[2] << 32) | al[1]) >> sh);
-                q8_word_to_h4(w0, d2, p);
-                q8_word_to_h4(w1, d2, p + 2);
-            }
-            const h8_t b = __builtin_bit_cast(h8_t, u4_t{p[0], p[1], p[2], p[3]});
+            const int base = bbase + j * 32 * WROW + blk * BB;
+            d16[j] = *reinterpret_cast<const uint16_t *>(wb + base);
 #pragma unroll
-            for (int i = 0; i < IT; ++i)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b, acc[i][j], 0, 0, 0);
+            for (int w = 0; w < NW32; ++w)
+                q[j][w] = lds_word<SH>(wb, base + 2 + 8 * h + 4 * (w & 1) + 16 * (w >> 1));
+        }
+#pragma unroll
+        for (int j = 0; j < JT; ++j) {
+            const h2_t d2 = as_h2(d16[j] | (d16[j] << 16));
+            uint32_t p[8];
+            if constexpr (QT == Q4_0) {
+                q4_word_decode(q[j][0], d2, p[0], p[1], p[4], p[5]);
+                q4_word_decode(q[j][1], d2, p[2], p[3], p[6], p[7]);
+            } else {
+                q8_word_to_h4(q[j][0], d2, p + 0);
+                q8_word_to_h4(q[j][1], d2, p + 2);
+                q8_word_to_h4(q[j][2], d2, p + 4);
+                q8_word_to_h4(q[j][3], d2, p + 6);
+            }
+            dst[j][0] = __builtin_bit_cast(h8_t, u4_t{p[0], p[1], p[2], p[3]});
+            dst[j][1] = __builtin_bit_cast(h8_t, u4_t{p[4], p[5], p[6], p[7]});
+        }
+    };
+    // f32 X: registers (one step ahead) -> fp16 in LDS.
+    auto store_x = [&](int xb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < XF4; ++i)
+            *reinterpret_cast<u2_t *>(&xs[xb][xdst + i * 32 * 32]) = x_pack<QT>(xr[i]);
+    };
+    auto fetch_x = [&](int step) __attribute__((always_inline)) {
+        const uint8_t *xb = xbase + 128 * min(step, nsteps - 1);
+#pragma unroll
+        for (int i = 0; i < XF4; ++i) xr[i] = *reinterpret_cast<const f4_t *>(xb + xoff[i]);
+    };
+    // fp16 X: registers (two steps ahead) -> LDS, no conversion.
+    auto store_xh = [&](int xb, const u4_t (&src)[XH4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < XH4; ++i)
+            *reinterpret_cast<u4_t *>(&xs[xb][xdst + i * 64 * 32]) = src[i];
+    };
+    auto fetch_xh = [&](int step, u4_t (&dst)[XH4]) __attribute__((always_inline)) {
+        const uint8_t *xb = xbase + 64 * min(step, nsteps - 1);
+#pragma unroll
+        for (int i = 0; i < XH4; ++i) dst[i] = *reinterpret_cast<const u4_t *>(xb + xoff[i]);
+    };
+
+    // Slice S (compile-time) of chunk `chunk`: load to registers / store to LDS.
+    auto fetch_slice = [&](int chunk, auto s_c, u4_t (&dst)[MAXP]) __attribute__((always_inline)) {
+        constexpr int S = decltype(s_c)::value;
+        const uint8_t *src = wbase + (size_t)min(chunk, nch - 1) * WROW + wsrc_row;
+#pragma unroll
+        for (int p = 0; p < MAXP; ++p)
+            if (S + 8 * p < U4) dst[p] = *reinterpret_cast<const u4_t *>(src + 16 * (S + 8 * p));
+    };
+    auto store_slice = [&](uint8_t *buf, auto s_c, const u4_t (&src)[MAXP]) __attribute__((always_inline)) {
+        constexpr int S = decltype(s_c)::value;
+        if (wrow_thread) {
+#pragma unroll
+            for (int p = 0; p < MAXP; ++p)
+                if (S + 8 * p < U4) *reinterpret_cast<u4_t *>(buf + wdst_row + 16 * (S + 8 * p)) = src[p];
         }
     };
 
-    if (nsteps > 0) {
-        // ---- prologue: chunk 0 whole and X for step 0 in LDS; X for step 1 and
-        // the weight slices for steps 0, 1 (chunk 1) in registers.
-        for (int s = 0; s < 8; ++s) {
-            w_load(0, s, wr[0]);
-            w_store(0, s, wr[0]);
-        }
-        x_load(0, xr[0]);
-        x_store(xr[0], 0);
-        x_load(min(1, nsteps - 1), xr[0]);
-        w_load(1, 0, wr[0]);
-        w_load(1, 1, wr[1]);
-        __syncthreads();
+    // ---- prologue. LDS: chunk 0, slice 0 of chunk 1, X(0), X(1). Registers: X(2),
+    // the slices written by steps 0 and 1 (chunk 1 slices 1, 2), and the A and
+    // decoded B fragments of step 0.
+    {
+        u4_t tmp[MAXP];
+#define PF_CHUNK0_SLICE(S)                                           \
+        fetch_slice(0, std::integral_constant<int, S>{}, tmp);       \
+        store_slice(wsm[0], std::integral_constant<int, S>{}, tmp);
+        PF_CHUNK0_SLICE(0) PF_CHUNK0_SLICE(1) PF_CHUNK0_SLICE(2) PF_CHUNK0_SLICE(3)
+        PF_CHUNK0_SLICE(4) PF_CHUNK0_SLICE(5) PF_CHUNK0_SLICE(6) PF_CHUNK0_SLICE(7)
+#undef PF_CHUNK0_SLICE
+        fetch_slice(1, std::integral_constant<int, 0>{}, tmp);
+        if (nch > 1) store_slice(wsm[1], std::integral_constant<int, 0>{}, tmp);
+        fetch_slice(1, std::integral_constant<int, 1>{}, wr[0]);
+        fetch_slice(1, std::integral_constant<int, 2>{}, wr[1]);
+    }
+    if constexpr (XH) {
+        fetch_xh(0, xh[0]);
+        store_xh(0, xh[0]);
+        fetch_xh(1, xh[1]);
+        store_xh(1, xh[1]);
+        fetch_xh(2, xh[0]);
+        fetch_xh(3, xh[1]);
+    } else {
+        fetch_x(0);
+        store_x(0);
+        fetch_x(1);
+        store_x(1);
+        fetch_x(2);
+    }
+    __syncthreads();
+    load_a(0, afr[0]);
+    load_decode_b(wsm[0], std::integral_constant<int, 0>{}, bfr[0]);
 
-        // Step kb: X(kb+1) sits in xr[0]; the weight slice for step kb (chunk kb/8
-        // + 1, slice kb%8) in wr[0], the one for step kb+1 in wr[1]. X is fetched
-        // one step ahead, weights two.
-        for (int kb = 0; kb < nsteps; ++kb) {
-            if (kb + 1 < nsteps) x_store(xr[0], (kb + 1) & 1);
-            x_load(min(kb + 2, nsteps - 1), xr[0]);
-            w_store((kb >> 3) + 1, kb & 7, wr[0]);
+    for (int ch = 0; ch < nch; ++ch) {
+        // Step s = 8 ch + blk. At its start: LDS holds X(s), X(s+1) and every
+        // slice of chunk ch; afr/bfr[P] hold the fragments of step s; xr (or
+        // xh[P]) holds X(s+2); wr[P] the slice this step writes.
+        auto step_body = [&](auto blk_c) __attribute__((always_inline)) {
+            constexpr int blk = decltype(blk_c)::value;
+            constexpr int P = blk & 1;
+            constexpr int NB = (blk + 1) & 7;            // block of step s+1
+            const int s = ch * 8 + blk;
+            // (1) staging: X(s+2) -> xs[P] (X(s) was consumed during step s-1), then
+            // fetch X(s+3); slice NB of chunk (s+1)/8 + 1 -> LDS, then fetch the
+            // slice step s+2 writes.
+            if constexpr (XH) {
+                store_xh(P, xh[P]);         // X(s+2), fetched at step s-2
+                fetch_xh(s + 4, xh[P]);
+            } else {
+                store_x(P);                 // X(s+2), fetched at step s-1
+                fetch_x(s + 3);
+            }
+            {
+                const int wc = ch + 1 + (blk == 7 ? 1 : 0);  // chunk receiving the slice
+                if (wc < nch) store_slice(wsm[wc & 1], std::integral_constant<int, NB>{}, wr[P]);
+                // the slice written at step s+2: slice (blk+3)%8 of chunk (s+3)/8 + 1
+                fetch_slice(ch + 1 + ((blk + 3) >> 3), std::integral_constant<int, (blk + 3) & 7>{}, wr[P]);
+            }
+            // (2) fragments of step s+1 (its X and chunk are complete in LDS).
+            load_a(P ^ 1, afr[P ^ 1]);
+            load_decode_b(wsm[(ch + (blk == 7 ? 1 : 0)) & 1], std::integral_constant<int, NB>{},
+                          bfr[P ^ 1]);
+            // (3) this step's MFMAs.
 #pragma unroll
-            for (int i = 0; i < WPT; ++i) wr[0][i] = wr[1][i];
-            w_load(((kb + 2) >> 3) + 1, (kb + 2) & 7, wr[1]);
-            compute(kb);
+            for (int j = 0; j < JT; ++j)
+#pragma unroll
+                for (int i = 0; i < IT; ++i) {
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(afr[P][i][0], bfr[P][j][0], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(afr[P][i][1], bfr[P][j][1], acc[i][j], 0, 0, 0);
+                }
             __syncthreads();
-        }
+        };
+        step_body(std::integral_constant<int, 0>{});
+        step_body(std::integral_constant<int, 1>{});
+        step_body(std::integral_constant<int, 2>{});
+        step_body(std::integral_constant<int, 3>{});
+        step_body(std::integral_constant<int, 4>{});
+        step_body(std::integral_constant<int, 5>{});
+        step_body(std::integral_constant<int, 6>{});
+        step_body(std::integral_constant<int, 7>{});
     }
 
-    // ---- epilogue. Lane (c, g) holds D[4g + r][c] of each 16 x 16 tile.
-    constexpr int JO = (EPI == EPI_SWIGLU) ? JT / 2 : JT;
+    // ---- epilogue. Lane (c, h) holds D[8 (r/4) + 4h + r%4][c], r = 0..15.
+    // Indices come from an opaque copy of the thread id so that none of this is
+    // computed before the K loop and held in registers across it.
+    int etid = threadIdx.x;
+    asm volatile("" : "+v"(etid));
+    if constexpr (EPI == EPI_SWIGLU) __syncthreads();  // the X buffers become scratch
+    const int e_lane = etid & 63, e_wave = etid >> 6;
+    const int e_wm = e_wave >> 1, e_wn = e_wave & 1;
+    const int e_c = e_lane & 31, e_h = e_lane >> 5;
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
 #pragma unroll
-        for (int j = 0; j < JO; ++j) {
-            int o;
-            if constexpr (EPI == EPI_SWIGLU)
-                o = tn * (NW / 2) + wn * (JT / 2 * 16) + j * 16 + c;
-            else
-                o = tn * NW + wn * (JT * 16) + j * 16 + c;
-            if (o >= n) continue;
+        for (int j = 0; j < JT; ++j) {
+            const int tile_col = (e_wn * JT + j) * 32;
+            const int trow = m0 + e_wm * IT * 32 + i * 32 + 4 * e_h;
+            if constexpr (EPI == EPI_SWIGLU) {
+                // Columns 0..15 of the tile are gate rows, 16..31 the up rows of the
+                // same 16 outputs. The wave writes the tile to its own LDS slot
+                // transposed ([column][row], rows padded to 36 floats), then each lane
+                // reads four rows of one gate column and of its up column and
+                // finishes 2 x 4 outputs. Same-wave LDS accesses complete in order.
+                float *slot = reinterpret_cast<float *>(smem) + e_wave * (32 * 36);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = m0 + wm * IT * 16 + i * 16 + 4 * g + r;
-                if (t >= T) continue;
-                float *y = Y + (size_t)t * n + o;
-                if constexpr (EPI == EPI_SWIGLU) {
-                    *y = silu_f32(acc[i][j][r]) * acc[i][j + JT / 2][r];
-                } else if constexpr (SPLIT) {
-                    atomicAdd(y, acc[i][j][r]);
-                } else if constexpr (EPI == EPI_PLAIN) {
-                    *y = acc[i][j][r];
-                } else {
-                    *y = *y + acc[i][j][r];
+                for (int g4 = 0; g4 < 4; ++g4)
+                    *reinterpret_cast<f4_t *>(slot + e_c * 36 + 8 * g4 + 4 * e_h) =
+                        f4_t{acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2],
+                             acc[i][j][4 * g4 + 3]};
+                const int cc = e_lane & 15;
+                const int o = tn * (NW / 2) + (tile_col >> 1) + cc;
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const int q = (e_lane >> 4) + 4 * half;  // row quad 0..7
+                    const f4_t g = *reinterpret_cast<const f4_t *>(slot + cc * 36 + 4 * q);
+                    const f4_t u = *reinterpret_cast<const f4_t *>(slot + (cc + 16) * 36 + 4 * q);
+                    const int t0 = m0 + e_wm * IT * 32 + i * 32 + 4 * q;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (t0 + e < T && o < n) Y[(size_t)(t0 + e) * n + o] = silu_fast(g[e]) * u[e];
+                }
+            } else {
+                const int o = tn * NW + tile_col + e_c;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int t = trow + 8 * (r >> 2) + (r & 3);
+                    if (t < T && o < n) {
+                        float *y = Y + (size_t)t * n + o;
+                        // RESIDUAL adds into Y with an atomic even without a K split:
+                        // one writer per element, so the result is the single rounding
+                        // of R + acc either way, and the add needs no VGPR copy of acc.
+                        if constexpr (SPLIT || EPI == EPI_RESIDUAL)
+                            atomicAdd(y, acc[i][j][r]);
+                        else
+                            *y = acc[i][j][r];
+                    }
                 }
             }
         }
@@ -315,7 +451,6 @@ constexpr float CFG_EFF[4] = {1.0f, 0.92f, 0.75f, 0.35f};
 
 TileChoice choose_tiles(const GemmArgs &a) {
     const bool swiglu = a.epilogue == EPI_SWIGLU;
-    const long n_w = swiglu ? 2L * a.n : a.n;
     const int nchunks = a.k / 256;
     const int cus = 256;
     TileChoice best{3, 1};
@@ -333,7 +468,6 @@ TileChoice choose_tiles(const GemmArgs &a) {
             const float work = (float)MT * NW * ((float)a.k / s);
             float t = rounds * work / CFG_EFF[cfg];
             if (s > 1) t *= 1.0f + 0.02f * s;
-            (void)n_w;
             if (t < best_t) {
                 best_t = t;
                 best = TileChoice{cfg, s};
@@ -344,56 +478,86 @@ TileChoice choose_tiles(const GemmArgs &a) {
 }
 
 template <int QT, int EPI, int MT, int NW, bool SPLIT>
-hipError_t launch_cfg(const GemmArgs &a, int splits, hipStream_t s) {
+hipError_t launch_cfg(const GemmArgs &a, int splits, const uint16_t *xh, hipStream_t s) {
     constexpr int OUT = (EPI == EPI_SWIGLU) ? NW / 2 : NW;
     const int tm = (a.T + MT - 1) / MT;
     const int tn = (a.n + OUT - 1) / OUT;
     const int total = tm * tn * splits;
-    hipLaunchKernelGGL((gemm_f16_kernel<QT, EPI, MT, NW, SPLIT>), dim3(total), dim3(256), 0, s,
-                       a.W, a.X, a.Y, a.n, a.k, a.T, tm, tn, splits);
+    if (xh)
+        hipLaunchKernelGGL((gemm_f16_kernel<QT, EPI, MT, NW, SPLIT, true>), dim3(total), dim3(256), 0,
+                           s, a.W, (const void *)xh, a.Y, a.n, a.k, a.T, tm, tn, splits);
+    else
+        hipLaunchKernelGGL((gemm_f16_kernel<QT, EPI, MT, NW, SPLIT, false>), dim3(total), dim3(256), 0,
+                           s, a.W, (const void *)a.X, a.Y, a.n, a.k, a.T, tm, tn, splits);
     return hipGetLastError();
 }
 
 template <int QT, int EPI, bool SPLIT>
-hipError_t launch_split(const GemmArgs &a, TileChoice tc, hipStream_t s) {
+hipError_t launch_split(const GemmArgs &a, TileChoice tc, const uint16_t *xh, hipStream_t s) {
     switch (tc.cfg) {
-    case 0: return launch_cfg<QT, EPI, 256, 192, SPLIT>(a, tc.splits, s);
-    case 1: return launch_cfg<QT, EPI, 256, 128, SPLIT>(a, tc.splits, s);
-    case 2: return launch_cfg<QT, EPI, 128, 128, SPLIT>(a, tc.splits, s);
-    default: return launch_cfg<QT, EPI, 64, 64, SPLIT>(a, tc.splits, s);
+    case 0: return launch_cfg<QT, EPI, 256, 192, SPLIT>(a, tc.splits, xh, s);
+    case 1: return launch_cfg<QT, EPI, 256, 128, SPLIT>(a, tc.splits, xh, s);
+    case 2: return launch_cfg<QT, EPI, 128, 128, SPLIT>(a, tc.splits, xh, s);
+    default: return launch_cfg<QT, EPI, 64, 64, SPLIT>(a, tc.splits, xh, s);
     }
 }
 
 template <int QT, int EPI>
-hipError_t launch_epi(const GemmArgs &a, hipStream_t s) {
+hipError_t launch_epi(const GemmArgs &a, const uint16_t *xh, hipStream_t s) {
     const TileChoice tc = choose_tiles(a);
     if constexpr (EPI == EPI_SWIGLU) {
-        return launch_split<QT, EPI, false>(a, TileChoice{tc.cfg, 1}, s);
+        return launch_split<QT, EPI, false>(a, TileChoice{tc.cfg, 1}, xh, s);
     } else {
-        if (tc.splits == 1) return launch_split<QT, EPI, false>(a, tc, s);
+        if (tc.splits == 1) return launch_split<QT, EPI, false>(a, tc, xh, s);
         if constexpr (EPI == EPI_PLAIN) {
             const int count = a.T * a.n;
             hipLaunchKernelGGL(zero_fill_kernel, dim3((count + 255) / 256), dim3(256), 0, s, a.Y, count);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
-        return launch_split<QT, EPI, true>(a, tc, s);
+        return launch_split<QT, EPI, true>(a, tc, xh, s);
     }
 }
 
 template <int QT>
-hipError_t launch_q(const GemmArgs &a, hipStream_t s) {
+hipError_t launch_q(const GemmArgs &a, const uint16_t *xh, hipStream_t s) {
     switch (a.epilogue) {
-    case EPI_PLAIN: return launch_epi<QT, EPI_PLAIN>(a, s);
-    case EPI_RESIDUAL: return launch_epi<QT, EPI_RESIDUAL>(a, s);
-    default: return launch_epi<QT, EPI_SWIGLU>(a, s);
+    case EPI_PLAIN: return launch_epi<QT, EPI_PLAIN>(a, xh, s);
+    case EPI_RESIDUAL: return launch_epi<QT, EPI_RESIDUAL>(a, xh, s);
+    default: return launch_epi<QT, EPI_SWIGLU>(a, xh, s);
     }
+}
+
+// X [T][k] f32 -> fp16 (RNE) in the k order the GEMM's A fragments take: for
+// Q4_0 the order 0, 2, 1, 3 within each group of four, natural for Q8_0. One
+// thread writes 8 halves (16 bytes).
+template <int QT>
+__global__ __launch_bounds__(256) void x_to_f16_kernel(const float *__restrict__ X,
+                                                       uint16_t *__restrict__ Xh, int count8) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= count8) return;
+    const f4_t a = reinterpret_cast<const f4_t *>(X)[2 * i];
+    const f4_t b = reinterpret_cast<const f4_t *>(X)[2 * i + 1];
+    const u2_t pa = x_pack<QT>(a), pb = x_pack<QT>(b);
+    reinterpret_cast<u4_t *>(Xh)[i] = u4_t{pa[0], pa[1], pb[0], pb[1]};
 }
 
 }  // namespace
 
+hipError_t launch_gemm_f16_ws(const GemmArgs &a, void *workspace, hipStream_t s) {
+    uint16_t *xh = static_cast<uint16_t *>(workspace);
+    const int count8 = a.T * (a.k / 8);
+    if (a.qtype == Q4_0)
+        hipLaunchKernelGGL(x_to_f16_kernel<Q4_0>, dim3((count8 + 255) / 256), dim3(256), 0, s, a.X, xh, count8);
+    else
+        hipLaunchKernelGGL(x_to_f16_kernel<Q8_0>, dim3((count8 + 255) / 256), dim3(256), 0, s, a.X, xh, count8);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return a.qtype == Q4_0 ? launch_q<Q4_0>(a, xh, s) : launch_q<Q8_0>(a, xh, s);
+}
+
 hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t s) {
-    return a.qtype == Q4_0 ? launch_q<Q4_0>(a, s) : launch_q<Q8_0>(a, s);
+    return a.qtype == Q4_0 ? launch_q<Q4_0>(a, nullptr, s) : launch_q<Q8_0>(a, nullptr, s);
 }
 
 }  // namespace pf

@@ -23,6 +23,10 @@ struct GemmArgs {
 hipError_t launch_gemm_f32(const GemmArgs &a, hipStream_t s);
 // Tiled matrix-core GEMM, f16 leg (fp16 MFMA, fp32 accumulation).
 hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t s);
+// The same with a caller workspace: X is converted to fp16 once into it (in the
+// order the A fragments take), then the GEMM streams fp16 X. The workspace holds
+// T * k halves.
+hipError_t launch_gemm_f16_ws(const GemmArgs &a, void *workspace, hipStream_t s);
 // Small-T GEMV (T <= 8), f32 arithmetic.
 hipError_t launch_gemv(const GemmArgs &a, hipStream_t s);
 // Block decode to f32 / binary16.

@@ -17,8 +17,10 @@ def to_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def run_gpu(pf, qtype, W, n, k, X, epi, leg, R=None, path=0, stream=None, Wd=None, Xd=None):
-    """Y on the device via pf.gemm; returns the numpy result."""
+def run_gpu(pf, qtype, W, n, k, X, epi, leg, R=None, path=0, stream=None, Wd=None, Xd=None,
+            workspace=False):
+    """Y on the device via pf.gemm (or pf.gemm_ws with a NaN-filled workspace of
+    exactly the size it asks for, when workspace is True); returns the numpy result."""
     import torch
     T = X.shape[0]
     Wd = to_dev(W) if Wd is None else Wd
@@ -27,7 +29,13 @@ def run_gpu(pf, qtype, W, n, k, X, epi, leg, R=None, path=0, stream=None, Wd=Non
         Yd = to_dev(R.astype(np.float32))
     else:
         Yd = torch.full((T, n), float("nan"), dtype=torch.float32, device="cuda")
-    pf.gemm(qtype, Wd, n, k, Xd, Yd, epi, leg, stream=stream, path=path)
+    if workspace:
+        need = pf.workspace_bytes(qtype, n, k, T, epi, leg)
+        assert need >= 0
+        ws = torch.full((max(need, 16) // 2,), -1, dtype=torch.int16, device="cuda") if need else None
+        pf.gemm_ws(qtype, Wd, n, k, Xd, Yd, epi, leg, ws, stream=stream)
+    else:
+        pf.gemm(qtype, Wd, n, k, Xd, Yd, epi, leg, stream=stream, path=path)
     torch.cuda.synchronize()
     return Yd.cpu().numpy()
 

@@ -43,7 +43,7 @@ def test_header_enums_match_binding():
     for name in ["PF_Q4_0", "PF_Q8_0", "PF_PLAIN", "PF_RESIDUAL", "PF_GATE_UP_SWIGLU",
                  "PF_LEG_F32", "PF_LEG_F16", "PF_PATH_AUTO", "PF_PATH_GEMM", "PF_PATH_GEMV",
                  "PF_OK", "PF_E_NULL", "PF_E_QTYPE", "PF_E_EPILOGUE", "PF_E_LEG", "PF_E_SHAPE",
-                 "PF_E_ALIGN", "PF_E_ALIAS", "PF_E_LAUNCH", "PF_E_PATH"]:
+                 "PF_E_ALIGN", "PF_E_ALIAS", "PF_E_LAUNCH", "PF_E_PATH", "PF_E_WORKSPACE"]:
         m = re.search(r"\b%s\s*=\s*(\d+)" % name, src)
         assert m and int(m.group(1)) == getattr(pf, name), name
     assert int(re.search(r"#define PF_GEMV_MAX_T (\d+)", src).group(1)) == pf.PF_GEMV_MAX_T
@@ -59,7 +59,7 @@ def test_weight_bytes(lib):
 
 
 def test_strerror(lib):
-    for code in range(10):
+    for code in range(11):
         s = lib.pf_strerror(code).decode()
         assert s.startswith("PF_"), s
     assert lib.pf_strerror(99).decode() == "unknown status"
@@ -114,6 +114,46 @@ def test_gemm_argument_checks(lib):
     P = ctypes.c_void_p
     assert lib.pf_gemm(0, P(W), 64, 100, P(X), 16, P(Y), 0, 0, None) == pf.PF_E_SHAPE
     assert lib.pf_gemm(0, P(W), 64, 256, P(X), 0, P(Y), 0, 0, None) == pf.PF_OK
+
+
+def test_workspace_bytes(lib):
+    wb = lib.pf_workspace_bytes
+    # the f16 leg's matrix-core GEMM takes T * k halves; the GEMV and the f32 leg none
+    assert wb(pf.PF_Q4_0, 12288, 4096, 512, pf.PF_GATE_UP_SWIGLU, pf.PF_LEG_F16) == 512 * 4096 * 2
+    assert wb(pf.PF_Q8_0, 4096, 12288, 9, pf.PF_RESIDUAL, pf.PF_LEG_F16) == 9 * 12288 * 2
+    assert wb(pf.PF_Q4_0, 4096, 4096, 512, pf.PF_PLAIN, pf.PF_LEG_F32) == 0
+    assert wb(pf.PF_Q4_0, 4096, 4096, 8, pf.PF_PLAIN, pf.PF_LEG_F16) == 0
+    assert wb(pf.PF_Q4_0, 4096, 4096, 0, pf.PF_PLAIN, pf.PF_LEG_F16) == 0
+    assert wb(3, 64, 256, 16, 0, 1) == -pf.PF_E_QTYPE
+    assert wb(0, 64, 300, 16, 0, 1) == -pf.PF_E_SHAPE
+    assert wb(0, 64, 256, 16, 0, 5) == -pf.PF_E_LEG
+
+
+def test_gemm_ws_argument_checks(lib):
+    P = ctypes.c_void_p
+    W, X, Y, WS = FAKE, FAKE + (1 << 32), FAKE + (2 << 32), FAKE + (3 << 32)
+    n, k, T = 64, 256, 16
+    need = T * k * 2
+
+    def g(ws=WS, ws_bytes=need, leg=pf.PF_LEG_F16, **kw):
+        a = dict(qtype=0, W=W, n=n, k=k, X=X, T=T, Y=Y, epi=0)
+        a.update(kw)
+        return lib.pf_gemm_ws(a["qtype"], P(a["W"]), a["n"], a["k"], P(a["X"]), a["T"], P(a["Y"]),
+                              a["epi"], leg, P(ws), ws_bytes, None)
+
+    assert g(ws=0) == pf.PF_E_WORKSPACE
+    assert g(ws_bytes=need - 1) == pf.PF_E_WORKSPACE
+    assert g(ws=WS + 8) == pf.PF_E_WORKSPACE
+    assert g(ws=X + 16) == pf.PF_E_WORKSPACE
+    assert g(ws=Y) == pf.PF_E_WORKSPACE
+    assert g(ws=W + 16) == pf.PF_E_WORKSPACE
+    assert g(ws=X - need + 16) == pf.PF_E_WORKSPACE
+    # the ordinary checks come first and are the same as pf_gemm's
+    assert g(qtype=9) == pf.PF_E_QTYPE
+    assert g(k=100) == pf.PF_E_SHAPE
+    assert g(X=0) == pf.PF_E_NULL
+    assert g(Y=X) == pf.PF_E_ALIAS
+    assert g(T=0, ws=0, ws_bytes=0) == pf.PF_OK
 
 
 def test_dequant_argument_checks(lib):

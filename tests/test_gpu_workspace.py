@@ -1,0 +1,113 @@
+"""GPU parity of pf_gemm_ws (X rounded to binary16 once, into a caller workspace)
+against the fp64 CPU oracle, to the same bars as pf_gemm, and against pf_gemm itself:
+both feed the matrix cores the same fp16 operands, so wherever pf_gemm does not
+split k (the SwiGLU epilogue never does) the two agree bit for bit.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from quantized_weight_prefill_gguf_amd import synth
+from tests import parity
+from tests.test_gpu_parity import acts, weight
+
+pytestmark = pytest.mark.gpu
+
+Q4_0, Q8_0 = synth.Q4_0, synth.Q8_0
+PLAIN, RESIDUAL, SWIGLU = oracle.PLAIN, oracle.RESIDUAL, oracle.GATE_UP_SWIGLU
+F32, F16 = 0, 1
+
+
+def run_ws_and_check(gpu, qtype, n, k, T, epi, leg, wid, samples=None, row_scale=False, X=None,
+                     bitwise_vs_gemm=False):
+    W = weight(qtype, n, k, epi == SWIGLU, wid)
+    if X is None:
+        X = acts(T, k, wid, row_scale=row_scale)
+    R = acts(T, n, wid, synth.TENSOR_R) if epi == RESIDUAL else None
+    print("case ws qtype=%d n=%d k=%d T=%d epi=%d leg=%d wid=%d" % (qtype, n, k, T, epi, leg, wid),
+          flush=True)
+    Y = parity.run_gpu(gpu, qtype, W, n, k, X, epi, leg, R=R, workspace=True)
+    ok, err = parity.check(qtype, W, n, k, X, Y, epi, leg, R=R, samples=samples)
+    assert ok, "parity failed: metric %.3e" % err
+    if bitwise_vs_gemm:
+        Y0 = parity.run_gpu(gpu, qtype, W, n, k, X, epi, leg, R=R)
+        assert np.array_equal(Y.view(np.uint32), Y0.view(np.uint32))
+    return Y
+
+
+@pytest.mark.parametrize("epi", [PLAIN, RESIDUAL, SWIGLU])
+@pytest.mark.parametrize("qtype", [Q4_0, Q8_0])
+@pytest.mark.parametrize("T", [9, 12, 33, 100, 300])
+@pytest.mark.parametrize("n,k", [(17, 256), (200, 768), (640, 2048)])
+def test_ws_small_ragged(gpu, qtype, epi, T, n, k):
+    run_ws_and_check(gpu, qtype, n, k, T, epi, F16, wid=60 + n + T,
+                     bitwise_vs_gemm=(epi == SWIGLU))
+
+
+@pytest.mark.parametrize("epi", [PLAIN, RESIDUAL, SWIGLU])
+@pytest.mark.parametrize("T", [1, 8, 40])
+def test_ws_without_workspace_need(gpu, epi, T):
+    """The f32 leg and the GEMV need no workspace: pf_gemm_ws takes NULL there."""
+    for leg in (F32, F16):
+        if leg == F16 and T > 8:
+            continue
+        assert gpu.workspace_bytes(Q4_0, 96, 512, T, epi, leg) == 0
+        run_ws_and_check(gpu, Q4_0, 96, 512, T, epi, leg, wid=70 + T)
+
+
+@pytest.mark.parametrize("qtype", [Q4_0, Q8_0])
+def test_ws_workspace_is_scratch_only(gpu, qtype):
+    """Bytes past the requested size are never written; a reused workspace (second
+    call smaller, other k) gives each call its own correct result."""
+    import torch
+    n, T1, k1, T2, k2 = 384, 130, 1024, 37, 512
+    need1 = gpu.workspace_bytes(qtype, n, k1, T1, SWIGLU, F16)
+    need2 = gpu.workspace_bytes(qtype, n, k2, T2, PLAIN, F16)
+    assert need1 == T1 * k1 * 2 and need2 == T2 * k2 * 2
+    guard = 4096
+    buf = torch.full(((need1 + 2 * guard) // 2,), 0x5A5A, dtype=torch.int16, device="cuda")
+    ws = buf[guard // 2: (guard + need1) // 2]
+    outs = []
+    for (k, T, epi, wid) in [(k1, T1, SWIGLU, 80), (k2, T2, PLAIN, 81)]:
+        W = weight(qtype, n, k, epi == SWIGLU, wid)
+        X = acts(T, k, wid)
+        Y = torch.full((T, n), float("nan"), dtype=torch.float32, device="cuda")
+        gpu.gemm_ws(qtype, parity.to_dev(W), n, k, parity.to_dev(X), Y, epi, F16, ws)
+        torch.cuda.synchronize()
+        outs.append((W, k, T, epi, X, Y.cpu().numpy()))
+    b = buf.cpu().numpy()
+    assert np.all(b[:guard // 2] == 0x5A5A) and np.all(b[(guard + need1) // 2:] == 0x5A5A)
+    for W, k, T, epi, X, Y in outs:
+        ok, err = parity.check(qtype, W, n, k, X, Y, epi, F16)
+        assert ok, err
+
+
+def test_ws_refuses_small_workspace(gpu):
+    import torch
+    n, k, T = 64, 256, 16
+    W = parity.to_dev(weight(Q4_0, n, k, False, 82))
+    X = parity.to_dev(acts(T, k, 82))
+    Y = torch.empty((T, n), dtype=torch.float32, device="cuda")
+    ws = torch.empty((T * k - 8,), dtype=torch.int16, device="cuda")
+    with pytest.raises(gpu.PfError) as e:
+        gpu.gemm_ws(Q4_0, W, n, k, X, Y, PLAIN, F16, ws)
+    assert e.value.status == gpu.PF_E_WORKSPACE
+    with pytest.raises(gpu.PfError):
+        gpu.gemm_ws(Q4_0, W, n, k, X, Y, PLAIN, F16, None)
+
+
+def test_ws_workload3_ffn_chain(gpu):
+    """gate/up SwiGLU (Q4_0, T = 512) then the Q8_0 down projection with residual on
+    that output, both through the workspace path; gate/up also bit for bit against
+    pf_gemm."""
+    Y = run_ws_and_check(gpu, Q4_0, 12288, 4096, 512, SWIGLU, F16, wid=3, samples=8192,
+                         bitwise_vs_gemm=True)
+    run_ws_and_check(gpu, Q8_0, 4096, 12288, 512, RESIDUAL, F16, wid=3, samples=8192, X=Y)
+
+
+def test_ws_workload4_long_chunk(gpu):
+    Y = run_ws_and_check(gpu, Q4_0, 12288, 4096, 2048, SWIGLU, F16, wid=4, samples=8192,
+                         row_scale=True)
+    run_ws_and_check(gpu, Q8_0, 4096, 12288, 2048, RESIDUAL, F16, wid=4, samples=8192, X=Y)
+    run_ws_and_check(gpu, Q4_0, 4096, 4096, 2048, PLAIN, F16, wid=4, samples=8192,
+                     row_scale=True)
