@@ -137,6 +137,22 @@ def load_traffic(workload, label):
     return entry.get("bytes_per_launch")
 
 
+def copy_calibration(torch, mib=256, reps=3):
+    """Plain device-to-device copies of `mib` MiB, each between buffers no cache
+    holds (fresh pairs, > the 256 MB Infinity Cache apart). A counter pass over this
+    run reads the known bytes, which scales the same counters for the GEMM."""
+    n = mib * (1 << 20) // 4
+    bufs = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(2 * reps)]
+    for b in bufs:
+        b.fill_(1.0)
+    torch.cuda.synchronize()
+    for r in range(reps):
+        bufs[2 * r + 1].copy_(bufs[2 * r])
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "copies": reps, "bytes_read_per_copy": n * 4,
+                      "bytes_written_per_copy": n * 4}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -148,6 +164,9 @@ def main():
                     help="call pf_gemm (X rounded inside the GEMM) instead of pf_gemm_ws")
     ap.add_argument("--rotate-mb", type=float, default=640.0,
                     help="minimum total bytes of rotated weight copies")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run plain device copies of a known size (the reference reading "
+                         "for the FETCH_SIZE / WRITE_SIZE counters) and print them")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -157,6 +176,11 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+
     import quantized_weight_prefill_gguf_amd as pf
     from quantized_weight_prefill_gguf_amd import synth
 
