@@ -44,12 +44,21 @@ Q4_0, Q8_0 = 0, 1
 PLAIN, RESIDUAL, SWIGLU = 0, 1, 2
 BLOCK = {Q4_0: 18, Q8_0: 34}
 
-KERNEL_SOURCES = ["pf_gemm_f16.hip", "pf_gemm_f32.hip", "pf_gemv.hip", "pf_device.h"]
+# Sources whose change invalidates stored counter readings, per kernel family.
+KERNEL_SOURCES = {
+    "gemm_f16": ["pf_gemm_f16.hip", "pf_device.h"],
+    "gemm_f32": ["pf_gemm_f32.hip", "pf_device.h"],
+    "gemv": ["pf_gemv.hip", "pf_device.h"],
+}
 
 
-def kernel_source_sha():
+def kernel_family(T, leg):
+    return "gemv" if T <= 8 else ("gemm_f16" if leg == 1 else "gemm_f32")
+
+
+def kernel_source_sha(family):
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in KERNEL_SOURCES[family]:
         with open(os.path.join(ROOT, "quantized_weight_prefill_gguf_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -124,15 +133,18 @@ def cpu_baseline(T, ops, inputs, target_s=12.0):
     }
 
 
-def load_traffic(workload, label):
+def load_traffic(workload, label, family):
+    """HBM bytes per launch of the op from the stored counter passes (FETCH_SIZE and
+    WRITE_SIZE, scaled by the copy calibration), or None when none were taken for
+    this workload or the kernel sources changed since."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    entry = rec.get(workload, {}).get(label)
-    if not entry or entry.get("kernel_source_sha") != kernel_source_sha():
+    entry = rec.get("workloads", {}).get(workload, {}).get(label)
+    if not entry or entry.get("kernel_source_sha") != kernel_source_sha(family):
         return None
     return entry.get("bytes_per_launch")
 
@@ -256,16 +268,17 @@ def main():
     dom = int(np.argmax(kern_ms))
     dop = ops[dom]
     is_gemv = T <= 8
+    family = kernel_family(T, leg)
     if is_gemv:
         wb = op_rows(dop) * (dop[3] // 32) * BLOCK[dop[1]]
         achieved = wb / (kern_ms[dom] * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK["hbm_gbs"], "unit": "GB/s",
-                    "frac": achieved / PEAK["hbm_gbs"], "traffic": load_traffic(args.workload, dop[0])}
+                    "frac": achieved / PEAK["hbm_gbs"], "traffic": load_traffic(args.workload, dop[0], family)}
     else:
         achieved = op_flops(dop, T) / (kern_ms[dom] * 1e-3) / 1e12
         peak = PEAK["fp16_mfma_tflops"] if leg == 1 else PEAK["fp32_mfma_tflops"]
         roofline = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                    "frac": achieved / peak, "traffic": load_traffic(args.workload, dop[0])}
+                    "frac": achieved / peak, "traffic": load_traffic(args.workload, dop[0], family)}
     roofline["kernel"] = dop[0]
     roofline["avg_launch_us"] = kern_ms[dom] * 1e3
 
