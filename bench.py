@@ -81,6 +81,8 @@ def workloads():
         "plain_q4_0_4096_T512_f16": (512, 1, [("plain_q4_0", Q4_0, HIDDEN, HIDDEN, PLAIN, "x", "out")]),
         "gemv_q4_0_12288x4096_T1": (1, 0, [("gemv_q4_0", Q4_0, INTER, HIDDEN, PLAIN, "x", "out")]),
         "gemv_q8_0_4096x12288_T1": (1, 0, [("gemv_q8_0", Q8_0, HIDDEN, INTER, PLAIN, "x12288", "out")]),
+        "gemv_q4_0_12288x4096_T8": (8, 0, [("gemv_q4_0", Q4_0, INTER, HIDDEN, PLAIN, "x", "out")]),
+        "gemv_q8_0_4096x12288_T8": (8, 0, [("gemv_q8_0", Q8_0, HIDDEN, INTER, PLAIN, "x12288", "out")]),
     }
 
 
