@@ -125,13 +125,20 @@ def cpu_baseline(T, ops, inputs, target_s=12.0):
     if dt < target_s / 3 and ts < T:
         ts = int(min(T, max(ts + 1, ts * target_s / max(dt, 1e-3))))
         flops, dt = run(ts)
+    reps = 1
+    # The whole step is shorter than the target: repeat it (each run is the same work).
+    while ts == T and dt < target_s * 0.8 and reps < 64:
+        f2, d2 = run(ts)
+        flops += f2
+        dt += d2
+        reps += 1
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": "the step's %d ops on the first %d of %d token rows (%.1f GFLOP, %.1f s)"
-                  % (len(ops), ts, T, flops / 1e9, dt),
+        "sample": "the step's %d ops on the first %d of %d token rows, %d run(s) (%.1f GFLOP, %.1f s)"
+                  % (len(ops), ts, T, reps, flops / 1e9, dt),
     }
 
 
