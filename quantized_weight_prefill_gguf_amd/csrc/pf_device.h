@@ -106,6 +106,18 @@ __device__ __forceinline__ float q8_byte_f32(uint32_t w, int byte, float d) {
     return d * (float)(int)(int8_t)(uint8_t)(w >> (8 * byte));
 }
 
+// Orders one wave's LDS accesses before the call against those after it, for
+// communication between the lanes of that wave through LDS. The hardware already
+// completes one wave's LDS operations in order, so nothing is emitted; the fences
+// keep the compiler from moving accesses across (without them, a store whose
+// address no load of the same thread can alias may be sunk past another lane's
+// read of it).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // ---------------------------------------------------------------------------
 // Epilogue helpers. silu(g) = g / (1 + e^-g), evaluated in f32.
 // ---------------------------------------------------------------------------

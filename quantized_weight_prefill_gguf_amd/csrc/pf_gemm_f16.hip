@@ -60,18 +60,6 @@ template <int QT> __device__ __forceinline__ u2_t x_pack(f4_t v) {
                     h2_bits(h2_t{(_Float16)v[2], (_Float16)v[3]})};
 }
 
-// The 32-bit window starting at byte `addr` of LDS buffer `b`; (addr & 3) == SH
-// is a compile-time constant.
-template <int SH>
-__device__ __forceinline__ uint32_t lds_word(const uint8_t *b, int addr) {
-    if constexpr (SH == 0) {
-        return *reinterpret_cast<const uint32_t *>(b + addr);
-    } else {
-        const uint32_t *al = reinterpret_cast<const uint32_t *>(b + addr - SH);
-        return __builtin_amdgcn_alignbyte(al[1], al[0], SH);
-    }
-}
-
 }  // namespace
 
 // Global weight row of local tile row lr, or -1 past the weight.
@@ -177,18 +165,33 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
         // rows (tid >> 3) + 32 i share (row >> 2) & 3
         xdst = (tid >> 3) * 32 + ((((tid & 7) >> 1) ^ ((tid >> 5) & 3)) << 3) + 4 * (tid & 1);
     }
-    // Weight staging: thread t < NW copies local row t. Slice s of a chunk is the
-    // row's 16-byte pieces p == s (mod 8); offsets are a per-thread base plus
-    // compile-time immediates.
-    const bool wrow_thread = tid < NW;
+    // Weight staging. Slice S of a chunk is its rows S RS .. S RS + RS - 1 (RS = NW
+    // / 8), whole: RS * U4 16-byte pieces, which the threads take in order, piece
+    // f = tid + 256 i being piece f % U4 of slice row f / U4. Consecutive lanes thus
+    // read consecutive bytes of a row. Since RS * U4 is the same for every slice,
+    // a thread's (row in slice, piece) is fixed; only the weight row of slice row
+    // rr, i.e. its global offset, depends on S.
+    constexpr int RS = NW / 8;
+    constexpr int SP = RS * U4;                      // pieces per slice
+    constexpr int NPT = (SP + 255) / 256;            // pieces per thread per slice
+    uint32_t wsrc[8][NPT];                           // [slice][piece]: row offset + piece
+    int wdst[NPT];                                   // LDS offset within slice 0
+    bool wvalid[NPT];
     const uint8_t *wbase = W + (size_t)c_begin * WROW;
-    uint32_t wsrc_row;
-    {
-        int gr = f16_weight_row<EPI, NW>(tn, wrow_thread ? tid : 0, n);
-        gr = gr < 0 ? 0 : gr;
-        wsrc_row = (uint32_t)gr * row_bytes;
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+        const int f = tid + 256 * i;
+        wvalid[i] = f < SP;
+        const int ff = wvalid[i] ? f : 0;
+        const int rr = ff / U4, pp = ff % U4;
+        wdst[i] = rr * WROW + 16 * pp;
+#pragma unroll
+        for (int S = 0; S < 8; ++S) {
+            int gr = f16_weight_row<EPI, NW>(tn, S * RS + rr, n);
+            gr = gr < 0 ? 0 : gr;
+            wsrc[S][i] = (uint32_t)gr * row_bytes + 16 * pp;
+        }
     }
-    const int wdst_row = (wrow_thread ? tid : 0) * WROW;
 
     // LDS offsets of this lane's B rows (column c of tile j: bbase + j 32 WROW) and
     // A fragments.
@@ -205,10 +208,13 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
 
     h8_t afr[2][IT][2];   // A fragments [step parity][tile][MFMA half]
     h8_t bfr[2][JT][2];   // decoded B fragments [step parity][tile][MFMA half]
+    // Staging loads run PD steps ahead of their LDS writes (a ring of PD register
+    // sets): under a full weight stream the HBM latency exceeds two steps, and the
+    // wait counters complete loads in order.
+    constexpr int PD = 4;
     f4_t xr[XF4];         // f32 X for the staging write of the next step
-    u4_t xh[2][XH4];      // fp16 X for the staging writes of the next two steps
-    constexpr int MAXP = (U4 + 7) / 8;  // pieces in the largest slice (2 / 3)
-    u4_t wr[2][MAXP];     // weight slices for the writes of the next two steps
+    u4_t xh[PD][XH4];     // fp16 X for the staging writes of the next PD steps
+    u4_t wr[PD][NPT];     // weight slices for the writes of the next PD steps
 
     auto load_a = [&](int xb, h8_t (&dst)[IT][2]) __attribute__((always_inline)) {
 #pragma unroll
@@ -217,32 +223,56 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
             for (int s = 0; s < 2; ++s)
                 dst[i][s] = *reinterpret_cast<const h8_t *>(&xs[xb][aoff[s] + i * 32 * 32]);
     };
-    // Read this lane's raw bytes of block `blk` (compile-time) and decode them.
-    auto load_decode_b = [&](const uint8_t *wb, auto blk_c, h8_t (&dst)[JT][2])
+    // This lane's raw bytes of block `blk` (compile-time) for its JT B columns: the
+    // scale and the aligned dwords that hold its qs words (NRAW of them; when the
+    // qs start 2 bytes into a dword, a word straddles two dwords).
+    constexpr int NRAW = (QT == Q4_0) ? 3 : 6;
+    auto read_b = [&](const uint8_t *wb, auto blk_c, uint32_t (&d16)[JT], uint32_t (&raw)[JT][NRAW])
         __attribute__((always_inline)) {
         constexpr int blk = decltype(blk_c)::value;
         constexpr int SH = (blk * BB + 2) & 3;
-        uint32_t d16[JT], q[JT][NW32];
 #pragma unroll
         for (int j = 0; j < JT; ++j) {
             const int base = bbase + j * 32 * WROW + blk * BB;
             d16[j] = *reinterpret_cast<const uint16_t *>(wb + base);
+            const uint32_t *al = reinterpret_cast<const uint32_t *>(wb + base + 2 + 8 * h - SH);
+            if constexpr (SH == 0) {
 #pragma unroll
-            for (int w = 0; w < NW32; ++w)
-                q[j][w] = lds_word<SH>(wb, base + 2 + 8 * h + 4 * (w & 1) + 16 * (w >> 1));
+                for (int w = 0; w < NW32; ++w) raw[j][w] = al[(w & 1) + 4 * (w >> 1)];
+            } else {
+#pragma unroll
+                for (int g = 0; g < NW32 / 2; ++g)
+#pragma unroll
+                    for (int e = 0; e < 3; ++e) raw[j][3 * g + e] = al[4 * g + e];
+            }
         }
+    };
+    // Decode raw bytes read by read_b for block `blk` into the B fragments.
+    auto decode_b = [&](auto blk_c, const uint32_t (&d16)[JT], const uint32_t (&raw)[JT][NRAW],
+                        h8_t (&dst)[JT][2]) __attribute__((always_inline)) {
+        constexpr int blk = decltype(blk_c)::value;
+        constexpr int SH = (blk * BB + 2) & 3;
 #pragma unroll
         for (int j = 0; j < JT; ++j) {
+            uint32_t q[NW32];
+#pragma unroll
+            for (int w = 0; w < NW32; ++w) {
+                if constexpr (SH == 0)
+                    q[w] = raw[j][w];
+                else
+                    q[w] = __builtin_amdgcn_alignbyte(raw[j][3 * (w >> 1) + (w & 1) + 1],
+                                                      raw[j][3 * (w >> 1) + (w & 1)], SH);
+            }
             const h2_t d2 = as_h2(d16[j] | (d16[j] << 16));
             uint32_t p[8];
             if constexpr (QT == Q4_0) {
-                q4_word_decode(q[j][0], d2, p[0], p[1], p[4], p[5]);
-                q4_word_decode(q[j][1], d2, p[2], p[3], p[6], p[7]);
+                q4_word_decode(q[0], d2, p[0], p[1], p[4], p[5]);
+                q4_word_decode(q[1], d2, p[2], p[3], p[6], p[7]);
             } else {
-                q8_word_to_h4(q[j][0], d2, p + 0);
-                q8_word_to_h4(q[j][1], d2, p + 2);
-                q8_word_to_h4(q[j][2], d2, p + 4);
-                q8_word_to_h4(q[j][3], d2, p + 6);
+                q8_word_to_h4(q[0], d2, p + 0);
+                q8_word_to_h4(q[1], d2, p + 2);
+                q8_word_to_h4(q[2], d2, p + 4);
+                q8_word_to_h4(q[3], d2, p + 6);
             }
             dst[j][0] = __builtin_bit_cast(h8_t, u4_t{p[0], p[1], p[2], p[3]});
             dst[j][1] = __builtin_bit_cast(h8_t, u4_t{p[4], p[5], p[6], p[7]});
@@ -272,27 +302,25 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
     };
 
     // Slice S (compile-time) of chunk `chunk`: load to registers / store to LDS.
-    auto fetch_slice = [&](int chunk, auto s_c, u4_t (&dst)[MAXP]) __attribute__((always_inline)) {
+    auto fetch_slice = [&](int chunk, auto s_c, u4_t (&dst)[NPT]) __attribute__((always_inline)) {
         constexpr int S = decltype(s_c)::value;
-        const uint8_t *src = wbase + (size_t)min(chunk, nch - 1) * WROW + wsrc_row;
+        const uint8_t *src = wbase + (size_t)min(chunk, nch - 1) * WROW;
 #pragma unroll
-        for (int p = 0; p < MAXP; ++p)
-            if (S + 8 * p < U4) dst[p] = *reinterpret_cast<const u4_t *>(src + 16 * (S + 8 * p));
+        for (int i = 0; i < NPT; ++i) dst[i] = *reinterpret_cast<const u4_t *>(src + wsrc[S][i]);
     };
-    auto store_slice = [&](uint8_t *buf, auto s_c, const u4_t (&src)[MAXP]) __attribute__((always_inline)) {
+    auto store_slice = [&](uint8_t *buf, auto s_c, const u4_t (&src)[NPT]) __attribute__((always_inline)) {
         constexpr int S = decltype(s_c)::value;
-        if (wrow_thread) {
 #pragma unroll
-            for (int p = 0; p < MAXP; ++p)
-                if (S + 8 * p < U4) *reinterpret_cast<u4_t *>(buf + wdst_row + 16 * (S + 8 * p)) = src[p];
-        }
+        for (int i = 0; i < NPT; ++i)
+            if (wvalid[i]) *reinterpret_cast<u4_t *>(buf + S * RS * WROW + wdst[i]) = src[i];
     };
 
-    // ---- prologue. LDS: chunk 0, slice 0 of chunk 1, X(0), X(1). Registers: X(2),
-    // the slices written by steps 0 and 1 (chunk 1 slices 1, 2), and the A and
-    // decoded B fragments of step 0.
+    // ---- prologue. LDS: chunk 0, slices 0 and 1 of chunk 1, X(0), X(1).
+    // Registers: X(2) (X(2) .. X(PD+1) for fp16 X), the slices written by steps
+    // 0 .. PD-1 (chunk 1 slices 2 .. PD+1), the raw weight words of steps 0 and 1,
+    // and the A and decoded B fragments of step 0.
     {
-        u4_t tmp[MAXP];
+        u4_t tmp[NPT];
 #define PF_CHUNK0_SLICE(S)                                           \
         fetch_slice(0, std::integral_constant<int, S>{}, tmp);       \
         store_slice(wsm[0], std::integral_constant<int, S>{}, tmp);
@@ -301,16 +329,21 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
 #undef PF_CHUNK0_SLICE
         fetch_slice(1, std::integral_constant<int, 0>{}, tmp);
         if (nch > 1) store_slice(wsm[1], std::integral_constant<int, 0>{}, tmp);
-        fetch_slice(1, std::integral_constant<int, 1>{}, wr[0]);
-        fetch_slice(1, std::integral_constant<int, 2>{}, wr[1]);
+        fetch_slice(1, std::integral_constant<int, 1>{}, tmp);
+        if (nch > 1) store_slice(wsm[1], std::integral_constant<int, 1>{}, tmp);
+        fetch_slice(1, std::integral_constant<int, 2>{}, wr[0]);
+        fetch_slice(1, std::integral_constant<int, 3>{}, wr[1]);
+        fetch_slice(1, std::integral_constant<int, 4>{}, wr[2]);
+        fetch_slice(1, std::integral_constant<int, 5>{}, wr[3]);
+        static_assert(PD == 4, "prologue fills a ring of 4");
     }
     if constexpr (XH) {
         fetch_xh(0, xh[0]);
         store_xh(0, xh[0]);
         fetch_xh(1, xh[1]);
         store_xh(1, xh[1]);
-        fetch_xh(2, xh[0]);
-        fetch_xh(3, xh[1]);
+#pragma unroll
+        for (int j = 0; j < PD; ++j) fetch_xh(2 + j, xh[j]);
     } else {
         fetch_x(0);
         store_x(0);
@@ -319,39 +352,52 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
         fetch_x(2);
     }
     __syncthreads();
+    // raw weight words of steps s and s+1 (rwd/rwq[s & 1]), read two steps ahead
+    uint32_t rwd[2][JT], rwq[2][JT][NRAW];
     load_a(0, afr[0]);
-    load_decode_b(wsm[0], std::integral_constant<int, 0>{}, bfr[0]);
+    read_b(wsm[0], std::integral_constant<int, 0>{}, rwd[0], rwq[0]);
+    read_b(wsm[0], std::integral_constant<int, 1>{}, rwd[1], rwq[1]);
+    decode_b(std::integral_constant<int, 0>{}, rwd[0], rwq[0], bfr[0]);
 
     for (int ch = 0; ch < nch; ++ch) {
-        // Step s = 8 ch + blk. At its start: LDS holds X(s), X(s+1) and every
-        // slice of chunk ch; afr/bfr[P] hold the fragments of step s; xr (or
-        // xh[P]) holds X(s+2); wr[P] the slice this step writes.
+        // Step s = 8 ch + blk. At its start: LDS holds X(s+1) and every slice of
+        // the chunks of steps s+1 and s+2; afr/bfr[P] hold the fragments of step s;
+        // rwd/rwq[P ^ 1] the raw weight words of step s+1; xr (or xh[s % PD]) holds
+        // X(s+2); wr[s % PD] the slice this step writes. Slice u = s + 2 (slice u % 8
+        // of chunk u / 8 + 1) is written at step s, so a chunk is complete two
+        // steps before its first block is used, and a buffer is rewritten only
+        // after the raw reads of its previous chunk are done.
         auto step_body = [&](auto blk_c) __attribute__((always_inline)) {
             constexpr int blk = decltype(blk_c)::value;
             constexpr int P = blk & 1;
-            constexpr int NB = (blk + 1) & 7;            // block of step s+1
+            constexpr int RG = blk % PD;                 // ring slot of this step
+            constexpr int B1 = (blk + 1) & 7;            // block of step s+1
+            constexpr int B2 = (blk + 2) & 7;            // block of step s+2
             const int s = ch * 8 + blk;
-            // (1) staging: X(s+2) -> xs[P] (X(s) was consumed during step s-1), then
-            // fetch X(s+3); slice NB of chunk (s+1)/8 + 1 -> LDS, then fetch the
-            // slice step s+2 writes.
+            // (1) LDS reads first, so that their latency is spent under the MFMAs:
+            // A fragments of step s+1, raw weight words of step s+2.
+            load_a(P ^ 1, afr[P ^ 1]);
+            read_b(wsm[(ch + ((blk + 2) >> 3)) & 1], std::integral_constant<int, B2>{}, rwd[P],
+                   rwq[P]);
+            // (2) staging: X(s+2) -> xs[P] (X(s) was read during step s-1), then
+            // fetch the X that step s+PD writes (s+3 for f32 X, one step ahead);
+            // slice u = s+2 -> LDS, then fetch the slice step s+PD writes.
             if constexpr (XH) {
-                store_xh(P, xh[P]);         // X(s+2), fetched at step s-2
-                fetch_xh(s + 4, xh[P]);
+                store_xh(P, xh[RG]);        // X(s+2), fetched at step s-PD
+                fetch_xh(s + 2 + PD, xh[RG]);
             } else {
                 store_x(P);                 // X(s+2), fetched at step s-1
                 fetch_x(s + 3);
             }
             {
-                const int wc = ch + 1 + (blk == 7 ? 1 : 0);  // chunk receiving the slice
-                if (wc < nch) store_slice(wsm[wc & 1], std::integral_constant<int, NB>{}, wr[P]);
-                // the slice written at step s+2: slice (blk+3)%8 of chunk (s+3)/8 + 1
-                fetch_slice(ch + 1 + ((blk + 3) >> 3), std::integral_constant<int, (blk + 3) & 7>{}, wr[P]);
+                const int wc = ch + 1 + ((blk + 2) >> 3);  // chunk receiving the slice
+                if (wc < nch) store_slice(wsm[wc & 1], std::integral_constant<int, B2>{}, wr[RG]);
+                fetch_slice(ch + 1 + ((blk + PD + 2) >> 3),
+                            std::integral_constant<int, (blk + PD + 2) & 7>{}, wr[RG]);
             }
-            // (2) fragments of step s+1 (its X and chunk are complete in LDS).
-            load_a(P ^ 1, afr[P ^ 1]);
-            load_decode_b(wsm[(ch + (blk == 7 ? 1 : 0)) & 1], std::integral_constant<int, NB>{},
-                          bfr[P ^ 1]);
-            // (3) this step's MFMAs.
+            // (3) this step's MFMAs, with the decode of step s+1's weights (raw
+            // words read during step s-1) spread between them.
+            decode_b(std::integral_constant<int, B1>{}, rwd[P ^ 1], rwq[P ^ 1], bfr[P ^ 1]);
 #pragma unroll
             for (int j = 0; j < JT; ++j)
 #pragma unroll
@@ -359,6 +405,16 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(afr[P][i][0], bfr[P][j][0], acc[i][j], 0, 0, 0);
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(afr[P][i][1], bfr[P][j][1], acc[i][j], 0, 0, 0);
                 }
+            // Instruction order for the scheduler: LDS reads, global loads, LDS
+            // writes, then each MFMA followed by a few VALU instructions.
+            __builtin_amdgcn_sched_group_barrier(0x100, 32, 0);  // DS reads
+            __builtin_amdgcn_sched_group_barrier(0x020, 16, 0);  // VMEM reads
+            __builtin_amdgcn_sched_group_barrier(0x200, 16, 0);  // DS writes
+#pragma unroll
+            for (int q = 0; q < 2 * IT * JT; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+            }
             __syncthreads();
         };
         step_body(std::integral_constant<int, 0>{});
@@ -391,13 +447,16 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
                 // same 16 outputs. The wave writes the tile to its own LDS slot
                 // transposed ([column][row], rows padded to 36 floats), then each lane
                 // reads four rows of one gate column and of its up column and
-                // finishes 2 x 4 outputs. Same-wave LDS accesses complete in order.
+                // finishes 2 x 4 outputs. Wave-scope fences order the lanes' exchange
+                // (and this tile's writes after the previous tile's reads).
                 float *slot = reinterpret_cast<float *>(smem) + e_wave * (32 * 36);
+                wave_lds_sync();
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4)
                     *reinterpret_cast<f4_t *>(slot + e_c * 36 + 8 * g4 + 4 * e_h) =
                         f4_t{acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2],
                              acc[i][j][4 * g4 + 3]};
+                wave_lds_sync();
                 const int cc = e_lane & 15;
                 const int o = tn * (NW / 2) + (tile_col >> 1) + cc;
 #pragma unroll
