@@ -45,6 +45,15 @@ def test_ws_small_ragged(gpu, qtype, epi, T, n, k):
 
 
 @pytest.mark.parametrize("epi", [PLAIN, RESIDUAL, SWIGLU])
+@pytest.mark.parametrize("T", [1024, 1100])
+@pytest.mark.parametrize("n,k", [(17, 256), (300, 768), (1000, 512)])
+def test_ws_long_chunk_tiles(gpu, epi, T, n, k):
+    """T >= 1024 runs the eight-wave 256 x 256 tiling (Q4_0): every output, ragged
+    in T and n, against the full oracle."""
+    run_ws_and_check(gpu, Q4_0, n, k, T, epi, F16, wid=90 + n + T)
+
+
+@pytest.mark.parametrize("epi", [PLAIN, RESIDUAL, SWIGLU])
 @pytest.mark.parametrize("T", [1, 8, 40])
 def test_ws_without_workspace_need(gpu, epi, T):
     """The f32 leg and the GEMV need no workspace: pf_gemm_ws takes NULL there."""
