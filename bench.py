@@ -20,6 +20,7 @@ the CPU oracle timed on a bounded sample of the same workload.
                     [--no-workspace]
 """
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -243,13 +244,33 @@ def main():
     workspace = (torch.empty(((ws_bytes + 15) // 16) * 16, dtype=torch.uint8, device="cuda")
                  if use_ws and ws_bytes > 0 else None)
 
+    # Every call's ctypes arguments are marshalled once, here, so that the timed
+    # loop is C-ABI calls only and a short kernel does not wait on Python.
+    lib = pf.load()
+    P = ctypes.c_void_p
+    hstream = P(stream.cuda_stream)
+    calls = {}
+    for wset in range(copies):
+        for op in ops:
+            label, qtype, n, k, epi, src, dst = op
+            Y = bufs[dst] if dst != "out" else bufs["out"].view(-1)[: T * n].view(T, n)
+            # the checks the binding makes, once
+            pf.gemm_ws(qtype, dev_w[wset][label], n, k, bufs[src], Y, epi, leg, workspace) if use_ws \
+                else pf.gemm(qtype, dev_w[wset][label], n, k, bufs[src], Y, epi, leg)
+            w, x, y = P(dev_w[wset][label].data_ptr()), P(bufs[src].data_ptr()), P(Y.data_ptr())
+            if use_ws:
+                ws = P(workspace.data_ptr()) if workspace is not None else P(0)
+                wsb = workspace.numel() if workspace is not None else 0
+                calls[(op[0], wset)] = (lib.pf_gemm_ws, (qtype, w, n, k, x, T, y, epi, leg, ws, wsb, hstream))
+            else:
+                calls[(op[0], wset)] = (lib.pf_gemm, (qtype, w, n, k, x, T, y, epi, leg, hstream))
+    torch.cuda.synchronize()
+
     def launch(op, wset):
-        label, qtype, n, k, epi, src, dst = op
-        Y = bufs[dst] if dst != "out" else bufs["out"].view(-1)[: T * n].view(T, n)
-        if use_ws:
-            pf.gemm_ws(qtype, dev_w[wset][label], n, k, bufs[src], Y, epi, leg, workspace)
-        else:
-            pf.gemm(qtype, dev_w[wset][label], n, k, bufs[src], Y, epi, leg)
+        fn, argv = calls[(op[0], wset)]
+        st = fn(*argv)
+        if st != 0:
+            raise pf.PfError(st, fn.__name__)
 
     for i in range(args.warmup):
         for op in ops:
@@ -257,23 +278,36 @@ def main():
     torch.cuda.synchronize()
     log("warmup done (%d weight copies)" % copies)
 
-    # ---- timed region: K steps, HIP events around every launch
+    # ---- timed region: K steps. HIP events on the launch stream: around every
+    # launch when a step has several ops; around the whole region when it has one,
+    # so that the launches run back to back as in the kernel trace (a pair of event
+    # markers around each microsecond-scale launch would add their own gaps).
+    single = len(ops) == 1
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in ops] for _ in range(args.steps)]
+           for _ in ops] for _ in range(1 if single else args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
-        for j, op in enumerate(ops):
-            ev[s][j][0].record(stream)
-            launch(op, s % copies)
-            ev[s][j][1].record(stream)
+    if single:
+        ev[0][0][0].record(stream)
+        for s in range(args.steps):
+            launch(ops[0], s % copies)
+        ev[0][0][1].record(stream)
+    else:
+        for s in range(args.steps):
+            for j, op in enumerate(ops):
+                ev[s][j][0].record(stream)
+                launch(op, s % copies)
+                ev[s][j][1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
     step_flops = sum(op_flops(op, T) for op in ops)
     ms_per_step = elapsed * 1e3 / args.steps
-    kern_ms = [float(np.mean([ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(args.steps)]))
-               for j in range(len(ops))]
+    if single:
+        kern_ms = [ev[0][0][0].elapsed_time(ev[0][0][1]) / args.steps]
+    else:
+        kern_ms = [float(np.mean([ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(args.steps)]))
+                   for j in range(len(ops))]
     dom = int(np.argmax(kern_ms))
     dop = ops[dom]
     is_gemv = T <= 8

@@ -5,12 +5,14 @@
 // src/gpu_backend/cuda_q_std_prefill.rs", widened to up to 8 rows (the same page's
 // batch tests step tokens 8 at a time).
 //
-// Work split. A wave owns R weight rows (R outputs, or R/2 outputs with their gate
-// and up rows for the SwiGLU epilogue) over the whole reduction. Its lanes walk
-// the rows' block pairs: lane l takes pairs l, l + 64, ... A pair is 36 bytes
-// (Q4_0) or 68 bytes (Q8_0), 4-byte aligned, so one row segment of 64 pairs is a
-// contiguous 2304 or 4352 bytes read by the whole wave. Each x value a lane loads
-// serves all R rows.
+// Work split. A wave owns a group of R weight rows (R outputs, or R/2 outputs with
+// their gate and up rows for the SwiGLU epilogue) over the whole reduction;
+// persistent workgroups of four waves walk super-groups of four groups. Lanes own
+// block pairs: lane l takes pair l of each 64-pair step (a pair is 36 bytes for
+// Q4_0, 68 for Q8_0). A wave reads its rows' step in coalesced 16-byte chunks into
+// its own LDS region and each lane then takes its pair's dwords from there; x is
+// staged in LDS once per workgroup (lane-transposed, so that a wave's reads are
+// consecutive) and, for one step of few tokens, kept in registers.
 //
 // Arithmetic (f32 throughout, both legs). With u the unsigned code of a weight
 // (the nibble for Q4_0, the int8 byte + 128 for Q8_0) and c its offset (8 or 128),
@@ -465,13 +467,14 @@ hipError_t launch_r(const GemmArgs &a, hipStream_t s) {
     return launch_m<QT, EPI, TT, R, 0>(a, ngroups, s);
 }
 
-// Four rows per group share each x read; two when that would leave too few groups
-// for the CUs, or when many tokens already fill the registers and LDS.
+// Rows per group: one for PLAIN / RESIDUAL with up to four tokens (x is read
+// from registers or LDS, so sharing it buys little, while the smaller weight
+// staging and register use let more waves keep loads in flight: measured 11.2 ->
+// 9.9 us at T = 1 on Q4_0 12288 x 4096), else two (the SwiGLU gate/up pair, or
+// the FMAs of many tokens).
 template <int QT, int EPI, int TT>
 hipError_t launch_t(const GemmArgs &a, hipStream_t s) {
-    const int rows = EPI == EPI_SWIGLU ? 2 * a.n : a.n;
-    if constexpr (TT <= 4)
-        if (rows / 4 >= 256 * 12) return launch_r<QT, EPI, TT, 4>(a, s);
+    if constexpr (EPI != EPI_SWIGLU && TT <= 4) return launch_r<QT, EPI, TT, 1>(a, s);
     return launch_r<QT, EPI, TT, 2>(a, s);
 }
 
