@@ -107,13 +107,21 @@ __device__ __forceinline__ float q8_byte_f32(uint32_t w, int byte, float d) {
 }
 
 // Orders one wave's LDS accesses before the call against those after it, for
-// communication between the lanes of that wave through LDS. The hardware already
-// completes one wave's LDS operations in order, so nothing is emitted; the fences
-// keep the compiler from moving accesses across (without them, a store whose
-// address no load of the same thread can alias may be sunk past another lane's
-// read of it).
+// communication between the lanes of that wave through LDS.
+//  - The fences keep the compiler from moving accesses across (without them, a
+//    store whose address no load of the same thread can alias may be sunk past
+//    another lane's read of it).
+//  - The wait (lgkmcnt = 0) makes the wave's LDS operations complete before any
+//    later one issues. The compiler emits nothing for wavefront-scope fences, on
+//    the assumption that a wave's LDS operations are performed in order; on gfx950
+//    that did not hold for the SwiGLU epilogue's exchange (16-byte stores of
+//    accumulator registers, then 16-byte loads of other lanes' values issued right
+//    behind them): without the wait, whole groups of loads intermittently returned
+//    values other than the ones just stored.
+constexpr int WAITCNT_LGKM0 = 0xC07F;  // s_waitcnt lgkmcnt(0), vmcnt and expcnt not waited
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
