@@ -110,8 +110,9 @@ int pf_gemm(int qtype, const void *W_blocks, int64_t n, int64_t k, const float *
 int pf_gemm_path(int qtype, const void *W_blocks, int64_t n, int64_t k, const float *X,
                  int64_t T, float *Y, int epilogue, int leg, void *stream, int path);
 
-/* Workspace bytes pf_gemm_ws needs for these sizes: T * k * 2 when it runs the f16
- * leg's matrix-core GEMM (room for X rounded to binary16), 0 when it runs a kernel
+/* Workspace bytes pf_gemm_ws needs for these sizes: ceil(T / 32) * 32 * k * 2 when it
+ * runs the f16 leg's matrix-core GEMM (room for X rounded to binary16, T padded to
+ * whole 32-row tiles), 0 when it runs a kernel
  * that needs none (the f32 leg, the GEMV, T == 0), or -PF_E_* for arguments pf_gemm
  * would refuse. Host-only; touches no GPU state. */
 int64_t pf_workspace_bytes(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int leg);

@@ -43,9 +43,10 @@ int check_sizes(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int le
     return PF_OK;
 }
 
-// Bytes of workspace the f16 leg's GEMM takes (X as binary16), else 0.
+// Bytes of workspace the f16 leg's GEMM takes (X as binary16, T rounded up to a
+// multiple of 32 for the fragment-ordered copy), else 0.
 int64_t ws_need(int64_t k, int64_t T, int leg, int use) {
-    return (use == PF_PATH_GEMM && leg == PF_LEG_F16) ? T * k * 2 : 0;
+    return (use == PF_PATH_GEMM && leg == PF_LEG_F16) ? (T + 31) / 32 * 32 * k * 2 : 0;
 }
 
 int gemm_impl(int qtype, const void *W, int64_t n, int64_t k, const float *X, int64_t T, float *Y,

@@ -764,6 +764,324 @@ void gemm_f16_w8_kernel(const uint8_t *__restrict__ W, const uint16_t *__restric
     }
 }
 
+// ---------------------------------------------------------------------------
+// Cooperative decode: 8 waves (512 threads, two per SIMD) on a 256-row x
+// 192-weight-row tile, laid out 4 (rows) x 2 (weight rows); each wave owns 64 x 96
+// (2 x 3 MFMA tiles of 32 x 32, 96 accumulators).
+//  - B: every weight block of the tile is decoded once per workgroup, by all 512
+//    threads, into an fp16 tile in LDS kept in B-fragment order, so that a wave
+//    reads a B fragment with one 16-byte LDS load per lane (vs decoding in each
+//    wave the columns it uses: 4 times the decode work in this layout).
+//  - A: X comes from the workspace already in A-fragment order (x_to_frag_kernel),
+//    so each wave loads its A fragments straight from global memory, one 16-byte
+//    load per lane and fragment, AD steps ahead into a ring of registers. X thus
+//    costs no LDS traffic at all, which leaves the LDS to the B fragments, the
+//    decode's stores and the raw weight chunks (measured: staging X through LDS and
+//    reading it back cost as much as the decode).
+// Q4_0 only (the Q8_0 chunks would not fit in LDS).
+//
+// Per step s (one 32-k block), with one barrier at its end:
+//   (a) read the second half (k 16..31) of step s's B fragments;
+//   (b) the MFMAs of the first half, whose B fragments were read during step s-1;
+//   (c) staging: slice (s+2) % 8 (rows 24 S .. 24 S + 23, whole) of a raw weight
+//       chunk; decode of block s+2 from its raw chunk into B buffer (s+2) % 4;
+//   (d) read the first half of step s+1's B fragments;
+//   (e) the MFMAs of the second half; then load the A fragments of step s+AD.
+// Decoded B lives in a ring of four LDS buffers; raw chunks take two buffers,
+// chunk c being filled during steps 8c-10 .. 8c-3 and decoded during steps
+// 8c-2 .. 8c+5.
+//
+// Decode assignment (768 qs words per block): thread t decodes word t % 4 of tile
+// row t / 4 (rows 0..127) whole, and nibble half t % 2 of word (t / 2) % 4 of row
+// 128 + t / 8 (rows 128..191), so every wave carries the same share.
+template <int EPI, bool SPLIT>
+__global__ __launch_bounds__(512)
+void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ Xf,
+                          float *__restrict__ Y, int n, int k, int T, int tiles_m, int tiles_n,
+                          int splits) {
+    constexpr int QT = Q4_0;
+    using CT = ChunkTraits<QT>;
+    constexpr int MT = 256, NW = 192;
+    constexpr int BB = CT::BB;                      // 18
+    constexpr int IT = 2, JT = 3;                   // per wave: 64 rows x 96 weight rows
+    constexpr int U4 = CT::U4;                      // 9
+    constexpr int WROW = CT::ROW;                   // 144
+    constexpr int WBUF = NW * WROW;                 // raw chunk buffer
+    constexpr int BBUF = NW * 32 * 2;               // B(s): 6 tiles x 2 halves x 64 lanes x 16 B
+    constexpr int NBB = 4;                          // B buffers
+    constexpr int PD = 4;                           // weight staging ring depth (steps)
+    constexpr int AD = 2;                           // A fragment ring depth (steps)
+    constexpr int LOOP_BYTES = NBB * BBUF + 2 * WBUF;
+    constexpr int EPI_BYTES = 8 * 32 * 36 * 4;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[LOOP_BYTES > EPI_BYTES ? LOOP_BYTES : EPI_BYTES];
+    uint8_t *const bsm = smem;
+    uint8_t *const wsm0 = smem + NBB * BBUF;
+    static_assert(WBUF % 16 == 0 && BBUF % 16 == 0, "16-byte aligned carve-up");
+    static_assert(8 % PD == 0 && 8 % AD == 0 && 8 % NBB == 0, "rings follow the step within a chunk");
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+
+    // Workgroup -> tile, XCD-aware (as in gemm_f16_kernel).
+    const int total = tiles_m * tiles_n * splits;
+    int logical;
+    {
+        const int id = blockIdx.x;
+        const int per = (total + 7) / 8;
+        const int xcd = id & 7, slot = id >> 3;
+        const int full = total - 8 * (per - 1);
+        logical = (xcd < full) ? xcd * per + slot : full * per + (xcd - full) * (per - 1) + slot;
+    }
+    const int tm = logical % tiles_m;
+    const int rest = logical / tiles_m;
+    const int tn = rest % tiles_n;
+    const int split = rest / tiles_n;
+    const int m0 = tm * MT;
+    const int nchunks = k >> 8;
+    const int c_begin = (int)((long)nchunks * split / splits);
+    const int c_end = (int)((long)nchunks * (split + 1) / splits);
+    const int nch = c_end - c_begin;
+    if (nch <= 0) return;
+    const int nsteps = 8 * nch;
+    const uint32_t row_bytes = (uint32_t)(k >> 5) * BB;
+
+    // A fragments: 32-row tile rt, 16-k slice kk at fragment rt * (k / 16) + kk of
+    // the workspace (1 KB each; this lane's 16 bytes at 16 lane). Row tiles past
+    // the padded T read the last one; their outputs are never stored.
+    const int rt_last = ((T + 31) >> 5) - 1;
+    const uint8_t *abase[IT];
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+        const int rt = min((m0 >> 5) + wm * IT + i, rt_last);
+        abase[i] = reinterpret_cast<const uint8_t *>(Xf) +
+                   ((size_t)rt * (k >> 4) + (size_t)c_begin * 16) * 1024 + lane * 16;
+    }
+
+    // Weight staging: slice S of a chunk = its rows 24 S .. 24 S + 23, whole (216
+    // 16-byte pieces; thread t < 216 copies piece t % 9 of slice row t / 9).
+    constexpr int RS = NW / 8;
+    constexpr int SP = RS * U4;
+    static_assert(SP <= 512, "one piece per thread");
+    const bool wvalid = tid < SP;
+    const int wff = wvalid ? tid : 0;
+    const int wrr = wff / U4, wpp = wff % U4;
+    const int wdst = wrr * WROW + 16 * wpp;
+    uint32_t wsrc[8];
+#pragma unroll
+    for (int S = 0; S < 8; ++S) {
+        int gr = f16_weight_row<EPI, NW>(tn, S * RS + wrr, n);
+        gr = gr < 0 ? 0 : gr;
+        wsrc[S] = (uint32_t)gr * row_bytes + 16 * wpp;
+    }
+    const uint8_t *wbase = W + (size_t)c_begin * WROW;
+
+    // B fragment (tile jj, half q): 16 bytes of lane `lane` in fragment (wn 3 + jj, q).
+    const int boff = (wn * JT * 2 * 64 + lane) * 16;
+
+    // Decode: whole word w0 of row r0, nibble half e1 of word w1 of row r1. Raw
+    // offsets inside a chunk buffer (block 0); fragment offsets inside a B buffer:
+    // tile r / 32, half, lane (r % 32, w / 2), byte 8 (w % 2).
+    const int r0 = tid >> 2, w0 = tid & 3;
+    const int r1 = 128 + (tid >> 3), w1 = (tid >> 1) & 3, e1 = tid & 1;
+    const int sraw0 = r0 * WROW, qraw0 = sraw0 + 4 * w0;
+    const int sraw1 = r1 * WROW, qraw1 = sraw1 + 4 * w1;
+    const int bdst0 = (((r0 >> 5) * 2) * 64 + (w0 >> 1) * 32 + (r0 & 31)) * 16 + 8 * (w0 & 1);
+    const int bdst1 = (((r1 >> 5) * 2 + e1) * 64 + (w1 >> 1) * 32 + (r1 & 31)) * 16 + 8 * (w1 & 1);
+    const uint32_t nshift1 = 4 * e1;
+
+    f16v_t acc[IT][JT];
+#pragma unroll
+    for (int i = 0; i < IT; ++i)
+#pragma unroll
+        for (int j = 0; j < JT; ++j) acc[i][j] = f16v_t{};
+
+    auto fetch_slice = [&](int chunk, auto s_c, u4_t &dst) __attribute__((always_inline)) {
+        constexpr int S = decltype(s_c)::value;
+        dst = *reinterpret_cast<const u4_t *>(wbase + (size_t)min(chunk, nch - 1) * WROW + wsrc[S]);
+    };
+    auto store_slice = [&](int wbuf, auto s_c, const u4_t &src) __attribute__((always_inline)) {
+        constexpr int S = decltype(s_c)::value;
+        if (wvalid) *reinterpret_cast<u4_t *>(wsm0 + wbuf * WBUF + S * RS * WROW + wdst) = src;
+    };
+
+    // Block `blk` (compile-time) of raw chunk buffer `wbuf` -> B buffer `bbuf`.
+    auto decode_block = [&](int wbuf, auto blk_c, auto bbuf_c) __attribute__((always_inline)) {
+        constexpr int blk = decltype(blk_c)::value;
+        constexpr int SH = (blk * BB + 2) & 3;       // qs start 2 bytes into a dword for even blocks
+        const uint8_t *wb = wsm0 + wbuf * WBUF + blk * BB;
+        uint8_t *bb = bsm + decltype(bbuf_c)::value * BBUF;
+        const uint32_t d0 = *reinterpret_cast<const uint16_t *>(wb + sraw0);
+        const uint32_t d1 = *reinterpret_cast<const uint16_t *>(wb + sraw1);
+        uint32_t q0, q1;
+        if constexpr (SH == 0) {
+            q0 = *reinterpret_cast<const uint32_t *>(wb + qraw0 + 2);
+            q1 = *reinterpret_cast<const uint32_t *>(wb + qraw1 + 2);
+        } else {
+            const uint32_t *a0 = reinterpret_cast<const uint32_t *>(wb + qraw0);
+            const uint32_t *a1 = reinterpret_cast<const uint32_t *>(wb + qraw1);
+            q0 = __builtin_amdgcn_alignbyte(a0[1], a0[0], SH);
+            q1 = __builtin_amdgcn_alignbyte(a1[1], a1[0], SH);
+        }
+        const h2_t d20 = as_h2(d0 | (d0 << 16));
+        const h2_t d21 = as_h2(d1 | (d1 << 16));
+        uint32_t lo02, lo13, hi02, hi13;
+        q4_word_decode(q0, d20, lo02, lo13, hi02, hi13);
+        *reinterpret_cast<u2_t *>(bb + bdst0) = u2_t{lo02, lo13};
+        *reinterpret_cast<u2_t *>(bb + bdst0 + 1024) = u2_t{hi02, hi13};
+        const h2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
+        const uint32_t nib = (q1 >> nshift1) & 0x0F0F0F0Fu;
+        const uint32_t p02 = h2_bits((as_h2(magic_pair(nib, SEL_B02)) - off) * d21);
+        const uint32_t p13 = h2_bits((as_h2(magic_pair(nib, SEL_B13)) - off) * d21);
+        *reinterpret_cast<u2_t *>(bb + bdst1) = u2_t{p02, p13};
+    };
+
+    h8_t fa[AD][2][IT];  // A fragments [ring slot][k half][tile]
+    h8_t fb[2][JT];      // B fragments [k half][tile]
+    auto load_a = [&](int step, h8_t (&dst)[2][IT]) __attribute__((always_inline)) {
+        const size_t off = (size_t)min(step, nsteps - 1) * 2048;
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int i = 0; i < IT; ++i)
+                dst[q][i] = *reinterpret_cast<const h8_t *>(abase[i] + off + q * 1024);
+    };
+    auto load_b = [&](auto buf_c, auto q_c) __attribute__((always_inline)) {
+        constexpr int q = decltype(q_c)::value;
+        const uint8_t *bb = bsm + decltype(buf_c)::value * BBUF + boff + q * 1024;
+#pragma unroll
+        for (int j = 0; j < JT; ++j) fb[q][j] = *reinterpret_cast<const h8_t *>(bb + j * 2048);
+    };
+    auto mfma_half = [&](const h8_t (&a)[2][IT], auto q_c) __attribute__((always_inline)) {
+        constexpr int q = decltype(q_c)::value;
+#pragma unroll
+        for (int j = 0; j < JT; ++j)
+#pragma unroll
+            for (int i = 0; i < IT; ++i)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[q][i], fb[q][j], acc[i][j], 0, 0, 0);
+    };
+
+    u4_t wr[PD];      // the slices written by steps s .. s+PD-1
+
+    // ---- prologue (steps -2 and -1): chunk 0 whole and chunk 1 slices 0, 1;
+    // blocks 0 and 1 decoded; the first half of step 0's B fragments. The rings hold
+    // chunk 1 slices 2 .. PD+1 and the A fragments of steps 0 .. AD-1.
+    {
+        u4_t tmp;
+#define PF_COOP_CHUNK0(S)                                         \
+        fetch_slice(0, std::integral_constant<int, S>{}, tmp);    \
+        store_slice(0, std::integral_constant<int, S>{}, tmp);
+        PF_COOP_CHUNK0(0) PF_COOP_CHUNK0(1) PF_COOP_CHUNK0(2) PF_COOP_CHUNK0(3)
+        PF_COOP_CHUNK0(4) PF_COOP_CHUNK0(5) PF_COOP_CHUNK0(6) PF_COOP_CHUNK0(7)
+#undef PF_COOP_CHUNK0
+        fetch_slice(1, std::integral_constant<int, 0>{}, tmp);
+        if (nch > 1) store_slice(1, std::integral_constant<int, 0>{}, tmp);
+        fetch_slice(1, std::integral_constant<int, 1>{}, tmp);
+        if (nch > 1) store_slice(1, std::integral_constant<int, 1>{}, tmp);
+        // Ring loads in the order the loop issues them (per step: the weight slice,
+        // then the A fragments), so that the wait counts the compiler derives at the
+        // loop head are the steady-state ones rather than a merge of two orders.
+        static_assert(PD == 4 && AD == 2, "prologue fills rings of 4 and 2");
+        __builtin_amdgcn_sched_barrier(0);
+        fetch_slice(1, std::integral_constant<int, 2>{}, wr[0]);
+        fetch_slice(1, std::integral_constant<int, 3>{}, wr[1]);
+        load_a(0, fa[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        fetch_slice(1, std::integral_constant<int, 4>{}, wr[2]);
+        fetch_slice(1, std::integral_constant<int, 5>{}, wr[3]);
+        load_a(1, fa[1]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+    decode_block(0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+    decode_block(0, std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
+    __syncthreads();
+    load_b(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+
+    for (int ch = 0; ch < nch; ++ch) {
+        auto step_body = [&](auto blk_c) __attribute__((always_inline)) {
+            constexpr int blk = decltype(blk_c)::value;
+            constexpr int RG = blk % PD;
+            constexpr int RA = blk % AD;
+            const int s = ch * 8 + blk;
+            load_b(std::integral_constant<int, blk % NBB>{}, std::integral_constant<int, 1>{});
+            mfma_half(fa[RA], std::integral_constant<int, 0>{});
+            {
+                const int wc = ch + 1 + ((blk + 2) >> 3);  // chunk receiving the slice
+                if (wc < nch) store_slice(wc & 1, std::integral_constant<int, (blk + 2) & 7>{}, wr[RG]);
+                fetch_slice(ch + 1 + ((blk + PD + 2) >> 3),
+                            std::integral_constant<int, (blk + PD + 2) & 7>{}, wr[RG]);
+            }
+            decode_block((ch + ((blk + 2) >> 3)) & 1, std::integral_constant<int, (blk + 2) & 7>{},
+                         std::integral_constant<int, (blk + 2) % NBB>{});
+            load_b(std::integral_constant<int, (blk + 1) % NBB>{}, std::integral_constant<int, 0>{});
+            mfma_half(fa[RA], std::integral_constant<int, 1>{});
+            load_a(s + AD, fa[RA]);
+            __syncthreads();
+        };
+        step_body(std::integral_constant<int, 0>{});
+        step_body(std::integral_constant<int, 1>{});
+        step_body(std::integral_constant<int, 2>{});
+        step_body(std::integral_constant<int, 3>{});
+        step_body(std::integral_constant<int, 4>{});
+        step_body(std::integral_constant<int, 5>{});
+        step_body(std::integral_constant<int, 6>{});
+        step_body(std::integral_constant<int, 7>{});
+    }
+
+    // ---- epilogue (as gemm_f16_kernel, with the 4 x 2 wave layout). The loop's
+    // last barrier has retired every LDS access of the K loop.
+    int etid = threadIdx.x;
+    asm volatile("" : "+v"(etid));
+    const int e_lane = etid & 63, e_wave = etid >> 6;
+    const int e_wm = e_wave >> 1, e_wn = e_wave & 1;
+    const int e_c = e_lane & 31, e_h = e_lane >> 5;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+#pragma unroll
+        for (int j = 0; j < JT; ++j) {
+            const int tile_col = (e_wn * JT + j) * 32;
+            const int trow = m0 + e_wm * IT * 32 + i * 32 + 4 * e_h;
+            if constexpr (EPI == EPI_SWIGLU) {
+                float *slot = reinterpret_cast<float *>(smem) + e_wave * (32 * 36);
+                wave_lds_sync();
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4)
+                    *reinterpret_cast<f4_t *>(slot + e_c * 36 + 8 * g4 + 4 * e_h) =
+                        f4_t{acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2],
+                             acc[i][j][4 * g4 + 3]};
+                wave_lds_sync();
+                const int cc = e_lane & 15;
+                const int o = tn * (NW / 2) + (tile_col >> 1) + cc;
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const int q = (e_lane >> 4) + 4 * half;
+                    const f4_t g = *reinterpret_cast<const f4_t *>(slot + cc * 36 + 4 * q);
+                    const f4_t u = *reinterpret_cast<const f4_t *>(slot + (cc + 16) * 36 + 4 * q);
+                    const int t0 = m0 + e_wm * IT * 32 + i * 32 + 4 * q;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (t0 + e < T && o < n) Y[(size_t)(t0 + e) * n + o] = silu_fast(g[e]) * u[e];
+                }
+            } else {
+                const int o = tn * NW + tile_col + e_c;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int t = trow + 8 * (r >> 2) + (r & 3);
+                    if (t < T && o < n) {
+                        float *y = Y + (size_t)t * n + o;
+                        if constexpr (SPLIT || EPI == EPI_RESIDUAL)
+                            atomicAdd(y, acc[i][j][r]);
+                        else
+                            *y = acc[i][j][r];
+                    }
+                }
+            }
+        }
+    }
+}
+
 __global__ void zero_fill_kernel(float *__restrict__ Y, int count) {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i < count) Y[i] = 0.f;
@@ -875,6 +1193,32 @@ __global__ __launch_bounds__(256) void x_to_f16_kernel(const float *__restrict__
     reinterpret_cast<u4_t *>(Xh)[i] = u4_t{pa[0], pa[1], pb[0], pb[1]};
 }
 
+// X [T][k] f32 -> fp16 (RNE) in A-fragment order for gemm_f16_coop_kernel: for each
+// 32-row tile rt and 16-k slice kk, one 1 KB fragment at index rt * (k / 16) + kk,
+// whose lane (c, h) holds row 32 rt + c, k = 16 kk + 8 h .. + 7 in the order of
+// x_pack. Rows past T (up to the next multiple of 32) are zero. One thread writes
+// one lane's 16 bytes.
+template <int QT>
+__global__ __launch_bounds__(256) void x_to_frag_kernel(const float *__restrict__ X,
+                                                        uint16_t *__restrict__ Xf, int T, int k,
+                                                        int count) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= count) return;
+    const int lane = i & 63;
+    const int f = i >> 6;
+    const int k16 = k >> 4;
+    const int rt = f / k16, kk = f - rt * k16;
+    const int row = rt * 32 + (lane & 31);
+    u4_t out = u4_t{0u, 0u, 0u, 0u};
+    if (row < T) {
+        const float *src = X + (size_t)row * k + kk * 16 + 8 * (lane >> 5);
+        const u2_t pa = x_pack<QT>(*reinterpret_cast<const f4_t *>(src));
+        const u2_t pb = x_pack<QT>(*reinterpret_cast<const f4_t *>(src + 4));
+        out = u4_t{pa[0], pa[1], pb[0], pb[1]};
+    }
+    reinterpret_cast<u4_t *>(Xf)[i] = out;
+}
+
 }  // namespace
 
 // The 8-wave kernel: 256 x 256 tiles; split K for PLAIN / RESIDUAL when the
@@ -906,8 +1250,56 @@ hipError_t launch_w8(const GemmArgs &a, const uint16_t *xh, hipStream_t s) {
     return hipGetLastError();
 }
 
+// The cooperative-decode kernel: 256 x 192 tiles; split K for PLAIN / RESIDUAL
+// when the tiles alone would leave CUs idle (any split count; the chunk ranges of
+// the splits differ by at most one chunk).
+template <int EPI>
+hipError_t launch_coop(const GemmArgs &a, const uint16_t *xh, hipStream_t s) {
+    const int tm = (a.T + 255) / 256;
+    const int out_per_tile = EPI == EPI_SWIGLU ? 96 : 192;
+    const int tn = (a.n + out_per_tile - 1) / out_per_tile;
+    int splits = 1;
+    if constexpr (EPI != EPI_SWIGLU) {
+        const int nchunks = a.k / 256;
+        const int tiles = tm * tn;
+        if (tiles < 256) {
+            splits = 256 / tiles;
+            if (splits > nchunks) splits = nchunks;
+            if (splits > 16) splits = 16;
+        }
+    }
+    const int total = tm * tn * splits;
+    if (splits > 1) {
+        if constexpr (EPI == EPI_PLAIN) {
+            const int count = a.T * a.n;
+            hipLaunchKernelGGL(zero_fill_kernel, dim3((count + 255) / 256), dim3(256), 0, s, a.Y, count);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        hipLaunchKernelGGL((gemm_f16_coop_kernel<EPI, true>), dim3(total), dim3(512), 0, s, a.W, xh,
+                           a.Y, a.n, a.k, a.T, tm, tn, splits);
+    } else {
+        hipLaunchKernelGGL((gemm_f16_coop_kernel<EPI, false>), dim3(total), dim3(512), 0, s, a.W, xh,
+                           a.Y, a.n, a.k, a.T, tm, tn, splits);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm_f16_ws(const GemmArgs &a, void *workspace, hipStream_t s) {
     uint16_t *xh = static_cast<uint16_t *>(workspace);
+    if (a.qtype == Q4_0 && a.T >= 256) {
+        // The cooperative-decode kernel takes X in A-fragment order.
+        const int count = (a.T + 31) / 32 * 32 * (a.k / 8);
+        hipLaunchKernelGGL(x_to_frag_kernel<Q4_0>, dim3((count + 255) / 256), dim3(256), 0, s, a.X, xh,
+                           a.T, a.k, count);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        switch (a.epilogue) {
+        case EPI_PLAIN: return launch_coop<EPI_PLAIN>(a, xh, s);
+        case EPI_RESIDUAL: return launch_coop<EPI_RESIDUAL>(a, xh, s);
+        default: return launch_coop<EPI_SWIGLU>(a, xh, s);
+        }
+    }
     const int count8 = a.T * (a.k / 8);
     if (a.qtype == Q4_0)
         hipLaunchKernelGGL(x_to_f16_kernel<Q4_0>, dim3((count8 + 255) / 256), dim3(256), 0, s, a.X, xh, count8);

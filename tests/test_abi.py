@@ -118,9 +118,11 @@ def test_gemm_argument_checks(lib):
 
 def test_workspace_bytes(lib):
     wb = lib.pf_workspace_bytes
-    # the f16 leg's matrix-core GEMM takes T * k halves; the GEMV and the f32 leg none
+    # the f16 leg's matrix-core GEMM takes k halves per token row, T rounded up to a
+    # multiple of 32; the GEMV and the f32 leg none
     assert wb(pf.PF_Q4_0, 12288, 4096, 512, pf.PF_GATE_UP_SWIGLU, pf.PF_LEG_F16) == 512 * 4096 * 2
-    assert wb(pf.PF_Q8_0, 4096, 12288, 9, pf.PF_RESIDUAL, pf.PF_LEG_F16) == 9 * 12288 * 2
+    assert wb(pf.PF_Q8_0, 4096, 12288, 9, pf.PF_RESIDUAL, pf.PF_LEG_F16) == 32 * 12288 * 2
+    assert wb(pf.PF_Q4_0, 4096, 4096, 300, pf.PF_PLAIN, pf.PF_LEG_F16) == 320 * 4096 * 2
     assert wb(pf.PF_Q4_0, 4096, 4096, 512, pf.PF_PLAIN, pf.PF_LEG_F32) == 0
     assert wb(pf.PF_Q4_0, 4096, 4096, 8, pf.PF_PLAIN, pf.PF_LEG_F16) == 0
     assert wb(pf.PF_Q4_0, 4096, 4096, 0, pf.PF_PLAIN, pf.PF_LEG_F16) == 0
@@ -133,7 +135,7 @@ def test_gemm_ws_argument_checks(lib):
     P = ctypes.c_void_p
     W, X, Y, WS = FAKE, FAKE + (1 << 32), FAKE + (2 << 32), FAKE + (3 << 32)
     n, k, T = 64, 256, 16
-    need = T * k * 2
+    need = 32 * k * 2
 
     def g(ws=WS, ws_bytes=need, leg=pf.PF_LEG_F16, **kw):
         a = dict(qtype=0, W=W, n=n, k=k, X=X, T=T, Y=Y, epi=0)
