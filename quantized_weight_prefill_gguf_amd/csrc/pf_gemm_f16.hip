@@ -774,7 +774,7 @@ void gemm_f16_w8_kernel(const uint8_t *__restrict__ W, const uint16_t *__restric
 //    wave the columns it uses: 4 times the decode work in this layout).
 //  - A: X comes from the workspace already in A-fragment order (x_to_frag_kernel),
 //    so each wave loads its A fragments straight from global memory, one 16-byte
-//    load per lane and fragment, AD steps ahead into a ring of registers. X thus
+//    load per lane and fragment, AD (4) steps ahead into a ring of registers. X thus
 //    costs no LDS traffic at all, which leaves the LDS to the B fragments, the
 //    decode's stores and the raw weight chunks (measured: staging X through LDS and
 //    reading it back cost as much as the decode).
@@ -791,10 +791,11 @@ void gemm_f16_w8_kernel(const uint8_t *__restrict__ W, const uint16_t *__restric
 // chunk c being filled during steps 8c-10 .. 8c-3 and decoded during steps
 // 8c-2 .. 8c+5.
 //
-// Decode assignment (768 qs words per block): thread t decodes word t % 4 of tile
-// row t / 4 (rows 0..127) whole, and nibble half t % 2 of word (t / 2) % 4 of row
-// 128 + t / 8 (rows 128..191), so every wave carries the same share.
-template <int EPI, bool SPLIT>
+// Decode assignment (768 qs words per block): each thread decodes one word whole
+// (rows 0..127) and one nibble half of another (rows 128..191), so every wave
+// carries the same share. Within each half wave (32 lanes) the stores cover 256
+// contiguous bytes of one fragment half, so they are free of bank conflicts.
+template <int EPI, bool SPLIT, int AD = 4>
 __global__ __launch_bounds__(512)
 void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ Xf,
                           float *__restrict__ Y, int n, int k, int T, int tiles_m, int tiles_n,
@@ -810,7 +811,6 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
     constexpr int BBUF = NW * 32 * 2;               // B(s): 6 tiles x 2 halves x 64 lanes x 16 B
     constexpr int NBB = 4;                          // B buffers
     constexpr int PD = 4;                           // weight staging ring depth (steps)
-    constexpr int AD = 2;                           // A fragment ring depth (steps)
     constexpr int LOOP_BYTES = NBB * BBUF + 2 * WBUF;
     constexpr int EPI_BYTES = 8 * 32 * 36 * 4;
     __shared__ __attribute__((aligned(16))) uint8_t smem[LOOP_BYTES > EPI_BYTES ? LOOP_BYTES : EPI_BYTES];
@@ -883,8 +883,15 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
     // Decode: whole word w0 of row r0, nibble half e1 of word w1 of row r1. Raw
     // offsets inside a chunk buffer (block 0); fragment offsets inside a B buffer:
     // tile r / 32, half, lane (r % 32, w / 2), byte 8 (w % 2).
-    const int r0 = tid >> 2, w0 = tid & 3;
-    const int r1 = 128 + (tid >> 3), w1 = (tid >> 1) & 3, e1 = tid & 1;
+    //  - whole words: wave v takes rows 16 v .. 16 v + 15; its lane l the word
+    //    2 (l / 32) + l % 2 of row 16 v + (l / 2) % 16;
+    //  - nibble halves: the 32-lane group g = t / 32 takes nibble half g % 2 of words
+    //    2 ((g / 2) % 2) + {0, 1} of rows 128 + 16 (g / 4) .. + 15; lane l of the
+    //    group word 2 ((g / 2) % 2) + l % 2 of row 128 + 16 (g / 4) + l / 2.
+    const int r0 = 16 * (tid >> 6) + ((tid >> 1) & 15), w0 = 2 * ((tid >> 5) & 1) + (tid & 1);
+    const int g1 = tid >> 5;
+    const int r1 = 128 + 16 * (g1 >> 2) + ((tid & 31) >> 1), w1 = 2 * ((g1 >> 1) & 1) + (tid & 1);
+    const int e1 = g1 & 1;
     const int sraw0 = r0 * WROW, qraw0 = sraw0 + 4 * w0;
     const int sraw1 = r1 * WROW, qraw1 = sraw1 + 4 * w1;
     const int bdst0 = (((r0 >> 5) * 2) * 64 + (w0 >> 1) * 32 + (r0 & 31)) * 16 + 8 * (w0 & 1);
@@ -982,15 +989,29 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
         // Ring loads in the order the loop issues them (per step: the weight slice,
         // then the A fragments), so that the wait counts the compiler derives at the
         // loop head are the steady-state ones rather than a merge of two orders.
-        static_assert(PD == 4 && AD == 2, "prologue fills rings of 4 and 2");
+        static_assert(PD == 4 && (AD == 2 || AD == 4), "prologue fills rings of 4 and AD");
         __builtin_amdgcn_sched_barrier(0);
-        fetch_slice(1, std::integral_constant<int, 2>{}, wr[0]);
-        fetch_slice(1, std::integral_constant<int, 3>{}, wr[1]);
-        load_a(0, fa[0]);
-        __builtin_amdgcn_sched_barrier(0);
-        fetch_slice(1, std::integral_constant<int, 4>{}, wr[2]);
-        fetch_slice(1, std::integral_constant<int, 5>{}, wr[3]);
-        load_a(1, fa[1]);
+        if constexpr (AD == 2) {
+            fetch_slice(1, std::integral_constant<int, 2>{}, wr[0]);
+            fetch_slice(1, std::integral_constant<int, 3>{}, wr[1]);
+            load_a(0, fa[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            fetch_slice(1, std::integral_constant<int, 4>{}, wr[2]);
+            fetch_slice(1, std::integral_constant<int, 5>{}, wr[3]);
+            load_a(1, fa[1]);
+        } else {
+            fetch_slice(1, std::integral_constant<int, 2>{}, wr[0]);
+            load_a(0, fa[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            fetch_slice(1, std::integral_constant<int, 3>{}, wr[1]);
+            load_a(1, fa[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            fetch_slice(1, std::integral_constant<int, 4>{}, wr[2]);
+            load_a(2, fa[2]);
+            __builtin_amdgcn_sched_barrier(0);
+            fetch_slice(1, std::integral_constant<int, 5>{}, wr[3]);
+            load_a(3, fa[3]);
+        }
         __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
