@@ -778,7 +778,7 @@ void gemm_f16_w8_kernel(const uint8_t *__restrict__ W, const uint16_t *__restric
 //    costs no LDS traffic at all, which leaves the LDS to the B fragments, the
 //    decode's stores and the raw weight chunks (measured: staging X through LDS and
 //    reading it back cost as much as the decode).
-// Q4_0 only (the Q8_0 chunks would not fit in LDS).
+// Q4_0 and Q8_0 (LDS: four B buffers of 12 KB and two raw chunk buffers of 27 / 51 KB).
 //
 // Per step s (one 32-k block), with one barrier at its end:
 //   (a) read the second half (k 16..31) of step s's B fragments;
@@ -795,18 +795,17 @@ void gemm_f16_w8_kernel(const uint8_t *__restrict__ W, const uint16_t *__restric
 // (rows 0..127) and one nibble half of another (rows 128..191), so every wave
 // carries the same share. Within each half wave (32 lanes) the stores cover 256
 // contiguous bytes of one fragment half, so they are free of bank conflicts.
-template <int EPI, bool SPLIT, int AD = 4>
+template <int QT, int EPI, bool SPLIT, int AD = 4>
 __global__ __launch_bounds__(512)
 void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ Xf,
                           float *__restrict__ Y, int n, int k, int T, int tiles_m, int tiles_n,
                           int splits) {
-    constexpr int QT = Q4_0;
     using CT = ChunkTraits<QT>;
     constexpr int MT = 256, NW = 192;
-    constexpr int BB = CT::BB;                      // 18
+    constexpr int BB = CT::BB;                      // 18 / 34
     constexpr int IT = 2, JT = 3;                   // per wave: 64 rows x 96 weight rows
-    constexpr int U4 = CT::U4;                      // 9
-    constexpr int WROW = CT::ROW;                   // 144
+    constexpr int U4 = CT::U4;                      // 9 / 17
+    constexpr int WROW = CT::ROW;                   // 144 / 272
     constexpr int WBUF = NW * WROW;                 // raw chunk buffer
     constexpr int BBUF = NW * 32 * 2;               // B(s): 6 tiles x 2 halves x 64 lanes x 16 B
     constexpr int NBB = 4;                          // B buffers
@@ -859,8 +858,8 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
                    ((size_t)rt * (k >> 4) + (size_t)c_begin * 16) * 1024 + lane * 16;
     }
 
-    // Weight staging: slice S of a chunk = its rows 24 S .. 24 S + 23, whole (216
-    // 16-byte pieces; thread t < 216 copies piece t % 9 of slice row t / 9).
+    // Weight staging: slice S of a chunk = its rows 24 S .. 24 S + 23, whole (216 /
+    // 408 16-byte pieces; thread t < 24 U4 copies piece t % U4 of slice row t / U4).
     constexpr int RS = NW / 8;
     constexpr int SP = RS * U4;
     static_assert(SP <= 512, "one piece per thread");
@@ -888,15 +887,34 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
     //  - nibble halves: the 32-lane group g = t / 32 takes nibble half g % 2 of words
     //    2 ((g / 2) % 2) + {0, 1} of rows 128 + 16 (g / 4) .. + 15; lane l of the
     //    group word 2 ((g / 2) % 2) + l % 2 of row 128 + 16 (g / 4) + l / 2.
-    const int r0 = 16 * (tid >> 6) + ((tid >> 1) & 15), w0 = 2 * ((tid >> 5) & 1) + (tid & 1);
-    const int g1 = tid >> 5;
-    const int r1 = 128 + 16 * (g1 >> 2) + ((tid & 31) >> 1), w1 = 2 * ((g1 >> 1) & 1) + (tid & 1);
-    const int e1 = g1 & 1;
-    const int sraw0 = r0 * WROW, qraw0 = sraw0 + 4 * w0;
-    const int sraw1 = r1 * WROW, qraw1 = sraw1 + 4 * w1;
-    const int bdst0 = (((r0 >> 5) * 2) * 64 + (w0 >> 1) * 32 + (r0 & 31)) * 16 + 8 * (w0 & 1);
-    const int bdst1 = (((r1 >> 5) * 2 + e1) * 64 + (w1 >> 1) * 32 + (r1 & 31)) * 16 + 8 * (w1 & 1);
-    const uint32_t nshift1 = 4 * e1;
+    // Q8_0 (1536 words of 4 int8 per block): thread t decodes 3 words; 32-lane group
+    // g = t / 32 + 16 i (i = 0..2) takes rows 16 (g / 4) .. + 15, fragment half
+    // (g / 2) % 2, lane half g % 2: lane l of the group word 4 ((g / 2) % 2) +
+    // 2 (g % 2) + l % 2 of row 16 (g / 4) + l / 2.
+    constexpr int NDW = (QT == Q4_0) ? 2 : 3;       // words decoded per thread per step
+    int sraw[NDW], qraw[NDW], bdst[NDW];
+    uint32_t nshift1 = 0;
+    if constexpr (QT == Q4_0) {
+        const int r0 = 16 * (tid >> 6) + ((tid >> 1) & 15), w0 = 2 * ((tid >> 5) & 1) + (tid & 1);
+        const int g1 = tid >> 5;
+        const int r1 = 128 + 16 * (g1 >> 2) + ((tid & 31) >> 1), w1 = 2 * ((g1 >> 1) & 1) + (tid & 1);
+        const int e1 = g1 & 1;
+        sraw[0] = r0 * WROW; qraw[0] = sraw[0] + 4 * w0;
+        sraw[1] = r1 * WROW; qraw[1] = sraw[1] + 4 * w1;
+        bdst[0] = (((r0 >> 5) * 2) * 64 + (w0 >> 1) * 32 + (r0 & 31)) * 16 + 8 * (w0 & 1);
+        bdst[1] = (((r1 >> 5) * 2 + e1) * 64 + (w1 >> 1) * 32 + (r1 & 31)) * 16 + 8 * (w1 & 1);
+        nshift1 = 4 * e1;
+    } else {
+#pragma unroll
+        for (int i = 0; i < NDW; ++i) {
+            const int g = (tid >> 5) + 16 * i;
+            const int q = (g >> 1) & 1, hh = g & 1;
+            const int r = 16 * (g >> 2) + ((tid & 31) >> 1), w = 4 * q + 2 * hh + (tid & 1);
+            sraw[i] = r * WROW;
+            qraw[i] = sraw[i] + 4 * w;
+            bdst[i] = (((r >> 5) * 2 + q) * 64 + hh * 32 + (r & 31)) * 16 + 8 * (tid & 1);
+        }
+    }
 
     f16v_t acc[IT][JT];
 #pragma unroll
@@ -919,29 +937,37 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
         constexpr int SH = (blk * BB + 2) & 3;       // qs start 2 bytes into a dword for even blocks
         const uint8_t *wb = wsm0 + wbuf * WBUF + blk * BB;
         uint8_t *bb = bsm + decltype(bbuf_c)::value * BBUF;
-        const uint32_t d0 = *reinterpret_cast<const uint16_t *>(wb + sraw0);
-        const uint32_t d1 = *reinterpret_cast<const uint16_t *>(wb + sraw1);
-        uint32_t q0, q1;
-        if constexpr (SH == 0) {
-            q0 = *reinterpret_cast<const uint32_t *>(wb + qraw0 + 2);
-            q1 = *reinterpret_cast<const uint32_t *>(wb + qraw1 + 2);
-        } else {
-            const uint32_t *a0 = reinterpret_cast<const uint32_t *>(wb + qraw0);
-            const uint32_t *a1 = reinterpret_cast<const uint32_t *>(wb + qraw1);
-            q0 = __builtin_amdgcn_alignbyte(a0[1], a0[0], SH);
-            q1 = __builtin_amdgcn_alignbyte(a1[1], a1[0], SH);
+        uint32_t d[NDW], qw[NDW];
+#pragma unroll
+        for (int i = 0; i < NDW; ++i) {
+            d[i] = *reinterpret_cast<const uint16_t *>(wb + sraw[i]);
+            if constexpr (SH == 0) {
+                qw[i] = *reinterpret_cast<const uint32_t *>(wb + qraw[i] + 2);
+            } else {
+                const uint32_t *al = reinterpret_cast<const uint32_t *>(wb + qraw[i]);
+                qw[i] = __builtin_amdgcn_alignbyte(al[1], al[0], SH);
+            }
         }
-        const h2_t d20 = as_h2(d0 | (d0 << 16));
-        const h2_t d21 = as_h2(d1 | (d1 << 16));
-        uint32_t lo02, lo13, hi02, hi13;
-        q4_word_decode(q0, d20, lo02, lo13, hi02, hi13);
-        *reinterpret_cast<u2_t *>(bb + bdst0) = u2_t{lo02, lo13};
-        *reinterpret_cast<u2_t *>(bb + bdst0 + 1024) = u2_t{hi02, hi13};
-        const h2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
-        const uint32_t nib = (q1 >> nshift1) & 0x0F0F0F0Fu;
-        const uint32_t p02 = h2_bits((as_h2(magic_pair(nib, SEL_B02)) - off) * d21);
-        const uint32_t p13 = h2_bits((as_h2(magic_pair(nib, SEL_B13)) - off) * d21);
-        *reinterpret_cast<u2_t *>(bb + bdst1) = u2_t{p02, p13};
+        if constexpr (QT == Q4_0) {
+            const h2_t d20 = as_h2(d[0] | (d[0] << 16));
+            const h2_t d21 = as_h2(d[1] | (d[1] << 16));
+            uint32_t lo02, lo13, hi02, hi13;
+            q4_word_decode(qw[0], d20, lo02, lo13, hi02, hi13);
+            *reinterpret_cast<u2_t *>(bb + bdst[0]) = u2_t{lo02, lo13};
+            *reinterpret_cast<u2_t *>(bb + bdst[0] + 1024) = u2_t{hi02, hi13};
+            const h2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
+            const uint32_t nib = (qw[1] >> nshift1) & 0x0F0F0F0Fu;
+            const uint32_t p02 = h2_bits((as_h2(magic_pair(nib, SEL_B02)) - off) * d21);
+            const uint32_t p13 = h2_bits((as_h2(magic_pair(nib, SEL_B13)) - off) * d21);
+            *reinterpret_cast<u2_t *>(bb + bdst[1]) = u2_t{p02, p13};
+        } else {
+#pragma unroll
+            for (int i = 0; i < NDW; ++i) {
+                uint32_t p[2];
+                q8_word_to_h4(qw[i], as_h2(d[i] | (d[i] << 16)), p);
+                *reinterpret_cast<u2_t *>(bb + bdst[i]) = u2_t{p[0], p[1]};
+            }
+        }
     };
 
     h8_t fa[AD][2][IT];  // A fragments [ring slot][k half][tile]
@@ -1274,7 +1300,7 @@ hipError_t launch_w8(const GemmArgs &a, const uint16_t *xh, hipStream_t s) {
 // The cooperative-decode kernel: 256 x 192 tiles; split K for PLAIN / RESIDUAL
 // when the tiles alone would leave CUs idle (any split count; the chunk ranges of
 // the splits differ by at most one chunk).
-template <int EPI>
+template <int QT, int EPI>
 hipError_t launch_coop(const GemmArgs &a, const uint16_t *xh, hipStream_t s) {
     const int tm = (a.T + 255) / 256;
     const int out_per_tile = EPI == EPI_SWIGLU ? 96 : 192;
@@ -1297,29 +1323,38 @@ hipError_t launch_coop(const GemmArgs &a, const uint16_t *xh, hipStream_t s) {
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
-        hipLaunchKernelGGL((gemm_f16_coop_kernel<EPI, true>), dim3(total), dim3(512), 0, s, a.W, xh,
+        hipLaunchKernelGGL((gemm_f16_coop_kernel<QT, EPI, true>), dim3(total), dim3(512), 0, s, a.W, xh,
                            a.Y, a.n, a.k, a.T, tm, tn, splits);
     } else {
-        hipLaunchKernelGGL((gemm_f16_coop_kernel<EPI, false>), dim3(total), dim3(512), 0, s, a.W, xh,
+        hipLaunchKernelGGL((gemm_f16_coop_kernel<QT, EPI, false>), dim3(total), dim3(512), 0, s, a.W, xh,
                            a.Y, a.n, a.k, a.T, tm, tn, splits);
     }
     return hipGetLastError();
 }
 
+template <int QT>
+hipError_t launch_coop_q(const GemmArgs &a, const uint16_t *xh, hipStream_t s) {
+    switch (a.epilogue) {
+    case EPI_PLAIN: return launch_coop<QT, EPI_PLAIN>(a, xh, s);
+    case EPI_RESIDUAL: return launch_coop<QT, EPI_RESIDUAL>(a, xh, s);
+    default: return launch_coop<QT, EPI_SWIGLU>(a, xh, s);
+    }
+}
+
 hipError_t launch_gemm_f16_ws(const GemmArgs &a, void *workspace, hipStream_t s) {
     uint16_t *xh = static_cast<uint16_t *>(workspace);
-    if (a.qtype == Q4_0 && a.T >= 256) {
+    if (a.T >= 256) {
         // The cooperative-decode kernel takes X in A-fragment order.
         const int count = (a.T + 31) / 32 * 32 * (a.k / 8);
-        hipLaunchKernelGGL(x_to_frag_kernel<Q4_0>, dim3((count + 255) / 256), dim3(256), 0, s, a.X, xh,
-                           a.T, a.k, count);
+        if (a.qtype == Q4_0)
+            hipLaunchKernelGGL(x_to_frag_kernel<Q4_0>, dim3((count + 255) / 256), dim3(256), 0, s, a.X,
+                               xh, a.T, a.k, count);
+        else
+            hipLaunchKernelGGL(x_to_frag_kernel<Q8_0>, dim3((count + 255) / 256), dim3(256), 0, s, a.X,
+                               xh, a.T, a.k, count);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        switch (a.epilogue) {
-        case EPI_PLAIN: return launch_coop<EPI_PLAIN>(a, xh, s);
-        case EPI_RESIDUAL: return launch_coop<EPI_RESIDUAL>(a, xh, s);
-        default: return launch_coop<EPI_SWIGLU>(a, xh, s);
-        }
+        return a.qtype == Q4_0 ? launch_coop_q<Q4_0>(a, xh, s) : launch_coop_q<Q8_0>(a, xh, s);
     }
     const int count8 = a.T * (a.k / 8);
     if (a.qtype == Q4_0)

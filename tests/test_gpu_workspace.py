@@ -45,12 +45,13 @@ def test_ws_small_ragged(gpu, qtype, epi, T, n, k):
 
 
 @pytest.mark.parametrize("epi", [PLAIN, RESIDUAL, SWIGLU])
-@pytest.mark.parametrize("T", [1024, 1100])
+@pytest.mark.parametrize("qtype", [Q4_0, Q8_0])
+@pytest.mark.parametrize("T", [256, 1100])
 @pytest.mark.parametrize("n,k", [(17, 256), (300, 768), (1000, 512)])
-def test_ws_long_chunk_tiles(gpu, epi, T, n, k):
-    """T >= 1024 runs the eight-wave 256 x 256 tiling (Q4_0): every output, ragged
-    in T and n, against the full oracle."""
-    run_ws_and_check(gpu, Q4_0, n, k, T, epi, F16, wid=90 + n + T)
+def test_ws_long_chunk_tiles(gpu, qtype, epi, T, n, k):
+    """T >= 256 runs the cooperative-decode 256 x 192 tiling: every output, ragged
+    in T and n (T = 256 is one whole tile), against the full oracle."""
+    run_ws_and_check(gpu, qtype, n, k, T, epi, F16, wid=90 + n + T)
 
 
 @pytest.mark.parametrize("epi", [PLAIN, RESIDUAL, SWIGLU])
