@@ -491,280 +491,6 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
 }
 
 // ---------------------------------------------------------------------------
-// Two waves per SIMD: 8 waves (512 threads) on a 256-row x 256-weight-row tile,
-// laid out 2 (rows) x 4 (weight rows); each wave owns 128 x 64 (4 x 2 MFMA tiles of
-// 32 x 32, 128 accumulators), so a wave fits in 256 registers and the SIMD
-// interleaves two of them: one wave's decode, LDS and staging instructions run
-// while the other's MFMAs occupy the matrix core. Each weight column is decoded by
-// 2 waves (vs the 2 x 2 layout's 2 of 4 waves over 96 columns), at 60 VALU per 16
-// MFMAs per wave. fp16 X only (the workspace path), Q4_0 only (the Q8_0 chunks
-// would not fit in LDS beside the X buffers).
-//
-// Per step s (one 32-k block): A fragments of X(s) and the decoded weights of
-// block s are read straight from LDS into single-buffered registers; X(s+2) and
-// slice s % 8 of the next chunk (rows 32 (s % 8) .. + 31, whole) are stored from a
-// 2-step ring of staging registers; then the 16 MFMAs. A barrier follows every
-// second step. X lives in a ring of four LDS buffers: X(s+2) goes to the buffer
-// X(s-2) left, read in the previous pair of steps; chunk c+1 fills during chunk
-// c's 8 steps, into the buffer chunk c-1 left, and is complete at the barrier
-// after chunk c's last step.
-template <int QT, int EPI, bool SPLIT>
-__global__ __launch_bounds__(512)
-void gemm_f16_w8_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ Xh,
-                        float *__restrict__ Y, int n, int k, int T, int tiles_m, int tiles_n,
-                        int splits) {
-    static_assert(QT == Q4_0, "Q4_0 only");
-    using CT = ChunkTraits<QT>;
-    constexpr int MT = 256, NW = 256;
-    constexpr int BB = CT::BB;
-    constexpr int IT = 4, JT = 2;                   // per wave: 128 rows x 64 weight rows
-    constexpr int U4 = CT::U4;
-    constexpr int WROW = CT::ROW;
-    constexpr int WBUF = NW * WROW + 16;            // +16: decode reads a dword past a row
-    constexpr int NW32 = 2;                         // qs words per lane per block
-    constexpr int PD = 2;                           // staging ring depth (steps)
-    constexpr int XBUF_BYTES = MT * 32 * 2;
-    constexpr int NXB = 4;                          // X buffers: X(s) .. X(s+3)
-    constexpr int LOOP_BYTES = NXB * XBUF_BYTES + 2 * WBUF;
-    constexpr int EPI_BYTES = 8 * 32 * 36 * 4;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[LOOP_BYTES > EPI_BYTES ? LOOP_BYTES : EPI_BYTES];
-    _Float16 (*xs)[MT * 32] = reinterpret_cast<_Float16 (*)[MT * 32]>(smem);
-    uint8_t (*wsm)[WBUF] = reinterpret_cast<uint8_t (*)[WBUF]>(smem + NXB * XBUF_BYTES);
-    static_assert(WBUF % 16 == 0 && XBUF_BYTES % 16 == 0, "16-byte aligned carve-up");
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 2, wn = wave & 3;
-    const int c = lane & 31, h = lane >> 5;
-
-    // Workgroup -> tile, XCD-aware (as in gemm_f16_kernel).
-    const int total = tiles_m * tiles_n * splits;
-    int logical;
-    {
-        const int id = blockIdx.x;
-        const int per = (total + 7) / 8;
-        const int xcd = id & 7, slot = id >> 3;
-        const int full = total - 8 * (per - 1);
-        logical = (xcd < full) ? xcd * per + slot : full * per + (xcd - full) * (per - 1) + slot;
-    }
-    const int tm = logical % tiles_m;
-    const int rest = logical / tiles_m;
-    const int tn = rest % tiles_n;
-    const int split = rest / tiles_n;
-    const int m0 = tm * MT;
-    const int nchunks = k >> 8;
-    const int c_begin = (int)((long)nchunks * split / splits);
-    const int c_end = (int)((long)nchunks * (split + 1) / splits);
-    const int nch = c_end - c_begin;
-    if (nch <= 0) return;
-    const int nsteps = 8 * nch;
-    const uint32_t row_bytes = (uint32_t)(k >> 5) * BB;
-
-    // X staging: thread t copies 16-byte chunk (t & 3) of rows (t >> 2) + 128 i,
-    // i = 0, 1, swizzled as in gemm_f16_kernel (rows (t >> 2) + 128 i share
-    // (row >> 2) & 3).
-    const uint8_t *xbase = reinterpret_cast<const uint8_t *>(Xh) + (size_t)c_begin * 256 * 2;
-    uint32_t xoff[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int t = min(m0 + (tid >> 2) + 128 * i, T - 1);
-        xoff[i] = ((uint32_t)t * (uint32_t)k + 8 * (tid & 3)) * 2;
-    }
-    const int xdst = (tid >> 2) * 32 + (((tid & 3) ^ ((tid >> 4) & 3)) << 3);
-
-    // Weight staging: slice S of a chunk = its rows 32 S .. 32 S + 31, whole (288
-    // 16-byte pieces; thread t < 288 copies piece t: piece t % 9 of slice row t / 9).
-    constexpr int RS = NW / 8;
-    constexpr int SP = RS * U4;
-    static_assert(SP <= 512, "one piece per thread");
-    const bool wvalid = tid < SP;
-    const int wff = wvalid ? tid : 0;
-    const int wrr = wff / U4, wpp = wff % U4;
-    const int wdst = wrr * WROW + 16 * wpp;
-    uint32_t wsrc[8];
-#pragma unroll
-    for (int S = 0; S < 8; ++S) {
-        int gr = f16_weight_row<EPI, NW>(tn, S * RS + wrr, n);
-        gr = gr < 0 ? 0 : gr;
-        wsrc[S] = (uint32_t)gr * row_bytes + 16 * wpp;
-    }
-    const uint8_t *wbase = W + (size_t)c_begin * WROW;
-
-    const int bbase = (wn * JT * 32 + c) * WROW;
-    const int sw = (c >> 2) & 3;
-    const int arow = (wm * IT * 32 + c) * 32;
-    const int aoff[2] = {arow + ((h ^ sw) << 3), arow + (((2 + h) ^ sw) << 3)};
-
-    f16v_t acc[IT][JT];
-#pragma unroll
-    for (int i = 0; i < IT; ++i)
-#pragma unroll
-        for (int j = 0; j < JT; ++j) acc[i][j] = f16v_t{};
-
-    auto fetch_x = [&](int step, u4_t (&dst)[2]) __attribute__((always_inline)) {
-        const uint8_t *xb = xbase + 64 * min(step, nsteps - 1);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) dst[i] = *reinterpret_cast<const u4_t *>(xb + xoff[i]);
-    };
-    auto store_x = [&](int xb, const u4_t (&src)[2]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-            *reinterpret_cast<u4_t *>(&xs[xb][xdst + i * 128 * 32]) = src[i];
-    };
-    auto fetch_slice = [&](int chunk, auto s_c, u4_t &dst) __attribute__((always_inline)) {
-        constexpr int S = decltype(s_c)::value;
-        dst = *reinterpret_cast<const u4_t *>(wbase + (size_t)min(chunk, nch - 1) * WROW + wsrc[S]);
-    };
-    auto store_slice = [&](uint8_t *buf, auto s_c, const u4_t &src) __attribute__((always_inline)) {
-        constexpr int S = decltype(s_c)::value;
-        if (wvalid) *reinterpret_cast<u4_t *>(buf + S * RS * WROW + wdst) = src;
-    };
-    auto load_a = [&](int xb, h8_t (&dst)[IT][2]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < IT; ++i)
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2)
-                dst[i][s2] = *reinterpret_cast<const h8_t *>(&xs[xb][aoff[s2] + i * 32 * 32]);
-    };
-    auto load_decode_b = [&](const uint8_t *wb, auto blk_c, h8_t (&dst)[JT][2]) __attribute__((always_inline)) {
-        constexpr int blk = decltype(blk_c)::value;
-        constexpr int SH = (blk * BB + 2) & 3;
-#pragma unroll
-        for (int j = 0; j < JT; ++j) {
-            const int base = bbase + j * 32 * WROW + blk * BB;
-            const uint32_t d16 = *reinterpret_cast<const uint16_t *>(wb + base);
-            const uint32_t *al = reinterpret_cast<const uint32_t *>(wb + base + 2 + 8 * h - SH);
-            uint32_t q[NW32];
-            if constexpr (SH == 0) {
-                q[0] = al[0];
-                q[1] = al[1];
-            } else {
-                const uint32_t r0 = al[0], r1 = al[1], r2 = al[2];
-                q[0] = __builtin_amdgcn_alignbyte(r1, r0, SH);
-                q[1] = __builtin_amdgcn_alignbyte(r2, r1, SH);
-            }
-            const h2_t d2 = as_h2(d16 | (d16 << 16));
-            uint32_t p[8];
-            q4_word_decode(q[0], d2, p[0], p[1], p[4], p[5]);
-            q4_word_decode(q[1], d2, p[2], p[3], p[6], p[7]);
-            dst[j][0] = __builtin_bit_cast(h8_t, u4_t{p[0], p[1], p[2], p[3]});
-            dst[j][1] = __builtin_bit_cast(h8_t, u4_t{p[4], p[5], p[6], p[7]});
-        }
-    };
-
-    u4_t xh[PD][2];   // X(s+2) .. X(s+PD+1) for the staging writes of steps s .. s+PD-1
-    u4_t wr[PD];      // the slices written by steps s .. s+PD-1
-
-    // ---- prologue: chunk 0, X(0) and X(1) in LDS; the rings hold the first PD
-    // steps' staging data (X(2), X(3); chunk 1 slices 0, 1).
-    {
-        u4_t tmp;
-#define PF_W8_CHUNK0(S)                                           \
-        fetch_slice(0, std::integral_constant<int, S>{}, tmp);    \
-        store_slice(wsm[0], std::integral_constant<int, S>{}, tmp);
-        PF_W8_CHUNK0(0) PF_W8_CHUNK0(1) PF_W8_CHUNK0(2) PF_W8_CHUNK0(3)
-        PF_W8_CHUNK0(4) PF_W8_CHUNK0(5) PF_W8_CHUNK0(6) PF_W8_CHUNK0(7)
-#undef PF_W8_CHUNK0
-        fetch_slice(1, std::integral_constant<int, 0>{}, wr[0]);
-        fetch_slice(1, std::integral_constant<int, 1>{}, wr[1]);
-        u4_t x0[2];
-        fetch_x(0, x0);
-        store_x(0, x0);
-        fetch_x(1, x0);
-        store_x(1, x0);
-        fetch_x(2, xh[0]);
-        fetch_x(3, xh[1]);
-    }
-    __syncthreads();
-
-    for (int ch = 0; ch < nch; ++ch) {
-        auto step_body = [&](auto blk_c) __attribute__((always_inline)) {
-            constexpr int blk = decltype(blk_c)::value;
-            constexpr int P = blk & 1;
-            constexpr int RG = blk % PD;
-            const int s = ch * 8 + blk;
-            h8_t afr[IT][2], bfr[JT][2];
-            load_a(blk & 3, afr);
-            load_decode_b(wsm[ch & 1], std::integral_constant<int, blk>{}, bfr);
-            // staging: X(s+2) -> xs[(s+2) % 4]; slice blk of chunk ch+1
-            store_x((blk + 2) & 3, xh[RG]);
-            fetch_x(s + 2 + PD, xh[RG]);
-            if (ch + 1 < nch) store_slice(wsm[(ch + 1) & 1], std::integral_constant<int, blk>{}, wr[RG]);
-            fetch_slice(ch + 1 + ((blk + PD) >> 3), std::integral_constant<int, (blk + PD) & 7>{}, wr[RG]);
-#pragma unroll
-            for (int j = 0; j < JT; ++j)
-#pragma unroll
-                for (int i = 0; i < IT; ++i) {
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(afr[i][0], bfr[j][0], acc[i][j], 0, 0, 0);
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(afr[i][1], bfr[j][1], acc[i][j], 0, 0, 0);
-                }
-            // One barrier per two steps, so that the two waves of a SIMD can drift
-            // apart within a pair.
-            if constexpr (P == 1) __syncthreads();
-        };
-        step_body(std::integral_constant<int, 0>{});
-        step_body(std::integral_constant<int, 1>{});
-        step_body(std::integral_constant<int, 2>{});
-        step_body(std::integral_constant<int, 3>{});
-        step_body(std::integral_constant<int, 4>{});
-        step_body(std::integral_constant<int, 5>{});
-        step_body(std::integral_constant<int, 6>{});
-        step_body(std::integral_constant<int, 7>{});
-    }
-
-    // ---- epilogue (as gemm_f16_kernel, with the 2 x 4 wave layout).
-    int etid = threadIdx.x;
-    asm volatile("" : "+v"(etid));
-    const int e_lane = etid & 63, e_wave = etid >> 6;
-    const int e_wm = e_wave >> 2, e_wn = e_wave & 3;
-    const int e_c = e_lane & 31, e_h = e_lane >> 5;
-#pragma unroll
-    for (int i = 0; i < IT; ++i) {
-#pragma unroll
-        for (int j = 0; j < JT; ++j) {
-            const int tile_col = (e_wn * JT + j) * 32;
-            const int trow = m0 + e_wm * IT * 32 + i * 32 + 4 * e_h;
-            if constexpr (EPI == EPI_SWIGLU) {
-                float *slot = reinterpret_cast<float *>(smem) + e_wave * (32 * 36);
-                wave_lds_sync();
-#pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4)
-                    *reinterpret_cast<f4_t *>(slot + e_c * 36 + 8 * g4 + 4 * e_h) =
-                        f4_t{acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2],
-                             acc[i][j][4 * g4 + 3]};
-                wave_lds_sync();
-                const int cc = e_lane & 15;
-                const int o = tn * (NW / 2) + (tile_col >> 1) + cc;
-#pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const int q = (e_lane >> 4) + 4 * half;
-                    const f4_t g = *reinterpret_cast<const f4_t *>(slot + cc * 36 + 4 * q);
-                    const f4_t u = *reinterpret_cast<const f4_t *>(slot + (cc + 16) * 36 + 4 * q);
-                    const int t0 = m0 + e_wm * IT * 32 + i * 32 + 4 * q;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (t0 + e < T && o < n) Y[(size_t)(t0 + e) * n + o] = silu_fast(g[e]) * u[e];
-                }
-            } else {
-                const int o = tn * NW + tile_col + e_c;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int t = trow + 8 * (r >> 2) + (r & 3);
-                    if (t < T && o < n) {
-                        float *y = Y + (size_t)t * n + o;
-                        if constexpr (SPLIT || EPI == EPI_RESIDUAL)
-                            atomicAdd(y, acc[i][j][r]);
-                        else
-                            *y = acc[i][j][r];
-                    }
-                }
-            }
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
 // Cooperative decode: 8 waves (512 threads, two per SIMD) on a 256-row x
 // 192-weight-row tile, laid out 4 (rows) x 2 (weight rows); each wave owns 64 x 96
 // (2 x 3 MFMA tiles of 32 x 32, 96 accumulators).
@@ -781,12 +507,14 @@ void gemm_f16_w8_kernel(const uint8_t *__restrict__ W, const uint16_t *__restric
 // Q4_0 and Q8_0 (LDS: four B buffers of 12 KB and two raw chunk buffers of 27 / 51 KB).
 //
 // Per step s (one 32-k block), with one barrier at its end:
-//   (a) read the second half (k 16..31) of step s's B fragments;
-//   (b) the MFMAs of the first half, whose B fragments were read during step s-1;
-//   (c) staging: slice (s+2) % 8 (rows 24 S .. 24 S + 23, whole) of a raw weight
-//       chunk; decode of block s+2 from its raw chunk into B buffer (s+2) % 4;
-//   (d) read the first half of step s+1's B fragments;
-//   (e) the MFMAs of the second half; then load the A fragments of step s+AD.
+//   (a) read the second half (k 16..31) of step s's B fragments, and block s+2's
+//       raw words from its chunk;
+//   (b) the MFMAs of the first half, whose B fragments were read during step s-1,
+//       with the staging of slice (s+2) % 8 (rows 24 S .. 24 S + 23, whole) of a raw
+//       weight chunk;
+//   (c) read the first half of step s+1's B fragments;
+//   (d) the MFMAs of the second half, with the decode of block s+2 into B buffer
+//       (s+2) % 4; then load the A fragments of step s+AD.
 // Decoded B lives in a ring of four LDS buffers; raw chunks take two buffers,
 // chunk c being filled during steps 8c-10 .. 8c-3 and decoded during steps
 // 8c-2 .. 8c+5.
@@ -795,21 +523,25 @@ void gemm_f16_w8_kernel(const uint8_t *__restrict__ W, const uint16_t *__restric
 // (rows 0..127) and one nibble half of another (rows 128..191), so every wave
 // carries the same share. Within each half wave (32 lanes) the stores cover 256
 // contiguous bytes of one fragment half, so they are free of bank conflicts.
-template <int QT, int EPI, bool SPLIT, int AD = 4>
+template <int QT, int EPI, bool SPLIT, int MT = 256, int AD = 2>
 __global__ __launch_bounds__(512)
 void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ Xf,
                           float *__restrict__ Y, int n, int k, int T, int tiles_m, int tiles_n,
                           int splits) {
     using CT = ChunkTraits<QT>;
-    constexpr int MT = 256, NW = 192;
+    static_assert(MT == 256 || MT == 512, "tile: 256 x 192 or 512 x 96");
+    constexpr int NW = MT == 256 ? 192 : 96;        // weight rows per tile
+    constexpr int WN = NW / 96;                     // waves across the weight rows (2 or 1)
     constexpr int BB = CT::BB;                      // 18 / 34
     constexpr int IT = 2, JT = 3;                   // per wave: 64 rows x 96 weight rows
     constexpr int U4 = CT::U4;                      // 9 / 17
     constexpr int WROW = CT::ROW;                   // 144 / 272
     constexpr int WBUF = NW * WROW;                 // raw chunk buffer
-    constexpr int BBUF = NW * 32 * 2;               // B(s): 6 tiles x 2 halves x 64 lanes x 16 B
+    constexpr int BBUF = NW * 32 * 2;               // B(s): NW/32 tiles x 2 halves x 64 lanes x 16 B
     constexpr int NBB = 4;                          // B buffers
     constexpr int PD = 4;                           // weight staging ring depth (steps)
+    static_assert(JT == 3, "the barrier's wait count below assumes JT reads in flight");
+    constexpr int WAITCNT_LGKM_JT = 0xC37F;         // s_waitcnt lgkmcnt(3)
     constexpr int LOOP_BYTES = NBB * BBUF + 2 * WBUF;
     constexpr int EPI_BYTES = 8 * 32 * 36 * 4;
     __shared__ __attribute__((aligned(16))) uint8_t smem[LOOP_BYTES > EPI_BYTES ? LOOP_BYTES : EPI_BYTES];
@@ -821,7 +553,7 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
 
     // Workgroup -> tile, XCD-aware (as in gemm_f16_kernel).
     const int total = tiles_m * tiles_n * splits;
@@ -891,10 +623,30 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
     // g = t / 32 + 16 i (i = 0..2) takes rows 16 (g / 4) .. + 15, fragment half
     // (g / 2) % 2, lane half g % 2: lane l of the group word 4 ((g / 2) % 2) +
     // 2 (g % 2) + l % 2 of row 16 (g / 4) + l / 2.
-    constexpr int NDW = (QT == Q4_0) ? 2 : 3;       // words decoded per thread per step
+    // 512 x 96 tiles (768 units of 4 weights per block): unit = one Q8_0 word, or
+    // one nibble half of a Q4_0 word. 32-lane group g (g = t / 32, and 16 + t / 32
+    // for t < 256) takes rows 16 (g / 4) .. + 15, fragment half (g / 2) % 2 and lane
+    // half g % 2; its lane l the word 2 (g % 2) + l % 2 of that lane half (Q4_0,
+    // nibble half (g / 2) % 2) or 4 ((g / 2) % 2) + 2 (g % 2) + l % 2 (Q8_0), of row
+    // 16 (g / 4) + l / 2.
+    constexpr bool UNITS = NW == 96;
+    constexpr int NDW = UNITS ? 2 : (QT == Q4_0) ? 2 : 3;  // words read per thread per step
     int sraw[NDW], qraw[NDW], bdst[NDW];
-    uint32_t nshift1 = 0;
-    if constexpr (QT == Q4_0) {
+    uint32_t nshift[NDW] = {};
+    const bool has2 = !UNITS || tid < 256;          // second unit (UNITS only; wave-uniform)
+    if constexpr (UNITS) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int g = i == 0 ? (tid >> 5) : 16 + ((tid >> 5) & 7);
+            const int q = (g >> 1) & 1, hh = g & 1;
+            const int r = 16 * (g >> 2) + ((tid & 31) >> 1);
+            const int w = (QT == Q4_0) ? 2 * hh + (tid & 1) : 4 * q + 2 * hh + (tid & 1);
+            sraw[i] = r * WROW;
+            qraw[i] = sraw[i] + 4 * w;
+            bdst[i] = (((r >> 5) * 2 + q) * 64 + hh * 32 + (r & 31)) * 16 + 8 * (tid & 1);
+            nshift[i] = 4 * q;
+        }
+    } else if constexpr (QT == Q4_0) {
         const int r0 = 16 * (tid >> 6) + ((tid >> 1) & 15), w0 = 2 * ((tid >> 5) & 1) + (tid & 1);
         const int g1 = tid >> 5;
         const int r1 = 128 + 16 * (g1 >> 2) + ((tid & 31) >> 1), w1 = 2 * ((g1 >> 1) & 1) + (tid & 1);
@@ -903,7 +655,7 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
         sraw[1] = r1 * WROW; qraw[1] = sraw[1] + 4 * w1;
         bdst[0] = (((r0 >> 5) * 2) * 64 + (w0 >> 1) * 32 + (r0 & 31)) * 16 + 8 * (w0 & 1);
         bdst[1] = (((r1 >> 5) * 2 + e1) * 64 + (w1 >> 1) * 32 + (r1 & 31)) * 16 + 8 * (w1 & 1);
-        nshift1 = 4 * e1;
+        nshift[1] = 4 * e1;
     } else {
 #pragma unroll
         for (int i = 0; i < NDW; ++i) {
@@ -931,43 +683,74 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
         if (wvalid) *reinterpret_cast<u4_t *>(wsm0 + wbuf * WBUF + S * RS * WROW + wdst) = src;
     };
 
-    // Block `blk` (compile-time) of raw chunk buffer `wbuf` -> B buffer `bbuf`.
-    auto decode_block = [&](int wbuf, auto blk_c, auto bbuf_c) __attribute__((always_inline)) {
+    // Block `blk` (compile-time) of raw chunk buffer `wbuf` -> B buffer `bbuf`, in
+    // two parts so that the LDS reads are issued a phase before the math: read_raw
+    // fetches this thread's scales and the dwords holding its qs words; decode_store
+    // aligns, decodes and stores them.
+    struct RawWords {
+        uint32_t d[NDW], lo[NDW], hi[NDW];
+    };
+    auto read_raw = [&](int wbuf, auto blk_c, RawWords &rw) __attribute__((always_inline)) {
         constexpr int blk = decltype(blk_c)::value;
         constexpr int SH = (blk * BB + 2) & 3;       // qs start 2 bytes into a dword for even blocks
         const uint8_t *wb = wsm0 + wbuf * WBUF + blk * BB;
-        uint8_t *bb = bsm + decltype(bbuf_c)::value * BBUF;
-        uint32_t d[NDW], qw[NDW];
 #pragma unroll
         for (int i = 0; i < NDW; ++i) {
-            d[i] = *reinterpret_cast<const uint16_t *>(wb + sraw[i]);
+            rw.d[i] = *reinterpret_cast<const uint16_t *>(wb + sraw[i]);
             if constexpr (SH == 0) {
-                qw[i] = *reinterpret_cast<const uint32_t *>(wb + qraw[i] + 2);
+                rw.lo[i] = *reinterpret_cast<const uint32_t *>(wb + qraw[i] + 2);
             } else {
                 const uint32_t *al = reinterpret_cast<const uint32_t *>(wb + qraw[i]);
-                qw[i] = __builtin_amdgcn_alignbyte(al[1], al[0], SH);
+                rw.lo[i] = al[0];
+                rw.hi[i] = al[1];
             }
         }
-        if constexpr (QT == Q4_0) {
-            const h2_t d20 = as_h2(d[0] | (d[0] << 16));
-            const h2_t d21 = as_h2(d[1] | (d[1] << 16));
+    };
+    auto decode_store = [&](const RawWords &rw, auto blk_c, auto bbuf_c) __attribute__((always_inline)) {
+        constexpr int blk = decltype(blk_c)::value;
+        constexpr int SH = (blk * BB + 2) & 3;
+        uint8_t *bb = bsm + decltype(bbuf_c)::value * BBUF;
+        uint32_t qw[NDW];
+#pragma unroll
+        for (int i = 0; i < NDW; ++i)
+            qw[i] = SH == 0 ? rw.lo[i] : __builtin_amdgcn_alignbyte(rw.hi[i], rw.lo[i], SH);
+        // One unit: 4 weights (Q4_0 nibble half `sh` of word w, or Q8_0 word w) -> 8 bytes.
+        auto unit = [&](int i) __attribute__((always_inline)) {
+            const h2_t d2 = as_h2(rw.d[i] | (rw.d[i] << 16));
+            uint32_t p[2];
+            if constexpr (QT == Q4_0) {
+                const h2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
+                const uint32_t nib = (qw[i] >> nshift[i]) & 0x0F0F0F0Fu;
+                p[0] = h2_bits((as_h2(magic_pair(nib, SEL_B02)) - off) * d2);
+                p[1] = h2_bits((as_h2(magic_pair(nib, SEL_B13)) - off) * d2);
+            } else {
+                q8_word_to_h4(qw[i], d2, p);
+            }
+            *reinterpret_cast<u2_t *>(bb + bdst[i]) = u2_t{p[0], p[1]};
+        };
+        if constexpr (UNITS) {
+            unit(0);
+            if (has2) unit(1);
+        } else if constexpr (QT == Q4_0) {
+            const h2_t d20 = as_h2(rw.d[0] | (rw.d[0] << 16));
             uint32_t lo02, lo13, hi02, hi13;
             q4_word_decode(qw[0], d20, lo02, lo13, hi02, hi13);
             *reinterpret_cast<u2_t *>(bb + bdst[0]) = u2_t{lo02, lo13};
             *reinterpret_cast<u2_t *>(bb + bdst[0] + 1024) = u2_t{hi02, hi13};
-            const h2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
-            const uint32_t nib = (qw[1] >> nshift1) & 0x0F0F0F0Fu;
-            const uint32_t p02 = h2_bits((as_h2(magic_pair(nib, SEL_B02)) - off) * d21);
-            const uint32_t p13 = h2_bits((as_h2(magic_pair(nib, SEL_B13)) - off) * d21);
-            *reinterpret_cast<u2_t *>(bb + bdst[1]) = u2_t{p02, p13};
+            unit(1);
         } else {
 #pragma unroll
             for (int i = 0; i < NDW; ++i) {
                 uint32_t p[2];
-                q8_word_to_h4(qw[i], as_h2(d[i] | (d[i] << 16)), p);
+                q8_word_to_h4(qw[i], as_h2(rw.d[i] | (rw.d[i] << 16)), p);
                 *reinterpret_cast<u2_t *>(bb + bdst[i]) = u2_t{p[0], p[1]};
             }
         }
+    };
+    auto decode_block = [&](int wbuf, auto blk_c, auto bbuf_c) __attribute__((always_inline)) {
+        RawWords rw;
+        read_raw(wbuf, blk_c, rw);
+        decode_store(rw, blk_c, bbuf_c);
     };
 
     h8_t fa[AD][2][IT];  // A fragments [ring slot][k half][tile]
@@ -1052,7 +835,16 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
             constexpr int RG = blk % PD;
             constexpr int RA = blk % AD;
             const int s = ch * 8 + blk;
+            // Scheduling: the first half's MFMAs each carry an LDS read, a global load
+            // or store and a few scalar/vector instructions; the second half's each
+            // carry about six decode instructions and a store. Left to itself the
+            // scheduler pulls MFMAs up against the reads that feed them and leaves the
+            // staging and decode between them. The next step's first-half B reads go
+            // last and stay in flight across the barrier: they feed only this wave's
+            // registers, and the buffer they read is not rewritten before step s+3.
+            RawWords rw;
             load_b(std::integral_constant<int, blk % NBB>{}, std::integral_constant<int, 1>{});
+            read_raw((ch + ((blk + 2) >> 3)) & 1, std::integral_constant<int, (blk + 2) & 7>{}, rw);
             mfma_half(fa[RA], std::integral_constant<int, 0>{});
             {
                 const int wc = ch + 1 + ((blk + 2) >> 3);  // chunk receiving the slice
@@ -1060,12 +852,35 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
                 fetch_slice(ch + 1 + ((blk + PD + 2) >> 3),
                             std::integral_constant<int, (blk + PD + 2) & 7>{}, wr[RG]);
             }
-            decode_block((ch + ((blk + 2) >> 3)) & 1, std::integral_constant<int, (blk + 2) & 7>{},
-                         std::integral_constant<int, (blk + 2) % NBB>{});
-            load_b(std::integral_constant<int, (blk + 1) % NBB>{}, std::integral_constant<int, 0>{});
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);      // LDS read
+            for (int q = 0; q < 6; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
+                __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
+                __builtin_amdgcn_sched_group_barrier(0x006, 3, 0);  // VALU / SALU
+            }
+            __builtin_amdgcn_sched_barrier(0);
             mfma_half(fa[RA], std::integral_constant<int, 1>{});
+            decode_store(rw, std::integral_constant<int, (blk + 2) & 7>{},
+                         std::integral_constant<int, (blk + 2) % NBB>{});
             load_a(s + AD, fa[RA]);
-            __syncthreads();
+            for (int q = 0; q < 6; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);  // VALU
+                __builtin_amdgcn_sched_group_barrier(0x200, 1, 1);  // LDS write
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);  // global load
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            load_b(std::integral_constant<int, (blk + 1) % NBB>{}, std::integral_constant<int, 0>{});
+            // Barrier: every earlier LDS operation of this wave (the decode's and the
+            // staging's stores) is complete; the JT reads just issued may not be.
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM_JT);
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         };
         step_body(std::integral_constant<int, 0>{});
         step_body(std::integral_constant<int, 1>{});
@@ -1077,12 +892,12 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
         step_body(std::integral_constant<int, 7>{});
     }
 
-    // ---- epilogue (as gemm_f16_kernel, with the 4 x 2 wave layout). The loop's
+    // ---- epilogue (as gemm_f16_kernel, with the (8 / WN) x WN wave layout). The loop's
     // last barrier has retired every LDS access of the K loop.
     int etid = threadIdx.x;
     asm volatile("" : "+v"(etid));
     const int e_lane = etid & 63, e_wave = etid >> 6;
-    const int e_wm = e_wave >> 1, e_wn = e_wave & 1;
+    const int e_wm = e_wave / WN, e_wn = e_wave % WN;
     const int e_c = e_lane & 31, e_h = e_lane >> 5;
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
@@ -1268,42 +1083,21 @@ __global__ __launch_bounds__(256) void x_to_frag_kernel(const float *__restrict_
 
 }  // namespace
 
-// The 8-wave kernel: 256 x 256 tiles; split K for PLAIN / RESIDUAL when the
-// tiles alone would leave CUs idle.
-template <int EPI>
-hipError_t launch_w8(const GemmArgs &a, const uint16_t *xh, hipStream_t s) {
-    const int tm = (a.T + 255) / 256;
-    const int out_per_tile = EPI == EPI_SWIGLU ? 128 : 256;
-    const int tn = (a.n + out_per_tile - 1) / out_per_tile;
-    int splits = 1;
-    if constexpr (EPI != EPI_SWIGLU) {
-        const int nchunks = a.k / 256;
-        while (splits < 8 && splits * 2 <= nchunks && tm * tn * splits * 2 <= 256) splits *= 2;
-    }
-    const int total = tm * tn * splits;
-    if (splits > 1) {
-        if constexpr (EPI == EPI_PLAIN) {
-            const int count = a.T * a.n;
-            hipLaunchKernelGGL(zero_fill_kernel, dim3((count + 255) / 256), dim3(256), 0, s, a.Y, count);
-            const hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
-        }
-        hipLaunchKernelGGL((gemm_f16_w8_kernel<Q4_0, EPI, true>), dim3(total), dim3(512), 0, s, a.W, xh,
-                           a.Y, a.n, a.k, a.T, tm, tn, splits);
-    } else {
-        hipLaunchKernelGGL((gemm_f16_w8_kernel<Q4_0, EPI, false>), dim3(total), dim3(512), 0, s, a.W,
-                           xh, a.Y, a.n, a.k, a.T, tm, tn, splits);
-    }
-    return hipGetLastError();
-}
+#ifndef PF_COOP_T512
+#define PF_COOP_T512 512
+#endif
+constexpr int COOP_T512 = PF_COOP_T512;  // smallest T that takes the 512 x 96 tiles
 
-// The cooperative-decode kernel: 256 x 192 tiles; split K for PLAIN / RESIDUAL
+// The cooperative-decode kernel: 256 x 192 tiles, or 512 x 96 (each weight block
+// decoded once per 512 token rows instead of per 256: half the decode and weight
+// staging per output, at twice the X reads from L2). Split K for PLAIN / RESIDUAL
 // when the tiles alone would leave CUs idle (any split count; the chunk ranges of
 // the splits differ by at most one chunk).
-template <int QT, int EPI>
+template <int QT, int EPI, int MT>
 hipError_t launch_coop(const GemmArgs &a, const uint16_t *xh, hipStream_t s) {
-    const int tm = (a.T + 255) / 256;
-    const int out_per_tile = EPI == EPI_SWIGLU ? 96 : 192;
+    constexpr int NW = MT == 256 ? 192 : 96;
+    const int tm = (a.T + MT - 1) / MT;
+    const int out_per_tile = EPI == EPI_SWIGLU ? NW / 2 : NW;
     const int tn = (a.n + out_per_tile - 1) / out_per_tile;
     int splits = 1;
     if constexpr (EPI != EPI_SWIGLU) {
@@ -1323,22 +1117,27 @@ hipError_t launch_coop(const GemmArgs &a, const uint16_t *xh, hipStream_t s) {
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
-        hipLaunchKernelGGL((gemm_f16_coop_kernel<QT, EPI, true>), dim3(total), dim3(512), 0, s, a.W, xh,
-                           a.Y, a.n, a.k, a.T, tm, tn, splits);
+        hipLaunchKernelGGL((gemm_f16_coop_kernel<QT, EPI, true, MT>), dim3(total), dim3(512), 0, s, a.W,
+                           xh, a.Y, a.n, a.k, a.T, tm, tn, splits);
     } else {
-        hipLaunchKernelGGL((gemm_f16_coop_kernel<QT, EPI, false>), dim3(total), dim3(512), 0, s, a.W, xh,
-                           a.Y, a.n, a.k, a.T, tm, tn, splits);
+        hipLaunchKernelGGL((gemm_f16_coop_kernel<QT, EPI, false, MT>), dim3(total), dim3(512), 0, s, a.W,
+                           xh, a.Y, a.n, a.k, a.T, tm, tn, splits);
     }
     return hipGetLastError();
 }
 
+template <int QT, int MT>
+hipError_t launch_coop_e(const GemmArgs &a, const uint16_t *xh, hipStream_t s) {
+    switch (a.epilogue) {
+    case EPI_PLAIN: return launch_coop<QT, EPI_PLAIN, MT>(a, xh, s);
+    case EPI_RESIDUAL: return launch_coop<QT, EPI_RESIDUAL, MT>(a, xh, s);
+    default: return launch_coop<QT, EPI_SWIGLU, MT>(a, xh, s);
+    }
+}
+
 template <int QT>
 hipError_t launch_coop_q(const GemmArgs &a, const uint16_t *xh, hipStream_t s) {
-    switch (a.epilogue) {
-    case EPI_PLAIN: return launch_coop<QT, EPI_PLAIN>(a, xh, s);
-    case EPI_RESIDUAL: return launch_coop<QT, EPI_RESIDUAL>(a, xh, s);
-    default: return launch_coop<QT, EPI_SWIGLU>(a, xh, s);
-    }
+    return a.T >= COOP_T512 ? launch_coop_e<QT, 512>(a, xh, s) : launch_coop_e<QT, 256>(a, xh, s);
 }
 
 hipError_t launch_gemm_f16_ws(const GemmArgs &a, void *workspace, hipStream_t s) {
@@ -1363,16 +1162,6 @@ hipError_t launch_gemm_f16_ws(const GemmArgs &a, void *workspace, hipStream_t s)
         hipLaunchKernelGGL(x_to_f16_kernel<Q8_0>, dim3((count8 + 255) / 256), dim3(256), 0, s, a.X, xh, count8);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // The 8-wave kernel's 256 x 256 tiles pay off once there are enough of them to
-    // fill the CUs several times over (measured: +16 % at T = 2048 on the gate/up
-    // shape; at T = 512 its 192 tiles leave a quarter of the CUs idle).
-    if (a.qtype == Q4_0 && a.T >= 1024) {
-        switch (a.epilogue) {
-        case EPI_PLAIN: return launch_w8<EPI_PLAIN>(a, xh, s);
-        case EPI_RESIDUAL: return launch_w8<EPI_RESIDUAL>(a, xh, s);
-        default: return launch_w8<EPI_SWIGLU>(a, xh, s);
-        }
-    }
     return a.qtype == Q4_0 ? launch_q<Q4_0>(a, xh, s) : launch_q<Q8_0>(a, xh, s);
 }
 
