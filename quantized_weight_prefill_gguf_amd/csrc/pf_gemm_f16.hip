@@ -320,17 +320,31 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
     // 0 .. PD-1 (chunk 1 slices 2 .. PD+1), the raw weight words of steps 0 and 1,
     // and the A and decoded B fragments of step 0.
     {
-        u4_t tmp[NPT];
-#define PF_CHUNK0_SLICE(S)                                           \
-        fetch_slice(0, std::integral_constant<int, S>{}, tmp);       \
-        store_slice(wsm[0], std::integral_constant<int, S>{}, tmp);
-        PF_CHUNK0_SLICE(0) PF_CHUNK0_SLICE(1) PF_CHUNK0_SLICE(2) PF_CHUNK0_SLICE(3)
-        PF_CHUNK0_SLICE(4) PF_CHUNK0_SLICE(5) PF_CHUNK0_SLICE(6) PF_CHUNK0_SLICE(7)
-#undef PF_CHUNK0_SLICE
-        fetch_slice(1, std::integral_constant<int, 0>{}, tmp);
-        if (nch > 1) store_slice(wsm[1], std::integral_constant<int, 0>{}, tmp);
-        fetch_slice(1, std::integral_constant<int, 1>{}, tmp);
-        if (nch > 1) store_slice(wsm[1], std::integral_constant<int, 1>{}, tmp);
+        // All ten slice loads are issued before the first store (one memory round
+        // trip, not ten in a row).
+        u4_t tmp[10][NPT];
+        fetch_slice(0, std::integral_constant<int, 0>{}, tmp[0]);
+        fetch_slice(0, std::integral_constant<int, 1>{}, tmp[1]);
+        fetch_slice(0, std::integral_constant<int, 2>{}, tmp[2]);
+        fetch_slice(0, std::integral_constant<int, 3>{}, tmp[3]);
+        fetch_slice(0, std::integral_constant<int, 4>{}, tmp[4]);
+        fetch_slice(0, std::integral_constant<int, 5>{}, tmp[5]);
+        fetch_slice(0, std::integral_constant<int, 6>{}, tmp[6]);
+        fetch_slice(0, std::integral_constant<int, 7>{}, tmp[7]);
+        fetch_slice(1, std::integral_constant<int, 0>{}, tmp[8]);
+        fetch_slice(1, std::integral_constant<int, 1>{}, tmp[9]);
+        store_slice(wsm[0], std::integral_constant<int, 0>{}, tmp[0]);
+        store_slice(wsm[0], std::integral_constant<int, 1>{}, tmp[1]);
+        store_slice(wsm[0], std::integral_constant<int, 2>{}, tmp[2]);
+        store_slice(wsm[0], std::integral_constant<int, 3>{}, tmp[3]);
+        store_slice(wsm[0], std::integral_constant<int, 4>{}, tmp[4]);
+        store_slice(wsm[0], std::integral_constant<int, 5>{}, tmp[5]);
+        store_slice(wsm[0], std::integral_constant<int, 6>{}, tmp[6]);
+        store_slice(wsm[0], std::integral_constant<int, 7>{}, tmp[7]);
+        if (nch > 1) {
+            store_slice(wsm[1], std::integral_constant<int, 0>{}, tmp[8]);
+            store_slice(wsm[1], std::integral_constant<int, 1>{}, tmp[9]);
+        }
         fetch_slice(1, std::integral_constant<int, 2>{}, wr[0]);
         fetch_slice(1, std::integral_constant<int, 3>{}, wr[1]);
         fetch_slice(1, std::integral_constant<int, 4>{}, wr[2]);
@@ -491,38 +505,38 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
 }
 
 // ---------------------------------------------------------------------------
-// Cooperative decode: 8 waves (512 threads, two per SIMD) on a 256-row x
-// 192-weight-row tile, laid out 4 (rows) x 2 (weight rows); each wave owns 64 x 96
-// (2 x 3 MFMA tiles of 32 x 32, 96 accumulators).
+// Cooperative decode: 8 waves (512 threads, two per SIMD) on a tile of MT token
+// rows x NW weight rows: 256 x 192 (waves 4 x 2) or 512 x 96 (waves 8 x 1). Either
+// way each wave owns 64 x 96 outputs (2 x 3 MFMA tiles of 32 x 32, 96 accumulators).
 //  - B: every weight block of the tile is decoded once per workgroup, by all 512
 //    threads, into an fp16 tile in LDS kept in B-fragment order, so that a wave
 //    reads a B fragment with one 16-byte LDS load per lane (vs decoding in each
-//    wave the columns it uses: 4 times the decode work in this layout).
+//    wave the columns it uses: 4 or 8 times the decode work). The 512 x 96 tile
+//    decodes each block once per 512 token rows.
 //  - A: X comes from the workspace already in A-fragment order (x_to_frag_kernel),
 //    so each wave loads its A fragments straight from global memory, one 16-byte
-//    load per lane and fragment, AD (4) steps ahead into a ring of registers. X thus
-//    costs no LDS traffic at all, which leaves the LDS to the B fragments, the
-//    decode's stores and the raw weight chunks (measured: staging X through LDS and
-//    reading it back cost as much as the decode).
-// Q4_0 and Q8_0 (LDS: four B buffers of 12 KB and two raw chunk buffers of 27 / 51 KB).
+//    load per lane and fragment, AD steps ahead into a ring of registers. X thus
+//    costs no LDS traffic at all (measured: staging X through LDS and reading it
+//    back cost as much as the decode).
+// LDS: four B buffers of NW x 64 bytes and two raw chunk buffers of NW x 144 (Q4_0)
+// or NW x 272 (Q8_0) bytes.
 //
 // Per step s (one 32-k block), with one barrier at its end:
 //   (a) read the second half (k 16..31) of step s's B fragments, and block s+2's
 //       raw words from its chunk;
 //   (b) the MFMAs of the first half, whose B fragments were read during step s-1,
-//       with the staging of slice (s+2) % 8 (rows 24 S .. 24 S + 23, whole) of a raw
-//       weight chunk;
-//   (c) read the first half of step s+1's B fragments;
-//   (d) the MFMAs of the second half, with the decode of block s+2 into B buffer
-//       (s+2) % 4; then load the A fragments of step s+AD.
+//       with the staging of slice (s+2) % 8 (NW / 8 whole rows) of a raw weight chunk;
+//   (c) the MFMAs of the second half, with the decode of block s+2 into B buffer
+//       (s+2) % 4, and the A loads of step s+AD;
+//   (d) read the first half of step s+1's B fragments, then the barrier.
 // Decoded B lives in a ring of four LDS buffers; raw chunks take two buffers,
 // chunk c being filled during steps 8c-10 .. 8c-3 and decoded during steps
 // 8c-2 .. 8c+5.
 //
-// Decode assignment (768 qs words per block): each thread decodes one word whole
-// (rows 0..127) and one nibble half of another (rows 128..191), so every wave
-// carries the same share. Within each half wave (32 lanes) the stores cover 256
-// contiguous bytes of one fragment half, so they are free of bank conflicts.
+// Decode assignment: 256 x 192 tiles give each thread one Q4_0 word whole and one
+// nibble half of another, or three Q8_0 words; 512 x 96 tiles give each thread
+// one or two units of 4 weights. Within each half wave (32 lanes) the stores cover
+// 256 contiguous bytes of one fragment half, so they are free of bank conflicts.
 template <int QT, int EPI, bool SPLIT, int MT = 256, int AD = 2>
 __global__ __launch_bounds__(512)
 void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ Xf,
@@ -784,17 +798,31 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
     // blocks 0 and 1 decoded; the first half of step 0's B fragments. The rings hold
     // chunk 1 slices 2 .. PD+1 and the A fragments of steps 0 .. AD-1.
     {
-        u4_t tmp;
-#define PF_COOP_CHUNK0(S)                                         \
-        fetch_slice(0, std::integral_constant<int, S>{}, tmp);    \
-        store_slice(0, std::integral_constant<int, S>{}, tmp);
-        PF_COOP_CHUNK0(0) PF_COOP_CHUNK0(1) PF_COOP_CHUNK0(2) PF_COOP_CHUNK0(3)
-        PF_COOP_CHUNK0(4) PF_COOP_CHUNK0(5) PF_COOP_CHUNK0(6) PF_COOP_CHUNK0(7)
-#undef PF_COOP_CHUNK0
-        fetch_slice(1, std::integral_constant<int, 0>{}, tmp);
-        if (nch > 1) store_slice(1, std::integral_constant<int, 0>{}, tmp);
-        fetch_slice(1, std::integral_constant<int, 1>{}, tmp);
-        if (nch > 1) store_slice(1, std::integral_constant<int, 1>{}, tmp);
+        // All ten slice loads are issued before the first store, so the prologue
+        // waits for one memory round trip rather than ten in a row.
+        u4_t tmp[10];
+        fetch_slice(0, std::integral_constant<int, 0>{}, tmp[0]);
+        fetch_slice(0, std::integral_constant<int, 1>{}, tmp[1]);
+        fetch_slice(0, std::integral_constant<int, 2>{}, tmp[2]);
+        fetch_slice(0, std::integral_constant<int, 3>{}, tmp[3]);
+        fetch_slice(0, std::integral_constant<int, 4>{}, tmp[4]);
+        fetch_slice(0, std::integral_constant<int, 5>{}, tmp[5]);
+        fetch_slice(0, std::integral_constant<int, 6>{}, tmp[6]);
+        fetch_slice(0, std::integral_constant<int, 7>{}, tmp[7]);
+        fetch_slice(1, std::integral_constant<int, 0>{}, tmp[8]);
+        fetch_slice(1, std::integral_constant<int, 1>{}, tmp[9]);
+        store_slice(0, std::integral_constant<int, 0>{}, tmp[0]);
+        store_slice(0, std::integral_constant<int, 1>{}, tmp[1]);
+        store_slice(0, std::integral_constant<int, 2>{}, tmp[2]);
+        store_slice(0, std::integral_constant<int, 3>{}, tmp[3]);
+        store_slice(0, std::integral_constant<int, 4>{}, tmp[4]);
+        store_slice(0, std::integral_constant<int, 5>{}, tmp[5]);
+        store_slice(0, std::integral_constant<int, 6>{}, tmp[6]);
+        store_slice(0, std::integral_constant<int, 7>{}, tmp[7]);
+        if (nch > 1) {
+            store_slice(1, std::integral_constant<int, 0>{}, tmp[8]);
+            store_slice(1, std::integral_constant<int, 1>{}, tmp[9]);
+        }
         // Ring loads in the order the loop issues them (per step: the weight slice,
         // then the A fragments), so that the wait counts the compiler derives at the
         // loop head are the steady-state ones rather than a merge of two orders.
@@ -1103,9 +1131,14 @@ hipError_t launch_coop(const GemmArgs &a, const uint16_t *xh, hipStream_t s) {
     if constexpr (EPI != EPI_SWIGLU) {
         const int nchunks = a.k / 256;
         const int tiles = tm * tn;
+        // Fill the CUs, but give every split at least 5 chunks: a split's prologue,
+        // its fp32 atomics and the zero fill cost more than the parallelism buys
+        // below that (measured: k = 4096 at n = 4096 runs 10 % faster with 3 splits
+        // than with 5; k = 12288 wants 5).
         if (tiles < 256) {
             splits = 256 / tiles;
-            if (splits > nchunks) splits = nchunks;
+            const int by_k = nchunks / 5 > 1 ? nchunks / 5 : 1;
+            if (splits > by_k) splits = by_k;
             if (splits > 16) splits = 16;
         }
     }

@@ -121,3 +121,13 @@ def test_ws_workload4_long_chunk(gpu):
     run_ws_and_check(gpu, Q8_0, 4096, 12288, 2048, RESIDUAL, F16, wid=4, samples=8192, X=Y)
     run_ws_and_check(gpu, Q4_0, 4096, 4096, 2048, PLAIN, F16, wid=4, samples=8192,
                      row_scale=True)
+
+
+@pytest.mark.parametrize("epi", [PLAIN, RESIDUAL])
+@pytest.mark.parametrize("qtype", [Q4_0, Q8_0])
+def test_ws_split_k_narrow(gpu, qtype, epi):
+    """Narrow n with long k splits k across workgroups (fp32 atomics; PLAIN zero-fills
+    first): 4096^2 at T = 512 on sampled outputs, and a ragged 1000 x 3072 at T = 300
+    on every output."""
+    run_ws_and_check(gpu, qtype, 4096, 4096, 512, epi, F16, wid=120 + epi, samples=4096)
+    run_ws_and_check(gpu, qtype, 1000, 3072, 300, epi, F16, wid=130 + epi)
