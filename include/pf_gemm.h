@@ -110,19 +110,24 @@ int pf_gemm(int qtype, const void *W_blocks, int64_t n, int64_t k, const float *
 int pf_gemm_path(int qtype, const void *W_blocks, int64_t n, int64_t k, const float *X,
                  int64_t T, float *Y, int epilogue, int leg, void *stream, int path);
 
-/* Workspace bytes pf_gemm_ws needs for these sizes: ceil(T / 32) * 32 * k * 2 when it
- * runs the f16 leg's matrix-core GEMM (room for X rounded to binary16, T padded to
- * whole 32-row tiles), 0 when it runs a kernel
- * that needs none (the f32 leg, the GEMV, T == 0), or -PF_E_* for arguments pf_gemm
- * would refuse. Host-only; touches no GPU state. */
+/* Workspace bytes pf_gemm_ws needs for these sizes, or -PF_E_* for arguments pf_gemm
+ * would refuse. Host-only; touches no GPU state.
+ *  - 0 when pf_gemm_ws runs a kernel that needs none (the f32 leg, the GEMV, T == 0);
+ *  - the f16 leg's matrix-core GEMM: X_b = ceil(T / 32) * 32 * k * 2 (X rounded to
+ *    binary16, T padded to whole 32-row tiles);
+ *  - and where that GEMM splits k across S workgroups (PLAIN or RESIDUAL, T >= 256,
+ *    too few output tiles to fill the chip): ceil(X_b / 256) * 256 + S * ceil(T * n / 4)
+ *    * 16, room for S blocks of [T][n] f32 partial sums. */
 int64_t pf_workspace_bytes(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int leg);
 
 /* pf_gemm with a caller workspace. On the f16 leg's matrix-core GEMM, X is first
  * rounded to binary16 once, into the workspace, and the GEMM then streams that copy
  * instead of rounding X again in every tile. The operands (RNE_fp16(x) and the
  * decoded weights) and the accumulation are the same as pf_gemm's, so the result is
- * pf_gemm's, bit for bit wherever pf_gemm itself is deterministic (it is not where
- * it splits k across workgroups, whose fp32 atomic adds land in any order).
+ * pf_gemm's, bit for bit wherever neither splits k across workgroups. Where this
+ * GEMM splits k (T >= 256), each split stores its partial sums in the workspace and
+ * a second kernel adds R (RESIDUAL), then the splits in order: the result is
+ * deterministic (pf_gemm's splits add with fp32 atomics, in any order).
  *  workspace        device, owned by the caller, 16-byte aligned, at least
  *                   pf_workspace_bytes() bytes, not overlapping W, X or Y. Its
  *                   contents on entry are ignored and undefined on return. May be

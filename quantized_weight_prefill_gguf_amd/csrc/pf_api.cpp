@@ -44,9 +44,11 @@ int check_sizes(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int le
 }
 
 // Bytes of workspace the f16 leg's GEMM takes (X as binary16, T rounded up to a
-// multiple of 32 for the fragment-ordered copy), else 0.
-int64_t ws_need(int64_t k, int64_t T, int leg, int use) {
-    return (use == PF_PATH_GEMM && leg == PF_LEG_F16) ? (T + 31) / 32 * 32 * k * 2 : 0;
+// multiple of 32 for the fragment-ordered copy, plus the partial sums of a K split),
+// else 0.
+int64_t ws_need(int64_t n, int64_t k, int64_t T, int epilogue, int leg, int use) {
+    return (use == PF_PATH_GEMM && leg == PF_LEG_F16) ? pf::f16_ws_bytes((int)T, (int)n, (int)k, epilogue)
+                                                      : 0;
 }
 
 int gemm_impl(int qtype, const void *W, int64_t n, int64_t k, const float *X, int64_t T, float *Y,
@@ -64,7 +66,7 @@ int gemm_impl(int qtype, const void *W, int64_t n, int64_t k, const float *X, in
     const int64_t x_bytes = T * k * 4, y_bytes = T * n * 4;
     if (overlap(Y, y_bytes, X, x_bytes) || overlap(Y, y_bytes, W, w_bytes)) return PF_E_ALIAS;
     const int use = path == PF_PATH_AUTO ? (T <= PF_GEMV_MAX_T ? PF_PATH_GEMV : PF_PATH_GEMM) : path;
-    const int64_t need = with_ws ? ws_need(k, T, leg, use) : 0;
+    const int64_t need = with_ws ? ws_need(n, k, T, epilogue, leg, use) : 0;
     if (need > 0) {
         if (!ws || ws_bytes < need || !aligned16(ws)) return PF_E_WORKSPACE;
         if (overlap(ws, need, W, w_bytes) || overlap(ws, need, X, x_bytes) ||
@@ -126,7 +128,7 @@ int64_t pf_workspace_bytes(int qtype, int64_t n, int64_t k, int64_t T, int epilo
     const int st = check_sizes(qtype, n, k, T, epilogue, leg, &n_w);
     if (st != PF_OK) return -st;
     if (T == 0) return 0;
-    return ws_need(k, T, leg, T <= PF_GEMV_MAX_T ? PF_PATH_GEMV : PF_PATH_GEMM);
+    return ws_need(n, k, T, epilogue, leg, T <= PF_GEMV_MAX_T ? PF_PATH_GEMV : PF_PATH_GEMM);
 }
 
 int pf_gemm_path(int qtype, const void *W_blocks, int64_t n, int64_t k, const float *X,

@@ -540,8 +540,8 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
 template <int QT, int EPI, bool SPLIT, int MT = 256, int AD = 2>
 __global__ __launch_bounds__(512)
 void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ Xf,
-                          float *__restrict__ Y, int n, int k, int T, int tiles_m, int tiles_n,
-                          int splits) {
+                          float *__restrict__ Y, float *__restrict__ Ps, long pstride, int n,
+                          int k, int T, int tiles_m, int tiles_n, int splits) {
     using CT = ChunkTraits<QT>;
     static_assert(MT == 256 || MT == 512, "tile: 256 x 192 or 512 x 96");
     constexpr int NW = MT == 256 ? 192 : 96;        // weight rows per tile
@@ -956,18 +956,60 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
                 }
             } else {
                 const int o = tn * NW + tile_col + e_c;
+                if constexpr (SPLIT) {
+                    // This split's partial sums, [T][n] at Ps + split * pstride; the
+                    // sum kernel adds the splits (and R) in a fixed order.
+                    float *const pb = Ps + (size_t)split * pstride;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int t = trow + 8 * (r >> 2) + (r & 3);
-                    if (t < T && o < n) {
-                        float *y = Y + (size_t)t * n + o;
-                        if constexpr (SPLIT || EPI == EPI_RESIDUAL)
-                            atomicAdd(y, acc[i][j][r]);
-                        else
-                            *y = acc[i][j][r];
+                    for (int r = 0; r < 16; ++r) {
+                        const int t = trow + 8 * (r >> 2) + (r & 3);
+                        if (t < T && o < n) pb[(size_t)t * n + o] = acc[i][j][r];
+                    }
+                } else if constexpr (EPI == EPI_RESIDUAL) {
+                    // One writer per element: a plain read of R, then R + acc.
+                    float rv[16];
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int t = trow + 8 * (r >> 2) + (r & 3);
+                        rv[r] = (t < T && o < n) ? Y[(size_t)t * n + o] : 0.f;
+                    }
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int t = trow + 8 * (r >> 2) + (r & 3);
+                        if (t < T && o < n) Y[(size_t)t * n + o] = rv[r] + acc[i][j][r];
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int t = trow + 8 * (r >> 2) + (r & 3);
+                        if (t < T && o < n) Y[(size_t)t * n + o] = acc[i][j][r];
                     }
                 }
             }
+        }
+    }
+}
+
+// Y = [R +] P_0 + P_1 + ... + P_{splits-1}, element by element in that order: the
+// cooperative kernel's split-K partial sums, [T][n] each, pstride floats apart
+// (pstride a multiple of 4). Four elements per thread; the thread past the last
+// whole quad takes the 1-3 left over.
+template <int EPI>
+__global__ __launch_bounds__(256) void split_sum_kernel(const float *__restrict__ Ps,
+                                                        float *__restrict__ Y, long count,
+                                                        long pstride, int splits) {
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    const long quads = count >> 2;
+    if (i < quads) {
+        f4_t a = EPI == EPI_RESIDUAL ? reinterpret_cast<const f4_t *>(Y)[i] : f4_t{0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < splits; ++s)
+            a += reinterpret_cast<const f4_t *>(Ps + (size_t)s * pstride)[i];
+        reinterpret_cast<f4_t *>(Y)[i] = a;
+    } else if (i == quads) {
+        for (long e = 4 * quads; e < count; ++e) {
+            float a = EPI == EPI_RESIDUAL ? Y[e] : 0.f;
+            for (int s = 0; s < splits; ++s) a += Ps[(size_t)s * pstride + e];
+            Y[e] = a;
         }
     }
 }
@@ -1116,51 +1158,70 @@ __global__ __launch_bounds__(256) void x_to_frag_kernel(const float *__restrict_
 #endif
 constexpr int COOP_T512 = PF_COOP_T512;  // smallest T that takes the 512 x 96 tiles
 
+// Split count of the cooperative-decode kernel. PLAIN / RESIDUAL split K when the
+// tiles alone would leave CUs idle (any split count; the chunk ranges of the splits
+// differ by at most one chunk), but every split keeps at least 5 chunks: a split's
+// prologue and the partial-sum traffic cost more than the parallelism buys below
+// that (measured: k = 4096 at n = 4096 runs 10 % faster with 3 splits than with 5;
+// k = 12288 wants 5). SwiGLU never splits.
+static int coop_splits(int T, int n, int k, int epilogue) {
+    if (epilogue == EPI_SWIGLU) return 1;
+    const int MT = T >= COOP_T512 ? 512 : 256;
+    const int NW = MT == 256 ? 192 : 96;
+    const int tiles = ((T + MT - 1) / MT) * ((n + NW - 1) / NW);
+    if (tiles >= 256) return 1;
+    int splits = 256 / tiles;
+    const int by_k = (k / 256) / 5 > 1 ? (k / 256) / 5 : 1;
+    if (splits > by_k) splits = by_k;
+    if (splits > 16) splits = 16;
+    return splits;
+}
+
+// Byte offset of the partial sums in the workspace, and the floats between splits.
+static int64_t ws_x_bytes(int T, int k) { return ((int64_t)(T + 31) / 32 * 32 * k * 2 + 255) / 256 * 256; }
+static int64_t ws_pstride(int T, int n) { return ((int64_t)T * n + 3) / 4 * 4; }
+
+int64_t f16_ws_bytes(int T, int n, int k, int epilogue) {
+    const int64_t xb = (int64_t)(T + 31) / 32 * 32 * k * 2;
+    if (T < 256) return xb;
+    const int splits = coop_splits(T, n, k, epilogue);
+    return splits > 1 ? ws_x_bytes(T, k) + (int64_t)splits * ws_pstride(T, n) * 4 : xb;
+}
+
 // The cooperative-decode kernel: 256 x 192 tiles, or 512 x 96 (each weight block
 // decoded once per 512 token rows instead of per 256: half the decode and weight
-// staging per output, at twice the X reads from L2). Split K for PLAIN / RESIDUAL
-// when the tiles alone would leave CUs idle (any split count; the chunk ranges of
-// the splits differ by at most one chunk).
+// staging per output, at twice the X reads from L2). A K split writes partial sums
+// into the workspace behind the fp16 X copy, and split_sum_kernel adds them.
 template <int QT, int EPI, int MT>
-hipError_t launch_coop(const GemmArgs &a, const uint16_t *xh, hipStream_t s) {
+hipError_t launch_coop(const GemmArgs &a, uint16_t *xh, hipStream_t s) {
     constexpr int NW = MT == 256 ? 192 : 96;
     const int tm = (a.T + MT - 1) / MT;
     const int out_per_tile = EPI == EPI_SWIGLU ? NW / 2 : NW;
     const int tn = (a.n + out_per_tile - 1) / out_per_tile;
-    int splits = 1;
-    if constexpr (EPI != EPI_SWIGLU) {
-        const int nchunks = a.k / 256;
-        const int tiles = tm * tn;
-        // Fill the CUs, but give every split at least 5 chunks: a split's prologue,
-        // its fp32 atomics and the zero fill cost more than the parallelism buys
-        // below that (measured: k = 4096 at n = 4096 runs 10 % faster with 3 splits
-        // than with 5; k = 12288 wants 5).
-        if (tiles < 256) {
-            splits = 256 / tiles;
-            const int by_k = nchunks / 5 > 1 ? nchunks / 5 : 1;
-            if (splits > by_k) splits = by_k;
-            if (splits > 16) splits = 16;
-        }
-    }
+    const int splits = coop_splits(a.T, a.n, a.k, EPI);
     const int total = tm * tn * splits;
     if (splits > 1) {
-        if constexpr (EPI == EPI_PLAIN) {
-            const int count = a.T * a.n;
-            hipLaunchKernelGGL(zero_fill_kernel, dim3((count + 255) / 256), dim3(256), 0, s, a.Y, count);
-            const hipError_t e = hipGetLastError();
+        if constexpr (EPI != EPI_SWIGLU) {
+            float *ps = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(xh) + ws_x_bytes(a.T, a.k));
+            const long pstride = (long)ws_pstride(a.T, a.n);
+            hipLaunchKernelGGL((gemm_f16_coop_kernel<QT, EPI, true, MT>), dim3(total), dim3(512), 0, s,
+                               a.W, xh, a.Y, ps, pstride, a.n, a.k, a.T, tm, tn, splits);
+            hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
+            const long count = (long)a.T * a.n;
+            const long threads = count / 4 + 1;
+            hipLaunchKernelGGL(split_sum_kernel<EPI>, dim3((unsigned)((threads + 255) / 256)), dim3(256),
+                               0, s, ps, a.Y, count, pstride, splits);
         }
-        hipLaunchKernelGGL((gemm_f16_coop_kernel<QT, EPI, true, MT>), dim3(total), dim3(512), 0, s, a.W,
-                           xh, a.Y, a.n, a.k, a.T, tm, tn, splits);
     } else {
         hipLaunchKernelGGL((gemm_f16_coop_kernel<QT, EPI, false, MT>), dim3(total), dim3(512), 0, s, a.W,
-                           xh, a.Y, a.n, a.k, a.T, tm, tn, splits);
+                           xh, a.Y, nullptr, 0L, a.n, a.k, a.T, tm, tn, splits);
     }
     return hipGetLastError();
 }
 
 template <int QT, int MT>
-hipError_t launch_coop_e(const GemmArgs &a, const uint16_t *xh, hipStream_t s) {
+hipError_t launch_coop_e(const GemmArgs &a, uint16_t *xh, hipStream_t s) {
     switch (a.epilogue) {
     case EPI_PLAIN: return launch_coop<QT, EPI_PLAIN, MT>(a, xh, s);
     case EPI_RESIDUAL: return launch_coop<QT, EPI_RESIDUAL, MT>(a, xh, s);
@@ -1169,7 +1230,7 @@ hipError_t launch_coop_e(const GemmArgs &a, const uint16_t *xh, hipStream_t s) {
 }
 
 template <int QT>
-hipError_t launch_coop_q(const GemmArgs &a, const uint16_t *xh, hipStream_t s) {
+hipError_t launch_coop_q(const GemmArgs &a, uint16_t *xh, hipStream_t s) {
     return a.T >= COOP_T512 ? launch_coop_e<QT, 512>(a, xh, s) : launch_coop_e<QT, 256>(a, xh, s);
 }
 

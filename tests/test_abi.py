@@ -122,7 +122,24 @@ def test_workspace_bytes(lib):
     # multiple of 32; the GEMV and the f32 leg none
     assert wb(pf.PF_Q4_0, 12288, 4096, 512, pf.PF_GATE_UP_SWIGLU, pf.PF_LEG_F16) == 512 * 4096 * 2
     assert wb(pf.PF_Q8_0, 4096, 12288, 9, pf.PF_RESIDUAL, pf.PF_LEG_F16) == 32 * 12288 * 2
-    assert wb(pf.PF_Q4_0, 4096, 4096, 300, pf.PF_PLAIN, pf.PF_LEG_F16) == 320 * 4096 * 2
+    # a K split adds S blocks of [T][n] f32 partial sums behind X (256-byte boundary):
+    # 4096^2 at T = 300 is 2 x 22 tiles of 256 x 192, split 3 ways (16 chunks of 256
+    # k, at least 5 per split); at T = 512, 43 tiles of 512 x 96, again 3 ways; the
+    # down projection (k = 12288, 48 chunks) at T = 512 splits 5 ways; at T = 2048 its
+    # 172 tiles need no split.
+    xb = 320 * 4096 * 2
+    assert wb(pf.PF_Q4_0, 4096, 4096, 300, pf.PF_PLAIN, pf.PF_LEG_F16) == xb + 3 * 300 * 4096 * 4
+    assert wb(pf.PF_Q4_0, 4096, 4096, 512, pf.PF_RESIDUAL, pf.PF_LEG_F16) == \
+        512 * 4096 * 2 + 3 * 512 * 4096 * 4
+    assert wb(pf.PF_Q8_0, 4096, 12288, 512, pf.PF_RESIDUAL, pf.PF_LEG_F16) == \
+        512 * 12288 * 2 + 5 * 512 * 4096 * 4
+    assert wb(pf.PF_Q8_0, 4096, 12288, 2048, pf.PF_RESIDUAL, pf.PF_LEG_F16) == 2048 * 12288 * 2
+    # ragged: X bytes rounded up to 256, each split's block to 4 floats
+    assert wb(pf.PF_Q4_0, 1001, 3072, 300, pf.PF_PLAIN, pf.PF_LEG_F16) == \
+        320 * 3072 * 2 + 2 * ((300 * 1001 + 3) // 4 * 4) * 4
+    assert wb(pf.PF_Q4_0, 17, 256, 300, pf.PF_PLAIN, pf.PF_LEG_F16) == 320 * 256 * 2
+    # 5 chunks of k are too few to split
+    assert wb(pf.PF_Q4_0, 17, 1280, 290, pf.PF_RESIDUAL, pf.PF_LEG_F16) == 320 * 1280 * 2
     assert wb(pf.PF_Q4_0, 4096, 4096, 512, pf.PF_PLAIN, pf.PF_LEG_F32) == 0
     assert wb(pf.PF_Q4_0, 4096, 4096, 8, pf.PF_PLAIN, pf.PF_LEG_F16) == 0
     assert wb(pf.PF_Q4_0, 4096, 4096, 0, pf.PF_PLAIN, pf.PF_LEG_F16) == 0

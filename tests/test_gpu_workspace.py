@@ -126,8 +126,42 @@ def test_ws_workload4_long_chunk(gpu):
 @pytest.mark.parametrize("epi", [PLAIN, RESIDUAL])
 @pytest.mark.parametrize("qtype", [Q4_0, Q8_0])
 def test_ws_split_k_narrow(gpu, qtype, epi):
-    """Narrow n with long k splits k across workgroups (fp32 atomics; PLAIN zero-fills
-    first): 4096^2 at T = 512 on sampled outputs, and a ragged 1000 x 3072 at T = 300
-    on every output."""
-    run_ws_and_check(gpu, qtype, 4096, 4096, 512, epi, F16, wid=120 + epi, samples=4096)
-    run_ws_and_check(gpu, qtype, 1000, 3072, 300, epi, F16, wid=130 + epi)
+    """Narrow n with long k splits k across workgroups, each storing its partial sums
+    in the workspace; a second kernel adds R and the splits in a fixed order: 4096^2
+    at T = 512 on sampled outputs, and a ragged 1001 x 3072 at T = 300 on every
+    output. A second run gives the same bits."""
+    Y = run_ws_and_check(gpu, qtype, 4096, 4096, 512, epi, F16, wid=120 + epi, samples=4096)
+    W = weight(qtype, 4096, 4096, False, 120 + epi)
+    X = acts(512, 4096, 120 + epi)
+    R = acts(512, 4096, 120 + epi, synth.TENSOR_R) if epi == RESIDUAL else None
+    Y2 = parity.run_gpu(gpu, qtype, W, 4096, 4096, X, epi, F16, R=R, workspace=True)
+    assert np.array_equal(Y.view(np.uint32), Y2.view(np.uint32))
+    run_ws_and_check(gpu, qtype, 1001, 3072, 300, epi, F16, wid=130 + epi)
+
+
+@pytest.mark.parametrize("epi", [PLAIN, RESIDUAL])
+def test_ws_split_k_scratch_only(gpu, epi):
+    """The partial sums stay inside the pf_workspace_bytes() the split asks for (guard
+    bytes on both sides untouched), and a larger call's stale partials in a reused
+    workspace do not leak into a smaller split call."""
+    import torch
+    n = 1001
+    calls = [(3072, 300, 140 + epi), (2560, 260, 150 + epi)]
+    needs = [gpu.workspace_bytes(Q4_0, n, k, T, epi, F16) for k, T, _ in calls]
+    assert needs[0] > 320 * 3072 * 2 and needs[1] > 288 * 2560 * 2   # both split
+    guard = 4096
+    buf = torch.full(((max(needs) + 2 * guard) // 2,), 0x5A5A, dtype=torch.int16, device="cuda")
+    ws = buf[guard // 2: (guard + max(needs)) // 2]
+    for k, T, wid in calls:
+        W = weight(Q4_0, n, k, False, wid)
+        X = acts(T, k, wid)
+        R = acts(T, n, wid, synth.TENSOR_R) if epi == RESIDUAL else None
+        print("case ws-split-scratch n=%d k=%d T=%d epi=%d" % (n, k, T, epi), flush=True)
+        Y = torch.from_numpy(R.copy()).cuda() if R is not None else \
+            torch.full((T, n), float("nan"), dtype=torch.float32, device="cuda")
+        gpu.gemm_ws(Q4_0, parity.to_dev(W), n, k, parity.to_dev(X), Y, epi, F16, ws)
+        torch.cuda.synchronize()
+        ok, err = parity.check(Q4_0, W, n, k, X, Y.cpu().numpy(), epi, F16, R=R)
+        assert ok, err
+    b = buf.cpu().numpy()
+    assert np.all(b[:guard // 2] == 0x5A5A) and np.all(b[(guard + max(needs)) // 2:] == 0x5A5A)
