@@ -175,6 +175,124 @@ def copy_calibration(torch, mib=256, reps=3):
                       "bytes_written_per_copy": n * 4}), flush=True)
 
 
+def _counter_csv(d):
+    """{(dispatch id, kernel name): {counter: value}} from a rocprofv3 --pmc output
+    directory (its *_counter_collection.csv, wherever rocprofv3 put it)."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection.csv under %s" % d)
+    out = {}
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+                cs = out.setdefault(key, {})
+                cs[r["Counter_Name"]] = cs.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def _short_kernel(name):
+    """'void pf::(anonymous namespace)::x_to_frag_kernel<1>(float const*, ...)' ->
+    'x_to_frag_kernel<1>': no return type, namespaces or parameter list."""
+    name = name.strip()
+    if name.startswith("void "):
+        name = name[5:]
+    name = name.replace("(anonymous namespace)::", "").split("(")[0]
+    return name[4:] if name.startswith("pf::") else name
+
+
+def _op_of_kernel(short, ops):
+    """Which op of a workload launched the library kernel `short` (None if not ours).
+    Block-type templated kernels name the qtype first; split_sum_kernel names the
+    epilogue; zero_fill_kernel belongs to the PLAIN op."""
+    import re
+    m = re.match(r"(\w+)<(\d+)", short)
+    base = m.group(1) if m else short
+    for op in ops:
+        if base == "split_sum_kernel":
+            if int(m.group(2)) == op[4]:
+                return op
+        elif base == "zero_fill_kernel":
+            if op[4] == PLAIN:
+                return op
+        elif base in ("x_to_frag_kernel", "x_to_f16_kernel", "gemm_f16_coop_kernel", "gemm_f16_kernel",
+                      "gemm_f32_kernel", "gemv_kernel") and m and int(m.group(2)) == op[1]:
+            return op
+    return None
+
+
+def traffic_summary(workload, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
+    """HBM bytes per launch of each op of `workload` from rocprofv3 FETCH_SIZE and
+    WRITE_SIZE passes over `bench.py --workload W`, each scaled by what the same
+    counter reads for plain copies of known size (`bench.py --copy-calibration`).
+    Updates profiles/traffic.json and prints a text summary. CPU only."""
+    T, leg, ops = workloads()[workload]
+    cal_bytes = 256 * (1 << 20)
+    cal = {}
+    for cname, d in (("FETCH_SIZE", cal_fetch_dir), ("WRITE_SIZE", cal_write_dir)):
+        vals = [cs[cname] for (_, kn), cs in _counter_csv(d).items() if "copyBuffer" in kn and cname in cs]
+        cal[cname] = sum(vals) / len(vals)   # KiB per copy
+    scale = {c: cal_bytes / (v * 1024.0) for c, v in cal.items()}
+    per_kernel = {}
+    for cname, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        for (_, kn), cs in _counter_csv(d).items():
+            short = _short_kernel(kn)
+            if cname in cs and _op_of_kernel(short, ops) is not None:
+                per_kernel.setdefault(short, {}).setdefault(cname, []).append(cs[cname] * 1024.0 * scale[cname])
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    rec["calibration"] = {"copy_bytes": cal_bytes, "fetch_size_kib": cal["FETCH_SIZE"],
+                          "write_size_kib": cal["WRITE_SIZE"], "fetch_scale": scale["FETCH_SIZE"],
+                          "write_scale": scale["WRITE_SIZE"]}
+    wl = rec.setdefault("workloads", {})
+    wl[workload] = {}
+    lines = ["%-52s %12s %12s %12s" % ("kernel", "read MB", "write MB", "total MB")]
+    for op in ops:
+        total = 0.0
+        kern = {}
+        for short, cs in sorted(per_kernel.items()):
+            if _op_of_kernel(short, ops) is not op:
+                continue
+            rd = sum(cs.get("FETCH_SIZE", [0.0])) / max(1, len(cs.get("FETCH_SIZE", [])))
+            wr = sum(cs.get("WRITE_SIZE", [0.0])) / max(1, len(cs.get("WRITE_SIZE", [])))
+            kern[short] = {"read_bytes": rd, "write_bytes": wr, "dispatches": len(cs.get("FETCH_SIZE", []))}
+            total += rd + wr
+            lines.append("%-52s %12.2f %12.2f %12.2f" % (short, rd / 1e6, wr / 1e6, (rd + wr) / 1e6))
+        lines.append("%-52s %12s %12s %12.2f" % ("op " + op[0] + " (all its kernels)", "", "", total / 1e6))
+        wl[workload][op[0]] = {"kernel_source_sha": kernel_source_sha(kernel_family(T, leg)),
+                               "bytes_per_launch": total, "kernels": kern}
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print("Calibration: a plain device copy of 256 MiB reads FETCH_SIZE = %.1f KiB and WRITE_SIZE = "
+          "%.1f KiB,\n  so FETCH_SIZE is scaled by %.4f and WRITE_SIZE by %.4f below.\n"
+          % (cal["FETCH_SIZE"], cal["WRITE_SIZE"], scale["FETCH_SIZE"], scale["WRITE_SIZE"]))
+    print("\n".join(lines))
+    print("\nkernel_source_sha (%s): %s" % (" + ".join(KERNEL_SOURCES[kernel_family(T, leg)]),
+                                           kernel_source_sha(kernel_family(T, leg))))
+
+
+def trace_summary(kt_dir):
+    """CPU only: per-kernel launch statistics from a rocprofv3 --kernel-trace --stats
+    output directory (its *kernel_stats.csv), in microseconds."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(kt_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no kernel_stats.csv under %s" % kt_dir)
+    print("%-52s %8s %12s %12s %12s %10s" % ("kernel", "calls", "avg_us", "min_us", "max_us", "std_us"))
+    with open(files[0]) as fh:
+        for r in csv.DictReader(fh):
+            print("%-52s %8d %12.2f %12.2f %12.2f %10.2f" % (
+                _short_kernel(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["StdDev"]) / 1e3))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,7 +307,21 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain device copies of a known size (the reference reading "
                          "for the FETCH_SIZE / WRITE_SIZE counters) and print them")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR",
+                                                           "CAL_WRITE_DIR"),
+                    help="CPU only: turn rocprofv3 FETCH_SIZE / WRITE_SIZE pass outputs over "
+                         "--workload (and over --copy-calibration) into profiles/traffic.json")
+    ap.add_argument("--trace-summary", metavar="KT_DIR",
+                    help="CPU only: print the per-kernel table of a rocprofv3 --kernel-trace "
+                         "--stats output directory")
     args = ap.parse_args()
+
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
+    if args.traffic_summary:
+        traffic_summary(args.workload, *args.traffic_summary)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this path has no multi-GPU mode "

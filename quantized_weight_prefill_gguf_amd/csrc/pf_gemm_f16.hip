@@ -372,6 +372,10 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
     read_b(wsm[0], std::integral_constant<int, 0>{}, rwd[0], rwq[0]);
     read_b(wsm[0], std::integral_constant<int, 1>{}, rwd[1], rwq[1]);
     decode_b(std::integral_constant<int, 0>{}, rwd[0], rwq[0], bfr[0]);
+    // Step 0 writes X(2) into xs[0]: every wave's read of X(0) from it must be done
+    // first (in the loop the step-end barrier separates a buffer's reads from its
+    // next write; here nothing else would).
+    __syncthreads();
 
     for (int ch = 0; ch < nch; ++ch) {
         // Step s = 8 ch + blk. At its start: LDS holds X(s+1) and every slice of
