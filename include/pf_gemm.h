@@ -140,6 +140,26 @@ int pf_gemm_ws(int qtype, const void *W_blocks, int64_t n, int64_t k, const floa
                float *Y, int epilogue, int leg, void *workspace, int64_t workspace_bytes,
                void *stream);
 
+/* pf_gemm / pf_gemm_ws with a strided Y: row t of the output starts ldy floats after
+ * row t-1, so the result can land in a wider destination (a column range of a
+ * [T][ldy] buffer, such as one head group's columns of a KV cache) without a copy;
+ * the columns between rows are neither read nor written. This is the `ldc >= n` of
+ * `qwen35_project_rows` on the page "aprender-serve 0.70.2 -
+ * src/cuda/executor/gdn_prefill_ops.rs". A fused projection (the q, k and v weights
+ * stacked row-wise in one buffer, as the page "oxibonsai-kernels 0.1.4 -
+ * src/gpu_backend/cuda_q_std_prefill.rs" runs its fused QKV GEMM) is one call with n
+ * = the stacked row count; ldy then places its output inside a wider row.
+ *  ldy        floats between consecutive rows of Y, ldy >= n (ldy == n is pf_gemm).
+ *             Y's rows lie in the (T - 1) * ldy + n floats from Y; PF_RESIDUAL reads
+ *             R with the same stride. ldy < n, or T * ldy >= 2^31, is PF_E_SHAPE.
+ *  workspace  NULL with workspace_bytes 0: as pf_gemm (X rounded inside the GEMM).
+ *             Otherwise as pf_gemm_ws: at least pf_workspace_bytes() bytes (the
+ *             size does not depend on ldy), 16-byte aligned, overlapping nothing.
+ * Other arguments, ownership and errors as pf_gemm / pf_gemm_ws. */
+int pf_gemm_ex(int qtype, const void *W_blocks, int64_t n, int64_t k, const float *X, int64_t T,
+               float *Y, int64_t ldy, int epilogue, int leg, void *workspace,
+               int64_t workspace_bytes, void *stream);
+
 /* Which family pf_gemm would run for these sizes: PF_PATH_GEMM, PF_PATH_GEMV, 0
  * for T == 0 (nothing runs), or -PF_E_* for arguments pf_gemm would refuse
  * (pointers are not checked). Host-only; touches no GPU state. */

@@ -24,8 +24,8 @@ EPILOGUES = {"plain": PF_PLAIN, "residual": PF_RESIDUAL, "swiglu": PF_GATE_UP_SW
 LEGS = {"f32": PF_LEG_F32, "f16": PF_LEG_F16}
 
 # Every symbol include/pf_gemm.h declares.
-EXPORTS = ("pf_gemm", "pf_gemm_path", "pf_workspace_bytes", "pf_gemm_ws", "pf_select_path",
-           "pf_dequant_f32", "pf_dequant_f16", "pf_weight_bytes", "pf_strerror")
+EXPORTS = ("pf_gemm", "pf_gemm_path", "pf_workspace_bytes", "pf_gemm_ws", "pf_gemm_ex",
+           "pf_select_path", "pf_dequant_f32", "pf_dequant_f16", "pf_weight_bytes", "pf_strerror")
 
 
 class PfError(RuntimeError):
@@ -54,6 +54,8 @@ def load():
     lib.pf_workspace_bytes.restype = i64
     lib.pf_gemm_ws.argtypes = [i32, P, i64, i64, P, i64, P, i32, i32, P, i64, P]
     lib.pf_gemm_ws.restype = i32
+    lib.pf_gemm_ex.argtypes = [i32, P, i64, i64, P, i64, P, i64, i32, i32, P, i64, P]
+    lib.pf_gemm_ex.restype = i32
     lib.pf_select_path.argtypes = [i32, i64, i64, i64, i32, i32]
     lib.pf_select_path.restype = i32
     lib.pf_dequant_f32.argtypes = [i32, P, i64, i64, P, P]
@@ -129,6 +131,34 @@ def gemm_ws(qtype, W, n, k, X, Y, epilogue, leg, workspace, stream=None):
                            epilogue, leg, ws, ws_bytes, _stream_handle(stream))
     if st != PF_OK:
         raise PfError(st, "pf_gemm_ws")
+    return Y
+
+
+def gemm_ex(qtype, W, n, k, X, Y, epilogue, leg, workspace=None, stream=None):
+    """gemm / gemm_ws into a strided Y (see pf_gemm_ex): Y is a float32 device view
+    [T][n] whose rows may lie ldy >= n floats apart (unit stride within a row), e.g.
+    a column range of a wider buffer. workspace None runs as gemm."""
+    import torch
+    T = X.numel() // k if k > 0 else 0
+    if X.dtype != torch.float32 or Y.dtype != torch.float32 or W.dtype != torch.uint8:
+        raise TypeError("X and Y must be float32 and W uint8")
+    if X.numel() != T * k or not X.is_contiguous():
+        raise ValueError("X must be a contiguous [T][k] tensor")
+    if not Y.is_cuda or Y.dim() != 2 or tuple(Y.shape) != (T, n) or (T > 1 and Y.stride(1) != 1):
+        raise ValueError("Y must be a [T][n] device view with unit stride within rows")
+    ldy = Y.stride(0) if T > 1 else n
+    rows = 2 * n if epilogue == PF_GATE_UP_SWIGLU else n
+    need = load().pf_weight_bytes(qtype, rows, k)
+    if need >= 0 and W.numel() < need:
+        raise ValueError("W holds %d bytes, %d needed" % (W.numel(), need))
+    if workspace is None:
+        ws, ws_bytes = ctypes.c_void_p(0), 0
+    else:
+        ws, ws_bytes = _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    st = load().pf_gemm_ex(qtype, _dev_ptr(W, "W"), n, k, _dev_ptr(X, "X"), T, ctypes.c_void_p(Y.data_ptr()),
+                           ldy, epilogue, leg, ws, ws_bytes, _stream_handle(stream))
+    if st != PF_OK:
+        raise PfError(st, "pf_gemm_ex")
     return Y
 
 

@@ -52,18 +52,19 @@ int64_t ws_need(int64_t n, int64_t k, int64_t T, int epilogue, int leg, int use)
 }
 
 int gemm_impl(int qtype, const void *W, int64_t n, int64_t k, const float *X, int64_t T, float *Y,
-              int epilogue, int leg, void *stream, int path, bool with_ws, void *ws,
+              int64_t ldy, int epilogue, int leg, void *stream, int path, bool with_ws, void *ws,
               int64_t ws_bytes) {
     int64_t n_w = 0;
     int st = check_sizes(qtype, n, k, T, epilogue, leg, &n_w);
     if (st != PF_OK) return st;
+    if (ldy < n || (T > 0 && ldy > kMax31 / T)) return PF_E_SHAPE;
     if (path != PF_PATH_AUTO && path != PF_PATH_GEMM && path != PF_PATH_GEMV) return PF_E_PATH;
     if (path == PF_PATH_GEMV && T > PF_GEMV_MAX_T) return PF_E_PATH;
     if (T == 0) return PF_OK;  // an empty batch is a no-op
     if (!W || !X || !Y) return PF_E_NULL;
     if (!aligned16(W) || !aligned16(X) || !aligned16(Y)) return PF_E_ALIGN;
     const int64_t w_bytes = n_w * (k / 32) * block_bytes(qtype);
-    const int64_t x_bytes = T * k * 4, y_bytes = T * n * 4;
+    const int64_t x_bytes = T * k * 4, y_bytes = ((T - 1) * ldy + n) * 4;  // Y's rows and gaps
     if (overlap(Y, y_bytes, X, x_bytes) || overlap(Y, y_bytes, W, w_bytes)) return PF_E_ALIAS;
     const int use = path == PF_PATH_AUTO ? (T <= PF_GEMV_MAX_T ? PF_PATH_GEMV : PF_PATH_GEMM) : path;
     const int64_t need = with_ws ? ws_need(n, k, T, epilogue, leg, use) : 0;
@@ -81,6 +82,7 @@ int gemm_impl(int qtype, const void *W, int64_t n, int64_t k, const float *X, in
     a.X = X;
     a.Y = Y;
     a.n = (int)n;
+    a.ldy = (int)ldy;
     a.k = (int)k;
     a.T = (int)T;
     const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -112,14 +114,22 @@ extern "C" {
 
 int pf_gemm(int qtype, const void *W_blocks, int64_t n, int64_t k, const float *X, int64_t T,
             float *Y, int epilogue, int leg, void *stream) {
-    return gemm_impl(qtype, W_blocks, n, k, X, T, Y, epilogue, leg, stream, PF_PATH_AUTO, false,
+    return gemm_impl(qtype, W_blocks, n, k, X, T, Y, n, epilogue, leg, stream, PF_PATH_AUTO, false,
                      nullptr, 0);
+}
+
+int pf_gemm_ex(int qtype, const void *W_blocks, int64_t n, int64_t k, const float *X, int64_t T,
+               float *Y, int64_t ldy, int epilogue, int leg, void *workspace,
+               int64_t workspace_bytes, void *stream) {
+    const bool with_ws = workspace != nullptr || workspace_bytes != 0;
+    return gemm_impl(qtype, W_blocks, n, k, X, T, Y, ldy, epilogue, leg, stream, PF_PATH_AUTO,
+                     with_ws, workspace, workspace_bytes);
 }
 
 int pf_gemm_ws(int qtype, const void *W_blocks, int64_t n, int64_t k, const float *X, int64_t T,
                float *Y, int epilogue, int leg, void *workspace, int64_t workspace_bytes,
                void *stream) {
-    return gemm_impl(qtype, W_blocks, n, k, X, T, Y, epilogue, leg, stream, PF_PATH_AUTO, true,
+    return gemm_impl(qtype, W_blocks, n, k, X, T, Y, n, epilogue, leg, stream, PF_PATH_AUTO, true,
                      workspace, workspace_bytes);
 }
 
@@ -133,7 +143,7 @@ int64_t pf_workspace_bytes(int qtype, int64_t n, int64_t k, int64_t T, int epilo
 
 int pf_gemm_path(int qtype, const void *W_blocks, int64_t n, int64_t k, const float *X,
                  int64_t T, float *Y, int epilogue, int leg, void *stream, int path) {
-    return gemm_impl(qtype, W_blocks, n, k, X, T, Y, epilogue, leg, stream, path, false, nullptr, 0);
+    return gemm_impl(qtype, W_blocks, n, k, X, T, Y, n, epilogue, leg, stream, path, false, nullptr, 0);
 }
 
 int pf_select_path(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int leg) {

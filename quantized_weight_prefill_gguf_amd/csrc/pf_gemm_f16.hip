@@ -80,7 +80,7 @@ template <int QT, int EPI, int MT, int NW, bool SPLIT, bool XH>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
-                     float *__restrict__ Y, int n, int k, int T, int tiles_m, int tiles_n,
+                     float *__restrict__ Y, int n, int ldy, int k, int T, int tiles_m, int tiles_n,
                      int splits) {
     using CT = ChunkTraits<QT>;
     constexpr int BB = CT::BB;
@@ -485,7 +485,7 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
                     const int t0 = m0 + e_wm * IT * 32 + i * 32 + 4 * q;
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        if (t0 + e < T && o < n) Y[(size_t)(t0 + e) * n + o] = silu_fast(g[e]) * u[e];
+                        if (t0 + e < T && o < n) Y[(size_t)(t0 + e) * ldy + o] = silu_fast(g[e]) * u[e];
                 }
             } else {
                 const int o = tn * NW + tile_col + e_c;
@@ -493,7 +493,7 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
                 for (int r = 0; r < 16; ++r) {
                     const int t = trow + 8 * (r >> 2) + (r & 3);
                     if (t < T && o < n) {
-                        float *y = Y + (size_t)t * n + o;
+                        float *y = Y + (size_t)t * ldy + o;
                         // RESIDUAL adds into Y with an atomic even without a K split:
                         // one writer per element, so the result is the single rounding
                         // of R + acc either way, and the add needs no VGPR copy of acc.
@@ -545,7 +545,7 @@ template <int QT, int EPI, bool SPLIT, int MT = 256, int AD = 2>
 __global__ __launch_bounds__(512)
 void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ Xf,
                           float *__restrict__ Y, float *__restrict__ Ps, long pstride, int n,
-                          int k, int T, int tiles_m, int tiles_n, int splits) {
+                          int ldy, int k, int T, int tiles_m, int tiles_n, int splits) {
     using CT = ChunkTraits<QT>;
     static_assert(MT == 256 || MT == 512, "tile: 256 x 192 or 512 x 96");
     constexpr int NW = MT == 256 ? 192 : 96;        // weight rows per tile
@@ -956,7 +956,7 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
                     const int t0 = m0 + e_wm * IT * 32 + i * 32 + 4 * q;
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        if (t0 + e < T && o < n) Y[(size_t)(t0 + e) * n + o] = silu_fast(g[e]) * u[e];
+                        if (t0 + e < T && o < n) Y[(size_t)(t0 + e) * ldy + o] = silu_fast(g[e]) * u[e];
                 }
             } else {
                 const int o = tn * NW + tile_col + e_c;
@@ -975,18 +975,18 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int t = trow + 8 * (r >> 2) + (r & 3);
-                        rv[r] = (t < T && o < n) ? Y[(size_t)t * n + o] : 0.f;
+                        rv[r] = (t < T && o < n) ? Y[(size_t)t * ldy + o] : 0.f;
                     }
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int t = trow + 8 * (r >> 2) + (r & 3);
-                        if (t < T && o < n) Y[(size_t)t * n + o] = rv[r] + acc[i][j][r];
+                        if (t < T && o < n) Y[(size_t)t * ldy + o] = rv[r] + acc[i][j][r];
                     }
                 } else {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int t = trow + 8 * (r >> 2) + (r & 3);
-                        if (t < T && o < n) Y[(size_t)t * n + o] = acc[i][j][r];
+                        if (t < T && o < n) Y[(size_t)t * ldy + o] = acc[i][j][r];
                     }
                 }
             }
@@ -996,13 +996,23 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
 
 // Y = [R +] P_0 + P_1 + ... + P_{splits-1}, element by element in that order: the
 // cooperative kernel's split-K partial sums, [T][n] each, pstride floats apart
-// (pstride a multiple of 4). Four elements per thread; the thread past the last
-// whole quad takes the 1-3 left over.
-template <int EPI>
+// (pstride a multiple of 4). DENSE (rows of Y n floats apart): four elements per
+// thread, and the thread past the last whole quad takes the 1-3 left over.
+// Otherwise one element per thread, Y[t][o] at Y + t ldy + o.
+template <int EPI, bool DENSE>
 __global__ __launch_bounds__(256) void split_sum_kernel(const float *__restrict__ Ps,
                                                         float *__restrict__ Y, long count,
-                                                        long pstride, int splits) {
+                                                        long pstride, int splits, int n, int ldy) {
     const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if constexpr (!DENSE) {
+        if (i < count) {
+            float *y = Y + (size_t)(i / n) * ldy + i % n;
+            float a = EPI == EPI_RESIDUAL ? *y : 0.f;
+            for (int s = 0; s < splits; ++s) a += Ps[(size_t)s * pstride + i];
+            *y = a;
+        }
+        return;
+    }
     const long quads = count >> 2;
     if (i < quads) {
         f4_t a = EPI == EPI_RESIDUAL ? reinterpret_cast<const f4_t *>(Y)[i] : f4_t{0.f, 0.f, 0.f, 0.f};
@@ -1018,9 +1028,10 @@ __global__ __launch_bounds__(256) void split_sum_kernel(const float *__restrict_
     }
 }
 
-__global__ void zero_fill_kernel(float *__restrict__ Y, int count) {
+// Y[t][o] = 0 for t < T, o < n (rows ldy floats apart).
+__global__ void zero_fill_kernel(float *__restrict__ Y, int T, int n, int ldy) {
     const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i < count) Y[i] = 0.f;
+    if (i < T * n) Y[(size_t)(i / n) * ldy + i % n] = 0.f;
 }
 
 namespace {
@@ -1072,10 +1083,10 @@ hipError_t launch_cfg(const GemmArgs &a, int splits, const uint16_t *xh, hipStre
     const int total = tm * tn * splits;
     if (xh)
         hipLaunchKernelGGL((gemm_f16_kernel<QT, EPI, MT, NW, SPLIT, true>), dim3(total), dim3(256), 0,
-                           s, a.W, (const void *)xh, a.Y, a.n, a.k, a.T, tm, tn, splits);
+                           s, a.W, (const void *)xh, a.Y, a.n, a.ldy, a.k, a.T, tm, tn, splits);
     else
         hipLaunchKernelGGL((gemm_f16_kernel<QT, EPI, MT, NW, SPLIT, false>), dim3(total), dim3(256), 0,
-                           s, a.W, (const void *)a.X, a.Y, a.n, a.k, a.T, tm, tn, splits);
+                           s, a.W, (const void *)a.X, a.Y, a.n, a.ldy, a.k, a.T, tm, tn, splits);
     return hipGetLastError();
 }
 
@@ -1098,7 +1109,8 @@ hipError_t launch_epi(const GemmArgs &a, const uint16_t *xh, hipStream_t s) {
         if (tc.splits == 1) return launch_split<QT, EPI, false>(a, tc, xh, s);
         if constexpr (EPI == EPI_PLAIN) {
             const int count = a.T * a.n;
-            hipLaunchKernelGGL(zero_fill_kernel, dim3((count + 255) / 256), dim3(256), 0, s, a.Y, count);
+            hipLaunchKernelGGL(zero_fill_kernel, dim3((count + 255) / 256), dim3(256), 0, s, a.Y, a.T, a.n,
+                               a.ldy);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
@@ -1209,17 +1221,22 @@ hipError_t launch_coop(const GemmArgs &a, uint16_t *xh, hipStream_t s) {
             float *ps = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(xh) + ws_x_bytes(a.T, a.k));
             const long pstride = (long)ws_pstride(a.T, a.n);
             hipLaunchKernelGGL((gemm_f16_coop_kernel<QT, EPI, true, MT>), dim3(total), dim3(512), 0, s,
-                               a.W, xh, a.Y, ps, pstride, a.n, a.k, a.T, tm, tn, splits);
+                               a.W, xh, a.Y, ps, pstride, a.n, a.ldy, a.k, a.T, tm, tn, splits);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
             const long count = (long)a.T * a.n;
-            const long threads = count / 4 + 1;
-            hipLaunchKernelGGL(split_sum_kernel<EPI>, dim3((unsigned)((threads + 255) / 256)), dim3(256),
-                               0, s, ps, a.Y, count, pstride, splits);
+            if (a.ldy == a.n) {
+                const long threads = count / 4 + 1;
+                hipLaunchKernelGGL((split_sum_kernel<EPI, true>), dim3((unsigned)((threads + 255) / 256)),
+                                   dim3(256), 0, s, ps, a.Y, count, pstride, splits, a.n, a.ldy);
+            } else {
+                hipLaunchKernelGGL((split_sum_kernel<EPI, false>), dim3((unsigned)((count + 255) / 256)),
+                                   dim3(256), 0, s, ps, a.Y, count, pstride, splits, a.n, a.ldy);
+            }
         }
     } else {
         hipLaunchKernelGGL((gemm_f16_coop_kernel<QT, EPI, false, MT>), dim3(total), dim3(512), 0, s, a.W,
-                           xh, a.Y, nullptr, 0L, a.n, a.k, a.T, tm, tn, splits);
+                           xh, a.Y, nullptr, 0L, a.n, a.ldy, a.k, a.T, tm, tn, splits);
     }
     return hipGetLastError();
 }

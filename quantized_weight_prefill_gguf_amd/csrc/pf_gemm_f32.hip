@@ -45,8 +45,8 @@ __device__ __forceinline__ int tile_weight_row(int tile_n, int lr, int n) {
 template <int QT, int EPI>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const uint8_t *__restrict__ W,
                                                        const float *__restrict__ X,
-                                                       float *__restrict__ Y, int n, int k,
-                                                       int T) {
+                                                       float *__restrict__ Y, int n, int ldy,
+                                                       int k, int T) {
     constexpr int MT = F32_MT, NW = F32_NW, WM = F32_WM, WN = F32_WN, XS = F32_XS;
     constexpr int BB = BlockTraits<QT>::BYTES;
     constexpr int HW = BlockTraits<QT>::HALFWORDS;
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const uint8_t *__restrict
             for (int r = 0; r < 4; ++r) {
                 const int t = m0 + wm * WM * 16 + i * 16 + 4 * g + r;
                 if (t >= T) continue;
-                float *y = Y + (size_t)t * n + o;
+                float *y = Y + (size_t)t * ldy + o;
                 if constexpr (EPI == EPI_PLAIN) {
                     *y = acc[i][j][r];
                 } else if constexpr (EPI == EPI_RESIDUAL) {
@@ -221,7 +221,7 @@ template <int QT, int EPI>
 static hipError_t launch_f32_typed(const GemmArgs &a, hipStream_t s) {
     constexpr int OUT_PER_TILE = (EPI == EPI_SWIGLU) ? F32_NW / 2 : F32_NW;
     const dim3 grid((a.n + OUT_PER_TILE - 1) / OUT_PER_TILE, (a.T + F32_MT - 1) / F32_MT);
-    hipLaunchKernelGGL((gemm_f32_kernel<QT, EPI>), grid, dim3(256), 0, s, a.W, a.X, a.Y, a.n, a.k,
+    hipLaunchKernelGGL((gemm_f32_kernel<QT, EPI>), grid, dim3(256), 0, s, a.W, a.X, a.Y, a.n, a.ldy, a.k,
                        a.T);
     return hipGetLastError();
 }

@@ -218,8 +218,8 @@ constexpr int LDS_MAX = 160 * 1024;
 template <int QT, int EPI, int TT, int R, int NS>
 __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t *__restrict__ W,
                                                    const float *__restrict__ X,
-                                                   float *__restrict__ Y, int n, int k,
-                                                   int ngroups) {
+                                                   float *__restrict__ Y, int n, int ldy,
+                                                   int k, int ngroups) {
     using PT = PairTraits<QT>;
     using ST = StepTraits<QT>;
     constexpr int OUTW = (EPI == EPI_SWIGLU) ? R / 2 : R;  // outputs per group
@@ -368,7 +368,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t *__restrict__ W
             const int t = idx / R, r = idx % R;
             const int o = (4 * csg + wid) * OUTW + r;
             if (owner && idx < R * TT && r < OUTW && o < n) {
-                float *dst = Y + (size_t)t * n + o;
+                float *dst = Y + (size_t)t * ldy + o;
                 if constexpr (EPI == EPI_RESIDUAL)
                     *dst = *dst + y;
                 else
@@ -445,7 +445,7 @@ hipError_t launch_m(const GemmArgs &a, int ngroups, hipStream_t s) {
     // Persistent workgroups: one resident round, each streaming one or more
     // super-groups.
     const int blocks = min((ngroups + 15) / 16, per_cu * cus);
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, s, a.W, a.X, a.Y, a.n, a.k, ngroups);
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, s, a.W, a.X, a.Y, a.n, a.ldy, a.k, ngroups);
     return hipGetLastError();
 }
 
@@ -482,7 +482,7 @@ hipError_t launch_t(const GemmArgs &a, hipStream_t s) {
 inline GemmArgs token_slice(const GemmArgs &a, int t0, int tt) {
     GemmArgs b = a;
     b.X = a.X + (size_t)t0 * a.k;
-    b.Y = a.Y + (size_t)t0 * a.n;
+    b.Y = a.Y + (size_t)t0 * a.ldy;
     b.T = tt;
     return b;
 }

@@ -15,6 +15,7 @@ struct GemmArgs {
     const float *X;
     float *Y;
     int n;          // output columns
+    int ldy;        // floats between consecutive rows of Y (>= n)
     int k;          // reduction length, multiple of 256
     int T;          // token rows, >= 1
 };

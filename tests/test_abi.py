@@ -175,6 +175,37 @@ def test_gemm_ws_argument_checks(lib):
     assert g(T=0, ws=0, ws_bytes=0) == pf.PF_OK
 
 
+def test_gemm_ex_argument_checks(lib):
+    """pf_gemm_ex: ldy >= n, the strided Y span ((T-1) ldy + n floats) in the alias
+    checks, and the workspace rules of pf_gemm_ws when a workspace is given."""
+    P = ctypes.c_void_p
+    W, X, Y, WS = FAKE, FAKE + (1 << 32), FAKE + (2 << 32), FAKE + (3 << 32)
+    n, k, T, ldy = 64, 256, 16, 100
+
+    def g(ws=0, ws_bytes=0, leg=pf.PF_LEG_F32, **kw):
+        a = dict(qtype=0, W=W, n=n, k=k, X=X, T=T, Y=Y, ldy=ldy, epi=0)
+        a.update(kw)
+        return lib.pf_gemm_ex(a["qtype"], P(a["W"]), a["n"], a["k"], P(a["X"]), a["T"], P(a["Y"]),
+                              a["ldy"], a["epi"], leg, P(ws), ws_bytes, None)
+
+    assert g(ldy=n - 1) == pf.PF_E_SHAPE
+    assert g(ldy=0, T=0) == pf.PF_E_SHAPE          # a bad stride is refused even when T = 0
+    assert g(T=4096, ldy=1 << 19) == pf.PF_E_SHAPE  # T * ldy >= 2^31
+    assert g(T=0) == pf.PF_OK
+    span = ((T - 1) * ldy + n) * 4
+    assert g(X=Y + span - 16) == pf.PF_E_ALIAS      # X starts inside the last row
+    assert g(X=Y + 4 * 80) == pf.PF_E_ALIAS         # X inside the gap after row 0: still Y's span
+    assert g(Y=X + T * k * 4 - 16) == pf.PF_E_ALIAS
+    assert g(Y=Y + 8) == pf.PF_E_ALIGN
+    assert g(qtype=5) == pf.PF_E_QTYPE
+    # f16 leg with a workspace: too small, or NULL with a size, is refused
+    need = lib.pf_workspace_bytes(0, n, k, T, 0, pf.PF_LEG_F16)
+    assert need == 32 * k * 2
+    assert g(leg=pf.PF_LEG_F16, ws=WS, ws_bytes=need - 16) == pf.PF_E_WORKSPACE
+    assert g(leg=pf.PF_LEG_F16, ws=0, ws_bytes=need) == pf.PF_E_WORKSPACE
+    assert g(leg=pf.PF_LEG_F16, ws=Y + 16, ws_bytes=need) == pf.PF_E_WORKSPACE
+
+
 def test_dequant_argument_checks(lib):
     P = ctypes.c_void_p
     W, out = P(FAKE), P(FAKE + (1 << 32))
