@@ -6,7 +6,9 @@ binding) never imports it and shares no code with it.
 
 The arithmetic lives in ``oracle.c`` (plain C, fp64, no FMA contraction). This
 module only marshals numpy arrays through ctypes. See ``oracle.c`` for the
-passages each function follows. ``tolerance.py`` holds the pass/fail rules.
+passages each function follows. ``tolerance.py`` holds the pass/fail rules. The
+batched RMSNorm prologue (``rmsnorm``) and the GEMM on its fp64 output
+(``matmul_f64``) are plain numpy fp64 here.
 """
 import ctypes
 import os
@@ -175,3 +177,24 @@ def gemm(qtype, W, n, k, X, epi, R=None):
     _load().oracle_gemm(qtype, _ptr(W), n, k, _ptr(X), T,
                         _ptr(R) if R is not None else None, epi, _ptr(Y))
     return Y
+
+
+def rmsnorm(X, w, eps):
+    """Batched RMSNorm in fp64: row t of X divided by sqrt(mean_j X[t][j]^2 + eps),
+    then multiplied by the norm weight w[j] element by element. The pages name the
+    step (`batched_rmsnorm_into(x, norm_weight, out, hidden, rows, eps)` on the page
+    "aprender-serve 0.70.2 - src/gguf/cuda/forward_qwen35_cuda_prefill.rs", before
+    the QKV and gate/up projections) but print no formula; this is the textbook
+    definition with eps inside the square root."""
+    X = np.asarray(X, np.float64)
+    w = np.asarray(w, np.float64).reshape(1, -1)
+    ms = np.mean(X * X, axis=1, keepdims=True)
+    return X / np.sqrt(ms + eps) * w
+
+
+def matmul_f64(qtype, W, rows, k, X64):
+    """fp64 X64 . W_hat^T for fp64 activations [T][k] (an RMSNorm output, which f32
+    would round), with W_hat the exact block decode (dequant_f32); the product is
+    numpy's fp64 matrix multiply."""
+    Wh = dequant_f32(qtype, W, rows, k).astype(np.float64)
+    return np.asarray(X64, np.float64).reshape(-1, k) @ Wh.T

@@ -294,3 +294,50 @@ def test_silu_against_torch(oracle_lib):
     ref = torch.nn.functional.silu(torch.from_numpy(g)).numpy()
     assert np.all(np.abs(ours - ref) <= 4 * 2.0 ** -52 * np.abs(ref) + 1e-300)
     assert oracle_lib.silu(0.0) == 0.0
+
+
+# --------------------------------------------------------------------------- RMSNorm
+
+def test_rmsnorm_hand_worked(oracle_lib):
+    """x = (3, 4), w = (1, 2), eps = 0: mean square 12.5, so x / sqrt(12.5) * w =
+    (3 sqrt(2) / 5, 8 sqrt(2) / 5)."""
+    got = oracle_lib.rmsnorm(np.array([[3.0, 4.0]]), np.array([1.0, 2.0]), 0.0)
+    assert np.allclose(got, [[3 * np.sqrt(2) / 5, 8 * np.sqrt(2) / 5]], rtol=1e-15, atol=0)
+
+
+def test_rmsnorm_eps_inside_the_root(oracle_lib):
+    """A row of ones with eps = 3: 1 / sqrt(1 + 3) = 0.5 exactly (eps added after the
+    square root would give 0.25; a sum instead of a mean, 1 / sqrt(4 + 3))."""
+    got = oracle_lib.rmsnorm(np.ones((1, 4)), np.array([1.0, -2.0, 4.0, 0.5]), 3.0)
+    assert np.array_equal(got, [[0.5, -1.0, 2.0, 0.25]])
+
+
+def test_rmsnorm_closed_forms(oracle_lib):
+    rng = np.random.default_rng(5)
+    X = rng.normal(0, 1, (6, 256))
+    w = rng.uniform(0.5, 1.5, 256)
+    # a constant row c: c / |c| * w exactly when eps = 0
+    C = np.outer([2.5, -0.75], np.ones(256))
+    assert np.array_equal(oracle_lib.rmsnorm(C, w, 0.0), np.outer([1.0, -1.0], w))
+    # invariant to a positive row scale when eps = 0
+    assert np.allclose(oracle_lib.rmsnorm(3.7 * X, w, 0.0), oracle_lib.rmsnorm(X, w, 0.0), rtol=1e-14)
+    # unit weight, eps = 0: every row has mean square 1
+    ms = np.mean(oracle_lib.rmsnorm(X, np.ones(256), 0.0) ** 2, axis=1)
+    assert np.allclose(ms, 1.0, rtol=1e-14)
+    # a zero row stays zero for eps > 0
+    assert np.array_equal(oracle_lib.rmsnorm(np.zeros((1, 256)), w, 1e-6), np.zeros((1, 256)))
+    # the weight multiplies column by column (a transposed w would not broadcast here)
+    Xn1 = oracle_lib.rmsnorm(X, np.ones(256), 1e-6)
+    assert np.allclose(oracle_lib.rmsnorm(X, w, 1e-6), Xn1 * w[None, :], rtol=1e-15)
+
+
+@pytest.mark.parametrize("qtype", [Q4_0, Q8_0])
+def test_matmul_f64_against_c_oracle(oracle_lib, qtype):
+    """On f32-representable activations the numpy fp64 product equals the C oracle's
+    (both exact products, fp64 sums; differences are sum-order rounding only)."""
+    n, k, T = 40, 512, 7
+    W = synth.quantized_weight(qtype, n, k, workload_id=77)
+    X = synth.activations(T, k, workload_id=77)
+    a = oracle_lib.matmul_f64(qtype, W, n, k, X.astype(np.float64))
+    b = oracle_lib.matmul(qtype, W, n, k, X)
+    assert np.allclose(a, b, rtol=1e-12, atol=1e-12)
