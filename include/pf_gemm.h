@@ -160,6 +160,32 @@ int pf_gemm_ex(int qtype, const void *W_blocks, int64_t n, int64_t k, const floa
                float *Y, int64_t ldy, int epilogue, int leg, void *workspace,
                int64_t workspace_bytes, void *stream);
 
+/* The projection with its batched RMSNorm prologue: Y = epilogue(Xn . W_hat^T) where
+ * Xn[t][j] = X[t][j] / sqrt(mean_j' X[t][j']^2 + eps) * norm_w[j], the norm that
+ * precedes the QKV and gate/up projections on the page "aprender-serve 0.70.2 -
+ * src/gguf/cuda/forward_qwen35_cuda_prefill.rs" (`batched_rmsnorm_into`: one weight
+ * of k floats for every row, one eps). The mean square and its reciprocal square
+ * root are f32; Xn is f32 (then RNE_fp16 on the f16 leg). On the f16 leg's
+ * matrix-core GEMM the norm is applied while X is rounded into the workspace, so
+ * the normalised rows never go to memory in f32; the GEMV and the f32 leg read Xn
+ * from the workspace. X is not modified.
+ *  norm_w     device, f32 [k], 16-byte aligned, not overlapping Y.
+ *  eps        finite, >= 0 (else PF_E_SHAPE).
+ *  Y, ldy     as pf_gemm_ex.
+ *  workspace  required (T > 0): device, 16-byte aligned, at least
+ *             pf_rmsnorm_workspace_bytes() bytes, overlapping none of W, X, Y,
+ *             norm_w; contents ignored on entry, undefined on return.
+ * Other arguments, ownership and errors as pf_gemm_ex. */
+int pf_gemm_rmsnorm(int qtype, const void *W_blocks, int64_t n, int64_t k, const float *X, int64_t T,
+                    const float *norm_w, float eps, float *Y, int64_t ldy, int epilogue, int leg,
+                    void *workspace, int64_t workspace_bytes, void *stream);
+
+/* Workspace bytes pf_gemm_rmsnorm needs, or -PF_E_* for sizes pf_gemm would refuse.
+ * 0 for T == 0; else ceil(T * 4 / 256) * 256 (the rows' 1 / rms) plus, on the f16
+ * leg's matrix-core GEMM (T > PF_GEMV_MAX_T), pf_workspace_bytes() for the same
+ * sizes, otherwise T * k * 4 (Xn in f32). Host-only. */
+int64_t pf_rmsnorm_workspace_bytes(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int leg);
+
 /* Which family pf_gemm would run for these sizes: PF_PATH_GEMM, PF_PATH_GEMV, 0
  * for T == 0 (nothing runs), or -PF_E_* for arguments pf_gemm would refuse
  * (pointers are not checked). Host-only; touches no GPU state. */

@@ -25,7 +25,8 @@ LEGS = {"f32": PF_LEG_F32, "f16": PF_LEG_F16}
 
 # Every symbol include/pf_gemm.h declares.
 EXPORTS = ("pf_gemm", "pf_gemm_path", "pf_workspace_bytes", "pf_gemm_ws", "pf_gemm_ex",
-           "pf_select_path", "pf_dequant_f32", "pf_dequant_f16", "pf_weight_bytes", "pf_strerror")
+           "pf_gemm_rmsnorm", "pf_rmsnorm_workspace_bytes", "pf_select_path", "pf_dequant_f32",
+           "pf_dequant_f16", "pf_weight_bytes", "pf_strerror")
 
 
 class PfError(RuntimeError):
@@ -56,6 +57,11 @@ def load():
     lib.pf_gemm_ws.restype = i32
     lib.pf_gemm_ex.argtypes = [i32, P, i64, i64, P, i64, P, i64, i32, i32, P, i64, P]
     lib.pf_gemm_ex.restype = i32
+    lib.pf_gemm_rmsnorm.argtypes = [i32, P, i64, i64, P, i64, P, ctypes.c_float, P, i64, i32, i32, P,
+                                    i64, P]
+    lib.pf_gemm_rmsnorm.restype = i32
+    lib.pf_rmsnorm_workspace_bytes.argtypes = [i32, i64, i64, i64, i32, i32]
+    lib.pf_rmsnorm_workspace_bytes.restype = i64
     lib.pf_select_path.argtypes = [i32, i64, i64, i64, i32, i32]
     lib.pf_select_path.restype = i32
     lib.pf_dequant_f32.argtypes = [i32, P, i64, i64, P, P]
@@ -159,6 +165,41 @@ def gemm_ex(qtype, W, n, k, X, Y, epilogue, leg, workspace=None, stream=None):
                            ldy, epilogue, leg, ws, ws_bytes, _stream_handle(stream))
     if st != PF_OK:
         raise PfError(st, "pf_gemm_ex")
+    return Y
+
+
+def rmsnorm_workspace_bytes(qtype, n, k, T, epilogue, leg):
+    """Bytes of workspace gemm_rmsnorm needs (negative status on bad sizes)."""
+    return load().pf_rmsnorm_workspace_bytes(qtype, n, k, T, epilogue, leg)
+
+
+def gemm_rmsnorm(qtype, W, n, k, X, norm_w, eps, Y, epilogue, leg, workspace, stream=None):
+    """Y = epilogue(RMSNorm(X; norm_w, eps) . W_hat^T) (see pf_gemm_rmsnorm). norm_w is
+    a float32 device tensor of k values; Y a [T][n] device view as in gemm_ex; the
+    workspace a device tensor of at least rmsnorm_workspace_bytes() bytes."""
+    import torch
+    T = X.numel() // k if k > 0 else 0
+    if X.dtype != torch.float32 or Y.dtype != torch.float32 or W.dtype != torch.uint8 or \
+            norm_w.dtype != torch.float32:
+        raise TypeError("X, Y and norm_w must be float32 and W uint8")
+    if X.numel() != T * k or norm_w.numel() != k:
+        raise ValueError("X must hold T*k and norm_w k elements")
+    if not Y.is_cuda or Y.dim() != 2 or tuple(Y.shape) != (T, n) or (T > 1 and Y.stride(1) != 1):
+        raise ValueError("Y must be a [T][n] device view with unit stride within rows")
+    ldy = Y.stride(0) if T > 1 else n
+    rows = 2 * n if epilogue == PF_GATE_UP_SWIGLU else n
+    need = load().pf_weight_bytes(qtype, rows, k)
+    if need >= 0 and W.numel() < need:
+        raise ValueError("W holds %d bytes, %d needed" % (W.numel(), need))
+    if workspace is None:
+        ws, ws_bytes = ctypes.c_void_p(0), 0
+    else:
+        ws, ws_bytes = _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    st = load().pf_gemm_rmsnorm(qtype, _dev_ptr(W, "W"), n, k, _dev_ptr(X, "X"), T,
+                                _dev_ptr(norm_w, "norm_w"), float(eps), ctypes.c_void_p(Y.data_ptr()),
+                                ldy, epilogue, leg, ws, ws_bytes, _stream_handle(stream))
+    if st != PF_OK:
+        raise PfError(st, "pf_gemm_rmsnorm")
     return Y
 
 

@@ -8,6 +8,8 @@
 // `qwen35_dequant_f32` there).
 #include <stdint.h>
 
+#include <cmath>
+
 #include "../../include/pf_gemm.h"
 #include "pf_internal.h"
 
@@ -98,6 +100,71 @@ int gemm_impl(int qtype, const void *W, int64_t n, int64_t k, const float *X, in
     return err == hipSuccess ? PF_OK : PF_E_LAUNCH;
 }
 
+int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
+
+// Workspace of the RMSNorm entry point: inv[T] (rounded up to 256 bytes), then the
+// f16 GEMM's own workspace (X rounded to binary16 with the norm applied, and any
+// split-K partial sums), or, for the kernels that read f32 X, Xn [T][k] f32.
+int64_t rms_ws_need(int64_t n, int64_t k, int64_t T, int epilogue, int leg, int use) {
+    if (T == 0) return 0;
+    const int64_t tail = (use == PF_PATH_GEMM && leg == PF_LEG_F16)
+                             ? pf::f16_ws_bytes((int)T, (int)n, (int)k, epilogue)
+                             : T * k * 4;
+    return round256(T * 4) + tail;
+}
+
+int rms_impl(int qtype, const void *W, int64_t n, int64_t k, const float *X, int64_t T,
+             const float *norm_w, float eps, float *Y, int64_t ldy, int epilogue, int leg, void *ws,
+             int64_t ws_bytes, void *stream) {
+    int64_t n_w = 0;
+    int st = check_sizes(qtype, n, k, T, epilogue, leg, &n_w);
+    if (st != PF_OK) return st;
+    if (ldy < n || (T > 0 && ldy > kMax31 / T)) return PF_E_SHAPE;
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return PF_E_SHAPE;
+    if (T == 0) return PF_OK;  // an empty batch is a no-op
+    if (!W || !X || !Y || !norm_w) return PF_E_NULL;
+    if (!aligned16(W) || !aligned16(X) || !aligned16(Y) || !aligned16(norm_w)) return PF_E_ALIGN;
+    const int64_t w_bytes = n_w * (k / 32) * block_bytes(qtype);
+    const int64_t x_bytes = T * k * 4, y_bytes = ((T - 1) * ldy + n) * 4, nw_bytes = k * 4;
+    if (overlap(Y, y_bytes, X, x_bytes) || overlap(Y, y_bytes, W, w_bytes) ||
+        overlap(Y, y_bytes, norm_w, nw_bytes))
+        return PF_E_ALIAS;
+    const int use = T <= PF_GEMV_MAX_T ? PF_PATH_GEMV : PF_PATH_GEMM;
+    const int64_t need = rms_ws_need(n, k, T, epilogue, leg, use);
+    if (!ws || ws_bytes < need || !aligned16(ws)) return PF_E_WORKSPACE;
+    if (overlap(ws, need, W, w_bytes) || overlap(ws, need, X, x_bytes) || overlap(ws, need, Y, y_bytes) ||
+        overlap(ws, need, norm_w, nw_bytes))
+        return PF_E_WORKSPACE;
+
+    pf::GemmArgs a;
+    a.qtype = qtype;
+    a.epilogue = epilogue;
+    a.W = static_cast<const uint8_t *>(W);
+    a.X = X;
+    a.Y = Y;
+    a.n = (int)n;
+    a.ldy = (int)ldy;
+    a.k = (int)k;
+    a.T = (int)T;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    float *inv = static_cast<float *>(ws);
+    uint8_t *rest = static_cast<uint8_t *>(ws) + round256(T * 4);
+    hipError_t err = pf::launch_rms_inv(X, a.T, a.k, eps, inv, s);
+    if (err != hipSuccess) return PF_E_LAUNCH;
+    if (use == PF_PATH_GEMM && leg == PF_LEG_F16) {
+        a.norm_inv = inv;
+        a.norm_w = norm_w;
+        err = pf::launch_gemm_f16_ws(a, rest, s);
+    } else {
+        float *Xn = reinterpret_cast<float *>(rest);
+        err = pf::launch_rms_apply(X, inv, norm_w, Xn, a.T, a.k, s);
+        if (err != hipSuccess) return PF_E_LAUNCH;
+        a.X = Xn;
+        err = use == PF_PATH_GEMV ? pf::launch_gemv(a, s) : pf::launch_gemm_f32(a, s);
+    }
+    return err == hipSuccess ? PF_OK : PF_E_LAUNCH;
+}
+
 int dequant_check(int qtype, const void *W, int64_t rows, int64_t k, const void *out, int out_elem) {
     if (block_bytes(qtype) < 0) return PF_E_QTYPE;
     if (rows < 1 || k < 32 || k % 32 != 0) return PF_E_SHAPE;
@@ -131,6 +198,20 @@ int pf_gemm_ws(int qtype, const void *W_blocks, int64_t n, int64_t k, const floa
                void *stream) {
     return gemm_impl(qtype, W_blocks, n, k, X, T, Y, n, epilogue, leg, stream, PF_PATH_AUTO, true,
                      workspace, workspace_bytes);
+}
+
+int pf_gemm_rmsnorm(int qtype, const void *W_blocks, int64_t n, int64_t k, const float *X, int64_t T,
+                    const float *norm_w, float eps, float *Y, int64_t ldy, int epilogue, int leg,
+                    void *workspace, int64_t workspace_bytes, void *stream) {
+    return rms_impl(qtype, W_blocks, n, k, X, T, norm_w, eps, Y, ldy, epilogue, leg, workspace,
+                    workspace_bytes, stream);
+}
+
+int64_t pf_rmsnorm_workspace_bytes(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int leg) {
+    int64_t n_w = 0;
+    const int st = check_sizes(qtype, n, k, T, epilogue, leg, &n_w);
+    if (st != PF_OK) return -st;
+    return rms_ws_need(n, k, T, epilogue, leg, T <= PF_GEMV_MAX_T ? PF_PATH_GEMV : PF_PATH_GEMM);
 }
 
 int64_t pf_workspace_bytes(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int leg) {

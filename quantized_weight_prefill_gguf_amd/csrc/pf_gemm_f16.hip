@@ -1127,16 +1127,30 @@ hipError_t launch_q(const GemmArgs &a, const uint16_t *xh, hipStream_t s) {
     }
 }
 
+// RMSNorm prologue inside the conversion: x * inv (the row's) * w (the columns')
+// in f32, in the order rms_apply_kernel uses, before the rounding to binary16.
+__device__ __forceinline__ f4_t rms_scale(f4_t v, float r, const float *__restrict__ w) {
+    const f4_t g = *reinterpret_cast<const f4_t *>(w);
+    return f4_t{v[0] * r * g[0], v[1] * r * g[1], v[2] * r * g[2], v[3] * r * g[3]};
+}
+
 // X [T][k] f32 -> fp16 (RNE) in the k order the GEMM's A fragments take: for
 // Q4_0 the order 0, 2, 1, 3 within each group of four, natural for Q8_0. One
-// thread writes 8 halves (16 bytes).
-template <int QT>
+// thread writes 8 halves (16 bytes). NORM: the RMSNorm prologue first.
+template <int QT, bool NORM>
 __global__ __launch_bounds__(256) void x_to_f16_kernel(const float *__restrict__ X,
-                                                       uint16_t *__restrict__ Xh, int count8) {
+                                                       uint16_t *__restrict__ Xh, int count8, int k,
+                                                       const float *__restrict__ inv,
+                                                       const float *__restrict__ nw) {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= count8) return;
-    const f4_t a = reinterpret_cast<const f4_t *>(X)[2 * i];
-    const f4_t b = reinterpret_cast<const f4_t *>(X)[2 * i + 1];
+    f4_t a = reinterpret_cast<const f4_t *>(X)[2 * i];
+    f4_t b = reinterpret_cast<const f4_t *>(X)[2 * i + 1];
+    if constexpr (NORM) {
+        const int row = (int)((long)i * 8 / k), col = i * 8 - row * k;
+        a = rms_scale(a, inv[row], nw + col);
+        b = rms_scale(b, inv[row], nw + col + 4);
+    }
     const u2_t pa = x_pack<QT>(a), pb = x_pack<QT>(b);
     reinterpret_cast<u4_t *>(Xh)[i] = u4_t{pa[0], pa[1], pb[0], pb[1]};
 }
@@ -1145,11 +1159,12 @@ __global__ __launch_bounds__(256) void x_to_f16_kernel(const float *__restrict__
 // 32-row tile rt and 16-k slice kk, one 1 KB fragment at index rt * (k / 16) + kk,
 // whose lane (c, h) holds row 32 rt + c, k = 16 kk + 8 h .. + 7 in the order of
 // x_pack. Rows past T (up to the next multiple of 32) are zero. One thread writes
-// one lane's 16 bytes.
-template <int QT>
+// one lane's 16 bytes. NORM: the RMSNorm prologue first.
+template <int QT, bool NORM>
 __global__ __launch_bounds__(256) void x_to_frag_kernel(const float *__restrict__ X,
                                                         uint16_t *__restrict__ Xf, int T, int k,
-                                                        int count) {
+                                                        int count, const float *__restrict__ inv,
+                                                        const float *__restrict__ nw) {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= count) return;
     const int lane = i & 63;
@@ -1159,9 +1174,16 @@ __global__ __launch_bounds__(256) void x_to_frag_kernel(const float *__restrict_
     const int row = rt * 32 + (lane & 31);
     u4_t out = u4_t{0u, 0u, 0u, 0u};
     if (row < T) {
-        const float *src = X + (size_t)row * k + kk * 16 + 8 * (lane >> 5);
-        const u2_t pa = x_pack<QT>(*reinterpret_cast<const f4_t *>(src));
-        const u2_t pb = x_pack<QT>(*reinterpret_cast<const f4_t *>(src + 4));
+        const int col = kk * 16 + 8 * (lane >> 5);
+        const float *src = X + (size_t)row * k + col;
+        f4_t a = *reinterpret_cast<const f4_t *>(src);
+        f4_t b = *reinterpret_cast<const f4_t *>(src + 4);
+        if constexpr (NORM) {
+            a = rms_scale(a, inv[row], nw + col);
+            b = rms_scale(b, inv[row], nw + col + 4);
+        }
+        const u2_t pa = x_pack<QT>(a);
+        const u2_t pb = x_pack<QT>(b);
         out = u4_t{pa[0], pa[1], pb[0], pb[1]};
     }
     reinterpret_cast<u4_t *>(Xf)[i] = out;
@@ -1260,21 +1282,41 @@ hipError_t launch_gemm_f16_ws(const GemmArgs &a, void *workspace, hipStream_t s)
     if (a.T >= 256) {
         // The cooperative-decode kernel takes X in A-fragment order.
         const int count = (a.T + 31) / 32 * 32 * (a.k / 8);
-        if (a.qtype == Q4_0)
-            hipLaunchKernelGGL(x_to_frag_kernel<Q4_0>, dim3((count + 255) / 256), dim3(256), 0, s, a.X,
-                               xh, a.T, a.k, count);
-        else
-            hipLaunchKernelGGL(x_to_frag_kernel<Q8_0>, dim3((count + 255) / 256), dim3(256), 0, s, a.X,
-                               xh, a.T, a.k, count);
+        const dim3 g((count + 255) / 256);
+        if (a.norm_inv) {
+            if (a.qtype == Q4_0)
+                hipLaunchKernelGGL((x_to_frag_kernel<Q4_0, true>), g, dim3(256), 0, s, a.X, xh, a.T, a.k,
+                                   count, a.norm_inv, a.norm_w);
+            else
+                hipLaunchKernelGGL((x_to_frag_kernel<Q8_0, true>), g, dim3(256), 0, s, a.X, xh, a.T, a.k,
+                                   count, a.norm_inv, a.norm_w);
+        } else if (a.qtype == Q4_0) {
+            hipLaunchKernelGGL((x_to_frag_kernel<Q4_0, false>), g, dim3(256), 0, s, a.X, xh, a.T, a.k,
+                               count, nullptr, nullptr);
+        } else {
+            hipLaunchKernelGGL((x_to_frag_kernel<Q8_0, false>), g, dim3(256), 0, s, a.X, xh, a.T, a.k,
+                               count, nullptr, nullptr);
+        }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         return a.qtype == Q4_0 ? launch_coop_q<Q4_0>(a, xh, s) : launch_coop_q<Q8_0>(a, xh, s);
     }
     const int count8 = a.T * (a.k / 8);
-    if (a.qtype == Q4_0)
-        hipLaunchKernelGGL(x_to_f16_kernel<Q4_0>, dim3((count8 + 255) / 256), dim3(256), 0, s, a.X, xh, count8);
-    else
-        hipLaunchKernelGGL(x_to_f16_kernel<Q8_0>, dim3((count8 + 255) / 256), dim3(256), 0, s, a.X, xh, count8);
+    const dim3 g((count8 + 255) / 256);
+    if (a.norm_inv) {
+        if (a.qtype == Q4_0)
+            hipLaunchKernelGGL((x_to_f16_kernel<Q4_0, true>), g, dim3(256), 0, s, a.X, xh, count8, a.k,
+                               a.norm_inv, a.norm_w);
+        else
+            hipLaunchKernelGGL((x_to_f16_kernel<Q8_0, true>), g, dim3(256), 0, s, a.X, xh, count8, a.k,
+                               a.norm_inv, a.norm_w);
+    } else if (a.qtype == Q4_0) {
+        hipLaunchKernelGGL((x_to_f16_kernel<Q4_0, false>), g, dim3(256), 0, s, a.X, xh, count8, a.k,
+                           nullptr, nullptr);
+    } else {
+        hipLaunchKernelGGL((x_to_f16_kernel<Q8_0, false>), g, dim3(256), 0, s, a.X, xh, count8, a.k,
+                           nullptr, nullptr);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return a.qtype == Q4_0 ? launch_q<Q4_0>(a, xh, s) : launch_q<Q8_0>(a, xh, s);

@@ -18,6 +18,10 @@ struct GemmArgs {
     int ldy;        // floats between consecutive rows of Y (>= n)
     int k;          // reduction length, multiple of 256
     int T;          // token rows, >= 1
+    // RMSNorm prologue for the f16 workspace path (both null: none): X is read as
+    // X[t][j] * norm_inv[t] * norm_w[j].
+    const float *norm_w = nullptr;
+    const float *norm_inv = nullptr;
 };
 
 // Tiled matrix-core GEMM, f32 leg (fp32 MFMA).
@@ -32,6 +36,11 @@ hipError_t launch_gemm_f16_ws(const GemmArgs &a, void *workspace, hipStream_t s)
 // multiple of 32), and for T >= 256 with a K split, behind it (at the next 256-byte
 // boundary) one [T][n] f32 block of partial sums per split.
 int64_t f16_ws_bytes(int T, int n, int k, int epilogue);
+// RMSNorm prologue: inv[t] = 1 / sqrt(mean_j X[t][j]^2 + eps) (T workgroups), and
+// Xn[t][j] = X[t][j] * inv[t] * w[j] for the kernels that read f32 X.
+hipError_t launch_rms_inv(const float *X, int T, int k, float eps, float *inv, hipStream_t s);
+hipError_t launch_rms_apply(const float *X, const float *inv, const float *w, float *Xn, int T, int k,
+                            hipStream_t s);
 // Small-T GEMV (T <= 8), f32 arithmetic.
 hipError_t launch_gemv(const GemmArgs &a, hipStream_t s);
 // Block decode to f32 / binary16.

@@ -206,6 +206,48 @@ def test_gemm_ex_argument_checks(lib):
     assert g(leg=pf.PF_LEG_F16, ws=Y + 16, ws_bytes=need) == pf.PF_E_WORKSPACE
 
 
+def test_rmsnorm_workspace_bytes(lib):
+    wb = lib.pf_rmsnorm_workspace_bytes
+    # 1 / rms per row (rounded up to 256 bytes), then the f16 GEMM's workspace ...
+    assert wb(pf.PF_Q4_0, 12288, 4096, 512, pf.PF_GATE_UP_SWIGLU, pf.PF_LEG_F16) == \
+        2048 + lib.pf_workspace_bytes(pf.PF_Q4_0, 12288, 4096, 512, pf.PF_GATE_UP_SWIGLU, pf.PF_LEG_F16)
+    assert wb(pf.PF_Q4_0, 4096, 4096, 300, pf.PF_PLAIN, pf.PF_LEG_F16) == \
+        1280 + lib.pf_workspace_bytes(pf.PF_Q4_0, 4096, 4096, 300, pf.PF_PLAIN, pf.PF_LEG_F16)
+    # ... or the normalised rows in f32 for the GEMV and the f32 leg
+    assert wb(pf.PF_Q8_0, 4096, 12288, 3, pf.PF_PLAIN, pf.PF_LEG_F16) == 256 + 3 * 12288 * 4
+    assert wb(pf.PF_Q4_0, 200, 768, 40, pf.PF_RESIDUAL, pf.PF_LEG_F32) == 256 + 40 * 768 * 4
+    assert wb(pf.PF_Q4_0, 200, 768, 0, pf.PF_RESIDUAL, pf.PF_LEG_F32) == 0
+    assert wb(pf.PF_Q4_0, 200, 700, 4, pf.PF_PLAIN, pf.PF_LEG_F32) == -pf.PF_E_SHAPE
+
+
+def test_gemm_rmsnorm_argument_checks(lib):
+    P = ctypes.c_void_p
+    W, X, Y, WS, NW = FAKE, FAKE + (1 << 32), FAKE + (2 << 32), FAKE + (3 << 32), FAKE + (4 << 32)
+    n, k, T = 64, 256, 16
+    need = lib.pf_rmsnorm_workspace_bytes(0, n, k, T, 0, pf.PF_LEG_F32)
+    assert need == 256 + T * k * 4
+
+    def g(ws=WS, ws_bytes=need, eps=1e-6, nw=NW, ldy=n, **kw):
+        a = dict(qtype=0, W=W, n=n, k=k, X=X, T=T, Y=Y, epi=0, leg=pf.PF_LEG_F32)
+        a.update(kw)
+        return lib.pf_gemm_rmsnorm(a["qtype"], P(a["W"]), a["n"], a["k"], P(a["X"]), a["T"], P(nw), eps,
+                                   P(a["Y"]), ldy, a["epi"], a["leg"], P(ws), ws_bytes, None)
+
+    assert g(eps=float("nan")) == pf.PF_E_SHAPE
+    assert g(eps=-1.0) == pf.PF_E_SHAPE
+    assert g(eps=float("inf")) == pf.PF_E_SHAPE
+    assert g(ldy=n - 4) == pf.PF_E_SHAPE
+    assert g(nw=0) == pf.PF_E_NULL
+    assert g(nw=NW + 4) == pf.PF_E_ALIGN
+    assert g(nw=Y + 16) == pf.PF_E_ALIAS
+    assert g(ws=0) == pf.PF_E_WORKSPACE
+    assert g(ws_bytes=need - 16) == pf.PF_E_WORKSPACE
+    assert g(ws=NW - 16) == pf.PF_E_WORKSPACE          # overlaps norm_w
+    assert g(ws=X + 64) == pf.PF_E_WORKSPACE
+    assert g(qtype=4) == pf.PF_E_QTYPE
+    assert g(T=0, ws=0, ws_bytes=0, nw=0) == pf.PF_OK
+
+
 def test_dequant_argument_checks(lib):
     P = ctypes.c_void_p
     W, out = P(FAKE), P(FAKE + (1 << 32))
