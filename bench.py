@@ -41,6 +41,7 @@ PEAK = {
 }
 
 HIDDEN, INTER = 4096, 12288
+NORM_EPS = 1e-6
 Q4_0, Q8_0 = 0, 1
 PLAIN, RESIDUAL, SWIGLU = 0, 1, 2
 BLOCK = {Q4_0: 18, Q8_0: 34}
@@ -78,6 +79,12 @@ def workloads():
     return {
         "ffn_T512_f16": ffn(512),
         "ffn_T2048_f16": ffn(2048),
+        # the FFN sublayer as the pages run it: RMSNorm, gate/up SwiGLU, down + residual,
+        # with the norm inside the gate/up call (pf_gemm_rmsnorm)
+        "ffn_rmsnorm_T512_f16": (512, 1, [
+            ("rmsnorm_gate_up_swiglu_q4_0", Q4_0, INTER, HIDDEN, SWIGLU, "x", "act"),
+            ("down_residual_q8_0", Q8_0, HIDDEN, INTER, RESIDUAL, "act", "res"),
+        ]),
         "ffn_T512_f32": (512, 0, ffn(512)[2]),
         "plain_q4_0_4096_T512_f16": (512, 1, [("plain_q4_0", Q4_0, HIDDEN, HIDDEN, PLAIN, "x", "out")]),
         "gemv_q4_0_12288x4096_T1": (1, 0, [("gemv_q4_0", Q4_0, INTER, HIDDEN, PLAIN, "x", "out")]),
@@ -116,6 +123,8 @@ def cpu_baseline(T, ops, inputs, target_s=12.0):
         for op in ops:
             label, qtype, n, k, epi, src, _ = op
             X = inputs[src][:ts]
+            if label.startswith("rmsnorm_"):
+                X = oracle.rmsnorm(X, inputs["norm_w"], NORM_EPS).astype(np.float32)
             R = inputs["res"][:ts] if epi == RESIDUAL else None
             oracle.gemm(qtype, inputs["w_" + label], n, k, X, epi, R)
             flops += op_flops(op, ts)
@@ -216,6 +225,9 @@ def _op_of_kernel(short, ops):
                 return op
         elif base == "zero_fill_kernel":
             if op[4] == PLAIN:
+                return op
+        elif base in ("rms_inv_kernel", "rms_apply_kernel"):
+            if op[0].startswith("rmsnorm_"):
                 return op
         elif base in ("x_to_frag_kernel", "x_to_f16_kernel", "gemm_f16_coop_kernel", "gemm_f16_kernel",
                       "gemm_f32_kernel", "gemv_kernel") and m and int(m.group(2)) == op[1]:
@@ -356,6 +368,7 @@ def main():
     inputs["x12288"] = synth.activations(T, INTER, workload_id=wid)
     inputs["res"] = synth.activations(T, HIDDEN, workload_id=wid, tensor_id=synth.TENSOR_R)
     inputs["act"] = synth.activations(T, INTER, workload_id=wid, tensor_id=synth.TENSOR_W_UP)
+    inputs["norm_w"] = np.random.default_rng([wid, 9]).uniform(0.5, 1.5, HIDDEN).astype(np.float32)
 
     log("inputs generated for %s" % args.workload)
     wbytes = sum(inputs["w_" + op[0]].size for op in ops)
@@ -369,10 +382,12 @@ def main():
         "act": torch.from_numpy(inputs["act"]).cuda(),
         "res": torch.from_numpy(inputs["res"]).cuda(),
         "out": torch.empty((T, max(HIDDEN, INTER)), dtype=torch.float32, device="cuda"),
+        "norm_w": torch.from_numpy(inputs["norm_w"]).cuda(),
     }
     stream = torch.cuda.current_stream()
     use_ws = not args.no_workspace
-    ws_bytes = max(pf.workspace_bytes(op[1], op[2], op[3], T, op[4], leg) for op in ops)
+    ws_bytes = max((pf.rmsnorm_workspace_bytes if op[0].startswith("rmsnorm_") else pf.workspace_bytes)(
+        op[1], op[2], op[3], T, op[4], leg) for op in ops)
     workspace = (torch.empty(((ws_bytes + 15) // 16) * 16, dtype=torch.uint8, device="cuda")
                  if use_ws and ws_bytes > 0 else None)
 
@@ -386,10 +401,19 @@ def main():
         for op in ops:
             label, qtype, n, k, epi, src, dst = op
             Y = bufs[dst] if dst != "out" else bufs["out"].view(-1)[: T * n].view(T, n)
+            w, x, y = P(dev_w[wset][label].data_ptr()), P(bufs[src].data_ptr()), P(Y.data_ptr())
+            if label.startswith("rmsnorm_"):
+                if workspace is None:
+                    raise SystemExit("the RMSNorm prologue needs a workspace")
+                pf.gemm_rmsnorm(qtype, dev_w[wset][label], n, k, bufs[src], bufs["norm_w"], NORM_EPS, Y, epi,
+                                leg, workspace)
+                calls[(op[0], wset)] = (lib.pf_gemm_rmsnorm, (
+                    qtype, w, n, k, x, T, P(bufs["norm_w"].data_ptr()), NORM_EPS, y, n, epi, leg,
+                    P(workspace.data_ptr()), workspace.numel(), hstream))
+                continue
             # the checks the binding makes, once
             pf.gemm_ws(qtype, dev_w[wset][label], n, k, bufs[src], Y, epi, leg, workspace) if use_ws \
                 else pf.gemm(qtype, dev_w[wset][label], n, k, bufs[src], Y, epi, leg)
-            w, x, y = P(dev_w[wset][label].data_ptr()), P(bufs[src].data_ptr()), P(Y.data_ptr())
             if use_ws:
                 ws = P(workspace.data_ptr()) if workspace is not None else P(0)
                 wsb = workspace.numel() if workspace is not None else 0
