@@ -198,3 +198,16 @@ def matmul_f64(qtype, W, rows, k, X64):
     numpy's fp64 matrix multiply."""
     Wh = dequant_f32(qtype, W, rows, k).astype(np.float64)
     return np.asarray(X64, np.float64).reshape(-1, k) @ Wh.T
+
+
+def argmax_last(logits):
+    """The greedy token of a logit row: the index of its largest value, the largest
+    such index when several are equal (-0 and +0 are equal). The page
+    "oxibonsai-kernels 0.1.4 - src/gpu_backend/cuda_q_std_prefill.rs" picks it on
+    the host with Rust's Iterator::max_by over partial_cmp, which returns the last
+    of equal maxima. Plain Python over the values as given (no rounding)."""
+    best_i, best_v = 0, None
+    for i, v in enumerate(np.asarray(logits).reshape(-1).tolist()):
+        if best_v is None or v >= best_v:
+            best_i, best_v = i, v
+    return best_i

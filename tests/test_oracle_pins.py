@@ -341,3 +341,26 @@ def test_matmul_f64_against_c_oracle(oracle_lib, qtype):
     a = oracle_lib.matmul_f64(qtype, W, n, k, X.astype(np.float64))
     b = oracle_lib.matmul(qtype, W, n, k, X)
     assert np.allclose(a, b, rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- argmax
+
+def test_argmax_last_hand_cases(oracle_lib):
+    am = oracle_lib.argmax_last
+    assert am([1.0]) == 0
+    assert am([0.5, 2.0, -3.0]) == 1
+    assert am([2.0, 1.0, 2.0, 0.0]) == 2          # equal maxima: the last one
+    assert am([-5.0, -1.0, -1.0, -7.0]) == 2      # all negative
+    assert am([0.0, -0.0]) == 1                    # -0 == +0: a tie
+    assert am([-0.0, 0.0]) == 1
+    assert am(np.array([3, 9, 9, 9, 1], np.float32)) == 3
+
+
+def test_argmax_last_against_numpy(oracle_lib):
+    """Distinct values: numpy.argmax; with a planted tie, the later index."""
+    rng = np.random.default_rng(11)
+    x = rng.normal(0, 1, 1000).astype(np.float32)
+    assert oracle_lib.argmax_last(x) == int(np.argmax(x))
+    i = int(np.argmax(x))
+    x[900 if i < 900 else 10] = x[i]
+    assert oracle_lib.argmax_last(x) == max(i, 900 if i < 900 else 10)
