@@ -186,6 +186,21 @@ int pf_gemm_rmsnorm(int qtype, const void *W_blocks, int64_t n, int64_t k, const
  * sizes, otherwise T * k * 4 (Xn in f32). Host-only. */
 int64_t pf_rmsnorm_workspace_bytes(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int leg);
 
+/* The lm_head step of a prefill: logits = x . W_hat^T for one activation row (the
+ * GEMV, f32), then the greedy token, on the device. The page "oxibonsai-kernels 0.1.4 -
+ * src/gpu_backend/cuda_q_std_prefill.rs" runs this GEMV on the normed last row and
+ * picks the token on the host with Rust's max_by over partial_cmp, the last of equal
+ * maxima; here token[0] is the largest index among the maxima of the f32 logits
+ * just written (-0 and +0 equal; NaN logits make the pick unspecified).
+ *  W_blocks  device, n rows (the vocabulary) of k/32 blocks; k a multiple of 256.
+ *  x         device, f32 [k] (e.g. the output of the final RMSNorm), 16-byte aligned.
+ *  logits    device, f32 [n], written; 16-byte aligned; overlapping neither W nor x.
+ *  token     device, one int32, written; 4-byte aligned; overlapping nothing above.
+ * Two launches on the stream (the GEMV, then a one-workgroup pick); nothing is
+ * allocated. Returns PF_OK or a PF_E_* code as pf_gemm. */
+int pf_lm_head_argmax(int qtype, const void *W_blocks, int64_t n, int64_t k, const float *x,
+                      float *logits, int32_t *token, void *stream);
+
 /* Which family pf_gemm would run for these sizes: PF_PATH_GEMM, PF_PATH_GEMV, 0
  * for T == 0 (nothing runs), or -PF_E_* for arguments pf_gemm would refuse
  * (pointers are not checked). Host-only; touches no GPU state. */

@@ -25,7 +25,8 @@ LEGS = {"f32": PF_LEG_F32, "f16": PF_LEG_F16}
 
 # Every symbol include/pf_gemm.h declares.
 EXPORTS = ("pf_gemm", "pf_gemm_path", "pf_workspace_bytes", "pf_gemm_ws", "pf_gemm_ex",
-           "pf_gemm_rmsnorm", "pf_rmsnorm_workspace_bytes", "pf_select_path", "pf_dequant_f32",
+           "pf_gemm_rmsnorm", "pf_rmsnorm_workspace_bytes", "pf_lm_head_argmax", "pf_select_path",
+           "pf_dequant_f32",
            "pf_dequant_f16", "pf_weight_bytes", "pf_strerror")
 
 
@@ -62,6 +63,8 @@ def load():
     lib.pf_gemm_rmsnorm.restype = i32
     lib.pf_rmsnorm_workspace_bytes.argtypes = [i32, i64, i64, i64, i32, i32]
     lib.pf_rmsnorm_workspace_bytes.restype = i64
+    lib.pf_lm_head_argmax.argtypes = [i32, P, i64, i64, P, P, P, P]
+    lib.pf_lm_head_argmax.restype = i32
     lib.pf_select_path.argtypes = [i32, i64, i64, i64, i32, i32]
     lib.pf_select_path.restype = i32
     lib.pf_dequant_f32.argtypes = [i32, P, i64, i64, P, P]
@@ -201,6 +204,26 @@ def gemm_rmsnorm(qtype, W, n, k, X, norm_w, eps, Y, epilogue, leg, workspace, st
     if st != PF_OK:
         raise PfError(st, "pf_gemm_rmsnorm")
     return Y
+
+
+def lm_head_argmax(qtype, W, n, k, x, logits, token, stream=None):
+    """logits[n] = x[k] . W_hat^T and token[0] = the largest index among its maxima
+    (see pf_lm_head_argmax). x, logits: float32 device tensors; token: an int32
+    device tensor of at least one element."""
+    import torch
+    if x.dtype != torch.float32 or logits.dtype != torch.float32 or W.dtype != torch.uint8 or \
+            token.dtype != torch.int32:
+        raise TypeError("x and logits must be float32, W uint8, token int32")
+    if x.numel() != k or logits.numel() != n or token.numel() < 1:
+        raise ValueError("x must hold k, logits n and token at least one element")
+    need = load().pf_weight_bytes(qtype, n, k)
+    if need >= 0 and W.numel() < need:
+        raise ValueError("W holds %d bytes, %d needed" % (W.numel(), need))
+    st = load().pf_lm_head_argmax(qtype, _dev_ptr(W, "W"), n, k, _dev_ptr(x, "x"), _dev_ptr(logits, "logits"),
+                                  _dev_ptr(token, "token"), _stream_handle(stream))
+    if st != PF_OK:
+        raise PfError(st, "pf_lm_head_argmax")
+    return token
 
 
 def gemm(qtype, W, n, k, X, Y, epilogue, leg, stream=None, path=PF_PATH_AUTO):

@@ -207,6 +207,35 @@ int pf_gemm_rmsnorm(int qtype, const void *W_blocks, int64_t n, int64_t k, const
                     workspace_bytes, stream);
 }
 
+int pf_lm_head_argmax(int qtype, const void *W_blocks, int64_t n, int64_t k, const float *x,
+                      float *logits, int32_t *token, void *stream) {
+    int64_t n_w = 0;
+    const int st = check_sizes(qtype, n, k, 1, PF_PLAIN, PF_LEG_F32, &n_w);
+    if (st != PF_OK) return st;
+    if (!W_blocks || !x || !logits || !token) return PF_E_NULL;
+    if (!aligned16(W_blocks) || !aligned16(x) || !aligned16(logits) ||
+        (reinterpret_cast<uintptr_t>(token) & 3u) != 0)
+        return PF_E_ALIGN;
+    const int64_t w_bytes = n_w * (k / 32) * block_bytes(qtype), x_bytes = k * 4, l_bytes = n * 4;
+    if (overlap(logits, l_bytes, W_blocks, w_bytes) || overlap(logits, l_bytes, x, x_bytes) ||
+        overlap(token, 4, logits, l_bytes) || overlap(token, 4, W_blocks, w_bytes) ||
+        overlap(token, 4, x, x_bytes))
+        return PF_E_ALIAS;
+    pf::GemmArgs a;
+    a.qtype = qtype;
+    a.epilogue = PF_PLAIN;
+    a.W = static_cast<const uint8_t *>(W_blocks);
+    a.X = x;
+    a.Y = logits;
+    a.n = (int)n;
+    a.ldy = (int)n;
+    a.k = (int)k;
+    a.T = 1;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (pf::launch_gemv(a, s) != hipSuccess) return PF_E_LAUNCH;
+    return pf::launch_argmax(logits, (int)n, token, s) == hipSuccess ? PF_OK : PF_E_LAUNCH;
+}
+
 int64_t pf_rmsnorm_workspace_bytes(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int leg) {
     int64_t n_w = 0;
     const int st = check_sizes(qtype, n, k, T, epilogue, leg, &n_w);

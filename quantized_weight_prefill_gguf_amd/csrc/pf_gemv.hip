@@ -149,11 +149,16 @@ __device__ __forceinline__ void pair_accumulate(const uint32_t (&dw)[R][PairTrai
                     xa[t] = xg.f[t][8 * h + m];
                     if constexpr (QT == Q4_0) xb[t] = xg.f[t][8 * h + 4 + m];
                 } else {
+                    // x summed one element at a time in the order of the FMA chain
+                    // below, so that a block whose codes all equal the offset (a
+                    // zero weight) gives exactly s == OFF * x_sum, i.e. 0.
                     xa[t] = xl[x_lds_index(t, 8 * h + m, lane)];
-                    xs[t] += (xa[t][0] + xa[t][1]) + (xa[t][2] + xa[t][3]);
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) xs[t] = xs[t] + xa[t][b];
                     if constexpr (QT == Q4_0) {
                         xb[t] = xl[x_lds_index(t, 8 * h + 4 + m, lane)];
-                        xs[t] += (xb[t][0] + xb[t][1]) + (xb[t][2] + xb[t][3]);
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) xs[t] = xs[t] + xb[t][b];
                     }
                 }
             }
@@ -401,11 +406,19 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t *__restrict__ W
                 for (int i = 0; i < 16; ++i) xg.f[t][i] = xl[x_lds_index(t, i, lane)];
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
+                    // the order of pair_accumulate's FMA chain (see there)
+                    using PT = PairTraits<QT>;
                     float a = 0.f;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const f4_t q = xg.f[t][8 * h + i];
-                        a += (q[0] + q[1]) + (q[2] + q[3]);
+                    for (int m = 0; m < PT::WORDS; ++m) {
+                        const f4_t qa = xg.f[t][8 * h + m];
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) a = a + qa[b];
+                        if constexpr (QT == Q4_0) {
+                            const f4_t qb = xg.f[t][8 * h + 4 + m];
+#pragma unroll
+                            for (int b = 0; b < 4; ++b) a = a + qb[b];
+                        }
                     }
                     xg.xs[t][h] = a;
                 }
@@ -488,26 +501,35 @@ inline GemmArgs token_slice(const GemmArgs &a, int t0, int tt) {
 }
 
 template <int QT, int EPI>
-hipError_t launch_epi(const GemmArgs &a, hipStream_t s) {
+hipError_t launch_tt(const GemmArgs &a, hipStream_t s) {
     switch (a.T) {
     case 1: return launch_t<QT, EPI, 1>(a, s);
     case 2: return launch_t<QT, EPI, 2>(a, s);
     case 3: return launch_t<QT, EPI, 3>(a, s);
-    case 4: return launch_t<QT, EPI, 4>(a, s);
-    case 5: return launch_t<QT, EPI, 5>(a, s);
-    case 6: return launch_t<QT, EPI, 6>(a, s);
-    case 7: return launch_t<QT, EPI, 7>(a, s);
-    default:
-        if constexpr (QT == Q8_0) {
-            // 8 tokens of x (128 KB) and the Q8_0 weight staging exceed the LDS:
-            // two launches of 4 tokens each (rows are independent).
-            const hipError_t e = launch_t<QT, EPI, 4>(token_slice(a, 0, 4), s);
-            if (e != hipSuccess) return e;
-            return launch_t<QT, EPI, 4>(token_slice(a, 4, 4), s);
-        } else {
-            return launch_t<QT, EPI, 8>(a, s);
-        }
+    default: return launch_t<QT, EPI, 4>(a, s);
     }
+}
+
+// Tokens per launch: at most four (one weight row per group), and at most 96 KB of
+// x, so that the chunk's x stays staged in LDS for the whole run beside the weight
+// staging. Larger chunks restage x per item or run at lower occupancy; measured on
+// Q4_0 12288 x 4096: T = 8 in one launch 55.9 us, as 4 + 4 tokens 43.3 us; Q8_0
+// 4096 x 12288 (48 KB of x per token): T = 4 in one launch 56.4 us, as 2 + 2 44 us,
+// T = 3 47.3 us against 2 + 1 39.7 us. Rows are independent, so each chunk is its
+// own problem; the weights stream once per chunk.
+inline int gemv_tokens_per_launch(int k) {
+    const int by_x = (96 * 1024) / (k * 4);
+    return by_x < 1 ? 1 : (by_x > 4 ? 4 : by_x);
+}
+
+template <int QT, int EPI>
+hipError_t launch_epi(const GemmArgs &a, hipStream_t s) {
+    const int per = gemv_tokens_per_launch(a.k);
+    for (int t0 = 0; t0 < a.T; t0 += per) {
+        const hipError_t e = launch_tt<QT, EPI>(token_slice(a, t0, min(per, a.T - t0)), s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <int QT>

@@ -41,6 +41,8 @@ int64_t f16_ws_bytes(int T, int n, int k, int epilogue);
 hipError_t launch_rms_inv(const float *X, int T, int k, float eps, float *inv, hipStream_t s);
 hipError_t launch_rms_apply(const float *X, const float *inv, const float *w, float *Xn, int T, int k,
                             hipStream_t s);
+// token[0] = the largest index among the maxima of logits[0 .. n) (one workgroup).
+hipError_t launch_argmax(const float *logits, int n, int32_t *token, hipStream_t s);
 // Small-T GEMV (T <= 8), f32 arithmetic.
 hipError_t launch_gemv(const GemmArgs &a, hipStream_t s);
 // Block decode to f32 / binary16.

@@ -248,6 +248,29 @@ def test_gemm_rmsnorm_argument_checks(lib):
     assert g(T=0, ws=0, ws_bytes=0, nw=0) == pf.PF_OK
 
 
+def test_lm_head_argmax_argument_checks(lib):
+    P = ctypes.c_void_p
+    W, x, L, tok = FAKE, FAKE + (1 << 32), FAKE + (2 << 32), FAKE + (3 << 32)
+    n, k = 1000, 256
+
+    def g(**kw):
+        a = dict(qtype=0, W=W, n=n, k=k, x=x, L=L, tok=tok)
+        a.update(kw)
+        return lib.pf_lm_head_argmax(a["qtype"], P(a["W"]), a["n"], a["k"], P(a["x"]), P(a["L"]),
+                                     P(a["tok"]), None)
+
+    assert g(qtype=3) == pf.PF_E_QTYPE
+    assert g(k=300) == pf.PF_E_SHAPE
+    assert g(n=0) == pf.PF_E_SHAPE
+    for name in ("W", "x", "L", "tok"):
+        assert g(**{name: 0}) == pf.PF_E_NULL, name
+    assert g(L=L + 8) == pf.PF_E_ALIGN
+    assert g(tok=tok + 2) == pf.PF_E_ALIGN
+    assert g(L=x + 16) == pf.PF_E_ALIAS
+    assert g(tok=L + 4 * (n - 1)) == pf.PF_E_ALIAS
+    assert g(tok=x) == pf.PF_E_ALIAS
+
+
 def test_dequant_argument_checks(lib):
     P = ctypes.c_void_p
     W, out = P(FAKE), P(FAKE + (1 << 32))

@@ -215,3 +215,30 @@ def test_empty_batch_is_noop(gpu):
     Y = torch.empty((0, 64), dtype=torch.float32, device="cuda")
     gpu.gemm(Q4_0, W, 64, 256, X, Y, PLAIN, F32)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("qtype", [Q4_0, Q8_0])
+@pytest.mark.parametrize("T,leg,epi", [(1, F32, PLAIN), (2, F32, RESIDUAL), (3, F32, PLAIN),
+                                       (5, F16, PLAIN), (8, F32, PLAIN), (8, F32, RESIDUAL),
+                                       (40, F32, PLAIN), (40, F16, RESIDUAL)])
+def test_zero_weight_rows_exact(gpu, qtype, T, leg, epi):
+    """Rows whose every code is the offset (Q4_0 nibbles 8, Q8_0 bytes 0) under a
+    nonzero scale decode to +0 or -0 weights: their outputs must be exactly 0 (R
+    for RESIDUAL) for general x, in every kernel family (the GEMV's per-block
+    algebra d (sum u x - c sum x) included)."""
+    n, k = 64, 1024
+    B = synth.BLOCK_BYTES[qtype]
+    W = weight(qtype, n, k, False, 500 + qtype).reshape(n, k // 32, B).copy()
+    zero_rows = [0, 7, 31, 63]
+    for r in zero_rows:
+        W[r, :, 2:] = 0x88 if qtype == Q4_0 else 0
+    W = W.reshape(-1)
+    X = acts(T, k, 501)
+    R = acts(T, n, 501, synth.TENSOR_R) if epi == RESIDUAL else None
+    print("case zero-rows qtype=%d T=%d leg=%d epi=%d" % (qtype, T, leg, epi), flush=True)
+    Y = parity.run_gpu(gpu, qtype, W, n, k, X, epi, leg, R=R)
+    for r in zero_rows:
+        want = R[:, r] if R is not None else np.zeros(T, np.float32)
+        assert np.array_equal(Y[:, r], want), (r, Y[:, r][:4])
+    ok, err = parity.check(qtype, W, n, k, X, Y, epi, leg, R=R)
+    assert ok, "parity failed: metric %.3e" % err
