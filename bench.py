@@ -41,6 +41,8 @@ PEAK = {
 }
 
 HIDDEN, INTER = 4096, 12288
+VOCAB = 151936
+LM_UNIQUE_ROWS = 16384  # lm_head weights: this many seeded rows, tiled to VOCAB
 NORM_EPS = 1e-6
 Q4_0, Q8_0 = 0, 1
 PLAIN, RESIDUAL, SWIGLU = 0, 1, 2
@@ -91,6 +93,10 @@ def workloads():
         "gemv_q8_0_4096x12288_T1": (1, 0, [("gemv_q8_0", Q8_0, HIDDEN, INTER, PLAIN, "x12288", "out")]),
         "gemv_q4_0_12288x4096_T8": (8, 0, [("gemv_q4_0", Q4_0, INTER, HIDDEN, PLAIN, "x", "out")]),
         "gemv_q8_0_4096x12288_T8": (8, 0, [("gemv_q8_0", Q8_0, HIDDEN, INTER, PLAIN, "x12288", "out")]),
+        # lm_head GEMV on one row plus the greedy token (pf_lm_head_argmax); the pages
+        # give no vocabulary size: 151936 rows stand in for it
+        "lm_head_q8_0_151936x4096_T1": (1, 0, [("lm_head_q8_0", Q8_0, VOCAB, HIDDEN, PLAIN, "x", "logits")]),
+        "lm_head_q4_0_151936x4096_T1": (1, 0, [("lm_head_q4_0", Q4_0, VOCAB, HIDDEN, PLAIN, "x", "logits")]),
     }
 
 
@@ -126,7 +132,9 @@ def cpu_baseline(T, ops, inputs, target_s=12.0):
             if label.startswith("rmsnorm_"):
                 X = oracle.rmsnorm(X, inputs["norm_w"], NORM_EPS).astype(np.float32)
             R = inputs["res"][:ts] if epi == RESIDUAL else None
-            oracle.gemm(qtype, inputs["w_" + label], n, k, X, epi, R)
+            Y = oracle.gemm(qtype, inputs["w_" + label], n, k, X, epi, R)
+            if label.startswith("lm_head_"):
+                oracle.argmax_last(Y[0].astype(np.float32))
             flops += op_flops(op, ts)
         return flops, time.perf_counter() - t0
 
@@ -228,6 +236,9 @@ def _op_of_kernel(short, ops):
                 return op
         elif base in ("rms_inv_kernel", "rms_apply_kernel"):
             if op[0].startswith("rmsnorm_"):
+                return op
+        elif base == "argmax_kernel":
+            if op[0].startswith("lm_head_"):
                 return op
         elif base in ("x_to_frag_kernel", "x_to_f16_kernel", "gemm_f16_coop_kernel", "gemm_f16_kernel",
                       "gemm_f32_kernel", "gemv_kernel") and m and int(m.group(2)) == op[1]:
@@ -361,6 +372,12 @@ def main():
         label, qtype, n, k, epi, src, dst = op
         if epi == SWIGLU:
             inputs["w_" + label] = synth.gate_up_weight(qtype, n, k, workload_id=wid)
+        elif label.startswith("lm_head_"):
+            # quantising 620 M weights on the host takes minutes: seeded rows, tiled
+            # (the timing does not depend on the values)
+            base = synth.quantized_weight(qtype, LM_UNIQUE_ROWS, k, workload_id=wid).reshape(LM_UNIQUE_ROWS, -1)
+            reps = -(-n // LM_UNIQUE_ROWS)
+            inputs["w_" + label] = np.ascontiguousarray(np.tile(base, (reps, 1))[:n]).reshape(-1)
         else:
             tid = synth.TENSOR_W_DOWN if label.startswith("down") else synth.TENSOR_W
             inputs["w_" + label] = synth.quantized_weight(qtype, n, k, workload_id=wid, tensor_id=tid)
@@ -383,6 +400,8 @@ def main():
         "res": torch.from_numpy(inputs["res"]).cuda(),
         "out": torch.empty((T, max(HIDDEN, INTER)), dtype=torch.float32, device="cuda"),
         "norm_w": torch.from_numpy(inputs["norm_w"]).cuda(),
+        "logits": torch.empty((VOCAB,), dtype=torch.float32, device="cuda"),
+        "token": torch.zeros((1,), dtype=torch.int32, device="cuda"),
     }
     stream = torch.cuda.current_stream()
     use_ws = not args.no_workspace
@@ -402,6 +421,11 @@ def main():
             label, qtype, n, k, epi, src, dst = op
             Y = bufs[dst] if dst != "out" else bufs["out"].view(-1)[: T * n].view(T, n)
             w, x, y = P(dev_w[wset][label].data_ptr()), P(bufs[src].data_ptr()), P(Y.data_ptr())
+            if label.startswith("lm_head_"):
+                pf.lm_head_argmax(qtype, dev_w[wset][label], n, k, bufs[src][0], bufs["logits"], bufs["token"])
+                calls[(op[0], wset)] = (lib.pf_lm_head_argmax, (
+                    qtype, w, n, k, x, P(bufs["logits"].data_ptr()), P(bufs["token"].data_ptr()), hstream))
+                continue
             if label.startswith("rmsnorm_"):
                 if workspace is None:
                     raise SystemExit("the RMSNorm prologue needs a workspace")

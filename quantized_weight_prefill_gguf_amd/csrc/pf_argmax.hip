@@ -5,10 +5,11 @@
 // returns the last of equal maxima; here the pick runs on the device over the same
 // f32 logits.
 //
-// One workgroup of 1024 threads: each thread folds its strided share of the row
-// into one 64-bit key, (order-preserving bits of the value) << 32 | index, so that
-// the unsigned maximum of the keys is the largest value and, among equal values,
-// the largest index; then a reduction across lanes, waves and the workgroup.
+// One workgroup of 1024 threads. Each thread scans its strided share of the row in
+// increasing index order keeping (value, index) with `v >= best`, so among equal
+// values its later index wins, and -0 == +0 as IEEE compares them; then the pairs
+// are combined across lanes, waves and the workgroup (larger value, or the larger
+// index on equal values). NaN never wins a comparison; a row of NaN gives 0.
 #include "pf_device.h"
 #include "pf_internal.h"
 
@@ -16,39 +17,51 @@ namespace pf {
 
 namespace {
 
-__device__ __forceinline__ uint64_t argmax_key(float v, uint32_t i) {
-    // -0 -> +0; then an order-preserving map of IEEE bits to unsigned integers.
-    uint32_t u = __builtin_bit_cast(uint32_t, v == 0.f ? 0.f : v);
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)u << 32) | i;
-}
+struct Best {
+    float v;
+    int i;
+};
 
-__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ Best pick(Best a, Best b) {
+    return (b.v > a.v || (b.v == a.v && b.i > a.i)) ? b : a;
+}
 
 __global__ __launch_bounds__(1024) void argmax_kernel(const float *__restrict__ logits, int n,
                                                       int32_t *__restrict__ token) {
-    uint64_t best = 0;  // below every real key
+    Best best{-__builtin_inff(), -1};
     const int quads = n >> 2;
-    for (int q = threadIdx.x; q < quads; q += 1024) {
-        const f4_t v = reinterpret_cast<const f4_t *>(logits)[q];
+    // Eight independent 16-byte loads in flight per thread per round.
+    constexpr int U = 8;
+    for (int q0 = threadIdx.x; q0 < quads; q0 += 1024 * U) {
+        f4_t v[U];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) best = max_u64(best, argmax_key(v[e], (uint32_t)(4 * q + e)));
+        for (int u = 0; u < U; ++u) {
+            const int q = q0 + 1024 * u;
+            v[u] = q < quads ? reinterpret_cast<const f4_t *>(logits)[q] : f4_t{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int q = q0 + 1024 * u;
+            if (q < quads) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (v[u][e] >= best.v) best = Best{v[u][e], 4 * q + e};
+                }
+            }
+        }
     }
     for (int i = 4 * quads + threadIdx.x; i < n; i += 1024)
-        best = max_u64(best, argmax_key(logits[i], (uint32_t)i));
+        if (logits[i] >= best.v) best = Best{logits[i], i};
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const uint32_t lo = __shfl_xor((uint32_t)best, off, 64);
-        const uint32_t hi = __shfl_xor((uint32_t)(best >> 32), off, 64);
-        best = max_u64(best, ((uint64_t)hi << 32) | lo);
-    }
-    __shared__ uint64_t part[16];
+    for (int off = 32; off >= 1; off >>= 1)
+        best = pick(best, Best{__shfl_xor(best.v, off, 64), __shfl_xor(best.i, off, 64)});
+    __shared__ Best part[16];
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = best;
     __syncthreads();
     if (threadIdx.x == 0) {
-        uint64_t b = part[0];
-        for (int w = 1; w < 16; ++w) b = max_u64(b, part[w]);
-        token[0] = (int32_t)(uint32_t)b;
+        Best b = part[0];
+        for (int w = 1; w < 16; ++w) b = pick(b, part[w]);
+        token[0] = b.i < 0 ? 0 : b.i;
     }
 }
 
