@@ -1158,35 +1158,39 @@ __global__ __launch_bounds__(256) void x_to_f16_kernel(const float *__restrict__
 // X [T][k] f32 -> fp16 (RNE) in A-fragment order for gemm_f16_coop_kernel: for each
 // 32-row tile rt and 16-k slice kk, one 1 KB fragment at index rt * (k / 16) + kk,
 // whose lane (c, h) holds row 32 rt + c, k = 16 kk + 8 h .. + 7 in the order of
-// x_pack. Rows past T (up to the next multiple of 32) are zero. One thread writes
-// one lane's 16 bytes. NORM: the RMSNorm prologue first.
+// x_pack. Rows past T (up to the next multiple of 32) are zero. Thread p converts
+// the 16 values of row c = p % 32 in fragment f = p / 32 (64 contiguous bytes) and
+// writes lanes (c, 0) and (c, 1): a wave reads 128 contiguous bytes of each of 32
+// rows and writes two whole fragments. NORM: the RMSNorm prologue first.
 template <int QT, bool NORM>
 __global__ __launch_bounds__(256) void x_to_frag_kernel(const float *__restrict__ X,
                                                         uint16_t *__restrict__ Xf, int T, int k,
-                                                        int count, const float *__restrict__ inv,
+                                                        int pairs, const float *__restrict__ inv,
                                                         const float *__restrict__ nw) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i >= count) return;
-    const int lane = i & 63;
-    const int f = i >> 6;
+    const int p = blockIdx.x * 256 + threadIdx.x;
+    if (p >= pairs) return;
+    const int c = p & 31;
+    const int f = p >> 5;
     const int k16 = k >> 4;
     const int rt = f / k16, kk = f - rt * k16;
-    const int row = rt * 32 + (lane & 31);
-    u4_t out = u4_t{0u, 0u, 0u, 0u};
+    const int row = rt * 32 + c;
+    u4_t out0 = u4_t{0u, 0u, 0u, 0u}, out1 = out0;
     if (row < T) {
-        const int col = kk * 16 + 8 * (lane >> 5);
-        const float *src = X + (size_t)row * k + col;
-        f4_t a = *reinterpret_cast<const f4_t *>(src);
-        f4_t b = *reinterpret_cast<const f4_t *>(src + 4);
+        const int col = kk * 16;
+        const f4_t *src = reinterpret_cast<const f4_t *>(X + (size_t)row * k + col);
+        f4_t v[4] = {src[0], src[1], src[2], src[3]};
         if constexpr (NORM) {
-            a = rms_scale(a, inv[row], nw + col);
-            b = rms_scale(b, inv[row], nw + col + 4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = rms_scale(v[j], inv[row], nw + col + 4 * j);
         }
-        const u2_t pa = x_pack<QT>(a);
-        const u2_t pb = x_pack<QT>(b);
-        out = u4_t{pa[0], pa[1], pb[0], pb[1]};
+        const u2_t p0 = x_pack<QT>(v[0]), p1 = x_pack<QT>(v[1]);
+        const u2_t p2 = x_pack<QT>(v[2]), p3 = x_pack<QT>(v[3]);
+        out0 = u4_t{p0[0], p0[1], p1[0], p1[1]};
+        out1 = u4_t{p2[0], p2[1], p3[0], p3[1]};
     }
-    reinterpret_cast<u4_t *>(Xf)[i] = out;
+    u4_t *dst = reinterpret_cast<u4_t *>(Xf) + (size_t)f * 64 + c;
+    dst[0] = out0;
+    dst[32] = out1;
 }
 
 }  // namespace
@@ -1281,7 +1285,7 @@ hipError_t launch_gemm_f16_ws(const GemmArgs &a, void *workspace, hipStream_t s)
     uint16_t *xh = static_cast<uint16_t *>(workspace);
     if (a.T >= 256) {
         // The cooperative-decode kernel takes X in A-fragment order.
-        const int count = (a.T + 31) / 32 * 32 * (a.k / 8);
+        const int count = (a.T + 31) / 32 * 32 * (a.k / 16);  // (row, 16-k slice) pairs
         const dim3 g((count + 255) / 256);
         if (a.norm_inv) {
             if (a.qtype == Q4_0)
