@@ -242,3 +242,35 @@ def test_zero_weight_rows_exact(gpu, qtype, T, leg, epi):
         assert np.array_equal(Y[:, r], want), (r, Y[:, r][:4])
     ok, err = parity.check(qtype, W, n, k, X, Y, epi, leg, R=R)
     assert ok, "parity failed: metric %.3e" % err
+
+
+# ----------------------------------------------------------------------------- large sizes
+
+@pytest.mark.parametrize("qtype", [Q4_0, Q8_0])
+@pytest.mark.parametrize("T,leg,epi", [(1, F32, PLAIN), (64, F32, RESIDUAL), (64, F16, PLAIN),
+                                       (300, F16, RESIDUAL)])
+def test_long_k(gpu, qtype, T, leg, epi):
+    """k = 32768 (128 chunks of 256): the GEMV, the f32 GEMM, the f16 GEMM and the
+    cooperative kernel (through the workspace) over a long reduction, every output."""
+    n, k = 96, 32768
+    wid = 510 + T + qtype
+    W = weight(qtype, n, k, False, wid)
+    X = acts(T, k, wid)
+    R = acts(T, n, wid, synth.TENSOR_R) if epi == RESIDUAL else None
+    print("case long-k qtype=%d T=%d leg=%d epi=%d" % (qtype, T, leg, epi), flush=True)
+    Y = parity.run_gpu(gpu, qtype, W, n, k, X, epi, leg, R=R, workspace=(T >= 256))
+    ok, err = parity.check(qtype, W, n, k, X, Y, epi, leg, R=R)
+    assert ok, "parity failed: metric %.3e" % err
+
+
+@pytest.mark.parametrize("epi", [PLAIN, SWIGLU])
+def test_large_T(gpu, epi):
+    """T = 4096 token rows (8 M-tiles of the 512 x 96 cooperative kernel, 8 MB of
+    fp16 X in the workspace), sampled outputs including the last row and column."""
+    n, k, T = 1024, 4096, 4096
+    print("case large-T epi=%d" % epi, flush=True)
+    W = weight(Q4_0, n, k, epi == SWIGLU, 520 + epi)
+    X = acts(T, k, 520 + epi, row_scale=True)
+    Y = parity.run_gpu(gpu, Q4_0, W, n, k, X, epi, F16, workspace=True)
+    ok, err = parity.check(Q4_0, W, n, k, X, Y, epi, F16, samples=4096)
+    assert ok, "parity failed: metric %.3e" % err
