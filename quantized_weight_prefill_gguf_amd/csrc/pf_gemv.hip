@@ -123,10 +123,12 @@ struct PairXRegs {
     float xs[TT][2];
 };
 
-template <int QT, int TT, int R, bool XR>
+// XS (x from LDS, fixed for the run): the two blocks' sums of x come precomputed in
+// xsum[t][h] instead of being added up again for every row.
+template <int QT, int TT, int R, bool XR, bool XS>
 __device__ __forceinline__ void pair_accumulate(const uint32_t (&dw)[R][PairTraits<QT>::DW],
                                                 const f4_t *xl, const PairXRegs<XR ? TT : 1> &xg,
-                                                int lane, bool valid,
+                                                const float (&xsum)[TT][2], int lane, bool valid,
                                                 float (&acc)[pow2_ceil(R * TT)]) {
     using PT = PairTraits<QT>;
 #pragma unroll
@@ -153,12 +155,16 @@ __device__ __forceinline__ void pair_accumulate(const uint32_t (&dw)[R][PairTrai
                     // below, so that a block whose codes all equal the offset (a
                     // zero weight) gives exactly s == OFF * x_sum, i.e. 0.
                     xa[t] = xl[x_lds_index(t, 8 * h + m, lane)];
+                    if constexpr (!XS) {
 #pragma unroll
-                    for (int b = 0; b < 4; ++b) xs[t] = xs[t] + xa[t][b];
+                        for (int b = 0; b < 4; ++b) xs[t] = xs[t] + xa[t][b];
+                    }
                     if constexpr (QT == Q4_0) {
                         xb[t] = xl[x_lds_index(t, 8 * h + 4 + m, lane)];
+                        if constexpr (!XS) {
 #pragma unroll
-                        for (int b = 0; b < 4; ++b) xs[t] = xs[t] + xb[t][b];
+                            for (int b = 0; b < 4; ++b) xs[t] = xs[t] + xb[t][b];
+                        }
                     }
                 }
             }
@@ -199,7 +205,7 @@ __device__ __forceinline__ void pair_accumulate(const uint32_t (&dw)[R][PairTrai
             const float d = pair_scale<QT>(dw[r], h);
 #pragma unroll
             for (int t = 0; t < TT; ++t) {
-                const float x_sum = XR ? xg.xs[t][h] : xs[t];
+                const float x_sum = XR ? xg.xs[t][h] : (XS ? xsum[t][h] : xs[t]);
                 const float c = d * fmaf(-PT::OFF, x_sum, s[r][t]);
                 acc[t * R + r] += valid ? c : 0.f;
             }
@@ -334,6 +340,11 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t *__restrict__ W
     for (int i = 0; i < NV; ++i) acc[i] = 0.f;
 
     PairXRegs<XR ? TT : 1> xg;
+    // XS: x of a single pair step stays in LDS for the run; this lane's block sums,
+    // once. (With several steps held, selecting the step's sums per item measured
+    // slower than adding them up again: Q8_0 4096 x 12288 at T = 2, 22 -> 34 us.)
+    constexpr bool XS = !MULTI && !XR && NS == 1;
+    float xsp[XS ? NXS : 1][TT][2] = {};
     int csg = blockIdx.x, cpi = 0;  // item being computed
     // x of the item's step into LDS (all four waves take part).
     auto stage_x = [&](const auto &xr) __attribute__((always_inline)) {
@@ -350,8 +361,18 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t *__restrict__ W
     };
     auto compute = [&](const uint32_t (&dw)[R][PT::DW]) __attribute__((always_inline)) {
         const int p = lane + 64 * cpi;
-        pair_accumulate<QT, TT, R, XR>(dw, xl + (MULTI ? 0 : cpi * TT * 1024), xg, lane,
-                                       p < npairs, acc);
+        float cur[TT][2];
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                cur[t][h] = xsp[0][t][h];
+#pragma unroll
+                for (int st = 1; st < (XS ? NXS : 1); ++st)
+                    if (cpi == st) cur[t][h] = xsp[st][t][h];
+            }
+        pair_accumulate<QT, TT, R, XR, XS>(dw, xl + (MULTI ? 0 : cpi * TT * 1024), xg, cur, lane,
+                                           p < npairs, acc);
         if (++cpi == ipg) {  // group complete: reduce over the lanes and store
             cpi = 0;
             float v[NV];
@@ -399,6 +420,31 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t *__restrict__ W
             }
         }
         __syncthreads();
+        if constexpr (XS) {
+            // the order of pair_accumulate's FMA chain (see there)
+            using PT = PairTraits<QT>;
+#pragma unroll
+            for (int st = 0; st < NXS; ++st)
+#pragma unroll
+                for (int t = 0; t < TT; ++t)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const f4_t *xs_l = xl + st * TT * 1024;
+                        float a = 0.f;
+#pragma unroll
+                        for (int m = 0; m < PT::WORDS; ++m) {
+                            const f4_t qa = xs_l[x_lds_index(t, 8 * h + m, lane)];
+#pragma unroll
+                            for (int b = 0; b < 4; ++b) a = a + qa[b];
+                            if constexpr (QT == Q4_0) {
+                                const f4_t qb = xs_l[x_lds_index(t, 8 * h + 4 + m, lane)];
+#pragma unroll
+                                for (int b = 0; b < 4; ++b) a = a + qb[b];
+                            }
+                        }
+                        xsp[st][t][h] = a;
+                    }
+        }
         if constexpr (XR) {
 #pragma unroll
             for (int t = 0; t < TT; ++t) {
