@@ -150,10 +150,20 @@ def cpu_baseline(T, ops, inputs, target_s=12.0):
         flops += f2
         dt += d2
         reps += 1
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": oracle.num_threads(),
+        "cpu": cpu,
         "kind": "oracle",
         "sample": "the step's %d ops on the first %d of %d token rows, %d run(s) (%.1f GFLOP, %.1f s)"
                   % (len(ops), ts, T, reps, flops / 1e9, dt),
