@@ -433,34 +433,43 @@ def main():
             w, x, y = P(dev_w[wset][label].data_ptr()), P(bufs[src].data_ptr()), P(Y.data_ptr())
             if label.startswith("lm_head_"):
                 pf.lm_head_argmax(qtype, dev_w[wset][label], n, k, bufs[src][0], bufs["logits"], bufs["token"])
-                calls[(op[0], wset)] = (lib.pf_lm_head_argmax, (
-                    qtype, w, n, k, x, P(bufs["logits"].data_ptr()), P(bufs["token"].data_ptr()), hstream))
+                calls[(op[0], wset)] = [(lib.pf_lm_head_argmax, (
+                    qtype, w, n, k, x, P(bufs["logits"].data_ptr()), P(bufs["token"].data_ptr()), hstream))]
                 continue
             if label.startswith("rmsnorm_"):
                 if workspace is None:
                     raise SystemExit("the RMSNorm prologue needs a workspace")
                 pf.gemm_rmsnorm(qtype, dev_w[wset][label], n, k, bufs[src], bufs["norm_w"], NORM_EPS, Y, epi,
                                 leg, workspace)
-                calls[(op[0], wset)] = (lib.pf_gemm_rmsnorm, (
+                calls[(op[0], wset)] = [(lib.pf_gemm_rmsnorm, (
                     qtype, w, n, k, x, T, P(bufs["norm_w"].data_ptr()), NORM_EPS, y, n, epi, leg,
-                    P(workspace.data_ptr()), workspace.numel(), hstream))
+                    P(workspace.data_ptr()), workspace.numel(), hstream))]
                 continue
             # the checks the binding makes, once
             pf.gemm_ws(qtype, dev_w[wset][label], n, k, bufs[src], Y, epi, leg, workspace) if use_ws \
                 else pf.gemm(qtype, dev_w[wset][label], n, k, bufs[src], Y, epi, leg)
-            if use_ws:
+            if use_ws and leg == 1 and T > 8:
+                # the same kernels as pf_gemm_ws in two calls, so that the GEMM's own
+                # launch can be timed: X rounded to fp16 into the workspace, then the GEMM
+                ws, wsb = P(workspace.data_ptr()), workspace.numel()
+                calls[(op[0], wset)] = [(lib.pf_prepare_x, (qtype, k, x, T, ws, wsb, hstream)),
+                                        (lib.pf_gemm_prepared, (qtype, w, n, k, T, y, n, epi, ws, wsb, hstream))]
+            elif use_ws:
                 ws = P(workspace.data_ptr()) if workspace is not None else P(0)
                 wsb = workspace.numel() if workspace is not None else 0
-                calls[(op[0], wset)] = (lib.pf_gemm_ws, (qtype, w, n, k, x, T, y, epi, leg, ws, wsb, hstream))
+                calls[(op[0], wset)] = [(lib.pf_gemm_ws, (qtype, w, n, k, x, T, y, epi, leg, ws, wsb, hstream))]
             else:
-                calls[(op[0], wset)] = (lib.pf_gemm, (qtype, w, n, k, x, T, y, epi, leg, hstream))
+                calls[(op[0], wset)] = [(lib.pf_gemm, (qtype, w, n, k, x, T, y, epi, leg, hstream))]
     torch.cuda.synchronize()
 
-    def launch(op, wset):
-        fn, argv = calls[(op[0], wset)]
-        st = fn(*argv)
-        if st != 0:
-            raise pf.PfError(st, fn.__name__)
+    def launch(op, wset, marks=None):
+        """The op's C-ABI calls; marks[i + 1] is recorded after call i."""
+        for i, (fn, argv) in enumerate(calls[(op[0], wset)]):
+            st = fn(*argv)
+            if st != 0:
+                raise pf.PfError(st, fn.__name__)
+            if marks is not None:
+                marks[i + 1].record(stream)
 
     for i in range(args.warmup):
         for op in ops:
@@ -468,35 +477,42 @@ def main():
     torch.cuda.synchronize()
     log("warmup done (%d weight copies)" % copies)
 
-    # ---- timed region: K steps. HIP events on the launch stream: around every
-    # launch when a step has several ops; around the whole region when it has one,
-    # so that the launches run back to back as in the kernel trace (a pair of event
-    # markers around each microsecond-scale launch would add their own gaps).
+    # ---- timed region: K steps. HIP events on the launch stream: before every op
+    # and after each of its C-ABI calls when a step has several ops (so an op that
+    # is a conversion call then a GEMM call gives the GEMM's own duration); around
+    # the whole region when it has one, so that the launches run back to back as in
+    # the kernel trace (event markers around each microsecond-scale launch would add
+    # their own gaps).
     single = len(ops) == 1
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in ops] for _ in range(1 if single else args.steps)]
+    newev = lambda: torch.cuda.Event(enable_timing=True)
+    nparts = [len(calls[(op[0], 0)]) for op in ops]
+    ev = [[[newev() for _ in range(1 + nparts[j])] for j in range(len(ops))]
+          for _ in range(1 if single else args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     if single:
         ev[0][0][0].record(stream)
         for s in range(args.steps):
             launch(ops[0], s % copies)
-        ev[0][0][1].record(stream)
+        ev[0][0][-1].record(stream)
     else:
         for s in range(args.steps):
             for j, op in enumerate(ops):
                 ev[s][j][0].record(stream)
-                launch(op, s % copies)
-                ev[s][j][1].record(stream)
+                launch(op, s % copies, ev[s][j])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
     step_flops = sum(op_flops(op, T) for op in ops)
     ms_per_step = elapsed * 1e3 / args.steps
     if single:
-        kern_ms = [ev[0][0][0].elapsed_time(ev[0][0][1]) / args.steps]
+        op_ms = [ev[0][0][0].elapsed_time(ev[0][0][-1]) / args.steps]
+        kern_ms = list(op_ms)
     else:
-        kern_ms = [float(np.mean([ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(args.steps)]))
+        op_ms = [float(np.mean([ev[s][j][0].elapsed_time(ev[s][j][-1]) for s in range(args.steps)]))
+                 for j in range(len(ops))]
+        # the op's last call (the GEMM, when X is converted by a call of its own)
+        kern_ms = [float(np.mean([ev[s][j][-2].elapsed_time(ev[s][j][-1]) for s in range(args.steps)]))
                    for j in range(len(ops))]
     dom = int(np.argmax(kern_ms))
     dop = ops[dom]
@@ -512,8 +528,10 @@ def main():
         peak = PEAK["fp16_mfma_tflops"] if leg == 1 else PEAK["fp32_mfma_tflops"]
         roofline = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                     "frac": achieved / peak, "traffic": load_traffic(args.workload, dop[0], family)}
-    roofline["kernel"] = dop[0]
+    roofline["kernel"] = dop[0] + (" (GEMM call)" if nparts[dom] > 1 else "")
     roofline["avg_launch_us"] = kern_ms[dom] * 1e3
+    roofline["op_us"] = op_ms[dom] * 1e3
+    roofline["op_frac"] = roofline["frac"] * kern_ms[dom] / op_ms[dom]
 
     out = {
         "metric": METRIC,
@@ -530,12 +548,13 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "T": T, "hidden": HIDDEN, "intermediate": INTER,
                    "leg": "f16" if leg == 1 else "f32",
-                   "ops": [{"op": op[0], "n": op[2], "k": op[3], "avg_us": kern_ms[j] * 1e3,
-                            "tflops": op_flops(op, T) / (kern_ms[j] * 1e-3) / 1e12,
-                            "gbs": op_bytes(op, T) / (kern_ms[j] * 1e-3) / 1e9}
+                   "ops": [{"op": op[0], "n": op[2], "k": op[3], "avg_us": op_ms[j] * 1e3,
+                            "gemm_call_us": kern_ms[j] * 1e3,
+                            "tflops": op_flops(op, T) / (op_ms[j] * 1e-3) / 1e12,
+                            "gbs": op_bytes(op, T) / (op_ms[j] * 1e-3) / 1e9,
+                            "calls": [fn.__name__ for fn, _ in calls[(op[0], 0)]]}
                            for j, op in enumerate(ops)],
                    "weight_copies": copies,
-                   "entry_point": "pf_gemm_ws" if use_ws else "pf_gemm",
                    "workspace_bytes": ws_bytes if use_ws else 0},
         "roofline": roofline,
     }

@@ -201,6 +201,25 @@ int64_t pf_rmsnorm_workspace_bytes(int qtype, int64_t n, int64_t k, int64_t T, i
 int pf_lm_head_argmax(int qtype, const void *W_blocks, int64_t n, int64_t k, const float *x,
                       float *logits, int32_t *token, void *stream);
 
+/* The f16 leg's matrix-core GEMM of pf_gemm_ws in two calls, so that one rounding of X
+ * serves several projections of the same rows (separate q, k and v weights, say):
+ *  pf_prepare_x   rounds X [T][k] (f32, 16-byte aligned) to binary16 into the workspace,
+ *                 in the layout the GEMM for (qtype, T) reads; the copy depends on qtype
+ *                 (the k order within groups of four follows the block type's decode).
+ *                 Needs ceil(T / 32) * 32 * k * 2 bytes of workspace.
+ *  pf_gemm_prepared  the GEMM on that copy: Y = epilogue(X . W_hat^T) with Y, ldy as
+ *                 pf_gemm_ex; the workspace must hold pf_workspace_bytes(qtype, n, k, T,
+ *                 epilogue, PF_LEG_F16) bytes and its first part a pf_prepare_x copy for
+ *                 the same qtype, k and T, enqueued before it on the same stream (or
+ *                 synchronised). The GEMM reads the copy and writes only past it (split-K
+ *                 partial sums), so the copy stays valid for further calls.
+ * The result is pf_gemm_ws's, bit for bit. T <= PF_GEMV_MAX_T (the GEMV, which reads
+ * f32 X) is PF_E_PATH; T == 0 is a no-op. Other errors as pf_gemm_ws. */
+int pf_prepare_x(int qtype, int64_t k, const float *X, int64_t T, void *workspace, int64_t workspace_bytes,
+                 void *stream);
+int pf_gemm_prepared(int qtype, const void *W_blocks, int64_t n, int64_t k, int64_t T, float *Y, int64_t ldy,
+                     int epilogue, void *workspace, int64_t workspace_bytes, void *stream);
+
 /* Which family pf_gemm would run for these sizes: PF_PATH_GEMM, PF_PATH_GEMV, 0
  * for T == 0 (nothing runs), or -PF_E_* for arguments pf_gemm would refuse
  * (pointers are not checked). Host-only; touches no GPU state. */

@@ -25,7 +25,8 @@ LEGS = {"f32": PF_LEG_F32, "f16": PF_LEG_F16}
 
 # Every symbol include/pf_gemm.h declares.
 EXPORTS = ("pf_gemm", "pf_gemm_path", "pf_workspace_bytes", "pf_gemm_ws", "pf_gemm_ex",
-           "pf_gemm_rmsnorm", "pf_rmsnorm_workspace_bytes", "pf_lm_head_argmax", "pf_select_path",
+           "pf_gemm_rmsnorm", "pf_rmsnorm_workspace_bytes", "pf_lm_head_argmax", "pf_prepare_x",
+           "pf_gemm_prepared", "pf_select_path",
            "pf_dequant_f32",
            "pf_dequant_f16", "pf_weight_bytes", "pf_strerror")
 
@@ -65,6 +66,10 @@ def load():
     lib.pf_rmsnorm_workspace_bytes.restype = i64
     lib.pf_lm_head_argmax.argtypes = [i32, P, i64, i64, P, P, P, P]
     lib.pf_lm_head_argmax.restype = i32
+    lib.pf_prepare_x.argtypes = [i32, i64, P, i64, P, i64, P]
+    lib.pf_prepare_x.restype = i32
+    lib.pf_gemm_prepared.argtypes = [i32, P, i64, i64, i64, P, i64, i32, P, i64, P]
+    lib.pf_gemm_prepared.restype = i32
     lib.pf_select_path.argtypes = [i32, i64, i64, i64, i32, i32]
     lib.pf_select_path.restype = i32
     lib.pf_dequant_f32.argtypes = [i32, P, i64, i64, P, P]
@@ -224,6 +229,41 @@ def lm_head_argmax(qtype, W, n, k, x, logits, token, stream=None):
     if st != PF_OK:
         raise PfError(st, "pf_lm_head_argmax")
     return token
+
+
+def prepare_x(qtype, k, X, workspace, stream=None):
+    """X [T][k] (float32 device) rounded to binary16 into the workspace for
+    gemm_prepared (see pf_prepare_x)."""
+    import torch
+    T = X.numel() // k if k > 0 else 0
+    if X.dtype != torch.float32 or X.numel() != T * k:
+        raise ValueError("X must be float32 [T][k]")
+    st = load().pf_prepare_x(qtype, k, _dev_ptr(X, "X"), T, _dev_ptr(workspace, "workspace"),
+                             workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    if st != PF_OK:
+        raise PfError(st, "pf_prepare_x")
+    return workspace
+
+
+def gemm_prepared(qtype, W, n, k, T, Y, epilogue, workspace, stream=None):
+    """The f16-leg GEMM on a prepare_x copy in the workspace (see pf_gemm_prepared); Y
+    a [T][n] float32 device view as in gemm_ex."""
+    import torch
+    if Y.dtype != torch.float32 or W.dtype != torch.uint8:
+        raise TypeError("Y must be float32 and W uint8")
+    if not Y.is_cuda or Y.dim() != 2 or tuple(Y.shape) != (T, n) or (T > 1 and Y.stride(1) != 1):
+        raise ValueError("Y must be a [T][n] device view with unit stride within rows")
+    ldy = Y.stride(0) if T > 1 else n
+    rows = 2 * n if epilogue == PF_GATE_UP_SWIGLU else n
+    need = load().pf_weight_bytes(qtype, rows, k)
+    if need >= 0 and W.numel() < need:
+        raise ValueError("W holds %d bytes, %d needed" % (W.numel(), need))
+    st = load().pf_gemm_prepared(qtype, _dev_ptr(W, "W"), n, k, T, ctypes.c_void_p(Y.data_ptr()), ldy, epilogue,
+                                 _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                                 _stream_handle(stream))
+    if st != PF_OK:
+        raise PfError(st, "pf_gemm_prepared")
+    return Y
 
 
 def gemm(qtype, W, n, k, X, Y, epilogue, leg, stream=None, path=PF_PATH_AUTO):

@@ -236,6 +236,63 @@ int pf_lm_head_argmax(int qtype, const void *W_blocks, int64_t n, int64_t k, con
     return pf::launch_argmax(logits, (int)n, token, s) == hipSuccess ? PF_OK : PF_E_LAUNCH;
 }
 
+int pf_prepare_x(int qtype, int64_t k, const float *X, int64_t T, void *workspace, int64_t workspace_bytes,
+                 void *stream) {
+    if (block_bytes(qtype) < 0) return PF_E_QTYPE;
+    if (T < 0 || k < 256 || k % 256 != 0 || (T > 0 && k > kMax31 / T)) return PF_E_SHAPE;
+    if (T > 0 && T <= PF_GEMV_MAX_T) return PF_E_PATH;  // the GEMV reads f32 X
+    if (T == 0) return PF_OK;
+    if (!X) return PF_E_NULL;
+    if (!aligned16(X)) return PF_E_ALIGN;
+    const int64_t need = (T + 31) / 32 * 32 * k * 2;
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PF_E_WORKSPACE;
+    if (overlap(workspace, need, X, T * k * 4)) return PF_E_WORKSPACE;
+    pf::GemmArgs a;
+    a.qtype = qtype;
+    a.epilogue = PF_PLAIN;
+    a.W = nullptr;
+    a.X = X;
+    a.Y = nullptr;
+    a.n = 1;
+    a.ldy = 1;
+    a.k = (int)k;
+    a.T = (int)T;
+    return pf::launch_prepare_x_f16(a, workspace, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? PF_OK
+               : PF_E_LAUNCH;
+}
+
+int pf_gemm_prepared(int qtype, const void *W_blocks, int64_t n, int64_t k, int64_t T, float *Y, int64_t ldy,
+                     int epilogue, void *workspace, int64_t workspace_bytes, void *stream) {
+    int64_t n_w = 0;
+    const int st = check_sizes(qtype, n, k, T, epilogue, PF_LEG_F16, &n_w);
+    if (st != PF_OK) return st;
+    if (ldy < n || (T > 0 && ldy > kMax31 / T)) return PF_E_SHAPE;
+    if (T > 0 && T <= PF_GEMV_MAX_T) return PF_E_PATH;
+    if (T == 0) return PF_OK;
+    if (!W_blocks || !Y) return PF_E_NULL;
+    if (!aligned16(W_blocks) || !aligned16(Y)) return PF_E_ALIGN;
+    const int64_t w_bytes = n_w * (k / 32) * block_bytes(qtype), y_bytes = ((T - 1) * ldy + n) * 4;
+    if (overlap(Y, y_bytes, W_blocks, w_bytes)) return PF_E_ALIAS;
+    const int64_t need = pf::f16_ws_bytes((int)T, (int)n, (int)k, epilogue);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PF_E_WORKSPACE;
+    if (overlap(workspace, need, W_blocks, w_bytes) || overlap(workspace, need, Y, y_bytes))
+        return PF_E_WORKSPACE;
+    pf::GemmArgs a;
+    a.qtype = qtype;
+    a.epilogue = epilogue;
+    a.W = static_cast<const uint8_t *>(W_blocks);
+    a.X = nullptr;
+    a.Y = Y;
+    a.n = (int)n;
+    a.ldy = (int)ldy;
+    a.k = (int)k;
+    a.T = (int)T;
+    return pf::launch_gemm_f16_prepared(a, workspace, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? PF_OK
+               : PF_E_LAUNCH;
+}
+
 int64_t pf_rmsnorm_workspace_bytes(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int leg) {
     int64_t n_w = 0;
     const int st = check_sizes(qtype, n, k, T, epilogue, leg, &n_w);

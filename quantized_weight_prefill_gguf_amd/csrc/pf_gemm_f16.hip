@@ -1281,10 +1281,11 @@ hipError_t launch_coop_q(const GemmArgs &a, uint16_t *xh, hipStream_t s) {
     return a.T >= COOP_T512 ? launch_coop_e<QT, 512>(a, xh, s) : launch_coop_e<QT, 256>(a, xh, s);
 }
 
-hipError_t launch_gemm_f16_ws(const GemmArgs &a, void *workspace, hipStream_t s) {
+// X -> binary16 into the workspace, in the layout the GEMM for (qtype, T) reads: A-fragment
+// order for T >= 256 (the cooperative kernel), [T][k] below.
+hipError_t launch_prepare_x_f16(const GemmArgs &a, void *workspace, hipStream_t s) {
     uint16_t *xh = static_cast<uint16_t *>(workspace);
     if (a.T >= 256) {
-        // The cooperative-decode kernel takes X in A-fragment order.
         const int count = (a.T + 31) / 32 * 32 * (a.k / 16);  // (row, 16-k slice) pairs
         const dim3 g((count + 255) / 256);
         if (a.norm_inv) {
@@ -1301,9 +1302,7 @@ hipError_t launch_gemm_f16_ws(const GemmArgs &a, void *workspace, hipStream_t s)
             hipLaunchKernelGGL((x_to_frag_kernel<Q8_0, false>), g, dim3(256), 0, s, a.X, xh, a.T, a.k,
                                count, nullptr, nullptr);
         }
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        return a.qtype == Q4_0 ? launch_coop_q<Q4_0>(a, xh, s) : launch_coop_q<Q8_0>(a, xh, s);
+        return hipGetLastError();
     }
     const int count8 = a.T * (a.k / 8);
     const dim3 g((count8 + 255) / 256);
@@ -1321,9 +1320,21 @@ hipError_t launch_gemm_f16_ws(const GemmArgs &a, void *workspace, hipStream_t s)
         hipLaunchKernelGGL((x_to_f16_kernel<Q8_0, false>), g, dim3(256), 0, s, a.X, xh, count8, a.k,
                            nullptr, nullptr);
     }
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    return hipGetLastError();
+}
+
+// The f16 GEMM on X already in the workspace (launch_prepare_x_f16 with the same
+// qtype, k and T); any split-K partial sums go behind it.
+hipError_t launch_gemm_f16_prepared(const GemmArgs &a, void *workspace, hipStream_t s) {
+    uint16_t *xh = static_cast<uint16_t *>(workspace);
+    if (a.T >= 256) return a.qtype == Q4_0 ? launch_coop_q<Q4_0>(a, xh, s) : launch_coop_q<Q8_0>(a, xh, s);
     return a.qtype == Q4_0 ? launch_q<Q4_0>(a, xh, s) : launch_q<Q8_0>(a, xh, s);
+}
+
+hipError_t launch_gemm_f16_ws(const GemmArgs &a, void *workspace, hipStream_t s) {
+    const hipError_t e = launch_prepare_x_f16(a, workspace, s);
+    if (e != hipSuccess) return e;
+    return launch_gemm_f16_prepared(a, workspace, s);
 }
 
 hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t s) {

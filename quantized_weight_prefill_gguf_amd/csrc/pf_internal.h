@@ -32,6 +32,10 @@ hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t s);
 // order the A fragments take), then the GEMM streams fp16 X. The workspace holds
 // T * k halves.
 hipError_t launch_gemm_f16_ws(const GemmArgs &a, void *workspace, hipStream_t s);
+// The two halves of launch_gemm_f16_ws: X to binary16 into the workspace, then the
+// GEMM on that copy.
+hipError_t launch_prepare_x_f16(const GemmArgs &a, void *workspace, hipStream_t s);
+hipError_t launch_gemm_f16_prepared(const GemmArgs &a, void *workspace, hipStream_t s);
 // Workspace bytes launch_gemm_f16_ws takes: X as binary16 (T rounded up to a
 // multiple of 32), and for T >= 256 with a K split, behind it (at the next 256-byte
 // boundary) one [T][n] f32 block of partial sums per split.

@@ -271,6 +271,36 @@ def test_lm_head_argmax_argument_checks(lib):
     assert g(tok=x) == pf.PF_E_ALIAS
 
 
+def test_prepared_argument_checks(lib):
+    P = ctypes.c_void_p
+    W, X, Y, WS = FAKE, FAKE + (1 << 32), FAKE + (2 << 32), FAKE + (3 << 32)
+    n, k, T = 64, 256, 40
+    xneed = 64 * k * 2
+    px = lambda **kw: lib.pf_prepare_x(kw.get("qtype", 0), kw.get("k", k), P(kw.get("X", X)), kw.get("T", T),
+                                       P(kw.get("ws", WS)), kw.get("wsb", xneed), None)
+    assert px(qtype=7) == pf.PF_E_QTYPE
+    assert px(k=300) == pf.PF_E_SHAPE
+    assert px(T=8) == pf.PF_E_PATH            # the GEMV reads f32 X
+    assert px(T=0) == pf.PF_OK
+    assert px(X=0) == pf.PF_E_NULL
+    assert px(X=X + 4) == pf.PF_E_ALIGN
+    assert px(wsb=xneed - 16) == pf.PF_E_WORKSPACE
+    assert px(ws=X + 64) == pf.PF_E_WORKSPACE
+    need = lib.pf_workspace_bytes(0, n, k, T, 0, pf.PF_LEG_F16)
+    gp = lambda **kw: lib.pf_gemm_prepared(kw.get("qtype", 0), P(kw.get("W", W)), kw.get("n", n), k,
+                                           kw.get("T", T), P(kw.get("Y", Y)), kw.get("ldy", n), kw.get("epi", 0),
+                                           P(kw.get("ws", WS)), kw.get("wsb", need), None)
+    assert gp(T=5) == pf.PF_E_PATH
+    assert gp(ldy=n - 1) == pf.PF_E_SHAPE
+    assert gp(epi=4) == pf.PF_E_EPILOGUE
+    assert gp(W=0) == pf.PF_E_NULL
+    assert gp(Y=Y + 8) == pf.PF_E_ALIGN
+    assert gp(Y=W + 16) == pf.PF_E_ALIAS
+    assert gp(wsb=need - 16) == pf.PF_E_WORKSPACE
+    assert gp(ws=Y + 16) == pf.PF_E_WORKSPACE
+    assert gp(T=0) == pf.PF_OK
+
+
 def test_dequant_argument_checks(lib):
     P = ctypes.c_void_p
     W, out = P(FAKE), P(FAKE + (1 << 32))
