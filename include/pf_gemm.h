@@ -64,14 +64,16 @@ enum { PF_PLAIN = 0, PF_RESIDUAL = 1, PF_GATE_UP_SWIGLU = 2 };
  *              RNE_fp16(x), fp32 accumulation, f32 output. X stays f32 in memory;
  *              pf_gemm rounds it inside the GEMM, pf_gemm_ws once into its
  *              workspace.
- *  For T <= PF_GEMV_MAX_T both legs run the f32 GEMV, whose error bound is the
- *  f32 leg's and therefore also meets the f16 leg's.
+ *  Where the GEMV runs (T <= PF_GEMV_MAX_T, see PF_PATH_AUTO) both legs compute in
+ *  f32, whose error bound is the f32 leg's and therefore also meets the f16 leg's.
  */
 enum { PF_LEG_F32 = 0, PF_LEG_F16 = 1 };
 
 /* Kernel family. PF_PATH_AUTO picks the GEMV for 1 <= T <= PF_GEMV_MAX_T and the
- * tiled matrix-core GEMM otherwise. The other two force a family (tests compare
- * them); PF_PATH_GEMV requires T <= PF_GEMV_MAX_T. */
+ * tiled matrix-core GEMM otherwise, except that the f16 leg's PLAIN and RESIDUAL
+ * epilogues take the GEMM from T = 3 (faster there: its K split spreads the weight
+ * stream over every CU). The other two force a family (tests compare them);
+ * PF_PATH_GEMV requires T <= PF_GEMV_MAX_T. */
 enum { PF_PATH_AUTO = 0, PF_PATH_GEMM = 1, PF_PATH_GEMV = 2 };
 #define PF_GEMV_MAX_T 8
 
@@ -182,7 +184,7 @@ int pf_gemm_rmsnorm(int qtype, const void *W_blocks, int64_t n, int64_t k, const
 
 /* Workspace bytes pf_gemm_rmsnorm needs, or -PF_E_* for sizes pf_gemm would refuse.
  * 0 for T == 0; else ceil(T * 4 / 256) * 256 (the rows' 1 / rms) plus, on the f16
- * leg's matrix-core GEMM (T > PF_GEMV_MAX_T), pf_workspace_bytes() for the same
+ * leg's matrix-core GEMM (the family PF_PATH_AUTO picks), pf_workspace_bytes() for the same
  * sizes, otherwise T * k * 4 (Xn in f32). Host-only. */
 int64_t pf_rmsnorm_workspace_bytes(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int leg);
 
@@ -213,8 +215,11 @@ int pf_lm_head_argmax(int qtype, const void *W_blocks, int64_t n, int64_t k, con
  *                 the same qtype, k and T, enqueued before it on the same stream (or
  *                 synchronised). The GEMM reads the copy and writes only past it (split-K
  *                 partial sums), so the copy stays valid for further calls.
- * The result is pf_gemm_ws's, bit for bit. T <= PF_GEMV_MAX_T (the GEMV, which reads
- * f32 X) is PF_E_PATH; T == 0 is a no-op. Other errors as pf_gemm_ws. */
+ * The result is pf_gemm_ws's, bit for bit, wherever that is deterministic (from 256 rows;
+ * below, a K split adds its partial sums with atomics in any order). pf_gemm_prepared
+ * returns PF_E_PATH where PF_PATH_AUTO picks the GEMV for the f16 leg (which reads f32 X:
+ * T <= 2, or T <= PF_GEMV_MAX_T with the SwiGLU epilogue); T == 0 is a no-op. Other
+ * errors as pf_gemm_ws. */
 int pf_prepare_x(int qtype, int64_t k, const float *X, int64_t T, void *workspace, int64_t workspace_bytes,
                  void *stream);
 int pf_gemm_prepared(int qtype, const void *W_blocks, int64_t n, int64_t k, int64_t T, float *Y, int64_t ldy,

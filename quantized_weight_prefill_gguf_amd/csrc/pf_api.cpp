@@ -45,6 +45,17 @@ int check_sizes(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int le
     return PF_OK;
 }
 
+// Kernel family of PF_PATH_AUTO for T >= 1 rows. The GEMV up to PF_GEMV_MAX_T rows,
+// except on the f16 leg from 3 rows for PLAIN and RESIDUAL: there the matrix-core
+// GEMM's 32-row tile, split along K over every CU, streams the weights faster than
+// the GEMV (which reads them once per pair of rows). The SwiGLU epilogue cannot
+// split K, so it keeps the GEMV up to PF_GEMV_MAX_T.
+int auto_path(int64_t T, int epilogue, int leg) {
+    if (T > PF_GEMV_MAX_T) return PF_PATH_GEMM;
+    if (leg == PF_LEG_F16 && epilogue != PF_GATE_UP_SWIGLU && T >= 3) return PF_PATH_GEMM;
+    return PF_PATH_GEMV;
+}
+
 // Bytes of workspace the f16 leg's GEMM takes (X as binary16, T rounded up to a
 // multiple of 32 for the fragment-ordered copy, plus the partial sums of a K split),
 // else 0.
@@ -68,7 +79,7 @@ int gemm_impl(int qtype, const void *W, int64_t n, int64_t k, const float *X, in
     const int64_t w_bytes = n_w * (k / 32) * block_bytes(qtype);
     const int64_t x_bytes = T * k * 4, y_bytes = ((T - 1) * ldy + n) * 4;  // Y's rows and gaps
     if (overlap(Y, y_bytes, X, x_bytes) || overlap(Y, y_bytes, W, w_bytes)) return PF_E_ALIAS;
-    const int use = path == PF_PATH_AUTO ? (T <= PF_GEMV_MAX_T ? PF_PATH_GEMV : PF_PATH_GEMM) : path;
+    const int use = path == PF_PATH_AUTO ? auto_path(T, epilogue, leg) : path;
     const int64_t need = with_ws ? ws_need(n, k, T, epilogue, leg, use) : 0;
     if (need > 0) {
         if (!ws || ws_bytes < need || !aligned16(ws)) return PF_E_WORKSPACE;
@@ -129,7 +140,7 @@ int rms_impl(int qtype, const void *W, int64_t n, int64_t k, const float *X, int
     if (overlap(Y, y_bytes, X, x_bytes) || overlap(Y, y_bytes, W, w_bytes) ||
         overlap(Y, y_bytes, norm_w, nw_bytes))
         return PF_E_ALIAS;
-    const int use = T <= PF_GEMV_MAX_T ? PF_PATH_GEMV : PF_PATH_GEMM;
+    const int use = auto_path(T, epilogue, leg);
     const int64_t need = rms_ws_need(n, k, T, epilogue, leg, use);
     if (!ws || ws_bytes < need || !aligned16(ws)) return PF_E_WORKSPACE;
     if (overlap(ws, need, W, w_bytes) || overlap(ws, need, X, x_bytes) || overlap(ws, need, Y, y_bytes) ||
@@ -240,7 +251,6 @@ int pf_prepare_x(int qtype, int64_t k, const float *X, int64_t T, void *workspac
                  void *stream) {
     if (block_bytes(qtype) < 0) return PF_E_QTYPE;
     if (T < 0 || k < 256 || k % 256 != 0 || (T > 0 && k > kMax31 / T)) return PF_E_SHAPE;
-    if (T > 0 && T <= PF_GEMV_MAX_T) return PF_E_PATH;  // the GEMV reads f32 X
     if (T == 0) return PF_OK;
     if (!X) return PF_E_NULL;
     if (!aligned16(X)) return PF_E_ALIGN;
@@ -268,7 +278,8 @@ int pf_gemm_prepared(int qtype, const void *W_blocks, int64_t n, int64_t k, int6
     const int st = check_sizes(qtype, n, k, T, epilogue, PF_LEG_F16, &n_w);
     if (st != PF_OK) return st;
     if (ldy < n || (T > 0 && ldy > kMax31 / T)) return PF_E_SHAPE;
-    if (T > 0 && T <= PF_GEMV_MAX_T) return PF_E_PATH;
+    // where pf_gemm_ws would run the GEMV (which reads f32 X) there is no prepared form
+    if (T > 0 && auto_path(T, epilogue, PF_LEG_F16) != PF_PATH_GEMM) return PF_E_PATH;
     if (T == 0) return PF_OK;
     if (!W_blocks || !Y) return PF_E_NULL;
     if (!aligned16(W_blocks) || !aligned16(Y)) return PF_E_ALIGN;
@@ -297,7 +308,7 @@ int64_t pf_rmsnorm_workspace_bytes(int qtype, int64_t n, int64_t k, int64_t T, i
     int64_t n_w = 0;
     const int st = check_sizes(qtype, n, k, T, epilogue, leg, &n_w);
     if (st != PF_OK) return -st;
-    return rms_ws_need(n, k, T, epilogue, leg, T <= PF_GEMV_MAX_T ? PF_PATH_GEMV : PF_PATH_GEMM);
+    return rms_ws_need(n, k, T, epilogue, leg, auto_path(T, epilogue, leg));
 }
 
 int64_t pf_workspace_bytes(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int leg) {
@@ -305,7 +316,7 @@ int64_t pf_workspace_bytes(int qtype, int64_t n, int64_t k, int64_t T, int epilo
     const int st = check_sizes(qtype, n, k, T, epilogue, leg, &n_w);
     if (st != PF_OK) return -st;
     if (T == 0) return 0;
-    return ws_need(n, k, T, epilogue, leg, T <= PF_GEMV_MAX_T ? PF_PATH_GEMV : PF_PATH_GEMM);
+    return ws_need(n, k, T, epilogue, leg, auto_path(T, epilogue, leg));
 }
 
 int pf_gemm_path(int qtype, const void *W_blocks, int64_t n, int64_t k, const float *X,
@@ -318,7 +329,7 @@ int pf_select_path(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int
     const int st = check_sizes(qtype, n, k, T, epilogue, leg, &n_w);
     if (st != PF_OK) return -st;
     if (T == 0) return 0;
-    return T <= PF_GEMV_MAX_T ? PF_PATH_GEMV : PF_PATH_GEMM;
+    return auto_path(T, epilogue, leg);
 }
 
 int pf_dequant_f32(int qtype, const void *W_blocks, int64_t rows, int64_t k, float *out,

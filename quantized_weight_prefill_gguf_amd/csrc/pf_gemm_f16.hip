@@ -63,6 +63,10 @@ template <int QT> __device__ __forceinline__ u2_t x_pack(f4_t v) {
 }  // namespace
 
 // Global weight row of local tile row lr, or -1 past the weight.
+// Workgroups of a 32-row tile resident per CU (waves per SIMD): as many as its LDS
+// (41 KB for Q4_0, 74 KB for Q8_0) and registers allow.
+constexpr int small_tile_waves(int qt) { return qt == Q4_0 ? 3 : 2; }
+
 template <int EPI, int NW>
 __device__ __forceinline__ int f16_weight_row(int tile_n, int lr, int n) {
     if constexpr (EPI == EPI_SWIGLU) {
@@ -78,16 +82,23 @@ __device__ __forceinline__ int f16_weight_row(int tile_n, int lr, int n) {
 
 template <int QT, int EPI, int MT, int NW, bool SPLIT, bool XH>
 __global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(1, 1)))
+__attribute__((amdgpu_waves_per_eu(1, MT <= 32 ? small_tile_waves(QT) : 1)))
 void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
                      float *__restrict__ Y, int n, int ldy, int k, int T, int tiles_m, int tiles_n,
                      int splits) {
     using CT = ChunkTraits<QT>;
     constexpr int BB = CT::BB;
-    constexpr int IT = MT / 64;           // 32-row MFMA tiles per wave
-    constexpr int JT = NW / 64;           // 32-column MFMA tiles per wave
+    // Waves: WVM x WVN over the tile. 32-row tiles (few token rows) put all four
+    // side by side along the weight rows, so that no two decode the same columns.
+    constexpr int WVM = MT >= 64 ? 2 : 1;
+    constexpr int WVN = 4 / WVM;
+    constexpr int IT = MT / (32 * WVM);   // 32-row MFMA tiles per wave
+    constexpr int JT = NW / (32 * WVN);   // 32-column MFMA tiles per wave
+    static_assert(IT >= 1 && JT >= 1 && MT % 32 == 0, "tile shape");
     constexpr int XF4 = MT / 32;          // f32 X: float4 loads per thread per step
-    constexpr int XH4 = MT / 64;          // fp16 X: 16-byte loads per thread per step
+    constexpr int XH4 = MT >= 64 ? MT / 64 : 1;  // fp16 X: 16-byte loads per thread per step
+    // fp16 X staging covers 64 rows per pass; a 32-row tile uses threads < 128 only.
+    const bool xh_store = MT >= 64 || threadIdx.x < 128;
     constexpr int U4 = CT::U4;                      // 16-byte pieces per row chunk
     constexpr int WROW = CT::ROW;
     constexpr int WBUF = NW * WROW + 16;            // +16: decode reads a dword past a row
@@ -106,7 +117,7 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WVN, wn = wave % WVN;
     const int c = lane & 31, h = lane >> 5;
 
     // Workgroup -> tile. Dispatch spreads consecutive workgroup ids over the 8
@@ -293,7 +304,7 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
     auto store_xh = [&](int xb, const u4_t (&src)[XH4]) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < XH4; ++i)
-            *reinterpret_cast<u4_t *>(&xs[xb][xdst + i * 64 * 32]) = src[i];
+            if (xh_store) *reinterpret_cast<u4_t *>(&xs[xb][xdst + i * 64 * 32]) = src[i];
     };
     auto fetch_xh = [&](int step, u4_t (&dst)[XH4]) __attribute__((always_inline)) {
         const uint8_t *xb = xbase + 64 * min(step, nsteps - 1);
@@ -452,7 +463,7 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
     asm volatile("" : "+v"(etid));
     if constexpr (EPI == EPI_SWIGLU) __syncthreads();  // the X buffers become scratch
     const int e_lane = etid & 63, e_wave = etid >> 6;
-    const int e_wm = e_wave >> 1, e_wn = e_wave & 1;
+    const int e_wm = e_wave / WVN, e_wn = e_wave % WVN;
     const int e_c = e_lane & 31, e_h = e_lane >> 5;
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
@@ -1037,7 +1048,7 @@ __global__ void zero_fill_kernel(float *__restrict__ Y, int T, int n, int ldy) {
 namespace {
 
 struct TileChoice {
-    int cfg;     // 0: 256x192, 1: 256x128, 2: 128x128, 3: 64x64
+    int cfg;     // 0: 256x192, 1: 256x128, 2: 128x128, 3: 64x64, 4: 32x128
     int splits;
 };
 
@@ -1051,6 +1062,27 @@ TileChoice choose_tiles(const GemmArgs &a) {
     const bool swiglu = a.epilogue == EPI_SWIGLU;
     const int nchunks = a.k / 256;
     const int cus = 256;
+    if (a.T <= 32) {
+        // One row tile: the matrix-core work is small and the time is the weight
+        // stream and its decode. 32 x 128 tiles (no column decoded twice), split
+        // along K to fill the resident slots: the split count minimises rounds of
+        // workgroups x (chunks per workgroup + one chunk's worth of fixed cost).
+        // SwiGLU cannot split: its epilogue is not linear in the partial sums.
+        const int tn = (a.n + 127) / 128;
+        if (swiglu) return TileChoice{4, 1};
+        const long slots = (long)cus * small_tile_waves(a.qtype);
+        int best_s = 1;
+        long best_c = -1;
+        for (int s = 1; s <= nchunks && s <= 32; ++s) {
+            const long rounds = ((long)tn * s + slots - 1) / slots;
+            const long cost = rounds * ((nchunks + s - 1) / s + 1);
+            if (best_c < 0 || cost < best_c) {
+                best_c = cost;
+                best_s = s;
+            }
+        }
+        return TileChoice{4, best_s};
+    }
     TileChoice best{3, 1};
     float best_t = 1e30f;
     for (int cfg = 0; cfg < 4; ++cfg) {
@@ -1096,7 +1128,8 @@ hipError_t launch_split(const GemmArgs &a, TileChoice tc, const uint16_t *xh, hi
     case 0: return launch_cfg<QT, EPI, 256, 192, SPLIT>(a, tc.splits, xh, s);
     case 1: return launch_cfg<QT, EPI, 256, 128, SPLIT>(a, tc.splits, xh, s);
     case 2: return launch_cfg<QT, EPI, 128, 128, SPLIT>(a, tc.splits, xh, s);
-    default: return launch_cfg<QT, EPI, 64, 64, SPLIT>(a, tc.splits, xh, s);
+    case 3: return launch_cfg<QT, EPI, 64, 64, SPLIT>(a, tc.splits, xh, s);
+    default: return launch_cfg<QT, EPI, 32, 128, SPLIT>(a, tc.splits, xh, s);
     }
 }
 

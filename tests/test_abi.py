@@ -69,7 +69,12 @@ def test_select_path(lib):
     sel = lib.pf_select_path
     assert sel(pf.PF_Q4_0, 4096, 4096, 0, pf.PF_PLAIN, pf.PF_LEG_F32) == 0
     for T in (1, 2, 8):
-        assert sel(pf.PF_Q4_0, 4096, 4096, T, pf.PF_PLAIN, pf.PF_LEG_F16) == pf.PF_PATH_GEMV
+        assert sel(pf.PF_Q4_0, 4096, 4096, T, pf.PF_PLAIN, pf.PF_LEG_F32) == pf.PF_PATH_GEMV
+        assert sel(pf.PF_Q4_0, 4096, 4096, T, pf.PF_GATE_UP_SWIGLU, pf.PF_LEG_F16) == pf.PF_PATH_GEMV
+    # f16 leg, PLAIN and RESIDUAL: the GEMM from three rows on
+    for T, want in ((1, pf.PF_PATH_GEMV), (2, pf.PF_PATH_GEMV), (3, pf.PF_PATH_GEMM), (8, pf.PF_PATH_GEMM)):
+        assert sel(pf.PF_Q4_0, 4096, 4096, T, pf.PF_PLAIN, pf.PF_LEG_F16) == want
+        assert sel(pf.PF_Q8_0, 4096, 4096, T, pf.PF_RESIDUAL, pf.PF_LEG_F16) == want
     for T in (9, 16, 512, 2048):
         assert sel(pf.PF_Q8_0, 4096, 12288, T, pf.PF_RESIDUAL, pf.PF_LEG_F16) == pf.PF_PATH_GEMM
     assert sel(5, 1, 256, 1, 0, 0) == -pf.PF_E_QTYPE
@@ -141,7 +146,12 @@ def test_workspace_bytes(lib):
     # 5 chunks of k are too few to split
     assert wb(pf.PF_Q4_0, 17, 1280, 290, pf.PF_RESIDUAL, pf.PF_LEG_F16) == 320 * 1280 * 2
     assert wb(pf.PF_Q4_0, 4096, 4096, 512, pf.PF_PLAIN, pf.PF_LEG_F32) == 0
-    assert wb(pf.PF_Q4_0, 4096, 4096, 8, pf.PF_PLAIN, pf.PF_LEG_F16) == 0
+    # the GEMV (f16 leg: up to 2 rows, or up to 8 with the SwiGLU epilogue) takes none;
+    # from 3 rows the f16 leg's PLAIN and RESIDUAL run the GEMM
+    assert wb(pf.PF_Q4_0, 4096, 4096, 2, pf.PF_PLAIN, pf.PF_LEG_F16) == 0
+    assert wb(pf.PF_Q4_0, 4096, 4096, 8, pf.PF_GATE_UP_SWIGLU, pf.PF_LEG_F16) == 0
+    assert wb(pf.PF_Q4_0, 4096, 4096, 8, pf.PF_PLAIN, pf.PF_LEG_F16) == 32 * 4096 * 2
+    assert wb(pf.PF_Q8_0, 4096, 4096, 3, pf.PF_RESIDUAL, pf.PF_LEG_F16) == 32 * 4096 * 2
     assert wb(pf.PF_Q4_0, 4096, 4096, 0, pf.PF_PLAIN, pf.PF_LEG_F16) == 0
     assert wb(3, 64, 256, 16, 0, 1) == -pf.PF_E_QTYPE
     assert wb(0, 64, 300, 16, 0, 1) == -pf.PF_E_SHAPE
@@ -214,7 +224,10 @@ def test_rmsnorm_workspace_bytes(lib):
     assert wb(pf.PF_Q4_0, 4096, 4096, 300, pf.PF_PLAIN, pf.PF_LEG_F16) == \
         1280 + lib.pf_workspace_bytes(pf.PF_Q4_0, 4096, 4096, 300, pf.PF_PLAIN, pf.PF_LEG_F16)
     # ... or the normalised rows in f32 for the GEMV and the f32 leg
-    assert wb(pf.PF_Q8_0, 4096, 12288, 3, pf.PF_PLAIN, pf.PF_LEG_F16) == 256 + 3 * 12288 * 4
+    assert wb(pf.PF_Q8_0, 4096, 12288, 2, pf.PF_PLAIN, pf.PF_LEG_F16) == 256 + 2 * 12288 * 4
+    assert wb(pf.PF_Q8_0, 4096, 12288, 3, pf.PF_GATE_UP_SWIGLU, pf.PF_LEG_F16) == 256 + 3 * 12288 * 4
+    assert wb(pf.PF_Q8_0, 4096, 12288, 3, pf.PF_PLAIN, pf.PF_LEG_F16) == \
+        256 + lib.pf_workspace_bytes(pf.PF_Q8_0, 4096, 12288, 3, pf.PF_PLAIN, pf.PF_LEG_F16)
     assert wb(pf.PF_Q4_0, 200, 768, 40, pf.PF_RESIDUAL, pf.PF_LEG_F32) == 256 + 40 * 768 * 4
     assert wb(pf.PF_Q4_0, 200, 768, 0, pf.PF_RESIDUAL, pf.PF_LEG_F32) == 0
     assert wb(pf.PF_Q4_0, 200, 700, 4, pf.PF_PLAIN, pf.PF_LEG_F32) == -pf.PF_E_SHAPE
@@ -280,7 +293,6 @@ def test_prepared_argument_checks(lib):
                                        P(kw.get("ws", WS)), kw.get("wsb", xneed), None)
     assert px(qtype=7) == pf.PF_E_QTYPE
     assert px(k=300) == pf.PF_E_SHAPE
-    assert px(T=8) == pf.PF_E_PATH            # the GEMV reads f32 X
     assert px(T=0) == pf.PF_OK
     assert px(X=0) == pf.PF_E_NULL
     assert px(X=X + 4) == pf.PF_E_ALIGN
@@ -290,7 +302,9 @@ def test_prepared_argument_checks(lib):
     gp = lambda **kw: lib.pf_gemm_prepared(kw.get("qtype", 0), P(kw.get("W", W)), kw.get("n", n), k,
                                            kw.get("T", T), P(kw.get("Y", Y)), kw.get("ldy", n), kw.get("epi", 0),
                                            P(kw.get("ws", WS)), kw.get("wsb", need), None)
-    assert gp(T=5) == pf.PF_E_PATH
+    # where pf_gemm_ws runs the GEMV (which reads f32 X) there is no prepared GEMM
+    assert gp(T=2) == pf.PF_E_PATH
+    assert gp(T=8, epi=pf.PF_GATE_UP_SWIGLU) == pf.PF_E_PATH
     assert gp(ldy=n - 1) == pf.PF_E_SHAPE
     assert gp(epi=4) == pf.PF_E_EPILOGUE
     assert gp(W=0) == pf.PF_E_NULL

@@ -1,0 +1,45 @@
+"""GPU parity of the f16-leg GEMM on short chunks (9 <= T <= 32 token rows, one row
+tile): the model's projection shapes (Q4_0 4096 -> 12288 and 4096 -> 2 x 12288
+SwiGLU, Q8_0 12288 -> 4096 with the residual), with X rounded inside the GEMM
+(pf_gemm) and once into a workspace (pf_gemm_ws), each split along K where the
+epilogue allows, against the fp64 CPU oracle on sampled columns; and the edge rows
+of the tile (T = 31, 32, 33) at a small shape, fully checked.
+"""
+import pytest
+
+import oracle
+from quantized_weight_prefill_gguf_amd import synth
+from tests.test_gpu_parity import run_and_check
+from tests.test_gpu_workspace import run_ws_and_check
+
+pytestmark = pytest.mark.gpu
+
+Q4_0, Q8_0 = synth.Q4_0, synth.Q8_0
+PLAIN, RESIDUAL, SWIGLU = oracle.PLAIN, oracle.RESIDUAL, oracle.GATE_UP_SWIGLU
+F16 = 1
+
+SHAPES = [(Q4_0, 12288, 4096, PLAIN), (Q4_0, 12288, 4096, SWIGLU), (Q8_0, 4096, 12288, RESIDUAL)]
+
+
+@pytest.mark.parametrize("ws", [False, True])
+@pytest.mark.parametrize("T", [9, 16, 32])
+@pytest.mark.parametrize("qtype,n,k,epi", SHAPES)
+def test_short_chunk_model_shapes(gpu, qtype, n, k, epi, T, ws):
+    wid = 500 + T + 7 * epi
+    if ws:
+        run_ws_and_check(gpu, qtype, n, k, T, epi, F16, wid=wid, samples=96)
+    else:
+        run_and_check(gpu, qtype, n, k, T, epi, F16, wid=wid, samples=96)
+
+
+@pytest.mark.parametrize("ws", [False, True])
+@pytest.mark.parametrize("epi", [PLAIN, RESIDUAL, SWIGLU])
+@pytest.mark.parametrize("qtype", [Q4_0, Q8_0])
+@pytest.mark.parametrize("T", [31, 32, 33])
+def test_tile_edge_rows(gpu, qtype, epi, T, ws):
+    n, k = 391, 2304
+    wid = 540 + T + 3 * epi + qtype
+    if ws:
+        run_ws_and_check(gpu, qtype, n, k, T, epi, F16, wid=wid)
+    else:
+        run_and_check(gpu, qtype, n, k, T, epi, F16, wid=wid)
