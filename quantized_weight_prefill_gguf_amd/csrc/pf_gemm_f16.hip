@@ -63,9 +63,14 @@ template <int QT> __device__ __forceinline__ u2_t x_pack(f4_t v) {
 }  // namespace
 
 // Global weight row of local tile row lr, or -1 past the weight.
-// Workgroups of a 32-row tile resident per CU (waves per SIMD): as many as its LDS
-// (41 KB for Q4_0, 74 KB for Q8_0) and registers allow.
-constexpr int small_tile_waves(int qt) { return qt == Q4_0 ? 3 : 2; }
+// Workgroups of a one-row-of-waves tile (MT x 128, waves 1 x 4) resident per CU
+// (waves per SIMD), as its LDS (Q4_0: 41 KB at 32 rows, 45 KB at 64, 53 KB at 128;
+// Q8_0: 74 KB and up) and registers allow.
+// Up to this many token rows the GEMM below 256 rows takes one such row tile.
+constexpr int SHORT_T = 128;
+constexpr int short_tile_waves(int qt, int mt) {
+    return mt > 64 ? 1 : (qt == Q4_0 && mt <= 32) ? 3 : 2;
+}
 
 template <int EPI, int NW>
 __device__ __forceinline__ int f16_weight_row(int tile_n, int lr, int n) {
@@ -80,17 +85,17 @@ __device__ __forceinline__ int f16_weight_row(int tile_n, int lr, int n) {
     }
 }
 
-template <int QT, int EPI, int MT, int NW, bool SPLIT, bool XH>
+template <int QT, int EPI, int MT, int NW, bool SPLIT, bool XH, bool ROW1>
 __global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(1, MT <= 32 ? small_tile_waves(QT) : 1)))
+__attribute__((amdgpu_waves_per_eu(1, ROW1 ? short_tile_waves(QT, MT) : 1)))
 void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
                      float *__restrict__ Y, int n, int ldy, int k, int T, int tiles_m, int tiles_n,
                      int splits) {
     using CT = ChunkTraits<QT>;
     constexpr int BB = CT::BB;
-    // Waves: WVM x WVN over the tile. 32-row tiles (few token rows) put all four
-    // side by side along the weight rows, so that no two decode the same columns.
-    constexpr int WVM = MT >= 64 ? 2 : 1;
+    // Waves: WVM x WVN over the tile. ROW1 tiles (few token rows) put all four side
+    // by side along the weight rows, so that no two decode the same columns.
+    constexpr int WVM = ROW1 ? 1 : 2;
     constexpr int WVN = 4 / WVM;
     constexpr int IT = MT / (32 * WVM);   // 32-row MFMA tiles per wave
     constexpr int JT = NW / (32 * WVN);   // 32-column MFMA tiles per wave
@@ -1045,10 +1050,22 @@ __global__ void zero_fill_kernel(float *__restrict__ Y, int T, int n, int ldy) {
     if (i < T * n) Y[(size_t)(i / n) * ldy + i % n] = 0.f;
 }
 
+// Y [T][n] (rows ldy apart) = silu(G[t][o]) * G[t][n + o], G [T][2n] holding the
+// gate rows' products in columns 0..n-1 and the up rows' in n..2n-1.
+__global__ void swiglu_apply_kernel(const float *__restrict__ G, float *__restrict__ Y, int T, int n,
+                                    int ldy) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= T * n) return;
+    const int t = i / n, o = i - t * n;
+    const float *g = G + (size_t)t * 2 * n;
+    Y[(size_t)t * ldy + o] = silu_fast(g[o]) * g[n + o];
+}
+
 namespace {
 
 struct TileChoice {
-    int cfg;     // 0: 256x192, 1: 256x128, 2: 128x128, 3: 64x64, 4: 32x128
+    int cfg;     // 0: 256x192, 1: 256x128, 2: 128x128, 3: 64x64; waves 1 x 4: 4: 32x128,
+                 // 5: 64x128, 6: 128x128
     int splits;
 };
 
@@ -1062,15 +1079,18 @@ TileChoice choose_tiles(const GemmArgs &a) {
     const bool swiglu = a.epilogue == EPI_SWIGLU;
     const int nchunks = a.k / 256;
     const int cus = 256;
-    if (a.T <= 32) {
+    if (a.T <= SHORT_T) {
         // One row tile: the matrix-core work is small and the time is the weight
-        // stream and its decode. 32 x 128 tiles (no column decoded twice), split
-        // along K to fill the resident slots: the split count minimises rounds of
-        // workgroups x (chunks per workgroup + one chunk's worth of fixed cost).
-        // SwiGLU cannot split: its epilogue is not linear in the partial sums.
+        // stream and its decode. MT x 128 tiles with the waves side by side (no
+        // column decoded twice), split along K to fill the resident slots: the
+        // split count minimises rounds of workgroups x (chunks per workgroup + one
+        // chunk's worth of fixed cost). SwiGLU cannot split: its epilogue is not
+        // linear in the partial sums.
+        const int mt = a.T <= 32 ? 32 : a.T <= 64 ? 64 : 128;
+        const int cfg = mt == 32 ? 4 : mt == 64 ? 5 : 6;
         const int tn = (a.n + 127) / 128;
-        if (swiglu) return TileChoice{4, 1};
-        const long slots = (long)cus * small_tile_waves(a.qtype);
+        if (swiglu) return TileChoice{cfg, 1};
+        const long slots = (long)cus * short_tile_waves(a.qtype, mt);
         int best_s = 1;
         long best_c = -1;
         for (int s = 1; s <= nchunks && s <= 32; ++s) {
@@ -1081,7 +1101,7 @@ TileChoice choose_tiles(const GemmArgs &a) {
                 best_s = s;
             }
         }
-        return TileChoice{4, best_s};
+        return TileChoice{cfg, best_s};
     }
     TileChoice best{3, 1};
     float best_t = 1e30f;
@@ -1107,17 +1127,17 @@ TileChoice choose_tiles(const GemmArgs &a) {
     return best;
 }
 
-template <int QT, int EPI, int MT, int NW, bool SPLIT>
+template <int QT, int EPI, int MT, int NW, bool SPLIT, bool ROW1 = false>
 hipError_t launch_cfg(const GemmArgs &a, int splits, const uint16_t *xh, hipStream_t s) {
     constexpr int OUT = (EPI == EPI_SWIGLU) ? NW / 2 : NW;
     const int tm = (a.T + MT - 1) / MT;
     const int tn = (a.n + OUT - 1) / OUT;
     const int total = tm * tn * splits;
     if (xh)
-        hipLaunchKernelGGL((gemm_f16_kernel<QT, EPI, MT, NW, SPLIT, true>), dim3(total), dim3(256), 0,
+        hipLaunchKernelGGL((gemm_f16_kernel<QT, EPI, MT, NW, SPLIT, true, ROW1>), dim3(total), dim3(256), 0,
                            s, a.W, (const void *)xh, a.Y, a.n, a.ldy, a.k, a.T, tm, tn, splits);
     else
-        hipLaunchKernelGGL((gemm_f16_kernel<QT, EPI, MT, NW, SPLIT, false>), dim3(total), dim3(256), 0,
+        hipLaunchKernelGGL((gemm_f16_kernel<QT, EPI, MT, NW, SPLIT, false, ROW1>), dim3(total), dim3(256), 0,
                            s, a.W, (const void *)a.X, a.Y, a.n, a.ldy, a.k, a.T, tm, tn, splits);
     return hipGetLastError();
 }
@@ -1129,7 +1149,9 @@ hipError_t launch_split(const GemmArgs &a, TileChoice tc, const uint16_t *xh, hi
     case 1: return launch_cfg<QT, EPI, 256, 128, SPLIT>(a, tc.splits, xh, s);
     case 2: return launch_cfg<QT, EPI, 128, 128, SPLIT>(a, tc.splits, xh, s);
     case 3: return launch_cfg<QT, EPI, 64, 64, SPLIT>(a, tc.splits, xh, s);
-    default: return launch_cfg<QT, EPI, 32, 128, SPLIT>(a, tc.splits, xh, s);
+    case 4: return launch_cfg<QT, EPI, 32, 128, SPLIT, true>(a, tc.splits, xh, s);
+    case 5: return launch_cfg<QT, EPI, 64, 128, SPLIT, true>(a, tc.splits, xh, s);
+    default: return launch_cfg<QT, EPI, 128, 128, SPLIT, true>(a, tc.splits, xh, s);
     }
 }
 
@@ -1256,8 +1278,19 @@ static int coop_splits(int T, int n, int k, int epilogue) {
 static int64_t ws_x_bytes(int T, int k) { return ((int64_t)(T + 31) / 32 * 32 * k * 2 + 255) / 256 * 256; }
 static int64_t ws_pstride(int T, int n) { return ((int64_t)T * n + 3) / 4 * 4; }
 
+// Short chunks with the SwiGLU epilogue, on the workspace path: the gate and up rows
+// run as one PLAIN GEMM over all 2n weight rows, split along K like the other short
+// chunks, into G [T][2n] f32 behind the fp16 X; swiglu_apply_kernel then writes
+// Y = silu(gate) * up. Measured faster than the unsplit fused epilogue up to 64 rows
+// (gate/up 2 x 12288 x 4096: 28-43 us against 43-46), slower at 100-128 (the atomics
+// and G's round trip grow with T). Without a workspace there is no room for G, and
+// the fused epilogue runs unsplit.
+constexpr int SWIGLU_SCRATCH_T = 64;
+static bool swiglu_via_scratch(int T, int epilogue) { return epilogue == EPI_SWIGLU && T <= SWIGLU_SCRATCH_T; }
+
 int64_t f16_ws_bytes(int T, int n, int k, int epilogue) {
     const int64_t xb = (int64_t)(T + 31) / 32 * 32 * k * 2;
+    if (swiglu_via_scratch(T, epilogue)) return ws_x_bytes(T, k) + (int64_t)T * 2 * n * 4;
     if (T < 256) return xb;
     const int splits = coop_splits(T, n, k, epilogue);
     return splits > 1 ? ws_x_bytes(T, k) + (int64_t)splits * ws_pstride(T, n) * 4 : xb;
@@ -1357,10 +1390,24 @@ hipError_t launch_prepare_x_f16(const GemmArgs &a, void *workspace, hipStream_t 
 }
 
 // The f16 GEMM on X already in the workspace (launch_prepare_x_f16 with the same
-// qtype, k and T); any split-K partial sums go behind it.
+// qtype, k and T); any split-K partial sums (or the SwiGLU scratch G) go behind it.
 hipError_t launch_gemm_f16_prepared(const GemmArgs &a, void *workspace, hipStream_t s) {
     uint16_t *xh = static_cast<uint16_t *>(workspace);
     if (a.T >= 256) return a.qtype == Q4_0 ? launch_coop_q<Q4_0>(a, xh, s) : launch_coop_q<Q8_0>(a, xh, s);
+    if (swiglu_via_scratch(a.T, a.epilogue)) {
+        float *G = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(workspace) + ws_x_bytes(a.T, a.k));
+        GemmArgs g = a;
+        g.epilogue = EPI_PLAIN;
+        g.n = 2 * a.n;
+        g.Y = G;
+        g.ldy = 2 * a.n;
+        const hipError_t e = a.qtype == Q4_0 ? launch_q<Q4_0>(g, xh, s) : launch_q<Q8_0>(g, xh, s);
+        if (e != hipSuccess) return e;
+        const int count = a.T * a.n;
+        hipLaunchKernelGGL(swiglu_apply_kernel, dim3((count + 255) / 256), dim3(256), 0, s, G, a.Y, a.T, a.n,
+                           a.ldy);
+        return hipGetLastError();
+    }
     return a.qtype == Q4_0 ? launch_q<Q4_0>(a, xh, s) : launch_q<Q8_0>(a, xh, s);
 }
 

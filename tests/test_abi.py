@@ -127,6 +127,12 @@ def test_workspace_bytes(lib):
     # multiple of 32; the GEMV and the f32 leg none
     assert wb(pf.PF_Q4_0, 12288, 4096, 512, pf.PF_GATE_UP_SWIGLU, pf.PF_LEG_F16) == 512 * 4096 * 2
     assert wb(pf.PF_Q8_0, 4096, 12288, 9, pf.PF_RESIDUAL, pf.PF_LEG_F16) == 32 * 12288 * 2
+    # SwiGLU on up to 64 rows adds G [T][2n] f32 (the gate and up products, split along K)
+    assert wb(pf.PF_Q4_0, 12288, 4096, 16, pf.PF_GATE_UP_SWIGLU, pf.PF_LEG_F16) == \
+        32 * 4096 * 2 + 16 * 24576 * 4
+    assert wb(pf.PF_Q4_0, 12288, 4096, 64, pf.PF_GATE_UP_SWIGLU, pf.PF_LEG_F16) == \
+        64 * 4096 * 2 + 64 * 24576 * 4
+    assert wb(pf.PF_Q4_0, 12288, 4096, 65, pf.PF_GATE_UP_SWIGLU, pf.PF_LEG_F16) == 96 * 4096 * 2
     # a K split adds S blocks of [T][n] f32 partial sums behind X (256-byte boundary):
     # 4096^2 at T = 300 is 2 x 22 tiles of 256 x 192, split 3 ways (16 chunks of 256
     # k, at least 5 per split); at T = 512, 43 tiles of 512 x 96, again 3 ways; the

@@ -1,9 +1,10 @@
-"""GPU parity of the f16-leg GEMM on short chunks (9 <= T <= 32 token rows, one row
-tile): the model's projection shapes (Q4_0 4096 -> 12288 and 4096 -> 2 x 12288
-SwiGLU, Q8_0 12288 -> 4096 with the residual), with X rounded inside the GEMM
-(pf_gemm) and once into a workspace (pf_gemm_ws), each split along K where the
-epilogue allows, against the fp64 CPU oracle on sampled columns; and the edge rows
-of the tile (T = 31, 32, 33) at a small shape, fully checked.
+"""GPU parity of the f16-leg GEMM on short chunks (up to 128 token rows: one row tile
+of 32, 64 or 128 rows with the four waves side by side): the model's projection
+shapes (Q4_0 4096 -> 12288 and 4096 -> 2 x 12288 SwiGLU, Q8_0 12288 -> 4096 with the
+residual), with X rounded inside the GEMM (pf_gemm) and once into a workspace
+(pf_gemm_ws; SwiGLU there splits along K through its gate/up scratch), each split
+along K where the epilogue allows, against the fp64 CPU oracle on sampled columns;
+and the rows at each tile size's edge at a small shape, fully checked.
 """
 import pytest
 
@@ -22,7 +23,7 @@ SHAPES = [(Q4_0, 12288, 4096, PLAIN), (Q4_0, 12288, 4096, SWIGLU), (Q8_0, 4096, 
 
 
 @pytest.mark.parametrize("ws", [False, True])
-@pytest.mark.parametrize("T", [9, 16, 32])
+@pytest.mark.parametrize("T", [9, 16, 32, 48, 100, 128])
 @pytest.mark.parametrize("qtype,n,k,epi", SHAPES)
 def test_short_chunk_model_shapes(gpu, qtype, n, k, epi, T, ws):
     wid = 500 + T + 7 * epi
@@ -35,7 +36,7 @@ def test_short_chunk_model_shapes(gpu, qtype, n, k, epi, T, ws):
 @pytest.mark.parametrize("ws", [False, True])
 @pytest.mark.parametrize("epi", [PLAIN, RESIDUAL, SWIGLU])
 @pytest.mark.parametrize("qtype", [Q4_0, Q8_0])
-@pytest.mark.parametrize("T", [31, 32, 33])
+@pytest.mark.parametrize("T", [31, 32, 33, 64, 65, 127, 128, 129])
 def test_tile_edge_rows(gpu, qtype, epi, T, ws):
     n, k = 391, 2304
     wid = 540 + T + 3 * epi + qtype
