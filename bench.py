@@ -81,6 +81,8 @@ def workloads():
     return {
         "ffn_T512_f16": ffn(512),
         "ffn_T2048_f16": ffn(2048),
+        # a short chunk (32 rows): the same two projections, bound by the weight stream
+        "ffn_T32_f16": ffn(32),
         # the FFN sublayer as the pages run it: RMSNorm, gate/up SwiGLU, down + residual,
         # with the norm inside the gate/up call (pf_gemm_rmsnorm)
         "ffn_rmsnorm_T512_f16": (512, 1, [
@@ -233,16 +235,23 @@ def _short_kernel(name):
 def _op_of_kernel(short, ops):
     """Which op of a workload launched the library kernel `short` (None if not ours).
     Block-type templated kernels name the qtype first; split_sum_kernel names the
-    epilogue; zero_fill_kernel belongs to the PLAIN op."""
+    epilogue; zero_fill_kernel belongs to the PLAIN op, else to the SwiGLU op (whose
+    split on short chunks clears its gate/up scratch), as swiglu_apply_kernel does."""
     import re
     m = re.match(r"(\w+)<(\d+)", short)
     base = m.group(1) if m else short
+    if base == "zero_fill_kernel":
+        for want in (PLAIN, SWIGLU):
+            for op in ops:
+                if op[4] == want:
+                    return op
+        return None
     for op in ops:
         if base == "split_sum_kernel":
             if int(m.group(2)) == op[4]:
                 return op
-        elif base == "zero_fill_kernel":
-            if op[4] == PLAIN:
+        elif base == "swiglu_apply_kernel":
+            if op[4] == SWIGLU:
                 return op
         elif base in ("rms_inv_kernel", "rms_apply_kernel"):
             if op[0].startswith("rmsnorm_"):
@@ -516,18 +525,20 @@ def main():
                    for j in range(len(ops))]
     dom = int(np.argmax(kern_ms))
     dop = ops[dom]
-    is_gemv = T <= 8
     family = kernel_family(T, leg)
-    if is_gemv:
-        wb = op_rows(dop) * (dop[3] // 32) * BLOCK[dop[1]]
-        achieved = wb / (kern_ms[dom] * 1e-3) / 1e9
+    # the bound is whichever takes longer at peak: streaming the weights once from HBM,
+    # or the op's matrix-core flops (the GEMV, and the GEMM on short chunks, are HBM-bound)
+    wbytes = op_rows(dop) * (dop[3] // 32) * BLOCK[dop[1]]
+    mfma_peak = PEAK["fp16_mfma_tflops"] if leg == 1 else PEAK["fp32_mfma_tflops"]
+    hbm_bound = wbytes / (PEAK["hbm_gbs"] * 1e9) > op_flops(dop, T) / (mfma_peak * 1e12)
+    if hbm_bound:
+        achieved = wbytes / (kern_ms[dom] * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK["hbm_gbs"], "unit": "GB/s",
                     "frac": achieved / PEAK["hbm_gbs"], "traffic": load_traffic(args.workload, dop[0], family)}
     else:
         achieved = op_flops(dop, T) / (kern_ms[dom] * 1e-3) / 1e12
-        peak = PEAK["fp16_mfma_tflops"] if leg == 1 else PEAK["fp32_mfma_tflops"]
-        roofline = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                    "frac": achieved / peak, "traffic": load_traffic(args.workload, dop[0], family)}
+        roofline = {"bound": "mfma", "achieved": achieved, "peak": mfma_peak, "unit": "TFLOP/s",
+                    "frac": achieved / mfma_peak, "traffic": load_traffic(args.workload, dop[0], family)}
     roofline["kernel"] = dop[0] + (" (GEMM call)" if nparts[dom] > 1 else "")
     roofline["avg_launch_us"] = kern_ms[dom] * 1e3
     roofline["op_us"] = op_ms[dom] * 1e3
