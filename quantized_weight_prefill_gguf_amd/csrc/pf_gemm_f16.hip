@@ -90,7 +90,7 @@ __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(1, ROW1 ? short_tile_waves(QT, MT) : 1)))
 void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
                      float *__restrict__ Y, int n, int ldy, int k, int T, int tiles_m, int tiles_n,
-                     int splits) {
+                     int splits, long pstride) {
     using CT = ChunkTraits<QT>;
     constexpr int BB = CT::BB;
     // Waves: WVM x WVN over the tile. ROW1 tiles (few token rows) put all four side
@@ -510,10 +510,15 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
                     const int t = trow + 8 * (r >> 2) + (r & 3);
                     if (t < T && o < n) {
                         float *y = Y + (size_t)t * ldy + o;
-                        // RESIDUAL adds into Y with an atomic even without a K split:
-                        // one writer per element, so the result is the single rounding
-                        // of R + acc either way, and the add needs no VGPR copy of acc.
-                        if constexpr (SPLIT || EPI == EPI_RESIDUAL)
+                        // A K split with pstride > 0 stores its partial sums in block
+                        // `split` of Y (the workspace; a sum kernel adds them in a fixed
+                        // order), else adds into Y with atomics. RESIDUAL adds into Y
+                        // with an atomic even without a K split: one writer per
+                        // element, so the result is the single rounding of R + acc
+                        // either way, and the add needs no VGPR copy of acc.
+                        if (SPLIT && pstride > 0)
+                            y[(size_t)split * pstride] = acc[i][j][r];
+                        else if constexpr (SPLIT || EPI == EPI_RESIDUAL)
                             atomicAdd(y, acc[i][j][r]);
                         else
                             *y = acc[i][j][r];
@@ -1050,15 +1055,21 @@ __global__ void zero_fill_kernel(float *__restrict__ Y, int T, int n, int ldy) {
     if (i < T * n) Y[(size_t)(i / n) * ldy + i % n] = 0.f;
 }
 
-// Y [T][n] (rows ldy apart) = silu(G[t][o]) * G[t][n + o], G [T][2n] holding the
-// gate rows' products in columns 0..n-1 and the up rows' in n..2n-1.
+// Y [T][n] (rows ldy apart) = silu(g) * u with g = sum_s G_s[t][o], u = sum_s G_s[t][n + o]
+// over the `splits` blocks G_s [T][2n] (pstride floats apart) in order: the gate rows'
+// products in columns 0..n-1, the up rows' in n..2n-1.
 __global__ void swiglu_apply_kernel(const float *__restrict__ G, float *__restrict__ Y, int T, int n,
-                                    int ldy) {
+                                    int ldy, int splits, long pstride) {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= T * n) return;
     const int t = i / n, o = i - t * n;
     const float *g = G + (size_t)t * 2 * n;
-    Y[(size_t)t * ldy + o] = silu_fast(g[o]) * g[n + o];
+    float gs = g[o], us = g[n + o];
+    for (int sp = 1; sp < splits; ++sp) {
+        gs += g[(size_t)sp * pstride + o];
+        us += g[(size_t)sp * pstride + n + o];
+    }
+    Y[(size_t)t * ldy + o] = silu_fast(gs) * us;
 }
 
 namespace {
@@ -1128,40 +1139,62 @@ TileChoice choose_tiles(const GemmArgs &a) {
 }
 
 template <int QT, int EPI, int MT, int NW, bool SPLIT, bool ROW1 = false>
-hipError_t launch_cfg(const GemmArgs &a, int splits, const uint16_t *xh, hipStream_t s) {
+hipError_t launch_cfg(const GemmArgs &a, int splits, const uint16_t *xh, long pstride, hipStream_t s) {
     constexpr int OUT = (EPI == EPI_SWIGLU) ? NW / 2 : NW;
     const int tm = (a.T + MT - 1) / MT;
     const int tn = (a.n + OUT - 1) / OUT;
     const int total = tm * tn * splits;
     if (xh)
         hipLaunchKernelGGL((gemm_f16_kernel<QT, EPI, MT, NW, SPLIT, true, ROW1>), dim3(total), dim3(256), 0,
-                           s, a.W, (const void *)xh, a.Y, a.n, a.ldy, a.k, a.T, tm, tn, splits);
+                           s, a.W, (const void *)xh, a.Y, a.n, a.ldy, a.k, a.T, tm, tn, splits, pstride);
     else
         hipLaunchKernelGGL((gemm_f16_kernel<QT, EPI, MT, NW, SPLIT, false, ROW1>), dim3(total), dim3(256), 0,
-                           s, a.W, (const void *)a.X, a.Y, a.n, a.ldy, a.k, a.T, tm, tn, splits);
+                           s, a.W, (const void *)a.X, a.Y, a.n, a.ldy, a.k, a.T, tm, tn, splits, pstride);
     return hipGetLastError();
 }
 
 template <int QT, int EPI, bool SPLIT>
-hipError_t launch_split(const GemmArgs &a, TileChoice tc, const uint16_t *xh, hipStream_t s) {
+hipError_t launch_split(const GemmArgs &a, TileChoice tc, const uint16_t *xh, hipStream_t s,
+                        long pstride = 0) {
     switch (tc.cfg) {
-    case 0: return launch_cfg<QT, EPI, 256, 192, SPLIT>(a, tc.splits, xh, s);
-    case 1: return launch_cfg<QT, EPI, 256, 128, SPLIT>(a, tc.splits, xh, s);
-    case 2: return launch_cfg<QT, EPI, 128, 128, SPLIT>(a, tc.splits, xh, s);
-    case 3: return launch_cfg<QT, EPI, 64, 64, SPLIT>(a, tc.splits, xh, s);
-    case 4: return launch_cfg<QT, EPI, 32, 128, SPLIT, true>(a, tc.splits, xh, s);
-    case 5: return launch_cfg<QT, EPI, 64, 128, SPLIT, true>(a, tc.splits, xh, s);
-    default: return launch_cfg<QT, EPI, 128, 128, SPLIT, true>(a, tc.splits, xh, s);
+    case 0: return launch_cfg<QT, EPI, 256, 192, SPLIT>(a, tc.splits, xh, pstride, s);
+    case 1: return launch_cfg<QT, EPI, 256, 128, SPLIT>(a, tc.splits, xh, pstride, s);
+    case 2: return launch_cfg<QT, EPI, 128, 128, SPLIT>(a, tc.splits, xh, pstride, s);
+    case 3: return launch_cfg<QT, EPI, 64, 64, SPLIT>(a, tc.splits, xh, pstride, s);
+    case 4: return launch_cfg<QT, EPI, 32, 128, SPLIT, true>(a, tc.splits, xh, pstride, s);
+    case 5: return launch_cfg<QT, EPI, 64, 128, SPLIT, true>(a, tc.splits, xh, pstride, s);
+    default: return launch_cfg<QT, EPI, 128, 128, SPLIT, true>(a, tc.splits, xh, pstride, s);
     }
 }
 
+// Partial sums of a K split: block `split` (pstride floats apart) of ps [T][n], each
+// stored whole by one workgroup.
+long part_stride(int T, int n) { return ((long)T * n + 3) / 4 * 4; }
+
 template <int QT, int EPI>
-hipError_t launch_epi(const GemmArgs &a, const uint16_t *xh, hipStream_t s) {
+hipError_t launch_epi(const GemmArgs &a, const uint16_t *xh, hipStream_t s, float *ps = nullptr) {
     const TileChoice tc = choose_tiles(a);
     if constexpr (EPI == EPI_SWIGLU) {
         return launch_split<QT, EPI, false>(a, TileChoice{tc.cfg, 1}, xh, s);
     } else {
         if (tc.splits == 1) return launch_split<QT, EPI, false>(a, tc, xh, s);
+        if (ps) {
+            // workspace: partial sums, then the fixed-order sum (deterministic)
+            GemmArgs p = a;
+            p.Y = ps;
+            p.ldy = a.n;
+            const long pstride = part_stride(a.T, a.n);
+            hipError_t e = launch_split<QT, EPI, true>(p, tc, xh, s, pstride);
+            if (e != hipSuccess) return e;
+            const long count = (long)a.T * a.n;
+            if (a.ldy == a.n)
+                hipLaunchKernelGGL((split_sum_kernel<EPI, true>), dim3((unsigned)((count / 4 + 1 + 255) / 256)),
+                                   dim3(256), 0, s, ps, a.Y, count, pstride, tc.splits, a.n, a.ldy);
+            else
+                hipLaunchKernelGGL((split_sum_kernel<EPI, false>), dim3((unsigned)((count + 255) / 256)),
+                                   dim3(256), 0, s, ps, a.Y, count, pstride, tc.splits, a.n, a.ldy);
+            return hipGetLastError();
+        }
         if constexpr (EPI == EPI_PLAIN) {
             const int count = a.T * a.n;
             hipLaunchKernelGGL(zero_fill_kernel, dim3((count + 255) / 256), dim3(256), 0, s, a.Y, a.T, a.n,
@@ -1174,12 +1207,54 @@ hipError_t launch_epi(const GemmArgs &a, const uint16_t *xh, hipStream_t s) {
 }
 
 template <int QT>
-hipError_t launch_q(const GemmArgs &a, const uint16_t *xh, hipStream_t s) {
+hipError_t launch_q(const GemmArgs &a, const uint16_t *xh, hipStream_t s, float *ps = nullptr) {
     switch (a.epilogue) {
-    case EPI_PLAIN: return launch_epi<QT, EPI_PLAIN>(a, xh, s);
-    case EPI_RESIDUAL: return launch_epi<QT, EPI_RESIDUAL>(a, xh, s);
+    case EPI_PLAIN: return launch_epi<QT, EPI_PLAIN>(a, xh, s, ps);
+    case EPI_RESIDUAL: return launch_epi<QT, EPI_RESIDUAL>(a, xh, s, ps);
     default: return launch_epi<QT, EPI_SWIGLU>(a, xh, s);
     }
+}
+
+// SwiGLU on a short chunk through the workspace: the gate and up rows as one PLAIN
+// GEMM over 2n weight rows into G (partial sums of its K split, or the products
+// themselves unsplit), then swiglu_apply_kernel.
+template <int QT>
+hipError_t launch_swiglu_scratch(const GemmArgs &a, const uint16_t *xh, float *G, hipStream_t s) {
+    GemmArgs g = a;
+    g.epilogue = EPI_PLAIN;
+    g.n = 2 * a.n;
+    g.Y = G;
+    g.ldy = 2 * a.n;
+    const TileChoice tc = choose_tiles(g);
+    const long pstride = part_stride(a.T, 2 * a.n);
+    const hipError_t e = tc.splits == 1 ? launch_split<QT, EPI_PLAIN, false>(g, tc, xh, s)
+                                        : launch_split<QT, EPI_PLAIN, true>(g, tc, xh, s, pstride);
+    if (e != hipSuccess) return e;
+    const int count = a.T * a.n;
+    hipLaunchKernelGGL(swiglu_apply_kernel, dim3((count + 255) / 256), dim3(256), 0, s, G, a.Y, a.T, a.n, a.ldy,
+                       tc.splits, pstride);
+    return hipGetLastError();
+}
+
+// Most K splits the GEMM below 256 rows takes for these sizes, over both block types
+// (the workspace size does not depend on the block type).
+int small_t_splits(int T, int n, int k, int epilogue) {
+    int m = 1;
+    for (int q : {Q4_0, Q8_0}) {
+        GemmArgs g;
+        g.qtype = q;
+        g.epilogue = epilogue;
+        g.W = nullptr;
+        g.X = nullptr;
+        g.Y = nullptr;
+        g.n = n;
+        g.ldy = n;
+        g.k = k;
+        g.T = T;
+        const int sp = choose_tiles(g).splits;
+        m = sp > m ? sp : m;
+    }
+    return m;
 }
 
 // RMSNorm prologue inside the conversion: x * inv (the row's) * w (the columns')
@@ -1276,7 +1351,7 @@ static int coop_splits(int T, int n, int k, int epilogue) {
 
 // Byte offset of the partial sums in the workspace, and the floats between splits.
 static int64_t ws_x_bytes(int T, int k) { return ((int64_t)(T + 31) / 32 * 32 * k * 2 + 255) / 256 * 256; }
-static int64_t ws_pstride(int T, int n) { return ((int64_t)T * n + 3) / 4 * 4; }
+static int64_t ws_pstride(int T, int n) { return part_stride(T, n); }
 
 // Short chunks with the SwiGLU epilogue, on the workspace path: the gate and up rows
 // run as one PLAIN GEMM over all 2n weight rows, split along K like the other short
@@ -1290,8 +1365,12 @@ static bool swiglu_via_scratch(int T, int epilogue) { return epilogue == EPI_SWI
 
 int64_t f16_ws_bytes(int T, int n, int k, int epilogue) {
     const int64_t xb = (int64_t)(T + 31) / 32 * 32 * k * 2;
-    if (swiglu_via_scratch(T, epilogue)) return ws_x_bytes(T, k) + (int64_t)T * 2 * n * 4;
-    if (T < 256) return xb;
+    if (swiglu_via_scratch(T, epilogue))
+        return ws_x_bytes(T, k) + (int64_t)small_t_splits(T, 2 * n, k, EPI_PLAIN) * ws_pstride(T, 2 * n) * 4;
+    if (T < 256) {
+        const int splits = small_t_splits(T, n, k, epilogue);
+        return splits > 1 ? ws_x_bytes(T, k) + (int64_t)splits * ws_pstride(T, n) * 4 : xb;
+    }
     const int splits = coop_splits(T, n, k, epilogue);
     return splits > 1 ? ws_x_bytes(T, k) + (int64_t)splits * ws_pstride(T, n) * 4 : xb;
 }
@@ -1394,21 +1473,11 @@ hipError_t launch_prepare_x_f16(const GemmArgs &a, void *workspace, hipStream_t 
 hipError_t launch_gemm_f16_prepared(const GemmArgs &a, void *workspace, hipStream_t s) {
     uint16_t *xh = static_cast<uint16_t *>(workspace);
     if (a.T >= 256) return a.qtype == Q4_0 ? launch_coop_q<Q4_0>(a, xh, s) : launch_coop_q<Q8_0>(a, xh, s);
-    if (swiglu_via_scratch(a.T, a.epilogue)) {
-        float *G = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(workspace) + ws_x_bytes(a.T, a.k));
-        GemmArgs g = a;
-        g.epilogue = EPI_PLAIN;
-        g.n = 2 * a.n;
-        g.Y = G;
-        g.ldy = 2 * a.n;
-        const hipError_t e = a.qtype == Q4_0 ? launch_q<Q4_0>(g, xh, s) : launch_q<Q8_0>(g, xh, s);
-        if (e != hipSuccess) return e;
-        const int count = a.T * a.n;
-        hipLaunchKernelGGL(swiglu_apply_kernel, dim3((count + 255) / 256), dim3(256), 0, s, G, a.Y, a.T, a.n,
-                           a.ldy);
-        return hipGetLastError();
-    }
-    return a.qtype == Q4_0 ? launch_q<Q4_0>(a, xh, s) : launch_q<Q8_0>(a, xh, s);
+    // split-K partial sums (or the SwiGLU scratch G) go behind the fp16 X
+    float *ps = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(workspace) + ws_x_bytes(a.T, a.k));
+    if (swiglu_via_scratch(a.T, a.epilogue))
+        return a.qtype == Q4_0 ? launch_swiglu_scratch<Q4_0>(a, xh, ps, s) : launch_swiglu_scratch<Q8_0>(a, xh, ps, s);
+    return a.qtype == Q4_0 ? launch_q<Q4_0>(a, xh, s, ps) : launch_q<Q8_0>(a, xh, s, ps);
 }
 
 hipError_t launch_gemm_f16_ws(const GemmArgs &a, void *workspace, hipStream_t s) {

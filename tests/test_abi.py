@@ -121,17 +121,30 @@ def test_gemm_argument_checks(lib):
     assert lib.pf_gemm(0, P(W), 64, 256, P(X), 0, P(Y), 0, 0, None) == pf.PF_OK
 
 
+def _split_blocks(total, x_bytes, T, n):
+    """Number of [T][n] f32 partial-sum blocks (each rounded up to 4 floats) that
+    follow x_bytes of fp16 X in a workspace of `total` bytes, or None if it does not
+    divide."""
+    per = (T * n + 3) // 4 * 4 * 4
+    extra = total - x_bytes
+    return extra // per if extra > 0 and extra % per == 0 else None
+
+
 def test_workspace_bytes(lib):
     wb = lib.pf_workspace_bytes
     # the f16 leg's matrix-core GEMM takes k halves per token row, T rounded up to a
     # multiple of 32; the GEMV and the f32 leg none
     assert wb(pf.PF_Q4_0, 12288, 4096, 512, pf.PF_GATE_UP_SWIGLU, pf.PF_LEG_F16) == 512 * 4096 * 2
-    assert wb(pf.PF_Q8_0, 4096, 12288, 9, pf.PF_RESIDUAL, pf.PF_LEG_F16) == 32 * 12288 * 2
-    # SwiGLU on up to 64 rows adds G [T][2n] f32 (the gate and up products, split along K)
-    assert wb(pf.PF_Q4_0, 12288, 4096, 16, pf.PF_GATE_UP_SWIGLU, pf.PF_LEG_F16) == \
-        32 * 4096 * 2 + 16 * 24576 * 4
-    assert wb(pf.PF_Q4_0, 12288, 4096, 64, pf.PF_GATE_UP_SWIGLU, pf.PF_LEG_F16) == \
-        64 * 4096 * 2 + 64 * 24576 * 4
+    # below 256 rows a K split of the narrow down projection stores 2..32 blocks of
+    # [T][n] partial sums behind X (X rounded up to 256 bytes)
+    assert 2 <= _split_blocks(wb(pf.PF_Q8_0, 4096, 12288, 9, pf.PF_RESIDUAL, pf.PF_LEG_F16),
+                              32 * 12288 * 2, 9, 4096) <= 32
+    # SwiGLU on up to 64 rows adds G_s [T][2n] f32 (the gate and up products, one block
+    # per K split); from 65 rows it does not split
+    assert 1 <= _split_blocks(wb(pf.PF_Q4_0, 12288, 4096, 16, pf.PF_GATE_UP_SWIGLU, pf.PF_LEG_F16),
+                              32 * 4096 * 2, 16, 24576) <= 32
+    assert 1 <= _split_blocks(wb(pf.PF_Q4_0, 12288, 4096, 64, pf.PF_GATE_UP_SWIGLU, pf.PF_LEG_F16),
+                              64 * 4096 * 2, 64, 24576) <= 32
     assert wb(pf.PF_Q4_0, 12288, 4096, 65, pf.PF_GATE_UP_SWIGLU, pf.PF_LEG_F16) == 96 * 4096 * 2
     # a K split adds S blocks of [T][n] f32 partial sums behind X (256-byte boundary):
     # 4096^2 at T = 300 is 2 x 22 tiles of 256 x 192, split 3 ways (16 chunks of 256
@@ -156,8 +169,12 @@ def test_workspace_bytes(lib):
     # from 3 rows the f16 leg's PLAIN and RESIDUAL run the GEMM
     assert wb(pf.PF_Q4_0, 4096, 4096, 2, pf.PF_PLAIN, pf.PF_LEG_F16) == 0
     assert wb(pf.PF_Q4_0, 4096, 4096, 8, pf.PF_GATE_UP_SWIGLU, pf.PF_LEG_F16) == 0
-    assert wb(pf.PF_Q4_0, 4096, 4096, 8, pf.PF_PLAIN, pf.PF_LEG_F16) == 32 * 4096 * 2
-    assert wb(pf.PF_Q8_0, 4096, 4096, 3, pf.PF_RESIDUAL, pf.PF_LEG_F16) == 32 * 4096 * 2
+    assert 2 <= _split_blocks(wb(pf.PF_Q4_0, 4096, 4096, 8, pf.PF_PLAIN, pf.PF_LEG_F16),
+                              32 * 4096 * 2, 8, 4096) <= 32
+    assert 2 <= _split_blocks(wb(pf.PF_Q8_0, 4096, 4096, 3, pf.PF_RESIDUAL, pf.PF_LEG_F16),
+                              32 * 4096 * 2, 3, 4096) <= 32
+    # a single K chunk cannot split: X alone
+    assert wb(pf.PF_Q4_0, 64, 256, 40, pf.PF_PLAIN, pf.PF_LEG_F16) == 64 * 256 * 2
     assert wb(pf.PF_Q4_0, 4096, 4096, 0, pf.PF_PLAIN, pf.PF_LEG_F16) == 0
     assert wb(3, 64, 256, 16, 0, 1) == -pf.PF_E_QTYPE
     assert wb(0, 64, 300, 16, 0, 1) == -pf.PF_E_SHAPE

@@ -44,3 +44,22 @@ def test_tile_edge_rows(gpu, qtype, epi, T, ws):
         run_ws_and_check(gpu, qtype, n, k, T, epi, F16, wid=wid)
     else:
         run_and_check(gpu, qtype, n, k, T, epi, F16, wid=wid)
+
+
+@pytest.mark.parametrize("qtype,n,k,epi,T", [(Q4_0, 12288, 4096, SWIGLU, 16), (Q8_0, 4096, 12288, RESIDUAL, 9),
+                                             (Q4_0, 12288, 4096, PLAIN, 100)])
+def test_workspace_path_deterministic(gpu, qtype, n, k, epi, T):
+    """pf_gemm_ws splits K into partial sums in the workspace and adds them in a fixed
+    order: two calls give the same bits."""
+    import numpy as np
+    from tests import parity
+    from tests.test_gpu_parity import acts, weight
+    wid = 580 + T + epi
+    W = weight(qtype, n, k, epi == SWIGLU, wid)
+    X = acts(T, k, wid)
+    R = acts(T, n, wid, synth.TENSOR_R) if epi == RESIDUAL else None
+    print("case ws-determinism qtype=%d n=%d k=%d T=%d epi=%d" % (qtype, n, k, T, epi), flush=True)
+    Wd = parity.to_dev(W)
+    Y1 = parity.run_gpu(gpu, qtype, None, n, k, X, epi, F16, R=R, Wd=Wd, workspace=True)
+    Y2 = parity.run_gpu(gpu, qtype, None, n, k, X, epi, F16, R=R, Wd=Wd, workspace=True)
+    assert np.array_equal(Y1.view(np.uint32), Y2.view(np.uint32))

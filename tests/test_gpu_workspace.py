@@ -75,7 +75,8 @@ def test_ws_workspace_is_scratch_only(gpu, qtype):
     n, T1, k1, T2, k2 = 384, 300, 1024, 37, 512
     need1 = gpu.workspace_bytes(qtype, n, k1, T1, SWIGLU, F16)
     need2 = gpu.workspace_bytes(qtype, n, k2, T2, PLAIN, F16)
-    assert need1 == 320 * k1 * 2 and need2 == 64 * k2 * 2
+    # the second call (K split into partial sums behind X) fits in the first's workspace
+    assert need1 == 320 * k1 * 2 and 64 * k2 * 2 < need2 <= need1
     guard = 4096
     buf = torch.full(((need1 + 2 * guard) // 2,), 0x5A5A, dtype=torch.int16, device="cuda")
     ws = buf[guard // 2: (guard + need1) // 2]
