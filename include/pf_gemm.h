@@ -117,9 +117,12 @@ int pf_gemm_path(int qtype, const void *W_blocks, int64_t n, int64_t k, const fl
  *  - 0 when pf_gemm_ws runs a kernel that needs none (the f32 leg, the GEMV, T == 0);
  *  - the f16 leg's matrix-core GEMM: X_b = ceil(T / 32) * 32 * k * 2 (X rounded to
  *    binary16, T padded to whole 32-row tiles);
- *  - and where that GEMM splits k across S workgroups (PLAIN or RESIDUAL, T >= 256,
- *    too few output tiles to fill the chip): ceil(X_b / 256) * 256 + S * ceil(T * n / 4)
- *    * 16, room for S blocks of [T][n] f32 partial sums. */
+ *  - and where that GEMM splits k across S workgroups (PLAIN or RESIDUAL with too few
+ *    output tiles to fill the chip; S is the largest count either block type takes):
+ *    ceil(X_b / 256) * 256 + S * ceil(T * n / 4) * 16, room for S blocks of [T][n] f32
+ *    partial sums;
+ *  - the SwiGLU epilogue on up to 64 rows, which runs as a split PLAIN GEMM over the 2n
+ *    gate and up rows: ceil(X_b / 256) * 256 + S * ceil(T * 2n / 4) * 16 (S >= 1). */
 int64_t pf_workspace_bytes(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int leg);
 
 /* pf_gemm with a caller workspace. On the f16 leg's matrix-core GEMM, X is first
@@ -127,9 +130,9 @@ int64_t pf_workspace_bytes(int qtype, int64_t n, int64_t k, int64_t T, int epilo
  * instead of rounding X again in every tile. The operands (RNE_fp16(x) and the
  * decoded weights) and the accumulation are the same as pf_gemm's, so the result is
  * pf_gemm's, bit for bit wherever neither splits k across workgroups. Where this
- * GEMM splits k (T >= 256), each split stores its partial sums in the workspace and
- * a second kernel adds R (RESIDUAL), then the splits in order: the result is
- * deterministic (pf_gemm's splits add with fp32 atomics, in any order).
+ * GEMM splits k, each split stores its partial sums in the workspace and a second
+ * kernel adds R (RESIDUAL), then the splits in order: the result is deterministic at
+ * every T (pf_gemm's splits below 256 rows add with fp32 atomics, in any order).
  *  workspace        device, owned by the caller, 16-byte aligned, at least
  *                   pf_workspace_bytes() bytes, not overlapping W, X or Y. Its
  *                   contents on entry are ignored and undefined on return. May be
@@ -215,8 +218,7 @@ int pf_lm_head_argmax(int qtype, const void *W_blocks, int64_t n, int64_t k, con
  *                 the same qtype, k and T, enqueued before it on the same stream (or
  *                 synchronised). The GEMM reads the copy and writes only past it (split-K
  *                 partial sums), so the copy stays valid for further calls.
- * The result is pf_gemm_ws's, bit for bit, wherever that is deterministic (from 256 rows;
- * below, a K split adds its partial sums with atomics in any order). pf_gemm_prepared
+ * The result is pf_gemm_ws's, bit for bit. pf_gemm_prepared
  * returns PF_E_PATH where PF_PATH_AUTO picks the GEMV for the f16 leg (which reads f32 X:
  * T <= 2, or T <= PF_GEMV_MAX_T with the SwiGLU epilogue); T == 0 is a no-op. Other
  * errors as pf_gemm_ws. */
