@@ -1037,8 +1037,17 @@ __global__ __launch_bounds__(256) void split_sum_kernel(const float *__restrict_
     const long quads = count >> 2;
     if (i < quads) {
         f4_t a = EPI == EPI_RESIDUAL ? reinterpret_cast<const f4_t *>(Y)[i] : f4_t{0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < splits; ++s)
-            a += reinterpret_cast<const f4_t *>(Ps + (size_t)s * pstride)[i];
+        auto part = [&](int s) { return reinterpret_cast<const f4_t *>(Ps + (size_t)s * pstride)[i]; };
+        // four splits' loads in flight at a time; the additions keep split order
+        int s = 0;
+        for (; s + 4 <= splits; s += 4) {
+            const f4_t p0 = part(s), p1 = part(s + 1), p2 = part(s + 2), p3 = part(s + 3);
+            a += p0;
+            a += p1;
+            a += p2;
+            a += p3;
+        }
+        for (; s < splits; ++s) a += part(s);
         reinterpret_cast<f4_t *>(Y)[i] = a;
     } else if (i == quads) {
         for (long e = 4 * quads; e < count; ++e) {
