@@ -70,10 +70,10 @@ enum { PF_PLAIN = 0, PF_RESIDUAL = 1, PF_GATE_UP_SWIGLU = 2 };
 enum { PF_LEG_F32 = 0, PF_LEG_F16 = 1 };
 
 /* Kernel family. PF_PATH_AUTO picks the GEMV for 1 <= T <= PF_GEMV_MAX_T and the
- * tiled matrix-core GEMM otherwise, except that the f16 leg's PLAIN and RESIDUAL
- * epilogues take the GEMM from T = 3 (faster there: its K split spreads the weight
- * stream over every CU). The other two force a family (tests compare them);
- * PF_PATH_GEMV requires T <= PF_GEMV_MAX_T. */
+ * tiled matrix-core GEMM otherwise, except that the f16 leg takes the GEMM from T = 3
+ * for PLAIN and RESIDUAL and from T = 5 for SwiGLU (faster there: its K split spreads
+ * the weight stream over every CU). The other two force a family (tests compare
+ * them); PF_PATH_GEMV requires T <= PF_GEMV_MAX_T. */
 enum { PF_PATH_AUTO = 0, PF_PATH_GEMM = 1, PF_PATH_GEMV = 2 };
 #define PF_GEMV_MAX_T 8
 
@@ -220,7 +220,7 @@ int pf_lm_head_argmax(int qtype, const void *W_blocks, int64_t n, int64_t k, con
  *                 partial sums), so the copy stays valid for further calls.
  * The result is pf_gemm_ws's, bit for bit. pf_gemm_prepared
  * returns PF_E_PATH where PF_PATH_AUTO picks the GEMV for the f16 leg (which reads f32 X:
- * T <= 2, or T <= PF_GEMV_MAX_T with the SwiGLU epilogue); T == 0 is a no-op. Other
+ * T <= 2, or T <= 4 with the SwiGLU epilogue); T == 0 is a no-op. Other
  * errors as pf_gemm_ws. */
 int pf_prepare_x(int qtype, int64_t k, const float *X, int64_t T, void *workspace, int64_t workspace_bytes,
                  void *stream);

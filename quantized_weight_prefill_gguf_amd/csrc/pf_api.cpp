@@ -46,13 +46,14 @@ int check_sizes(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int le
 }
 
 // Kernel family of PF_PATH_AUTO for T >= 1 rows. The GEMV up to PF_GEMV_MAX_T rows,
-// except on the f16 leg from 3 rows for PLAIN and RESIDUAL: there the matrix-core
-// GEMM's 32-row tile, split along K over every CU, streams the weights faster than
-// the GEMV (which reads them once per pair of rows). The SwiGLU epilogue cannot
-// split K, so it keeps the GEMV up to PF_GEMV_MAX_T.
+// except on the f16 leg from 3 rows for PLAIN and RESIDUAL and from 5 for SwiGLU:
+// there the matrix-core GEMM's 32-row tile, split along K over every CU, streams the
+// weights faster than the GEMV (whose time grows with each pair of rows). SwiGLU
+// splits K only through a workspace, so its crossing comes later (gate/up 2 x 12288 x
+// 4096: GEMV 36 us at 4 rows and 54 at 6, GEMM 43 unsplit or 28 through a workspace).
 int auto_path(int64_t T, int epilogue, int leg) {
     if (T > PF_GEMV_MAX_T) return PF_PATH_GEMM;
-    if (leg == PF_LEG_F16 && epilogue != PF_GATE_UP_SWIGLU && T >= 3) return PF_PATH_GEMM;
+    if (leg == PF_LEG_F16 && T >= (epilogue == PF_GATE_UP_SWIGLU ? 5 : 3)) return PF_PATH_GEMM;
     return PF_PATH_GEMV;
 }
 

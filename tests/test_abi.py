@@ -70,7 +70,9 @@ def test_select_path(lib):
     assert sel(pf.PF_Q4_0, 4096, 4096, 0, pf.PF_PLAIN, pf.PF_LEG_F32) == 0
     for T in (1, 2, 8):
         assert sel(pf.PF_Q4_0, 4096, 4096, T, pf.PF_PLAIN, pf.PF_LEG_F32) == pf.PF_PATH_GEMV
-        assert sel(pf.PF_Q4_0, 4096, 4096, T, pf.PF_GATE_UP_SWIGLU, pf.PF_LEG_F16) == pf.PF_PATH_GEMV
+    # f16 leg, SwiGLU: the GEMM from five rows on
+    for T, want in ((1, pf.PF_PATH_GEMV), (4, pf.PF_PATH_GEMV), (5, pf.PF_PATH_GEMM), (8, pf.PF_PATH_GEMM)):
+        assert sel(pf.PF_Q4_0, 4096, 4096, T, pf.PF_GATE_UP_SWIGLU, pf.PF_LEG_F16) == want
     # f16 leg, PLAIN and RESIDUAL: the GEMM from three rows on
     for T, want in ((1, pf.PF_PATH_GEMV), (2, pf.PF_PATH_GEMV), (3, pf.PF_PATH_GEMM), (8, pf.PF_PATH_GEMM)):
         assert sel(pf.PF_Q4_0, 4096, 4096, T, pf.PF_PLAIN, pf.PF_LEG_F16) == want
@@ -165,10 +167,10 @@ def test_workspace_bytes(lib):
     # 5 chunks of k are too few to split
     assert wb(pf.PF_Q4_0, 17, 1280, 290, pf.PF_RESIDUAL, pf.PF_LEG_F16) == 320 * 1280 * 2
     assert wb(pf.PF_Q4_0, 4096, 4096, 512, pf.PF_PLAIN, pf.PF_LEG_F32) == 0
-    # the GEMV (f16 leg: up to 2 rows, or up to 8 with the SwiGLU epilogue) takes none;
+    # the GEMV (f16 leg: up to 2 rows, or up to 4 with the SwiGLU epilogue) takes none;
     # from 3 rows the f16 leg's PLAIN and RESIDUAL run the GEMM
     assert wb(pf.PF_Q4_0, 4096, 4096, 2, pf.PF_PLAIN, pf.PF_LEG_F16) == 0
-    assert wb(pf.PF_Q4_0, 4096, 4096, 8, pf.PF_GATE_UP_SWIGLU, pf.PF_LEG_F16) == 0
+    assert wb(pf.PF_Q4_0, 4096, 4096, 4, pf.PF_GATE_UP_SWIGLU, pf.PF_LEG_F16) == 0
     assert 2 <= _split_blocks(wb(pf.PF_Q4_0, 4096, 4096, 8, pf.PF_PLAIN, pf.PF_LEG_F16),
                               32 * 4096 * 2, 8, 4096) <= 32
     assert 2 <= _split_blocks(wb(pf.PF_Q8_0, 4096, 4096, 3, pf.PF_RESIDUAL, pf.PF_LEG_F16),
@@ -327,7 +329,7 @@ def test_prepared_argument_checks(lib):
                                            P(kw.get("ws", WS)), kw.get("wsb", need), None)
     # where pf_gemm_ws runs the GEMV (which reads f32 X) there is no prepared GEMM
     assert gp(T=2) == pf.PF_E_PATH
-    assert gp(T=8, epi=pf.PF_GATE_UP_SWIGLU) == pf.PF_E_PATH
+    assert gp(T=4, epi=pf.PF_GATE_UP_SWIGLU) == pf.PF_E_PATH
     assert gp(ldy=n - 1) == pf.PF_E_SHAPE
     assert gp(epi=4) == pf.PF_E_EPILOGUE
     assert gp(W=0) == pf.PF_E_NULL

@@ -76,27 +76,30 @@ def test_one_copy_many_projections(gpu, qtype, T):
 @pytest.mark.parametrize("qtype", [Q4_0, Q8_0])
 @pytest.mark.parametrize("epi", [PLAIN, RESIDUAL, SWIGLU])
 def test_prepared_few_rows(gpu, qtype, epi):
-    """Five rows: PLAIN and RESIDUAL run the GEMM on the prepared copy (the family
-    pf_gemm_ws picks there on the f16 leg) and meet the oracle's bar; SwiGLU, which
-    pf_gemm_ws runs on the GEMV, has no prepared form and is refused."""
+    """Five rows: every epilogue runs the GEMM on the prepared copy (the family
+    pf_gemm_ws picks there on the f16 leg), bit for bit as pf_gemm_ws; where pf_gemm_ws
+    runs the GEMV (PLAIN at 2 rows, SwiGLU at 4) there is no prepared form and the call
+    is refused."""
     import torch
     n, k, T = 300, 1024, 5
     wid = 650 + epi + qtype
     W_np = weight(qtype, n, k, epi == SWIGLU, wid)
+    Wd = parity.to_dev(W_np)
     X = acts(T, k, wid)
     R = acts(T, n, wid, synth.TENSOR_R) if epi == RESIDUAL else None
     print("case prepared-few qtype=%d T=%d epi=%d" % (qtype, T, epi), flush=True)
-    xws = torch.full((32 * k,), -1, dtype=torch.int16, device="cuda")
-    gpu.prepare_x(qtype, k, parity.to_dev(X), xws)
+    ws = ws_for(gpu, qtype, n, k, T, epi)
+    gpu.prepare_x(qtype, k, parity.to_dev(X), ws)
     Y = torch.from_numpy(R.copy()).cuda() if R is not None else \
         torch.full((T, n), float("nan"), dtype=torch.float32, device="cuda")
-    if epi == SWIGLU:
-        with pytest.raises(gpu.PfError):
-            gpu.gemm_prepared(qtype, parity.to_dev(W_np), n, k, T, Y, epi, xws)
-        return
-    ws = ws_for(gpu, qtype, n, k, T, epi)
-    ws[:32 * k].copy_(xws)
-    gpu.gemm_prepared(qtype, parity.to_dev(W_np), n, k, T, Y, epi, ws)
+    gpu.gemm_prepared(qtype, Wd, n, k, T, Y, epi, ws)
     torch.cuda.synchronize()
+    Y0 = parity.run_gpu(gpu, qtype, None, n, k, X, epi, F16, R=R, Wd=Wd, workspace=True)
+    check(qtype, Wd, n, k, X, Y.cpu().numpy(), Y0, epi)
     ok, err = parity.check(qtype, W_np, n, k, X, Y.cpu().numpy(), epi, F16, R=R)
     assert ok, "parity failed: metric %.3e" % err
+    # the GEMV's row counts: refused before anything is enqueued
+    tg = 4 if epi == SWIGLU else 2
+    Yg = torch.zeros((tg, n), dtype=torch.float32, device="cuda")
+    with pytest.raises(gpu.PfError):
+        gpu.gemm_prepared(qtype, Wd, n, k, tg, Yg, epi, ws)
