@@ -172,10 +172,11 @@ def cpu_baseline(T, ops, inputs, target_s=12.0):
     }
 
 
-def load_traffic(workload, label, family):
+def load_traffic(workload, label, family, gemm_call_only=False):
     """HBM bytes per launch of the op from the stored counter passes (FETCH_SIZE and
     WRITE_SIZE, scaled by the copy calibration), or None when none were taken for
-    this workload or the kernel sources changed since."""
+    this workload or the kernel sources changed since. gemm_call_only: leave out the
+    X conversion kernels (the op's first call when it is timed as two)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -185,6 +186,10 @@ def load_traffic(workload, label, family):
     entry = rec.get("workloads", {}).get(workload, {}).get(label)
     if not entry or entry.get("kernel_source_sha") != kernel_source_sha(family):
         return None
+    if gemm_call_only:
+        conv = ("x_to_frag_kernel", "x_to_f16_kernel")
+        return sum(v["read_bytes"] + v["write_bytes"] for name, v in entry.get("kernels", {}).items()
+                   if not name.startswith(conv))
     return entry.get("bytes_per_launch")
 
 
@@ -534,11 +539,13 @@ def main():
     if hbm_bound:
         achieved = wbytes / (kern_ms[dom] * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK["hbm_gbs"], "unit": "GB/s",
-                    "frac": achieved / PEAK["hbm_gbs"], "traffic": load_traffic(args.workload, dop[0], family)}
+                    "frac": achieved / PEAK["hbm_gbs"],
+                    "traffic": load_traffic(args.workload, dop[0], family, nparts[dom] > 1)}
     else:
         achieved = op_flops(dop, T) / (kern_ms[dom] * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": achieved, "peak": mfma_peak, "unit": "TFLOP/s",
-                    "frac": achieved / mfma_peak, "traffic": load_traffic(args.workload, dop[0], family)}
+                    "frac": achieved / mfma_peak,
+                    "traffic": load_traffic(args.workload, dop[0], family, nparts[dom] > 1)}
     roofline["kernel"] = dop[0] + (" (GEMM call)" if nparts[dom] > 1 else "")
     roofline["avg_launch_us"] = kern_ms[dom] * 1e3
     roofline["op_us"] = op_ms[dom] * 1e3
