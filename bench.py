@@ -1,23 +1,31 @@
 #!/usr/bin/env python3
 """Benchmark of the quantized-weight prefill GEMM on one MI355X.
 
-A step is one pass of the hot path over one 512-token prefill chunk of the FFN:
-the fused gate/up SwiGLU GEMM (Q4_0, 4096 -> 2 x 12288) followed by the down
-projection with residual add (Q8_0, 12288 -> 4096), f16 leg (fp16 inputs, fp32
-accumulation), each through pf_gemm_ws (X rounded to fp16 once into a workspace,
-then the GEMM; both kernels sit inside the op's timing). Inputs are synthetic
-(seeded N(0, 0.02) weights quantized to Q4_0/Q8_0, N(0, 1) activations) and
-resident in HBM before timing starts; the weights rotate over enough copies
-(> 512 MB) that the 256 MB Infinity Cache does not hold them from one step to the
-next.
+A step (the default workload, gate_up_T512_f16) is the fused gate/up SwiGLU GEMM of
+one 512-token prefill chunk: Q4_0, 4096 -> 2 x 12288, f16 leg (fp16 inputs, fp32
+accumulation), as pf_gemm_ws runs it: X rounded to fp16 once into the workspace
+(pf_prepare_x), then the GEMM (pf_gemm_prepared); both calls are inside the step.
+Inputs are synthetic (seeded N(0, 0.02) weights quantized to Q4_0 / Q8_0, N(0, 1)
+activations) and resident in HBM before timing starts; the weights rotate over
+enough copies (> 512 MB) that the 256 MB Infinity Cache does not hold them from
+one step to the next.
 
-Prints one JSON line: value = FLOPs of the step / time (TFLOP/s), a roofline entry
-for the dominant kernel (the gate/up GEMM: its algorithmic FLOPs over its average
-HIP-event duration inside the timed region, against the fp16 dense MFMA peak), and
-the CPU oracle timed on a bounded sample of the same workload.
+Timing: --trials trials of --steps back-to-back steps, HIP events on the launch
+stream around each trial and a synchronize on both sides; ms_per_step is the median
+trial. Then each op, and the GEMM call of each op, run alone back to back for at
+least --kernel-ms per trial (median of --trials): that gives the roofline entry of
+the dominant kernel (its algorithmic FLOPs, or weight bytes where the weight stream
+bounds it, over its average launch duration, against the MI355X spec peak). The
+Q8_0 down projection with residual (12288 -> 4096) that follows in the FFN is timed
+after the step, with it, as `ffn_chain`. The CPU oracle is timed on a bounded sample
+of the step.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                    [--no-workspace]
+Prints one JSON line: value = FLOPs of the step / ms_per_step (TFLOP/s).
+
+    python bench.py [--steps K] [--warmup W] [--trials N] [--workload NAME]
+                    [--no-cpu-baseline] [--no-workspace]
+    python bench.py --trace-summary KT_DIR | --traffic-summary F W CF CW |
+                    --counter-summary PMC_DIR KT_DIR      (CPU only)
 """
 import argparse
 import ctypes
@@ -73,32 +81,40 @@ def log(msg):
 
 
 def workloads():
-    """name -> (T, leg, ops). op = (label, qtype, n, k, epilogue, input, output)."""
-    ffn = lambda T: (T, 1, [
-        ("gate_up_swiglu_q4_0", Q4_0, INTER, HIDDEN, SWIGLU, "x", "act"),
-        ("down_residual_q8_0", Q8_0, HIDDEN, INTER, RESIDUAL, "act", "res"),
-    ])
+    """name -> (T, leg, ops, step_ops). op = (label, qtype, n, k, epilogue, input,
+    output). A step is the first step_ops ops; any further ops are timed after the
+    step, with it, as the FFN chain they form."""
+    gu = ("gate_up_swiglu_q4_0", Q4_0, INTER, HIDDEN, SWIGLU, "x", "act")
+    down = ("down_residual_q8_0", Q8_0, HIDDEN, INTER, RESIDUAL, "act", "res")
     return {
-        "ffn_T512_f16": ffn(512),
-        "ffn_T2048_f16": ffn(2048),
+        # the metric's configuration: the fused gate/up SwiGLU GEMM at T = 512 (X
+        # conversion included); the down projection follows as the FFN chain
+        "gate_up_T512_f16": (512, 1, [gu, down], 1),
+        "ffn_T512_f16": (512, 1, [gu, down], 2),
+        "gate_up_T2048_f16": (2048, 1, [gu, down], 1),
+        "ffn_T2048_f16": (2048, 1, [gu, down], 2),
+        "down_T512_f16": (512, 1, [down], 1),
         # a short chunk (32 rows): the same two projections, bound by the weight stream
-        "ffn_T32_f16": ffn(32),
+        "ffn_T32_f16": (32, 1, [gu, down], 2),
         # the FFN sublayer as the pages run it: RMSNorm, gate/up SwiGLU, down + residual,
         # with the norm inside the gate/up call (pf_gemm_rmsnorm)
         "ffn_rmsnorm_T512_f16": (512, 1, [
-            ("rmsnorm_gate_up_swiglu_q4_0", Q4_0, INTER, HIDDEN, SWIGLU, "x", "act"),
-            ("down_residual_q8_0", Q8_0, HIDDEN, INTER, RESIDUAL, "act", "res"),
-        ]),
-        "ffn_T512_f32": (512, 0, ffn(512)[2]),
-        "plain_q4_0_4096_T512_f16": (512, 1, [("plain_q4_0", Q4_0, HIDDEN, HIDDEN, PLAIN, "x", "out")]),
-        "gemv_q4_0_12288x4096_T1": (1, 0, [("gemv_q4_0", Q4_0, INTER, HIDDEN, PLAIN, "x", "out")]),
-        "gemv_q8_0_4096x12288_T1": (1, 0, [("gemv_q8_0", Q8_0, HIDDEN, INTER, PLAIN, "x12288", "out")]),
-        "gemv_q4_0_12288x4096_T8": (8, 0, [("gemv_q4_0", Q4_0, INTER, HIDDEN, PLAIN, "x", "out")]),
-        "gemv_q8_0_4096x12288_T8": (8, 0, [("gemv_q8_0", Q8_0, HIDDEN, INTER, PLAIN, "x12288", "out")]),
+            ("rmsnorm_gate_up_swiglu_q4_0", Q4_0, INTER, HIDDEN, SWIGLU, "x", "act"), down], 2),
+        "gate_up_T512_f32": (512, 0, [gu, down], 1),
+        "plain_q4_0_4096_T512_f16": (512, 1, [("plain_q4_0", Q4_0, HIDDEN, HIDDEN, PLAIN, "x", "out")], 1),
+        "plain_q4_0_4096_T2048_f16": (2048, 1, [("plain_q4_0", Q4_0, HIDDEN, HIDDEN, PLAIN, "x", "out")], 1),
+        "gemv_q4_0_12288x4096_T1": (1, 0, [("gemv_q4_0", Q4_0, INTER, HIDDEN, PLAIN, "x", "out")], 1),
+        "gemv_q8_0_4096x12288_T1": (1, 0, [("gemv_q8_0", Q8_0, HIDDEN, INTER, PLAIN, "x12288", "out")], 1),
+        "gemv_q4_0_4096x12288_T1": (1, 0, [("gemv_q4_0", Q4_0, HIDDEN, INTER, PLAIN, "x12288", "out")], 1),
+        "gemv_q8_0_12288x4096_T1": (1, 0, [("gemv_q8_0", Q8_0, INTER, HIDDEN, PLAIN, "x", "out")], 1),
+        "gemv_q4_0_12288x4096_T2": (2, 0, [("gemv_q4_0", Q4_0, INTER, HIDDEN, PLAIN, "x", "out")], 1),
+        "gemv_q4_0_12288x4096_T4": (4, 0, [("gemv_q4_0", Q4_0, INTER, HIDDEN, PLAIN, "x", "out")], 1),
+        "gemv_q4_0_12288x4096_T8": (8, 0, [("gemv_q4_0", Q4_0, INTER, HIDDEN, PLAIN, "x", "out")], 1),
+        "gemv_q8_0_4096x12288_T8": (8, 0, [("gemv_q8_0", Q8_0, HIDDEN, INTER, PLAIN, "x12288", "out")], 1),
         # lm_head GEMV on one row plus the greedy token (pf_lm_head_argmax); the pages
         # give no vocabulary size: 151936 rows stand in for it
-        "lm_head_q8_0_151936x4096_T1": (1, 0, [("lm_head_q8_0", Q8_0, VOCAB, HIDDEN, PLAIN, "x", "logits")]),
-        "lm_head_q4_0_151936x4096_T1": (1, 0, [("lm_head_q4_0", Q4_0, VOCAB, HIDDEN, PLAIN, "x", "logits")]),
+        "lm_head_q8_0_151936x4096_T1": (1, 0, [("lm_head_q8_0", Q8_0, VOCAB, HIDDEN, PLAIN, "x", "logits")], 1),
+        "lm_head_q4_0_151936x4096_T1": (1, 0, [("lm_head_q4_0", Q4_0, VOCAB, HIDDEN, PLAIN, "x", "logits")], 1),
     }
 
 
@@ -275,7 +291,7 @@ def traffic_summary(workload, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir
     WRITE_SIZE passes over `bench.py --workload W`, each scaled by what the same
     counter reads for plain copies of known size (`bench.py --copy-calibration`).
     Updates profiles/traffic.json and prints a text summary. CPU only."""
-    T, leg, ops = workloads()[workload]
+    T, leg, ops, _ = workloads()[workload]
     cal_bytes = 256 * (1 << 20)
     cal = {}
     for cname, d in (("FETCH_SIZE", cal_fetch_dir), ("WRITE_SIZE", cal_write_dir)):
@@ -324,6 +340,86 @@ def traffic_summary(workload, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir
                                            kernel_source_sha(kernel_family(T, leg))))
 
 
+# Chip organisation used to turn chip-total counters into per-unit figures:
+# 8 XCDs x 32 CUs x 4 SIMDs.
+N_XCD, N_CU, N_SIMD = 8, 256, 1024
+
+
+def _trace_avg_ns(kt_dir):
+    """{short kernel name: (calls, average ns)} from a --kernel-trace --stats run."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(kt_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no kernel_stats.csv under %s" % kt_dir)
+    out = {}
+    with open(files[0]) as fh:
+        for r in csv.DictReader(fh):
+            out[_short_kernel(r["Name"])] = (int(r["Calls"]), float(r["AverageNs"]))
+    return out
+
+
+def counter_summary(workload, pmc_dir, kt_dir):
+    """MFMA utilisation and shader clock of each op's GEMM kernel, CPU only: from a
+    rocprofv3 --pmc pass with SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CYCLES, SQ_CYCLES and
+    GRBM_GUI_ACTIVE over `bench.py --workload W`, and the average launch duration of
+    the same kernel from a --kernel-trace --stats run of the same command.
+
+      sclk          = GRBM_GUI_ACTIVE / N_XCD / duration (GPU-busy cycles of one
+                      XCD's clock over the launch)
+      mfma_busy     = SQ_VALU_MFMA_BUSY_CYCLES / N_SIMD / (GRBM_GUI_ACTIVE / N_XCD)
+      frac_at_sclk  = achieved / (spec peak x sclk / 2.4 GHz)
+
+    Updates profiles/counters.json (keyed by the kernel sources' hash, as the
+    traffic table) and prints the raw totals next to the derived figures."""
+    T, leg, ops, _ = workloads()[workload]
+    counters = _counter_csv(pmc_dir)
+    trace = _trace_avg_ns(kt_dir)
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    rec["units"] = {"xcd": N_XCD, "cu": N_CU, "simd": N_SIMD, "spec_clock_ghz": 2.4}
+    wl = rec.setdefault("workloads", {})
+    wl[workload] = {}
+    names = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_CYCLES", "GRBM_GUI_ACTIVE")
+    peak = PEAK["fp16_mfma_tflops"] if leg == 1 else PEAK["fp32_mfma_tflops"]
+    lines = ["%-46s %6s %11s %14s %14s %14s %14s %8s %9s %8s" % (
+        "kernel", "disp", "avg_us", *names, "sclk", "mfma_busy", "frac@sclk")]
+    gemm_kernels = ("gemm_f16_coop_kernel", "gemm_f16_kernel", "gemm_f32_kernel", "gemv_kernel")
+    for op in ops:
+        per = {}
+        for (_, kn), cs in counters.items():
+            short = _short_kernel(kn)
+            if _op_of_kernel(short, ops) is op and short.startswith(gemm_kernels):
+                per.setdefault(short, []).append(cs)
+        for short, lst in sorted(per.items()):
+            avg = {c: sum(cs.get(c, 0.0) for cs in lst) / len(lst) for c in names}
+            if short not in trace:
+                continue
+            dur_ns = trace[short][1]
+            cycles = avg["GRBM_GUI_ACTIVE"] / N_XCD
+            sclk = cycles / dur_ns if dur_ns > 0 else 0.0
+            busy = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / N_SIMD / cycles if cycles > 0 else 0.0
+            achieved = op_flops(op, T) / (dur_ns * 1e-9) / 1e12
+            frac_sclk = achieved / (peak * sclk / 2.4) if sclk > 0 else 0.0
+            lines.append("%-46s %6d %11.2f %14.0f %14.0f %14.0f %14.0f %8.3f %9.3f %8.3f" % (
+                short[:46], len(lst), dur_ns / 1e3, *[avg[c] for c in names], sclk, busy, frac_sclk))
+            wl[workload][op[0]] = {"kernel_source_sha": kernel_source_sha(kernel_family(T, leg)),
+                                   "kernel": short, "dispatches": len(lst), "avg_us": dur_ns / 1e3,
+                                   "raw": avg, "sclk_ghz": sclk, "mfma_busy_frac": busy,
+                                   "frac_of_spec_peak": achieved / peak, "frac_at_sclk": frac_sclk}
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print("Counters per dispatch (chip totals), averaged over the dispatches; sclk in GHz;\n"
+          "mfma_busy = MFMA-busy cycles per SIMD over GPU-busy cycles per XCD.\n")
+    print("\n".join(lines))
+    print("\nkernel_source_sha (%s): %s" % (" + ".join(KERNEL_SOURCES[kernel_family(T, leg)]),
+                                           kernel_source_sha(kernel_family(T, leg))))
+
+
 def trace_summary(kt_dir):
     """CPU only: per-kernel launch statistics from a rocprofv3 --kernel-trace --stats
     output directory (its *kernel_stats.csv), in microseconds."""
@@ -340,12 +436,39 @@ def trace_summary(kt_dir):
                 float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["StdDev"]) / 1e3))
 
 
+def median(v):
+    v = sorted(v)
+    m = len(v) // 2
+    return v[m] if len(v) % 2 else 0.5 * (v[m - 1] + v[m])
+
+
+def load_counters(workload, label, family):
+    """Stored counter-pass figures of the op's GEMM kernel (profiles/counters.json,
+    written by --counter-summary), or None when none were taken for this workload or
+    the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get("workloads", {}).get(workload, {}).get(label)
+    if not entry or entry.get("kernel_source_sha") != kernel_source_sha(family):
+        return None
+    return {key: entry[key] for key in ("kernel", "mfma_busy_frac", "sclk_ghz", "frac_at_sclk")
+            if key in entry}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200, help="timed steps per trial")
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="ffn_T512_f16", choices=sorted(workloads()))
+    ap.add_argument("--trials", type=int, default=5,
+                    help="trials of --steps steps; the median trial is reported")
+    ap.add_argument("--kernel-ms", type=float, default=200.0,
+                    help="least GPU time per trial when an op or its GEMM call is timed alone")
+    ap.add_argument("--workload", default="gate_up_T512_f16", choices=sorted(workloads()))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-workspace", action="store_true",
                     help="call pf_gemm (X rounded inside the GEMM) instead of pf_gemm_ws")
@@ -358,6 +481,10 @@ def main():
                                                            "CAL_WRITE_DIR"),
                     help="CPU only: turn rocprofv3 FETCH_SIZE / WRITE_SIZE pass outputs over "
                          "--workload (and over --copy-calibration) into profiles/traffic.json")
+    ap.add_argument("--counter-summary", nargs=2, metavar=("PMC_DIR", "KT_DIR"),
+                    help="CPU only: turn a rocprofv3 --pmc pass (SQ_VALU_MFMA_BUSY_CYCLES "
+                         "SQ_BUSY_CYCLES SQ_CYCLES GRBM_GUI_ACTIVE) and a --kernel-trace run over "
+                         "--workload into profiles/counters.json")
     ap.add_argument("--trace-summary", metavar="KT_DIR",
                     help="CPU only: print the per-kernel table of a rocprofv3 --kernel-trace "
                          "--stats output directory")
@@ -368,6 +495,9 @@ def main():
         return
     if args.traffic_summary:
         traffic_summary(args.workload, *args.traffic_summary)
+        return
+    if args.counter_summary:
+        counter_summary(args.workload, *args.counter_summary)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -387,7 +517,8 @@ def main():
 
     pf.load()
     torch.cuda.set_device(0)
-    T, leg, ops = workloads()[args.workload]
+    T, leg, ops, step_ops = workloads()[args.workload]
+    step = ops[:step_ops]
 
     # ---- inputs (host, seeded), then resident in HBM
     wid = 3
@@ -435,7 +566,7 @@ def main():
                  if use_ws and ws_bytes > 0 else None)
 
     # Every call's ctypes arguments are marshalled once, here, so that the timed
-    # loop is C-ABI calls only and a short kernel does not wait on Python.
+    # loops are C-ABI calls only and a short kernel does not wait on Python.
     lib = pf.load()
     P = ctypes.c_void_p
     hstream = P(stream.cuda_stream)
@@ -462,7 +593,7 @@ def main():
             # the checks the binding makes, once
             pf.gemm_ws(qtype, dev_w[wset][label], n, k, bufs[src], Y, epi, leg, workspace) if use_ws \
                 else pf.gemm(qtype, dev_w[wset][label], n, k, bufs[src], Y, epi, leg)
-            if use_ws and leg == 1 and T > 8:
+            if use_ws and leg == 1 and pf.select_path(qtype, n, k, T, epi, leg) == pf.PF_PATH_GEMM:
                 # the same kernels as pf_gemm_ws in two calls, so that the GEMM's own
                 # launch can be timed: X rounded to fp16 into the workspace, then the GEMM
                 ws, wsb = P(workspace.data_ptr()), workspace.numel()
@@ -476,14 +607,34 @@ def main():
                 calls[(op[0], wset)] = [(lib.pf_gemm, (qtype, w, n, k, x, T, y, epi, leg, hstream))]
     torch.cuda.synchronize()
 
-    def launch(op, wset, marks=None):
-        """The op's C-ABI calls; marks[i + 1] is recorded after call i."""
-        for i, (fn, argv) in enumerate(calls[(op[0], wset)]):
-            st = fn(*argv)
-            if st != 0:
-                raise pf.PfError(st, fn.__name__)
-            if marks is not None:
-                marks[i + 1].record(stream)
+    def run(fn, argv):
+        st = fn(*argv)
+        if st != 0:
+            raise pf.PfError(st, fn.__name__)
+
+    def launch(op, wset, parts=None):
+        """The op's C-ABI calls (or the listed ones only)."""
+        cl = calls[(op[0], wset)]
+        for i in (range(len(cl)) if parts is None else parts):
+            run(*cl[i])
+
+    newev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed(body, count, trials):
+        """Median over trials of the GPU time of `count` back-to-back bodies, in ms per
+        body: HIP events on the launch stream around each trial, a synchronize on
+        both sides."""
+        per = []
+        for tr in range(trials):
+            e0, e1 = newev(), newev()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(count):
+                body(tr * count + i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) / count)
+        return median(per), per
 
     for i in range(args.warmup):
         for op in ops:
@@ -491,69 +642,82 @@ def main():
     torch.cuda.synchronize()
     log("warmup done (%d weight copies)" % copies)
 
-    # ---- timed region: K steps. HIP events on the launch stream: before every op
-    # and after each of its C-ABI calls when a step has several ops (so an op that
-    # is a conversion call then a GEMM call gives the GEMM's own duration); around
-    # the whole region when it has one, so that the launches run back to back as in
-    # the kernel trace (event markers around each microsecond-scale launch would add
-    # their own gaps).
-    single = len(ops) == 1
-    newev = lambda: torch.cuda.Event(enable_timing=True)
-    nparts = [len(calls[(op[0], 0)]) for op in ops]
-    ev = [[[newev() for _ in range(1 + nparts[j])] for j in range(len(ops))]
-          for _ in range(1 if single else args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    if single:
-        ev[0][0][0].record(stream)
-        for s in range(args.steps):
-            launch(ops[0], s % copies)
-        ev[0][0][-1].record(stream)
-    else:
-        for s in range(args.steps):
-            for j, op in enumerate(ops):
-                ev[s][j][0].record(stream)
-                launch(op, s % copies, ev[s][j])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    # ---- the timed region: trials x K steps (a step = the workload's first step_ops
+    # ops, each its C-ABI calls), each trial bracketed by a synchronize.
+    def one_step(i):
+        for op in step:
+            launch(op, i % copies)
 
-    step_flops = sum(op_flops(op, T) for op in ops)
-    ms_per_step = elapsed * 1e3 / args.steps
-    if single:
-        op_ms = [ev[0][0][0].elapsed_time(ev[0][0][-1]) / args.steps]
-        kern_ms = list(op_ms)
-    else:
-        op_ms = [float(np.mean([ev[s][j][0].elapsed_time(ev[s][j][-1]) for s in range(args.steps)]))
-                 for j in range(len(ops))]
-        # the op's last call (the GEMM, when X is converted by a call of its own)
-        kern_ms = [float(np.mean([ev[s][j][-2].elapsed_time(ev[s][j][-1]) for s in range(args.steps)]))
-                   for j in range(len(ops))]
-    dom = int(np.argmax(kern_ms))
-    dop = ops[dom]
+    t0 = time.perf_counter()
+    ms_per_step, trial_ms = timed(one_step, args.steps, args.trials)
+    elapsed = time.perf_counter() - t0
+    log("timed region done: %.4f ms/step (trials %s)" % (ms_per_step, ", ".join("%.4f" % v for v in trial_ms)))
+
+    # ---- each op alone, and each op's last call alone (the GEMM, when X is converted
+    # by a call of its own), back to back for at least --kernel-ms per trial.
+    def count_for(ms_est):
+        return int(max(100, min(20000, np.ceil(args.kernel_ms / max(ms_est, 1e-4)))))
+
+    op_ms, kern_ms, kern_launches = [], [], []
+    for op in ops:
+        nparts = len(calls[(op[0], 0)])
+        est, _ = timed(lambda i: launch(op, i % copies), 20, 1)
+        m, _ = timed(lambda i: launch(op, i % copies), count_for(est), args.trials)
+        op_ms.append(m)
+        if nparts > 1:
+            launch(op, 0, range(nparts - 1))  # the prepared X the GEMM call reads
+            last = [nparts - 1]
+            est, _ = timed(lambda i: launch(op, i % copies, last), 20, 1)
+            cnt = count_for(est)
+            m, _ = timed(lambda i: launch(op, i % copies, last), cnt, args.trials)
+        else:
+            cnt = count_for(est)
+        kern_ms.append(m)
+        kern_launches.append(cnt)
+    log("per-op timing done")
+
+    chain = None
+    if len(ops) > step_ops:
+        def one_chain(i):
+            for op in ops:
+                launch(op, i % copies)
+        c_ms, _ = timed(one_chain, max(args.steps, 20), args.trials)
+        cflops = sum(op_flops(op, T) for op in ops)
+        chain = {"ops": [op[0] for op in ops], "ms": c_ms, "tflops": cflops / (c_ms * 1e-3) / 1e12}
+
+    step_flops = sum(op_flops(op, T) for op in step)
+    dom = int(np.argmax(kern_ms[:step_ops]))
+    dop = step[dom]
+    nparts_dom = len(calls[(dop[0], 0)])
     family = kernel_family(T, leg)
     # the bound is whichever takes longer at peak: streaming the weights once from HBM,
     # or the op's matrix-core flops (the GEMV, and the GEMM on short chunks, are HBM-bound)
     wbytes = op_rows(dop) * (dop[3] // 32) * BLOCK[dop[1]]
     mfma_peak = PEAK["fp16_mfma_tflops"] if leg == 1 else PEAK["fp32_mfma_tflops"]
     hbm_bound = wbytes / (PEAK["hbm_gbs"] * 1e9) > op_flops(dop, T) / (mfma_peak * 1e12)
+    traffic = load_traffic(args.workload, dop[0], family, nparts_dom > 1)
     if hbm_bound:
         achieved = wbytes / (kern_ms[dom] * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK["hbm_gbs"], "unit": "GB/s",
-                    "frac": achieved / PEAK["hbm_gbs"],
-                    "traffic": load_traffic(args.workload, dop[0], family, nparts[dom] > 1)}
+                    "frac": achieved / PEAK["hbm_gbs"], "traffic": traffic}
+        op_frac = wbytes / (op_ms[dom] * 1e-3) / 1e9 / PEAK["hbm_gbs"]
     else:
         achieved = op_flops(dop, T) / (kern_ms[dom] * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": achieved, "peak": mfma_peak, "unit": "TFLOP/s",
-                    "frac": achieved / mfma_peak,
-                    "traffic": load_traffic(args.workload, dop[0], family, nparts[dom] > 1)}
-    roofline["kernel"] = dop[0] + (" (GEMM call)" if nparts[dom] > 1 else "")
+                    "frac": achieved / mfma_peak, "traffic": traffic}
+        op_frac = op_flops(dop, T) / (op_ms[dom] * 1e-3) / 1e12 / mfma_peak
+    roofline["kernel"] = dop[0] + (" (GEMM call)" if nparts_dom > 1 else "")
     roofline["avg_launch_us"] = kern_ms[dom] * 1e3
+    roofline["launches_per_trial"] = kern_launches[dom]
+    roofline["trials"] = args.trials
     roofline["op_us"] = op_ms[dom] * 1e3
-    roofline["op_frac"] = roofline["frac"] * kern_ms[dom] / op_ms[dom]
+    roofline["op_frac"] = op_frac
+    roofline["counters"] = load_counters(args.workload, dop[0], family)
 
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
     out = {
         "metric": METRIC,
-        "value": step_flops / (ms_per_step * 1e-3) / 1e12,
+        "value": value,
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -566,6 +730,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "T": T, "hidden": HIDDEN, "intermediate": INTER,
                    "leg": "f16" if leg == 1 else "f32",
+                   "step": [op[0] for op in step],
+                   "frac_of_peak": (value / mfma_peak) if not hbm_bound else None,
+                   "trials": args.trials, "trial_ms_per_step": trial_ms,
+                   "timed_wall_s": elapsed,
                    "ops": [{"op": op[0], "n": op[2], "k": op[3], "avg_us": op_ms[j] * 1e3,
                             "gemm_call_us": kern_ms[j] * 1e3,
                             "tflops": op_flops(op, T) / (op_ms[j] * 1e-3) / 1e12,
@@ -576,9 +744,10 @@ def main():
                    "workspace_bytes": ws_bytes if use_ws else 0},
         "roofline": roofline,
     }
-    log("timed region done: %.3f ms/step" % ms_per_step)
+    if chain is not None:
+        out["ffn_chain"] = chain
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(T, ops, inputs)
+        out["cpu_baseline"] = cpu_baseline(T, step, inputs)
         log("cpu baseline done")
     print(json.dumps(out), flush=True)
 

@@ -104,6 +104,10 @@ enum {
  *  epilogue  PF_PLAIN, PF_RESIDUAL or PF_GATE_UP_SWIGLU.
  *  leg       PF_LEG_F32 or PF_LEG_F16.
  *  stream    hipStream_t to enqueue on (NULL = default stream).
+ * Deterministic: with no workspace nothing is split across workgroups, so each
+ * output element is computed by one workgroup in a fixed order and repeated calls
+ * return the same bits. pf_gemm_ws is the faster form where the output alone leaves
+ * matrix cores idle (narrow n, short chunks): it splits k through its workspace.
  * Returns PF_OK or a PF_E_* code. */
 int pf_gemm(int qtype, const void *W_blocks, int64_t n, int64_t k, const float *X, int64_t T,
             float *Y, int epilogue, int leg, void *stream);
@@ -129,10 +133,10 @@ int64_t pf_workspace_bytes(int qtype, int64_t n, int64_t k, int64_t T, int epilo
  * rounded to binary16 once, into the workspace, and the GEMM then streams that copy
  * instead of rounding X again in every tile. The operands (RNE_fp16(x) and the
  * decoded weights) and the accumulation are the same as pf_gemm's, so the result is
- * pf_gemm's, bit for bit wherever neither splits k across workgroups. Where this
- * GEMM splits k, each split stores its partial sums in the workspace and a second
- * kernel adds R (RESIDUAL), then the splits in order: the result is deterministic at
- * every T (pf_gemm's splits below 256 rows add with fp32 atomics, in any order).
+ * pf_gemm's, bit for bit wherever this GEMM does not split k across workgroups
+ * (pf_gemm never does). Where it splits k, each split stores its partial sums in the
+ * workspace and a second kernel adds R (RESIDUAL), then the splits in order: the
+ * result is deterministic at every T.
  *  workspace        device, owned by the caller, 16-byte aligned, at least
  *                   pf_workspace_bytes() bytes, not overlapping W, X or Y. Its
  *                   contents on entry are ignored and undefined on return. May be

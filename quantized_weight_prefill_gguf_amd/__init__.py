@@ -114,6 +114,18 @@ def _dev_ptr(t, name):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def y_view_ldy(Y, T, n):
+    """ldy of a [T][n] float32 view Y whose rows may lie ldy >= n floats apart: the
+    elements of a row must be adjacent (stride 1) whenever a row has more than one,
+    whatever T is, since the library writes n consecutive floats per row. Raises
+    ValueError otherwise. Checks the view only (not the device)."""
+    if Y.dim() != 2 or tuple(Y.shape) != (T, n):
+        raise ValueError("Y must be a [T][n] view, got shape %s" % (tuple(Y.shape),))
+    if n > 1 and Y.stride(1) != 1:
+        raise ValueError("Y must have unit stride within rows")
+    return Y.stride(0) if T > 1 else n
+
+
 def workspace_bytes(qtype, n, k, T, epilogue, leg):
     """Bytes of workspace gemm_ws needs (0 if none; negative status on bad sizes)."""
     return load().pf_workspace_bytes(qtype, n, k, T, epilogue, leg)
@@ -158,9 +170,9 @@ def gemm_ex(qtype, W, n, k, X, Y, epilogue, leg, workspace=None, stream=None):
         raise TypeError("X and Y must be float32 and W uint8")
     if X.numel() != T * k or not X.is_contiguous():
         raise ValueError("X must be a contiguous [T][k] tensor")
-    if not Y.is_cuda or Y.dim() != 2 or tuple(Y.shape) != (T, n) or (T > 1 and Y.stride(1) != 1):
-        raise ValueError("Y must be a [T][n] device view with unit stride within rows")
-    ldy = Y.stride(0) if T > 1 else n
+    if not Y.is_cuda:
+        raise ValueError("Y must be a device tensor")
+    ldy = y_view_ldy(Y, T, n)
     rows = 2 * n if epilogue == PF_GATE_UP_SWIGLU else n
     need = load().pf_weight_bytes(qtype, rows, k)
     if need >= 0 and W.numel() < need:
@@ -192,9 +204,9 @@ def gemm_rmsnorm(qtype, W, n, k, X, norm_w, eps, Y, epilogue, leg, workspace, st
         raise TypeError("X, Y and norm_w must be float32 and W uint8")
     if X.numel() != T * k or norm_w.numel() != k:
         raise ValueError("X must hold T*k and norm_w k elements")
-    if not Y.is_cuda or Y.dim() != 2 or tuple(Y.shape) != (T, n) or (T > 1 and Y.stride(1) != 1):
-        raise ValueError("Y must be a [T][n] device view with unit stride within rows")
-    ldy = Y.stride(0) if T > 1 else n
+    if not Y.is_cuda:
+        raise ValueError("Y must be a device tensor")
+    ldy = y_view_ldy(Y, T, n)
     rows = 2 * n if epilogue == PF_GATE_UP_SWIGLU else n
     need = load().pf_weight_bytes(qtype, rows, k)
     if need >= 0 and W.numel() < need:
@@ -251,9 +263,9 @@ def gemm_prepared(qtype, W, n, k, T, Y, epilogue, workspace, stream=None):
     import torch
     if Y.dtype != torch.float32 or W.dtype != torch.uint8:
         raise TypeError("Y must be float32 and W uint8")
-    if not Y.is_cuda or Y.dim() != 2 or tuple(Y.shape) != (T, n) or (T > 1 and Y.stride(1) != 1):
-        raise ValueError("Y must be a [T][n] device view with unit stride within rows")
-    ldy = Y.stride(0) if T > 1 else n
+    if not Y.is_cuda:
+        raise ValueError("Y must be a device tensor")
+    ldy = y_view_ldy(Y, T, n)
     rows = 2 * n if epilogue == PF_GATE_UP_SWIGLU else n
     need = load().pf_weight_bytes(qtype, rows, k)
     if need >= 0 and W.numel() < need:

@@ -28,9 +28,10 @@
 // the same outputs, so g and u of one output sit in lanes c and c+16 of the same
 // register; the epilogue swaps them across the two lane groups.
 //
-// Large-n shapes run one workgroup per output tile; narrow ones (n = 4096 at
-// T = 512) split K over workgroups that add partial sums into Y with fp32 atomics
-// (PLAIN zero-fills Y first).
+// Large-n shapes run one workgroup per output tile. With a caller workspace, narrow
+// ones (n = 4096 at T = 512) and short chunks split K over workgroups that store
+// their partial sums in the workspace; a second kernel adds them in split order, so
+// the result is the same from run to run. Without a workspace nothing splits.
 #include <type_traits>
 
 #include "pf_device.h"
@@ -160,9 +161,12 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
     // f32 X (XH false): thread t converts float4 (t & 7) of rows (t >> 3) + 32 i.
     // fp16 X (XH true, already in fragment k order): thread t copies 16-byte chunk
     // (t & 3) of rows (t >> 2) + 64 i.
+    // Byte offsets: fp16 X holds T k < 2^31 halves, so 2 t k stays below 2^32; f32
+    // X reaches 4 t k >= 2^32 once t k >= 2^30, so its offsets are 64-bit.
     constexpr int XN = XH ? XH4 : XF4;
     const uint8_t *xbase = reinterpret_cast<const uint8_t *>(Xv) + (size_t)c_begin * 256 * (XH ? 2 : 4);
-    uint32_t xoff[XN];
+    typedef typename std::conditional<XH, uint32_t, uint64_t>::type xoff_t;
+    xoff_t xoff[XN];
     int xdst;
     if constexpr (XH) {
 #pragma unroll
@@ -176,7 +180,7 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
 #pragma unroll
         for (int i = 0; i < XN; ++i) {
             const int t = min(m0 + (tid >> 3) + 32 * i, T - 1);
-            xoff[i] = ((uint32_t)t * (uint32_t)k + 4 * (tid & 7)) * 4;
+            xoff[i] = ((uint64_t)t * (uint64_t)k + 4 * (tid & 7)) * 4;
         }
         // rows (tid >> 3) + 32 i share (row >> 2) & 3
         xdst = (tid >> 3) * 32 + ((((tid & 7) >> 1) ^ ((tid >> 5) & 3)) << 3) + 4 * (tid & 1);
@@ -510,16 +514,14 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
                     const int t = trow + 8 * (r >> 2) + (r & 3);
                     if (t < T && o < n) {
                         float *y = Y + (size_t)t * ldy + o;
-                        // A K split with pstride > 0 stores its partial sums in block
-                        // `split` of Y (the workspace; a sum kernel adds them in a fixed
-                        // order), else adds into Y with atomics. RESIDUAL adds into Y
-                        // with an atomic even without a K split: one writer per
-                        // element, so the result is the single rounding of R + acc
-                        // either way, and the add needs no VGPR copy of acc.
-                        if (SPLIT && pstride > 0)
+                        // A K split stores its partial sums in block `split` of Y
+                        // (the workspace, pstride floats apart; a sum kernel adds
+                        // them in split order). RESIDUAL without a split: one
+                        // writer per element reads R and stores R + acc.
+                        if constexpr (SPLIT)
                             y[(size_t)split * pstride] = acc[i][j][r];
-                        else if constexpr (SPLIT || EPI == EPI_RESIDUAL)
-                            atomicAdd(y, acc[i][j][r]);
+                        else if constexpr (EPI == EPI_RESIDUAL)
+                            *y = *y + acc[i][j][r];
                         else
                             *y = acc[i][j][r];
                     }
@@ -562,7 +564,7 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
 // nibble half of another, or three Q8_0 words; 512 x 96 tiles give each thread
 // one or two units of 4 weights. Within each half wave (32 lanes) the stores cover
 // 256 contiguous bytes of one fragment half, so they are free of bank conflicts.
-template <int QT, int EPI, bool SPLIT, int MT = 256, int AD = 2>
+template <int QT, int EPI, bool SPLIT, int MT = 256, int AD = 2, bool TALL = false>
 __global__ __launch_bounds__(512)
 void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ Xf,
                           float *__restrict__ Y, float *__restrict__ Ps, long pstride, int n,
@@ -570,17 +572,21 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
     using CT = ChunkTraits<QT>;
     static_assert(MT == 256 || MT == 512, "tile: 256 x 192 or 512 x 96");
     constexpr int NW = MT == 256 ? 192 : 96;        // weight rows per tile
-    constexpr int WN = NW / 96;                     // waves across the weight rows (2 or 1)
+    static_assert(!TALL || MT == 256, "the tall wave layout is for 256 x 192 tiles");
+    // TALL: the 8 waves stacked along the token rows, each 32 x 192 (1 x 6 MFMA
+    // tiles), so that every A row is loaded once per workgroup.
+    constexpr int WN = TALL ? 1 : NW / 96;          // waves across the weight rows
     constexpr int BB = CT::BB;                      // 18 / 34
-    constexpr int IT = 2, JT = 3;                   // per wave: 64 rows x 96 weight rows
+    constexpr int IT = TALL ? 1 : 2, JT = TALL ? 6 : 3;  // per wave: 64 x 96 or 32 x 192
     constexpr int U4 = CT::U4;                      // 9 / 17
     constexpr int WROW = CT::ROW;                   // 144 / 272
     constexpr int WBUF = NW * WROW;                 // raw chunk buffer
     constexpr int BBUF = NW * 32 * 2;               // B(s): NW/32 tiles x 2 halves x 64 lanes x 16 B
     constexpr int NBB = 4;                          // B buffers
     constexpr int PD = 4;                           // weight staging ring depth (steps)
-    static_assert(JT == 3, "the barrier's wait count below assumes JT reads in flight");
-    constexpr int WAITCNT_LGKM_JT = 0xC37F;         // s_waitcnt lgkmcnt(3)
+    // s_waitcnt lgkmcnt(JT): the barrier lets the JT B reads just issued stay in flight
+    constexpr int WAITCNT_LGKM_JT = 0xC07F | (JT << 8);
+    static_assert(JT <= 15, "lgkmcnt field");
     constexpr int LOOP_BYTES = NBB * BBUF + 2 * WBUF;
     constexpr int EPI_BYTES = 8 * 32 * 36 * 4;
     __shared__ __attribute__((aligned(16))) uint8_t smem[LOOP_BYTES > EPI_BYTES ? LOOP_BYTES : EPI_BYTES];
@@ -905,8 +911,8 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
                 fetch_slice(ch + 1 + ((blk + PD + 2) >> 3),
                             std::integral_constant<int, (blk + PD + 2) & 7>{}, wr[RG]);
             }
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);      // LDS read
-            for (int q = 0; q < 6; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x100, JT - 1, 0);  // LDS read
+            for (int q = 0; q < IT * JT; ++q) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
                 __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
@@ -918,7 +924,7 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
             decode_store(rw, std::integral_constant<int, (blk + 2) & 7>{},
                          std::integral_constant<int, (blk + 2) % NBB>{});
             load_a(s + AD, fa[RA]);
-            for (int q = 0; q < 6; ++q) {
+            for (int q = 0; q < IT * JT; ++q) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
                 __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);  // VALU
                 __builtin_amdgcn_sched_group_barrier(0x200, 1, 1);  // LDS write
@@ -1058,12 +1064,6 @@ __global__ __launch_bounds__(256) void split_sum_kernel(const float *__restrict_
     }
 }
 
-// Y[t][o] = 0 for t < T, o < n (rows ldy floats apart).
-__global__ void zero_fill_kernel(float *__restrict__ Y, int T, int n, int ldy) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i < T * n) Y[(size_t)(i / n) * ldy + i % n] = 0.f;
-}
-
 // Y [T][n] (rows ldy apart) = silu(g) * u with g = sum_s G_s[t][o], u = sum_s G_s[t][n + o]
 // over the `splits` blocks G_s [T][2n] (pstride floats apart) in order: the gate rows'
 // products in columns 0..n-1, the up rows' in n..2n-1.
@@ -1107,7 +1107,9 @@ constexpr int CFG_NW[4] = {192, 128, 128, 64};
 // cores with fewer LDS bytes and decode instructions per flop).
 constexpr float CFG_EFF[4] = {1.0f, 0.92f, 0.75f, 0.35f};
 
-TileChoice choose_tiles(const GemmArgs &a) {
+// allow_split: a K split needs room for its partial sums (a workspace); without
+// one the choice is among unsplit tilings only.
+TileChoice choose_tiles(const GemmArgs &a, bool allow_split) {
     const bool swiglu = a.epilogue == EPI_SWIGLU;
     const int nchunks = a.k / 256;
     const int cus = 256;
@@ -1121,7 +1123,7 @@ TileChoice choose_tiles(const GemmArgs &a) {
         const int mt = a.T <= 32 ? 32 : a.T <= 64 ? 64 : 128;
         const int cfg = mt == 32 ? 4 : mt == 64 ? 5 : 6;
         const int tn = (a.n + 127) / 128;
-        if (swiglu) return TileChoice{cfg, 1};
+        if (swiglu || !allow_split) return TileChoice{cfg, 1};
         const long slots = (long)cus * short_tile_waves(a.qtype, mt);
         int best_s = 1;
         long best_c = -1;
@@ -1143,7 +1145,7 @@ TileChoice choose_tiles(const GemmArgs &a) {
         const long tm = (a.T + MT - 1) / MT;
         const long tn = (a.n + out_per_tile - 1) / out_per_tile;
         for (int s = 1; s <= 8; ++s) {
-            if (s > 1 && (swiglu || s > nchunks)) break;
+            if (s > 1 && (swiglu || !allow_split || s > nchunks)) break;
             const long wgs = tm * tn * s;
             const long rounds = (wgs + cus - 1) / cus;
             // time ~ rounds x work per workgroup / efficiency, plus a split-K cost
@@ -1192,38 +1194,30 @@ hipError_t launch_split(const GemmArgs &a, TileChoice tc, const uint16_t *xh, hi
 // stored whole by one workgroup.
 long part_stride(int T, int n) { return ((long)T * n + 3) / 4 * 4; }
 
+// ps: room for the partial sums of a K split (the workspace), or null: then the
+// GEMM does not split, and every output has one writer.
 template <int QT, int EPI>
 hipError_t launch_epi(const GemmArgs &a, const uint16_t *xh, hipStream_t s, float *ps = nullptr) {
-    const TileChoice tc = choose_tiles(a);
+    const TileChoice tc = choose_tiles(a, ps != nullptr);
     if constexpr (EPI == EPI_SWIGLU) {
         return launch_split<QT, EPI, false>(a, TileChoice{tc.cfg, 1}, xh, s);
     } else {
         if (tc.splits == 1) return launch_split<QT, EPI, false>(a, tc, xh, s);
-        if (ps) {
-            // workspace: partial sums, then the fixed-order sum (deterministic)
-            GemmArgs p = a;
-            p.Y = ps;
-            p.ldy = a.n;
-            const long pstride = part_stride(a.T, a.n);
-            hipError_t e = launch_split<QT, EPI, true>(p, tc, xh, s, pstride);
-            if (e != hipSuccess) return e;
-            const long count = (long)a.T * a.n;
-            if (a.ldy == a.n)
-                hipLaunchKernelGGL((split_sum_kernel<EPI, true>), dim3((unsigned)((count / 4 + 1 + 255) / 256)),
-                                   dim3(256), 0, s, ps, a.Y, count, pstride, tc.splits, a.n, a.ldy);
-            else
-                hipLaunchKernelGGL((split_sum_kernel<EPI, false>), dim3((unsigned)((count + 255) / 256)),
-                                   dim3(256), 0, s, ps, a.Y, count, pstride, tc.splits, a.n, a.ldy);
-            return hipGetLastError();
-        }
-        if constexpr (EPI == EPI_PLAIN) {
-            const int count = a.T * a.n;
-            hipLaunchKernelGGL(zero_fill_kernel, dim3((count + 255) / 256), dim3(256), 0, s, a.Y, a.T, a.n,
-                               a.ldy);
-            const hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
-        }
-        return launch_split<QT, EPI, true>(a, tc, xh, s);
+        // partial sums into the workspace, then the fixed-order sum (deterministic)
+        GemmArgs p = a;
+        p.Y = ps;
+        p.ldy = a.n;
+        const long pstride = part_stride(a.T, a.n);
+        hipError_t e = launch_split<QT, EPI, true>(p, tc, xh, s, pstride);
+        if (e != hipSuccess) return e;
+        const long count = (long)a.T * a.n;
+        if (a.ldy == a.n)
+            hipLaunchKernelGGL((split_sum_kernel<EPI, true>), dim3((unsigned)((count / 4 + 1 + 255) / 256)),
+                               dim3(256), 0, s, ps, a.Y, count, pstride, tc.splits, a.n, a.ldy);
+        else
+            hipLaunchKernelGGL((split_sum_kernel<EPI, false>), dim3((unsigned)((count + 255) / 256)),
+                               dim3(256), 0, s, ps, a.Y, count, pstride, tc.splits, a.n, a.ldy);
+        return hipGetLastError();
     }
 }
 
@@ -1246,7 +1240,7 @@ hipError_t launch_swiglu_scratch(const GemmArgs &a, const uint16_t *xh, float *G
     g.n = 2 * a.n;
     g.Y = G;
     g.ldy = 2 * a.n;
-    const TileChoice tc = choose_tiles(g);
+    const TileChoice tc = choose_tiles(g, true);
     const long pstride = part_stride(a.T, 2 * a.n);
     const hipError_t e = tc.splits == 1 ? launch_split<QT, EPI_PLAIN, false>(g, tc, xh, s)
                                         : launch_split<QT, EPI_PLAIN, true>(g, tc, xh, s, pstride);
@@ -1272,7 +1266,7 @@ int small_t_splits(int T, int n, int k, int epilogue) {
         g.ldy = n;
         g.k = k;
         g.T = T;
-        const int sp = choose_tiles(g).splits;
+        const int sp = choose_tiles(g, true).splits;
         m = sp > m ? sp : m;
     }
     return m;
@@ -1350,6 +1344,10 @@ __global__ __launch_bounds__(256) void x_to_frag_kernel(const float *__restrict_
 #define PF_COOP_T512 512
 #endif
 constexpr int COOP_T512 = PF_COOP_T512;  // smallest T that takes the 512 x 96 tiles
+#ifndef PF_COOP_TALL
+#define PF_COOP_TALL 0
+#endif
+constexpr bool COOP_TALL = PF_COOP_TALL != 0;  // 256 x 192 tiles: waves 8 x 1 (else 4 x 2)
 
 // Split count of the cooperative-decode kernel. PLAIN / RESIDUAL split K when the
 // tiles alone would leave CUs idle (any split count; the chunk ranges of the splits
@@ -1378,8 +1376,8 @@ static int64_t ws_pstride(int T, int n) { return part_stride(T, n); }
 // run as one PLAIN GEMM over all 2n weight rows, split along K like the other short
 // chunks, into G [T][2n] f32 behind the fp16 X; swiglu_apply_kernel then writes
 // Y = silu(gate) * up. Measured faster than the unsplit fused epilogue up to 64 rows
-// (gate/up 2 x 12288 x 4096: 28-43 us against 43-46), slower at 100-128 (the atomics
-// and G's round trip grow with T). Without a workspace there is no room for G, and
+// (gate/up 2 x 12288 x 4096: 28-43 us against 43-46), slower at 100-128 (G's round
+// trip grows with T). Without a workspace there is no room for G, and
 // the fused epilogue runs unsplit.
 constexpr int SWIGLU_SCRATCH_T = 64;
 static bool swiglu_via_scratch(int T, int epilogue) { return epilogue == EPI_SWIGLU && T <= SWIGLU_SCRATCH_T; }
@@ -1412,7 +1410,8 @@ hipError_t launch_coop(const GemmArgs &a, uint16_t *xh, hipStream_t s) {
         if constexpr (EPI != EPI_SWIGLU) {
             float *ps = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(xh) + ws_x_bytes(a.T, a.k));
             const long pstride = (long)ws_pstride(a.T, a.n);
-            hipLaunchKernelGGL((gemm_f16_coop_kernel<QT, EPI, true, MT>), dim3(total), dim3(512), 0, s,
+            hipLaunchKernelGGL((gemm_f16_coop_kernel<QT, EPI, true, MT, 2, MT == 256 && COOP_TALL>), dim3(total),
+                               dim3(512), 0, s,
                                a.W, xh, a.Y, ps, pstride, a.n, a.ldy, a.k, a.T, tm, tn, splits);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
@@ -1427,8 +1426,8 @@ hipError_t launch_coop(const GemmArgs &a, uint16_t *xh, hipStream_t s) {
             }
         }
     } else {
-        hipLaunchKernelGGL((gemm_f16_coop_kernel<QT, EPI, false, MT>), dim3(total), dim3(512), 0, s, a.W,
-                           xh, a.Y, nullptr, 0L, a.n, a.ldy, a.k, a.T, tm, tn, splits);
+        hipLaunchKernelGGL((gemm_f16_coop_kernel<QT, EPI, false, MT, 2, MT == 256 && COOP_TALL>), dim3(total),
+                           dim3(512), 0, s, a.W, xh, a.Y, nullptr, 0L, a.n, a.ldy, a.k, a.T, tm, tn, splits);
     }
     return hipGetLastError();
 }

@@ -315,10 +315,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t *__restrict__ W
         }
     };
     // Chunks -> this wave's LDS region -> the dwords of each lane's pair. Lanes
-    // read what other lanes wrote, so a wave-scope release/acquire pair separates
-    // the writes from the reads, and the previous item's reads from these writes
-    // (no instruction is emitted: one wave's LDS operations complete in order; the
-    // fences keep the compiler from moving the accesses across).
+    // read what other lanes wrote, so wave_lds_sync separates the writes from the
+    // reads, and the previous item's reads from these writes: its fences keep the
+    // compiler from moving the accesses across, and its s_waitcnt lgkmcnt(0) makes
+    // the wave's earlier LDS operations complete before a later one issues.
     auto unpack = [&](const u4_t (&ch)[R][ST::NCH], uint32_t (&dw)[R][PT::DW]) __attribute__((always_inline)) {
         wave_lds_sync();
 #pragma unroll

@@ -360,3 +360,20 @@ def test_binding_refuses_host_tensors():
     Y = torch.zeros(1, 1)
     with pytest.raises(ValueError):
         pf.gemm(pf.PF_Q4_0, W, 1, 256, X, Y, pf.PF_PLAIN, pf.PF_LEG_F32)
+
+
+def test_binding_y_view_stride_rules():
+    """The strided-Y check of the binding (gemm_ex, gemm_rmsnorm, gemm_prepared):
+    the library writes n consecutive floats per row, so a row with more than one
+    element must have unit stride, also when T = 1 (a view such as buf[:1, ::2]
+    would otherwise have the columns between its elements overwritten)."""
+    import torch
+    buf = torch.zeros((4, 64), dtype=torch.float32)
+    assert pf.y_view_ldy(buf[:, :10], 4, 10) == 64
+    assert pf.y_view_ldy(buf[:1, :10], 1, 10) == 10
+    assert pf.y_view_ldy(buf[:, 3:4], 4, 1) == 64          # one column: any column stride
+    assert pf.y_view_ldy(buf[:1, ::64], 1, 1) == 1
+    for bad, T, n in [(buf[:1, ::2], 1, 32), (buf[:, ::2], 4, 32), (buf[:, :10], 4, 11),
+                      (buf[:, :10].reshape(-1), 4, 10)]:
+        with pytest.raises(ValueError):
+            pf.y_view_ldy(bad, T, n)

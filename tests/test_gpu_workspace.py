@@ -41,7 +41,8 @@ def run_ws_and_check(gpu, qtype, n, k, T, epi, leg, wid, samples=None, row_scale
 @pytest.mark.parametrize("n,k", [(17, 256), (200, 768), (640, 2048)])
 def test_ws_small_ragged(gpu, qtype, epi, T, n, k):
     # SwiGLU: the same bits as pf_gemm where neither splits K (above 64 rows; up to
-    # 64 the workspace path splits the gate and up products with atomics)
+    # 64 the workspace path splits the gate and up products into partial sums that
+    # a second kernel adds in split order)
     run_ws_and_check(gpu, qtype, n, k, T, epi, F16, wid=60 + n + T,
                      bitwise_vs_gemm=(epi == SWIGLU and T > 64))
 

@@ -132,3 +132,51 @@ def test_silu_range_is_exact_on_intervals():
     assert np.all(hi >= s.max(axis=1) - 1e-15)
     assert np.all(s.min(axis=1) - lo <= 1e-6)
     assert abs(tolerance.G_STAR + 1.2784645427610738) < 1e-12
+
+
+def test_f32_output_rounding_is_admitted_and_nothing_more():
+    """A residual far larger than the product's norms: the exact sum rounded once to
+    f32 passes (no f32 value is nearer), the next f32 value beyond the interval's
+    outward rounding fails, and so does a dropped product."""
+    rng = np.random.default_rng(5)
+    R = rng.standard_normal(4000)
+    acc = rng.standard_normal(4000) * 1e-6          # |acc| << ulp(R)
+    den = np.full(4000, 1e-6)                       # tau den = 1e-11 on the f32 leg
+    ref = R + acc
+    y = ref.astype(np.float32).astype(np.float64)
+    assert np.max(np.abs(y - ref) / den) > 1e-5      # the old |Y - Y_ref| <= tau D fails it
+    assert tolerance.check_linear_elems(y, ref, den, "f32")[0]
+    hi = tolerance.f32_up(ref + 1e-5 * den)
+    over = np.nextafter(hi.astype(np.float32), np.float32(np.inf)).astype(np.float64)
+    for i in range(0, 4000, 397):
+        y2 = y.copy()
+        y2[i] = over[i]
+        assert not tolerance.check_linear_elems(y2, ref, den, "f32")[0], i
+    assert not tolerance.check_linear_elems(R.astype(np.float32), ref, np.full(4000, 1e-9), "f32")[0]
+
+
+def test_f32_bounds_are_the_neighbouring_f32_values():
+    v = np.array([1.0, 1.0 + 2.0 ** -30, -1.0 - 2.0 ** -30, 1e-50, -1e-50, 3e38 * 1.2])
+    lo, hi = tolerance.f32_down(v), tolerance.f32_up(v)
+    assert list(lo[:3]) == [1.0, 1.0, np.nextafter(np.float32(-1.0), np.float32(-2))]
+    assert list(hi[:3]) == [1.0, np.nextafter(np.float32(1.0), np.float32(2)), -1.0]
+    assert lo[3] == 0.0 and hi[3] == 2.0 ** -149 and lo[4] == -(2.0 ** -149) and hi[4] == 0.0
+    assert lo[5] == np.finfo(np.float32).max and hi[5] == np.inf
+
+
+def test_swiglu_f32_underflow_is_admitted():
+    """g = -115.8 with a large u: any f32 silu(g) is 0 (e^-g overflows), so Y = 0 must
+    pass although silu(g) u = -1.4e-42 is an f32 subnormal; the allowance is
+    2^-120 (|u| + tau U) = 1.8e-30 here, so 1e-28 fails, and away from underflow
+    nothing changes."""
+    g = np.array([-115.84, -115.84, 3.0, -2.0])
+    u = np.array([2.45433e6, 2.45433e6, 5.0, 7.0])
+    gden = np.array([4.7e3, 4.7e3, 10.0, 10.0])
+    uden = np.array([9.4e7, 9.4e7, 10.0, 10.0])
+    yref = g / (1 + np.exp(-g)) * u
+    ok, _ = tolerance.swiglu_check_elems(np.array([0.0, -0.0, yref[2], yref[3]]), g, u, gden, uden, "f32")
+    assert ok
+    bad = np.array([0.0, 1e-28, yref[2], yref[3]])
+    assert not tolerance.swiglu_check_elems(bad, g, u, gden, uden, "f32")[0]
+    bad = np.array([0.0, 0.0, yref[2] * (1 + 1e-3), yref[3]])
+    assert not tolerance.swiglu_check_elems(bad, g, u, gden, uden, "f32")[0]
