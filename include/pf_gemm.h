@@ -91,8 +91,10 @@ enum {
     PF_E_ALIAS = 7,    /* Y (or out) overlaps W or X */
     PF_E_LAUNCH = 8,   /* the HIP runtime refused the launch */
     PF_E_PATH = 9,     /* unknown path, or PF_PATH_GEMV with T > PF_GEMV_MAX_T */
-    PF_E_WORKSPACE = 10 /* workspace NULL, smaller than pf_workspace_bytes(), not
-                           16-byte aligned, or overlapping W, X or Y */
+    PF_E_WORKSPACE = 10, /* workspace NULL, smaller than pf_workspace_bytes(), not
+                            16-byte aligned, or overlapping W, X or Y */
+    PF_E_SCRATCH = 11    /* pf_gemm_noalloc: pf_workspace_bytes() of the call exceeds
+                            PF_NOALLOC_SCRATCH_BYTES */
 };
 
 /* The projection GEMM.
@@ -194,6 +196,26 @@ int pf_gemm_rmsnorm(int qtype, const void *W_blocks, int64_t n, int64_t k, const
  * leg's matrix-core GEMM (the family PF_PATH_AUTO picks), pf_workspace_bytes() for the same
  * sizes, otherwise T * k * 4 (Xn in f32). Host-only. */
 int64_t pf_rmsnorm_workspace_bytes(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int leg);
+
+/* pf_gemm_ws without a caller workspace and without any allocation, for callers that
+ * cannot allocate device memory (code under stream capture, tight serving loops,
+ * harnesses that forbid hipMalloc). The workspace is a static device array of
+ * PF_NOALLOC_SCRATCH_BYTES in the library, one per GPU, held until the process
+ * ends; its address is looked up once per device, at the first call there (that
+ * call may load the library's code object on that device). Results equal
+ * pf_gemm_ws's bit for bit (the same kernels on the same operands).
+ *  - Calls needing more than PF_NOALLOC_SCRATCH_BYTES (pf_workspace_bytes() of the
+ *    same arguments) return PF_E_SCRATCH and launch nothing. 64 MiB holds every
+ *    shape of the FFN at hidden 4096 / intermediate 12288 up to T = 2048.
+ *  - Every call on a GPU shares that GPU's scratch: calls that may overlap on one
+ *    GPU (different streams without ordering) race and must be serialised by the
+ *    caller. The scratch keeps the last call's contents; no call reads what it
+ *    did not write itself, so nothing needs clearing.
+ *  - The scratch lives on the device of `stream` (the current device for NULL).
+ * Other arguments, ownership and errors as pf_gemm. */
+#define PF_NOALLOC_SCRATCH_BYTES (64ll << 20)
+int pf_gemm_noalloc(int qtype, const void *W_blocks, int64_t n, int64_t k, const float *X, int64_t T,
+                    float *Y, int epilogue, int leg, void *stream);
 
 /* The lm_head step of a prefill: logits = x . W_hat^T for one activation row (the
  * GEMV, f32), then the greedy token, on the device. The page "oxibonsai-kernels 0.1.4 -

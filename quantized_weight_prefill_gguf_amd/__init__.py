@@ -16,7 +16,8 @@ PF_LEG_F32, PF_LEG_F16 = 0, 1
 PF_PATH_AUTO, PF_PATH_GEMM, PF_PATH_GEMV = 0, 1, 2
 PF_GEMV_MAX_T = 8
 (PF_OK, PF_E_NULL, PF_E_QTYPE, PF_E_EPILOGUE, PF_E_LEG, PF_E_SHAPE, PF_E_ALIGN,
- PF_E_ALIAS, PF_E_LAUNCH, PF_E_PATH, PF_E_WORKSPACE) = range(11)
+ PF_E_ALIAS, PF_E_LAUNCH, PF_E_PATH, PF_E_WORKSPACE, PF_E_SCRATCH) = range(12)
+PF_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 BLOCK_BYTES = {PF_Q4_0: 18, PF_Q8_0: 34}
 QTYPES = {"q4_0": PF_Q4_0, "q8_0": PF_Q8_0}
@@ -26,7 +27,7 @@ LEGS = {"f32": PF_LEG_F32, "f16": PF_LEG_F16}
 # Every symbol include/pf_gemm.h declares.
 EXPORTS = ("pf_gemm", "pf_gemm_path", "pf_workspace_bytes", "pf_gemm_ws", "pf_gemm_ex",
            "pf_gemm_rmsnorm", "pf_rmsnorm_workspace_bytes", "pf_lm_head_argmax", "pf_prepare_x",
-           "pf_gemm_prepared", "pf_select_path",
+           "pf_gemm_prepared", "pf_select_path", "pf_gemm_noalloc",
            "pf_dequant_f32",
            "pf_dequant_f16", "pf_weight_bytes", "pf_strerror")
 
@@ -51,6 +52,8 @@ def load():
     i32, i64, P = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p
     lib.pf_gemm.argtypes = [i32, P, i64, i64, P, i64, P, i32, i32, P]
     lib.pf_gemm.restype = i32
+    lib.pf_gemm_noalloc.argtypes = [i32, P, i64, i64, P, i64, P, i32, i32, P]
+    lib.pf_gemm_noalloc.restype = i32
     lib.pf_gemm_path.argtypes = [i32, P, i64, i64, P, i64, P, i32, i32, P, i32]
     lib.pf_gemm_path.restype = i32
     lib.pf_workspace_bytes.argtypes = [i32, i64, i64, i64, i32, i32]
@@ -289,6 +292,17 @@ def gemm(qtype, W, n, k, X, Y, epilogue, leg, stream=None, path=PF_PATH_AUTO):
                           epilogue, leg, _stream_handle(stream), path)
     if st != PF_OK:
         raise PfError(st, "pf_gemm")
+    return Y
+
+
+def gemm_noalloc(qtype, W, n, k, X, Y, epilogue, leg, stream=None):
+    """gemm_ws in the library's static device scratch: no workspace argument and no
+    allocation (see pf_gemm_noalloc; calls that overlap on one GPU race)."""
+    T = _check_gemm_args(qtype, W, n, k, X, Y, epilogue)
+    st = load().pf_gemm_noalloc(qtype, _dev_ptr(W, "W"), n, k, _dev_ptr(X, "X"), T, _dev_ptr(Y, "Y"),
+                                epilogue, leg, _stream_handle(stream))
+    if st != PF_OK:
+        raise PfError(st, "pf_gemm_noalloc")
     return Y
 
 

@@ -65,8 +65,12 @@ int64_t ws_need(int64_t n, int64_t k, int64_t T, int epilogue, int leg, int use)
                                                       : 0;
 }
 
+// Where a call's workspace comes from: none (the kernels that need none, or the
+// f16 GEMM rounding X inside itself), the caller, or the static device scratch.
+enum WsMode { WS_NONE = 0, WS_CALLER = 1, WS_STATIC = 2 };
+
 int gemm_impl(int qtype, const void *W, int64_t n, int64_t k, const float *X, int64_t T, float *Y,
-              int64_t ldy, int epilogue, int leg, void *stream, int path, bool with_ws, void *ws,
+              int64_t ldy, int epilogue, int leg, void *stream, int path, int ws_mode, void *ws,
               int64_t ws_bytes) {
     int64_t n_w = 0;
     int st = check_sizes(qtype, n, k, T, epilogue, leg, &n_w);
@@ -81,8 +85,14 @@ int gemm_impl(int qtype, const void *W, int64_t n, int64_t k, const float *X, in
     const int64_t x_bytes = T * k * 4, y_bytes = ((T - 1) * ldy + n) * 4;  // Y's rows and gaps
     if (overlap(Y, y_bytes, X, x_bytes) || overlap(Y, y_bytes, W, w_bytes)) return PF_E_ALIAS;
     const int use = path == PF_PATH_AUTO ? auto_path(T, epilogue, leg) : path;
-    const int64_t need = with_ws ? ws_need(n, k, T, epilogue, leg, use) : 0;
-    if (need > 0) {
+    const int64_t need = ws_mode != WS_NONE ? ws_need(n, k, T, epilogue, leg, use) : 0;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (need > 0 && ws_mode == WS_STATIC) {
+        // every check is done: the first HIP call of the request
+        if (need > pf::kNoallocScratchBytes) return PF_E_SCRATCH;
+        if (pf::noalloc_scratch(s, &ws) != hipSuccess) return PF_E_LAUNCH;
+        ws_bytes = pf::kNoallocScratchBytes;
+    } else if (need > 0) {
         if (!ws || ws_bytes < need || !aligned16(ws)) return PF_E_WORKSPACE;
         if (overlap(ws, need, W, w_bytes) || overlap(ws, need, X, x_bytes) ||
             overlap(ws, need, Y, y_bytes))
@@ -99,7 +109,6 @@ int gemm_impl(int qtype, const void *W, int64_t n, int64_t k, const float *X, in
     a.ldy = (int)ldy;
     a.k = (int)k;
     a.T = (int)T;
-    const hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t err;
     if (use == PF_PATH_GEMV)
         err = pf::launch_gemv(a, s);
@@ -193,7 +202,13 @@ extern "C" {
 
 int pf_gemm(int qtype, const void *W_blocks, int64_t n, int64_t k, const float *X, int64_t T,
             float *Y, int epilogue, int leg, void *stream) {
-    return gemm_impl(qtype, W_blocks, n, k, X, T, Y, n, epilogue, leg, stream, PF_PATH_AUTO, false,
+    return gemm_impl(qtype, W_blocks, n, k, X, T, Y, n, epilogue, leg, stream, PF_PATH_AUTO, WS_NONE,
+                     nullptr, 0);
+}
+
+int pf_gemm_noalloc(int qtype, const void *W_blocks, int64_t n, int64_t k, const float *X, int64_t T,
+                    float *Y, int epilogue, int leg, void *stream) {
+    return gemm_impl(qtype, W_blocks, n, k, X, T, Y, n, epilogue, leg, stream, PF_PATH_AUTO, WS_STATIC,
                      nullptr, 0);
 }
 
@@ -202,13 +217,13 @@ int pf_gemm_ex(int qtype, const void *W_blocks, int64_t n, int64_t k, const floa
                int64_t workspace_bytes, void *stream) {
     const bool with_ws = workspace != nullptr || workspace_bytes != 0;
     return gemm_impl(qtype, W_blocks, n, k, X, T, Y, ldy, epilogue, leg, stream, PF_PATH_AUTO,
-                     with_ws, workspace, workspace_bytes);
+                     with_ws ? WS_CALLER : WS_NONE, workspace, workspace_bytes);
 }
 
 int pf_gemm_ws(int qtype, const void *W_blocks, int64_t n, int64_t k, const float *X, int64_t T,
                float *Y, int epilogue, int leg, void *workspace, int64_t workspace_bytes,
                void *stream) {
-    return gemm_impl(qtype, W_blocks, n, k, X, T, Y, n, epilogue, leg, stream, PF_PATH_AUTO, true,
+    return gemm_impl(qtype, W_blocks, n, k, X, T, Y, n, epilogue, leg, stream, PF_PATH_AUTO, WS_CALLER,
                      workspace, workspace_bytes);
 }
 
@@ -322,7 +337,7 @@ int64_t pf_workspace_bytes(int qtype, int64_t n, int64_t k, int64_t T, int epilo
 
 int pf_gemm_path(int qtype, const void *W_blocks, int64_t n, int64_t k, const float *X,
                  int64_t T, float *Y, int epilogue, int leg, void *stream, int path) {
-    return gemm_impl(qtype, W_blocks, n, k, X, T, Y, n, epilogue, leg, stream, path, false, nullptr, 0);
+    return gemm_impl(qtype, W_blocks, n, k, X, T, Y, n, epilogue, leg, stream, path, WS_NONE, nullptr, 0);
 }
 
 int pf_select_path(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int leg) {
@@ -373,6 +388,7 @@ const char *pf_strerror(int status) {
     case PF_E_LAUNCH: return "PF_E_LAUNCH: kernel launch failed";
     case PF_E_PATH: return "PF_E_PATH: unknown path or GEMV with T > 8";
     case PF_E_WORKSPACE: return "PF_E_WORKSPACE: workspace missing, too small, misaligned or overlapping";
+    case PF_E_SCRATCH: return "PF_E_SCRATCH: the call needs more than the static scratch holds";
     default: return "unknown status";
     }
 }

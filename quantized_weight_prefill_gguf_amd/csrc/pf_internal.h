@@ -49,6 +49,10 @@ hipError_t launch_rms_apply(const float *X, const float *inv, const float *w, fl
 hipError_t launch_argmax(const float *logits, int n, int32_t *token, hipStream_t s);
 // Small-T GEMV (T <= 8), f32 arithmetic.
 hipError_t launch_gemv(const GemmArgs &a, hipStream_t s);
+// Size of the static device scratch pf_gemm_noalloc runs in (PF_NOALLOC_SCRATCH_BYTES),
+// and its address on the device of stream s (taken once per device, then cached).
+constexpr int64_t kNoallocScratchBytes = int64_t(64) << 20;
+hipError_t noalloc_scratch(hipStream_t s, void **ptr);
 // Block decode to f32 / binary16.
 hipError_t launch_dequant_f32(int qtype, const uint8_t *W, int rows, int k, float *out,
                               hipStream_t s);

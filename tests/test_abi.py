@@ -43,10 +43,13 @@ def test_header_enums_match_binding():
     for name in ["PF_Q4_0", "PF_Q8_0", "PF_PLAIN", "PF_RESIDUAL", "PF_GATE_UP_SWIGLU",
                  "PF_LEG_F32", "PF_LEG_F16", "PF_PATH_AUTO", "PF_PATH_GEMM", "PF_PATH_GEMV",
                  "PF_OK", "PF_E_NULL", "PF_E_QTYPE", "PF_E_EPILOGUE", "PF_E_LEG", "PF_E_SHAPE",
-                 "PF_E_ALIGN", "PF_E_ALIAS", "PF_E_LAUNCH", "PF_E_PATH", "PF_E_WORKSPACE"]:
+                 "PF_E_ALIGN", "PF_E_ALIAS", "PF_E_LAUNCH", "PF_E_PATH", "PF_E_WORKSPACE",
+                 "PF_E_SCRATCH"]:
         m = re.search(r"\b%s\s*=\s*(\d+)" % name, src)
         assert m and int(m.group(1)) == getattr(pf, name), name
     assert int(re.search(r"#define PF_GEMV_MAX_T (\d+)", src).group(1)) == pf.PF_GEMV_MAX_T
+    m = re.search(r"#define PF_NOALLOC_SCRATCH_BYTES \((\d+)ll << (\d+)\)", src)
+    assert int(m.group(1)) << int(m.group(2)) == pf.PF_NOALLOC_SCRATCH_BYTES
 
 
 def test_weight_bytes(lib):
@@ -59,7 +62,7 @@ def test_weight_bytes(lib):
 
 
 def test_strerror(lib):
-    for code in range(11):
+    for code in range(12):
         s = lib.pf_strerror(code).decode()
         assert s.startswith("PF_"), s
     assert lib.pf_strerror(99).decode() == "unknown status"
@@ -377,3 +380,33 @@ def test_binding_y_view_stride_rules():
                       (buf[:, :10].reshape(-1), 4, 10)]:
         with pytest.raises(ValueError):
             pf.y_view_ldy(bad, T, n)
+
+
+def test_gemm_noalloc_argument_checks(lib):
+    """pf_gemm_noalloc refuses on the host, before its first HIP call (the scratch
+    lookup): the codes of pf_gemm, and PF_E_SCRATCH where pf_workspace_bytes()
+    exceeds the static scratch."""
+    P = ctypes.c_void_p
+    W, X, Y = FAKE, FAKE + (1 << 36), FAKE + (2 << 36)
+    f16, f32 = pf.PF_LEG_F16, pf.PF_LEG_F32
+
+    def g(qtype=pf.PF_Q4_0, W=W, n=64, k=256, X=X, T=16, Y=Y, epi=pf.PF_PLAIN, leg=f16):
+        return lib.pf_gemm_noalloc(qtype, P(W), n, k, P(X), T, P(Y), epi, leg, None)
+
+    assert g(qtype=5) == pf.PF_E_QTYPE
+    assert g(epi=7) == pf.PF_E_EPILOGUE
+    assert g(leg=3) == pf.PF_E_LEG
+    assert g(k=100) == pf.PF_E_SHAPE
+    assert g(W=0) == pf.PF_E_NULL
+    assert g(X=X + 4) == pf.PF_E_ALIGN
+    assert g(Y=X) == pf.PF_E_ALIAS
+    assert g(T=0) == pf.PF_OK and g(T=0, W=0, X=0, Y=0) == pf.PF_OK
+    # the down projection at T = 4096: 100 MB of fp16 X alone
+    need = lib.pf_workspace_bytes(pf.PF_Q8_0, 4096, 12288, 4096, pf.PF_RESIDUAL, f16)
+    assert need > pf.PF_NOALLOC_SCRATCH_BYTES
+    assert g(qtype=pf.PF_Q8_0, n=4096, k=12288, T=4096, epi=pf.PF_RESIDUAL) == pf.PF_E_SCRATCH
+    # the FFN's shapes up to T = 2048 fit
+    for qt, n, k, epi in [(pf.PF_Q4_0, 12288, 4096, pf.PF_GATE_UP_SWIGLU),
+                          (pf.PF_Q8_0, 4096, 12288, pf.PF_RESIDUAL), (pf.PF_Q4_0, 4096, 4096, pf.PF_PLAIN)]:
+        for T in (16, 64, 300, 512, 2048):
+            assert 0 <= lib.pf_workspace_bytes(qt, n, k, T, epi, f16) <= pf.PF_NOALLOC_SCRATCH_BYTES
