@@ -17,9 +17,10 @@ import numpy as np
 
 from . import build as _build
 
-Q4_0, Q8_0 = 0, 1
+Q4_0, Q8_0, F16, Q4_K, Q5_K, Q6_K = 0, 1, 2, 3, 4, 5
 PLAIN, RESIDUAL, GATE_UP_SWIGLU = 0, 1, 2
-BLOCK_BYTES = {Q4_0: 18, Q8_0: 34}
+BLOCK_BYTES = {Q4_0: 18, Q8_0: 34, F16: 64, Q4_K: 144, Q5_K: 176, Q6_K: 210}
+BLOCK_ELEMS = {Q4_0: 32, Q8_0: 32, F16: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256}
 
 _lib = None
 
@@ -88,8 +89,9 @@ def f32_to_fp16(x):
 
 def _check_blocks(qtype, W, rows, k):
     W = _c(W, np.uint8).reshape(-1)
-    need = rows * (k // 32) * BLOCK_BYTES[qtype]
-    if k % 32 or W.size < need:
+    be = BLOCK_ELEMS[qtype]
+    need = rows * (k // be) * BLOCK_BYTES[qtype]
+    if k % be or W.size < need:
         raise ValueError("weight buffer does not hold %d rows of k=%d" % (rows, k))
     return W
 

@@ -26,6 +26,12 @@
  *  - GGUF block formats: Q4_0 = fp16 d + 16 bytes of nibbles, element j < 16 is
  *    the low nibble of byte j, element j >= 16 the high nibble of byte j-16,
  *    value d*(q-8). Q8_0 = fp16 d + 32 int8 q, value d*q.
+ *  - aprender-serve 0.70.2, src/cuda/executor/gdn_prefill_ops.rs,
+ *    `qwen35_dequant_f32`: the further weight types the f32 leg dequantizes (F16,
+ *    Q4_K, Q5_K, Q6_K over 256-element super-blocks, F16 over 32-element groups),
+ *    and `qwen35_fp16_weight`: the f16 leg's weight is that f32 value rounded to
+ *    binary16. The pages print none of these layouts; they are GGUF's, restated
+ *    at decode_k_block below.
  *  - IEEE 754 binary16 for the scale and for the f16 leg's input rounding.
  *
  * Every floating-point step is written out: no fast-math, no FMA contraction
@@ -42,6 +48,10 @@
 
 #define ORACLE_Q4_0 0
 #define ORACLE_Q8_0 1
+#define ORACLE_F16 2
+#define ORACLE_Q4_K 3
+#define ORACLE_Q5_K 4
+#define ORACLE_Q6_K 5
 
 #define ORACLE_PLAIN 0
 #define ORACLE_RESIDUAL 1
@@ -161,11 +171,21 @@ void oracle_f32_to_fp16_array(const float *x, int64_t count, uint16_t *out)
  * ------------------------------------------------------------------------- */
 int oracle_block_bytes(int qtype)
 {
-    if (qtype == ORACLE_Q4_0)
-        return 18;
-    if (qtype == ORACLE_Q8_0)
-        return 34;
-    return -1;
+    switch (qtype) {
+    case ORACLE_Q4_0: return 18;
+    case ORACLE_Q8_0: return 34;
+    case ORACLE_F16: return 64;     /* 32 binary16 values */
+    case ORACLE_Q4_K: return 144;
+    case ORACLE_Q5_K: return 176;
+    case ORACLE_Q6_K: return 210;
+    default: return -1;
+    }
+}
+
+/* Weights per block: 32, or 256 for the super-block types. */
+int oracle_block_elems(int qtype)
+{
+    return (qtype == ORACLE_Q4_K || qtype == ORACLE_Q5_K || qtype == ORACLE_Q6_K) ? 256 : 32;
 }
 
 /* The scale: a binary16 stored little-endian in bytes 0-1 of the block. Its
@@ -176,12 +196,93 @@ static float block_scale(const uint8_t *blk)
     return (float)oracle_fp16_to_f64(h);
 }
 
-/* Decode one 32-element block into f32. Each value is one f32 multiply of the
- * scale by a small integer; the product of an 11-bit and a <= 8-bit significand
- * is exact in f32, so these are the canonical bits (including -0.0 when the
- * scale is negative and the integer is zero). */
-static void decode_block(int qtype, const uint8_t *blk, float out[32])
+static float fp16_at(const uint8_t *p)
 {
+    return (float)oracle_fp16_to_f64((uint16_t)(p[0] | (p[1] << 8)));
+}
+
+/* The 6-bit scale and min of sub-block j (0..7) of a Q4_K / Q5_K super-block, from
+ * its 12 packed bytes: sub-blocks 0-3 keep theirs in the low 6 bits of bytes j
+ * (scale) and j + 4 (min); sub-blocks 4-7 take their low 4 bits from the two
+ * nibbles of byte j + 4 (scale low, min high) and their top 2 bits from the top
+ * bits of bytes j - 4 (scale) and j (min). */
+static void k_scale_min(const uint8_t sc[12], int j, int *s, int *m)
+{
+    if (j < 4) {
+        *s = sc[j] & 63;
+        *m = sc[j + 4] & 63;
+    } else {
+        *s = (sc[j + 4] & 15) | ((sc[j - 4] >> 6) << 4);
+        *m = (sc[j + 4] >> 4) | ((sc[j] >> 6) << 4);
+    }
+}
+
+/* Decode one 256-element super-block (GGUF's K types) into f32.
+ *
+ * Q4_K (144 bytes): fp16 d, fp16 dmin, 12 bytes of 6-bit scales and mins, 128
+ *   bytes of nibbles. Element e lies in 64-element group p = e / 64; within it,
+ *   element l < 32 is the low nibble of qs[32p + l] and 32 + l its high nibble;
+ *   its sub-block is j = e / 32. Value (d s_j) q - dmin m_j: d s_j, dmin m_j and
+ *   (d s_j) q are exact in f32 (11 + 6 + 4 significant bits), so the one rounding
+ *   is the subtraction's.
+ * Q5_K (176 bytes): as Q4_K with 32 bytes qh after the scales (then the 128 qs):
+ *   element e = 32 b + l (b = 0..7, l = 0..31) adds 16 times bit b of qh[l].
+ * Q6_K (210 bytes): ql[128], qh[64], 16 int8 scales, fp16 d last. In half
+ *   h = e / 128 (ql from 64 h, qh from 32 h, scales from 8 h), quarter c = (e % 128)
+ *   / 32 and l = e % 32: the low 4 bits are the low (c = 0, 1) or high (c = 2, 3)
+ *   nibble of ql[l + 32 (c % 2)], the top 2 bits are bits 2c, 2c+1 of qh[l], and the
+ *   scale is scales[l / 16 + 2c]. Value (d sc) (q - 32): d sc is exact, the product
+ *   with q - 32 rounds once. */
+static void decode_k_block(int qtype, const uint8_t *blk, float *out)
+{
+    if (qtype == ORACLE_Q6_K) {
+        const uint8_t *ql = blk, *qh = blk + 128;
+        const int8_t *sc = (const int8_t *)(blk + 192);
+        float d = fp16_at(blk + 208);
+        for (int e = 0; e < 256; ++e) {
+            int h = e / 128, c = (e % 128) / 32, l = e % 32;
+            int lo = ql[64 * h + l + 32 * (c % 2)];
+            lo = (c < 2) ? (lo & 15) : (lo >> 4);
+            int hi = (qh[32 * h + l] >> (2 * c)) & 3;
+            int q = lo | (hi << 4);
+            float ds = d * (float)sc[8 * h + l / 16 + 2 * c];
+            out[e] = ds * (float)(q - 32);
+        }
+        return;
+    }
+    float d = fp16_at(blk), dmin = fp16_at(blk + 2);
+    const uint8_t *sc = blk + 4;
+    const uint8_t *qh = (qtype == ORACLE_Q5_K) ? blk + 16 : NULL;
+    const uint8_t *qs = (qtype == ORACLE_Q5_K) ? blk + 48 : blk + 16;
+    for (int e = 0; e < 256; ++e) {
+        int p = e / 64, l = e % 32, upper = (e % 64) >= 32;
+        int q = upper ? (qs[32 * p + l] >> 4) : (qs[32 * p + l] & 15);
+        if (qh)
+            q += ((qh[l] >> (e / 32)) & 1) * 16;
+        int s, m;
+        k_scale_min(sc, e / 32, &s, &m);
+        float a = d * (float)s, b = dmin * (float)m;
+        float aq = a * (float)q;
+        out[e] = aq - b;
+    }
+}
+
+/* Decode one block into f32 (32 or 256 elements, see oracle_block_elems). Q4_0 /
+ * Q8_0: each value is one f32 multiply of the scale by a small integer; the
+ * product of an 11-bit and a <= 8-bit significand is exact in f32, so these are
+ * the canonical bits (including -0.0 when the scale is negative and the integer
+ * is zero). F16: 32 little-endian binary16 values, widened exactly. */
+static void decode_block(int qtype, const uint8_t *blk, float *out)
+{
+    if (qtype == ORACLE_F16) {
+        for (int j = 0; j < 32; ++j)
+            out[j] = fp16_at(blk + 2 * j);
+        return;
+    }
+    if (qtype >= ORACLE_Q4_K) {
+        decode_k_block(qtype, blk, out);
+        return;
+    }
     float d = block_scale(blk);
     const uint8_t *qs = blk + 2;
     if (qtype == ORACLE_Q4_0) {
@@ -197,40 +298,40 @@ static void decode_block(int qtype, const uint8_t *blk, float out[32])
     }
 }
 
-/* Decode `rows` rows of k/32 blocks each (row r, block b at byte
- * (r*(k/32) + b) * block_bytes) into out[rows][k]. */
+/* Decode `rows` rows of k / E blocks each (E = oracle_block_elems; row r, block b
+ * at byte (r*(k/E) + b) * block_bytes) into out[rows][k]. */
 void oracle_dequant_f32(int qtype, const uint8_t *W, int64_t rows, int64_t k, float *out)
 {
-    int bb = oracle_block_bytes(qtype);
-    int64_t nb = k / 32;
+    int bb = oracle_block_bytes(qtype), be = oracle_block_elems(qtype);
+    int64_t nb = k / be;
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r)
         for (int64_t b = 0; b < nb; ++b)
-            decode_block(qtype, W + (r * nb + b) * bb, out + r * k + b * 32);
+            decode_block(qtype, W + (r * nb + b) * bb, out + r * k + b * be);
 }
 
 /* f16-leg weights: the f32 decode, then one RNE rounding to binary16. */
 void oracle_dequant_f16(int qtype, const uint8_t *W, int64_t rows, int64_t k, uint16_t *out)
 {
-    int bb = oracle_block_bytes(qtype);
-    int64_t nb = k / 32;
+    int bb = oracle_block_bytes(qtype), be = oracle_block_elems(qtype);
+    int64_t nb = k / be;
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
-        float tmp[32];
+        float tmp[256];
         for (int64_t b = 0; b < nb; ++b) {
             decode_block(qtype, W + (r * nb + b) * bb, tmp);
-            for (int j = 0; j < 32; ++j)
-                out[r * k + b * 32 + j] = oracle_f32_to_fp16_rne(tmp[j]);
+            for (int j = 0; j < be; ++j)
+                out[r * k + b * be + j] = oracle_f32_to_fp16_rne(tmp[j]);
         }
     }
 }
 
 static void decode_row(int qtype, const uint8_t *W, int64_t r, int64_t k, float *row)
 {
-    int bb = oracle_block_bytes(qtype);
-    int64_t nb = k / 32;
+    int bb = oracle_block_bytes(qtype), be = oracle_block_elems(qtype);
+    int64_t nb = k / be;
     for (int64_t b = 0; b < nb; ++b)
-        decode_block(qtype, W + (r * nb + b) * bb, row + b * 32);
+        decode_block(qtype, W + (r * nb + b) * bb, row + b * be);
 }
 
 /* Dot product in fp64, ascending index: each product of two f32 values is exact

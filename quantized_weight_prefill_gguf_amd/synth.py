@@ -19,13 +19,27 @@ bytes 0-1):
   byte 2+(j-16).
 * An all-zero block gets d16 = +0 and q = 0 (Q8_0) or 8 (Q4_0).
 
+* F16: the weight rounded to binary16, little-endian, 32 values (64 bytes) per
+  block.
+* Q4_K / Q5_K (256 weights, 144 / 176 B): per 32-weight sub-block j, an affine
+  code range from min(0, min w) to max w over 2^b - 1 steps (b = 4 or 5); the
+  super-block's d and dmin are the largest sub-block step and offset over 63
+  (binary16), the sub-block's 6-bit s_j, m_j their ratios to those (rounded), and
+  q = clamp(round((w + dmin m_j) / (d s_j)), 0, 2^b - 1).
+* Q6_K (256 weights, 210 B): per 16-weight sub-block a step amax / 31, d the
+  largest step over 127 (binary16), sc_j = round(step / d) as int8, and
+  q = clamp(round(w / (d sc_j)) + 32, 0, 63).
+  These encoders are test-input generators, not llama.cpp's quantizers; any valid
+  block serves the parity tests. Byte layouts: GGUF's, as the oracle restates them.
+
 numpy's float32 -> float16 cast is IEEE round-to-nearest-even.
 """
 import numpy as np
 
-Q4_0, Q8_0 = 0, 1
-BLOCK_BYTES = {Q4_0: 18, Q8_0: 34}
-QTYPE_NAMES = {"q4_0": Q4_0, "q8_0": Q8_0}
+Q4_0, Q8_0, F16, Q4_K, Q5_K, Q6_K = 0, 1, 2, 3, 4, 5
+BLOCK_BYTES = {Q4_0: 18, Q8_0: 34, F16: 64, Q4_K: 144, Q5_K: 176, Q6_K: 210}
+BLOCK_ELEMS = {Q4_0: 32, Q8_0: 32, F16: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256}
+QTYPE_NAMES = {"q4_0": Q4_0, "q8_0": Q8_0, "f16": F16, "q4_k": Q4_K, "q5_k": Q5_K, "q6_k": Q6_K}
 
 TENSOR_W, TENSOR_W_UP, TENSOR_W_DOWN, TENSOR_X, TENSOR_R, TENSOR_ROWSCALE = range(6)
 
@@ -102,8 +116,120 @@ def quantize_q4_0(w):
     return out.reshape(-1)
 
 
+def quantize_f16(w):
+    """f32 [rows][k] -> binary16 little-endian, uint8 [rows * k * 2]."""
+    w = np.ascontiguousarray(w, np.float32)
+    if w.shape[1] % 32:
+        raise ValueError("k must be a multiple of 32")
+    return w.astype(np.float16).view(np.uint8).reshape(-1).copy()
+
+
+def _fp16_bits(v):
+    return np.asarray(v, np.float32).astype(np.float16).view(np.uint16)
+
+
+def pack_k_scales(s, m):
+    """6-bit scales s and mins m [..., 8] -> the 12 packed bytes of a Q4_K / Q5_K
+    super-block: sub-blocks 0-3 in the low 6 bits of bytes j (scale) and j + 4
+    (min); sub-blocks 4-7 split into low nibbles (byte j + 4: scale low, min high)
+    and top 2 bits (bits 6-7 of bytes j - 4 and j)."""
+    s = np.asarray(s, np.uint8)
+    m = np.asarray(m, np.uint8)
+    out = np.zeros(s.shape[:-1] + (12,), np.uint8)
+    for j in range(4):
+        out[..., j] = (s[..., j] & 63) | ((s[..., j + 4] >> 4) << 6)
+        out[..., j + 4] = (m[..., j] & 63) | ((m[..., j + 4] >> 4) << 6)
+        out[..., j + 8] = (s[..., j + 4] & 15) | ((m[..., j + 4] & 15) << 4)
+    return out
+
+
+def _quantize_kaffine(w, bits):
+    w = np.ascontiguousarray(w, np.float32)
+    rows, k = w.shape
+    if k % 256:
+        raise ValueError("k must be a multiple of 256")
+    nq = (1 << bits) - 1
+    sb = w.reshape(rows, k // 256, 8, 32)
+    lo = np.minimum(sb.min(axis=3), 0.0).astype(np.float32)
+    hi = sb.max(axis=3).astype(np.float32)
+    step = (hi - lo) / np.float32(nq)
+    off = -lo
+    d16 = _fp16_bits(step.max(axis=2) / np.float32(63))
+    dm16 = _fp16_bits(off.max(axis=2) / np.float32(63))
+    d = d16.view(np.float16).astype(np.float32)[..., None]
+    dm = dm16.view(np.float16).astype(np.float32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        sj = np.where(d > 0, np.clip(_round_half_away(step / np.where(d > 0, d, 1)), 0, 63), 0).astype(np.uint8)
+        mj = np.where(dm > 0, np.clip(_round_half_away(off / np.where(dm > 0, dm, 1)), 0, 63), 0).astype(np.uint8)
+        a = (d * sj.astype(np.float32))[..., None]
+        b = (dm * mj.astype(np.float32))[..., None]
+        q = np.where(a > 0, np.clip(_round_half_away((sb + b) / np.where(a > 0, a, 1)), 0, nq), 0).astype(np.uint8)
+    return rows, k, d16, dm16, pack_k_scales(sj, mj), q.reshape(rows, k // 256, 256)
+
+
+def quantize_q4_k(w):
+    """f32 [rows][k] -> Q4_K super-blocks, uint8 [rows * (k/256) * 144]."""
+    rows, k, d16, dm16, sc, q = _quantize_kaffine(w, 4)
+    out = np.zeros((rows, k // 256, 144), np.uint8)
+    out[..., 0:2] = d16[..., None].view(np.uint8).reshape(rows, k // 256, 2)
+    out[..., 2:4] = dm16[..., None].view(np.uint8).reshape(rows, k // 256, 2)
+    out[..., 4:16] = sc
+    g = q.reshape(rows, k // 256, 4, 2, 32)     # [p][upper][l]
+    out[..., 16:144] = (g[..., 0, :] | (g[..., 1, :] << 4)).reshape(rows, k // 256, 128)
+    return out.reshape(-1)
+
+
+def quantize_q5_k(w):
+    """f32 [rows][k] -> Q5_K super-blocks, uint8 [rows * (k/256) * 176]."""
+    rows, k, d16, dm16, sc, q = _quantize_kaffine(w, 5)
+    out = np.zeros((rows, k // 256, 176), np.uint8)
+    out[..., 0:2] = d16[..., None].view(np.uint8).reshape(rows, k // 256, 2)
+    out[..., 2:4] = dm16[..., None].view(np.uint8).reshape(rows, k // 256, 2)
+    out[..., 4:16] = sc
+    hb = (q >> 4).reshape(rows, k // 256, 8, 32)  # element 32 b + l -> bit b of qh[l]
+    qh = np.zeros((rows, k // 256, 32), np.uint8)
+    for b in range(8):
+        qh |= (hb[..., b, :] << b).astype(np.uint8)
+    out[..., 16:48] = qh
+    g = (q & 15).reshape(rows, k // 256, 4, 2, 32)
+    out[..., 48:176] = (g[..., 0, :] | (g[..., 1, :] << 4)).reshape(rows, k // 256, 128)
+    return out.reshape(-1)
+
+
+def quantize_q6_k(w):
+    """f32 [rows][k] -> Q6_K super-blocks, uint8 [rows * (k/256) * 210]."""
+    w = np.ascontiguousarray(w, np.float32)
+    rows, k = w.shape
+    if k % 256:
+        raise ValueError("k must be a multiple of 256")
+    sb = w.reshape(rows, k // 256, 16, 16)
+    step = (np.abs(sb).max(axis=3) / np.float32(31)).astype(np.float32)
+    d16 = _fp16_bits(step.max(axis=2) / np.float32(127))
+    d = d16.view(np.float16).astype(np.float32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        sc = np.where(d > 0, np.clip(_round_half_away(step / np.where(d > 0, d, 1)), -128, 127), 0).astype(np.int8)
+        a = (d * sc.astype(np.float32))[..., None]
+        q = np.where(a != 0, np.clip(_round_half_away(sb / np.where(a != 0, a, 1)) + 32, 0, 63), 32)
+    q = q.astype(np.uint8).reshape(rows, k // 256, 2, 4, 32)   # [half][quarter][l]
+    out = np.zeros((rows, k // 256, 210), np.uint8)
+    ql = np.zeros((rows, k // 256, 2, 64), np.uint8)
+    ql[..., 0:32] = (q[..., 0, :] & 15) | ((q[..., 2, :] & 15) << 4)
+    ql[..., 32:64] = (q[..., 1, :] & 15) | ((q[..., 3, :] & 15) << 4)
+    qh = ((q[..., 0, :] >> 4) | ((q[..., 1, :] >> 4) << 2) | ((q[..., 2, :] >> 4) << 4)
+          | ((q[..., 3, :] >> 4) << 6)).astype(np.uint8)
+    out[..., 0:128] = ql.reshape(rows, k // 256, 128)
+    out[..., 128:192] = qh.reshape(rows, k // 256, 64)
+    out[..., 192:208] = sc.view(np.uint8)
+    out[..., 208:210] = d16[..., None].view(np.uint8).reshape(rows, k // 256, 2)
+    return out.reshape(-1)
+
+
+QUANTIZERS = {Q4_0: quantize_q4_0, Q8_0: quantize_q8_0, F16: quantize_f16, Q4_K: quantize_q4_k,
+              Q5_K: quantize_q5_k, Q6_K: quantize_q6_k}
+
+
 def quantize(qtype, w):
-    return quantize_q4_0(w) if qtype == Q4_0 else quantize_q8_0(w)
+    return QUANTIZERS[qtype](w)
 
 
 def quantized_weight(qtype, rows, k, seed=0, workload_id=0, tensor_id=TENSOR_W):
