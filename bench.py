@@ -52,19 +52,27 @@ HIDDEN, INTER = 4096, 12288
 VOCAB = 151936
 LM_UNIQUE_ROWS = 16384  # lm_head weights: this many seeded rows, tiled to VOCAB
 NORM_EPS = 1e-6
-Q4_0, Q8_0 = 0, 1
+Q4_0, Q8_0, F16W, Q4_K, Q5_K, Q6_K = 0, 1, 2, 3, 4, 5
 PLAIN, RESIDUAL, SWIGLU = 0, 1, 2
-BLOCK = {Q4_0: 18, Q8_0: 34}
+BLOCK = {Q4_0: 18, Q8_0: 34, F16W: 64, Q4_K: 144, Q5_K: 176, Q6_K: 210}
+BLOCK_ELEMS = {Q4_0: 32, Q8_0: 32, F16W: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256}
+
+
+def weight_bytes(qtype, rows, k):
+    return rows * (k // BLOCK_ELEMS[qtype]) * BLOCK[qtype]
 
 # Sources whose change invalidates stored counter readings, per kernel family.
 KERNEL_SOURCES = {
     "gemm_f16": ["pf_gemm_f16.hip", "pf_device.h"],
     "gemm_f32": ["pf_gemm_f32.hip", "pf_device.h"],
     "gemv": ["pf_gemv.hip", "pf_device.h"],
+    "xq": ["pf_xq.hip", "pf_device.h"],
 }
 
 
-def kernel_family(T, leg):
+def kernel_family(T, leg, qtype=0):
+    if qtype not in (Q4_0, Q8_0):
+        return "xq"
     return "gemv" if T <= 8 else ("gemm_f16" if leg == 1 else "gemm_f32")
 
 
@@ -111,6 +119,19 @@ def workloads():
         "gemv_q4_0_12288x4096_T4": (4, 0, [("gemv_q4_0", Q4_0, INTER, HIDDEN, PLAIN, "x", "out")], 1),
         "gemv_q4_0_12288x4096_T8": (8, 0, [("gemv_q4_0", Q4_0, INTER, HIDDEN, PLAIN, "x", "out")], 1),
         "gemv_q8_0_4096x12288_T8": (8, 0, [("gemv_q8_0", Q8_0, HIDDEN, INTER, PLAIN, "x12288", "out")], 1),
+        # the further weight types (the same projections with F16 / Q4_K / Q6_K weights)
+        "gate_up_q4_k_T512_f16": (512, 1, [("gate_up_swiglu_q4_k", Q4_K, INTER, HIDDEN, SWIGLU, "x", "act")], 1),
+        "gate_up_q4_k_T512_f32": (512, 0, [("gate_up_swiglu_q4_k", Q4_K, INTER, HIDDEN, SWIGLU, "x", "act")], 1),
+        "gate_up_f16w_T512_f16": (512, 1, [("gate_up_swiglu_f16w", F16W, INTER, HIDDEN, SWIGLU, "x", "act")], 1),
+        "down_q6_k_T512_f16": (512, 1, [("down_residual_q6_k", Q6_K, HIDDEN, INTER, RESIDUAL, "act", "res")], 1),
+        "gemv_q4_k_12288x4096_T1": (1, 0, [("gemv_q4_k", Q4_K, INTER, HIDDEN, PLAIN, "x", "out")], 1),
+        "gemv_q5_k_12288x4096_T1": (1, 0, [("gemv_q5_k", Q5_K, INTER, HIDDEN, PLAIN, "x", "out")], 1),
+        "gemv_q6_k_4096x12288_T1": (1, 0, [("gemv_q6_k", Q6_K, HIDDEN, INTER, PLAIN, "x12288", "out")], 1),
+        "gemv_f16w_4096x12288_T1": (1, 0, [("gemv_f16w", F16W, HIDDEN, INTER, PLAIN, "x12288", "out")], 1),
+        # the plain-read floor: one launch that only streams the same weight bytes as the
+        # T = 1 GEMV of that shape (include/pf_probe.h)
+        "read_floor_q4_0_12288x4096": (1, 0, [("read_floor_q4_0", Q4_0, INTER, HIDDEN, PLAIN, "x", "out")], 1),
+        "read_floor_q8_0_4096x12288": (1, 0, [("read_floor_q8_0", Q8_0, HIDDEN, INTER, PLAIN, "x12288", "out")], 1),
         # lm_head GEMV on one row plus the greedy token (pf_lm_head_argmax); the pages
         # give no vocabulary size: 151936 rows stand in for it
         "lm_head_q8_0_151936x4096_T1": (1, 0, [("lm_head_q8_0", Q8_0, VOCAB, HIDDEN, PLAIN, "x", "logits")], 1),
@@ -129,7 +150,7 @@ def op_flops(op, T):
 def op_bytes(op, T):
     """Algorithmic HBM bytes of one launch: weight blocks once, X read, Y written
     (and read again for RESIDUAL)."""
-    w = op_rows(op) * (op[3] // 32) * BLOCK[op[1]]
+    w = weight_bytes(op[1], op_rows(op), op[3])
     x = 4 * T * op[3]
     y = 4 * T * op[2] * (2 if op[4] == RESIDUAL else 1)
     return w + x + y
@@ -472,6 +493,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-workspace", action="store_true",
                     help="call pf_gemm (X rounded inside the GEMM) instead of pf_gemm_ws")
+    ap.add_argument("--single-call", action="store_true",
+                    help="time each op as its one pf_gemm_ws call, not as pf_prepare_x then "
+                         "pf_gemm_prepared")
     ap.add_argument("--rotate-mb", type=float, default=640.0,
                     help="minimum total bytes of rotated weight copies")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -557,6 +581,7 @@ def main():
         "norm_w": torch.from_numpy(inputs["norm_w"]).cuda(),
         "logits": torch.empty((VOCAB,), dtype=torch.float32, device="cuda"),
         "token": torch.zeros((1,), dtype=torch.int32, device="cuda"),
+        "sink": torch.zeros((int(pf.load().pf_probe_read_sink_words()),), dtype=torch.int32, device="cuda"),
     }
     stream = torch.cuda.current_stream()
     use_ws = not args.no_workspace
@@ -576,6 +601,10 @@ def main():
             label, qtype, n, k, epi, src, dst = op
             Y = bufs[dst] if dst != "out" else bufs["out"].view(-1)[: T * n].view(T, n)
             w, x, y = P(dev_w[wset][label].data_ptr()), P(bufs[src].data_ptr()), P(Y.data_ptr())
+            if label.startswith("read_floor_"):
+                nb = weight_bytes(qtype, op_rows(op), k)
+                calls[(op[0], wset)] = [(lib.pf_probe_read, (w, nb, P(bufs["sink"].data_ptr()), hstream))]
+                continue
             if label.startswith("lm_head_"):
                 pf.lm_head_argmax(qtype, dev_w[wset][label], n, k, bufs[src][0], bufs["logits"], bufs["token"])
                 calls[(op[0], wset)] = [(lib.pf_lm_head_argmax, (
@@ -593,7 +622,8 @@ def main():
             # the checks the binding makes, once
             pf.gemm_ws(qtype, dev_w[wset][label], n, k, bufs[src], Y, epi, leg, workspace) if use_ws \
                 else pf.gemm(qtype, dev_w[wset][label], n, k, bufs[src], Y, epi, leg)
-            if use_ws and leg == 1 and pf.select_path(qtype, n, k, T, epi, leg) == pf.PF_PATH_GEMM:
+            if use_ws and leg == 1 and qtype in (Q4_0, Q8_0) and not args.single_call and \
+                    pf.select_path(qtype, n, k, T, epi, leg) == pf.PF_PATH_GEMM:
                 # the same kernels as pf_gemm_ws in two calls, so that the GEMM's own
                 # launch can be timed: X rounded to fp16 into the workspace, then the GEMM
                 ws, wsb = P(workspace.data_ptr()), workspace.numel()
@@ -689,10 +719,10 @@ def main():
     dom = int(np.argmax(kern_ms[:step_ops]))
     dop = step[dom]
     nparts_dom = len(calls[(dop[0], 0)])
-    family = kernel_family(T, leg)
+    family = kernel_family(T, leg, dop[1])
     # the bound is whichever takes longer at peak: streaming the weights once from HBM,
     # or the op's matrix-core flops (the GEMV, and the GEMM on short chunks, are HBM-bound)
-    wbytes = op_rows(dop) * (dop[3] // 32) * BLOCK[dop[1]]
+    wbytes = weight_bytes(dop[1], op_rows(dop), dop[3])
     mfma_peak = PEAK["fp16_mfma_tflops"] if leg == 1 else PEAK["fp32_mfma_tflops"]
     hbm_bound = wbytes / (PEAK["hbm_gbs"] * 1e9) > op_flops(dop, T) / (mfma_peak * 1e12)
     traffic = load_traffic(args.workload, dop[0], family, nparts_dom > 1)
@@ -715,10 +745,15 @@ def main():
     roofline["counters"] = load_counters(args.workload, dop[0], family)
 
     value = step_flops / (ms_per_step * 1e-3) / 1e12
+    unit = "TFLOP/s"
+    if all(op[0].startswith("read_floor_") for op in step):
+        # a plain read moves bytes, not FLOPs: the value is the weight bytes per second
+        value = sum(weight_bytes(op[1], op_rows(op), op[3]) for op in step) / (ms_per_step * 1e-3) / 1e9
+        unit = "GB/s"
     out = {
         "metric": METRIC,
         "value": value,
-        "unit": "TFLOP/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -746,7 +781,7 @@ def main():
     }
     if chain is not None:
         out["ffn_chain"] = chain
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not any(op[0].startswith("read_floor_") for op in step):
         out["cpu_baseline"] = cpu_baseline(T, step, inputs)
         log("cpu baseline done")
     print(json.dumps(out), flush=True)

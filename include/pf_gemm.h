@@ -21,12 +21,29 @@
  *    the weight upload in `try_cuda_prefill_q_std` (gate rows, then up rows, in one
  *    buffer), and `try_cuda_prefill_q_std` (an empty batch is a no-op).
  *
- * Block formats (GGUF, 32 weights per block, rows stored block after block):
- *  - Q4_0, 18 bytes: fp16 scale d (little-endian, bytes 0-1), 16 bytes qs. Weight
- *    j < 16 is the low nibble of qs[j], weight j >= 16 the high nibble of
- *    qs[j-16]; value d * (q - 8).
- *  - Q8_0, 34 bytes: fp16 scale d, then 32 int8 q; value d * q.
- *  Block b of weight row r starts at byte (r * (k/32) + b) * block_bytes.
+ * Block formats (GGUF, rows stored block after block):
+ *  - Q4_0, 18 bytes per 32 weights: fp16 scale d (little-endian, bytes 0-1), 16
+ *    bytes qs. Weight j < 16 is the low nibble of qs[j], weight j >= 16 the high
+ *    nibble of qs[j-16]; value d * (q - 8).
+ *  - Q8_0, 34 bytes per 32 weights: fp16 scale d, then 32 int8 q; value d * q.
+ *  The further types the page "aprender-serve 0.70.2 -
+ *  src/cuda/executor/gdn_prefill_ops.rs" dequantizes (`qwen35_dequant_f32`; the f16
+ *  leg's weight is that f32 value rounded to binary16, `qwen35_fp16_weight`). The
+ *  pages print no layout; these are GGUF's:
+ *  - F16, 64 bytes per 32 weights: little-endian binary16.
+ *  - Q4_K, 144 bytes per 256: fp16 d, fp16 dmin, 12 bytes of 6-bit sub-block scales
+ *    s_j and mins m_j (j = e / 32; j < 4: low 6 bits of bytes j and j+4; j >= 4: the
+ *    nibbles of byte j+4 and the top 2 bits of bytes j-4 and j), 128 bytes of
+ *    nibbles (element e: qs[32 (e/64) + e%32], low nibble if e%64 < 32 else high);
+ *    value (d s_j) q - dmin m_j.
+ *  - Q5_K, 176 bytes per 256: as Q4_K with 32 bytes qh before the nibbles; bit j of
+ *    qh[l] adds 16 to element 32 j + l.
+ *  - Q6_K, 210 bytes per 256: ql[128], qh[64], 16 int8 scales, fp16 d; element e (h
+ *    = e/128, c = e%128/32, l = e%32) takes the low (c < 2) or high nibble of ql[64h
+ *    + l + 32 (c%2)] and bits 2c, 2c+1 of qh[32h + l]; value (d sc[8h + l/16 + 2c]) *
+ *    (q - 32).
+ *  Block b of weight row r starts at byte (r * (k/E) + b) * block_bytes, E = 32 or
+ *  256 weights per block.
  *
  * Memory and ownership: every pointer is a device pointer (HBM) owned by the
  * caller. The library allocates nothing, frees nothing and keeps no pointer after
@@ -47,8 +64,9 @@
 extern "C" {
 #endif
 
-/* Block types. */
-enum { PF_Q4_0 = 0, PF_Q8_0 = 1 };
+/* Block types. F16 .. Q6_K run their own kernels on both legs and need no workspace
+ * on any path; pf_prepare_x and pf_gemm_prepared take Q4_0 and Q8_0 only. */
+enum { PF_Q4_0 = 0, PF_Q8_0 = 1, PF_F16 = 2, PF_Q4_K = 3, PF_Q5_K = 4, PF_Q6_K = 5 };
 
 /* Epilogues.
  *  PF_PLAIN          Y = X . W_hat^T                      (W has n rows; Y overwritten)
@@ -70,10 +88,11 @@ enum { PF_PLAIN = 0, PF_RESIDUAL = 1, PF_GATE_UP_SWIGLU = 2 };
 enum { PF_LEG_F32 = 0, PF_LEG_F16 = 1 };
 
 /* Kernel family. PF_PATH_AUTO picks the GEMV for 1 <= T <= PF_GEMV_MAX_T and the
- * tiled matrix-core GEMM otherwise, except that the f16 leg takes the GEMM from T = 3
- * for PLAIN and RESIDUAL and from T = 5 for SwiGLU (faster there: its K split spreads
- * the weight stream over every CU). The other two force a family (tests compare
- * them); PF_PATH_GEMV requires T <= PF_GEMV_MAX_T. */
+ * tiled matrix-core GEMM otherwise, except that for Q4_0 and Q8_0 the f16 leg takes
+ * the GEMM from T = 3 for PLAIN and RESIDUAL and from T = 5 for SwiGLU (faster there
+ * through a workspace, whose K split spreads the weight stream over every CU). The
+ * other two force a family (tests compare them); PF_PATH_GEMV requires T <=
+ * PF_GEMV_MAX_T. */
 enum { PF_PATH_AUTO = 0, PF_PATH_GEMM = 1, PF_PATH_GEMV = 2 };
 #define PF_GEMV_MAX_T 8
 
@@ -81,12 +100,13 @@ enum { PF_PATH_AUTO = 0, PF_PATH_GEMM = 1, PF_PATH_GEMV = 2 };
 enum {
     PF_OK = 0,
     PF_E_NULL = 1,     /* a required pointer is NULL */
-    PF_E_QTYPE = 2,    /* unknown block type */
+    PF_E_QTYPE = 2,    /* unknown block type (or one the call does not take) */
     PF_E_EPILOGUE = 3, /* unknown epilogue */
     PF_E_LEG = 4,      /* unknown leg */
-    PF_E_SHAPE = 5,    /* n < 1, T < 0, k < 256 or k % 256 != 0 (pf_gemm), k % 32 != 0
-                          (pf_dequant_*), or an element count of X, Y or W_hat
-                          reaching 2^31 */
+    PF_E_SHAPE = 5,    /* n < 1, T < 0, k < 256 or k % 256 != 0 (pf_gemm), k not a
+                          whole number of blocks (pf_dequant_*, pf_weight_bytes), or
+                          an element count of X, Y or W_hat, or W's bytes, reaching
+                          2^31 */
     PF_E_ALIGN = 6,    /* W, X, Y or out not 16-byte aligned */
     PF_E_ALIAS = 7,    /* Y (or out) overlaps W or X */
     PF_E_LAUNCH = 8,   /* the HIP runtime refused the launch */
@@ -258,8 +278,9 @@ int pf_gemm_prepared(int qtype, const void *W_blocks, int64_t n, int64_t k, int6
  * (pointers are not checked). Host-only; touches no GPU state. */
 int pf_select_path(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int leg);
 
-/* Bit-exact block decode into out[rows][k] (device, f32), out = d * (q - 8) or d * q.
- * Same block layout as pf_gemm; k a multiple of 32. This is the f32 leg's weight. */
+/* Bit-exact block decode into out[rows][k] (device, f32): d * (q - 8), d * q, or the
+ * value each further type defines (see the block formats above). Same block layout
+ * as pf_gemm; k a whole number of blocks. This is the f32 leg's weight. */
 int pf_dequant_f32(int qtype, const void *W_blocks, int64_t rows, int64_t k, float *out,
                    void *stream);
 
@@ -268,9 +289,9 @@ int pf_dequant_f32(int qtype, const void *W_blocks, int64_t rows, int64_t k, flo
 int pf_dequant_f16(int qtype, const void *W_blocks, int64_t rows, int64_t k, uint16_t *out,
                    void *stream);
 
-/* Bytes of a weight of `rows` rows and reduction length k: rows * (k/32) *
- * block_bytes (18 for Q4_0, 34 for Q8_0). Returns -PF_E_QTYPE or -PF_E_SHAPE (k not
- * a multiple of 32, rows < 0) on bad arguments. Host-only. */
+/* Bytes of a weight of `rows` rows and reduction length k: rows * (k/E) *
+ * block_bytes (see the block formats above). Returns -PF_E_QTYPE or -PF_E_SHAPE (k
+ * not a multiple of E, rows < 0) on bad arguments. Host-only. */
 int64_t pf_weight_bytes(int qtype, int64_t rows, int64_t k);
 
 /* Static, NUL-terminated name of a status code ("unknown status" otherwise). */

@@ -17,11 +17,23 @@ namespace {
 
 constexpr int64_t kMax31 = (int64_t(1) << 31) - 1;
 
+// Bytes and weights of one block of each type (the K types' super-blocks hold 256).
 int block_bytes(int qtype) {
-    if (qtype == PF_Q4_0) return 18;
-    if (qtype == PF_Q8_0) return 34;
-    return -1;
+    switch (qtype) {
+    case PF_Q4_0: return 18;
+    case PF_Q8_0: return 34;
+    case PF_F16: return 64;
+    case PF_Q4_K: return 144;
+    case PF_Q5_K: return 176;
+    case PF_Q6_K: return 210;
+    default: return -1;
+    }
 }
+int block_elems(int qtype) { return (qtype == PF_Q4_K || qtype == PF_Q5_K || qtype == PF_Q6_K) ? 256 : 32; }
+// The further types (F16, Q4_K, Q5_K, Q6_K) run their own kernels (pf_xq.hip), with no
+// workspace on any path.
+bool is_xq(int qtype) { return qtype >= PF_F16 && qtype <= PF_Q6_K; }
+int64_t w_bytes_of(int qtype, int64_t rows, int64_t k) { return rows * (k / block_elems(qtype)) * block_bytes(qtype); }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -40,7 +52,7 @@ int check_sizes(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int le
     const int64_t rows = epilogue == PF_GATE_UP_SWIGLU ? 2 * n : n;
     // Element counts stay below 2^31 so that 32-bit index arithmetic is exact.
     if (k > kMax31 / rows || (T > 0 && (k > kMax31 / T || n > kMax31 / T))) return PF_E_SHAPE;
-    if ((rows * (k / 32)) > kMax31 / block_bytes(qtype)) return PF_E_SHAPE;
+    if ((rows * (k / block_elems(qtype))) > kMax31 / block_bytes(qtype)) return PF_E_SHAPE;
     *n_w = rows;
     return PF_OK;
 }
@@ -51,18 +63,21 @@ int check_sizes(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int le
 // weights faster than the GEMV (whose time grows with each pair of rows). SwiGLU
 // splits K only through a workspace, so its crossing comes later (gate/up 2 x 12288 x
 // 4096: GEMV 36 us at 4 rows and 54 at 6, GEMM 43 unsplit or 28 through a workspace).
-int auto_path(int64_t T, int epilogue, int leg) {
+// The further types take the GEMV up to PF_GEMV_MAX_T rows on both legs.
+int auto_path(int qtype, int64_t T, int epilogue, int leg) {
     if (T > PF_GEMV_MAX_T) return PF_PATH_GEMM;
-    if (leg == PF_LEG_F16 && T >= (epilogue == PF_GATE_UP_SWIGLU ? 5 : 3)) return PF_PATH_GEMM;
+    if (!is_xq(qtype) && leg == PF_LEG_F16 && T >= (epilogue == PF_GATE_UP_SWIGLU ? 5 : 3))
+        return PF_PATH_GEMM;
     return PF_PATH_GEMV;
 }
 
 // Bytes of workspace the f16 leg's GEMM takes (X as binary16, T rounded up to a
 // multiple of 32 for the fragment-ordered copy, plus the partial sums of a K split),
 // else 0.
-int64_t ws_need(int64_t n, int64_t k, int64_t T, int epilogue, int leg, int use) {
-    return (use == PF_PATH_GEMM && leg == PF_LEG_F16) ? pf::f16_ws_bytes((int)T, (int)n, (int)k, epilogue)
-                                                      : 0;
+int64_t ws_need(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int leg, int use) {
+    return (use == PF_PATH_GEMM && leg == PF_LEG_F16 && !is_xq(qtype))
+               ? pf::f16_ws_bytes((int)T, (int)n, (int)k, epilogue)
+               : 0;
 }
 
 // Where a call's workspace comes from: none (the kernels that need none, or the
@@ -81,11 +96,11 @@ int gemm_impl(int qtype, const void *W, int64_t n, int64_t k, const float *X, in
     if (T == 0) return PF_OK;  // an empty batch is a no-op
     if (!W || !X || !Y) return PF_E_NULL;
     if (!aligned16(W) || !aligned16(X) || !aligned16(Y)) return PF_E_ALIGN;
-    const int64_t w_bytes = n_w * (k / 32) * block_bytes(qtype);
+    const int64_t w_bytes = w_bytes_of(qtype, n_w, k);
     const int64_t x_bytes = T * k * 4, y_bytes = ((T - 1) * ldy + n) * 4;  // Y's rows and gaps
     if (overlap(Y, y_bytes, X, x_bytes) || overlap(Y, y_bytes, W, w_bytes)) return PF_E_ALIAS;
-    const int use = path == PF_PATH_AUTO ? auto_path(T, epilogue, leg) : path;
-    const int64_t need = ws_mode != WS_NONE ? ws_need(n, k, T, epilogue, leg, use) : 0;
+    const int use = path == PF_PATH_AUTO ? auto_path(qtype, T, epilogue, leg) : path;
+    const int64_t need = ws_mode != WS_NONE ? ws_need(qtype, n, k, T, epilogue, leg, use) : 0;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (need > 0 && ws_mode == WS_STATIC) {
         // every check is done: the first HIP call of the request
@@ -110,7 +125,9 @@ int gemm_impl(int qtype, const void *W, int64_t n, int64_t k, const float *X, in
     a.k = (int)k;
     a.T = (int)T;
     hipError_t err;
-    if (use == PF_PATH_GEMV)
+    if (is_xq(qtype))
+        err = use == PF_PATH_GEMV ? pf::launch_xq_gemv(a, s) : pf::launch_xq_gemm(a, leg == PF_LEG_F16, s);
+    else if (use == PF_PATH_GEMV)
         err = pf::launch_gemv(a, s);
     else if (leg == PF_LEG_F32)
         err = pf::launch_gemm_f32(a, s);
@@ -126,9 +143,9 @@ int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
 // Workspace of the RMSNorm entry point: inv[T] (rounded up to 256 bytes), then the
 // f16 GEMM's own workspace (X rounded to binary16 with the norm applied, and any
 // split-K partial sums), or, for the kernels that read f32 X, Xn [T][k] f32.
-int64_t rms_ws_need(int64_t n, int64_t k, int64_t T, int epilogue, int leg, int use) {
+int64_t rms_ws_need(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int leg, int use) {
     if (T == 0) return 0;
-    const int64_t tail = (use == PF_PATH_GEMM && leg == PF_LEG_F16)
+    const int64_t tail = (use == PF_PATH_GEMM && leg == PF_LEG_F16 && !is_xq(qtype))
                              ? pf::f16_ws_bytes((int)T, (int)n, (int)k, epilogue)
                              : T * k * 4;
     return round256(T * 4) + tail;
@@ -145,13 +162,13 @@ int rms_impl(int qtype, const void *W, int64_t n, int64_t k, const float *X, int
     if (T == 0) return PF_OK;  // an empty batch is a no-op
     if (!W || !X || !Y || !norm_w) return PF_E_NULL;
     if (!aligned16(W) || !aligned16(X) || !aligned16(Y) || !aligned16(norm_w)) return PF_E_ALIGN;
-    const int64_t w_bytes = n_w * (k / 32) * block_bytes(qtype);
+    const int64_t w_bytes = w_bytes_of(qtype, n_w, k);
     const int64_t x_bytes = T * k * 4, y_bytes = ((T - 1) * ldy + n) * 4, nw_bytes = k * 4;
     if (overlap(Y, y_bytes, X, x_bytes) || overlap(Y, y_bytes, W, w_bytes) ||
         overlap(Y, y_bytes, norm_w, nw_bytes))
         return PF_E_ALIAS;
-    const int use = auto_path(T, epilogue, leg);
-    const int64_t need = rms_ws_need(n, k, T, epilogue, leg, use);
+    const int use = auto_path(qtype, T, epilogue, leg);
+    const int64_t need = rms_ws_need(qtype, n, k, T, epilogue, leg, use);
     if (!ws || ws_bytes < need || !aligned16(ws)) return PF_E_WORKSPACE;
     if (overlap(ws, need, W, w_bytes) || overlap(ws, need, X, x_bytes) || overlap(ws, need, Y, y_bytes) ||
         overlap(ws, need, norm_w, nw_bytes))
@@ -172,7 +189,7 @@ int rms_impl(int qtype, const void *W, int64_t n, int64_t k, const float *X, int
     uint8_t *rest = static_cast<uint8_t *>(ws) + round256(T * 4);
     hipError_t err = pf::launch_rms_inv(X, a.T, a.k, eps, inv, s);
     if (err != hipSuccess) return PF_E_LAUNCH;
-    if (use == PF_PATH_GEMM && leg == PF_LEG_F16) {
+    if (use == PF_PATH_GEMM && leg == PF_LEG_F16 && !is_xq(qtype)) {
         a.norm_inv = inv;
         a.norm_w = norm_w;
         err = pf::launch_gemm_f16_ws(a, rest, s);
@@ -181,18 +198,22 @@ int rms_impl(int qtype, const void *W, int64_t n, int64_t k, const float *X, int
         err = pf::launch_rms_apply(X, inv, norm_w, Xn, a.T, a.k, s);
         if (err != hipSuccess) return PF_E_LAUNCH;
         a.X = Xn;
-        err = use == PF_PATH_GEMV ? pf::launch_gemv(a, s) : pf::launch_gemm_f32(a, s);
+        if (is_xq(qtype))
+            err = use == PF_PATH_GEMV ? pf::launch_xq_gemv(a, s) : pf::launch_xq_gemm(a, leg == PF_LEG_F16, s);
+        else
+            err = use == PF_PATH_GEMV ? pf::launch_gemv(a, s) : pf::launch_gemm_f32(a, s);
     }
     return err == hipSuccess ? PF_OK : PF_E_LAUNCH;
 }
 
 int dequant_check(int qtype, const void *W, int64_t rows, int64_t k, const void *out, int out_elem) {
     if (block_bytes(qtype) < 0) return PF_E_QTYPE;
-    if (rows < 1 || k < 32 || k % 32 != 0) return PF_E_SHAPE;
-    if (k > kMax31 / rows || (rows * (k / 32)) > kMax31 / block_bytes(qtype)) return PF_E_SHAPE;
+    const int be = block_elems(qtype);
+    if (rows < 1 || k < be || k % be != 0) return PF_E_SHAPE;
+    if (k > kMax31 / rows || (rows * (k / be)) > kMax31 / block_bytes(qtype)) return PF_E_SHAPE;
     if (!W || !out) return PF_E_NULL;
     if (!aligned16(W) || !aligned16(out)) return PF_E_ALIGN;
-    if (overlap(out, rows * k * out_elem, W, rows * (k / 32) * block_bytes(qtype))) return PF_E_ALIAS;
+    if (overlap(out, rows * k * out_elem, W, w_bytes_of(qtype, rows, k))) return PF_E_ALIAS;
     return PF_OK;
 }
 
@@ -243,7 +264,7 @@ int pf_lm_head_argmax(int qtype, const void *W_blocks, int64_t n, int64_t k, con
     if (!aligned16(W_blocks) || !aligned16(x) || !aligned16(logits) ||
         (reinterpret_cast<uintptr_t>(token) & 3u) != 0)
         return PF_E_ALIGN;
-    const int64_t w_bytes = n_w * (k / 32) * block_bytes(qtype), x_bytes = k * 4, l_bytes = n * 4;
+    const int64_t w_bytes = w_bytes_of(qtype, n_w, k), x_bytes = k * 4, l_bytes = n * 4;
     if (overlap(logits, l_bytes, W_blocks, w_bytes) || overlap(logits, l_bytes, x, x_bytes) ||
         overlap(token, 4, logits, l_bytes) || overlap(token, 4, W_blocks, w_bytes) ||
         overlap(token, 4, x, x_bytes))
@@ -259,13 +280,13 @@ int pf_lm_head_argmax(int qtype, const void *W_blocks, int64_t n, int64_t k, con
     a.k = (int)k;
     a.T = 1;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    if (pf::launch_gemv(a, s) != hipSuccess) return PF_E_LAUNCH;
+    if ((is_xq(qtype) ? pf::launch_xq_gemv(a, s) : pf::launch_gemv(a, s)) != hipSuccess) return PF_E_LAUNCH;
     return pf::launch_argmax(logits, (int)n, token, s) == hipSuccess ? PF_OK : PF_E_LAUNCH;
 }
 
 int pf_prepare_x(int qtype, int64_t k, const float *X, int64_t T, void *workspace, int64_t workspace_bytes,
                  void *stream) {
-    if (block_bytes(qtype) < 0) return PF_E_QTYPE;
+    if (block_bytes(qtype) < 0 || is_xq(qtype)) return PF_E_QTYPE;
     if (T < 0 || k < 256 || k % 256 != 0 || (T > 0 && k > kMax31 / T)) return PF_E_SHAPE;
     if (T == 0) return PF_OK;
     if (!X) return PF_E_NULL;
@@ -291,15 +312,16 @@ int pf_prepare_x(int qtype, int64_t k, const float *X, int64_t T, void *workspac
 int pf_gemm_prepared(int qtype, const void *W_blocks, int64_t n, int64_t k, int64_t T, float *Y, int64_t ldy,
                      int epilogue, void *workspace, int64_t workspace_bytes, void *stream) {
     int64_t n_w = 0;
+    if (is_xq(qtype)) return PF_E_QTYPE;  // their GEMM reads f32 X: no prepared form
     const int st = check_sizes(qtype, n, k, T, epilogue, PF_LEG_F16, &n_w);
     if (st != PF_OK) return st;
     if (ldy < n || (T > 0 && ldy > kMax31 / T)) return PF_E_SHAPE;
     // where pf_gemm_ws would run the GEMV (which reads f32 X) there is no prepared form
-    if (T > 0 && auto_path(T, epilogue, PF_LEG_F16) != PF_PATH_GEMM) return PF_E_PATH;
+    if (T > 0 && auto_path(qtype, T, epilogue, PF_LEG_F16) != PF_PATH_GEMM) return PF_E_PATH;
     if (T == 0) return PF_OK;
     if (!W_blocks || !Y) return PF_E_NULL;
     if (!aligned16(W_blocks) || !aligned16(Y)) return PF_E_ALIGN;
-    const int64_t w_bytes = n_w * (k / 32) * block_bytes(qtype), y_bytes = ((T - 1) * ldy + n) * 4;
+    const int64_t w_bytes = w_bytes_of(qtype, n_w, k), y_bytes = ((T - 1) * ldy + n) * 4;
     if (overlap(Y, y_bytes, W_blocks, w_bytes)) return PF_E_ALIAS;
     const int64_t need = pf::f16_ws_bytes((int)T, (int)n, (int)k, epilogue);
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PF_E_WORKSPACE;
@@ -324,7 +346,7 @@ int64_t pf_rmsnorm_workspace_bytes(int qtype, int64_t n, int64_t k, int64_t T, i
     int64_t n_w = 0;
     const int st = check_sizes(qtype, n, k, T, epilogue, leg, &n_w);
     if (st != PF_OK) return -st;
-    return rms_ws_need(n, k, T, epilogue, leg, auto_path(T, epilogue, leg));
+    return rms_ws_need(qtype, n, k, T, epilogue, leg, auto_path(qtype, T, epilogue, leg));
 }
 
 int64_t pf_workspace_bytes(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int leg) {
@@ -332,7 +354,7 @@ int64_t pf_workspace_bytes(int qtype, int64_t n, int64_t k, int64_t T, int epilo
     const int st = check_sizes(qtype, n, k, T, epilogue, leg, &n_w);
     if (st != PF_OK) return -st;
     if (T == 0) return 0;
-    return ws_need(n, k, T, epilogue, leg, auto_path(T, epilogue, leg));
+    return ws_need(qtype, n, k, T, epilogue, leg, auto_path(qtype, T, epilogue, leg));
 }
 
 int pf_gemm_path(int qtype, const void *W_blocks, int64_t n, int64_t k, const float *X,
@@ -345,16 +367,18 @@ int pf_select_path(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int
     const int st = check_sizes(qtype, n, k, T, epilogue, leg, &n_w);
     if (st != PF_OK) return -st;
     if (T == 0) return 0;
-    return auto_path(T, epilogue, leg);
+    return auto_path(qtype, T, epilogue, leg);
 }
 
 int pf_dequant_f32(int qtype, const void *W_blocks, int64_t rows, int64_t k, float *out,
                    void *stream) {
     const int st = dequant_check(qtype, W_blocks, rows, k, out, 4);
     if (st != PF_OK) return st;
-    const hipError_t err = pf::launch_dequant_f32(qtype, static_cast<const uint8_t *>(W_blocks),
-                                                  (int)rows, (int)k, out,
-                                                  static_cast<hipStream_t>(stream));
+    const hipError_t err =
+        is_xq(qtype) ? pf::launch_xq_dequant(qtype, static_cast<const uint8_t *>(W_blocks), (int)rows, (int)k, out,
+                                             false, static_cast<hipStream_t>(stream))
+                     : pf::launch_dequant_f32(qtype, static_cast<const uint8_t *>(W_blocks), (int)rows, (int)k, out,
+                                              static_cast<hipStream_t>(stream));
     return err == hipSuccess ? PF_OK : PF_E_LAUNCH;
 }
 
@@ -362,17 +386,19 @@ int pf_dequant_f16(int qtype, const void *W_blocks, int64_t rows, int64_t k, uin
                    void *stream) {
     const int st = dequant_check(qtype, W_blocks, rows, k, out, 2);
     if (st != PF_OK) return st;
-    const hipError_t err = pf::launch_dequant_f16(qtype, static_cast<const uint8_t *>(W_blocks),
-                                                  (int)rows, (int)k, out,
-                                                  static_cast<hipStream_t>(stream));
+    const hipError_t err =
+        is_xq(qtype) ? pf::launch_xq_dequant(qtype, static_cast<const uint8_t *>(W_blocks), (int)rows, (int)k, out,
+                                             true, static_cast<hipStream_t>(stream))
+                     : pf::launch_dequant_f16(qtype, static_cast<const uint8_t *>(W_blocks), (int)rows, (int)k, out,
+                                              static_cast<hipStream_t>(stream));
     return err == hipSuccess ? PF_OK : PF_E_LAUNCH;
 }
 
 int64_t pf_weight_bytes(int qtype, int64_t rows, int64_t k) {
     const int bb = block_bytes(qtype);
     if (bb < 0) return -PF_E_QTYPE;
-    if (rows < 0 || k < 0 || k % 32 != 0) return -PF_E_SHAPE;
-    return rows * (k / 32) * bb;
+    if (rows < 0 || k < 0 || k % block_elems(qtype) != 0) return -PF_E_SHAPE;
+    return w_bytes_of(qtype, rows, k);
 }
 
 const char *pf_strerror(int status) {

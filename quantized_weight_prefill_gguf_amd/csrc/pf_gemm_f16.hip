@@ -564,7 +564,7 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
 // nibble half of another, or three Q8_0 words; 512 x 96 tiles give each thread
 // one or two units of 4 weights. Within each half wave (32 lanes) the stores cover
 // 256 contiguous bytes of one fragment half, so they are free of bank conflicts.
-template <int QT, int EPI, bool SPLIT, int MT = 256, int AD = 2, bool TALL = false>
+template <int QT, int EPI, bool SPLIT, int MT = 256, int AD = 2>
 __global__ __launch_bounds__(512)
 void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ Xf,
                           float *__restrict__ Y, float *__restrict__ Ps, long pstride, int n,
@@ -572,12 +572,9 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
     using CT = ChunkTraits<QT>;
     static_assert(MT == 256 || MT == 512, "tile: 256 x 192 or 512 x 96");
     constexpr int NW = MT == 256 ? 192 : 96;        // weight rows per tile
-    static_assert(!TALL || MT == 256, "the tall wave layout is for 256 x 192 tiles");
-    // TALL: the 8 waves stacked along the token rows, each 32 x 192 (1 x 6 MFMA
-    // tiles), so that every A row is loaded once per workgroup.
-    constexpr int WN = TALL ? 1 : NW / 96;          // waves across the weight rows
+    constexpr int WN = NW / 96;                     // waves across the weight rows (2 or 1)
     constexpr int BB = CT::BB;                      // 18 / 34
-    constexpr int IT = TALL ? 1 : 2, JT = TALL ? 6 : 3;  // per wave: 64 x 96 or 32 x 192
+    constexpr int IT = 2, JT = 3;                   // per wave: 64 rows x 96 weight rows
     constexpr int U4 = CT::U4;                      // 9 / 17
     constexpr int WROW = CT::ROW;                   // 144 / 272
     constexpr int WBUF = NW * WROW;                 // raw chunk buffer
@@ -1344,17 +1341,15 @@ __global__ __launch_bounds__(256) void x_to_frag_kernel(const float *__restrict_
 #define PF_COOP_T512 512
 #endif
 constexpr int COOP_T512 = PF_COOP_T512;  // smallest T that takes the 512 x 96 tiles
-#ifndef PF_COOP_TALL
-#define PF_COOP_TALL 0
-#endif
-constexpr bool COOP_TALL = PF_COOP_TALL != 0;  // 256 x 192 tiles: waves 8 x 1 (else 4 x 2)
 
 // Split count of the cooperative-decode kernel. PLAIN / RESIDUAL split K when the
 // tiles alone would leave CUs idle (any split count; the chunk ranges of the splits
-// differ by at most one chunk), but every split keeps at least 5 chunks: a split's
+// differ by at most one chunk), but every split keeps at least 4 chunks: a split's
 // prologue and the partial-sum traffic cost more than the parallelism buys below
-// that (measured: k = 4096 at n = 4096 runs 10 % faster with 3 splits than with 5;
-// k = 12288 wants 5). SwiGLU never splits.
+// that. Measured (GEMM kernel, T = 512): Q4_0 4096 x 4096 takes 38.7 us with at
+// least 5 chunks per split (3 splits), 34.0 with 4 (4 splits), 45.1 with 8; the
+// Q8_0 down projection (k = 12288, 5 splits under any of these) does not change.
+// SwiGLU never splits.
 static int coop_splits(int T, int n, int k, int epilogue) {
     if (epilogue == EPI_SWIGLU) return 1;
     const int MT = T >= COOP_T512 ? 512 : 256;
@@ -1362,7 +1357,8 @@ static int coop_splits(int T, int n, int k, int epilogue) {
     const int tiles = ((T + MT - 1) / MT) * ((n + NW - 1) / NW);
     if (tiles >= 256) return 1;
     int splits = 256 / tiles;
-    const int by_k = (k / 256) / 5 > 1 ? (k / 256) / 5 : 1;
+    constexpr int MIN_CHUNKS = 4;
+    const int by_k = (k / 256) / MIN_CHUNKS > 1 ? (k / 256) / MIN_CHUNKS : 1;
     if (splits > by_k) splits = by_k;
     if (splits > 16) splits = 16;
     return splits;
@@ -1410,8 +1406,7 @@ hipError_t launch_coop(const GemmArgs &a, uint16_t *xh, hipStream_t s) {
         if constexpr (EPI != EPI_SWIGLU) {
             float *ps = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(xh) + ws_x_bytes(a.T, a.k));
             const long pstride = (long)ws_pstride(a.T, a.n);
-            hipLaunchKernelGGL((gemm_f16_coop_kernel<QT, EPI, true, MT, 2, MT == 256 && COOP_TALL>), dim3(total),
-                               dim3(512), 0, s,
+            hipLaunchKernelGGL((gemm_f16_coop_kernel<QT, EPI, true, MT>), dim3(total), dim3(512), 0, s,
                                a.W, xh, a.Y, ps, pstride, a.n, a.ldy, a.k, a.T, tm, tn, splits);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
@@ -1426,8 +1421,8 @@ hipError_t launch_coop(const GemmArgs &a, uint16_t *xh, hipStream_t s) {
             }
         }
     } else {
-        hipLaunchKernelGGL((gemm_f16_coop_kernel<QT, EPI, false, MT, 2, MT == 256 && COOP_TALL>), dim3(total),
-                           dim3(512), 0, s, a.W, xh, a.Y, nullptr, 0L, a.n, a.ldy, a.k, a.T, tm, tn, splits);
+        hipLaunchKernelGGL((gemm_f16_coop_kernel<QT, EPI, false, MT>), dim3(total), dim3(512), 0, s, a.W,
+                           xh, a.Y, nullptr, 0L, a.n, a.ldy, a.k, a.T, tm, tn, splits);
     }
     return hipGetLastError();
 }

@@ -1,0 +1,563 @@
+// The further weight types of the f32 and f16 legs: F16, Q4_K, Q5_K and Q6_K, the
+// types the page "aprender-serve 0.70.2 - src/cuda/executor/gdn_prefill_ops.rs"
+// dequantizes besides Q8_0 (`qwen35_dequant_f32`: F16 over 32-element groups, the K
+// types over 256-element super-blocks; `qwen35_fp16_weight`: the f16 leg's weight is
+// that f32 value rounded to binary16). The pages print no layout; these are GGUF's:
+//
+//  F16   64 bytes per 32 weights: little-endian binary16 values.
+//  Q4_K  144 bytes per 256: fp16 d, fp16 dmin, 12 bytes of 6-bit scales s_j and mins
+//        m_j (8 sub-blocks of 32), 128 bytes of nibbles. Element e: group p = e / 64,
+//        l = e % 32, low nibble of qs[32p + l] for e % 64 < 32, else its high nibble;
+//        value (d s_j) q - dmin m_j, j = e / 32.
+//  Q5_K  176 bytes: as Q4_K, with 32 bytes qh between the scales and the nibbles; bit
+//        j of qh[l] adds 16 to element 32 j + l.
+//  Q6_K  210 bytes: ql[128], qh[64], 16 int8 scales, fp16 d. Element e: half h = e /
+//        128, quarter c = (e % 128) / 32, l = e % 32; low 4 bits from ql[64h + l + 32
+//        (c % 2)] (low nibble for c < 2, high for c >= 2), top 2 from bits 2c, 2c+1 of
+//        qh[32h + l]; value (d sc[8h + l/16 + 2c]) (q - 32).
+//
+// The decode is exact in f32 as these definitions give it: d s_j, dmin m_j and
+// (d s_j) q are exact, so the Q4_K / Q5_K value has the one rounding of the
+// subtraction (an FMA gives the same bits); Q6_K's d sc is exact and the product with
+// q - 32 rounds once. The f16 leg rounds that f32 value to binary16 (RNE).
+//
+// Kernels (no workspace; nothing splits, one writer per output):
+//  - xq_dequant_kernel: one 16-weight run per thread, f32 or binary16 out.
+//  - xq_gemv_kernel (T <= 8): a wave per output (or gate/up pair), lanes stride over
+//    16-weight runs, f32 FMAs, a butterfly over the lanes.
+//  - xq_gemm_kernel: 64 token rows x 128 weight rows per workgroup of 4 waves; per
+//    32-k step the workgroup decodes its 128 x 32 weights into LDS (binary16 or f32
+//    as the leg), stages X likewise, and each wave runs 32 x 64 outputs on the
+//    matrix cores (v_mfma_f32_32x32x16_f16, or v_mfma_f32_32x32x2f32 on the f32 leg).
+//    The accumulators go through LDS to the epilogue, so each store is a whole row.
+#include <type_traits>
+
+#include "pf_device.h"
+#include "pf_internal.h"
+
+namespace pf {
+
+namespace {
+
+template <int QT> struct XqTraits;
+template <> struct XqTraits<XQ_F16> {
+    static constexpr int ELEMS = 32, BYTES = 64;
+};
+template <> struct XqTraits<XQ_Q4_K> {
+    static constexpr int ELEMS = 256, BYTES = 144;
+};
+template <> struct XqTraits<XQ_Q5_K> {
+    static constexpr int ELEMS = 256, BYTES = 176;
+};
+template <> struct XqTraits<XQ_Q6_K> {
+    static constexpr int ELEMS = 256, BYTES = 210;
+};
+
+__device__ __forceinline__ uint32_t byte_of(const u4_t &v, int i) {
+    return (v[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+}
+
+// The 6-bit scale and min of sub-block j (0..7) from the 12 scale bytes held in the
+// words w1..w3 of a Q4_K / Q5_K header (header bytes 4..15).
+__device__ __forceinline__ void k_scale_min(const u4_t &hdr, int j, uint32_t &s, uint32_t &m) {
+    auto sb = [&](int i) { return byte_of(hdr, 4 + i); };  // scale byte i (0..11)
+    if (j < 4) {
+        s = sb(j) & 63u;
+        m = sb(j + 4) & 63u;
+    } else {
+        s = (sb(j + 4) & 15u) | ((sb(j - 4) >> 6) << 4);
+        m = (sb(j + 4) >> 4) | ((sb(j) >> 6) << 4);
+    }
+}
+
+// The bytes that weights e0 .. e0 + 15 (e0 % 16 == 0) of a block decode from, loaded
+// by load_raw16 and turned into exact f32 by decode_raw16, so that a caller can keep
+// the loads in flight across other work.
+template <int QT> struct Raw16;
+template <> struct Raw16<XQ_F16> {
+    u4_t a, b;             // the 16 binary16 values
+};
+template <> struct Raw16<XQ_Q4_K> {
+    u4_t hdr, qs;          // d, dmin and the 12 scale bytes; the 16 code bytes
+};
+template <> struct Raw16<XQ_Q5_K> {
+    u4_t hdr, qs, qh;      // and the 16 qh bytes of the same l
+};
+template <> struct Raw16<XQ_Q6_K> {
+    uint32_t ql[8], qh[8];  // halfwords of ql and qh (210-byte blocks are 2-byte aligned)
+    uint32_t sc, d;        // the halfword holding the scale byte; d
+};
+
+template <int QT>
+__device__ __forceinline__ void load_raw16(const uint8_t *__restrict__ blk, int e0, Raw16<QT> &r) {
+    if constexpr (QT == XQ_F16) {
+        r.a = *reinterpret_cast<const u4_t *>(blk + 2 * e0);
+        r.b = *reinterpret_cast<const u4_t *>(blk + 2 * e0 + 16);
+    } else if constexpr (QT == XQ_Q4_K || QT == XQ_Q5_K) {
+        // 144 and 176 are multiples of 16, and so is every offset read here: the
+        // block's rows start 16-byte aligned (k % 256 == 0, W 16-byte aligned).
+        const int p = e0 >> 6, l0 = e0 & 31;
+        constexpr int QS = QT == XQ_Q5_K ? 48 : 16;
+        r.hdr = *reinterpret_cast<const u4_t *>(blk);
+        r.qs = *reinterpret_cast<const u4_t *>(blk + QS + 32 * p + l0);
+        if constexpr (QT == XQ_Q5_K) r.qh = *reinterpret_cast<const u4_t *>(blk + 16 + l0);
+    } else {
+        const int h = e0 >> 7, c = (e0 & 127) >> 5, l0 = e0 & 31;
+        const uint16_t *ql = reinterpret_cast<const uint16_t *>(blk + 64 * h + l0 + 32 * (c & 1));
+        const uint16_t *qh = reinterpret_cast<const uint16_t *>(blk + 128 + 32 * h + l0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            r.ql[i] = ql[i];
+            r.qh[i] = qh[i];
+        }
+        const int si = 192 + 8 * h + (l0 >> 4) + 2 * c;
+        r.sc = *reinterpret_cast<const uint16_t *>(blk + (si & ~1));
+        r.d = *reinterpret_cast<const uint16_t *>(blk + 208);
+    }
+}
+
+// Weights e0 .. e0 + 15 from their bytes, exact f32. Each value is then made opaque
+// to the optimizer: the f16 leg's weight is this f32 value rounded to binary16, and
+// without that the compiler fuses the last multiply-add with the conversion
+// (v_fma_mix*_f16: one rounding straight to binary16), which differs from rounding
+// the f32 value where the two roundings meet a tie.
+template <int QT>
+__device__ __forceinline__ void decode_raw16(const Raw16<QT> &r, int e0, float (&w)[16]) {
+    if constexpr (QT == XQ_F16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            w[2 * i] = fp16_bits_to_f32(r.a[i] & 0xFFFFu);
+            w[2 * i + 1] = fp16_bits_to_f32(r.a[i] >> 16);
+            w[8 + 2 * i] = fp16_bits_to_f32(r.b[i] & 0xFFFFu);
+            w[8 + 2 * i + 1] = fp16_bits_to_f32(r.b[i] >> 16);
+        }
+    } else if constexpr (QT == XQ_Q4_K || QT == XQ_Q5_K) {
+        const int j = e0 >> 5;
+        const bool upper = (j & 1) != 0;
+        uint32_t s, m;
+        k_scale_min(r.hdr, j, s, m);
+        const float a = fp16_bits_to_f32(r.hdr[0] & 0xFFFFu) * (float)s;
+        const float b = fp16_bits_to_f32(r.hdr[0] >> 16) * (float)m;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t byte = byte_of(r.qs, i);
+            uint32_t q = upper ? (byte >> 4) : (byte & 15u);
+            if constexpr (QT == XQ_Q5_K) q += ((byte_of(r.qh, i) >> j) & 1u) << 4;
+            w[i] = a * (float)q - b;
+        }
+    } else {
+        const int h = e0 >> 7, c = (e0 & 127) >> 5, l0 = e0 & 31;
+        const int si = 192 + 8 * h + (l0 >> 4) + 2 * c;
+        const int sc = (int)(int8_t)(uint8_t)(r.sc >> (8 * (si & 1)));
+        const float ds = fp16_bits_to_f32(r.d) * (float)sc;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const uint32_t lb = (r.ql[i] >> (8 * b)) & 0xFFu, hb = (r.qh[i] >> (8 * b)) & 0xFFu;
+                const uint32_t lo = c < 2 ? (lb & 15u) : (lb >> 4);
+                const int q = (int)(lo | (((hb >> (2 * c)) & 3u) << 4));
+                w[2 * i + b] = ds * (float)(q - 32);
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) asm("" : "+v"(w[i]));
+}
+
+template <int QT>
+__device__ __forceinline__ void decode16(const uint8_t *__restrict__ blk, int e0, float (&w)[16]) {
+    Raw16<QT> r;
+    load_raw16<QT>(blk, e0, r);
+    decode_raw16<QT>(r, e0, w);
+}
+
+// Weights e .. e + 15 of a row (e % 16 == 0): the block holding them and the offset.
+template <int QT>
+__device__ __forceinline__ void decode_row16(const uint8_t *__restrict__ row, int e, float (&w)[16]) {
+    using TR = XqTraits<QT>;
+    decode16<QT>(row + (size_t)(e / TR::ELEMS) * TR::BYTES, e % TR::ELEMS, w);
+}
+
+// out[r][k]: f32 (F16OUT false) or binary16 bits; one 16-weight run per thread.
+template <int QT, bool F16OUT>
+__global__ __launch_bounds__(256) void xq_dequant_kernel(const uint8_t *__restrict__ W, int rows, int k,
+                                                         void *__restrict__ out) {
+    using TR = XqTraits<QT>;
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    const long runs = (long)rows * (k / 16);
+    if (i >= runs) return;
+    const int r = (int)(i / (k / 16)), e = (int)(i % (k / 16)) * 16;
+    float w[16];
+    decode_row16<QT>(W + (size_t)r * (k / TR::ELEMS) * TR::BYTES, e, w);
+    if constexpr (F16OUT) {
+        uint32_t p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) p[j] = h2_bits(h2_t{(_Float16)w[2 * j], (_Float16)w[2 * j + 1]});
+        u4_t *dst = reinterpret_cast<u4_t *>(static_cast<uint16_t *>(out) + (size_t)r * k + e);
+        dst[0] = u4_t{p[0], p[1], p[2], p[3]};
+        dst[1] = u4_t{p[4], p[5], p[6], p[7]};
+    } else {
+        f4_t *dst = reinterpret_cast<f4_t *>(static_cast<float *>(out) + (size_t)r * k + e);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dst[j] = f4_t{w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]};
+    }
+}
+
+// GEMV, T <= 8 tokens (TT of them per launch): wave g of the grid owns R weight rows,
+// outputs R g .. R g + R - 1 (PLAIN / RESIDUAL), or outputs (R / 2) g .. with their
+// gate and up rows (SwiGLU), so that each x value a lane loads serves R rows. Lanes
+// take 16-weight runs 64 apart; the R rows' raw bytes are all loaded before any is
+// decoded. R = 4 where that still leaves at least 8 waves per CU, else 1 (2 for
+// SwiGLU): memory latency wants the waves more than x wants the reuse.
+template <int QT, int EPI, int TT, int R>
+__global__ __launch_bounds__(256) void xq_gemv_kernel(const uint8_t *__restrict__ W,
+                                                      const float *__restrict__ X, float *__restrict__ Y,
+                                                      int n, int ldy, int k) {
+    using TR = XqTraits<QT>;
+    constexpr int OUTW = EPI == EPI_SWIGLU ? R / 2 : R;
+    const int lane = threadIdx.x & 63;
+    const int g = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (g * OUTW >= n) return;  // whole waves leave
+    const size_t row_bytes = (size_t)(k / TR::ELEMS) * TR::BYTES;
+    const uint8_t *rows[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        int wr;
+        if constexpr (EPI == EPI_SWIGLU)
+            wr = (r < OUTW ? 0 : n) + min(g * OUTW + r % OUTW, n - 1);
+        else
+            wr = min(g * OUTW + r, n - 1);
+        rows[r] = W + (size_t)wr * row_bytes;
+    }
+    float acc[R][TT];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int t = 0; t < TT; ++t) acc[r][t] = 0.f;
+    for (int e = 16 * lane; e < k; e += 16 * 64) {
+        Raw16<QT> raw[R];
+        const size_t boff = (size_t)(e / TR::ELEMS) * TR::BYTES;
+#pragma unroll
+        for (int r = 0; r < R; ++r) load_raw16<QT>(rows[r] + boff, e % TR::ELEMS, raw[r]);
+        f4_t xv[TT][4];
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+            const f4_t *xp = reinterpret_cast<const f4_t *>(X + (size_t)t * k + e);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xv[t][i] = xp[i];
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float w[16];
+            decode_raw16<QT>(raw[r], e % TR::ELEMS, w);
+#pragma unroll
+            for (int t = 0; t < TT; ++t) {
+                float a = acc[r][t];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) a = fmaf(w[i], xv[t][i >> 2][i & 3], a);
+                acc[r][t] = a;
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int dist = 32; dist >= 1; dist >>= 1) acc[r][t] += __shfl_xor(acc[r][t], dist, 64);
+    if (lane == 0) {
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int q = 0; q < OUTW; ++q) {
+                const int o = g * OUTW + q;
+                if (o >= n) continue;
+                float *y = Y + (size_t)t * ldy + o;
+                if constexpr (EPI == EPI_SWIGLU)
+                    *y = silu_f32(acc[q][t]) * acc[OUTW + q][t];
+                else if constexpr (EPI == EPI_RESIDUAL)
+                    *y = *y + acc[q][t];
+                else
+                    *y = acc[q][t];
+            }
+    }
+}
+
+typedef float f16v_t __attribute__((ext_vector_type(16)));
+
+// GEMM. Workgroup tile: MT token rows (128 on the f16 leg, 64 on the f32 leg) x XNW
+// = 128 weight rows (SwiGLU: the 64 gate rows of 64 outputs, then their 64 up rows).
+// Waves 2 x 2, each MT/2 rows x 64 weight rows (MT/64 x 2 accumulator tiles of
+// 32 x 32). LEG16: binary16 operands and v_mfma_f32_32x32x16_f16; else f32 operands
+// and v_mfma_f32_32x32x2f32. Per 32-k step: the next step's raw weight bytes and X
+// are loaded first, this step's MFMAs run while they arrive, then the next step is
+// decoded into the other LDS buffer, one barrier.
+constexpr int XNW = 128, XKS = 32;
+template <int QT, int EPI, bool LEG16, int MT>
+__global__ __launch_bounds__(256) void xq_gemm_kernel(const uint8_t *__restrict__ W,
+                                                      const float *__restrict__ X, float *__restrict__ Y,
+                                                      int n, int ldy, int k, int T, int tiles_m) {
+    using TR = XqTraits<QT>;
+    typedef typename std::conditional<LEG16, _Float16, float>::type op_t;
+    static_assert(MT == 64 || MT == 128, "tile rows");
+    constexpr int IT = MT / 64;                         // 32-row tiles per wave
+    constexpr int PADK = LEG16 ? XKS + 8 : XKS + 4;    // LDS row pitch, elements
+    constexpr int A_ELEMS = MT * PADK, B_ELEMS = XNW * PADK;
+    constexpr int LOOP_BYTES = 2 * (A_ELEMS + B_ELEMS) * (int)sizeof(op_t);
+    constexpr int C_PITCH = XNW + 4;
+    constexpr int EPI_BYTES = MT * C_PITCH * 4;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[LOOP_BYTES > EPI_BYTES ? LOOP_BYTES : EPI_BYTES];
+    op_t *As = reinterpret_cast<op_t *>(smem);
+    op_t *Bs = As + 2 * A_ELEMS;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
+    const int m0 = tm * MT;
+    constexpr int OUT = EPI == EPI_SWIGLU ? XNW / 2 : XNW;  // outputs per tile
+    const int o0 = tn * OUT;
+
+    // Staging: thread t decodes weights 16 (t & 1) .. + 15 of the step for tile row
+    // t >> 1, and converts X floats APT (t % (32 / APT)) .. + APT - 1 of token row
+    // t / (32 / APT).
+    const int brow = tid >> 1, bhalf = tid & 1;
+    int wr;  // global weight row of tile row brow (clamped inside the weight)
+    if constexpr (EPI == EPI_SWIGLU) {
+        const int o = min(o0 + (brow & (XNW / 2 - 1)), n - 1);
+        wr = brow < XNW / 2 ? o : n + o;
+    } else {
+        wr = min(o0 + brow, n - 1);
+    }
+    const uint8_t *wrow = W + (size_t)wr * (k / TR::ELEMS) * TR::BYTES;
+    constexpr int APT = MT * XKS / 256;                 // X floats per thread per step (8 / 16)
+    constexpr int AF4 = APT / 4;
+    const int arow = tid / (XKS / APT), acol = (tid % (XKS / APT)) * APT;
+    const float *xrow = X + (size_t)min(m0 + arow, T - 1) * k + acol;
+
+    Raw16<QT> raw;
+    f4_t xv[AF4];
+    auto load_step = [&](int ks) __attribute__((always_inline)) {
+        const int e = ks * XKS + 16 * bhalf;
+        load_raw16<QT>(wrow + (size_t)(e / TR::ELEMS) * TR::BYTES, e % TR::ELEMS, raw);
+        const f4_t *xp = reinterpret_cast<const f4_t *>(xrow + ks * XKS);
+#pragma unroll
+        for (int i = 0; i < AF4; ++i) xv[i] = xp[i];
+    };
+    // Decode, then 16-byte LDS stores (row pitches and offsets are multiples of 16 bytes).
+    auto store_step = [&](int ks, int buf) __attribute__((always_inline)) {
+        float wv[16];
+        decode_raw16<QT>(raw, (ks * XKS + 16 * bhalf) % TR::ELEMS, wv);
+        op_t *b = Bs + buf * B_ELEMS + brow * PADK + 16 * bhalf;
+        op_t *a = As + buf * A_ELEMS + arow * PADK + acol;
+        if constexpr (LEG16) {
+            uint32_t p[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) p[j] = h2_bits(h2_t{(_Float16)wv[2 * j], (_Float16)wv[2 * j + 1]});
+            reinterpret_cast<u4_t *>(b)[0] = u4_t{p[0], p[1], p[2], p[3]};
+            reinterpret_cast<u4_t *>(b)[1] = u4_t{p[4], p[5], p[6], p[7]};
+#pragma unroll
+            for (int i = 0; i < AF4 / 2; ++i) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const f4_t &v = xv[2 * i + (j >> 1)];
+                    p[j] = h2_bits(h2_t{(_Float16)v[2 * (j & 1)], (_Float16)v[2 * (j & 1) + 1]});
+                }
+                reinterpret_cast<u4_t *>(a)[i] = u4_t{p[0], p[1], p[2], p[3]};
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                reinterpret_cast<f4_t *>(b)[j] = f4_t{wv[4 * j], wv[4 * j + 1], wv[4 * j + 2], wv[4 * j + 3]};
+#pragma unroll
+            for (int i = 0; i < AF4; ++i) reinterpret_cast<f4_t *>(a)[i] = xv[i];
+        }
+    };
+
+    f16v_t acc[IT][2];
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+        acc[i][0] = f16v_t{};
+        acc[i][1] = f16v_t{};
+    }
+    const int c = lane & 31, hh = lane >> 5;
+    const int nks = k / XKS;
+    load_step(0);
+    store_step(0, 0);
+    __syncthreads();
+    for (int ks = 0; ks < nks; ++ks) {
+        const int buf = ks & 1;
+        if (ks + 1 < nks) load_step(ks + 1);
+        const op_t *a = As + buf * A_ELEMS + (wm * (MT / 2) + c) * PADK;
+        const op_t *b = Bs + buf * B_ELEMS + (wn * 64 + c) * PADK;
+        if constexpr (LEG16) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                h8_t bf[2];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) bf[j] = *reinterpret_cast<const h8_t *>(b + j * 32 * PADK + 16 * s + 8 * hh);
+#pragma unroll
+                for (int i = 0; i < IT; ++i) {
+                    const h8_t af = *reinterpret_cast<const h8_t *>(a + i * 32 * PADK + 16 * s + 8 * hh);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[j], acc[i][j], 0, 0, 0);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < XKS / 2; ++s) {
+#pragma unroll
+                for (int i = 0; i < IT; ++i) {
+                    const float af = a[i * 32 * PADK + 2 * s + hh];
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const float bf = b[j * 32 * PADK + 2 * s + hh];
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af, bf, acc[i][j], 0, 0, 0);
+                    }
+                }
+            }
+        }
+        if (ks + 1 < nks) store_step(ks + 1, buf ^ 1);
+        __syncthreads();
+    }
+
+    // Accumulators -> LDS C [token row][tile column] (lane (c, hh) of tile (i, j) holds
+    // rows 32 i + 8 (r / 4) + 4 hh + r % 4 of column 32 j + c), then whole rows to Y.
+    float *C = reinterpret_cast<float *>(smem);
+#pragma unroll
+    for (int i = 0; i < IT; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                C[(wm * (MT / 2) + i * 32 + 8 * (r >> 2) + 4 * hh + (r & 3)) * C_PITCH + wn * 64 + j * 32 + c] =
+                    acc[i][j][r];
+    __syncthreads();
+    for (int i = tid; i < MT * OUT; i += 256) {
+        const int t = i / OUT, oc = i % OUT;
+        const int tt = m0 + t, o = o0 + oc;
+        if (tt >= T || o >= n) continue;
+        float *y = Y + (size_t)tt * ldy + o;
+        const float v = C[t * C_PITCH + oc];
+        if constexpr (EPI == EPI_SWIGLU) {
+            const float u = C[t * C_PITCH + XNW / 2 + oc];
+            *y = LEG16 ? silu_fast(v) * u : silu_f32(v) * u;
+        } else if constexpr (EPI == EPI_RESIDUAL) {
+            *y = *y + v;
+        } else {
+            *y = v;
+        }
+    }
+}
+
+template <int QT, int EPI, int R>
+hipError_t launch_gemv_r(const GemmArgs &a, hipStream_t s) {
+    constexpr int OUTW = EPI == EPI_SWIGLU ? R / 2 : R;  // outputs per wave
+    const dim3 grid((a.n + 4 * OUTW - 1) / (4 * OUTW));
+    for (int t0 = 0; t0 < a.T; t0 += 4) {
+        const int tt = min(4, a.T - t0);
+        const float *x = a.X + (size_t)t0 * a.k;
+        float *y = a.Y + (size_t)t0 * a.ldy;
+        switch (tt) {
+        case 1: hipLaunchKernelGGL((xq_gemv_kernel<QT, EPI, 1, R>), grid, dim3(256), 0, s, a.W, x, y, a.n, a.ldy, a.k); break;
+        case 2: hipLaunchKernelGGL((xq_gemv_kernel<QT, EPI, 2, R>), grid, dim3(256), 0, s, a.W, x, y, a.n, a.ldy, a.k); break;
+        case 3: hipLaunchKernelGGL((xq_gemv_kernel<QT, EPI, 3, R>), grid, dim3(256), 0, s, a.W, x, y, a.n, a.ldy, a.k); break;
+        default: hipLaunchKernelGGL((xq_gemv_kernel<QT, EPI, 4, R>), grid, dim3(256), 0, s, a.W, x, y, a.n, a.ldy, a.k); break;
+        }
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+// Four rows per wave where n / 4 waves still give 8 per CU (256 CUs): n >= 8192.
+template <int QT, int EPI>
+hipError_t launch_gemv_e(const GemmArgs &a, hipStream_t s) {
+    if (a.n >= 8192) return launch_gemv_r<QT, EPI, 4>(a, s);
+    return launch_gemv_r<QT, EPI, EPI == EPI_SWIGLU ? 2 : 1>(a, s);
+}
+
+template <int QT>
+hipError_t launch_gemv_q(const GemmArgs &a, hipStream_t s) {
+    switch (a.epilogue) {
+    case EPI_PLAIN: return launch_gemv_e<QT, EPI_PLAIN>(a, s);
+    case EPI_RESIDUAL: return launch_gemv_e<QT, EPI_RESIDUAL>(a, s);
+    default: return launch_gemv_e<QT, EPI_SWIGLU>(a, s);
+    }
+}
+
+template <int QT, int EPI, bool LEG16, int MT>
+hipError_t launch_gemm_mt(const GemmArgs &a, hipStream_t s) {
+    constexpr int OUT = EPI == EPI_SWIGLU ? XNW / 2 : XNW;
+    const int tm = (a.T + MT - 1) / MT, tn = (a.n + OUT - 1) / OUT;
+    hipLaunchKernelGGL((xq_gemm_kernel<QT, EPI, LEG16, MT>), dim3(tm * tn), dim3(256), 0, s, a.W, a.X, a.Y, a.n,
+                       a.ldy, a.k, a.T, tm);
+    return hipGetLastError();
+}
+
+// Tile rows: 128 on the f16 leg (twice the matrix-core work per decoded weight) when
+// that still makes at least 256 workgroups, else 64 (the f32 leg always).
+template <int QT, int EPI, bool LEG16>
+hipError_t launch_gemm_e(const GemmArgs &a, hipStream_t s) {
+    constexpr int OUT = EPI == EPI_SWIGLU ? XNW / 2 : XNW;
+    if constexpr (LEG16) {
+        const long tiles128 = (long)((a.T + 127) / 128) * ((a.n + OUT - 1) / OUT);
+        if (tiles128 >= 256) return launch_gemm_mt<QT, EPI, true, 128>(a, s);
+    }
+    return launch_gemm_mt<QT, EPI, LEG16, 64>(a, s);
+}
+
+template <int QT, bool LEG16>
+hipError_t launch_gemm_q(const GemmArgs &a, hipStream_t s) {
+    switch (a.epilogue) {
+    case EPI_PLAIN: return launch_gemm_e<QT, EPI_PLAIN, LEG16>(a, s);
+    case EPI_RESIDUAL: return launch_gemm_e<QT, EPI_RESIDUAL, LEG16>(a, s);
+    default: return launch_gemm_e<QT, EPI_SWIGLU, LEG16>(a, s);
+    }
+}
+
+template <int QT, bool F16OUT>
+hipError_t launch_dequant_q(const uint8_t *W, int rows, int k, void *out, hipStream_t s) {
+    const long runs = (long)rows * (k / 16);
+    hipLaunchKernelGGL((xq_dequant_kernel<QT, F16OUT>), dim3((unsigned)((runs + 255) / 256)), dim3(256), 0, s, W,
+                       rows, k, out);
+    return hipGetLastError();
+}
+
+template <bool F16OUT>
+hipError_t launch_dequant_t(int qtype, const uint8_t *W, int rows, int k, void *out, hipStream_t s) {
+    switch (qtype) {
+    case XQ_F16: return launch_dequant_q<XQ_F16, F16OUT>(W, rows, k, out, s);
+    case XQ_Q4_K: return launch_dequant_q<XQ_Q4_K, F16OUT>(W, rows, k, out, s);
+    case XQ_Q5_K: return launch_dequant_q<XQ_Q5_K, F16OUT>(W, rows, k, out, s);
+    default: return launch_dequant_q<XQ_Q6_K, F16OUT>(W, rows, k, out, s);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_xq_gemv(const GemmArgs &a, hipStream_t s) {
+    switch (a.qtype) {
+    case XQ_F16: return launch_gemv_q<XQ_F16>(a, s);
+    case XQ_Q4_K: return launch_gemv_q<XQ_Q4_K>(a, s);
+    case XQ_Q5_K: return launch_gemv_q<XQ_Q5_K>(a, s);
+    default: return launch_gemv_q<XQ_Q6_K>(a, s);
+    }
+}
+
+hipError_t launch_xq_gemm(const GemmArgs &a, bool leg16, hipStream_t s) {
+    switch (a.qtype) {
+    case XQ_F16: return leg16 ? launch_gemm_q<XQ_F16, true>(a, s) : launch_gemm_q<XQ_F16, false>(a, s);
+    case XQ_Q4_K: return leg16 ? launch_gemm_q<XQ_Q4_K, true>(a, s) : launch_gemm_q<XQ_Q4_K, false>(a, s);
+    case XQ_Q5_K: return leg16 ? launch_gemm_q<XQ_Q5_K, true>(a, s) : launch_gemm_q<XQ_Q5_K, false>(a, s);
+    default: return leg16 ? launch_gemm_q<XQ_Q6_K, true>(a, s) : launch_gemm_q<XQ_Q6_K, false>(a, s);
+    }
+}
+
+hipError_t launch_xq_dequant(int qtype, const uint8_t *W, int rows, int k, void *out, bool f16_out, hipStream_t s) {
+    return f16_out ? launch_dequant_t<true>(qtype, W, rows, k, out, s)
+                   : launch_dequant_t<false>(qtype, W, rows, k, out, s);
+}
+
+}  // namespace pf

@@ -42,7 +42,7 @@ def run_gpu(pf, qtype, W, n, k, X, epi, leg, R=None, path=0, stream=None, Wd=Non
 
 def _rows_subset(qtype, W, k, rows):
     """Bytes of the listed weight rows, concatenated (rows are contiguous in W)."""
-    rb = (k // 32) * synth.BLOCK_BYTES[qtype]
+    rb = (k // synth.BLOCK_ELEMS[qtype]) * synth.BLOCK_BYTES[qtype]
     W2 = np.asarray(W, np.uint8).reshape(-1, rb)
     return np.ascontiguousarray(W2[rows]).reshape(-1)
 

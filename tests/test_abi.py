@@ -59,6 +59,11 @@ def test_weight_bytes(lib):
     assert lib.pf_weight_bytes(7, 1, 32) == -pf.PF_E_QTYPE
     assert lib.pf_weight_bytes(pf.PF_Q4_0, 1, 33) == -pf.PF_E_SHAPE
     assert lib.pf_weight_bytes(pf.PF_Q4_0, -1, 32) == -pf.PF_E_SHAPE
+    assert lib.pf_weight_bytes(pf.PF_F16, 3, 64) == 3 * 2 * 64
+    assert lib.pf_weight_bytes(pf.PF_Q4_K, 3, 512) == 3 * 2 * 144
+    assert lib.pf_weight_bytes(pf.PF_Q5_K, 3, 512) == 3 * 2 * 176
+    assert lib.pf_weight_bytes(pf.PF_Q6_K, 3, 512) == 3 * 2 * 210
+    assert lib.pf_weight_bytes(pf.PF_Q6_K, 3, 288) == -pf.PF_E_SHAPE   # not whole super-blocks
 
 
 def test_strerror(lib):
@@ -82,7 +87,14 @@ def test_select_path(lib):
         assert sel(pf.PF_Q8_0, 4096, 4096, T, pf.PF_RESIDUAL, pf.PF_LEG_F16) == want
     for T in (9, 16, 512, 2048):
         assert sel(pf.PF_Q8_0, 4096, 12288, T, pf.PF_RESIDUAL, pf.PF_LEG_F16) == pf.PF_PATH_GEMM
-    assert sel(5, 1, 256, 1, 0, 0) == -pf.PF_E_QTYPE
+    # the further types: the GEMV up to 8 rows on both legs, then the GEMM
+    for qt in (pf.PF_F16, pf.PF_Q4_K, pf.PF_Q5_K, pf.PF_Q6_K):
+        for leg in (pf.PF_LEG_F32, pf.PF_LEG_F16):
+            for epi in (pf.PF_PLAIN, pf.PF_GATE_UP_SWIGLU):
+                assert sel(qt, 4096, 4096, 8, epi, leg) == pf.PF_PATH_GEMV
+                assert sel(qt, 4096, 4096, 9, epi, leg) == pf.PF_PATH_GEMM
+    assert sel(6, 1, 256, 1, 0, 0) == -pf.PF_E_QTYPE
+    assert sel(-1, 1, 256, 1, 0, 0) == -pf.PF_E_QTYPE
     assert sel(0, 1, 256, 1, 3, 0) == -pf.PF_E_EPILOGUE
     assert sel(0, 1, 256, 1, 0, 2) == -pf.PF_E_LEG
     assert sel(0, 1, 128, 1, 0, 0) == -pf.PF_E_SHAPE
@@ -97,7 +109,7 @@ def _gemm(lib, qtype=0, W=FAKE, n=64, k=256, X=FAKE + 1 << 32, T=16, Y=FAKE + 2 
 def test_gemm_argument_checks(lib):
     W, X, Y = FAKE, FAKE + (1 << 32), FAKE + (2 << 32)
     g = lambda **kw: _gemm(lib, **{**dict(W=W, X=X, Y=Y), **kw})
-    assert g(qtype=2) == pf.PF_E_QTYPE
+    assert g(qtype=6) == pf.PF_E_QTYPE
     assert g(qtype=-1) == pf.PF_E_QTYPE
     assert g(epi=3) == pf.PF_E_EPILOGUE
     assert g(leg=2) == pf.PF_E_LEG
@@ -152,24 +164,30 @@ def test_workspace_bytes(lib):
                               64 * 4096 * 2, 64, 24576) <= 32
     assert wb(pf.PF_Q4_0, 12288, 4096, 65, pf.PF_GATE_UP_SWIGLU, pf.PF_LEG_F16) == 96 * 4096 * 2
     # a K split adds S blocks of [T][n] f32 partial sums behind X (256-byte boundary):
-    # 4096^2 at T = 300 is 2 x 22 tiles of 256 x 192, split 3 ways (16 chunks of 256
-    # k, at least 5 per split); at T = 512, 43 tiles of 512 x 96, again 3 ways; the
-    # down projection (k = 12288, 48 chunks) at T = 512 splits 5 ways; at T = 2048 its
-    # 172 tiles need no split.
+    # 4096^2 at T = 300 is 2 x 22 tiles of 256 x 192, split 4 ways (16 chunks of 256
+    # k, at least 4 per split); at T = 512, 43 tiles of 512 x 96, again 4 ways; the
+    # down projection (k = 12288, 48 chunks) at T = 512 splits 5 ways (256 / 43); at
+    # T = 2048 its 172 tiles need no split.
     xb = 320 * 4096 * 2
-    assert wb(pf.PF_Q4_0, 4096, 4096, 300, pf.PF_PLAIN, pf.PF_LEG_F16) == xb + 3 * 300 * 4096 * 4
+    assert wb(pf.PF_Q4_0, 4096, 4096, 300, pf.PF_PLAIN, pf.PF_LEG_F16) == xb + 4 * 300 * 4096 * 4
     assert wb(pf.PF_Q4_0, 4096, 4096, 512, pf.PF_RESIDUAL, pf.PF_LEG_F16) == \
-        512 * 4096 * 2 + 3 * 512 * 4096 * 4
+        512 * 4096 * 2 + 4 * 512 * 4096 * 4
     assert wb(pf.PF_Q8_0, 4096, 12288, 512, pf.PF_RESIDUAL, pf.PF_LEG_F16) == \
         512 * 12288 * 2 + 5 * 512 * 4096 * 4
     assert wb(pf.PF_Q8_0, 4096, 12288, 2048, pf.PF_RESIDUAL, pf.PF_LEG_F16) == 2048 * 12288 * 2
-    # ragged: X bytes rounded up to 256, each split's block to 4 floats
+    # ragged: X bytes rounded up to 256, each split's block to 4 floats (12 chunks: 3
+    # splits)
     assert wb(pf.PF_Q4_0, 1001, 3072, 300, pf.PF_PLAIN, pf.PF_LEG_F16) == \
-        320 * 3072 * 2 + 2 * ((300 * 1001 + 3) // 4 * 4) * 4
+        320 * 3072 * 2 + 3 * ((300 * 1001 + 3) // 4 * 4) * 4
     assert wb(pf.PF_Q4_0, 17, 256, 300, pf.PF_PLAIN, pf.PF_LEG_F16) == 320 * 256 * 2
-    # 5 chunks of k are too few to split
+    # 5 chunks of k are too few to split in two
     assert wb(pf.PF_Q4_0, 17, 1280, 290, pf.PF_RESIDUAL, pf.PF_LEG_F16) == 320 * 1280 * 2
     assert wb(pf.PF_Q4_0, 4096, 4096, 512, pf.PF_PLAIN, pf.PF_LEG_F32) == 0
+    # the further types never take a workspace
+    for qt in (pf.PF_F16, pf.PF_Q4_K, pf.PF_Q5_K, pf.PF_Q6_K):
+        for T in (1, 8, 9, 300, 512):
+            for epi in (pf.PF_PLAIN, pf.PF_RESIDUAL, pf.PF_GATE_UP_SWIGLU):
+                assert wb(qt, 4096, 4096, T, epi, pf.PF_LEG_F16) == 0
     # the GEMV (f16 leg: up to 2 rows, or up to 4 with the SwiGLU epilogue) takes none;
     # from 3 rows the f16 leg's PLAIN and RESIDUAL run the GEMM
     assert wb(pf.PF_Q4_0, 4096, 4096, 2, pf.PF_PLAIN, pf.PF_LEG_F16) == 0
@@ -181,7 +199,7 @@ def test_workspace_bytes(lib):
     # a single K chunk cannot split: X alone
     assert wb(pf.PF_Q4_0, 64, 256, 40, pf.PF_PLAIN, pf.PF_LEG_F16) == 64 * 256 * 2
     assert wb(pf.PF_Q4_0, 4096, 4096, 0, pf.PF_PLAIN, pf.PF_LEG_F16) == 0
-    assert wb(3, 64, 256, 16, 0, 1) == -pf.PF_E_QTYPE
+    assert wb(6, 64, 256, 16, 0, 1) == -pf.PF_E_QTYPE
     assert wb(0, 64, 300, 16, 0, 1) == -pf.PF_E_SHAPE
     assert wb(0, 64, 256, 16, 0, 5) == -pf.PF_E_LEG
 
@@ -235,7 +253,7 @@ def test_gemm_ex_argument_checks(lib):
     assert g(X=Y + 4 * 80) == pf.PF_E_ALIAS         # X inside the gap after row 0: still Y's span
     assert g(Y=X + T * k * 4 - 16) == pf.PF_E_ALIAS
     assert g(Y=Y + 8) == pf.PF_E_ALIGN
-    assert g(qtype=5) == pf.PF_E_QTYPE
+    assert g(qtype=6) == pf.PF_E_QTYPE
     # f16 leg with a workspace: too small, or NULL with a size, is refused
     need = lib.pf_workspace_bytes(0, n, k, T, 0, pf.PF_LEG_F16)
     assert need == 32 * k * 2
@@ -285,7 +303,7 @@ def test_gemm_rmsnorm_argument_checks(lib):
     assert g(ws_bytes=need - 16) == pf.PF_E_WORKSPACE
     assert g(ws=NW - 16) == pf.PF_E_WORKSPACE          # overlaps norm_w
     assert g(ws=X + 64) == pf.PF_E_WORKSPACE
-    assert g(qtype=4) == pf.PF_E_QTYPE
+    assert g(qtype=7) == pf.PF_E_QTYPE
     assert g(T=0, ws=0, ws_bytes=0, nw=0) == pf.PF_OK
 
 
@@ -300,7 +318,7 @@ def test_lm_head_argmax_argument_checks(lib):
         return lib.pf_lm_head_argmax(a["qtype"], P(a["W"]), a["n"], a["k"], P(a["x"]), P(a["L"]),
                                      P(a["tok"]), None)
 
-    assert g(qtype=3) == pf.PF_E_QTYPE
+    assert g(qtype=8) == pf.PF_E_QTYPE
     assert g(k=300) == pf.PF_E_SHAPE
     assert g(n=0) == pf.PF_E_SHAPE
     for name in ("W", "x", "L", "tok"):
@@ -320,6 +338,9 @@ def test_prepared_argument_checks(lib):
     px = lambda **kw: lib.pf_prepare_x(kw.get("qtype", 0), kw.get("k", k), P(kw.get("X", X)), kw.get("T", T),
                                        P(kw.get("ws", WS)), kw.get("wsb", xneed), None)
     assert px(qtype=7) == pf.PF_E_QTYPE
+    # the further types' GEMM reads f32 X: no prepared form
+    for qt in (pf.PF_F16, pf.PF_Q4_K, pf.PF_Q5_K, pf.PF_Q6_K):
+        assert px(qtype=qt) == pf.PF_E_QTYPE
     assert px(k=300) == pf.PF_E_SHAPE
     assert px(T=0) == pf.PF_OK
     assert px(X=0) == pf.PF_E_NULL
@@ -347,7 +368,7 @@ def test_dequant_argument_checks(lib):
     P = ctypes.c_void_p
     W, out = P(FAKE), P(FAKE + (1 << 32))
     for fn in (lib.pf_dequant_f32, lib.pf_dequant_f16):
-        assert fn(3, W, 4, 64, out, None) == pf.PF_E_QTYPE
+        assert fn(6, W, 4, 64, out, None) == pf.PF_E_QTYPE
         assert fn(0, W, 0, 64, out, None) == pf.PF_E_SHAPE
         assert fn(0, W, 4, 48, out, None) == pf.PF_E_SHAPE
         assert fn(0, P(0), 4, 64, out, None) == pf.PF_E_NULL
@@ -393,7 +414,7 @@ def test_gemm_noalloc_argument_checks(lib):
     def g(qtype=pf.PF_Q4_0, W=W, n=64, k=256, X=X, T=16, Y=Y, epi=pf.PF_PLAIN, leg=f16):
         return lib.pf_gemm_noalloc(qtype, P(W), n, k, P(X), T, P(Y), epi, leg, None)
 
-    assert g(qtype=5) == pf.PF_E_QTYPE
+    assert g(qtype=6) == pf.PF_E_QTYPE
     assert g(epi=7) == pf.PF_E_EPILOGUE
     assert g(leg=3) == pf.PF_E_LEG
     assert g(k=100) == pf.PF_E_SHAPE

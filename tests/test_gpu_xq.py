@@ -1,0 +1,137 @@
+"""GPU parity of the further weight types (F16, Q4_K, Q5_K, Q6_K) through the C ABI
+against the fp64 CPU oracle: bit-exact decode on both legs (f32, and its binary16
+rounding), and the GEMV (T <= 8) and tiled GEMM on every output of ragged shapes,
+each epilogue, both legs, at the legs' bars. Weights: the synthetic encoders'
+blocks (N(0, 0.02) weights), and random blocks under edge-valued scale fields
+(tests/xq_blocks.py).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from quantized_weight_prefill_gguf_amd import synth
+from tests import parity, xq_blocks
+
+pytestmark = pytest.mark.gpu
+
+XQ = [synth.F16, synth.Q4_K, synth.Q5_K, synth.Q6_K]
+NAMES = {synth.F16: "f16", synth.Q4_K: "q4_k", synth.Q5_K: "q5_k", synth.Q6_K: "q6_k"}
+PLAIN, RESIDUAL, SWIGLU = oracle.PLAIN, oracle.RESIDUAL, oracle.GATE_UP_SWIGLU
+F32, F16 = 0, 1
+
+
+def _weights(qtype, rows, k, kind, leg, seed):
+    if kind == "synth":
+        return synth.quantize(qtype, synth.weights_f32(rows, k, workload_id=seed))
+    return xq_blocks.weight(qtype, rows, k, seed, xq_blocks.TOP["f16" if leg == F16 else "f32"][qtype])
+
+
+@pytest.mark.parametrize("kind", ["synth", "edge"])
+@pytest.mark.parametrize("qtype", XQ, ids=lambda q: NAMES[q])
+def test_xq_dequant_bit_exact(gpu, qtype, kind):
+    import torch
+    rows, k = 70, 2048
+    W = _weights(qtype, rows, k, kind, F16, 600 + qtype)
+    Wd = parity.to_dev(W)
+    out32 = torch.empty(rows * k, dtype=torch.float32, device="cuda")
+    out16 = torch.empty(rows * k, dtype=torch.int16, device="cuda")
+    gpu.dequant_f32(qtype, Wd, rows, k, out32)
+    gpu.dequant_f16(qtype, Wd, rows, k, out16)
+    torch.cuda.synchronize()
+    ref32 = oracle.dequant_f32(qtype, W, rows, k).reshape(-1)
+    ref16 = oracle.dequant_f16(qtype, W, rows, k).reshape(-1)
+    assert np.array_equal(out32.cpu().numpy().view(np.uint32), ref32.view(np.uint32))
+    assert np.array_equal(out16.cpu().numpy().view(np.uint16), ref16)
+
+
+@pytest.mark.parametrize("leg", [F32, F16])
+@pytest.mark.parametrize("epi", [PLAIN, RESIDUAL, SWIGLU])
+@pytest.mark.parametrize("T", [1, 3, 8, 9, 64, 130])
+@pytest.mark.parametrize("kind", ["synth", "edge"])
+@pytest.mark.parametrize("qtype", XQ, ids=lambda q: NAMES[q])
+def test_xq_gemm_every_output(gpu, qtype, kind, T, epi, leg):
+    n, k = 150, 768
+    rows = 2 * n if epi == SWIGLU else n
+    seed = 610 + 7 * qtype + T + 3 * epi + leg
+    W = _weights(qtype, rows, k, kind, leg, seed)
+    X = synth.activations(T, k, workload_id=seed)
+    R = synth.activations(T, n, workload_id=seed, tensor_id=synth.TENSOR_R) if epi == RESIDUAL else None
+    want_path = gpu.PF_PATH_GEMV if T <= 8 else gpu.PF_PATH_GEMM
+    assert gpu.select_path(qtype, n, k, T, epi, leg) == want_path
+    print("case xq %s %s T=%d epi=%d leg=%d" % (NAMES[qtype], kind, T, epi, leg), flush=True)
+    Y = parity.run_gpu(gpu, qtype, W, n, k, X, epi, leg, R=R)
+    ok, err = parity.check(qtype, W, n, k, X, Y, epi, leg, R=R)
+    assert ok, "parity failed: metric %.3e" % err
+
+
+@pytest.mark.parametrize("qtype", XQ, ids=lambda q: NAMES[q])
+def test_xq_forced_families_and_noalloc(gpu, qtype):
+    """For T <= 8 the forced GEMM meets the bar too; pf_gemm_ws and pf_gemm_noalloc
+    need no workspace for these types and give pf_gemm's bits."""
+    import torch
+    n, k = 96, 1024
+    for T, epi, leg in [(5, SWIGLU, F16), (7, RESIDUAL, F32), (2, PLAIN, F16)]:
+        rows = 2 * n if epi == SWIGLU else n
+        W = _weights(qtype, rows, k, "synth", leg, 640 + T)
+        X = synth.activations(T, k, workload_id=640 + T)
+        R = synth.activations(T, n, workload_id=640 + T, tensor_id=synth.TENSOR_R) if epi == RESIDUAL else None
+        for path in (1, 2):
+            Y = parity.run_gpu(gpu, qtype, W, n, k, X, epi, leg, R=R, path=path)
+            ok, err = parity.check(qtype, W, n, k, X, Y, epi, leg, R=R)
+            assert ok, (path, err)
+        assert gpu.workspace_bytes(qtype, n, k, T, epi, leg) == 0
+        y0 = parity.run_gpu(gpu, qtype, W, n, k, X, epi, leg, R=R)
+        y1 = parity.run_gpu(gpu, qtype, W, n, k, X, epi, leg, R=R, workspace=True)
+        Wd, Xd = parity.to_dev(W), parity.to_dev(X)
+        Yd = parity.to_dev(R) if R is not None else torch.full((T, n), float("nan"), device="cuda")
+        gpu.gemm_noalloc(qtype, Wd, n, k, Xd, Yd, epi, leg)
+        torch.cuda.synchronize()
+        assert np.array_equal(y0.view(np.uint32), y1.view(np.uint32))
+        assert np.array_equal(y0.view(np.uint32), Yd.cpu().numpy().view(np.uint32))
+
+
+@pytest.mark.parametrize("qtype", XQ, ids=lambda q: NAMES[q])
+def test_xq_full_size_sampled(gpu, qtype):
+    """The gate/up shape at T = 512 on the f16 leg (sampled outputs)."""
+    n, k, T = 12288, 4096, 512
+    W = synth.quantize(qtype, np.concatenate([synth.weights_f32(n, k, workload_id=650),
+                                              synth.weights_f32(n, k, workload_id=650,
+                                                                tensor_id=synth.TENSOR_W_UP)]))
+    X = synth.activations(T, k, workload_id=650)
+    print("case xq full %s" % NAMES[qtype], flush=True)
+    Y = parity.run_gpu(gpu, qtype, W, n, k, X, SWIGLU, F16)
+    ok, err = parity.check(qtype, W, n, k, X, Y, SWIGLU, F16, samples=4096)
+    assert ok, "parity failed: metric %.3e" % err
+
+
+@pytest.mark.parametrize("qtype", XQ, ids=lambda q: NAMES[q])
+def test_xq_lm_head_and_rmsnorm(gpu, qtype):
+    import torch
+    from oracle import tolerance
+    n, k = 3000, 1024
+    W = synth.quantize(qtype, synth.weights_f32(n, k, workload_id=660))
+    x = synth.activations(1, k, workload_id=660).reshape(k)
+    logits = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    token = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    gpu.lm_head_argmax(qtype, parity.to_dev(W), n, k, parity.to_dev(x), logits, token)
+    torch.cuda.synchronize()
+    lg, tok = logits.cpu().numpy(), int(token.cpu().numpy()[0])
+    acc = oracle.matmul(qtype, W, n, k, x.reshape(1, k))
+    ok, err = tolerance.check_linear(lg.reshape(1, n), acc, oracle.row_norms(qtype, W, n, k),
+                                     np.linalg.norm(x.astype(np.float64)).reshape(1), "f32")
+    assert ok, err
+    assert tok == oracle.argmax_last(lg)
+    # RMSNorm prologue then the GEMM (T = 40, f16 leg)
+    T, eps = 40, 1e-6
+    X = synth.activations(T, k, workload_id=661)
+    nw = np.random.default_rng(661).uniform(0.5, 1.5, k).astype(np.float32)
+    Y = torch.full((T, n), float("nan"), dtype=torch.float32, device="cuda")
+    need = gpu.rmsnorm_workspace_bytes(qtype, n, k, T, PLAIN, F16)
+    ws = torch.empty((need,), dtype=torch.uint8, device="cuda")
+    gpu.gemm_rmsnorm(qtype, parity.to_dev(W), n, k, parity.to_dev(X), parity.to_dev(nw), eps, Y, PLAIN, F16, ws)
+    torch.cuda.synchronize()
+    Xn = oracle.rmsnorm(X, nw, eps)
+    ref = oracle.matmul_f64(qtype, W, n, k, Xn)
+    ok, err = tolerance.check_linear(Y.cpu().numpy(), ref, oracle.row_norms(qtype, W, n, k),
+                                     np.linalg.norm(Xn, axis=1), "f16")
+    assert ok, err

@@ -1,0 +1,55 @@
+"""Blocks of the further weight types (F16, Q4_K, Q5_K, Q6_K) for parity tests:
+random code bytes under chosen scale fields (input generation only).
+
+Any byte pattern is a block of these types, so the codes, 6-bit scales, mins and
+Q6_K's int8 scales are drawn uniformly; the binary16 fields (d, dmin, F16 values)
+come from a list of edge values with both signs (subnormal, normal minimum, one,
+zero) and a magnitude chosen so that on the f16 leg every weight stays finite in
+binary16 (|w| <= 65504; the f16 leg does not define infinite weights).
+"""
+import numpy as np
+
+from quantized_weight_prefill_gguf_amd import synth
+
+# binary16 magnitudes: 2^-24, largest subnormal, 2^-14, 1/3, 0.5, 1, 0
+EDGE = np.array([0x0001, 0x03FF, 0x0400, 0x3555, 0x3800, 0x3C00, 0x0000], np.uint16)
+
+
+def _f16(v):
+    return np.asarray(v, np.float32).astype(np.float16).view(np.uint16)
+
+
+def weight(qtype, rows, k, seed, top):
+    """uint8 blocks; `top` bounds |d| (and |dmin|) so that |w| stays below 65504 on the
+    f16 leg: Q4_K / Q5_K weights reach 63 (31 |d| + |dmin|), Q6_K 128 * 32 |d|."""
+    rng = np.random.default_rng([seed, 11, qtype])
+    B, E = synth.BLOCK_BYTES[qtype], synth.BLOCK_ELEMS[qtype]
+    nb = k // E
+    W = rng.integers(0, 256, size=(rows, nb, B), dtype=np.uint8)
+    if qtype == synth.F16:
+        h = _f16(np.clip(rng.standard_normal((rows, nb, 32)) * top / 5, -65504, 65504))
+        pick = rng.integers(0, len(EDGE) + 4, size=h.shape)
+        edge = pick < len(EDGE)
+        h[edge] = EDGE[pick[edge]]
+        h |= (rng.integers(0, 2, size=h.shape).astype(np.uint16) << 15)
+        return h.view(np.uint8).reshape(-1).copy()
+    mags = np.concatenate([EDGE, _f16([top, top / 3.0, top / 77.0])])
+    def field():
+        v = mags[rng.integers(0, len(mags), size=(rows, nb))]
+        return v | (rng.integers(0, 2, size=(rows, nb)).astype(np.uint16) << 15)
+    if qtype == synth.Q6_K:
+        d = field()
+        W[:, :, 208] = d & 0xFF
+        W[:, :, 209] = d >> 8
+    else:
+        d, dm = field(), field()
+        W[:, :, 0] = d & 0xFF
+        W[:, :, 1] = d >> 8
+        W[:, :, 2] = dm & 0xFF
+        W[:, :, 3] = dm >> 8
+    return W.reshape(-1)
+
+
+# largest |d| per type for the f16 leg (binary16-finite weights), and a value for the f32 leg
+TOP = {"f16": {synth.F16: 60000.0, synth.Q4_K: 30.0, synth.Q5_K: 30.0, synth.Q6_K: 15.0},
+       "f32": {synth.F16: 60000.0, synth.Q4_K: 60000.0, synth.Q5_K: 60000.0, synth.Q6_K: 60000.0}}
