@@ -23,21 +23,32 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-I", os.path.join(ROOT, "include")]
 
 
-def _compile(src):
+# Sanitizer switch for the host-side argument validation (pf_api.cpp, the C ABI's
+# checks that run before any HIP call): ASan + UBSan on its host code, each
+# -fsanitize directly after -Xarch_host so that no device code is built with it.
+SAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+SAN_SOURCES = ("pf_api.cpp",)
+
+
+def _compile(src, sanitize=False):
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    san = SAN_HOST if sanitize and src in SAN_SOURCES else []
+    cmd = [HIPCC, *FLAGS, *san, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
     return obj
 
 
-def build():
-    """Compile every source and link libpfgemm.so; returns its path."""
+def build(sanitize=False):
+    """Compile every source and link libpfgemm.so; returns its path. sanitize: the
+    host validation in pf_api.cpp built with ASan + UBSan (load the library with the
+    clang ASan runtime preloaded; see tests/sanitize_run.py)."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(lambda src: _compile(src, sanitize), SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -48,4 +59,5 @@ def build():
 
 
 if __name__ == "__main__":
-    print(build())
+    import sys
+    print(build(sanitize="--sanitize" in sys.argv))
