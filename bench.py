@@ -65,7 +65,7 @@ def weight_bytes(qtype, rows, k):
 KERNEL_SOURCES = {
     "gemm_f16": ["pf_gemm_f16.hip", "pf_device.h"],
     "gemm_f32": ["pf_gemm_f32.hip", "pf_device.h"],
-    "gemv": ["pf_gemv.hip", "pf_device.h"],
+    "gemv": ["pf_gemv.hip", "pf_gemv_mfma.hip", "pf_device.h"],
     "xq": ["pf_xq.hip", "pf_device.h"],
 }
 
@@ -86,6 +86,17 @@ def kernel_source_sha(family):
 
 def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def gemv_sweep():
+    """gemv_<qtype>_<n>x<k>_T<T>: one f32-leg PLAIN projection of T rows."""
+    out = {}
+    for qname, qtype in (("q4_0", Q4_0), ("q8_0", Q8_0)):
+        for n, k, src in ((INTER, HIDDEN, "x"), (HIDDEN, INTER, "x12288")):
+            for T in (1, 2, 4, 8):
+                out["gemv_%s_%dx%d_T%d" % (qname, n, k, T)] = (
+                    T, 0, [("gemv_" + qname, qtype, n, k, PLAIN, src, "out")], 1)
+    return out
 
 
 def workloads():
@@ -111,14 +122,8 @@ def workloads():
         "gate_up_T512_f32": (512, 0, [gu, down], 1),
         "plain_q4_0_4096_T512_f16": (512, 1, [("plain_q4_0", Q4_0, HIDDEN, HIDDEN, PLAIN, "x", "out")], 1),
         "plain_q4_0_4096_T2048_f16": (2048, 1, [("plain_q4_0", Q4_0, HIDDEN, HIDDEN, PLAIN, "x", "out")], 1),
-        "gemv_q4_0_12288x4096_T1": (1, 0, [("gemv_q4_0", Q4_0, INTER, HIDDEN, PLAIN, "x", "out")], 1),
-        "gemv_q8_0_4096x12288_T1": (1, 0, [("gemv_q8_0", Q8_0, HIDDEN, INTER, PLAIN, "x12288", "out")], 1),
-        "gemv_q4_0_4096x12288_T1": (1, 0, [("gemv_q4_0", Q4_0, HIDDEN, INTER, PLAIN, "x12288", "out")], 1),
-        "gemv_q8_0_12288x4096_T1": (1, 0, [("gemv_q8_0", Q8_0, INTER, HIDDEN, PLAIN, "x", "out")], 1),
-        "gemv_q4_0_12288x4096_T2": (2, 0, [("gemv_q4_0", Q4_0, INTER, HIDDEN, PLAIN, "x", "out")], 1),
-        "gemv_q4_0_12288x4096_T4": (4, 0, [("gemv_q4_0", Q4_0, INTER, HIDDEN, PLAIN, "x", "out")], 1),
-        "gemv_q4_0_12288x4096_T8": (8, 0, [("gemv_q4_0", Q4_0, INTER, HIDDEN, PLAIN, "x", "out")], 1),
-        "gemv_q8_0_4096x12288_T8": (8, 0, [("gemv_q8_0", Q8_0, HIDDEN, INTER, PLAIN, "x12288", "out")], 1),
+        # the small-T sweep: Q4_0 and Q8_0 at T in {1, 2, 4, 8} on both projection shapes
+        **gemv_sweep(),
         # the further weight types (the same projections with F16 / Q4_K / Q6_K weights)
         "gate_up_q4_k_T512_f16": (512, 1, [("gate_up_swiglu_q4_k", Q4_K, INTER, HIDDEN, SWIGLU, "x", "act")], 1),
         "gate_up_q4_k_T512_f32": (512, 0, [("gate_up_swiglu_q4_k", Q4_K, INTER, HIDDEN, SWIGLU, "x", "act")], 1),
@@ -277,17 +282,10 @@ def _short_kernel(name):
 def _op_of_kernel(short, ops):
     """Which op of a workload launched the library kernel `short` (None if not ours).
     Block-type templated kernels name the qtype first; split_sum_kernel names the
-    epilogue; zero_fill_kernel belongs to the PLAIN op, else to the SwiGLU op (whose
-    split on short chunks clears its gate/up scratch), as swiglu_apply_kernel does."""
+    epilogue; swiglu_apply_kernel belongs to the SwiGLU op."""
     import re
     m = re.match(r"(\w+)<(\d+)", short)
     base = m.group(1) if m else short
-    if base == "zero_fill_kernel":
-        for want in (PLAIN, SWIGLU):
-            for op in ops:
-                if op[4] == want:
-                    return op
-        return None
     for op in ops:
         if base == "split_sum_kernel":
             if int(m.group(2)) == op[4]:
@@ -302,7 +300,7 @@ def _op_of_kernel(short, ops):
             if op[0].startswith("lm_head_"):
                 return op
         elif base in ("x_to_frag_kernel", "x_to_f16_kernel", "gemm_f16_coop_kernel", "gemm_f16_kernel",
-                      "gemm_f32_kernel", "gemv_kernel") and m and int(m.group(2)) == op[1]:
+                      "gemm_f32_kernel", "gemv_kernel", "gemv_mfma_kernel") and m and int(m.group(2)) == op[1]:
             return op
     return None
 
@@ -409,7 +407,8 @@ def counter_summary(workload, pmc_dir, kt_dir):
     peak = PEAK["fp16_mfma_tflops"] if leg == 1 else PEAK["fp32_mfma_tflops"]
     lines = ["%-46s %6s %11s %14s %14s %14s %14s %8s %9s %8s" % (
         "kernel", "disp", "avg_us", *names, "sclk", "mfma_busy", "frac@sclk")]
-    gemm_kernels = ("gemm_f16_coop_kernel", "gemm_f16_kernel", "gemm_f32_kernel", "gemv_kernel")
+    gemm_kernels = ("gemm_f16_coop_kernel", "gemm_f16_kernel", "gemm_f32_kernel", "gemv_kernel",
+                    "gemv_mfma_kernel")
     for op in ops:
         per = {}
         for (_, kn), cs in counters.items():

@@ -13,7 +13,8 @@ LIB = os.path.join(HERE, "libpfgemm.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
 SOURCES = ["pf_api.cpp", "pf_dequant.hip", "pf_gemm_f32.hip", "pf_gemm_f16.hip", "pf_gemv.hip",
-           "pf_rmsnorm.hip", "pf_argmax.hip", "pf_noalloc.hip", "pf_xq.hip", "pf_probe.hip"]
+           "pf_rmsnorm.hip", "pf_argmax.hip", "pf_noalloc.hip", "pf_xq.hip", "pf_probe.hip",
+           "pf_gemv_mfma.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # gfx950 only. Packed fp32 instructions are switched off for device code (the

@@ -71,6 +71,15 @@ int auto_path(int qtype, int64_t T, int epilogue, int leg) {
     return PF_PATH_GEMV;
 }
 
+// The Q4_0 / Q8_0 GEMV: on the f32 leg from 3 tokens on the fp32 matrix cores, else
+// on the vector ALU. The vector-ALU form spends an FMA and an LDS read of x per weight
+// and token, which from about 3 tokens costs more than the matrix cores' fixed decode
+// (measured on Q4_0 12288 x 4096: T = 4 20.3 -> 15.7 us, T = 8 38.3 -> 20.6 us; at
+// T = 2 12.5 against 15.0).
+hipError_t launch_gemv_q(const pf::GemmArgs &a, int leg, hipStream_t s) {
+    return (leg == PF_LEG_F32 && a.T >= 3) ? pf::launch_gemv_mfma(a, s) : pf::launch_gemv(a, s);
+}
+
 // Bytes of workspace the f16 leg's GEMM takes (X as binary16, T rounded up to a
 // multiple of 32 for the fragment-ordered copy, plus the partial sums of a K split),
 // else 0.
@@ -128,7 +137,7 @@ int gemm_impl(int qtype, const void *W, int64_t n, int64_t k, const float *X, in
     if (is_xq(qtype))
         err = use == PF_PATH_GEMV ? pf::launch_xq_gemv(a, s) : pf::launch_xq_gemm(a, leg == PF_LEG_F16, s);
     else if (use == PF_PATH_GEMV)
-        err = pf::launch_gemv(a, s);
+        err = launch_gemv_q(a, leg, s);
     else if (leg == PF_LEG_F32)
         err = pf::launch_gemm_f32(a, s);
     else if (need > 0)
@@ -201,7 +210,7 @@ int rms_impl(int qtype, const void *W, int64_t n, int64_t k, const float *X, int
         if (is_xq(qtype))
             err = use == PF_PATH_GEMV ? pf::launch_xq_gemv(a, s) : pf::launch_xq_gemm(a, leg == PF_LEG_F16, s);
         else
-            err = use == PF_PATH_GEMV ? pf::launch_gemv(a, s) : pf::launch_gemm_f32(a, s);
+            err = use == PF_PATH_GEMV ? launch_gemv_q(a, leg, s) : pf::launch_gemm_f32(a, s);
     }
     return err == hipSuccess ? PF_OK : PF_E_LAUNCH;
 }

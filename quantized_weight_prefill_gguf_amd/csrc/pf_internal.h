@@ -47,8 +47,10 @@ hipError_t launch_rms_apply(const float *X, const float *inv, const float *w, fl
                             hipStream_t s);
 // token[0] = the largest index among the maxima of logits[0 .. n) (one workgroup).
 hipError_t launch_argmax(const float *logits, int n, int32_t *token, hipStream_t s);
-// Small-T GEMV (T <= 8), f32 arithmetic.
+// Small-T GEMV (T <= 8), f32 arithmetic on the vector ALU.
 hipError_t launch_gemv(const GemmArgs &a, hipStream_t s);
+// Small-T GEMV (T <= 8) on the fp32 matrix cores (exact f32 operands).
+hipError_t launch_gemv_mfma(const GemmArgs &a, hipStream_t s);
 // Size of the static device scratch pf_gemm_noalloc runs in (PF_NOALLOC_SCRATCH_BYTES),
 // and its address on the device of stream s (taken once per device, then cached).
 constexpr int64_t kNoallocScratchBytes = int64_t(64) << 20;
