@@ -17,10 +17,10 @@ import numpy as np
 
 from . import build as _build
 
-Q4_0, Q8_0, F16, Q4_K, Q5_K, Q6_K = 0, 1, 2, 3, 4, 5
+Q4_0, Q8_0, F16, Q4_K, Q5_K, Q6_K, IQ4_XS = 0, 1, 2, 3, 4, 5, 6
 PLAIN, RESIDUAL, GATE_UP_SWIGLU = 0, 1, 2
-BLOCK_BYTES = {Q4_0: 18, Q8_0: 34, F16: 64, Q4_K: 144, Q5_K: 176, Q6_K: 210}
-BLOCK_ELEMS = {Q4_0: 32, Q8_0: 32, F16: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256}
+BLOCK_BYTES = {Q4_0: 18, Q8_0: 34, F16: 64, Q4_K: 144, Q5_K: 176, Q6_K: 210, IQ4_XS: 136}
+BLOCK_ELEMS = {Q4_0: 32, Q8_0: 32, F16: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256, IQ4_XS: 256}
 
 _lib = None
 

@@ -31,7 +31,8 @@
  *    Q4_K, Q5_K, Q6_K over 256-element super-blocks, F16 over 32-element groups),
  *    and `qwen35_fp16_weight`: the f16 leg's weight is that f32 value rounded to
  *    binary16. The pages print none of these layouts; they are GGUF's, restated
- *    at decode_k_block below.
+ *    at decode_k_block and decode_iq4_xs_block below. The same function also
+ *    dequantizes IQ4_XS over 256-element super-blocks (`Iq4XsDequantKernel`).
  *  - IEEE 754 binary16 for the scale and for the f16 leg's input rounding.
  *
  * Every floating-point step is written out: no fast-math, no FMA contraction
@@ -52,6 +53,7 @@
 #define ORACLE_Q4_K 3
 #define ORACLE_Q5_K 4
 #define ORACLE_Q6_K 5
+#define ORACLE_IQ4_XS 6
 
 #define ORACLE_PLAIN 0
 #define ORACLE_RESIDUAL 1
@@ -178,6 +180,7 @@ int oracle_block_bytes(int qtype)
     case ORACLE_Q4_K: return 144;
     case ORACLE_Q5_K: return 176;
     case ORACLE_Q6_K: return 210;
+    case ORACLE_IQ4_XS: return 136;
     default: return -1;
     }
 }
@@ -185,7 +188,8 @@ int oracle_block_bytes(int qtype)
 /* Weights per block: 32, or 256 for the super-block types. */
 int oracle_block_elems(int qtype)
 {
-    return (qtype == ORACLE_Q4_K || qtype == ORACLE_Q5_K || qtype == ORACLE_Q6_K) ? 256 : 32;
+    return (qtype == ORACLE_Q4_K || qtype == ORACLE_Q5_K || qtype == ORACLE_Q6_K ||
+            qtype == ORACLE_IQ4_XS) ? 256 : 32;
 }
 
 /* The scale: a binary16 stored little-endian in bytes 0-1 of the block. Its
@@ -267,6 +271,35 @@ static void decode_k_block(int qtype, const uint8_t *blk, float *out)
     }
 }
 
+/* The 16 values an IQ4_XS code selects (GGUF's non-linear 4-bit grid, shared with
+ * IQ4_NL), indexed by the code. */
+static const int IQ4_GRID[16] = {-127, -104, -83, -65, -49, -35, -22, -10,
+                                 1, 13, 25, 38, 53, 69, 89, 113};
+
+/* Decode one IQ4_XS super-block (136 bytes, 256 elements) into f32: fp16 d, a
+ * little-endian uint16 scales_h, 4 bytes scales_l, then 128 bytes of codes. Element
+ * e lies in sub-block b = e / 32; its 6-bit scale has its low 4 bits in the nibble b
+ * % 2 (low for even b) of scales_l[b / 2] and its top 2 bits in bits 2b, 2b+1 of
+ * scales_h. With l = e % 32, the code is the low (l < 16) or high (l >= 16) nibble
+ * of qs[16 b + l % 16]. Value (d (ls - 32)) grid[code]: d (ls - 32) is exact in f32
+ * (11 + 6 significant bits) and so is its product with a grid value (7 more bits). */
+static void decode_iq4_xs_block(const uint8_t *blk, float *out)
+{
+    float d = fp16_at(blk);
+    int scales_h = blk[2] | (blk[3] << 8);
+    const uint8_t *scales_l = blk + 4, *qs = blk + 8;
+    for (int e = 0; e < 256; ++e) {
+        int b = e / 32, l = e % 32;
+        int lo4 = (scales_l[b / 2] >> (4 * (b % 2))) & 15;
+        int hi2 = (scales_h >> (2 * b)) & 3;
+        int ls = lo4 | (hi2 << 4);
+        float dl = d * (float)(ls - 32);
+        int byte = qs[16 * b + l % 16];
+        int code = (l < 16) ? (byte & 15) : (byte >> 4);
+        out[e] = dl * (float)IQ4_GRID[code];
+    }
+}
+
 /* Decode one block into f32 (32 or 256 elements, see oracle_block_elems). Q4_0 /
  * Q8_0: each value is one f32 multiply of the scale by a small integer; the
  * product of an 11-bit and a <= 8-bit significand is exact in f32, so these are
@@ -277,6 +310,10 @@ static void decode_block(int qtype, const uint8_t *blk, float *out)
     if (qtype == ORACLE_F16) {
         for (int j = 0; j < 32; ++j)
             out[j] = fp16_at(blk + 2 * j);
+        return;
+    }
+    if (qtype == ORACLE_IQ4_XS) {
+        decode_iq4_xs_block(blk, out);
         return;
     }
     if (qtype >= ORACLE_Q4_K) {

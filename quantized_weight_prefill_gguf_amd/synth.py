@@ -29,6 +29,10 @@ bytes 0-1):
 * Q6_K (256 weights, 210 B): per 16-weight sub-block a step amax / 31, d the
   largest step over 127 (binary16), sc_j = round(step / d) as int8, and
   q = clamp(round(w / (d sc_j)) + 32, 0, 63).
+* IQ4_XS (256 weights, 136 B): per 32-weight sub-block a step amax / 127, d the
+  largest step over 31 (binary16), the sub-block's 6-bit scale ls = 32 +
+  round(step / d), and each weight's code the index of the nearest of the 16 grid
+  values to w / (d (ls - 32)).
   These encoders are test-input generators, not llama.cpp's quantizers; any valid
   block serves the parity tests. Byte layouts: GGUF's, as the oracle restates them.
 
@@ -36,10 +40,11 @@ numpy's float32 -> float16 cast is IEEE round-to-nearest-even.
 """
 import numpy as np
 
-Q4_0, Q8_0, F16, Q4_K, Q5_K, Q6_K = 0, 1, 2, 3, 4, 5
-BLOCK_BYTES = {Q4_0: 18, Q8_0: 34, F16: 64, Q4_K: 144, Q5_K: 176, Q6_K: 210}
-BLOCK_ELEMS = {Q4_0: 32, Q8_0: 32, F16: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256}
-QTYPE_NAMES = {"q4_0": Q4_0, "q8_0": Q8_0, "f16": F16, "q4_k": Q4_K, "q5_k": Q5_K, "q6_k": Q6_K}
+Q4_0, Q8_0, F16, Q4_K, Q5_K, Q6_K, IQ4_XS = 0, 1, 2, 3, 4, 5, 6
+BLOCK_BYTES = {Q4_0: 18, Q8_0: 34, F16: 64, Q4_K: 144, Q5_K: 176, Q6_K: 210, IQ4_XS: 136}
+BLOCK_ELEMS = {Q4_0: 32, Q8_0: 32, F16: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256, IQ4_XS: 256}
+QTYPE_NAMES = {"q4_0": Q4_0, "q8_0": Q8_0, "f16": F16, "q4_k": Q4_K, "q5_k": Q5_K, "q6_k": Q6_K,
+               "iq4_xs": IQ4_XS}
 
 TENSOR_W, TENSOR_W_UP, TENSOR_W_DOWN, TENSOR_X, TENSOR_R, TENSOR_ROWSCALE = range(6)
 
@@ -224,8 +229,45 @@ def quantize_q6_k(w):
     return out.reshape(-1)
 
 
+# The 16 values an IQ4_XS code selects (GGUF's IQ4_NL grid), in code order.
+_IQ4_GRID = np.array([-127, -104, -83, -65, -49, -35, -22, -10, 1, 13, 25, 38, 53, 69, 89, 113],
+                     np.float32)
+
+
+def quantize_iq4_xs(w):
+    """f32 [rows][k] -> IQ4_XS super-blocks, uint8 [rows * (k/256) * 136]."""
+    w = np.ascontiguousarray(w, np.float32)
+    rows, k = w.shape
+    if k % 256:
+        raise ValueError("k must be a multiple of 256")
+    nsb = k // 256
+    sb = w.reshape(rows, nsb, 8, 32)
+    step = (np.abs(sb).max(axis=3) / np.float32(127)).astype(np.float32)
+    d16 = _fp16_bits(step.max(axis=2) / np.float32(31))
+    d = d16.view(np.float16).astype(np.float32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        m = np.where(d > 0, np.clip(_round_half_away(step / np.where(d > 0, d, 1)), 0, 31), 0)
+    ls = (m + 32).astype(np.uint32)
+    dl = (d * m.astype(np.float32))[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        v = np.where(dl > 0, sb / np.where(dl > 0, dl, 1), 0).astype(np.float32)
+    mids = (_IQ4_GRID[1:] + _IQ4_GRID[:-1]) / 2
+    code = np.searchsorted(mids, v).astype(np.uint8)          # [rows][nsb][8][32]
+    out = np.zeros((rows, nsb, 136), np.uint8)
+    out[..., 0:2] = d16[..., None].view(np.uint8).reshape(rows, nsb, 2)
+    sh = np.zeros((rows, nsb), np.uint32)
+    for b in range(8):
+        sh |= ((ls[..., b] >> 4) & 3) << (2 * b)
+    out[..., 2] = (sh & 0xFF).astype(np.uint8)
+    out[..., 3] = (sh >> 8).astype(np.uint8)
+    for i in range(4):
+        out[..., 4 + i] = ((ls[..., 2 * i] & 15) | ((ls[..., 2 * i + 1] & 15) << 4)).astype(np.uint8)
+    out[..., 8:136] = (code[..., 0:16] | (code[..., 16:32] << 4)).reshape(rows, nsb, 128)
+    return out.reshape(-1)
+
+
 QUANTIZERS = {Q4_0: quantize_q4_0, Q8_0: quantize_q8_0, F16: quantize_f16, Q4_K: quantize_q4_k,
-              Q5_K: quantize_q5_k, Q6_K: quantize_q6_k}
+              Q5_K: quantize_q5_k, Q6_K: quantize_q6_k, IQ4_XS: quantize_iq4_xs}
 
 
 def quantize(qtype, w):
