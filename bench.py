@@ -52,10 +52,10 @@ HIDDEN, INTER = 4096, 12288
 VOCAB = 151936
 LM_UNIQUE_ROWS = 16384  # lm_head weights: this many seeded rows, tiled to VOCAB
 NORM_EPS = 1e-6
-Q4_0, Q8_0, F16W, Q4_K, Q5_K, Q6_K = 0, 1, 2, 3, 4, 5
+Q4_0, Q8_0, F16W, Q4_K, Q5_K, Q6_K, IQ4_XS = 0, 1, 2, 3, 4, 5, 6
 PLAIN, RESIDUAL, SWIGLU = 0, 1, 2
-BLOCK = {Q4_0: 18, Q8_0: 34, F16W: 64, Q4_K: 144, Q5_K: 176, Q6_K: 210}
-BLOCK_ELEMS = {Q4_0: 32, Q8_0: 32, F16W: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256}
+BLOCK = {Q4_0: 18, Q8_0: 34, F16W: 64, Q4_K: 144, Q5_K: 176, Q6_K: 210, IQ4_XS: 136}
+BLOCK_ELEMS = {Q4_0: 32, Q8_0: 32, F16W: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256, IQ4_XS: 256}
 
 
 def weight_bytes(qtype, rows, k):
@@ -124,7 +124,10 @@ def workloads():
         "plain_q4_0_4096_T2048_f16": (2048, 1, [("plain_q4_0", Q4_0, HIDDEN, HIDDEN, PLAIN, "x", "out")], 1),
         # the small-T sweep: Q4_0 and Q8_0 at T in {1, 2, 4, 8} on both projection shapes
         **gemv_sweep(),
-        # the further weight types (the same projections with F16 / Q4_K / Q6_K weights)
+        # the further weight types (the same projections with F16 / Q4_K / Q6_K / IQ4_XS
+        # weights)
+        "gate_up_iq4_xs_T512_f16": (512, 1, [("gate_up_swiglu_iq4_xs", IQ4_XS, INTER, HIDDEN, SWIGLU, "x", "act")], 1),
+        "gemv_iq4_xs_12288x4096_T1": (1, 0, [("gemv_iq4_xs", IQ4_XS, INTER, HIDDEN, PLAIN, "x", "out")], 1),
         "gate_up_q4_k_T512_f16": (512, 1, [("gate_up_swiglu_q4_k", Q4_K, INTER, HIDDEN, SWIGLU, "x", "act")], 1),
         "gate_up_q4_k_T512_f32": (512, 0, [("gate_up_swiglu_q4_k", Q4_K, INTER, HIDDEN, SWIGLU, "x", "act")], 1),
         "gate_up_f16w_T512_f16": (512, 1, [("gate_up_swiglu_f16w", F16W, INTER, HIDDEN, SWIGLU, "x", "act")], 1),

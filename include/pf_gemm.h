@@ -42,6 +42,12 @@
  *    = e/128, c = e%128/32, l = e%32) takes the low (c < 2) or high nibble of ql[64h
  *    + l + 32 (c%2)] and bits 2c, 2c+1 of qh[32h + l]; value (d sc[8h + l/16 + 2c]) *
  *    (q - 32).
+ *  - IQ4_XS, 136 bytes per 256: fp16 d, uint16 scales_h, 4 bytes scales_l, 128 bytes
+ *    of codes; sub-block b = e/32 has the 6-bit scale ls (low 4 bits: nibble b%2 of
+ *    scales_l[b/2]; top 2: bits 2b, 2b+1 of scales_h); element e takes the low (e%32 <
+ *    16) or high nibble of qs[16b + e%16] as its code; value (d (ls - 32)) *
+ *    grid[code], grid = {-127, -104, -83, -65, -49, -35, -22, -10, 1, 13, 25, 38, 53,
+ *    69, 89, 113} (GGUF's IQ4_NL values).
  *  Block b of weight row r starts at byte (r * (k/E) + b) * block_bytes, E = 32 or
  *  256 weights per block.
  *
@@ -64,9 +70,9 @@
 extern "C" {
 #endif
 
-/* Block types. F16 .. Q6_K run their own kernels on both legs and need no workspace
- * on any path; pf_prepare_x and pf_gemm_prepared take Q4_0 and Q8_0 only. */
-enum { PF_Q4_0 = 0, PF_Q8_0 = 1, PF_F16 = 2, PF_Q4_K = 3, PF_Q5_K = 4, PF_Q6_K = 5 };
+/* Block types. F16 .. IQ4_XS run their own kernels on both legs and need no
+ * workspace on any path; pf_prepare_x and pf_gemm_prepared take Q4_0 and Q8_0 only. */
+enum { PF_Q4_0 = 0, PF_Q8_0 = 1, PF_F16 = 2, PF_Q4_K = 3, PF_Q5_K = 4, PF_Q6_K = 5, PF_IQ4_XS = 6 };
 
 /* Epilogues.
  *  PF_PLAIN          Y = X . W_hat^T                      (W has n rows; Y overwritten)

@@ -10,7 +10,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpfgemm.so")
 
-PF_Q4_0, PF_Q8_0, PF_F16, PF_Q4_K, PF_Q5_K, PF_Q6_K = 0, 1, 2, 3, 4, 5
+PF_Q4_0, PF_Q8_0, PF_F16, PF_Q4_K, PF_Q5_K, PF_Q6_K, PF_IQ4_XS = 0, 1, 2, 3, 4, 5, 6
 PF_PLAIN, PF_RESIDUAL, PF_GATE_UP_SWIGLU = 0, 1, 2
 PF_LEG_F32, PF_LEG_F16 = 0, 1
 PF_PATH_AUTO, PF_PATH_GEMM, PF_PATH_GEMV = 0, 1, 2
@@ -19,10 +19,12 @@ PF_GEMV_MAX_T = 8
  PF_E_ALIAS, PF_E_LAUNCH, PF_E_PATH, PF_E_WORKSPACE, PF_E_SCRATCH) = range(12)
 PF_NOALLOC_SCRATCH_BYTES = 64 << 20
 
-BLOCK_BYTES = {PF_Q4_0: 18, PF_Q8_0: 34, PF_F16: 64, PF_Q4_K: 144, PF_Q5_K: 176, PF_Q6_K: 210}
-BLOCK_ELEMS = {PF_Q4_0: 32, PF_Q8_0: 32, PF_F16: 32, PF_Q4_K: 256, PF_Q5_K: 256, PF_Q6_K: 256}
+BLOCK_BYTES = {PF_Q4_0: 18, PF_Q8_0: 34, PF_F16: 64, PF_Q4_K: 144, PF_Q5_K: 176, PF_Q6_K: 210,
+               PF_IQ4_XS: 136}
+BLOCK_ELEMS = {PF_Q4_0: 32, PF_Q8_0: 32, PF_F16: 32, PF_Q4_K: 256, PF_Q5_K: 256, PF_Q6_K: 256,
+               PF_IQ4_XS: 256}
 QTYPES = {"q4_0": PF_Q4_0, "q8_0": PF_Q8_0, "f16": PF_F16, "q4_k": PF_Q4_K, "q5_k": PF_Q5_K,
-          "q6_k": PF_Q6_K}
+          "q6_k": PF_Q6_K, "iq4_xs": PF_IQ4_XS}
 EPILOGUES = {"plain": PF_PLAIN, "residual": PF_RESIDUAL, "swiglu": PF_GATE_UP_SWIGLU}
 LEGS = {"f32": PF_LEG_F32, "f16": PF_LEG_F16}
 

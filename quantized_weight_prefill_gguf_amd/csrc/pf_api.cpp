@@ -26,13 +26,14 @@ int block_bytes(int qtype) {
     case PF_Q4_K: return 144;
     case PF_Q5_K: return 176;
     case PF_Q6_K: return 210;
+    case PF_IQ4_XS: return 136;
     default: return -1;
     }
 }
-int block_elems(int qtype) { return (qtype == PF_Q4_K || qtype == PF_Q5_K || qtype == PF_Q6_K) ? 256 : 32; }
-// The further types (F16, Q4_K, Q5_K, Q6_K) run their own kernels (pf_xq.hip), with no
+int block_elems(int qtype) { return (qtype >= PF_Q4_K && qtype <= PF_IQ4_XS) ? 256 : 32; }
+// The further types (F16, Q4_K, Q5_K, Q6_K, IQ4_XS) run their own kernels (pf_xq.hip), with no
 // workspace on any path.
-bool is_xq(int qtype) { return qtype >= PF_F16 && qtype <= PF_Q6_K; }
+bool is_xq(int qtype) { return qtype >= PF_F16 && qtype <= PF_IQ4_XS; }
 int64_t w_bytes_of(int qtype, int64_t rows, int64_t k) { return rows * (k / block_elems(qtype)) * block_bytes(qtype); }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

@@ -55,10 +55,10 @@ hipError_t launch_gemv_mfma(const GemmArgs &a, hipStream_t s);
 // and its address on the device of stream s (taken once per device, then cached).
 constexpr int64_t kNoallocScratchBytes = int64_t(64) << 20;
 hipError_t noalloc_scratch(hipStream_t s, void **ptr);
-// The further weight types (ids as the C ABI's PF_F16 .. PF_Q6_K), pf_xq.hip: the
+// The further weight types (ids as the C ABI's PF_F16 .. PF_IQ4_XS), pf_xq.hip: the
 // GEMV (T <= 8, f32), the tiled GEMM on either leg (leg16: binary16 operands), and
 // the block decode to f32 or binary16 bits. No workspace.
-enum { XQ_F16 = 2, XQ_Q4_K = 3, XQ_Q5_K = 4, XQ_Q6_K = 5 };
+enum { XQ_F16 = 2, XQ_Q4_K = 3, XQ_Q5_K = 4, XQ_Q6_K = 5, XQ_IQ4_XS = 6 };
 hipError_t launch_xq_gemv(const GemmArgs &a, hipStream_t s);
 hipError_t launch_xq_gemm(const GemmArgs &a, bool leg16, hipStream_t s);
 hipError_t launch_xq_dequant(int qtype, const uint8_t *W, int rows, int k, void *out, bool f16_out,

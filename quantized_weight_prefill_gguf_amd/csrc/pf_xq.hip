@@ -1,8 +1,9 @@
-// The further weight types of the f32 and f16 legs: F16, Q4_K, Q5_K and Q6_K, the
-// types the page "aprender-serve 0.70.2 - src/cuda/executor/gdn_prefill_ops.rs"
+// The further weight types of the f32 and f16 legs: F16, Q4_K, Q5_K, Q6_K and IQ4_XS,
+// the types the page "aprender-serve 0.70.2 - src/cuda/executor/gdn_prefill_ops.rs"
 // dequantizes besides Q8_0 (`qwen35_dequant_f32`: F16 over 32-element groups, the K
-// types over 256-element super-blocks; `qwen35_fp16_weight`: the f16 leg's weight is
-// that f32 value rounded to binary16). The pages print no layout; these are GGUF's:
+// types and IQ4_XS over 256-element super-blocks; `qwen35_fp16_weight`: the f16 leg's
+// weight is that f32 value rounded to binary16). The pages print no layout; these are
+// GGUF's:
 //
 //  F16   64 bytes per 32 weights: little-endian binary16 values.
 //  Q4_K  144 bytes per 256: fp16 d, fp16 dmin, 12 bytes of 6-bit scales s_j and mins
@@ -15,11 +16,18 @@
 //        128, quarter c = (e % 128) / 32, l = e % 32; low 4 bits from ql[64h + l + 32
 //        (c % 2)] (low nibble for c < 2, high for c >= 2), top 2 from bits 2c, 2c+1 of
 //        qh[32h + l]; value (d sc[8h + l/16 + 2c]) (q - 32).
+//  IQ4_XS 136 bytes per 256: fp16 d, uint16 scales_h, 4 bytes scales_l, 128 bytes of
+//        codes. Sub-block b = e / 32 has the 6-bit scale ls whose low 4 bits are
+//        nibble b % 2 of scales_l[b / 2] and whose top 2 are bits 2b, 2b+1 of
+//        scales_h; element e, l = e % 32, takes the low (l < 16) or high nibble of
+//        qs[16 b + l % 16] as its code; value (d (ls - 32)) grid[code], with GGUF's
+//        16-value grid (the IQ4_NL one).
 //
 // The decode is exact in f32 as these definitions give it: d s_j, dmin m_j and
 // (d s_j) q are exact, so the Q4_K / Q5_K value has the one rounding of the
 // subtraction (an FMA gives the same bits); Q6_K's d sc is exact and the product with
-// q - 32 rounds once. The f16 leg rounds that f32 value to binary16 (RNE).
+// q - 32 rounds once; IQ4_XS's d (ls - 32) and its product with a grid value (11 + 6 +
+// 7 significant bits) are exact. The f16 leg rounds that f32 value to binary16 (RNE).
 //
 // Kernels (no workspace; nothing splits, one writer per output):
 //  - xq_dequant_kernel: one 16-weight run per thread, f32 or binary16 out.
@@ -52,6 +60,27 @@ template <> struct XqTraits<XQ_Q5_K> {
 template <> struct XqTraits<XQ_Q6_K> {
     static constexpr int ELEMS = 256, BYTES = 210;
 };
+template <> struct XqTraits<XQ_IQ4_XS> {
+    static constexpr int ELEMS = 256, BYTES = 136;
+};
+
+// IQ4_XS's grid as int8 bytes, code order, little-endian in four words: byte c of the
+// 16 is the value of code c.
+constexpr uint32_t IQ4_GRID_B0 = 0x81u | (0x98u << 8) | (0xADu << 16) | (0xBFu << 24);  // -127 -104 -83 -65
+constexpr uint32_t IQ4_GRID_B1 = 0xCFu | (0xDDu << 8) | (0xEAu << 16) | (0xF6u << 24);  // -49 -35 -22 -10
+constexpr uint32_t IQ4_GRID_B2 = 0x01u | (0x0Du << 8) | (0x19u << 16) | (0x26u << 24);  // 1 13 25 38
+constexpr uint32_t IQ4_GRID_B3 = 0x35u | (0x45u << 8) | (0x59u << 16) | (0x71u << 24);  // 53 69 89 113
+
+// Four codes (one per byte, each 0..15) -> their grid bytes. v_perm_b32
+// picks bytes 0..3 of its second source and 4..7 of its first: the low three bits
+// of a code select within codes 0..7 or 8..15, bit 3 chooses between the two picks.
+__device__ __forceinline__ uint32_t iq4_grid_bytes(uint32_t codes) {
+    const uint32_t sel = codes & 0x07070707u;
+    const uint32_t lo = __builtin_amdgcn_perm(IQ4_GRID_B1, IQ4_GRID_B0, sel);
+    const uint32_t hi = __builtin_amdgcn_perm(IQ4_GRID_B3, IQ4_GRID_B2, sel);
+    const uint32_t m = ((codes >> 3) & 0x01010101u) * 0xFFu;
+    return (lo & ~m) | (hi & m);
+}
 
 __device__ __forceinline__ uint32_t byte_of(const u4_t &v, int i) {
     return (v[i >> 2] >> (8 * (i & 3))) & 0xFFu;
@@ -87,6 +116,10 @@ template <> struct Raw16<XQ_Q6_K> {
     uint32_t ql[8], qh[8];  // halfwords of ql and qh (210-byte blocks are 2-byte aligned)
     uint32_t sc, d;        // the halfword holding the scale byte; d
 };
+template <> struct Raw16<XQ_IQ4_XS> {
+    u2_t hdr;              // d, scales_h, scales_l (136-byte blocks are 8-byte aligned)
+    u2_t qa, qb;           // the 16 code bytes of the sub-block
+};
 
 template <int QT>
 __device__ __forceinline__ void load_raw16(const uint8_t *__restrict__ blk, int e0, Raw16<QT> &r) {
@@ -101,6 +134,11 @@ __device__ __forceinline__ void load_raw16(const uint8_t *__restrict__ blk, int 
         r.hdr = *reinterpret_cast<const u4_t *>(blk);
         r.qs = *reinterpret_cast<const u4_t *>(blk + QS + 32 * p + l0);
         if constexpr (QT == XQ_Q5_K) r.qh = *reinterpret_cast<const u4_t *>(blk + 16 + l0);
+    } else if constexpr (QT == XQ_IQ4_XS) {
+        const int b = e0 >> 5;
+        r.hdr = *reinterpret_cast<const u2_t *>(blk);
+        r.qa = *reinterpret_cast<const u2_t *>(blk + 8 + 16 * b);
+        r.qb = *reinterpret_cast<const u2_t *>(blk + 16 + 16 * b);
     } else {
         const int h = e0 >> 7, c = (e0 & 127) >> 5, l0 = e0 & 31;
         const uint16_t *ql = reinterpret_cast<const uint16_t *>(blk + 64 * h + l0 + 32 * (c & 1));
@@ -144,6 +182,22 @@ __device__ __forceinline__ void decode_raw16(const Raw16<QT> &r, int e0, float (
             uint32_t q = upper ? (byte >> 4) : (byte & 15u);
             if constexpr (QT == XQ_Q5_K) q += ((byte_of(r.qh, i) >> j) & 1u) << 4;
             w[i] = a * (float)q - b;
+        }
+    } else if constexpr (QT == XQ_IQ4_XS) {
+        const int b = e0 >> 5;
+        const bool upper = (e0 & 16) != 0;
+        const uint32_t sl = (r.hdr[1] >> (8 * (b >> 1))) & 0xFFu;
+        const uint32_t ls = ((sl >> (4 * (b & 1))) & 15u) | (((r.hdr[0] >> (16 + 2 * b)) & 3u) << 4);
+        const float dl = fp16_bits_to_f32(r.hdr[0] & 0xFFFFu) * (float)((int)ls - 32);
+        const uint32_t q[4] = {r.qa[0], r.qa[1], r.qb[0], r.qb[1]};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t codes = upper ? (q[j] >> 4) & 0x0F0F0F0Fu : q[j] & 0x0F0F0F0Fu;
+            const uint32_t g = iq4_grid_bytes(codes);
+            // the grid value (a signed byte, converted exactly), then one product:
+            // a zero scale keeps the sign the definition gives (dl * value)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) w[4 * j + c] = dl * (float)(int8_t)(uint8_t)(g >> (8 * c));
         }
     } else {
         const int h = e0 >> 7, c = (e0 & 127) >> 5, l0 = e0 & 31;
@@ -531,7 +585,8 @@ hipError_t launch_dequant_t(int qtype, const uint8_t *W, int rows, int k, void *
     case XQ_F16: return launch_dequant_q<XQ_F16, F16OUT>(W, rows, k, out, s);
     case XQ_Q4_K: return launch_dequant_q<XQ_Q4_K, F16OUT>(W, rows, k, out, s);
     case XQ_Q5_K: return launch_dequant_q<XQ_Q5_K, F16OUT>(W, rows, k, out, s);
-    default: return launch_dequant_q<XQ_Q6_K, F16OUT>(W, rows, k, out, s);
+    case XQ_Q6_K: return launch_dequant_q<XQ_Q6_K, F16OUT>(W, rows, k, out, s);
+    default: return launch_dequant_q<XQ_IQ4_XS, F16OUT>(W, rows, k, out, s);
     }
 }
 
@@ -542,7 +597,8 @@ hipError_t launch_xq_gemv(const GemmArgs &a, hipStream_t s) {
     case XQ_F16: return launch_gemv_q<XQ_F16>(a, s);
     case XQ_Q4_K: return launch_gemv_q<XQ_Q4_K>(a, s);
     case XQ_Q5_K: return launch_gemv_q<XQ_Q5_K>(a, s);
-    default: return launch_gemv_q<XQ_Q6_K>(a, s);
+    case XQ_Q6_K: return launch_gemv_q<XQ_Q6_K>(a, s);
+    default: return launch_gemv_q<XQ_IQ4_XS>(a, s);
     }
 }
 
@@ -551,7 +607,8 @@ hipError_t launch_xq_gemm(const GemmArgs &a, bool leg16, hipStream_t s) {
     case XQ_F16: return leg16 ? launch_gemm_q<XQ_F16, true>(a, s) : launch_gemm_q<XQ_F16, false>(a, s);
     case XQ_Q4_K: return leg16 ? launch_gemm_q<XQ_Q4_K, true>(a, s) : launch_gemm_q<XQ_Q4_K, false>(a, s);
     case XQ_Q5_K: return leg16 ? launch_gemm_q<XQ_Q5_K, true>(a, s) : launch_gemm_q<XQ_Q5_K, false>(a, s);
-    default: return leg16 ? launch_gemm_q<XQ_Q6_K, true>(a, s) : launch_gemm_q<XQ_Q6_K, false>(a, s);
+    case XQ_Q6_K: return leg16 ? launch_gemm_q<XQ_Q6_K, true>(a, s) : launch_gemm_q<XQ_Q6_K, false>(a, s);
+    default: return leg16 ? launch_gemm_q<XQ_IQ4_XS, true>(a, s) : launch_gemm_q<XQ_IQ4_XS, false>(a, s);
     }
 }
 

@@ -57,6 +57,8 @@ def test_weight_bytes(lib):
     assert lib.pf_weight_bytes(pf.PF_Q8_0, 4096, 12288) == 4096 * 384 * 34
     assert lib.pf_weight_bytes(pf.PF_Q4_0, 0, 32) == 0
     assert lib.pf_weight_bytes(7, 1, 32) == -pf.PF_E_QTYPE
+    assert lib.pf_weight_bytes(pf.PF_IQ4_XS, 3, 512) == 3 * 2 * 136
+    assert lib.pf_weight_bytes(pf.PF_IQ4_XS, 3, 288) == -pf.PF_E_SHAPE
     assert lib.pf_weight_bytes(pf.PF_Q4_0, 1, 33) == -pf.PF_E_SHAPE
     assert lib.pf_weight_bytes(pf.PF_Q4_0, -1, 32) == -pf.PF_E_SHAPE
     assert lib.pf_weight_bytes(pf.PF_F16, 3, 64) == 3 * 2 * 64
@@ -88,12 +90,12 @@ def test_select_path(lib):
     for T in (9, 16, 512, 2048):
         assert sel(pf.PF_Q8_0, 4096, 12288, T, pf.PF_RESIDUAL, pf.PF_LEG_F16) == pf.PF_PATH_GEMM
     # the further types: the GEMV up to 8 rows on both legs, then the GEMM
-    for qt in (pf.PF_F16, pf.PF_Q4_K, pf.PF_Q5_K, pf.PF_Q6_K):
+    for qt in (pf.PF_F16, pf.PF_Q4_K, pf.PF_Q5_K, pf.PF_Q6_K, pf.PF_IQ4_XS):
         for leg in (pf.PF_LEG_F32, pf.PF_LEG_F16):
             for epi in (pf.PF_PLAIN, pf.PF_GATE_UP_SWIGLU):
                 assert sel(qt, 4096, 4096, 8, epi, leg) == pf.PF_PATH_GEMV
                 assert sel(qt, 4096, 4096, 9, epi, leg) == pf.PF_PATH_GEMM
-    assert sel(6, 1, 256, 1, 0, 0) == -pf.PF_E_QTYPE
+    assert sel(7, 1, 256, 1, 0, 0) == -pf.PF_E_QTYPE
     assert sel(-1, 1, 256, 1, 0, 0) == -pf.PF_E_QTYPE
     assert sel(0, 1, 256, 1, 3, 0) == -pf.PF_E_EPILOGUE
     assert sel(0, 1, 256, 1, 0, 2) == -pf.PF_E_LEG
@@ -109,7 +111,7 @@ def _gemm(lib, qtype=0, W=FAKE, n=64, k=256, X=FAKE + 1 << 32, T=16, Y=FAKE + 2 
 def test_gemm_argument_checks(lib):
     W, X, Y = FAKE, FAKE + (1 << 32), FAKE + (2 << 32)
     g = lambda **kw: _gemm(lib, **{**dict(W=W, X=X, Y=Y), **kw})
-    assert g(qtype=6) == pf.PF_E_QTYPE
+    assert g(qtype=10) == pf.PF_E_QTYPE
     assert g(qtype=-1) == pf.PF_E_QTYPE
     assert g(epi=3) == pf.PF_E_EPILOGUE
     assert g(leg=2) == pf.PF_E_LEG
@@ -184,7 +186,7 @@ def test_workspace_bytes(lib):
     assert wb(pf.PF_Q4_0, 17, 1280, 290, pf.PF_RESIDUAL, pf.PF_LEG_F16) == 320 * 1280 * 2
     assert wb(pf.PF_Q4_0, 4096, 4096, 512, pf.PF_PLAIN, pf.PF_LEG_F32) == 0
     # the further types never take a workspace
-    for qt in (pf.PF_F16, pf.PF_Q4_K, pf.PF_Q5_K, pf.PF_Q6_K):
+    for qt in (pf.PF_F16, pf.PF_Q4_K, pf.PF_Q5_K, pf.PF_Q6_K, pf.PF_IQ4_XS):
         for T in (1, 8, 9, 300, 512):
             for epi in (pf.PF_PLAIN, pf.PF_RESIDUAL, pf.PF_GATE_UP_SWIGLU):
                 assert wb(qt, 4096, 4096, T, epi, pf.PF_LEG_F16) == 0
@@ -199,7 +201,7 @@ def test_workspace_bytes(lib):
     # a single K chunk cannot split: X alone
     assert wb(pf.PF_Q4_0, 64, 256, 40, pf.PF_PLAIN, pf.PF_LEG_F16) == 64 * 256 * 2
     assert wb(pf.PF_Q4_0, 4096, 4096, 0, pf.PF_PLAIN, pf.PF_LEG_F16) == 0
-    assert wb(6, 64, 256, 16, 0, 1) == -pf.PF_E_QTYPE
+    assert wb(7, 64, 256, 16, 0, 1) == -pf.PF_E_QTYPE
     assert wb(0, 64, 300, 16, 0, 1) == -pf.PF_E_SHAPE
     assert wb(0, 64, 256, 16, 0, 5) == -pf.PF_E_LEG
 
@@ -253,7 +255,7 @@ def test_gemm_ex_argument_checks(lib):
     assert g(X=Y + 4 * 80) == pf.PF_E_ALIAS         # X inside the gap after row 0: still Y's span
     assert g(Y=X + T * k * 4 - 16) == pf.PF_E_ALIAS
     assert g(Y=Y + 8) == pf.PF_E_ALIGN
-    assert g(qtype=6) == pf.PF_E_QTYPE
+    assert g(qtype=10) == pf.PF_E_QTYPE
     # f16 leg with a workspace: too small, or NULL with a size, is refused
     need = lib.pf_workspace_bytes(0, n, k, T, 0, pf.PF_LEG_F16)
     assert need == 32 * k * 2
@@ -339,7 +341,7 @@ def test_prepared_argument_checks(lib):
                                        P(kw.get("ws", WS)), kw.get("wsb", xneed), None)
     assert px(qtype=7) == pf.PF_E_QTYPE
     # the further types' GEMM reads f32 X: no prepared form
-    for qt in (pf.PF_F16, pf.PF_Q4_K, pf.PF_Q5_K, pf.PF_Q6_K):
+    for qt in (pf.PF_F16, pf.PF_Q4_K, pf.PF_Q5_K, pf.PF_Q6_K, pf.PF_IQ4_XS):
         assert px(qtype=qt) == pf.PF_E_QTYPE
     assert px(k=300) == pf.PF_E_SHAPE
     assert px(T=0) == pf.PF_OK
@@ -368,7 +370,7 @@ def test_dequant_argument_checks(lib):
     P = ctypes.c_void_p
     W, out = P(FAKE), P(FAKE + (1 << 32))
     for fn in (lib.pf_dequant_f32, lib.pf_dequant_f16):
-        assert fn(6, W, 4, 64, out, None) == pf.PF_E_QTYPE
+        assert fn(7, W, 4, 64, out, None) == pf.PF_E_QTYPE
         assert fn(0, W, 0, 64, out, None) == pf.PF_E_SHAPE
         assert fn(0, W, 4, 48, out, None) == pf.PF_E_SHAPE
         assert fn(0, P(0), 4, 64, out, None) == pf.PF_E_NULL
@@ -414,7 +416,7 @@ def test_gemm_noalloc_argument_checks(lib):
     def g(qtype=pf.PF_Q4_0, W=W, n=64, k=256, X=X, T=16, Y=Y, epi=pf.PF_PLAIN, leg=f16):
         return lib.pf_gemm_noalloc(qtype, P(W), n, k, P(X), T, P(Y), epi, leg, None)
 
-    assert g(qtype=6) == pf.PF_E_QTYPE
+    assert g(qtype=10) == pf.PF_E_QTYPE
     assert g(epi=7) == pf.PF_E_EPILOGUE
     assert g(leg=3) == pf.PF_E_LEG
     assert g(k=100) == pf.PF_E_SHAPE

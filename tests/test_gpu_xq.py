@@ -1,4 +1,4 @@
-"""GPU parity of the further weight types (F16, Q4_K, Q5_K, Q6_K) through the C ABI
+"""GPU parity of the further weight types (F16, Q4_K, Q5_K, Q6_K, IQ4_XS) through the C ABI
 against the fp64 CPU oracle: bit-exact decode on both legs (f32, and its binary16
 rounding), and the GEMV (T <= 8) and tiled GEMM on every output of ragged shapes,
 each epilogue, both legs, at the legs' bars. Weights: the synthetic encoders'
@@ -14,8 +14,8 @@ from tests import parity, xq_blocks
 
 pytestmark = pytest.mark.gpu
 
-XQ = [synth.F16, synth.Q4_K, synth.Q5_K, synth.Q6_K]
-NAMES = {synth.F16: "f16", synth.Q4_K: "q4_k", synth.Q5_K: "q5_k", synth.Q6_K: "q6_k"}
+XQ = [synth.F16, synth.Q4_K, synth.Q5_K, synth.Q6_K, synth.IQ4_XS]
+NAMES = {synth.F16: "f16", synth.Q4_K: "q4_k", synth.Q5_K: "q5_k", synth.Q6_K: "q6_k", synth.IQ4_XS: "iq4_xs"}
 PLAIN, RESIDUAL, SWIGLU = oracle.PLAIN, oracle.RESIDUAL, oracle.GATE_UP_SWIGLU
 F32, F16 = 0, 1
 

@@ -1,8 +1,8 @@
-"""Blocks of the further weight types (F16, Q4_K, Q5_K, Q6_K) for parity tests:
-random code bytes under chosen scale fields (input generation only).
+"""Blocks of the further weight types (F16, Q4_K, Q5_K, Q6_K, IQ4_XS) for parity
+tests: random code bytes under chosen scale fields (input generation only).
 
-Any byte pattern is a block of these types, so the codes, 6-bit scales, mins and
-Q6_K's int8 scales are drawn uniformly; the binary16 fields (d, dmin, F16 values)
+Any byte pattern is a block of these types, so the codes, 6-bit scales, mins,
+Q6_K's int8 scales and IQ4_XS's split 6-bit scales are drawn uniformly; the binary16 fields (d, dmin, F16 values)
 come from a list of edge values with both signs (subnormal, normal minimum, one,
 zero) and a magnitude chosen so that on the f16 leg every weight stays finite in
 binary16 (|w| <= 65504; the f16 leg does not define infinite weights).
@@ -21,7 +21,8 @@ def _f16(v):
 
 def weight(qtype, rows, k, seed, top):
     """uint8 blocks; `top` bounds |d| (and |dmin|) so that |w| stays below 65504 on the
-    f16 leg: Q4_K / Q5_K weights reach 63 (31 |d| + |dmin|), Q6_K 128 * 32 |d|."""
+    f16 leg: Q4_K / Q5_K weights reach 63 (31 |d| + |dmin|), Q6_K 128 * 32 |d|,
+    IQ4_XS 32 * 127 |d|."""
     rng = np.random.default_rng([seed, 11, qtype])
     B, E = synth.BLOCK_BYTES[qtype], synth.BLOCK_ELEMS[qtype]
     nb = k // E
@@ -41,6 +42,10 @@ def weight(qtype, rows, k, seed, top):
         d = field()
         W[:, :, 208] = d & 0xFF
         W[:, :, 209] = d >> 8
+    elif qtype == synth.IQ4_XS:
+        d = field()
+        W[:, :, 0] = d & 0xFF
+        W[:, :, 1] = d >> 8
     else:
         d, dm = field(), field()
         W[:, :, 0] = d & 0xFF
@@ -51,5 +56,6 @@ def weight(qtype, rows, k, seed, top):
 
 
 # largest |d| per type for the f16 leg (binary16-finite weights), and a value for the f32 leg
-TOP = {"f16": {synth.F16: 60000.0, synth.Q4_K: 30.0, synth.Q5_K: 30.0, synth.Q6_K: 15.0},
-       "f32": {synth.F16: 60000.0, synth.Q4_K: 60000.0, synth.Q5_K: 60000.0, synth.Q6_K: 60000.0}}
+TOP = {"f16": {synth.F16: 60000.0, synth.Q4_K: 30.0, synth.Q5_K: 30.0, synth.Q6_K: 15.0, synth.IQ4_XS: 15.0},
+       "f32": {synth.F16: 60000.0, synth.Q4_K: 60000.0, synth.Q5_K: 60000.0, synth.Q6_K: 60000.0,
+               synth.IQ4_XS: 60000.0}}
