@@ -445,17 +445,28 @@ def counter_summary(workload, pmc_dir, kt_dir):
 
 def trace_summary(kt_dir):
     """CPU only: per-kernel launch statistics from a rocprofv3 --kernel-trace --stats
-    output directory (its *kernel_stats.csv), in microseconds."""
+    output directory (its *kernel_stats.csv), in microseconds, with the median launch
+    from the per-dispatch trace (*kernel_trace.csv) where it is there: the mean also
+    averages the first, cold launches."""
     import csv
     import glob
     files = glob.glob(os.path.join(kt_dir, "**", "*kernel_stats.csv"), recursive=True)
     if not files:
         raise SystemExit("no kernel_stats.csv under %s" % kt_dir)
-    print("%-52s %8s %12s %12s %12s %10s" % ("kernel", "calls", "avg_us", "min_us", "max_us", "std_us"))
+    durs = {}
+    for tf in glob.glob(os.path.join(kt_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(tf) as fh:
+            for r in csv.DictReader(fh):
+                durs.setdefault(_short_kernel(r["Kernel_Name"]), []).append(
+                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print("%-52s %8s %12s %12s %12s %12s %10s" % ("kernel", "calls", "avg_us", "median_us", "min_us", "max_us",
+                                                   "std_us"))
     with open(files[0]) as fh:
         for r in csv.DictReader(fh):
-            print("%-52s %8d %12.2f %12.2f %12.2f %10.2f" % (
-                _short_kernel(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+            name = _short_kernel(r["Name"])
+            med = median(durs[name]) if name in durs else float("nan")
+            print("%-52s %8d %12.2f %12.2f %12.2f %12.2f %10.2f" % (
+                name, int(r["Calls"]), float(r["AverageNs"]) / 1e3, med,
                 float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["StdDev"]) / 1e3))
 
 
