@@ -213,21 +213,22 @@ __device__ __forceinline__ void pair_accumulate(const uint32_t (&dw)[R][PairTrai
     }
 }
 
-// LDS of the kernel: x of NXS pair steps, then the weight staging of 4 waves.
-template <int QT, int TT, int R, int NXS>
-constexpr int gemv_lds_bytes() { return NXS * TT * 16384 + 4 * R * StepTraits<QT>::ROW_LDS; }
+// LDS of the kernel: x of NXS pair steps, then the weight staging of WV waves.
+template <int QT, int TT, int R, int NXS, int WV>
+constexpr int gemv_lds_bytes() { return NXS * TT * 16384 + WV * R * StepTraits<QT>::ROW_LDS; }
 constexpr int LDS_MAX = 160 * 1024;
 
-// Grid: persistent workgroups of 4 waves. A workgroup takes super-groups sg =
-// blockIdx.x, + gridDim.x, ...; wave w of it owns row group 4 sg + w (R weight
+// Grid: persistent workgroups of WV waves (4, or 16 where x of a long row would
+// otherwise leave few waves per CU). A workgroup takes super-groups sg =
+// blockIdx.x, + gridDim.x, ...; wave w of it owns row group WV sg + w (R weight
 // rows, OUTW outputs).
 // NS >= 1: a row has NS pair steps (k <= 4096 NS) and the x of all of them is
 // staged in LDS once, at the start; the waves then run independently.
-// NS == 0: x of the whole row does not fit. The four waves walk the same
+// NS == 0: x of the whole row does not fit. The waves walk the same
 // (super-group, pair step) items in lockstep and each step's x is restaged, for
 // all of them at once, per item.
-template <int QT, int EPI, int TT, int R, int NS>
-__global__ __launch_bounds__(256) void gemv_kernel(const uint8_t *__restrict__ W,
+template <int QT, int EPI, int TT, int R, int NS, int WV>
+__global__ __launch_bounds__(64 * WV) void gemv_kernel(const uint8_t *__restrict__ W,
                                                    const float *__restrict__ X,
                                                    float *__restrict__ Y, int n, int ldy,
                                                    int k, int ngroups) {
@@ -241,9 +242,12 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t *__restrict__ W
     constexpr bool XPRE = MULTI && TT <= 2;  // next step's x prefetched in registers
     constexpr bool XR = NS == 1 && TT <= 2;  // a lane's x fixed for the run: in registers
     static_assert(NV <= 64, "too many partial sums per lane");
-    static_assert(gemv_lds_bytes<QT, TT, R, NXS>() <= LDS_MAX, "LDS");
+    constexpr int NT = 64 * WV;              // threads
+    constexpr int XC = 1024 / NT;            // x float4 per thread, token and step
+    static_assert(1024 % NT == 0, "x staging");
+    static_assert(gemv_lds_bytes<QT, TT, R, NXS, WV>() <= LDS_MAX, "LDS");
 
-    __shared__ __attribute__((aligned(16))) uint8_t smem[gemv_lds_bytes<QT, TT, R, NXS>()];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[gemv_lds_bytes<QT, TT, R, NXS, WV>()];
     f4_t *xl = reinterpret_cast<f4_t *>(smem);
 
     const int tid = threadIdx.x;
@@ -252,7 +256,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t *__restrict__ W
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     uint8_t *my_lds = smem + NXS * TT * 16384 + wid * (R * ST::ROW_LDS);
 
-    const int nsg = (ngroups + 3) >> 2;
+    const int nsg = (ngroups + WV - 1) / WV;
     if ((int)blockIdx.x >= nsg) return;  // whole workgroup leaves together
     const int npairs = k >> 6;
     const int ipg = (npairs + 63) >> 6;  // pair steps per row
@@ -260,31 +264,31 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t *__restrict__ W
     const size_t row_bytes = (size_t)npairs * ST::PB;
 
     auto row_of = [&](int sg, int r) __attribute__((always_inline)) {
-        const int o = (4 * sg + wid) * OUTW;
+        const int o = (WV * sg + wid) * OUTW;
         if constexpr (EPI == EPI_SWIGLU)
             return (r < R / 2) ? min(o + r, n - 1) : n + min(o + r - R / 2, n - 1);
         else
             return min(o + r, n - 1);
     };
 
-    // x of pair step `step`: thread tid holds float4 j = tid + 256 c of each token's
+    // x of pair step `step`: thread tid holds float4 j = tid + NT c of each token's
     // 1024 (pair j >> 4, float4 j & 15); float4s past the row's end are clamped.
-    auto load_x = [&](int step, f4_t (&xr)[TT][4]) __attribute__((always_inline)) {
+    auto load_x = [&](int step, f4_t (&xr)[TT][XC]) __attribute__((always_inline)) {
         const int np = min(64, npairs - 64 * step);
 #pragma unroll
         for (int t = 0; t < TT; ++t)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int j = min(tid + 256 * c, 16 * np - 1);
+            for (int c = 0; c < XC; ++c) {
+                const int j = min(tid + NT * c, 16 * np - 1);
                 xr[t][c] = *reinterpret_cast<const f4_t *>(X + (size_t)t * k + 4096 * step + 4 * j);
             }
     };
-    auto store_x = [&](const f4_t (&xr)[TT][4], int slot) __attribute__((always_inline)) {
+    auto store_x = [&](const f4_t (&xr)[TT][XC], int slot) __attribute__((always_inline)) {
 #pragma unroll
         for (int t = 0; t < TT; ++t)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int j = tid + 256 * c;
+            for (int c = 0; c < XC; ++c) {
+                const int j = tid + NT * c;
                 xl[slot * TT * 1024 + x_lds_index(t, j & 15, j >> 4)] = xr[t][c];
             }
     };
@@ -353,7 +357,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t *__restrict__ W
             store_x(xr, 0);
         } else {
             (void)xr;
-            f4_t xd[TT][4];
+            f4_t xd[TT][XC];
             load_x(cpi, xd);
             store_x(xd, 0);
         }
@@ -392,7 +396,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t *__restrict__ W
                 y = silu_f32(y) * u;
             }
             const int t = idx / R, r = idx % R;
-            const int o = (4 * csg + wid) * OUTW + r;
+            const int o = (WV * csg + wid) * OUTW + r;
             if (owner && idx < R * TT && r < OUTW && o < n) {
                 float *dst = Y + (size_t)t * ldy + o;
                 if constexpr (EPI == EPI_RESIDUAL)
@@ -405,7 +409,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t *__restrict__ W
     };
 
     u4_t cha[R][ST::NCH], chb[R][ST::NCH];
-    f4_t xra[XPRE ? TT : 1][4], xrb[XPRE ? TT : 1][4];
+    f4_t xra[XPRE ? TT : 1][XC], xrb[XPRE ? TT : 1][XC];
     uint32_t dw[R][PT::DW];
     load_next(cha, xra);  // the first weights are on their way while x is staged
     if constexpr (!MULTI) {
@@ -414,7 +418,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t *__restrict__ W
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
             if (st < ipg) {
-                f4_t xd[TT][4];
+                f4_t xd[TT][XC];
                 load_x(st, xd);
                 store_x(xd, st);
             }
@@ -485,26 +489,30 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t *__restrict__ W
     }
 }
 
-// Workgroups of kernel `kern` (256 threads) that fit on one CU at once.
+// Workgroups of kernel `kern` (`threads` threads) that fit on one CU at once.
 template <typename K>
-int resident_blocks_per_cu(K kern) {
+int resident_blocks_per_cu(K kern, int threads) {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, 256, 0) != hipSuccess || nb < 1) nb = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, threads, 0) != hipSuccess || nb < 1) nb = 1;
     return nb;
 }
 
-template <int QT, int EPI, int TT, int R, int NS>
+template <int QT, int EPI, int TT, int R, int NS, int WV>
 hipError_t launch_m(const GemmArgs &a, int ngroups, hipStream_t s) {
-    auto kern = gemv_kernel<QT, EPI, TT, R, NS>;
-    static const int per_cu = resident_blocks_per_cu(kern);
+    auto kern = gemv_kernel<QT, EPI, TT, R, NS, WV>;
+    static const int per_cu = resident_blocks_per_cu(kern, 64 * WV);
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
         cus = 256;
-    // Persistent workgroups: one resident round, each streaming one or more
-    // super-groups.
-    const int blocks = min((ngroups + 15) / 16, per_cu * cus);
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, s, a.W, a.X, a.Y, a.n, a.ldy, a.k, ngroups);
+    // Persistent workgroups: one resident round. With four waves each workgroup
+    // streams two or more super-groups (x is staged once per workgroup; four per
+    // workgroup left the 4096-row weights one workgroup per CU: Q8_0 4096 x 12288 at
+    // T = 1 16.2 -> 14.2 us with two, Q4_0 4096 x 12288 13.8 -> 11.4). With sixteen,
+    // one or more.
+    constexpr int SG_PER_WG = WV == 4 ? 2 : 1;
+    const int blocks = min((ngroups + SG_PER_WG * WV - 1) / (SG_PER_WG * WV), per_cu * cus);
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * WV), 0, s, a.W, a.X, a.Y, a.n, a.ldy, a.k, ngroups);
     return hipGetLastError();
 }
 
@@ -512,18 +520,26 @@ template <int QT, int EPI, int TT, int R>
 hipError_t launch_r(const GemmArgs &a, hipStream_t s) {
     constexpr int OUTW = (EPI == EPI_SWIGLU) ? R / 2 : R;
     const int ngroups = (a.n + OUTW - 1) / OUTW;
-    // Stage x of the whole row once when it fits beside the weight staging.
+    // Stage x of the whole row once when it fits beside the weight staging. Rows of
+    // two or three steps stage 32 or 48 KB of x per token: sixteen waves share it
+    // where that fits, so that more waves per CU keep weight loads in flight.
     const int steps = (a.k + 4095) / 4096;
-    constexpr bool F1 = gemv_lds_bytes<QT, TT, R, 1>() <= LDS_MAX;
-    constexpr bool F2 = gemv_lds_bytes<QT, TT, R, 2>() <= LDS_MAX;
-    constexpr bool F3 = gemv_lds_bytes<QT, TT, R, 3>() <= LDS_MAX;
+    constexpr bool F1 = gemv_lds_bytes<QT, TT, R, 1, 4>() <= LDS_MAX;
+    constexpr bool F2 = gemv_lds_bytes<QT, TT, R, 2, 4>() <= LDS_MAX;
+    constexpr bool F3 = gemv_lds_bytes<QT, TT, R, 3, 4>() <= LDS_MAX;
+    constexpr bool F2W = gemv_lds_bytes<QT, TT, R, 2, 16>() <= LDS_MAX;
+    constexpr bool F3W = gemv_lds_bytes<QT, TT, R, 3, 16>() <= LDS_MAX;
     if constexpr (F1)
-        if (steps == 1) return launch_m<QT, EPI, TT, R, 1>(a, ngroups, s);
+        if (steps == 1) return launch_m<QT, EPI, TT, R, 1, 4>(a, ngroups, s);
+    if constexpr (F2W)
+        if (steps == 2) return launch_m<QT, EPI, TT, R, 2, 16>(a, ngroups, s);
     if constexpr (F2)
-        if (steps == 2) return launch_m<QT, EPI, TT, R, 2>(a, ngroups, s);
+        if (steps == 2) return launch_m<QT, EPI, TT, R, 2, 4>(a, ngroups, s);
+    if constexpr (F3W)
+        if (steps == 3) return launch_m<QT, EPI, TT, R, 3, 16>(a, ngroups, s);
     if constexpr (F3)
-        if (steps == 3) return launch_m<QT, EPI, TT, R, 3>(a, ngroups, s);
-    return launch_m<QT, EPI, TT, R, 0>(a, ngroups, s);
+        if (steps == 3) return launch_m<QT, EPI, TT, R, 3, 4>(a, ngroups, s);
+    return launch_m<QT, EPI, TT, R, 0, 4>(a, ngroups, s);
 }
 
 // Rows per group: one for PLAIN / RESIDUAL with up to four tokens (x is read
