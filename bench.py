@@ -120,6 +120,10 @@ def workloads():
         "ffn_rmsnorm_T512_f16": (512, 1, [
             ("rmsnorm_gate_up_swiglu_q4_0", Q4_0, INTER, HIDDEN, SWIGLU, "x", "act"), down], 2),
         "gate_up_T512_f32": (512, 0, [gu, down], 1),
+        # the gate/up projection on a few rows (the GEMV twin's SwiGLU form)
+        "gate_up_T4_f32": (4, 0, [gu], 1),
+        "gate_up_T4_f16": (4, 1, [gu], 1),
+        "gate_up_T8_f32": (8, 0, [gu], 1),
         "plain_q4_0_4096_T512_f16": (512, 1, [("plain_q4_0", Q4_0, HIDDEN, HIDDEN, PLAIN, "x", "out")], 1),
         "plain_q4_0_4096_T2048_f16": (2048, 1, [("plain_q4_0", Q4_0, HIDDEN, HIDDEN, PLAIN, "x", "out")], 1),
         # the small-T sweep: Q4_0 and Q8_0 at T in {1, 2, 4, 8} on both projection shapes

@@ -90,8 +90,8 @@ enum { PF_PLAIN = 0, PF_RESIDUAL = 1, PF_GATE_UP_SWIGLU = 2 };
  *              workspace.
  *  Where the GEMV runs (T <= PF_GEMV_MAX_T, see PF_PATH_AUTO) both legs compute in
  *  f32, whose error bound is the f32 leg's and therefore also meets the f16 leg's.
- *  From 3 rows on the f32 leg the Q4_0 / Q8_0 GEMV runs on the fp32 matrix cores
- *  (exact f32 operands, f32 accumulation), below on the vector ALU.
+ *  From 3 rows the Q4_0 / Q8_0 GEMV runs on the fp32 matrix cores (exact f32
+ *  operands, f32 accumulation), below on the vector ALU.
  */
 enum { PF_LEG_F32 = 0, PF_LEG_F16 = 1 };
 

@@ -72,13 +72,15 @@ int auto_path(int qtype, int64_t T, int epilogue, int leg) {
     return PF_PATH_GEMV;
 }
 
-// The Q4_0 / Q8_0 GEMV: on the f32 leg from 3 tokens on the fp32 matrix cores, else
-// on the vector ALU. The vector-ALU form spends an FMA and an LDS read of x per weight
-// and token, which from about 3 tokens costs more than the matrix cores' fixed decode
-// (measured on Q4_0 12288 x 4096: T = 4 20.3 -> 15.7 us, T = 8 38.3 -> 20.6 us; at
-// T = 2 12.5 against 15.0).
+// The Q4_0 / Q8_0 GEMV: from 3 tokens on the fp32 matrix cores, else on the vector
+// ALU (both compute in f32 on either leg). The vector-ALU form spends an FMA and an LDS
+// read of x per weight and token, which from about 3 tokens costs more than the matrix
+// cores' fixed decode (measured on Q4_0 12288 x 4096: T = 4 20.3 -> 15.7 us, T = 8
+// 38.3 -> 20.6 us; at T = 2 12.5 against 15.0). On the f16 leg the GEMV runs up to 4
+// rows, for SwiGLU only (auto_path).
 hipError_t launch_gemv_q(const pf::GemmArgs &a, int leg, hipStream_t s) {
-    return (leg == PF_LEG_F32 && a.T >= 3) ? pf::launch_gemv_mfma(a, s) : pf::launch_gemv(a, s);
+    (void)leg;
+    return a.T >= 3 ? pf::launch_gemv_mfma(a, s) : pf::launch_gemv(a, s);
 }
 
 // Bytes of workspace the f16 leg's GEMM takes (X as binary16, T rounded up to a

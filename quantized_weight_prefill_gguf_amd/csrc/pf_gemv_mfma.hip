@@ -90,8 +90,10 @@ __global__ __launch_bounds__(64 * (CW + 1)) void gemv_mfma_kernel(const uint8_t 
     constexpr int NA = RQ * G < 2 ? 2 : 1;  // accumulator sets: independent MFMA chains
     constexpr int XF4 = 16 * G;             // x float4 the staging wave moves per lane and round
     // Rounds of weights in flight per compute wave: about IN_FLIGHT_CHUNKS 16-byte
-    // loads per lane, from two to four rounds.
-    constexpr int DEPTH = IN_FLIGHT_CHUNKS / ST::NCH < 2 ? 2 : (IN_FLIGHT_CHUNKS / ST::NCH > 4 ? 4 : IN_FLIGHT_CHUNKS / ST::NCH);
+    // loads per lane (three quarters of that with twelve compute waves, whose
+    // registers are scarcer), from two to four rounds.
+    constexpr int FLIGHT = CW == 4 ? IN_FLIGHT_CHUNKS : IN_FLIGHT_CHUNKS * 3 / 4;
+    constexpr int DEPTH = FLIGHT / ST::NCH < 2 ? 2 : (FLIGHT / ST::NCH > 4 ? 4 : FLIGHT / ST::NCH);
     static_assert(EPI != EPI_SWIGLU || RQ % 2 == 0, "SwiGLU pairs gate and up quads");
     static_assert(mgemv_lds_bytes<QT, G, RQ, CW>() <= 160 * 1024, "LDS");
 
@@ -355,16 +357,19 @@ hipError_t launch_mq(const GemmArgs &a, hipStream_t s) {
 template <int QT, int G, int RQ, int CW>
 constexpr bool mgemv_fits() { return mgemv_lds_bytes<QT, G, RQ, CW>() <= 160 * 1024; }
 
-// Waves and row quads per workgroup: twelve compute waves of one quad where that
-// still gives every CU a workgroup (three waves per SIMD cover each other's waits);
-// else four compute waves with two quads each (SwiGLU: four, the gate and up quads
-// of two), or one where two would leave CUs without a workgroup.
+// Waves and row quads per workgroup: twelve compute waves of one quad (SwiGLU: of a
+// gate and an up quad) where that fits in LDS and still gives every CU a workgroup
+// (three waves per SIMD cover each other's waits); else four compute waves with two
+// quads each (SwiGLU: four, the gate and up quads of two), or one where two would
+// leave CUs without a workgroup.
 template <int QT, int EPI, int G>
 hipError_t launch_mg(const GemmArgs &a, hipStream_t s) {
     constexpr int CUS = 256;
     constexpr int PER = (EPI == EPI_SWIGLU ? 2 : 4);  // outputs per wave and row quad
     auto enough = [&](int cw, int rq) { return (a.n + cw * PER * rq - 1) / (cw * PER * rq) >= CUS; };
     if constexpr (EPI == EPI_SWIGLU) {
+        if constexpr (mgemv_fits<QT, G, 2, 12>())
+            if (enough(12, 2)) return launch_mq<QT, EPI, G, 2, 12>(a, s);
         if constexpr (mgemv_fits<QT, G, 4, 4>())
             if (enough(4, 4)) return launch_mq<QT, EPI, G, 4, 4>(a, s);
         return launch_mq<QT, EPI, G, 2, 4>(a, s);
