@@ -27,7 +27,8 @@
 //
 // Loads. A compute wave reads its rows' round segments in coalesced 16-byte chunks
 // into registers, DEPTH rounds ahead; a round's chunks go to the wave's LDS staging
-// (double-buffered) one round before it is computed, and each lane then takes the
+// (double-buffered where that fits, else one buffer rewritten once the wave has read
+// it) one round before it is computed, and each lane then takes the
 // dwords of its pairs from there (a pair is 36 bytes for Q4_0, 68 for Q8_0, 4-byte
 // aligned).
 //
@@ -74,9 +75,14 @@ __device__ __forceinline__ int mx_index(int g, int h, int f, int l) { return ((g
 
 // A workgroup has CW compute waves (4, or 12 where the weight has rows enough to give
 // every CU 12 waves of one quad) and one more wave, index CW, that stages x.
-// LDS: x of two rounds (double-buffered), then two staging buffers per compute wave.
+// LDS: x of two rounds (double-buffered), then one or two weight staging buffers per
+// compute wave (two where they fit).
 template <int QT, int G, int RQ, int CW>
-constexpr int mgemv_lds_bytes() { return 2 * G * 16384 + 2 * CW * MStage<QT, RQ>::BYTES; }
+constexpr int mgemv_staging_buffers() { return 2 * G * 16384 + 2 * CW * MStage<QT, RQ>::BYTES <= 160 * 1024 ? 2 : 1; }
+template <int QT, int G, int RQ, int CW>
+constexpr int mgemv_lds_bytes() {
+    return 2 * G * 16384 + mgemv_staging_buffers<QT, G, RQ, CW>() * CW * MStage<QT, RQ>::BYTES;
+}
 
 __device__ __forceinline__ float ubyte_f32(uint32_t w, int b) { return (float)((w >> (8 * b)) & 0xFFu); }
 
@@ -143,7 +149,8 @@ __global__ __launch_bounds__(64 * (CW + 1)) void gemv_mfma_kernel(const uint8_t 
         return;
     }
 
-    uint8_t *wst = smem + 2 * G * 16384 + wid * (2 * ST::BYTES);  // this wave's two buffers
+    constexpr int NSB = mgemv_staging_buffers<QT, G, RQ, CW>();
+    uint8_t *wst = smem + 2 * G * 16384 + wid * (NSB * ST::BYTES);  // this wave's buffers
     const size_t row_bytes = (size_t)npairs * ST::PB;
 
     // Weight row of local row lr (quad lr / 4, row lr % 4) of this wave; rows past
@@ -213,7 +220,7 @@ __global__ __launch_bounds__(64 * (CW + 1)) void gemv_mfma_kernel(const uint8_t 
 #pragma unroll
             for (int p = 0; p < RQ; ++p) {
                 const uint32_t *src = reinterpret_cast<const uint32_t *>(
-                                          wst + buf * ST::BYTES + (4 * p + q) * (ST::ROW_CHUNKS * 16)) +
+                                          wst + (NSB == 2 ? buf : 0) * ST::BYTES + (4 * p + q) * (ST::ROW_CHUNKS * 16)) +
                                       PT::DW * lb;
 #pragma unroll
                 for (int i = 0; i < PT::DW; ++i) dw[p][i] = src[i];
@@ -298,8 +305,14 @@ __global__ __launch_bounds__(64 * (CW + 1)) void gemv_mfma_kernel(const uint8_t 
             }
         }
         // Round r + 1's weights to the other staging buffer (read last in round r - 1,
-        // before the barrier that ended it); the slot then takes round r + 1 + DEPTH.
-        store_w(ch[(j + 1) % DEPTH], buf ^ 1);
+        // before the barrier that ended it), or with one buffer to the same one once
+        // this wave's reads of it are done; the slot then takes round r + 1 + DEPTH.
+        if constexpr (NSB == 2) {
+            store_w(ch[(j + 1) % DEPTH], buf ^ 1);
+        } else {
+            wave_lds_sync();
+            store_w(ch[(j + 1) % DEPTH], 0);
+        }
         load_w(min(r + 1 + DEPTH, last_round), ch[(j + 1) % DEPTH]);
         __syncthreads();
     }
@@ -354,8 +367,13 @@ hipError_t launch_mq(const GemmArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// A form fits when its LDS does and its registers do: a Q8_0 pair is 17 dwords per
+// quad, so Q8_0 takes at most two quads per wave with four compute waves and one with
+// twelve (more spilled to scratch).
 template <int QT, int G, int RQ, int CW>
-constexpr bool mgemv_fits() { return mgemv_lds_bytes<QT, G, RQ, CW>() <= 160 * 1024; }
+constexpr bool mgemv_fits() {
+    return mgemv_lds_bytes<QT, G, RQ, CW>() <= 160 * 1024 && (QT == Q4_0 || RQ * (CW == 12 ? 2 : 1) <= 2);
+}
 
 // Waves and row quads per workgroup: twelve compute waves of one quad (SwiGLU: of a
 // gate and an up quad) where that fits in LDS and still gives every CU a workgroup
