@@ -78,6 +78,17 @@ def test_single_partial_round(gpu, qtype, epi):
     _case(gpu, qtype, 37, 256, 6, epi)
 
 
+@pytest.mark.parametrize("k", [3072, 3328, 5120])
+@pytest.mark.parametrize("T", [3, 4])
+@pytest.mark.parametrize("epi", [PLAIN, RESIDUAL])
+@pytest.mark.parametrize("qtype", [Q4_0, Q8_0])
+def test_one_quad_many_rounds(gpu, qtype, epi, T, k):
+    """Four compute waves of one row quad (4081 <= n <= 8160 at up to four tokens) over
+    three, three and a quarter, and five rounds: the weight ring wraps and the last
+    round is full or partial."""
+    _case(gpu, qtype, 4100, k, T, epi)
+
+
 @pytest.mark.parametrize("qtype", [Q4_0, Q8_0])
 def test_bitwise_repeatable(gpu, qtype):
     W, X, R, Y = _case(gpu, qtype, 8200, 1280, 7, RESIDUAL)
