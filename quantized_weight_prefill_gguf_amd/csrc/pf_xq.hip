@@ -113,9 +113,14 @@ template <> struct Raw16<XQ_Q5_K> {
     u4_t hdr, qs, qh;      // and the 16 qh bytes of the same l
 };
 template <> struct Raw16<XQ_Q6_K> {
-    uint32_t ql[8], qh[8];  // halfwords of ql and qh (210-byte blocks are 2-byte aligned)
+    // 210-byte blocks are only 2-byte aligned: the 16 ql and 16 qh bytes are read as
+    // five dwords each from the dword boundary at or below them, and `sh` (0 or 2) is
+    // the bytes to skip.
+    u4_t ql, qh;
+    uint32_t ql4, qh4, sh;
     uint32_t sc, d;        // the halfword holding the scale byte; d
 };
+typedef uint32_t u4a4_t __attribute__((ext_vector_type(4), aligned(4)));  // 4-byte aligned
 template <> struct Raw16<XQ_IQ4_XS> {
     u2_t hdr;              // d, scales_h, scales_l (136-byte blocks are 8-byte aligned)
     u2_t qa, qb;           // the 16 code bytes of the sub-block
@@ -141,13 +146,17 @@ __device__ __forceinline__ void load_raw16(const uint8_t *__restrict__ blk, int 
         r.qb = *reinterpret_cast<const u2_t *>(blk + 16 + 16 * b);
     } else {
         const int h = e0 >> 7, c = (e0 & 127) >> 5, l0 = e0 & 31;
-        const uint16_t *ql = reinterpret_cast<const uint16_t *>(blk + 64 * h + l0 + 32 * (c & 1));
-        const uint16_t *qh = reinterpret_cast<const uint16_t *>(blk + 128 + 32 * h + l0);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            r.ql[i] = ql[i];
-            r.qh[i] = qh[i];
-        }
+        // ql and qh offsets are even, so blk + offset is 0 or 2 mod 4 as blk is; the
+        // extra dword ends at block byte 132 (ql) or 196 (qh), inside the block.
+        const uint32_t sh = (uint32_t)(reinterpret_cast<uintptr_t>(blk) & 3);
+        const uint32_t *ql = reinterpret_cast<const uint32_t *>(blk + 64 * h + l0 + 32 * (c & 1) - sh);
+        const uint32_t *qh = reinterpret_cast<const uint32_t *>(blk + 128 + 32 * h + l0 - sh);
+        const u4a4_t a = *reinterpret_cast<const u4a4_t *>(ql), b = *reinterpret_cast<const u4a4_t *>(qh);
+        r.ql = u4_t{a[0], a[1], a[2], a[3]};
+        r.qh = u4_t{b[0], b[1], b[2], b[3]};
+        r.ql4 = ql[4];
+        r.qh4 = qh[4];
+        r.sh = sh;
         const int si = 192 + 8 * h + (l0 >> 4) + 2 * c;
         r.sc = *reinterpret_cast<const uint16_t *>(blk + (si & ~1));
         r.d = *reinterpret_cast<const uint16_t *>(blk + 208);
@@ -204,14 +213,18 @@ __device__ __forceinline__ void decode_raw16(const Raw16<QT> &r, int e0, float (
         const int si = 192 + 8 * h + (l0 >> 4) + 2 * c;
         const int sc = (int)(int8_t)(uint8_t)(r.sc >> (8 * (si & 1)));
         const float ds = fp16_bits_to_f32(r.d) * (float)sc;
+        const uint32_t qlw[5] = {r.ql[0], r.ql[1], r.ql[2], r.ql[3], r.ql4};
+        const uint32_t qhw[5] = {r.qh[0], r.qh[1], r.qh[2], r.qh[3], r.qh4};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t lw = __builtin_amdgcn_alignbyte(qlw[i + 1], qlw[i], r.sh);
+            const uint32_t hw = __builtin_amdgcn_alignbyte(qhw[i + 1], qhw[i], r.sh);
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                const uint32_t lb = (r.ql[i] >> (8 * b)) & 0xFFu, hb = (r.qh[i] >> (8 * b)) & 0xFFu;
+            for (int b = 0; b < 4; ++b) {
+                const uint32_t lb = (lw >> (8 * b)) & 0xFFu, hb = (hw >> (8 * b)) & 0xFFu;
                 const uint32_t lo = c < 2 ? (lb & 15u) : (lb >> 4);
                 const int q = (int)(lo | (((hb >> (2 * c)) & 3u) << 4));
-                w[2 * i + b] = ds * (float)(q - 32);
+                w[4 * i + b] = ds * (float)(q - 32);
             }
         }
     }
@@ -348,6 +361,7 @@ typedef float f16v_t __attribute__((ext_vector_type(16)));
 // are loaded first, this step's MFMAs run while they arrive, then the next step is
 // decoded into the other LDS buffer, one barrier.
 constexpr int XNW = 128, XKS = 32;
+constexpr int XPF = 4;  // steps of weight bytes and X in flight per thread
 template <int QT, int EPI, bool LEG16, int MT>
 __global__ __launch_bounds__(256) void xq_gemm_kernel(const uint8_t *__restrict__ W,
                                                       const float *__restrict__ X, float *__restrict__ Y,
@@ -389,19 +403,24 @@ __global__ __launch_bounds__(256) void xq_gemm_kernel(const uint8_t *__restrict_
     const int arow = tid / (XKS / APT), acol = (tid % (XKS / APT)) * APT;
     const float *xrow = X + (size_t)min(m0 + arow, T - 1) * k + acol;
 
-    Raw16<QT> raw;
-    f4_t xv[AF4];
-    auto load_step = [&](int ks) __attribute__((always_inline)) {
-        const int e = ks * XKS + 16 * bhalf;
-        load_raw16<QT>(wrow + (size_t)(e / TR::ELEMS) * TR::BYTES, e % TR::ELEMS, raw);
-        const f4_t *xp = reinterpret_cast<const f4_t *>(xrow + ks * XKS);
+    // Ring of XPF steps' raw weight bytes and X in registers: slot j % XPF holds step j
+    // from XPF steps before its decode. Step indices past the last are clamped, so
+    // every load is issued unconditionally (in-order wait counts then never wait for
+    // a younger load).
+    const int nks = k / XKS;
+    Raw16<QT> raw[XPF];
+    f4_t xv[XPF][AF4];
+    auto load_step = [&](int ks, int slot) __attribute__((always_inline)) {
+        const int e = min(ks, nks - 1) * XKS + 16 * bhalf;
+        load_raw16<QT>(wrow + (size_t)(e / TR::ELEMS) * TR::BYTES, e % TR::ELEMS, raw[slot]);
+        const f4_t *xp = reinterpret_cast<const f4_t *>(xrow + min(ks, nks - 1) * XKS);
 #pragma unroll
-        for (int i = 0; i < AF4; ++i) xv[i] = xp[i];
+        for (int i = 0; i < AF4; ++i) xv[slot][i] = xp[i];
     };
     // Decode, then 16-byte LDS stores (row pitches and offsets are multiples of 16 bytes).
-    auto store_step = [&](int ks, int buf) __attribute__((always_inline)) {
+    auto store_step = [&](int ks, int slot, int buf) __attribute__((always_inline)) {
         float wv[16];
-        decode_raw16<QT>(raw, (ks * XKS + 16 * bhalf) % TR::ELEMS, wv);
+        decode_raw16<QT>(raw[slot], (min(ks, nks - 1) * XKS + 16 * bhalf) % TR::ELEMS, wv);
         op_t *b = Bs + buf * B_ELEMS + brow * PADK + 16 * bhalf;
         op_t *a = As + buf * A_ELEMS + arow * PADK + acol;
         if constexpr (LEG16) {
@@ -414,7 +433,7 @@ __global__ __launch_bounds__(256) void xq_gemm_kernel(const uint8_t *__restrict_
             for (int i = 0; i < AF4 / 2; ++i) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const f4_t &v = xv[2 * i + (j >> 1)];
+                    const f4_t &v = xv[slot][2 * i + (j >> 1)];
                     p[j] = h2_bits(h2_t{(_Float16)v[2 * (j & 1)], (_Float16)v[2 * (j & 1) + 1]});
                 }
                 reinterpret_cast<u4_t *>(a)[i] = u4_t{p[0], p[1], p[2], p[3]};
@@ -424,7 +443,7 @@ __global__ __launch_bounds__(256) void xq_gemm_kernel(const uint8_t *__restrict_
             for (int j = 0; j < 4; ++j)
                 reinterpret_cast<f4_t *>(b)[j] = f4_t{wv[4 * j], wv[4 * j + 1], wv[4 * j + 2], wv[4 * j + 3]};
 #pragma unroll
-            for (int i = 0; i < AF4; ++i) reinterpret_cast<f4_t *>(a)[i] = xv[i];
+            for (int i = 0; i < AF4; ++i) reinterpret_cast<f4_t *>(a)[i] = xv[slot][i];
         }
     };
 
@@ -435,44 +454,54 @@ __global__ __launch_bounds__(256) void xq_gemm_kernel(const uint8_t *__restrict_
         acc[i][1] = f16v_t{};
     }
     const int c = lane & 31, hh = lane >> 5;
-    const int nks = k / XKS;
-    load_step(0);
-    store_step(0, 0);
+#pragma unroll
+    for (int j = 0; j < XPF; ++j) load_step(j, j);
+    store_step(0, 0, 0);
+    load_step(XPF, 0);
     __syncthreads();
-    for (int ks = 0; ks < nks; ++ks) {
+    // Steps are walked in groups of XPF (the ring's slots are indexed statically); a
+    // step past the last only moves data, and every wave reaches every barrier.
+    for (int ks0 = 0; ks0 < nks; ks0 += XPF)
+#pragma unroll
+    for (int jj = 0; jj < XPF; ++jj) {
+        const int ks = ks0 + jj;
         const int buf = ks & 1;
-        if (ks + 1 < nks) load_step(ks + 1);
-        const op_t *a = As + buf * A_ELEMS + (wm * (MT / 2) + c) * PADK;
-        const op_t *b = Bs + buf * B_ELEMS + (wn * 64 + c) * PADK;
-        if constexpr (LEG16) {
+        if (ks < nks) {
+            const op_t *a = As + buf * A_ELEMS + (wm * (MT / 2) + c) * PADK;
+            const op_t *b = Bs + buf * B_ELEMS + (wn * 64 + c) * PADK;
+            if constexpr (LEG16) {
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                h8_t bf[2];
+                for (int s = 0; s < 2; ++s) {
+                    h8_t bf[2];
 #pragma unroll
-                for (int j = 0; j < 2; ++j) bf[j] = *reinterpret_cast<const h8_t *>(b + j * 32 * PADK + 16 * s + 8 * hh);
+                    for (int j = 0; j < 2; ++j) bf[j] = *reinterpret_cast<const h8_t *>(b + j * 32 * PADK + 16 * s + 8 * hh);
 #pragma unroll
-                for (int i = 0; i < IT; ++i) {
-                    const h8_t af = *reinterpret_cast<const h8_t *>(a + i * 32 * PADK + 16 * s + 8 * hh);
+                    for (int i = 0; i < IT; ++i) {
+                        const h8_t af = *reinterpret_cast<const h8_t *>(a + i * 32 * PADK + 16 * s + 8 * hh);
 #pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[j], acc[i][j], 0, 0, 0);
+                        for (int j = 0; j < 2; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[j], acc[i][j], 0, 0, 0);
+                    }
                 }
-            }
-        } else {
+            } else {
 #pragma unroll
-            for (int s = 0; s < XKS / 2; ++s) {
+                for (int s = 0; s < XKS / 2; ++s) {
 #pragma unroll
-                for (int i = 0; i < IT; ++i) {
-                    const float af = a[i * 32 * PADK + 2 * s + hh];
+                    for (int i = 0; i < IT; ++i) {
+                        const float af = a[i * 32 * PADK + 2 * s + hh];
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const float bf = b[j * 32 * PADK + 2 * s + hh];
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af, bf, acc[i][j], 0, 0, 0);
+                        for (int j = 0; j < 2; ++j) {
+                            const float bf = b[j * 32 * PADK + 2 * s + hh];
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af, bf, acc[i][j], 0, 0, 0);
+                        }
                     }
                 }
             }
         }
-        if (ks + 1 < nks) store_step(ks + 1, buf ^ 1);
+        // Step ks + 1 into the other LDS buffer (its last reader finished before the
+        // barrier that ended step ks - 1); its slot then takes step ks + 1 + XPF.
+        store_step(ks + 1, (jj + 1) % XPF, buf ^ 1);
+        load_step(ks + 1 + XPF, (jj + 1) % XPF);
         __syncthreads();
     }
 

@@ -64,6 +64,24 @@ def test_xq_gemm_every_output(gpu, qtype, kind, T, epi, leg):
     assert ok, "parity failed: metric %.3e" % err
 
 
+@pytest.mark.parametrize("leg", [F32, F16])
+@pytest.mark.parametrize("epi", [PLAIN, SWIGLU])
+@pytest.mark.parametrize("qtype", XQ, ids=lambda q: NAMES[q])
+def test_xq_gemm_shortest_k(gpu, qtype, epi, leg):
+    """k = 256, the shortest row the GEMM takes: 8 steps of 32 k, of which the register
+    ring's prologue already loads four."""
+    n, k, T = 70, 256, 140
+    rows = 2 * n if epi == SWIGLU else n
+    seed = 660 + 7 * qtype + epi + leg
+    W = _weights(qtype, rows, k, "edge", leg, seed)
+    X = synth.activations(T, k, workload_id=seed)
+    assert gpu.select_path(qtype, n, k, T, epi, leg) == gpu.PF_PATH_GEMM
+    print("case xq %s k=%d T=%d epi=%d leg=%d" % (NAMES[qtype], k, T, epi, leg), flush=True)
+    Y = parity.run_gpu(gpu, qtype, W, n, k, X, epi, leg)
+    ok, err = parity.check(qtype, W, n, k, X, Y, epi, leg)
+    assert ok, "parity failed: metric %.3e" % err
+
+
 @pytest.mark.parametrize("qtype", XQ, ids=lambda q: NAMES[q])
 def test_xq_forced_families_and_noalloc(gpu, qtype):
     """For T <= 8 the forced GEMM meets the bar too; pf_gemm_ws and pf_gemm_noalloc
