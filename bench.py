@@ -72,7 +72,9 @@ KERNEL_SOURCES = {
 
 def kernel_family(T, leg, qtype=0):
     if qtype not in (Q4_0, Q8_0):
-        return "xq"
+        # F16, Q4_K and Q5_K take the cooperative-decode GEMM through a workspace from
+        # 512 rows on the f16 leg
+        return "gemm_f16" if leg == 1 and T >= 512 and qtype in (F16W, Q4_K, Q5_K) else "xq"
     return "gemv" if T <= 8 else ("gemm_f16" if leg == 1 else "gemm_f32")
 
 
@@ -134,6 +136,7 @@ def workloads():
         "gemv_iq4_xs_12288x4096_T1": (1, 0, [("gemv_iq4_xs", IQ4_XS, INTER, HIDDEN, PLAIN, "x", "out")], 1),
         "gate_up_q4_k_T512_f16": (512, 1, [("gate_up_swiglu_q4_k", Q4_K, INTER, HIDDEN, SWIGLU, "x", "act")], 1),
         "gate_up_q4_k_T512_f32": (512, 0, [("gate_up_swiglu_q4_k", Q4_K, INTER, HIDDEN, SWIGLU, "x", "act")], 1),
+        "gate_up_q5_k_T512_f16": (512, 1, [("gate_up_swiglu_q5_k", Q5_K, INTER, HIDDEN, SWIGLU, "x", "act")], 1),
         "gate_up_f16w_T512_f16": (512, 1, [("gate_up_swiglu_f16w", F16W, INTER, HIDDEN, SWIGLU, "x", "act")], 1),
         "down_q6_k_T512_f16": (512, 1, [("down_residual_q6_k", Q6_K, HIDDEN, INTER, RESIDUAL, "act", "res")], 1),
         "gemv_q4_k_12288x4096_T1": (1, 0, [("gemv_q4_k", Q4_K, INTER, HIDDEN, PLAIN, "x", "out")], 1),

@@ -71,7 +71,11 @@ extern "C" {
 #endif
 
 /* Block types. F16 .. IQ4_XS run their own kernels on both legs and need no
- * workspace on any path; pf_prepare_x and pf_gemm_prepared take Q4_0 and Q8_0 only. */
+ * workspace, except F16, Q4_K and Q5_K from 512 rows on the f16 leg: pf_gemm_ws runs
+ * them on Q4_0's cooperative-decode GEMM, which takes the same workspace as Q4_0 at
+ * those sizes (pf_gemm, and pf_gemm_noalloc where that workspace exceeds the static
+ * scratch, keep their own GEMM). pf_prepare_x and pf_gemm_prepared take Q4_0 and Q8_0
+ * only. */
 enum { PF_Q4_0 = 0, PF_Q8_0 = 1, PF_F16 = 2, PF_Q4_K = 3, PF_Q5_K = 4, PF_Q6_K = 5, PF_IQ4_XS = 6 };
 
 /* Epilogues.
@@ -148,7 +152,8 @@ int pf_gemm_path(int qtype, const void *W_blocks, int64_t n, int64_t k, const fl
 
 /* Workspace bytes pf_gemm_ws needs for these sizes, or -PF_E_* for arguments pf_gemm
  * would refuse. Host-only; touches no GPU state.
- *  - 0 when pf_gemm_ws runs a kernel that needs none (the f32 leg, the GEMV, T == 0);
+ *  - 0 when pf_gemm_ws runs a kernel that needs none (the f32 leg, the GEMV, T == 0,
+ *    the further types' own GEMM);
  *  - the f16 leg's matrix-core GEMM: X_b = ceil(T / 32) * 32 * k * 2 (X rounded to
  *    binary16, T padded to whole 32-row tiles);
  *  - and where that GEMM splits k across S workgroups (PLAIN or RESIDUAL with too few

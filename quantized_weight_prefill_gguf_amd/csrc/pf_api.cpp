@@ -32,7 +32,7 @@ int block_bytes(int qtype) {
 }
 int block_elems(int qtype) { return (qtype >= PF_Q4_K && qtype <= PF_IQ4_XS) ? 256 : 32; }
 // The further types (F16, Q4_K, Q5_K, Q6_K, IQ4_XS) run their own kernels (pf_xq.hip), with no
-// workspace on any path.
+// workspace, except where the f16 leg's workspace GEMM decodes them (pf::f16_coop_takes_xq).
 bool is_xq(int qtype) { return qtype >= PF_F16 && qtype <= PF_IQ4_XS; }
 int64_t w_bytes_of(int qtype, int64_t rows, int64_t k) { return rows * (k / block_elems(qtype)) * block_bytes(qtype); }
 
@@ -87,7 +87,7 @@ hipError_t launch_gemv_q(const pf::GemmArgs &a, int leg, hipStream_t s) {
 // multiple of 32 for the fragment-ordered copy, plus the partial sums of a K split),
 // else 0.
 int64_t ws_need(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int leg, int use) {
-    return (use == PF_PATH_GEMM && leg == PF_LEG_F16 && !is_xq(qtype))
+    return (use == PF_PATH_GEMM && leg == PF_LEG_F16 && (!is_xq(qtype) || pf::f16_coop_takes_xq(qtype, (int)T)))
                ? pf::f16_ws_bytes((int)T, (int)n, (int)k, epilogue)
                : 0;
 }
@@ -112,7 +112,10 @@ int gemm_impl(int qtype, const void *W, int64_t n, int64_t k, const float *X, in
     const int64_t x_bytes = T * k * 4, y_bytes = ((T - 1) * ldy + n) * 4;  // Y's rows and gaps
     if (overlap(Y, y_bytes, X, x_bytes) || overlap(Y, y_bytes, W, w_bytes)) return PF_E_ALIAS;
     const int use = path == PF_PATH_AUTO ? auto_path(qtype, T, epilogue, leg) : path;
-    const int64_t need = ws_mode != WS_NONE ? ws_need(qtype, n, k, T, epilogue, leg, use) : 0;
+    int64_t need = ws_mode != WS_NONE ? ws_need(qtype, n, k, T, epilogue, leg, use) : 0;
+    // A further type whose workspace would not fit the static scratch runs its own GEMM,
+    // which needs none (as it does without a workspace).
+    if (ws_mode == WS_STATIC && is_xq(qtype) && need > pf::kNoallocScratchBytes) need = 0;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (need > 0 && ws_mode == WS_STATIC) {
         // every check is done: the first HIP call of the request
@@ -137,7 +140,7 @@ int gemm_impl(int qtype, const void *W, int64_t n, int64_t k, const float *X, in
     a.k = (int)k;
     a.T = (int)T;
     hipError_t err;
-    if (is_xq(qtype))
+    if (is_xq(qtype) && need == 0)
         err = use == PF_PATH_GEMV ? pf::launch_xq_gemv(a, s) : pf::launch_xq_gemm(a, leg == PF_LEG_F16, s);
     else if (use == PF_PATH_GEMV)
         err = launch_gemv_q(a, leg, s);

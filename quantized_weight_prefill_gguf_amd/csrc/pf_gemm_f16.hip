@@ -46,6 +46,34 @@ template <int QT> struct ChunkTraits {
     static constexpr int ROW = 8 * BB;      // bytes of one row's chunk (144 / 272)
     static constexpr int U4 = ROW / 16;     // 16-byte pieces per row chunk (9 / 17)
 };
+// Further types on the cooperative kernel: a row's 256-k chunk is one super-block
+// (Q4_K 144 bytes, Q5_K 176) or eight F16 groups (512 bytes), every one a whole
+// number of 16-byte pieces, 16-byte aligned. BB (a 32-weight block) has no meaning.
+template <> struct ChunkTraits<XQ_Q4_K> {
+    static constexpr int BB = 0, ROW = 144, U4 = 9;
+};
+template <> struct ChunkTraits<XQ_Q5_K> {
+    static constexpr int BB = 0, ROW = 176, U4 = 11;
+};
+template <> struct ChunkTraits<XQ_F16> {
+    static constexpr int BB = 0, ROW = 512, U4 = 32;
+};
+template <int QT> constexpr bool coop_xq() { return QT == XQ_Q4_K || QT == XQ_Q5_K || QT == XQ_F16; }
+
+// Sub-block j's 6-bit scale and min of a Q4_K / Q5_K super-block header (d, dmin, then
+// the 12 scale bytes): j < 4 take the low 6 bits of bytes j and j + 4; j >= 4 the
+// nibbles of byte j + 4 with the top 2 bits of bytes j - 4 (scale) and j (min).
+template <int J>
+__device__ __forceinline__ void kq_scale_min(const u4_t &hdr, uint32_t &sc, uint32_t &mn) {
+    auto sb = [&](int i) { return (hdr[(4 + i) >> 2] >> (8 * ((4 + i) & 3))) & 0xFFu; };
+    if constexpr (J < 4) {
+        sc = sb(J) & 63u;
+        mn = sb(J + 4) & 63u;
+    } else {
+        sc = (sb(J + 4) & 15u) | ((sb(J - 4) >> 6) << 4);
+        mn = (sb(J + 4) >> 4) | ((sb(J) >> 6) << 4);
+    }
+}
 
 typedef float f16v_t __attribute__((ext_vector_type(16)));
 
@@ -571,6 +599,8 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
                           int ldy, int k, int T, int tiles_m, int tiles_n, int splits) {
     using CT = ChunkTraits<QT>;
     static_assert(MT == 256 || MT == 512, "tile: 256 x 192 or 512 x 96");
+    constexpr bool XQ = coop_xq<QT>();
+    static_assert(!XQ || MT == 512, "further types: 512 x 96 tiles only");
     constexpr int NW = MT == 256 ? 192 : 96;        // weight rows per tile
     constexpr int WN = NW / 96;                     // waves across the weight rows (2 or 1)
     constexpr int BB = CT::BB;                      // 18 / 34
@@ -618,7 +648,7 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
     const int nch = c_end - c_begin;
     if (nch <= 0) return;
     const int nsteps = 8 * nch;
-    const uint32_t row_bytes = (uint32_t)(k >> 5) * BB;
+    const uint32_t row_bytes = XQ ? (uint32_t)(k >> 8) * WROW : (uint32_t)(k >> 5) * BB;
 
     // A fragments: 32-row tile rt, 16-k slice kk at fragment rt * (k / 16) + kk of
     // the workspace (1 KB each; this lane's 16 bytes at 16 lane). Row tiles past
@@ -729,44 +759,88 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
     // two parts so that the LDS reads are issued a phase before the math: read_raw
     // fetches this thread's scales and the dwords holding its qs words; decode_store
     // aligns, decodes and stores them.
+    // Further types (a unit is weights 4 w .. 4 w + 3 of the step's sub-block or group
+    // blk, qraw = sraw + 4 w): Q4_K / Q5_K keep the 16-byte header in hdr, the qs word
+    // in lo and (Q5_K) the qh word in hi; F16 the unit's four binary16 values in hv.
     struct RawWords {
         uint32_t d[NDW], lo[NDW], hi[NDW];
+        u4_t hdr[XQ ? NDW : 1];
+        u2_t hv[XQ ? NDW : 1];
     };
     auto read_raw = [&](int wbuf, auto blk_c, RawWords &rw) __attribute__((always_inline)) {
         constexpr int blk = decltype(blk_c)::value;
-        constexpr int SH = (blk * BB + 2) & 3;       // qs start 2 bytes into a dword for even blocks
-        const uint8_t *wb = wsm0 + wbuf * WBUF + blk * BB;
+        if constexpr (XQ) {
+            const uint8_t *wb = wsm0 + wbuf * WBUF;
 #pragma unroll
-        for (int i = 0; i < NDW; ++i) {
-            rw.d[i] = *reinterpret_cast<const uint16_t *>(wb + sraw[i]);
-            if constexpr (SH == 0) {
-                rw.lo[i] = *reinterpret_cast<const uint32_t *>(wb + qraw[i] + 2);
-            } else {
-                const uint32_t *al = reinterpret_cast<const uint32_t *>(wb + qraw[i]);
-                rw.lo[i] = al[0];
-                rw.hi[i] = al[1];
+            for (int i = 0; i < NDW; ++i) {
+                if constexpr (QT == XQ_F16) {
+                    rw.hv[i] = *reinterpret_cast<const u2_t *>(wb + 2 * qraw[i] - sraw[i] + 64 * blk);
+                } else {
+                    constexpr int QS = QT == XQ_Q5_K ? 48 : 16;  // qs offset in the super-block
+                    rw.hdr[i] = *reinterpret_cast<const u4_t *>(wb + sraw[i]);
+                    rw.lo[i] = *reinterpret_cast<const uint32_t *>(wb + qraw[i] + QS + 32 * (blk >> 1));
+                    if constexpr (QT == XQ_Q5_K) rw.hi[i] = *reinterpret_cast<const uint32_t *>(wb + qraw[i] + 16);
+                }
+            }
+        } else {
+            constexpr int SH = (blk * BB + 2) & 3;   // qs start 2 bytes into a dword for even blocks
+            const uint8_t *wb = wsm0 + wbuf * WBUF + blk * BB;
+#pragma unroll
+            for (int i = 0; i < NDW; ++i) {
+                rw.d[i] = *reinterpret_cast<const uint16_t *>(wb + sraw[i]);
+                if constexpr (SH == 0) {
+                    rw.lo[i] = *reinterpret_cast<const uint32_t *>(wb + qraw[i] + 2);
+                } else {
+                    const uint32_t *al = reinterpret_cast<const uint32_t *>(wb + qraw[i]);
+                    rw.lo[i] = al[0];
+                    rw.hi[i] = al[1];
+                }
             }
         }
     };
     auto decode_store = [&](const RawWords &rw, auto blk_c, auto bbuf_c) __attribute__((always_inline)) {
         constexpr int blk = decltype(blk_c)::value;
-        constexpr int SH = (blk * BB + 2) & 3;
+        constexpr int SH = XQ ? 0 : (blk * BB + 2) & 3;
         uint8_t *bb = bsm + decltype(bbuf_c)::value * BBUF;
         uint32_t qw[NDW];
 #pragma unroll
         for (int i = 0; i < NDW; ++i)
             qw[i] = SH == 0 ? rw.lo[i] : __builtin_amdgcn_alignbyte(rw.hi[i], rw.lo[i], SH);
-        // One unit: 4 weights (Q4_0 nibble half `sh` of word w, or Q8_0 word w) -> 8 bytes.
+        // One unit: 4 weights (Q4_0 nibble half `sh` of word w, or Q8_0 word w, or the
+        // further types' unit) -> 8 bytes.
         auto unit = [&](int i) __attribute__((always_inline)) {
-            const h2_t d2 = as_h2(rw.d[i] | (rw.d[i] << 16));
+            if constexpr (QT == XQ_F16) {
+                // the binary16 weights themselves (the f32 value rounds back to them)
+                *reinterpret_cast<u2_t *>(bb + bdst[i]) = rw.hv[i];
+                return;
+            }
             uint32_t p[2];
-            if constexpr (QT == Q4_0) {
+            if constexpr (XQ) {
+                // Q4_K / Q5_K sub-block blk: (d s) q - dmin m in f32 ((d s) q is exact, so
+                // the FMA rounds once, as the subtraction would), then binary16 (RNE).
+                uint32_t sc, mn;
+                kq_scale_min<blk>(rw.hdr[i], sc, mn);
+                const float a = fp16_bits_to_f32(rw.hdr[i][0] & 0xFFFFu) * (float)sc;
+                const float b = fp16_bits_to_f32(rw.hdr[i][0] >> 16) * (float)mn;
+                uint32_t q = (rw.lo[i] >> (4 * (blk & 1))) & 0x0F0F0F0Fu;
+                if constexpr (QT == XQ_Q5_K) q |= ((rw.hi[i] >> blk) & 0x01010101u) << 4;
+                float w[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    w[c] = fmaf(a, (float)((q >> (8 * c)) & 0xFFu), -b);
+                    // opaque: a fused multiply-add into binary16 would round once, not twice
+                    asm("" : "+v"(w[c]));
+                }
+                p[0] = h2_bits(h2_t{(_Float16)w[0], (_Float16)w[1]});
+                p[1] = h2_bits(h2_t{(_Float16)w[2], (_Float16)w[3]});
+            } else if constexpr (QT == Q4_0) {
+                const h2_t d2 = as_h2(rw.d[i] | (rw.d[i] << 16));
                 const h2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
                 const uint32_t nib = (qw[i] >> nshift[i]) & 0x0F0F0F0Fu;
                 p[0] = h2_bits((as_h2(magic_pair(nib, SEL_B02)) - off) * d2);
                 p[1] = h2_bits((as_h2(magic_pair(nib, SEL_B13)) - off) * d2);
             } else {
-                q8_word_to_h4(qw[i], d2, p);
+                q8_word_to_h4(qw[i], as_h2(rw.d[i] | (rw.d[i] << 16)), p);
             }
             *reinterpret_cast<u2_t *>(bb + bdst[i]) = u2_t{p[0], p[1]};
         };
@@ -1364,6 +1438,10 @@ static int coop_splits(int T, int n, int k, int epilogue) {
     return splits;
 }
 
+bool f16_coop_takes_xq(int qtype, int T) {
+    return T >= COOP_T512 && (qtype == XQ_Q4_K || qtype == XQ_Q5_K || qtype == XQ_F16);
+}
+
 // Byte offset of the partial sums in the workspace, and the floats between splits.
 static int64_t ws_x_bytes(int T, int k) { return ((int64_t)(T + 31) / 32 * 32 * k * 2 + 255) / 256 * 256; }
 static int64_t ws_pstride(int T, int n) { return part_stride(T, n); }
@@ -1487,7 +1565,17 @@ hipError_t launch_prepare_x_f16(const GemmArgs &a, void *workspace, hipStream_t 
 // qtype, k and T); any split-K partial sums (or the SwiGLU scratch G) go behind it.
 hipError_t launch_gemm_f16_prepared(const GemmArgs &a, void *workspace, hipStream_t s) {
     uint16_t *xh = static_cast<uint16_t *>(workspace);
-    if (a.T >= 256) return a.qtype == Q4_0 ? launch_coop_q<Q4_0>(a, xh, s) : launch_coop_q<Q8_0>(a, xh, s);
+    if (a.T >= 256) {
+        switch (a.qtype) {
+        case Q4_0: return launch_coop_q<Q4_0>(a, xh, s);
+        case Q8_0: return launch_coop_q<Q8_0>(a, xh, s);
+        // further types (f16_coop_takes_xq): 512 x 96 tiles only
+        case XQ_Q4_K: return launch_coop_e<XQ_Q4_K, 512>(a, xh, s);
+        case XQ_Q5_K: return launch_coop_e<XQ_Q5_K, 512>(a, xh, s);
+        case XQ_F16: return launch_coop_e<XQ_F16, 512>(a, xh, s);
+        default: return hipErrorInvalidValue;
+        }
+    }
     // split-K partial sums (or the SwiGLU scratch G) go behind the fp16 X
     float *ps = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(workspace) + ws_x_bytes(a.T, a.k));
     if (swiglu_via_scratch(a.T, a.epilogue))

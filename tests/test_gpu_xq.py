@@ -108,6 +108,51 @@ def test_xq_forced_families_and_noalloc(gpu, qtype):
         assert np.array_equal(y0.view(np.uint32), Yd.cpu().numpy().view(np.uint32))
 
 
+COOP = [synth.F16, synth.Q4_K, synth.Q5_K]
+
+
+@pytest.mark.parametrize("epi", [PLAIN, RESIDUAL, SWIGLU])
+@pytest.mark.parametrize("kind", ["synth", "edge"])
+@pytest.mark.parametrize("qtype", COOP, ids=lambda q: NAMES[q])
+def test_xq_coop_every_output(gpu, qtype, kind, epi):
+    """With a workspace on the f16 leg from 512 rows, the cooperative-decode GEMM decodes
+    these types: T = 520 is a full 512-row tile and a ragged one, n = 150 a ragged weight
+    tile; PLAIN and RESIDUAL at k = 2048 split K in two (partial sums, then their fixed-
+    order sum). pf_gemm_noalloc runs the same kernels: same bits."""
+    import torch
+    n, T = 150, 520
+    k = 1024 if epi == SWIGLU else 2048
+    rows = 2 * n if epi == SWIGLU else n
+    seed = 670 + 7 * qtype + 3 * epi + (kind == "edge")
+    W = _weights(qtype, rows, k, kind, F16, seed)
+    X = synth.activations(T, k, workload_id=seed)
+    R = synth.activations(T, n, workload_id=seed, tensor_id=synth.TENSOR_R) if epi == RESIDUAL else None
+    assert gpu.workspace_bytes(qtype, n, k, T, epi, F16) > 0
+    print("case xq coop %s %s epi=%d" % (NAMES[qtype], kind, epi), flush=True)
+    Y = parity.run_gpu(gpu, qtype, W, n, k, X, epi, F16, R=R, workspace=True)
+    ok, err = parity.check(qtype, W, n, k, X, Y, epi, F16, R=R)
+    assert ok, "parity failed: metric %.3e" % err
+    Wd, Xd = parity.to_dev(W), parity.to_dev(X)
+    Yd = parity.to_dev(R) if R is not None else torch.full((T, n), float("nan"), device="cuda")
+    gpu.gemm_noalloc(qtype, Wd, n, k, Xd, Yd, epi, F16)
+    torch.cuda.synchronize()
+    assert np.array_equal(Y.view(np.uint32), Yd.cpu().numpy().view(np.uint32))
+
+
+@pytest.mark.parametrize("qtype", COOP, ids=lambda q: NAMES[q])
+def test_xq_coop_full_size_sampled(gpu, qtype):
+    """The gate/up shape at T = 512 through the workspace (sampled outputs)."""
+    n, k, T = 12288, 4096, 512
+    W = synth.quantize(qtype, np.concatenate([synth.weights_f32(n, k, workload_id=651),
+                                              synth.weights_f32(n, k, workload_id=651,
+                                                                tensor_id=synth.TENSOR_W_UP)]))
+    X = synth.activations(T, k, workload_id=651)
+    print("case xq coop full %s" % NAMES[qtype], flush=True)
+    Y = parity.run_gpu(gpu, qtype, W, n, k, X, SWIGLU, F16, workspace=True)
+    ok, err = parity.check(qtype, W, n, k, X, Y, SWIGLU, F16, samples=4096)
+    assert ok, "parity failed: metric %.3e" % err
+
+
 @pytest.mark.parametrize("qtype", XQ, ids=lambda q: NAMES[q])
 def test_xq_full_size_sampled(gpu, qtype):
     """The gate/up shape at T = 512 on the f16 leg (sampled outputs)."""
