@@ -72,9 +72,9 @@ KERNEL_SOURCES = {
 
 def kernel_family(T, leg, qtype=0):
     if qtype not in (Q4_0, Q8_0):
-        # F16, Q4_K and Q5_K take the cooperative-decode GEMM through a workspace from
-        # 512 rows on the f16 leg
-        return "gemm_f16" if leg == 1 and T >= 512 and qtype in (F16W, Q4_K, Q5_K) else "xq"
+        # F16, Q4_K, Q5_K and IQ4_XS take the cooperative-decode GEMM through a workspace
+        # from 512 rows on the f16 leg
+        return "gemm_f16" if leg == 1 and T >= 512 and qtype in (F16W, Q4_K, Q5_K, IQ4_XS) else "xq"
     return "gemv" if T <= 8 else ("gemm_f16" if leg == 1 else "gemm_f32")
 
 

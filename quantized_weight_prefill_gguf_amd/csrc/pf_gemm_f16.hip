@@ -58,7 +58,18 @@ template <> struct ChunkTraits<XQ_Q5_K> {
 template <> struct ChunkTraits<XQ_F16> {
     static constexpr int BB = 0, ROW = 512, U4 = 32;
 };
-template <int QT> constexpr bool coop_xq() { return QT == XQ_Q4_K || QT == XQ_Q5_K || QT == XQ_F16; }
+// IQ4_XS: 136 bytes per super-block, 8-byte aligned only: staged in 8-byte pieces
+// (U4 counts pieces of PIECE bytes).
+template <> struct ChunkTraits<XQ_IQ4_XS> {
+    static constexpr int BB = 0, ROW = 136, U4 = 17, PIECE = 8;
+};
+template <int QT> constexpr int chunk_piece() {
+    if constexpr (QT == XQ_IQ4_XS) return ChunkTraits<QT>::PIECE;
+    else return 16;
+}
+template <int QT> constexpr bool coop_xq() {
+    return QT == XQ_Q4_K || QT == XQ_Q5_K || QT == XQ_F16 || QT == XQ_IQ4_XS;
+}
 
 // Sub-block j's 6-bit scale and min of a Q4_K / Q5_K super-block header (d, dmin, then
 // the 12 scale bytes): j < 4 take the low 6 bits of bytes j and j + 4; j >= 4 the
@@ -664,19 +675,22 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
 
     // Weight staging: slice S of a chunk = its rows 24 S .. 24 S + 23, whole (216 /
     // 408 16-byte pieces; thread t < 24 U4 copies piece t % U4 of slice row t / U4).
+    // IQ4_XS moves 8-byte pieces (17 per 136-byte row chunk).
     constexpr int RS = NW / 8;
     constexpr int SP = RS * U4;
+    constexpr int PIECE = chunk_piece<QT>();
     static_assert(SP <= 512, "one piece per thread");
+    static_assert(U4 * PIECE == WROW, "whole pieces per row chunk");
     const bool wvalid = tid < SP;
     const int wff = wvalid ? tid : 0;
     const int wrr = wff / U4, wpp = wff % U4;
-    const int wdst = wrr * WROW + 16 * wpp;
+    const int wdst = wrr * WROW + PIECE * wpp;
     uint32_t wsrc[8];
 #pragma unroll
     for (int S = 0; S < 8; ++S) {
         int gr = f16_weight_row<EPI, NW>(tn, S * RS + wrr, n);
         gr = gr < 0 ? 0 : gr;
-        wsrc[S] = (uint32_t)gr * row_bytes + 16 * wpp;
+        wsrc[S] = (uint32_t)gr * row_bytes + PIECE * wpp;
     }
     const uint8_t *wbase = W + (size_t)c_begin * WROW;
 
@@ -748,11 +762,22 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
 
     auto fetch_slice = [&](int chunk, auto s_c, u4_t &dst) __attribute__((always_inline)) {
         constexpr int S = decltype(s_c)::value;
-        dst = *reinterpret_cast<const u4_t *>(wbase + (size_t)min(chunk, nch - 1) * WROW + wsrc[S]);
+        const uint8_t *src = wbase + (size_t)min(chunk, nch - 1) * WROW + wsrc[S];
+        if constexpr (PIECE == 16) {
+            dst = *reinterpret_cast<const u4_t *>(src);
+        } else {
+            const u2_t v = *reinterpret_cast<const u2_t *>(src);
+            dst = u4_t{v[0], v[1], 0u, 0u};
+        }
     };
     auto store_slice = [&](int wbuf, auto s_c, const u4_t &src) __attribute__((always_inline)) {
         constexpr int S = decltype(s_c)::value;
-        if (wvalid) *reinterpret_cast<u4_t *>(wsm0 + wbuf * WBUF + S * RS * WROW + wdst) = src;
+        uint8_t *dst = wsm0 + wbuf * WBUF + S * RS * WROW + wdst;
+        if constexpr (PIECE == 16) {
+            if (wvalid) *reinterpret_cast<u4_t *>(dst) = src;
+        } else {
+            if (wvalid) *reinterpret_cast<u2_t *>(dst) = u2_t{src[0], src[1]};
+        }
     };
 
     // Block `blk` (compile-time) of raw chunk buffer `wbuf` -> B buffer `bbuf`, in
@@ -775,6 +800,12 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
             for (int i = 0; i < NDW; ++i) {
                 if constexpr (QT == XQ_F16) {
                     rw.hv[i] = *reinterpret_cast<const u2_t *>(wb + 2 * qraw[i] - sraw[i] + 64 * blk);
+                } else if constexpr (QT == XQ_IQ4_XS) {
+                    // header (d, scales_h, scales_l); unit w's codes: low nibbles of bytes
+                    // 16 blk + 4 w .. (w < 4) or high nibbles of 16 blk + 4 (w - 4) ..
+                    const int w4 = qraw[i] - sraw[i];
+                    rw.hv[i] = *reinterpret_cast<const u2_t *>(wb + sraw[i]);
+                    rw.lo[i] = *reinterpret_cast<const uint32_t *>(wb + sraw[i] + 8 + 16 * blk + (w4 & 15));
                 } else {
                     constexpr int QS = QT == XQ_Q5_K ? 48 : 16;  // qs offset in the super-block
                     rw.hdr[i] = *reinterpret_cast<const u4_t *>(wb + sraw[i]);
@@ -815,7 +846,22 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
                 return;
             }
             uint32_t p[2];
-            if constexpr (XQ) {
+            if constexpr (QT == XQ_IQ4_XS) {
+                // sub-block blk's 6-bit scale ls (nibble of scales_l, 2 bits of scales_h);
+                // d (ls - 32) and its product with a grid value are exact in f32
+                const uint32_t h0 = rw.hv[i][0], sl = rw.hv[i][1];
+                const uint32_t ls = ((sl >> (4 * blk)) & 15u) | (((h0 >> (16 + 2 * blk)) & 3u) << 4);
+                const float dl = fp16_bits_to_f32(h0 & 0xFFFFu) * (float)((int)ls - 32);
+                const uint32_t g = iq4_grid_bytes((rw.lo[i] >> ((qraw[i] - sraw[i]) >> 2 & 4)) & 0x0F0F0F0Fu);
+                float w[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    w[c] = dl * (float)(int8_t)(uint8_t)(g >> (8 * c));
+                    asm("" : "+v"(w[c]));
+                }
+                p[0] = h2_bits(h2_t{(_Float16)w[0], (_Float16)w[1]});
+                p[1] = h2_bits(h2_t{(_Float16)w[2], (_Float16)w[3]});
+            } else if constexpr (XQ) {
                 // Q4_K / Q5_K sub-block blk: (d s) q - dmin m in f32 ((d s) q is exact, so
                 // the FMA rounds once, as the subtraction would), then binary16 (RNE).
                 uint32_t sc, mn;
@@ -1439,7 +1485,7 @@ static int coop_splits(int T, int n, int k, int epilogue) {
 }
 
 bool f16_coop_takes_xq(int qtype, int T) {
-    return T >= COOP_T512 && (qtype == XQ_Q4_K || qtype == XQ_Q5_K || qtype == XQ_F16);
+    return T >= COOP_T512 && (qtype == XQ_Q4_K || qtype == XQ_Q5_K || qtype == XQ_F16 || qtype == XQ_IQ4_XS);
 }
 
 // Byte offset of the partial sums in the workspace, and the floats between splits.
@@ -1573,6 +1619,7 @@ hipError_t launch_gemm_f16_prepared(const GemmArgs &a, void *workspace, hipStrea
         case XQ_Q4_K: return launch_coop_e<XQ_Q4_K, 512>(a, xh, s);
         case XQ_Q5_K: return launch_coop_e<XQ_Q5_K, 512>(a, xh, s);
         case XQ_F16: return launch_coop_e<XQ_F16, 512>(a, xh, s);
+        case XQ_IQ4_XS: return launch_coop_e<XQ_IQ4_XS, 512>(a, xh, s);
         default: return hipErrorInvalidValue;
         }
     }

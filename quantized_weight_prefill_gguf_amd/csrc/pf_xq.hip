@@ -64,24 +64,6 @@ template <> struct XqTraits<XQ_IQ4_XS> {
     static constexpr int ELEMS = 256, BYTES = 136;
 };
 
-// IQ4_XS's grid as int8 bytes, code order, little-endian in four words: byte c of the
-// 16 is the value of code c.
-constexpr uint32_t IQ4_GRID_B0 = 0x81u | (0x98u << 8) | (0xADu << 16) | (0xBFu << 24);  // -127 -104 -83 -65
-constexpr uint32_t IQ4_GRID_B1 = 0xCFu | (0xDDu << 8) | (0xEAu << 16) | (0xF6u << 24);  // -49 -35 -22 -10
-constexpr uint32_t IQ4_GRID_B2 = 0x01u | (0x0Du << 8) | (0x19u << 16) | (0x26u << 24);  // 1 13 25 38
-constexpr uint32_t IQ4_GRID_B3 = 0x35u | (0x45u << 8) | (0x59u << 16) | (0x71u << 24);  // 53 69 89 113
-
-// Four codes (one per byte, each 0..15) -> their grid bytes. v_perm_b32
-// picks bytes 0..3 of its second source and 4..7 of its first: the low three bits
-// of a code select within codes 0..7 or 8..15, bit 3 chooses between the two picks.
-__device__ __forceinline__ uint32_t iq4_grid_bytes(uint32_t codes) {
-    const uint32_t sel = codes & 0x07070707u;
-    const uint32_t lo = __builtin_amdgcn_perm(IQ4_GRID_B1, IQ4_GRID_B0, sel);
-    const uint32_t hi = __builtin_amdgcn_perm(IQ4_GRID_B3, IQ4_GRID_B2, sel);
-    const uint32_t m = ((codes >> 3) & 0x01010101u) * 0xFFu;
-    return (lo & ~m) | (hi & m);
-}
-
 __device__ __forceinline__ uint32_t byte_of(const u4_t &v, int i) {
     return (v[i >> 2] >> (8 * (i & 3))) & 0xFFu;
 }

@@ -108,7 +108,7 @@ def test_xq_forced_families_and_noalloc(gpu, qtype):
         assert np.array_equal(y0.view(np.uint32), Yd.cpu().numpy().view(np.uint32))
 
 
-COOP = [synth.F16, synth.Q4_K, synth.Q5_K]
+COOP = [synth.F16, synth.Q4_K, synth.Q5_K, synth.IQ4_XS]
 
 
 @pytest.mark.parametrize("epi", [PLAIN, RESIDUAL, SWIGLU])
