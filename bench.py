@@ -72,9 +72,9 @@ KERNEL_SOURCES = {
 
 def kernel_family(T, leg, qtype=0):
     if qtype not in (Q4_0, Q8_0):
-        # F16, Q4_K, Q5_K and IQ4_XS take the cooperative-decode GEMM through a workspace
-        # from 512 rows on the f16 leg
-        return "gemm_f16" if leg == 1 and T >= 512 and qtype in (F16W, Q4_K, Q5_K, IQ4_XS) else "xq"
+        # the further types take the cooperative-decode GEMM through a workspace from 512
+        # rows on the f16 leg (Q6_K with k % 512 == 0, as every workload here has)
+        return "gemm_f16" if leg == 1 and T >= 512 else "xq"
     return "gemv" if T <= 8 else ("gemm_f16" if leg == 1 else "gemm_f32")
 
 

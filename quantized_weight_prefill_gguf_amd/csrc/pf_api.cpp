@@ -87,7 +87,7 @@ hipError_t launch_gemv_q(const pf::GemmArgs &a, int leg, hipStream_t s) {
 // multiple of 32 for the fragment-ordered copy, plus the partial sums of a K split),
 // else 0.
 int64_t ws_need(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int leg, int use) {
-    return (use == PF_PATH_GEMM && leg == PF_LEG_F16 && (!is_xq(qtype) || pf::f16_coop_takes_xq(qtype, (int)T)))
+    return (use == PF_PATH_GEMM && leg == PF_LEG_F16 && (!is_xq(qtype) || pf::f16_coop_takes_xq(qtype, (int)T, (int)k)))
                ? pf::f16_ws_bytes((int)T, (int)n, (int)k, epilogue)
                : 0;
 }

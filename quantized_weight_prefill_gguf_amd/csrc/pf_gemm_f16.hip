@@ -63,13 +63,27 @@ template <> struct ChunkTraits<XQ_F16> {
 template <> struct ChunkTraits<XQ_IQ4_XS> {
     static constexpr int BB = 0, ROW = 136, U4 = 17, PIECE = 8;
 };
+// Q6_K: 210 bytes per super-block, 2-byte aligned. With rows a multiple of 4 bytes
+// (k % 512 == 0) a chunk starts sh = 2 (c % 2) bytes past a dword boundary, the same
+// for every row: a row's LDS chunk (216 bytes) holds the bytes from that boundary, as
+// 26 pieces of 8 bytes and a 27th whose first dword is chunk bytes 208 - sh .. 211 - sh,
+// read as two halfwords so that no load passes the chunk's end. GROW: bytes per row
+// chunk in the weight (ROW is the LDS row).
+template <> struct ChunkTraits<XQ_Q6_K> {
+    static constexpr int BB = 0, ROW = 216, U4 = 27, PIECE = 8, GROW = 210;
+};
 template <int QT> constexpr int chunk_piece() {
-    if constexpr (QT == XQ_IQ4_XS) return ChunkTraits<QT>::PIECE;
+    if constexpr (QT == XQ_IQ4_XS || QT == XQ_Q6_K) return ChunkTraits<QT>::PIECE;
     else return 16;
 }
-template <int QT> constexpr bool coop_xq() {
-    return QT == XQ_Q4_K || QT == XQ_Q5_K || QT == XQ_F16 || QT == XQ_IQ4_XS;
+template <int QT> constexpr int chunk_grow() {
+    if constexpr (QT == XQ_Q6_K) return ChunkTraits<QT>::GROW;
+    else return ChunkTraits<QT>::ROW;
 }
+template <int QT> constexpr bool coop_xq() {
+    return QT == XQ_Q4_K || QT == XQ_Q5_K || QT == XQ_F16 || QT == XQ_IQ4_XS || QT == XQ_Q6_K;
+}
+typedef uint32_t u2a4_t __attribute__((ext_vector_type(2), aligned(4)));  // 4-byte aligned
 
 // Sub-block j's 6-bit scale and min of a Q4_K / Q5_K super-block header (d, dmin, then
 // the 12 scale bytes): j < 4 take the low 6 bits of bytes j and j + 4; j >= 4 the
@@ -659,7 +673,8 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
     const int nch = c_end - c_begin;
     if (nch <= 0) return;
     const int nsteps = 8 * nch;
-    const uint32_t row_bytes = XQ ? (uint32_t)(k >> 8) * WROW : (uint32_t)(k >> 5) * BB;
+    constexpr int GROW = chunk_grow<QT>();          // a row chunk's bytes in the weight
+    const uint32_t row_bytes = XQ ? (uint32_t)(k >> 8) * GROW : (uint32_t)(k >> 5) * BB;
 
     // A fragments: 32-row tile rt, 16-k slice kk at fragment rt * (k / 16) + kk of
     // the workspace (1 KB each; this lane's 16 bytes at 16 lane). Row tiles past
@@ -690,9 +705,10 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
     for (int S = 0; S < 8; ++S) {
         int gr = f16_weight_row<EPI, NW>(tn, S * RS + wrr, n);
         gr = gr < 0 ? 0 : gr;
-        wsrc[S] = (uint32_t)gr * row_bytes + PIECE * wpp;
+        // Q6_K: the row's start; the piece offset is added per chunk
+        wsrc[S] = (uint32_t)gr * row_bytes + (QT == XQ_Q6_K ? 0 : PIECE * wpp);
     }
-    const uint8_t *wbase = W + (size_t)c_begin * WROW;
+    const uint8_t *wbase = W + (size_t)c_begin * GROW;
 
     // B fragment (tile jj, half q): 16 bytes of lane `lane` in fragment (wn 3 + jj, q).
     const int boff = (wn * JT * 2 * 64 + lane) * 16;
@@ -762,8 +778,18 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
 
     auto fetch_slice = [&](int chunk, auto s_c, u4_t &dst) __attribute__((always_inline)) {
         constexpr int S = decltype(s_c)::value;
-        const uint8_t *src = wbase + (size_t)min(chunk, nch - 1) * WROW + wsrc[S];
-        if constexpr (PIECE == 16) {
+        const uint8_t *src = wbase + (size_t)min(chunk, nch - 1) * GROW + wsrc[S];
+        if constexpr (QT == XQ_Q6_K) {
+            // src: this row's chunk start, sh bytes past a dword boundary. Every lane
+            // issues the same three loads (the 27th piece's lanes use the halfwords,
+            // assembled when stored, so that nothing here waits for a load).
+            const int sh = ((c_begin + min(chunk, nch - 1)) & 1) * 2;
+            const bool last = wpp == U4 - 1;
+            const u2a4_t v = *reinterpret_cast<const u2a4_t *>(src - sh + (last ? 200 : PIECE * wpp));
+            const uint32_t s0 = *reinterpret_cast<const uint16_t *>(src + 206);
+            const uint32_t s1 = *reinterpret_cast<const uint16_t *>(src + 208);
+            dst = u4_t{v[0], v[1], s0, s1};
+        } else if constexpr (PIECE == 16) {
             dst = *reinterpret_cast<const u4_t *>(src);
         } else {
             const u2_t v = *reinterpret_cast<const u2_t *>(src);
@@ -773,7 +799,13 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
     auto store_slice = [&](int wbuf, auto s_c, const u4_t &src) __attribute__((always_inline)) {
         constexpr int S = decltype(s_c)::value;
         uint8_t *dst = wsm0 + wbuf * WBUF + S * RS * WROW + wdst;
-        if constexpr (PIECE == 16) {
+        if constexpr (QT == XQ_Q6_K) {
+            // the 27th piece: chunk bytes 208 - sh .. 211 - sh (sh = 2: halfwords 206 and
+            // 208; sh = 0: halfword 208, then two bytes never read)
+            const bool odd = ((c_begin ^ wbuf) & 1) != 0;
+            const uint32_t tail = __builtin_amdgcn_perm(src[3], src[2], odd ? 0x05040100u : 0x05040504u);
+            if (wvalid) *reinterpret_cast<u2_t *>(dst) = wpp == U4 - 1 ? u2_t{tail, 0u} : u2_t{src[0], src[1]};
+        } else if constexpr (PIECE == 16) {
             if (wvalid) *reinterpret_cast<u4_t *>(dst) = src;
         } else {
             if (wvalid) *reinterpret_cast<u2_t *>(dst) = u2_t{src[0], src[1]};
@@ -791,6 +823,7 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
         uint32_t d[NDW], lo[NDW], hi[NDW];
         u4_t hdr[XQ ? NDW : 1];
         u2_t hv[XQ ? NDW : 1];
+        uint32_t sh;  // Q6_K: the chunk's byte shift in LDS
     };
     auto read_raw = [&](int wbuf, auto blk_c, RawWords &rw) __attribute__((always_inline)) {
         constexpr int blk = decltype(blk_c)::value;
@@ -800,6 +833,24 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
             for (int i = 0; i < NDW; ++i) {
                 if constexpr (QT == XQ_F16) {
                     rw.hv[i] = *reinterpret_cast<const u2_t *>(wb + 2 * qraw[i] - sraw[i] + 64 * blk);
+                } else if constexpr (QT == XQ_Q6_K) {
+                    // sub-block blk = 4 h + c, unit w: ql bytes 64 h + 32 (c % 2) + 4 w, qh
+                    // bytes 128 + 32 h + 4 w (each as the two dwords around them), the
+                    // scale byte 192 + 8 h + w / 4 + 2 c, d at 208; chunk byte b sits at
+                    // LDS byte sh + b of the row (sh = 2 for odd chunks)
+                    constexpr int H = blk >> 2, C = blk & 3;
+                    const int sh = ((c_begin ^ wbuf) & 1) * 2;
+                    const int w4 = qraw[i] - sraw[i];
+                    const uint32_t *ql = reinterpret_cast<const uint32_t *>(wb + sraw[i] + 64 * H + 32 * (C & 1) + w4);
+                    const uint32_t *qh = reinterpret_cast<const uint32_t *>(wb + sraw[i] + 128 + 32 * H + w4);
+                    rw.lo[i] = ql[0];
+                    rw.hi[i] = ql[1];
+                    rw.hdr[i][0] = qh[0];
+                    rw.hdr[i][1] = qh[1];
+                    rw.hdr[i][2] = (uint32_t)(int)*reinterpret_cast<const int8_t *>(
+                        wb + sraw[i] + sh + 192 + 8 * H + 2 * C + (w4 >> 4));
+                    rw.hdr[i][3] = *reinterpret_cast<const uint16_t *>(wb + sraw[i] + sh + 208);
+                    rw.sh = (uint32_t)sh;
                 } else if constexpr (QT == XQ_IQ4_XS) {
                     // header (d, scales_h, scales_l); unit w's codes: low nibbles of bytes
                     // 16 blk + 4 w .. (w < 4) or high nibbles of 16 blk + 4 (w - 4) ..
@@ -846,7 +897,24 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
                 return;
             }
             uint32_t p[2];
-            if constexpr (QT == XQ_IQ4_XS) {
+            if constexpr (QT == XQ_Q6_K) {
+                // (d sc) (q - 32): d sc is exact, the product rounds once in f32; then
+                // binary16 (RNE). q: 4 low bits from ql (high nibble for c >= 2), 2 high
+                // bits from qh bits 2 c, 2 c + 1.
+                constexpr int C = blk & 3;
+                const uint32_t qlw = __builtin_amdgcn_alignbyte(rw.hi[i], rw.lo[i], rw.sh);
+                const uint32_t qhw = __builtin_amdgcn_alignbyte(rw.hdr[i][1], rw.hdr[i][0], rw.sh);
+                const uint32_t q = ((qlw >> (4 * (C >> 1))) & 0x0F0F0F0Fu) | (((qhw >> (2 * C)) & 0x03030303u) << 4);
+                const float ds = fp16_bits_to_f32(rw.hdr[i][3]) * (float)(int)rw.hdr[i][2];
+                float w[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    w[c] = ds * (float)((int)((q >> (8 * c)) & 0xFFu) - 32);
+                    asm("" : "+v"(w[c]));
+                }
+                p[0] = h2_bits(h2_t{(_Float16)w[0], (_Float16)w[1]});
+                p[1] = h2_bits(h2_t{(_Float16)w[2], (_Float16)w[3]});
+            } else if constexpr (QT == XQ_IQ4_XS) {
                 // sub-block blk's 6-bit scale ls (nibble of scales_l, 2 bits of scales_h);
                 // d (ls - 32) and its product with a grid value are exact in f32
                 const uint32_t h0 = rw.hv[i][0], sl = rw.hv[i][1];
@@ -1484,8 +1552,9 @@ static int coop_splits(int T, int n, int k, int epilogue) {
     return splits;
 }
 
-bool f16_coop_takes_xq(int qtype, int T) {
-    return T >= COOP_T512 && (qtype == XQ_Q4_K || qtype == XQ_Q5_K || qtype == XQ_F16 || qtype == XQ_IQ4_XS);
+bool f16_coop_takes_xq(int qtype, int T, int k) {
+    return T >= COOP_T512 && (qtype == XQ_Q4_K || qtype == XQ_Q5_K || qtype == XQ_F16 || qtype == XQ_IQ4_XS ||
+                              (qtype == XQ_Q6_K && k % 512 == 0));
 }
 
 // Byte offset of the partial sums in the workspace, and the floats between splits.
@@ -1620,6 +1689,7 @@ hipError_t launch_gemm_f16_prepared(const GemmArgs &a, void *workspace, hipStrea
         case XQ_Q5_K: return launch_coop_e<XQ_Q5_K, 512>(a, xh, s);
         case XQ_F16: return launch_coop_e<XQ_F16, 512>(a, xh, s);
         case XQ_IQ4_XS: return launch_coop_e<XQ_IQ4_XS, 512>(a, xh, s);
+        case XQ_Q6_K: return launch_coop_e<XQ_Q6_K, 512>(a, xh, s);
         default: return hipErrorInvalidValue;
         }
     }

@@ -41,8 +41,9 @@ hipError_t launch_gemm_f16_prepared(const GemmArgs &a, void *workspace, hipStrea
 // boundary) one [T][n] f32 block of partial sums per split.
 int64_t f16_ws_bytes(int T, int n, int k, int epilogue);
 // The further types the f16 workspace path's cooperative-decode GEMM takes (F16,
-// Q4_K, Q5_K and IQ4_XS weights from COOP_T512 rows); Q6_K keeps its own GEMM.
-bool f16_coop_takes_xq(int qtype, int T);
+// Q4_K, Q5_K and IQ4_XS weights from COOP_T512 rows, and Q6_K there when k % 512 == 0);
+// the others keep their own GEMM.
+bool f16_coop_takes_xq(int qtype, int T, int k);
 // RMSNorm prologue: inv[t] = 1 / sqrt(mean_j X[t][j]^2 + eps) (T workgroups), and
 // Xn[t][j] = X[t][j] * inv[t] * w[j] for the kernels that read f32 X.
 hipError_t launch_rms_inv(const float *X, int T, int k, float eps, float *inv, hipStream_t s);

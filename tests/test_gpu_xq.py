@@ -108,7 +108,7 @@ def test_xq_forced_families_and_noalloc(gpu, qtype):
         assert np.array_equal(y0.view(np.uint32), Yd.cpu().numpy().view(np.uint32))
 
 
-COOP = [synth.F16, synth.Q4_K, synth.Q5_K, synth.IQ4_XS]
+COOP = [synth.F16, synth.Q4_K, synth.Q5_K, synth.Q6_K, synth.IQ4_XS]
 
 
 @pytest.mark.parametrize("epi", [PLAIN, RESIDUAL, SWIGLU])
@@ -117,11 +117,12 @@ COOP = [synth.F16, synth.Q4_K, synth.Q5_K, synth.IQ4_XS]
 def test_xq_coop_every_output(gpu, qtype, kind, epi):
     """With a workspace on the f16 leg from 512 rows, the cooperative-decode GEMM decodes
     these types: T = 520 is a full 512-row tile and a ragged one, n = 150 a ragged weight
-    tile; PLAIN and RESIDUAL at k = 2048 split K in two (partial sums, then their fixed-
-    order sum). pf_gemm_noalloc runs the same kernels: same bits."""
+    tile; PLAIN and RESIDUAL at k = 2560 split K in two (partial sums, then their fixed-
+    order sum), the second split starting at an odd chunk (Q6_K's chunks alternate between
+    0 and 2 bytes past a dword boundary). pf_gemm_noalloc runs the same kernels: same bits."""
     import torch
     n, T = 150, 520
-    k = 1024 if epi == SWIGLU else 2048
+    k = 1024 if epi == SWIGLU else 2560
     rows = 2 * n if epi == SWIGLU else n
     seed = 670 + 7 * qtype + 3 * epi + (kind == "edge")
     W = _weights(qtype, rows, k, kind, F16, seed)
