@@ -73,7 +73,8 @@ KERNEL_SOURCES = {
 def kernel_family(T, leg, qtype=0):
     if qtype not in (Q4_0, Q8_0):
         # the further types take the cooperative-decode GEMM through a workspace from 512
-        # rows on the f16 leg (Q6_K with k % 512 == 0, as every workload here has)
+        # rows on the f16 leg (Q6_K with k % 512 == 0, as every workload here has; Q4_K,
+        # Q5_K and IQ4_XS already from 256)
         return "gemm_f16" if leg == 1 and T >= 512 else "xq"
     return "gemv" if T <= 8 else ("gemm_f16" if leg == 1 else "gemm_f32")
 

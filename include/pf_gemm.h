@@ -71,7 +71,8 @@ extern "C" {
 #endif
 
 /* Block types. F16 .. IQ4_XS run their own kernels on both legs and need no
- * workspace, except from 512 rows on the f16 leg (Q6_K: with k % 512 == 0): pf_gemm_ws runs
+ * workspace, except on the f16 leg from 256 rows (Q4_K, Q5_K, IQ4_XS) or 512 (F16, and
+ * Q6_K with k % 512 == 0): pf_gemm_ws runs
  * them on Q4_0's cooperative-decode GEMM, which takes the same workspace as Q4_0 at
  * those sizes (pf_gemm, and pf_gemm_noalloc where that workspace exceeds the static
  * scratch, keep their own GEMM). pf_prepare_x and pf_gemm_prepared take Q4_0 and Q8_0

@@ -625,7 +625,7 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
     using CT = ChunkTraits<QT>;
     static_assert(MT == 256 || MT == 512, "tile: 256 x 192 or 512 x 96");
     constexpr bool XQ = coop_xq<QT>();
-    static_assert(!XQ || MT == 512, "further types: 512 x 96 tiles only");
+    static_assert(!XQ || MT == 512 || (QT != XQ_F16 && QT != XQ_Q6_K), "F16, Q6_K: 512 x 96 tiles only");
     constexpr int NW = MT == 256 ? 192 : 96;        // weight rows per tile
     constexpr int WN = NW / 96;                     // waves across the weight rows (2 or 1)
     constexpr int BB = CT::BB;                      // 18 / 34
@@ -968,6 +968,9 @@ void gemm_f16_coop_kernel(const uint8_t *__restrict__ W, const uint16_t *__restr
             *reinterpret_cast<u2_t *>(bb + bdst[0]) = u2_t{lo02, lo13};
             *reinterpret_cast<u2_t *>(bb + bdst[0] + 1024) = u2_t{hi02, hi13};
             unit(1);
+        } else if constexpr (XQ) {
+#pragma unroll
+            for (int i = 0; i < NDW; ++i) unit(i);
         } else {
 #pragma unroll
             for (int i = 0; i < NDW; ++i) {
@@ -1552,9 +1555,11 @@ static int coop_splits(int T, int n, int k, int epilogue) {
     return splits;
 }
 
+// Q4_K, Q5_K and IQ4_XS from 256 rows (both tiles); F16 and Q6_K (k % 512 == 0) from
+// COOP_T512 (their 256 x 192 tile's staging would need more than one piece per thread).
 bool f16_coop_takes_xq(int qtype, int T, int k) {
-    return T >= COOP_T512 && (qtype == XQ_Q4_K || qtype == XQ_Q5_K || qtype == XQ_F16 || qtype == XQ_IQ4_XS ||
-                              (qtype == XQ_Q6_K && k % 512 == 0));
+    if (qtype == XQ_Q4_K || qtype == XQ_Q5_K || qtype == XQ_IQ4_XS) return T >= 256;
+    return T >= COOP_T512 && (qtype == XQ_F16 || (qtype == XQ_Q6_K && k % 512 == 0));
 }
 
 // Byte offset of the partial sums in the workspace, and the floats between splits.
@@ -1684,11 +1689,11 @@ hipError_t launch_gemm_f16_prepared(const GemmArgs &a, void *workspace, hipStrea
         switch (a.qtype) {
         case Q4_0: return launch_coop_q<Q4_0>(a, xh, s);
         case Q8_0: return launch_coop_q<Q8_0>(a, xh, s);
-        // further types (f16_coop_takes_xq): 512 x 96 tiles only
-        case XQ_Q4_K: return launch_coop_e<XQ_Q4_K, 512>(a, xh, s);
-        case XQ_Q5_K: return launch_coop_e<XQ_Q5_K, 512>(a, xh, s);
+        // further types (f16_coop_takes_xq)
+        case XQ_Q4_K: return launch_coop_q<XQ_Q4_K>(a, xh, s);
+        case XQ_Q5_K: return launch_coop_q<XQ_Q5_K>(a, xh, s);
+        case XQ_IQ4_XS: return launch_coop_q<XQ_IQ4_XS>(a, xh, s);
         case XQ_F16: return launch_coop_e<XQ_F16, 512>(a, xh, s);
-        case XQ_IQ4_XS: return launch_coop_e<XQ_IQ4_XS, 512>(a, xh, s);
         case XQ_Q6_K: return launch_coop_e<XQ_Q6_K, 512>(a, xh, s);
         default: return hipErrorInvalidValue;
         }

@@ -40,9 +40,9 @@ hipError_t launch_gemm_f16_prepared(const GemmArgs &a, void *workspace, hipStrea
 // multiple of 32), and for T >= 256 with a K split, behind it (at the next 256-byte
 // boundary) one [T][n] f32 block of partial sums per split.
 int64_t f16_ws_bytes(int T, int n, int k, int epilogue);
-// The further types the f16 workspace path's cooperative-decode GEMM takes (F16,
-// Q4_K, Q5_K and IQ4_XS weights from COOP_T512 rows, and Q6_K there when k % 512 == 0);
-// the others keep their own GEMM.
+// The further types the f16 workspace path's cooperative-decode GEMM takes (Q4_K, Q5_K
+// and IQ4_XS from 256 rows; F16, and Q6_K with k % 512 == 0, from 512); the others keep
+// their own GEMM.
 bool f16_coop_takes_xq(int qtype, int T, int k);
 // RMSNorm prologue: inv[t] = 1 / sqrt(mean_j X[t][j]^2 + eps) (T workgroups), and
 // Xn[t][j] = X[t][j] * inv[t] * w[j] for the kernels that read f32 X.

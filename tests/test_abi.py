@@ -185,13 +185,13 @@ def test_workspace_bytes(lib):
     # 5 chunks of k are too few to split in two
     assert wb(pf.PF_Q4_0, 17, 1280, 290, pf.PF_RESIDUAL, pf.PF_LEG_F16) == 320 * 1280 * 2
     assert wb(pf.PF_Q4_0, 4096, 4096, 512, pf.PF_PLAIN, pf.PF_LEG_F32) == 0
-    # the further types take no workspace, except from 512 rows on the f16 leg, where they
-    # take the cooperative-decode GEMM's (as Q4_0 at the same sizes); Q6_K only with
-    # k % 512 == 0 (rows a multiple of 4 bytes)
+    # the further types take no workspace, except on the f16 leg from 256 rows (Q4_K, Q5_K,
+    # IQ4_XS) or 512 (F16, and Q6_K with k % 512 == 0: rows a multiple of 4 bytes), where
+    # they take the cooperative-decode GEMM's (as Q4_0 at the same sizes)
     for qt in (pf.PF_F16, pf.PF_Q4_K, pf.PF_Q5_K, pf.PF_Q6_K, pf.PF_IQ4_XS):
         for T in (1, 8, 9, 300, 511, 512, 2048):
             for epi in (pf.PF_PLAIN, pf.PF_RESIDUAL, pf.PF_GATE_UP_SWIGLU):
-                coop = T >= 512
+                coop = T >= 512 or (T >= 256 and qt in (pf.PF_Q4_K, pf.PF_Q5_K, pf.PF_IQ4_XS))
                 want = wb(pf.PF_Q4_0, 4096, 4096, T, epi, pf.PF_LEG_F16) if coop else 0
                 assert wb(qt, 4096, 4096, T, epi, pf.PF_LEG_F16) == want
                 assert wb(qt, 4096, 4096, T, epi, pf.PF_LEG_F32) == 0

@@ -140,6 +140,26 @@ def test_xq_coop_every_output(gpu, qtype, kind, epi):
     assert np.array_equal(Y.view(np.uint32), Yd.cpu().numpy().view(np.uint32))
 
 
+@pytest.mark.parametrize("epi", [PLAIN, RESIDUAL, SWIGLU])
+@pytest.mark.parametrize("qtype", [synth.Q4_K, synth.Q5_K, synth.IQ4_XS], ids=lambda q: NAMES[q])
+def test_xq_coop_256_rows(gpu, qtype, epi):
+    """Q4_K, Q5_K and IQ4_XS take the cooperative-decode GEMM's 256 x 192 tile from 256
+    rows (T = 300: one full and one ragged tile row); F16 and Q6_K do not there."""
+    n, T = 200, 300
+    k = 1024 if epi == SWIGLU else 2560
+    rows = 2 * n if epi == SWIGLU else n
+    seed = 690 + 7 * qtype + 3 * epi
+    W = _weights(qtype, rows, k, "edge", F16, seed)
+    X = synth.activations(T, k, workload_id=seed)
+    R = synth.activations(T, n, workload_id=seed, tensor_id=synth.TENSOR_R) if epi == RESIDUAL else None
+    assert gpu.workspace_bytes(qtype, n, k, T, epi, F16) > 0
+    assert gpu.workspace_bytes(synth.F16, n, k, T, epi, F16) == 0
+    print("case xq coop256 %s epi=%d" % (NAMES[qtype], epi), flush=True)
+    Y = parity.run_gpu(gpu, qtype, W, n, k, X, epi, F16, R=R, workspace=True)
+    ok, err = parity.check(qtype, W, n, k, X, Y, epi, F16, R=R)
+    assert ok, "parity failed: metric %.3e" % err
+
+
 @pytest.mark.parametrize("qtype", COOP, ids=lambda q: NAMES[q])
 def test_xq_coop_full_size_sampled(gpu, qtype):
     """The gate/up shape at T = 512 through the workspace (sampled outputs)."""
