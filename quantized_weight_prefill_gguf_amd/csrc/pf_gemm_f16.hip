@@ -1378,10 +1378,6 @@ hipError_t launch_split(const GemmArgs &a, TileChoice tc, const uint16_t *xh, hi
     }
 }
 
-// Partial sums of a K split: block `split` (pstride floats apart) of ps [T][n], each
-// stored whole by one workgroup.
-long part_stride(int T, int n) { return ((long)T * n + 3) / 4 * 4; }
-
 // ps: room for the partial sums of a K split (the workspace), or null: then the
 // GEMM does not split, and every output has one writer.
 template <int QT, int EPI>
@@ -1527,6 +1523,35 @@ __global__ __launch_bounds__(256) void x_to_frag_kernel(const float *__restrict_
 }
 
 }  // namespace
+
+// Partial sums of a K split: block `split` (pstride floats apart) of ps [T][n], each
+// stored whole by one workgroup.
+long part_stride(int T, int n) { return ((long)T * n + 3) / 4 * 4; }
+
+hipError_t launch_split_sum(const GemmArgs &a, const float *ps, int splits, hipStream_t s) {
+    const long pstride = part_stride(a.T, a.n);
+    const long count = (long)a.T * a.n;
+    const bool residual = a.epilogue == EPI_RESIDUAL;
+    if (a.ldy == a.n) {
+        const dim3 g((unsigned)((count / 4 + 1 + 255) / 256));
+        if (residual)
+            hipLaunchKernelGGL((split_sum_kernel<EPI_RESIDUAL, true>), g, dim3(256), 0, s, ps, a.Y, count, pstride,
+                               splits, a.n, a.ldy);
+        else
+            hipLaunchKernelGGL((split_sum_kernel<EPI_PLAIN, true>), g, dim3(256), 0, s, ps, a.Y, count, pstride,
+                               splits, a.n, a.ldy);
+    } else {
+        const dim3 g((unsigned)((count + 255) / 256));
+        if (residual)
+            hipLaunchKernelGGL((split_sum_kernel<EPI_RESIDUAL, false>), g, dim3(256), 0, s, ps, a.Y, count,
+                               pstride, splits, a.n, a.ldy);
+        else
+            hipLaunchKernelGGL((split_sum_kernel<EPI_PLAIN, false>), g, dim3(256), 0, s, ps, a.Y, count, pstride,
+                               splits, a.n, a.ldy);
+    }
+    return hipGetLastError();
+}
+
 
 #ifndef PF_COOP_T512
 #define PF_COOP_T512 512

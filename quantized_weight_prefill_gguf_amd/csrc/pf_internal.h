@@ -44,6 +44,10 @@ int64_t f16_ws_bytes(int T, int n, int k, int epilogue);
 // and IQ4_XS from 256 rows; F16, and Q6_K with k % 512 == 0, from 512); the others keep
 // their own GEMM.
 bool f16_coop_takes_xq(int qtype, int T, int k);
+// Floats between the [T][n] partial-sum blocks of a K split, and Y = [R +] the `splits`
+// blocks at ps added in split order (PLAIN or RESIDUAL; a.Y, a.ldy, a.T, a.n).
+long part_stride(int T, int n);
+hipError_t launch_split_sum(const GemmArgs &a, const float *ps, int splits, hipStream_t s);
 // RMSNorm prologue: inv[t] = 1 / sqrt(mean_j X[t][j]^2 + eps) (T workgroups), and
 // Xn[t][j] = X[t][j] * inv[t] * w[j] for the kernels that read f32 X.
 hipError_t launch_rms_inv(const float *X, int T, int k, float eps, float *inv, hipStream_t s);
@@ -61,10 +65,14 @@ constexpr int64_t kNoallocScratchBytes = int64_t(64) << 20;
 hipError_t noalloc_scratch(hipStream_t s, void **ptr);
 // The further weight types (ids as the C ABI's PF_F16 .. PF_IQ4_XS), pf_xq.hip: the
 // GEMV (T <= 8, f32), the tiled GEMM on either leg (leg16: binary16 operands), and
-// the block decode to f32 or binary16 bits. No workspace.
+// the block decode to f32 or binary16 bits.
 enum { XQ_F16 = 2, XQ_Q4_K = 3, XQ_Q5_K = 4, XQ_Q6_K = 5, XQ_IQ4_XS = 6 };
 hipError_t launch_xq_gemv(const GemmArgs &a, hipStream_t s);
-hipError_t launch_xq_gemm(const GemmArgs &a, bool leg16, hipStream_t s);
+// ws: room for xq_ws_bytes() of the call, or null (then nothing splits).
+hipError_t launch_xq_gemm(const GemmArgs &a, bool leg16, void *ws, hipStream_t s);
+// Workspace bytes of the further types' own GEMM on the f16 leg: the partial sums of a
+// K split where PLAIN / RESIDUAL tiles leave CUs idle, else 0.
+int64_t xq_ws_bytes(int T, int n, int k, int epilogue, bool leg16);
 hipError_t launch_xq_dequant(int qtype, const uint8_t *W, int rows, int k, void *out, bool f16_out,
                              hipStream_t s);
 // Block decode to f32 / binary16.

@@ -344,10 +344,11 @@ typedef float f16v_t __attribute__((ext_vector_type(16)));
 // decoded into the other LDS buffer, one barrier.
 constexpr int XNW = 128, XKS = 32;
 constexpr int XPF = 4;  // steps of weight bytes and X in flight per thread
-template <int QT, int EPI, bool LEG16, int MT>
+template <int QT, int EPI, bool LEG16, int MT, bool SPLIT = false>
 __global__ __launch_bounds__(256) void xq_gemm_kernel(const uint8_t *__restrict__ W,
                                                       const float *__restrict__ X, float *__restrict__ Y,
-                                                      int n, int ldy, int k, int T, int tiles_m) {
+                                                      int n, int ldy, int k, int T, int tiles_m, int tiles_n,
+                                                      int splits, long pstride) {
     using TR = XqTraits<QT>;
     typedef typename std::conditional<LEG16, _Float16, float>::type op_t;
     static_assert(MT == 64 || MT == 128, "tile rows");
@@ -363,8 +364,18 @@ __global__ __launch_bounds__(256) void xq_gemm_kernel(const uint8_t *__restrict_
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
+    const int tile = blockIdx.x % (tiles_m * tiles_n), split = blockIdx.x / (tiles_m * tiles_n);
+    const int tm = tile % tiles_m, tn = tile / tiles_m;
     const int m0 = tm * MT;
+    // SPLIT: this workgroup's share of the 32-k steps, whose sums go to block `split` of
+    // the partial sums ([T][n], pstride floats apart) as PLAIN outputs.
+    const int nks_all = k / XKS;
+    const int ks_begin = (int)((long)nks_all * split / splits);
+    const int ks_end = (int)((long)nks_all * (split + 1) / splits);
+    if constexpr (SPLIT) {
+        Y += (size_t)split * pstride;
+        ldy = n;
+    }
     constexpr int OUT = EPI == EPI_SWIGLU ? XNW / 2 : XNW;  // outputs per tile
     const int o0 = tn * OUT;
 
@@ -389,20 +400,20 @@ __global__ __launch_bounds__(256) void xq_gemm_kernel(const uint8_t *__restrict_
     // from XPF steps before its decode. Step indices past the last are clamped, so
     // every load is issued unconditionally (in-order wait counts then never wait for
     // a younger load).
-    const int nks = k / XKS;
+    const int nks = ks_end - ks_begin;
     Raw16<QT> raw[XPF];
     f4_t xv[XPF][AF4];
     auto load_step = [&](int ks, int slot) __attribute__((always_inline)) {
-        const int e = min(ks, nks - 1) * XKS + 16 * bhalf;
+        const int e = (ks_begin + min(ks, nks - 1)) * XKS + 16 * bhalf;
         load_raw16<QT>(wrow + (size_t)(e / TR::ELEMS) * TR::BYTES, e % TR::ELEMS, raw[slot]);
-        const f4_t *xp = reinterpret_cast<const f4_t *>(xrow + min(ks, nks - 1) * XKS);
+        const f4_t *xp = reinterpret_cast<const f4_t *>(xrow + (ks_begin + min(ks, nks - 1)) * XKS);
 #pragma unroll
         for (int i = 0; i < AF4; ++i) xv[slot][i] = xp[i];
     };
     // Decode, then 16-byte LDS stores (row pitches and offsets are multiples of 16 bytes).
     auto store_step = [&](int ks, int slot, int buf) __attribute__((always_inline)) {
         float wv[16];
-        decode_raw16<QT>(raw[slot], (min(ks, nks - 1) * XKS + 16 * bhalf) % TR::ELEMS, wv);
+        decode_raw16<QT>(raw[slot], ((ks_begin + min(ks, nks - 1)) * XKS + 16 * bhalf) % TR::ELEMS, wv);
         op_t *b = Bs + buf * B_ELEMS + brow * PADK + 16 * bhalf;
         op_t *a = As + buf * A_ELEMS + arow * PADK + acol;
         if constexpr (LEG16) {
@@ -508,7 +519,7 @@ __global__ __launch_bounds__(256) void xq_gemm_kernel(const uint8_t *__restrict_
         if constexpr (EPI == EPI_SWIGLU) {
             const float u = C[t * C_PITCH + XNW / 2 + oc];
             *y = LEG16 ? silu_fast(v) * u : silu_f32(v) * u;
-        } else if constexpr (EPI == EPI_RESIDUAL) {
+        } else if constexpr (EPI == EPI_RESIDUAL && !SPLIT) {
             *y = *y + v;
         } else {
             *y = v;
@@ -552,33 +563,62 @@ hipError_t launch_gemv_q(const GemmArgs &a, hipStream_t s) {
     }
 }
 
+// Tile rows: 128 on the f16 leg (twice the matrix-core work per decoded weight) when
+// that still makes at least 256 workgroups, else 64 (the f32 leg always).
+int xq_tile_rows(int T, int n, int epilogue, bool leg16) {
+    const int out = epilogue == EPI_SWIGLU ? XNW / 2 : XNW;
+    return leg16 && (long)((T + 127) / 128) * ((n + out - 1) / out) >= 256 ? 128 : 64;
+}
+
+// K split of the f16 leg's PLAIN / RESIDUAL tiles through a workspace, where the tiles
+// alone leave CUs idle: enough splits to fill the 256 CUs, each of at least 16 steps of
+// 32 k (512 k), at most 16. The splits' partial sums are added in split order by
+// split_sum_kernel (deterministic). SwiGLU and the f32 leg do not split.
+int xq_splits(int T, int n, int k, int epilogue, bool leg16) {
+    if (!leg16 || epilogue == EPI_SWIGLU) return 1;
+    const int mt = xq_tile_rows(T, n, epilogue, leg16);
+    const long tiles = (long)((T + mt - 1) / mt) * ((n + XNW - 1) / XNW);
+    if (tiles >= 256) return 1;
+    int splits = (int)(256 / tiles);
+    const int by_k = (k / XKS) / 16;
+    if (splits > by_k) splits = by_k;
+    if (splits > 16) splits = 16;
+    return splits < 1 ? 1 : splits;
+}
+
 template <int QT, int EPI, bool LEG16, int MT>
-hipError_t launch_gemm_mt(const GemmArgs &a, hipStream_t s) {
+hipError_t launch_gemm_mt(const GemmArgs &a, float *ps, int splits, hipStream_t s) {
     constexpr int OUT = EPI == EPI_SWIGLU ? XNW / 2 : XNW;
     const int tm = (a.T + MT - 1) / MT, tn = (a.n + OUT - 1) / OUT;
+    if constexpr (EPI != EPI_SWIGLU && LEG16) {
+        if (splits > 1) {
+            const long pstride = part_stride(a.T, a.n);
+            hipLaunchKernelGGL((xq_gemm_kernel<QT, EPI, LEG16, MT, true>), dim3(tm * tn * splits), dim3(256), 0, s,
+                               a.W, a.X, ps, a.n, a.n, a.k, a.T, tm, tn, splits, pstride);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            return launch_split_sum(a, ps, splits, s);
+        }
+    }
     hipLaunchKernelGGL((xq_gemm_kernel<QT, EPI, LEG16, MT>), dim3(tm * tn), dim3(256), 0, s, a.W, a.X, a.Y, a.n,
-                       a.ldy, a.k, a.T, tm);
+                       a.ldy, a.k, a.T, tm, tn, 1, 0L);
     return hipGetLastError();
 }
 
-// Tile rows: 128 on the f16 leg (twice the matrix-core work per decoded weight) when
-// that still makes at least 256 workgroups, else 64 (the f32 leg always).
 template <int QT, int EPI, bool LEG16>
-hipError_t launch_gemm_e(const GemmArgs &a, hipStream_t s) {
-    constexpr int OUT = EPI == EPI_SWIGLU ? XNW / 2 : XNW;
-    if constexpr (LEG16) {
-        const long tiles128 = (long)((a.T + 127) / 128) * ((a.n + OUT - 1) / OUT);
-        if (tiles128 >= 256) return launch_gemm_mt<QT, EPI, true, 128>(a, s);
-    }
-    return launch_gemm_mt<QT, EPI, LEG16, 64>(a, s);
+hipError_t launch_gemm_e(const GemmArgs &a, float *ps, hipStream_t s) {
+    const int splits = ps ? xq_splits(a.T, a.n, a.k, EPI, LEG16) : 1;
+    if constexpr (LEG16)
+        if (xq_tile_rows(a.T, a.n, EPI, LEG16) == 128) return launch_gemm_mt<QT, EPI, true, 128>(a, ps, splits, s);
+    return launch_gemm_mt<QT, EPI, LEG16, 64>(a, ps, splits, s);
 }
 
 template <int QT, bool LEG16>
-hipError_t launch_gemm_q(const GemmArgs &a, hipStream_t s) {
+hipError_t launch_gemm_q(const GemmArgs &a, float *ps, hipStream_t s) {
     switch (a.epilogue) {
-    case EPI_PLAIN: return launch_gemm_e<QT, EPI_PLAIN, LEG16>(a, s);
-    case EPI_RESIDUAL: return launch_gemm_e<QT, EPI_RESIDUAL, LEG16>(a, s);
-    default: return launch_gemm_e<QT, EPI_SWIGLU, LEG16>(a, s);
+    case EPI_PLAIN: return launch_gemm_e<QT, EPI_PLAIN, LEG16>(a, ps, s);
+    case EPI_RESIDUAL: return launch_gemm_e<QT, EPI_RESIDUAL, LEG16>(a, ps, s);
+    default: return launch_gemm_e<QT, EPI_SWIGLU, LEG16>(a, ps, s);
     }
 }
 
@@ -613,14 +653,20 @@ hipError_t launch_xq_gemv(const GemmArgs &a, hipStream_t s) {
     }
 }
 
-hipError_t launch_xq_gemm(const GemmArgs &a, bool leg16, hipStream_t s) {
+hipError_t launch_xq_gemm(const GemmArgs &a, bool leg16, void *ws, hipStream_t s) {
+    float *ps = static_cast<float *>(ws);
     switch (a.qtype) {
-    case XQ_F16: return leg16 ? launch_gemm_q<XQ_F16, true>(a, s) : launch_gemm_q<XQ_F16, false>(a, s);
-    case XQ_Q4_K: return leg16 ? launch_gemm_q<XQ_Q4_K, true>(a, s) : launch_gemm_q<XQ_Q4_K, false>(a, s);
-    case XQ_Q5_K: return leg16 ? launch_gemm_q<XQ_Q5_K, true>(a, s) : launch_gemm_q<XQ_Q5_K, false>(a, s);
-    case XQ_Q6_K: return leg16 ? launch_gemm_q<XQ_Q6_K, true>(a, s) : launch_gemm_q<XQ_Q6_K, false>(a, s);
-    default: return leg16 ? launch_gemm_q<XQ_IQ4_XS, true>(a, s) : launch_gemm_q<XQ_IQ4_XS, false>(a, s);
+    case XQ_F16: return leg16 ? launch_gemm_q<XQ_F16, true>(a, ps, s) : launch_gemm_q<XQ_F16, false>(a, ps, s);
+    case XQ_Q4_K: return leg16 ? launch_gemm_q<XQ_Q4_K, true>(a, ps, s) : launch_gemm_q<XQ_Q4_K, false>(a, ps, s);
+    case XQ_Q5_K: return leg16 ? launch_gemm_q<XQ_Q5_K, true>(a, ps, s) : launch_gemm_q<XQ_Q5_K, false>(a, ps, s);
+    case XQ_Q6_K: return leg16 ? launch_gemm_q<XQ_Q6_K, true>(a, ps, s) : launch_gemm_q<XQ_Q6_K, false>(a, ps, s);
+    default: return leg16 ? launch_gemm_q<XQ_IQ4_XS, true>(a, ps, s) : launch_gemm_q<XQ_IQ4_XS, false>(a, ps, s);
     }
+}
+
+int64_t xq_ws_bytes(int T, int n, int k, int epilogue, bool leg16) {
+    const int splits = xq_splits(T, n, k, epilogue, leg16);
+    return splits > 1 ? (int64_t)splits * part_stride(T, n) * 4 : 0;
 }
 
 hipError_t launch_xq_dequant(int qtype, const uint8_t *W, int rows, int k, void *out, bool f16_out, hipStream_t s) {

@@ -144,7 +144,7 @@ def test_xq_coop_every_output(gpu, qtype, kind, epi):
 @pytest.mark.parametrize("qtype", [synth.Q4_K, synth.Q5_K, synth.IQ4_XS], ids=lambda q: NAMES[q])
 def test_xq_coop_256_rows(gpu, qtype, epi):
     """Q4_K, Q5_K and IQ4_XS take the cooperative-decode GEMM's 256 x 192 tile from 256
-    rows (T = 300: one full and one ragged tile row); F16 and Q6_K do not there."""
+    rows (T = 300: one full and one ragged tile row)."""
     n, T = 200, 300
     k = 1024 if epi == SWIGLU else 2560
     rows = 2 * n if epi == SWIGLU else n
@@ -153,11 +153,40 @@ def test_xq_coop_256_rows(gpu, qtype, epi):
     X = synth.activations(T, k, workload_id=seed)
     R = synth.activations(T, n, workload_id=seed, tensor_id=synth.TENSOR_R) if epi == RESIDUAL else None
     assert gpu.workspace_bytes(qtype, n, k, T, epi, F16) > 0
-    assert gpu.workspace_bytes(synth.F16, n, k, T, epi, F16) == 0
     print("case xq coop256 %s epi=%d" % (NAMES[qtype], epi), flush=True)
     Y = parity.run_gpu(gpu, qtype, W, n, k, X, epi, F16, R=R, workspace=True)
     ok, err = parity.check(qtype, W, n, k, X, Y, epi, F16, R=R)
     assert ok, "parity failed: metric %.3e" % err
+
+
+@pytest.mark.parametrize("T", [9, 130, 300])
+@pytest.mark.parametrize("epi", [PLAIN, RESIDUAL])
+@pytest.mark.parametrize("qtype", XQ, ids=lambda q: NAMES[q])
+def test_xq_own_gemm_k_split(gpu, qtype, epi, T):
+    """Where the cooperative kernel does not take them (F16 and Q6_K below 512 rows, the
+    others below 256), the further types' own GEMM splits PLAIN / RESIDUAL K through the
+    workspace when its tiles leave CUs idle: n = 150 is two 128-column tiles, so k = 4096
+    splits 8 ways (512 k each), and the sum kernel adds R and the splits in order.
+    pf_gemm_noalloc runs the same kernels: same bits."""
+    import torch
+    n, k = 150, 4096
+    coop = T >= 256 and qtype in (synth.Q4_K, synth.Q5_K, synth.IQ4_XS)
+    if coop:
+        pytest.skip("the cooperative kernel's range")
+    seed = 700 + 7 * qtype + 3 * epi + T
+    W = _weights(qtype, n, k, "edge", F16, seed)
+    X = synth.activations(T, k, workload_id=seed)
+    R = synth.activations(T, n, workload_id=seed, tensor_id=synth.TENSOR_R) if epi == RESIDUAL else None
+    assert gpu.workspace_bytes(qtype, n, k, T, epi, F16) == 8 * ((T * n + 3) // 4 * 4) * 4
+    print("case xq split %s T=%d epi=%d" % (NAMES[qtype], T, epi), flush=True)
+    Y = parity.run_gpu(gpu, qtype, W, n, k, X, epi, F16, R=R, workspace=True)
+    ok, err = parity.check(qtype, W, n, k, X, Y, epi, F16, R=R)
+    assert ok, "parity failed: metric %.3e" % err
+    Wd, Xd = parity.to_dev(W), parity.to_dev(X)
+    Yd = parity.to_dev(R) if R is not None else torch.full((T, n), float("nan"), device="cuda")
+    gpu.gemm_noalloc(qtype, Wd, n, k, Xd, Yd, epi, F16)
+    torch.cuda.synchronize()
+    assert np.array_equal(Y.view(np.uint32), Yd.cpu().numpy().view(np.uint32))
 
 
 @pytest.mark.parametrize("qtype", COOP, ids=lambda q: NAMES[q])
