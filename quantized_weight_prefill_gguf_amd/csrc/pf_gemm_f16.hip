@@ -1528,6 +1528,14 @@ __global__ __launch_bounds__(256) void x_to_frag_kernel(const float *__restrict_
 // stored whole by one workgroup.
 long part_stride(int T, int n) { return ((long)T * n + 3) / 4 * 4; }
 
+hipError_t launch_swiglu_apply(const float *G, const GemmArgs &a, int splits, hipStream_t s) {
+    const long pstride = part_stride(a.T, 2 * a.n);
+    const int count = a.T * a.n;
+    hipLaunchKernelGGL(swiglu_apply_kernel, dim3((count + 255) / 256), dim3(256), 0, s, G, a.Y, a.T, a.n, a.ldy,
+                       splits, pstride);
+    return hipGetLastError();
+}
+
 hipError_t launch_split_sum(const GemmArgs &a, const float *ps, int splits, hipStream_t s) {
     const long pstride = part_stride(a.T, a.n);
     const long count = (long)a.T * a.n;

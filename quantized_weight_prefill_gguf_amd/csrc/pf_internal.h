@@ -48,6 +48,10 @@ bool f16_coop_takes_xq(int qtype, int T, int k);
 // blocks at ps added in split order (PLAIN or RESIDUAL; a.Y, a.ldy, a.T, a.n).
 long part_stride(int T, int n);
 hipError_t launch_split_sum(const GemmArgs &a, const float *ps, int splits, hipStream_t s);
+// Y [T][n] (a.Y, a.ldy) = silu(g) * u from the `splits` blocks G_s [T][2n] at G
+// (part_stride(T, 2n) floats apart; gate products in columns 0..n-1, up in n..2n-1),
+// each sum in split order.
+hipError_t launch_swiglu_apply(const float *G, const GemmArgs &a, int splits, hipStream_t s);
 // RMSNorm prologue: inv[t] = 1 / sqrt(mean_j X[t][j]^2 + eps) (T workgroups), and
 // Xn[t][j] = X[t][j] * inv[t] * w[j] for the kernels that read f32 X.
 hipError_t launch_rms_inv(const float *X, int T, int k, float eps, float *inv, hipStream_t s);

@@ -367,11 +367,12 @@ __global__ __launch_bounds__(256) void xq_gemm_kernel(const uint8_t *__restrict_
     const int tile = blockIdx.x % (tiles_m * tiles_n), split = blockIdx.x / (tiles_m * tiles_n);
     const int tm = tile % tiles_m, tn = tile / tiles_m;
     const int m0 = tm * MT;
-    // SPLIT: this workgroup's share of the 32-k steps, whose sums go to block `split` of
-    // the partial sums ([T][n], pstride floats apart) as PLAIN outputs.
+    // SPLIT (PLAIN only): this workgroup's share of the 32-k steps, whose sums go to
+    // block `split` of the partial sums ([T][n], pstride floats apart).
     const int nks_all = k / XKS;
     const int ks_begin = (int)((long)nks_all * split / splits);
     const int ks_end = (int)((long)nks_all * (split + 1) / splits);
+    static_assert(!SPLIT || EPI == EPI_PLAIN, "a split stores PLAIN partial sums");
     if constexpr (SPLIT) {
         Y += (size_t)split * pstride;
         ldy = n;
@@ -519,7 +520,7 @@ __global__ __launch_bounds__(256) void xq_gemm_kernel(const uint8_t *__restrict_
         if constexpr (EPI == EPI_SWIGLU) {
             const float u = C[t * C_PITCH + XNW / 2 + oc];
             *y = LEG16 ? silu_fast(v) * u : silu_f32(v) * u;
-        } else if constexpr (EPI == EPI_RESIDUAL && !SPLIT) {
+        } else if constexpr (EPI == EPI_RESIDUAL) {
             *y = *y + v;
         } else {
             *y = v;
@@ -570,47 +571,76 @@ int xq_tile_rows(int T, int n, int epilogue, bool leg16) {
     return leg16 && (long)((T + 127) / 128) * ((n + out - 1) / out) >= 256 ? 128 : 64;
 }
 
-// K split of the f16 leg's PLAIN / RESIDUAL tiles through a workspace, where the tiles
-// alone leave CUs idle: enough splits to fill the 256 CUs, each of at least 16 steps of
-// 32 k (512 k), at most 16. The splits' partial sums are added in split order by
-// split_sum_kernel (deterministic). SwiGLU and the f32 leg do not split.
+#ifndef PF_XQ_TARGET_WG
+#define PF_XQ_TARGET_WG 768
+#endif
+// K split of the f16 leg's tiles through a workspace where the tiles alone leave the
+// resident slots idle (three workgroups per CU): that many splits, each of at least 16
+// steps of 32 k (512 k), at most 16. PLAIN / RESIDUAL: the splits' partial sums are
+// added (with R) in split order by split_sum_kernel. SwiGLU up to XQ_SCRATCH_T rows: the
+// gate and up rows run as one split PLAIN GEMM over the 2n rows into G, and
+// swiglu_apply_kernel sums each half in split order and applies silu(g) * u (above that
+// the fused epilogue runs unsplit, as G's round trip grows with T). The f32 leg does not
+// split. Deterministic either way.
+constexpr int XQ_SCRATCH_T = 64;
 int xq_splits(int T, int n, int k, int epilogue, bool leg16) {
-    if (!leg16 || epilogue == EPI_SWIGLU) return 1;
-    const int mt = xq_tile_rows(T, n, epilogue, leg16);
-    const long tiles = (long)((T + mt - 1) / mt) * ((n + XNW - 1) / XNW);
-    if (tiles >= 256) return 1;
-    int splits = (int)(256 / tiles);
+    if (!leg16 || (epilogue == EPI_SWIGLU && T > XQ_SCRATCH_T)) return 1;
+    const int rows = epilogue == EPI_SWIGLU ? 2 * n : n;  // the PLAIN GEMM's weight rows
+    const int mt = xq_tile_rows(T, rows, EPI_PLAIN, leg16);
+    const long tiles = (long)((T + mt - 1) / mt) * ((rows + XNW - 1) / XNW);
+    if (tiles >= PF_XQ_TARGET_WG) return 1;
+    int splits = (int)(PF_XQ_TARGET_WG / tiles);
     const int by_k = (k / XKS) / 16;
     if (splits > by_k) splits = by_k;
     if (splits > 16) splits = 16;
     return splits < 1 ? 1 : splits;
 }
 
-template <int QT, int EPI, bool LEG16, int MT>
-hipError_t launch_gemm_mt(const GemmArgs &a, float *ps, int splits, hipStream_t s) {
+template <int QT, int EPI, bool LEG16, int MT, bool SPLIT>
+hipError_t launch_tiles(const GemmArgs &a, float *ps, int splits, hipStream_t s) {
     constexpr int OUT = EPI == EPI_SWIGLU ? XNW / 2 : XNW;
     const int tm = (a.T + MT - 1) / MT, tn = (a.n + OUT - 1) / OUT;
-    if constexpr (EPI != EPI_SWIGLU && LEG16) {
-        if (splits > 1) {
-            const long pstride = part_stride(a.T, a.n);
-            hipLaunchKernelGGL((xq_gemm_kernel<QT, EPI, LEG16, MT, true>), dim3(tm * tn * splits), dim3(256), 0, s,
-                               a.W, a.X, ps, a.n, a.n, a.k, a.T, tm, tn, splits, pstride);
-            const hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
-            return launch_split_sum(a, ps, splits, s);
-        }
-    }
-    hipLaunchKernelGGL((xq_gemm_kernel<QT, EPI, LEG16, MT>), dim3(tm * tn), dim3(256), 0, s, a.W, a.X, a.Y, a.n,
-                       a.ldy, a.k, a.T, tm, tn, 1, 0L);
+    if constexpr (SPLIT)
+        hipLaunchKernelGGL((xq_gemm_kernel<QT, EPI, LEG16, MT, true>), dim3(tm * tn * splits), dim3(256), 0, s, a.W,
+                           a.X, ps, a.n, a.n, a.k, a.T, tm, tn, splits, part_stride(a.T, a.n));
+    else
+        hipLaunchKernelGGL((xq_gemm_kernel<QT, EPI, LEG16, MT>), dim3(tm * tn), dim3(256), 0, s, a.W, a.X, a.Y,
+                           a.n, a.ldy, a.k, a.T, tm, tn, 1, 0L);
     return hipGetLastError();
+}
+
+// The split PLAIN GEMM of `a` (its n weight rows) into the partial-sum blocks at ps.
+template <int QT>
+hipError_t launch_split_plain(const GemmArgs &a, float *ps, int splits, hipStream_t s) {
+    if (xq_tile_rows(a.T, a.n, EPI_PLAIN, true) == 128)
+        return launch_tiles<QT, EPI_PLAIN, true, 128, true>(a, ps, splits, s);
+    return launch_tiles<QT, EPI_PLAIN, true, 64, true>(a, ps, splits, s);
 }
 
 template <int QT, int EPI, bool LEG16>
 hipError_t launch_gemm_e(const GemmArgs &a, float *ps, hipStream_t s) {
     const int splits = ps ? xq_splits(a.T, a.n, a.k, EPI, LEG16) : 1;
-    if constexpr (LEG16)
-        if (xq_tile_rows(a.T, a.n, EPI, LEG16) == 128) return launch_gemm_mt<QT, EPI, true, 128>(a, ps, splits, s);
-    return launch_gemm_mt<QT, EPI, LEG16, 64>(a, ps, splits, s);
+    if constexpr (LEG16) {
+        if (splits > 1) {
+            hipError_t e;
+            if constexpr (EPI == EPI_SWIGLU) {
+                GemmArgs g = a;  // the gate and up rows as one PLAIN GEMM over 2n rows
+                g.epilogue = EPI_PLAIN;
+                g.n = 2 * a.n;
+                g.ldy = 2 * a.n;
+                e = launch_split_plain<QT>(g, ps, splits, s);
+                if (e != hipSuccess) return e;
+                return launch_swiglu_apply(ps, a, splits, s);
+            } else {
+                // PLAIN partial sums; the sum kernel adds R for RESIDUAL
+                e = launch_split_plain<QT>(a, ps, splits, s);
+            }
+            if (e != hipSuccess) return e;
+            return launch_split_sum(a, ps, splits, s);
+        }
+        if (xq_tile_rows(a.T, a.n, EPI, true) == 128) return launch_tiles<QT, EPI, true, 128, false>(a, ps, 1, s);
+    }
+    return launch_tiles<QT, EPI, LEG16, 64, false>(a, ps, 1, s);
 }
 
 template <int QT, bool LEG16>
@@ -666,7 +696,7 @@ hipError_t launch_xq_gemm(const GemmArgs &a, bool leg16, void *ws, hipStream_t s
 
 int64_t xq_ws_bytes(int T, int n, int k, int epilogue, bool leg16) {
     const int splits = xq_splits(T, n, k, epilogue, leg16);
-    return splits > 1 ? (int64_t)splits * part_stride(T, n) * 4 : 0;
+    return splits > 1 ? (int64_t)splits * part_stride(T, epilogue == EPI_SWIGLU ? 2 * n : n) * 4 : 0;
 }
 
 hipError_t launch_xq_dequant(int qtype, const uint8_t *W, int rows, int k, void *out, bool f16_out, hipStream_t s) {

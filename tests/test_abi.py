@@ -188,29 +188,35 @@ def test_workspace_bytes(lib):
     # the further types take no workspace, except on the f16 leg from 256 rows (Q4_K, Q5_K,
     # IQ4_XS) or 512 (F16, and Q6_K with k % 512 == 0: rows a multiple of 4 bytes), where
     # they take the cooperative-decode GEMM's (as Q4_0 at the same sizes)
-    # Elsewhere on the f16 leg their own GEMM (64- or 128-row x 128-column tiles) splits
-    # PLAIN / RESIDUAL K through the workspace when the tiles leave CUs idle: 256 / tiles
-    # splits, each at least 512 k, at most 16, one [T][n] f32 block each.
+    # Elsewhere on the f16 leg their own GEMM (64- or 128-row x 128-column tiles) splits K
+    # through the workspace when the tiles leave the resident slots (3 per CU) idle:
+    # 768 / tiles splits, each at least 512 k, at most 16, one [T][rows] f32 block each;
+    # SwiGLU up to 64 rows as one PLAIN GEMM over its 2n rows.
     def own_splits(T, n, k, epi):
-        if T <= 8 or epi == pf.PF_GATE_UP_SWIGLU:
+        if T <= 8 or (epi == pf.PF_GATE_UP_SWIGLU and T > 64):
             return 1
-        out = 128
-        mt = 128 if -(-T // 128) * -(-n // out) >= 256 else 64
-        tiles = -(-T // mt) * -(-n // 128)
-        return 1 if tiles >= 256 else max(1, min(256 // tiles, k // 512, 16))
+        rows = 2 * n if epi == pf.PF_GATE_UP_SWIGLU else n
+        mt = 128 if -(-T // 128) * -(-rows // 128) >= 256 else 64
+        tiles = -(-T // mt) * -(-rows // 128)
+        return 1 if tiles >= 768 else max(1, min(768 // tiles, k // 512, 16))
     for qt in (pf.PF_F16, pf.PF_Q4_K, pf.PF_Q5_K, pf.PF_Q6_K, pf.PF_IQ4_XS):
         for T in (1, 8, 9, 300, 511, 512, 2048):
             for epi in (pf.PF_PLAIN, pf.PF_RESIDUAL, pf.PF_GATE_UP_SWIGLU):
                 coop = T >= 512 or (T >= 256 and qt in (pf.PF_Q4_K, pf.PF_Q5_K, pf.PF_IQ4_XS))
                 sp = own_splits(T, 4096, 4096, epi)
+                rows = 8192 if epi == pf.PF_GATE_UP_SWIGLU else 4096
                 want = wb(pf.PF_Q4_0, 4096, 4096, T, epi, pf.PF_LEG_F16) if coop else \
-                    (sp * ((T * 4096 + 3) // 4 * 4) * 4 if sp > 1 else 0)
+                    (sp * ((T * rows + 3) // 4 * 4) * 4 if sp > 1 else 0)
                 assert wb(qt, 4096, 4096, T, epi, pf.PF_LEG_F16) == want
                 assert wb(qt, 4096, 4096, T, epi, pf.PF_LEG_F32) == 0
-    # the narrow down projection at T = 32: 32 tiles, 8 splits
-    assert wb(pf.PF_Q6_K, 4096, 12288, 32, pf.PF_RESIDUAL, pf.PF_LEG_F16) == 8 * 32 * 4096 * 4
+    # the narrow down projection at T = 32: 32 tiles, 16 splits; gate/up at T = 32: 192
+    # tiles of the 24576 rows, 4 splits of G [32][24576]
+    assert wb(pf.PF_Q6_K, 4096, 12288, 32, pf.PF_RESIDUAL, pf.PF_LEG_F16) == 16 * 32 * 4096 * 4
+    assert wb(pf.PF_Q4_K, 12288, 4096, 32, pf.PF_GATE_UP_SWIGLU, pf.PF_LEG_F16) == 4 * 32 * 24576 * 4
     # Q6_K rows of an odd number of super-blocks (2-byte aligned rows) keep its own GEMM
-    assert wb(pf.PF_Q6_K, 4096, 4352, 512, pf.PF_PLAIN, pf.PF_LEG_F16) == 0
+    # (512 rows, 4096 columns: 256 tiles, 3 splits)
+    assert own_splits(512, 4096, 4352, pf.PF_PLAIN) == 3
+    assert wb(pf.PF_Q6_K, 4096, 4352, 512, pf.PF_PLAIN, pf.PF_LEG_F16) == 3 * 512 * 4096 * 4
     assert wb(pf.PF_Q6_K, 4096, 4608, 512, pf.PF_PLAIN, pf.PF_LEG_F16) > 0
     # the GEMV (f16 leg: up to 2 rows, or up to 4 with the SwiGLU epilogue) takes none;
     # from 3 rows the f16 leg's PLAIN and RESIDUAL run the GEMM

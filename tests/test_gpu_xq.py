@@ -166,7 +166,7 @@ def test_xq_own_gemm_k_split(gpu, qtype, epi, T):
     """Where the cooperative kernel does not take them (F16 and Q6_K below 512 rows, the
     others below 256), the further types' own GEMM splits PLAIN / RESIDUAL K through the
     workspace when its tiles leave CUs idle: n = 150 is two 128-column tiles, so k = 4096
-    splits 8 ways (512 k each), and the sum kernel adds R and the splits in order.
+    splits 8 ways (512 k each; the cap), and the sum kernel adds R and the splits in order.
     pf_gemm_noalloc runs the same kernels: same bits."""
     import torch
     n, k = 150, 4096
@@ -185,6 +185,29 @@ def test_xq_own_gemm_k_split(gpu, qtype, epi, T):
     Wd, Xd = parity.to_dev(W), parity.to_dev(X)
     Yd = parity.to_dev(R) if R is not None else torch.full((T, n), float("nan"), device="cuda")
     gpu.gemm_noalloc(qtype, Wd, n, k, Xd, Yd, epi, F16)
+    torch.cuda.synchronize()
+    assert np.array_equal(Y.view(np.uint32), Yd.cpu().numpy().view(np.uint32))
+
+
+@pytest.mark.parametrize("T", [9, 64])
+@pytest.mark.parametrize("qtype", XQ, ids=lambda q: NAMES[q])
+def test_xq_own_gemm_swiglu_scratch(gpu, qtype, T):
+    """SwiGLU on the f16 leg with a workspace up to 64 rows: the gate and up rows run as one
+    PLAIN GEMM over the 2n rows, split 8 ways along k = 4096 into G, then silu(g) * u sums
+    each half in split order. pf_gemm_noalloc runs the same kernels: same bits."""
+    import torch
+    n, k = 150, 4096
+    seed = 720 + 7 * qtype + T
+    W = _weights(qtype, 2 * n, k, "edge", F16, seed)
+    X = synth.activations(T, k, workload_id=seed)
+    assert gpu.workspace_bytes(qtype, n, k, T, SWIGLU, F16) == 8 * ((T * 2 * n + 3) // 4 * 4) * 4
+    print("case xq swiglu scratch %s T=%d" % (NAMES[qtype], T), flush=True)
+    Y = parity.run_gpu(gpu, qtype, W, n, k, X, SWIGLU, F16, workspace=True)
+    ok, err = parity.check(qtype, W, n, k, X, Y, SWIGLU, F16)
+    assert ok, "parity failed: metric %.3e" % err
+    Wd, Xd = parity.to_dev(W), parity.to_dev(X)
+    Yd = torch.full((T, n), float("nan"), device="cuda")
+    gpu.gemm_noalloc(qtype, Wd, n, k, Xd, Yd, SWIGLU, F16)
     torch.cuda.synchronize()
     assert np.array_equal(Y.view(np.uint32), Yd.cpu().numpy().view(np.uint32))
 
