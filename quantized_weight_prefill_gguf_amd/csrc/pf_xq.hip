@@ -582,7 +582,10 @@ int xq_tile_rows(int T, int n, int epilogue, bool leg16) {
 // swiglu_apply_kernel sums each half in split order and applies silu(g) * u (above that
 // the fused epilogue runs unsplit, as G's round trip grows with T). The f32 leg does not
 // split. Deterministic either way.
-constexpr int XQ_SCRATCH_T = 64;
+#ifndef PF_XQ_SCRATCH_T
+#define PF_XQ_SCRATCH_T 64
+#endif
+constexpr int XQ_SCRATCH_T = PF_XQ_SCRATCH_T;
 int xq_splits(int T, int n, int k, int epilogue, bool leg16) {
     if (!leg16 || (epilogue == EPI_SWIGLU && T > XQ_SCRATCH_T)) return 1;
     const int rows = epilogue == EPI_SWIGLU ? 2 * n : n;  // the PLAIN GEMM's weight rows
