@@ -212,6 +212,29 @@ def test_xq_own_gemm_swiglu_scratch(gpu, qtype, T):
     assert np.array_equal(Y.view(np.uint32), Yd.cpu().numpy().view(np.uint32))
 
 
+@pytest.mark.parametrize("epi", [PLAIN, RESIDUAL, SWIGLU])
+@pytest.mark.parametrize("T", [40, 300, 520])
+@pytest.mark.parametrize("qtype", XQ, ids=lambda q: NAMES[q])
+def test_xq_strided_y_workspace(gpu, qtype, T, epi):
+    """pf_gemm_ex with a workspace into a strided Y: the further types' own GEMM split
+    through the workspace (T = 40, SwiGLU through G; T = 300 for F16 and Q6_K, whose SwiGLU
+    there takes no workspace), and the cooperative kernel (T = 300 for Q4_K, Q5_K and
+    IQ4_XS; T = 520 for all); the columns between Y's rows keep their bits."""
+    from tests.test_gpu_strided import check_gaps, run_strided
+    n, k = 200, 2048
+    rows = 2 * n if epi == SWIGLU else n
+    seed = 740 + 7 * qtype + 3 * epi + T
+    W = _weights(qtype, rows, k, "synth", F16, seed)
+    X = synth.activations(T, k, workload_id=seed)
+    R = synth.activations(T, n, workload_id=seed, tensor_id=synth.TENSOR_R) if epi == RESIDUAL else None
+    print("case xq strided %s T=%d epi=%d" % (NAMES[qtype], T, epi), flush=True)
+    Y, host, ldy, left = run_strided(gpu, qtype, W, n, k, X, epi, F16, R=R, pad_left=4, pad_right=3,
+                                     use_ws=True)
+    ok, err = parity.check(qtype, W, n, k, X, Y, epi, F16, R=R)
+    assert ok, "parity failed: metric %.3e" % err
+    check_gaps(host, left, n)
+
+
 @pytest.mark.parametrize("qtype", COOP, ids=lambda q: NAMES[q])
 def test_xq_coop_full_size_sampled(gpu, qtype):
     """The gate/up shape at T = 512 through the workspace (sampled outputs)."""
