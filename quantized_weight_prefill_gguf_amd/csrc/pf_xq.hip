@@ -162,17 +162,20 @@ __device__ __forceinline__ void decode_raw16(const Raw16<QT> &r, int e0, float (
         }
     } else if constexpr (QT == XQ_Q4_K || QT == XQ_Q5_K) {
         const int j = e0 >> 5;
-        const bool upper = (j & 1) != 0;
         uint32_t s, m;
         k_scale_min(r.hdr, j, s, m);
         const float a = fp16_bits_to_f32(r.hdr[0] & 0xFFFFu) * (float)s;
         const float b = fp16_bits_to_f32(r.hdr[0] >> 16) * (float)m;
+        // the codes of four weights a word (their nibble half, and for Q5_K bit j of qh
+        // as bit 4), each then one byte conversion; (d s) q is exact, so the FMA rounds
+        // once, as the subtraction does
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const uint32_t byte = byte_of(r.qs, i);
-            uint32_t q = upper ? (byte >> 4) : (byte & 15u);
-            if constexpr (QT == XQ_Q5_K) q += ((byte_of(r.qh, i) >> j) & 1u) << 4;
-            w[i] = a * (float)q - b;
+        for (int wd = 0; wd < 4; ++wd) {
+            uint32_t q4 = (r.qs[wd] >> (4 * (j & 1))) & 0x0F0F0F0Fu;
+            if constexpr (QT == XQ_Q5_K) q4 |= ((r.qh[wd] >> j) & 0x01010101u) << 4;
+            asm("" : "+v"(q4));
+#pragma unroll
+            for (int c = 0; c < 4; ++c) w[4 * wd + c] = fmaf(a, (float)((q4 >> (8 * c)) & 0xFFu), -b);
         }
     } else if constexpr (QT == XQ_IQ4_XS) {
         const int b = e0 >> 5;
@@ -201,13 +204,13 @@ __device__ __forceinline__ void decode_raw16(const Raw16<QT> &r, int e0, float (
         for (int i = 0; i < 4; ++i) {
             const uint32_t lw = __builtin_amdgcn_alignbyte(qlw[i + 1], qlw[i], r.sh);
             const uint32_t hw = __builtin_amdgcn_alignbyte(qhw[i + 1], qhw[i], r.sh);
+            // four 6-bit codes a word, each then one byte conversion; ds (q - 32) as the
+            // definition writes it (q - 32 is exact; an FMA with -32 ds would turn the
+            // -0 of a negative ds at q = 32 into +0)
+            uint32_t q4 = ((lw >> (4 * (c >> 1))) & 0x0F0F0F0Fu) | (((hw >> (2 * c)) & 0x03030303u) << 4);
+            asm("" : "+v"(q4));
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const uint32_t lb = (lw >> (8 * b)) & 0xFFu, hb = (hw >> (8 * b)) & 0xFFu;
-                const uint32_t lo = c < 2 ? (lb & 15u) : (lb >> 4);
-                const int q = (int)(lo | (((hb >> (2 * c)) & 3u) << 4));
-                w[4 * i + b] = ds * (float)(q - 32);
-            }
+            for (int b = 0; b < 4; ++b) w[4 * i + b] = ds * ((float)((q4 >> (8 * b)) & 0xFFu) - 32.0f);
         }
     }
 #pragma unroll
