@@ -417,15 +417,21 @@ __global__ __launch_bounds__(256) void xq_gemm_kernel(const uint8_t *__restrict_
     // Decode, then 16-byte LDS stores (row pitches and offsets are multiples of 16 bytes).
     auto store_step = [&](int ks, int slot, int buf) __attribute__((always_inline)) {
         float wv[16];
-        decode_raw16<QT>(raw[slot], ((ks_begin + min(ks, nks - 1)) * XKS + 16 * bhalf) % TR::ELEMS, wv);
         op_t *b = Bs + buf * B_ELEMS + brow * PADK + 16 * bhalf;
         op_t *a = As + buf * A_ELEMS + arow * PADK + acol;
         if constexpr (LEG16) {
             uint32_t p[8];
+            if constexpr (QT == XQ_F16) {
+                // the binary16 weights themselves (their f32 values round back to them)
+                reinterpret_cast<u4_t *>(b)[0] = raw[slot].a;
+                reinterpret_cast<u4_t *>(b)[1] = raw[slot].b;
+            } else {
+                decode_raw16<QT>(raw[slot], ((ks_begin + min(ks, nks - 1)) * XKS + 16 * bhalf) % TR::ELEMS, wv);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) p[j] = h2_bits(h2_t{(_Float16)wv[2 * j], (_Float16)wv[2 * j + 1]});
-            reinterpret_cast<u4_t *>(b)[0] = u4_t{p[0], p[1], p[2], p[3]};
-            reinterpret_cast<u4_t *>(b)[1] = u4_t{p[4], p[5], p[6], p[7]};
+                for (int j = 0; j < 8; ++j) p[j] = h2_bits(h2_t{(_Float16)wv[2 * j], (_Float16)wv[2 * j + 1]});
+                reinterpret_cast<u4_t *>(b)[0] = u4_t{p[0], p[1], p[2], p[3]};
+                reinterpret_cast<u4_t *>(b)[1] = u4_t{p[4], p[5], p[6], p[7]};
+            }
 #pragma unroll
             for (int i = 0; i < AF4 / 2; ++i) {
 #pragma unroll
@@ -436,6 +442,7 @@ __global__ __launch_bounds__(256) void xq_gemm_kernel(const uint8_t *__restrict_
                 reinterpret_cast<u4_t *>(a)[i] = u4_t{p[0], p[1], p[2], p[3]};
             }
         } else {
+            decode_raw16<QT>(raw[slot], ((ks_begin + min(ks, nks - 1)) * XKS + 16 * bhalf) % TR::ELEMS, wv);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 reinterpret_cast<f4_t *>(b)[j] = f4_t{wv[4 * j], wv[4 * j + 1], wv[4 * j + 2], wv[4 * j + 3]};
