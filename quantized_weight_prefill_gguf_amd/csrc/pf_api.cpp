@@ -32,7 +32,7 @@ int block_bytes(int qtype) {
 }
 int block_elems(int qtype) { return (qtype >= PF_Q4_K && qtype <= PF_IQ4_XS) ? 256 : 32; }
 // The further types (F16, Q4_K, Q5_K, Q6_K, IQ4_XS) run their own kernels (pf_xq.hip), except
-// where the f16 leg's workspace GEMM decodes them (pf::f16_coop_takes_xq); on the f16 leg
+// where the f16 leg's workspace GEMM decodes them (pf::f16_takes_xq); on the f16 leg
 // their own GEMM splits K through the workspace where its tiles leave CUs idle.
 bool is_xq(int qtype) { return qtype >= PF_F16 && qtype <= PF_IQ4_XS; }
 int64_t w_bytes_of(int qtype, int64_t rows, int64_t k) { return rows * (k / block_elems(qtype)) * block_bytes(qtype); }
@@ -89,7 +89,7 @@ hipError_t launch_gemv_q(const pf::GemmArgs &a, int leg, hipStream_t s) {
 // else 0.
 int64_t ws_need(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int leg, int use) {
     if (use != PF_PATH_GEMM || leg != PF_LEG_F16) return 0;
-    if (!is_xq(qtype) || pf::f16_coop_takes_xq(qtype, (int)T, (int)k))
+    if (!is_xq(qtype) || pf::f16_takes_xq(qtype, (int)T, (int)k))
         return pf::f16_ws_bytes((int)T, (int)n, (int)k, epilogue);
     return pf::xq_ws_bytes((int)T, (int)n, (int)k, epilogue, true);  // their own GEMM's K split
 }
@@ -142,7 +142,7 @@ int gemm_impl(int qtype, const void *W, int64_t n, int64_t k, const float *X, in
     a.k = (int)k;
     a.T = (int)T;
     hipError_t err;
-    if (is_xq(qtype) && (need == 0 || !pf::f16_coop_takes_xq(qtype, (int)T, (int)k)))
+    if (is_xq(qtype) && (need == 0 || !pf::f16_takes_xq(qtype, (int)T, (int)k)))
         err = use == PF_PATH_GEMV ? pf::launch_xq_gemv(a, s)
                                   : pf::launch_xq_gemm(a, leg == PF_LEG_F16, need > 0 ? ws : nullptr, s);
     else if (use == PF_PATH_GEMV)

@@ -147,6 +147,10 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
                      int splits, long pstride) {
     using CT = ChunkTraits<QT>;
     constexpr int BB = CT::BB;
+    // Further types (Q4_K, Q5_K, IQ4_XS): short-chunk tiles on the fp16 X copy only; a
+    // row's 256-k chunk is one super-block, and step blk its sub-block blk.
+    constexpr bool XQ = coop_xq<QT>();
+    static_assert(!XQ || (XH && ROW1 && QT != XQ_F16 && QT != XQ_Q6_K), "further types: short-chunk tiles");
     // Waves: WVM x WVN over the tile. ROW1 tiles (few token rows) put all four side
     // by side along the weight rows, so that no two decode the same columns.
     constexpr int WVM = ROW1 ? 1 : 2;
@@ -158,10 +162,12 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
     constexpr int XH4 = MT >= 64 ? MT / 64 : 1;  // fp16 X: 16-byte loads per thread per step
     // fp16 X staging covers 64 rows per pass; a 32-row tile uses threads < 128 only.
     const bool xh_store = MT >= 64 || threadIdx.x < 128;
-    constexpr int U4 = CT::U4;                      // 16-byte pieces per row chunk
+    constexpr int U4 = CT::U4;                      // pieces per row chunk
+    constexpr int PIECE = chunk_piece<QT>();        // bytes per piece (16; IQ4_XS 8)
     constexpr int WROW = CT::ROW;
     constexpr int WBUF = NW * WROW + 16;            // +16: decode reads a dword past a row
     constexpr int NW32 = (QT == Q4_0) ? 2 : 4;      // qs words per lane per block
+    typedef typename std::conditional<PIECE == 16, u4_t, u2_t>::type piece_t;
 
     // One LDS block: the K loop's two X buffers and two weight chunks; after the
     // loop, the SwiGLU epilogue reuses its start as 4 per-wave 32 x 36 float slots.
@@ -202,7 +208,7 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
     const int nch = c_end - c_begin;
     if (nch <= 0) return;  // cannot happen (splits <= chunks); keeps the loop simple
     const int nsteps = 8 * nch;
-    const uint32_t row_bytes = (uint32_t)(k >> 5) * BB;
+    const uint32_t row_bytes = XQ ? (uint32_t)(k >> 8) * WROW : (uint32_t)(k >> 5) * BB;
 
     // ---- staging assignments (fixed over the K loop), as 32-bit byte offsets
     // from uniform bases. Global loads are all unconditional so that the wait
@@ -239,7 +245,7 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
         xdst = (tid >> 3) * 32 + ((((tid & 7) >> 1) ^ ((tid >> 5) & 3)) << 3) + 4 * (tid & 1);
     }
     // Weight staging. Slice S of a chunk is its rows S RS .. S RS + RS - 1 (RS = NW
-    // / 8), whole: RS * U4 16-byte pieces, which the threads take in order, piece
+    // / 8), whole: RS * U4 pieces (16 bytes, IQ4_XS 8), which the threads take in order, piece
     // f = tid + 256 i being piece f % U4 of slice row f / U4. Consecutive lanes thus
     // read consecutive bytes of a row. Since RS * U4 is the same for every slice,
     // a thread's (row in slice, piece) is fixed; only the weight row of slice row
@@ -257,12 +263,12 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
         wvalid[i] = f < SP;
         const int ff = wvalid[i] ? f : 0;
         const int rr = ff / U4, pp = ff % U4;
-        wdst[i] = rr * WROW + 16 * pp;
+        wdst[i] = rr * WROW + PIECE * pp;
 #pragma unroll
         for (int S = 0; S < 8; ++S) {
             int gr = f16_weight_row<EPI, NW>(tn, S * RS + rr, n);
             gr = gr < 0 ? 0 : gr;
-            wsrc[S][i] = (uint32_t)gr * row_bytes + 16 * pp;
+            wsrc[S][i] = (uint32_t)gr * row_bytes + PIECE * pp;
         }
     }
 
@@ -287,7 +293,7 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
     constexpr int PD = 4;
     f4_t xr[XF4];         // f32 X for the staging write of the next step
     u4_t xh[PD][XH4];     // fp16 X for the staging writes of the next PD steps
-    u4_t wr[PD][NPT];     // weight slices for the writes of the next PD steps
+    piece_t wr[PD][NPT];  // weight slices for the writes of the next PD steps
 
     auto load_a = [&](int xb, h8_t (&dst)[IT][2]) __attribute__((always_inline)) {
 #pragma unroll
@@ -299,24 +305,58 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
     // This lane's raw bytes of block `blk` (compile-time) for its JT B columns: the
     // scale and the aligned dwords that hold its qs words (NRAW of them; when the
     // qs start 2 bytes into a dword, a word straddles two dwords).
-    constexpr int NRAW = (QT == Q4_0) ? 3 : 6;
+    // Further types: the header dwords (Q4_K / Q5_K: d, dmin and the 12 scale bytes;
+    // IQ4_XS: d, scales_h, scales_l), then the dwords of codes for k = 8 h .. 8 h + 7
+    // and 16 + 8 h .. 16 + 8 h + 7 of sub-block blk (Q4_K / Q5_K: the qs bytes, nibble
+    // half blk % 2; IQ4_XS: one 8-byte run whose low nibbles are the first eight and
+    // high nibbles the second), and for Q5_K the qh dwords of the same k.
+    constexpr int NRAW = QT == XQ_Q5_K ? 12 : QT == XQ_Q4_K ? 8 : QT == XQ_IQ4_XS ? 4 : (QT == Q4_0) ? 3 : 6;
     auto read_b = [&](const uint8_t *wb, auto blk_c, uint32_t (&d16)[JT], uint32_t (&raw)[JT][NRAW])
         __attribute__((always_inline)) {
         constexpr int blk = decltype(blk_c)::value;
         constexpr int SH = (blk * BB + 2) & 3;
+        if constexpr (XQ) {
+            (void)d16;
 #pragma unroll
-        for (int j = 0; j < JT; ++j) {
-            const int base = bbase + j * 32 * WROW + blk * BB;
-            d16[j] = *reinterpret_cast<const uint16_t *>(wb + base);
-            const uint32_t *al = reinterpret_cast<const uint32_t *>(wb + base + 2 + 8 * h - SH);
-            if constexpr (SH == 0) {
+            for (int j = 0; j < JT; ++j) {
+                const uint8_t *rb = wb + bbase + j * 32 * WROW;  // the column's super-block
+                if constexpr (QT == XQ_IQ4_XS) {
+                    const u2_t hd = *reinterpret_cast<const u2_t *>(rb);
+                    const u2_t cw = *reinterpret_cast<const u2_t *>(rb + 8 + 16 * blk + 8 * h);
+                    raw[j][0] = hd[0]; raw[j][1] = hd[1];
+                    raw[j][2] = cw[0]; raw[j][3] = cw[1];
+                } else {
+                    constexpr int QS = QT == XQ_Q5_K ? 48 : 16;  // qs offset in the super-block
+                    const u4_t hd = *reinterpret_cast<const u4_t *>(rb);
+                    const u2_t q0 = *reinterpret_cast<const u2_t *>(rb + QS + 32 * (blk >> 1) + 8 * h);
+                    const u2_t q1 = *reinterpret_cast<const u2_t *>(rb + QS + 32 * (blk >> 1) + 16 + 8 * h);
 #pragma unroll
-                for (int w = 0; w < NW32; ++w) raw[j][w] = al[(w & 1) + 4 * (w >> 1)];
-            } else {
+                    for (int e = 0; e < 4; ++e) raw[j][e] = hd[e];
+                    raw[j][4] = q0[0]; raw[j][5] = q0[1];
+                    raw[j][6] = q1[0]; raw[j][7] = q1[1];
+                    if constexpr (QT == XQ_Q5_K) {
+                        const u2_t h0 = *reinterpret_cast<const u2_t *>(rb + 16 + 8 * h);
+                        const u2_t h1 = *reinterpret_cast<const u2_t *>(rb + 32 + 8 * h);
+                        raw[j][8] = h0[0]; raw[j][9] = h0[1];
+                        raw[j][10] = h1[0]; raw[j][11] = h1[1];
+                    }
+                }
+            }
+        } else {
 #pragma unroll
-                for (int g = 0; g < NW32 / 2; ++g)
+            for (int j = 0; j < JT; ++j) {
+                const int base = bbase + j * 32 * WROW + blk * BB;
+                d16[j] = *reinterpret_cast<const uint16_t *>(wb + base);
+                const uint32_t *al = reinterpret_cast<const uint32_t *>(wb + base + 2 + 8 * h - SH);
+                if constexpr (SH == 0) {
 #pragma unroll
-                    for (int e = 0; e < 3; ++e) raw[j][3 * g + e] = al[4 * g + e];
+                    for (int w = 0; w < NW32; ++w) raw[j][w] = al[(w & 1) + 4 * (w >> 1)];
+                } else {
+#pragma unroll
+                    for (int g = 0; g < NW32 / 2; ++g)
+#pragma unroll
+                        for (int e = 0; e < 3; ++e) raw[j][3 * g + e] = al[4 * g + e];
+                }
             }
         }
     };
@@ -325,30 +365,79 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
                         h8_t (&dst)[JT][2]) __attribute__((always_inline)) {
         constexpr int blk = decltype(blk_c)::value;
         constexpr int SH = (blk * BB + 2) & 3;
+        if constexpr (XQ) {
+            // Each weight's f32 value as the further types define it, made opaque, then
+            // binary16 (RNE): Q4_K / Q5_K (d s) q - dmin m as one FMA ((d s) q is exact,
+            // so it rounds once, as the subtraction would); IQ4_XS d (ls - 32) grid,
+            // exact in f32.
+            (void)d16;
 #pragma unroll
-        for (int j = 0; j < JT; ++j) {
-            uint32_t q[NW32];
+            for (int j = 0; j < JT; ++j) {
+                uint32_t p[8];
+                if constexpr (QT == XQ_IQ4_XS) {
+                    const uint32_t h0 = raw[j][0], sl = raw[j][1];
+                    const uint32_t ls = ((sl >> (4 * blk)) & 15u) | (((h0 >> (16 + 2 * blk)) & 3u) << 4);
+                    const float dl = fp16_bits_to_f32(h0 & 0xFFFFu) * (float)((int)ls - 32);
 #pragma unroll
-            for (int w = 0; w < NW32; ++w) {
-                if constexpr (SH == 0)
-                    q[w] = raw[j][w];
-                else
-                    q[w] = __builtin_amdgcn_alignbyte(raw[j][3 * (w >> 1) + (w & 1) + 1],
-                                                      raw[j][3 * (w >> 1) + (w & 1)], SH);
+                    for (int w = 0; w < 4; ++w) {
+                        const uint32_t g = iq4_grid_bytes((raw[j][2 + (w & 1)] >> (4 * (w >> 1))) & 0x0F0F0F0Fu);
+                        float v[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            v[e] = dl * (float)(int8_t)(uint8_t)(g >> (8 * e));
+                            asm("" : "+v"(v[e]));
+                        }
+                        p[2 * w] = h2_bits(h2_t{(_Float16)v[0], (_Float16)v[1]});
+                        p[2 * w + 1] = h2_bits(h2_t{(_Float16)v[2], (_Float16)v[3]});
+                    }
+                } else {
+                    uint32_t sc, mn;
+                    kq_scale_min<blk>(u4_t{raw[j][0], raw[j][1], raw[j][2], raw[j][3]}, sc, mn);
+                    const float a = fp16_bits_to_f32(raw[j][0] & 0xFFFFu) * (float)sc;
+                    const float b = fp16_bits_to_f32(raw[j][0] >> 16) * (float)mn;
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        uint32_t q = (raw[j][4 + w] >> (4 * (blk & 1))) & 0x0F0F0F0Fu;
+                        if constexpr (QT == XQ_Q5_K) q |= ((raw[j][8 + w] >> blk) & 0x01010101u) << 4;
+                        float v[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            v[e] = fmaf(a, (float)((q >> (8 * e)) & 0xFFu), -b);
+                            asm("" : "+v"(v[e]));
+                        }
+                        p[2 * w] = h2_bits(h2_t{(_Float16)v[0], (_Float16)v[1]});
+                        p[2 * w + 1] = h2_bits(h2_t{(_Float16)v[2], (_Float16)v[3]});
+                    }
+                }
+                dst[j][0] = __builtin_bit_cast(h8_t, u4_t{p[0], p[1], p[2], p[3]});
+                dst[j][1] = __builtin_bit_cast(h8_t, u4_t{p[4], p[5], p[6], p[7]});
             }
-            const h2_t d2 = as_h2(d16[j] | (d16[j] << 16));
-            uint32_t p[8];
-            if constexpr (QT == Q4_0) {
-                q4_word_decode(q[0], d2, p[0], p[1], p[4], p[5]);
-                q4_word_decode(q[1], d2, p[2], p[3], p[6], p[7]);
-            } else {
-                q8_word_to_h4(q[0], d2, p + 0);
-                q8_word_to_h4(q[1], d2, p + 2);
-                q8_word_to_h4(q[2], d2, p + 4);
-                q8_word_to_h4(q[3], d2, p + 6);
+        } else {
+#pragma unroll
+            for (int j = 0; j < JT; ++j) {
+                uint32_t q[NW32];
+#pragma unroll
+                for (int w = 0; w < NW32; ++w) {
+                    if constexpr (SH == 0)
+                        q[w] = raw[j][w];
+                    else
+                        q[w] = __builtin_amdgcn_alignbyte(raw[j][3 * (w >> 1) + (w & 1) + 1],
+                                                          raw[j][3 * (w >> 1) + (w & 1)], SH);
+                }
+                const h2_t d2 = as_h2(d16[j] | (d16[j] << 16));
+                uint32_t p[8];
+                if constexpr (QT == Q4_0) {
+                    q4_word_decode(q[0], d2, p[0], p[1], p[4], p[5]);
+                    q4_word_decode(q[1], d2, p[2], p[3], p[6], p[7]);
+                } else {
+                    q8_word_to_h4(q[0], d2, p + 0);
+                    q8_word_to_h4(q[1], d2, p + 2);
+                    q8_word_to_h4(q[2], d2, p + 4);
+                    q8_word_to_h4(q[3], d2, p + 6);
+                }
+                dst[j][0] = __builtin_bit_cast(h8_t, u4_t{p[0], p[1], p[2], p[3]});
+                dst[j][1] = __builtin_bit_cast(h8_t, u4_t{p[4], p[5], p[6], p[7]});
             }
-            dst[j][0] = __builtin_bit_cast(h8_t, u4_t{p[0], p[1], p[2], p[3]});
-            dst[j][1] = __builtin_bit_cast(h8_t, u4_t{p[4], p[5], p[6], p[7]});
         }
     };
     // f32 X: registers (one step ahead) -> fp16 in LDS.
@@ -375,17 +464,17 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
     };
 
     // Slice S (compile-time) of chunk `chunk`: load to registers / store to LDS.
-    auto fetch_slice = [&](int chunk, auto s_c, u4_t (&dst)[NPT]) __attribute__((always_inline)) {
+    auto fetch_slice = [&](int chunk, auto s_c, piece_t (&dst)[NPT]) __attribute__((always_inline)) {
         constexpr int S = decltype(s_c)::value;
         const uint8_t *src = wbase + (size_t)min(chunk, nch - 1) * WROW;
 #pragma unroll
-        for (int i = 0; i < NPT; ++i) dst[i] = *reinterpret_cast<const u4_t *>(src + wsrc[S][i]);
+        for (int i = 0; i < NPT; ++i) dst[i] = *reinterpret_cast<const piece_t *>(src + wsrc[S][i]);
     };
-    auto store_slice = [&](uint8_t *buf, auto s_c, const u4_t (&src)[NPT]) __attribute__((always_inline)) {
+    auto store_slice = [&](uint8_t *buf, auto s_c, const piece_t (&src)[NPT]) __attribute__((always_inline)) {
         constexpr int S = decltype(s_c)::value;
 #pragma unroll
         for (int i = 0; i < NPT; ++i)
-            if (wvalid[i]) *reinterpret_cast<u4_t *>(buf + S * RS * WROW + wdst[i]) = src[i];
+            if (wvalid[i]) *reinterpret_cast<piece_t *>(buf + S * RS * WROW + wdst[i]) = src[i];
     };
 
     // ---- prologue. LDS: chunk 0, slices 0 and 1 of chunk 1, X(0), X(1).
@@ -395,7 +484,7 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
     {
         // All ten slice loads are issued before the first store (one memory round
         // trip, not ten in a row).
-        u4_t tmp[10][NPT];
+        piece_t tmp[10][NPT];
         fetch_slice(0, std::integral_constant<int, 0>{}, tmp[0]);
         fetch_slice(0, std::integral_constant<int, 1>{}, tmp[1]);
         fetch_slice(0, std::integral_constant<int, 2>{}, tmp[2]);
@@ -1355,26 +1444,42 @@ hipError_t launch_cfg(const GemmArgs &a, int splits, const uint16_t *xh, long ps
     const int tm = (a.T + MT - 1) / MT;
     const int tn = (a.n + OUT - 1) / OUT;
     const int total = tm * tn * splits;
-    if (xh)
+    if constexpr (coop_xq<QT>()) {
+        // further types: the fp16 X copy only
+        if (!xh) return hipErrorInvalidValue;
         hipLaunchKernelGGL((gemm_f16_kernel<QT, EPI, MT, NW, SPLIT, true, ROW1>), dim3(total), dim3(256), 0,
                            s, a.W, (const void *)xh, a.Y, a.n, a.ldy, a.k, a.T, tm, tn, splits, pstride);
-    else
+    } else if (xh) {
+        hipLaunchKernelGGL((gemm_f16_kernel<QT, EPI, MT, NW, SPLIT, true, ROW1>), dim3(total), dim3(256), 0,
+                           s, a.W, (const void *)xh, a.Y, a.n, a.ldy, a.k, a.T, tm, tn, splits, pstride);
+    } else {
         hipLaunchKernelGGL((gemm_f16_kernel<QT, EPI, MT, NW, SPLIT, false, ROW1>), dim3(total), dim3(256), 0,
                            s, a.W, (const void *)a.X, a.Y, a.n, a.ldy, a.k, a.T, tm, tn, splits, pstride);
+    }
     return hipGetLastError();
 }
 
 template <int QT, int EPI, bool SPLIT>
 hipError_t launch_split(const GemmArgs &a, TileChoice tc, const uint16_t *xh, hipStream_t s,
                         long pstride = 0) {
-    switch (tc.cfg) {
-    case 0: return launch_cfg<QT, EPI, 256, 192, SPLIT>(a, tc.splits, xh, pstride, s);
-    case 1: return launch_cfg<QT, EPI, 256, 128, SPLIT>(a, tc.splits, xh, pstride, s);
-    case 2: return launch_cfg<QT, EPI, 128, 128, SPLIT>(a, tc.splits, xh, pstride, s);
-    case 3: return launch_cfg<QT, EPI, 64, 64, SPLIT>(a, tc.splits, xh, pstride, s);
-    case 4: return launch_cfg<QT, EPI, 32, 128, SPLIT, true>(a, tc.splits, xh, pstride, s);
-    case 5: return launch_cfg<QT, EPI, 64, 128, SPLIT, true>(a, tc.splits, xh, pstride, s);
-    default: return launch_cfg<QT, EPI, 128, 128, SPLIT, true>(a, tc.splits, xh, pstride, s);
+    if constexpr (coop_xq<QT>()) {
+        // further types: the short-chunk tiles only (T <= SHORT_T)
+        switch (tc.cfg) {
+        case 4: return launch_cfg<QT, EPI, 32, 128, SPLIT, true>(a, tc.splits, xh, pstride, s);
+        case 5: return launch_cfg<QT, EPI, 64, 128, SPLIT, true>(a, tc.splits, xh, pstride, s);
+        case 6: return launch_cfg<QT, EPI, 128, 128, SPLIT, true>(a, tc.splits, xh, pstride, s);
+        default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (tc.cfg) {
+        case 0: return launch_cfg<QT, EPI, 256, 192, SPLIT>(a, tc.splits, xh, pstride, s);
+        case 1: return launch_cfg<QT, EPI, 256, 128, SPLIT>(a, tc.splits, xh, pstride, s);
+        case 2: return launch_cfg<QT, EPI, 128, 128, SPLIT>(a, tc.splits, xh, pstride, s);
+        case 3: return launch_cfg<QT, EPI, 64, 64, SPLIT>(a, tc.splits, xh, pstride, s);
+        case 4: return launch_cfg<QT, EPI, 32, 128, SPLIT, true>(a, tc.splits, xh, pstride, s);
+        case 5: return launch_cfg<QT, EPI, 64, 128, SPLIT, true>(a, tc.splits, xh, pstride, s);
+        default: return launch_cfg<QT, EPI, 128, 128, SPLIT, true>(a, tc.splits, xh, pstride, s);
+        }
     }
 }
 
@@ -1588,10 +1693,12 @@ static int coop_splits(int T, int n, int k, int epilogue) {
     return splits;
 }
 
-// Q4_K, Q5_K and IQ4_XS from 256 rows (both tiles); F16 and Q6_K (k % 512 == 0) from
-// COOP_T512 (their 256 x 192 tile's staging would need more than one piece per thread).
-bool f16_coop_takes_xq(int qtype, int T, int k) {
-    if (qtype == XQ_Q4_K || qtype == XQ_Q5_K || qtype == XQ_IQ4_XS) return T >= 256;
+// The further types this file's GEMMs take on the workspace path: Q4_K, Q5_K and
+// IQ4_XS up to SHORT_T rows (the short-chunk tiles) and from 256 (the cooperative
+// kernel, both tiles); F16 and Q6_K (k % 512 == 0) from COOP_T512 (their 256 x 192
+// tile's staging would need more than one piece per thread).
+bool f16_takes_xq(int qtype, int T, int k) {
+    if (qtype == XQ_Q4_K || qtype == XQ_Q5_K || qtype == XQ_IQ4_XS) return T <= SHORT_T || T >= 256;
     return T >= COOP_T512 && (qtype == XQ_F16 || (qtype == XQ_Q6_K && k % 512 == 0));
 }
 
@@ -1722,7 +1829,7 @@ hipError_t launch_gemm_f16_prepared(const GemmArgs &a, void *workspace, hipStrea
         switch (a.qtype) {
         case Q4_0: return launch_coop_q<Q4_0>(a, xh, s);
         case Q8_0: return launch_coop_q<Q8_0>(a, xh, s);
-        // further types (f16_coop_takes_xq)
+        // further types (f16_takes_xq)
         case XQ_Q4_K: return launch_coop_q<XQ_Q4_K>(a, xh, s);
         case XQ_Q5_K: return launch_coop_q<XQ_Q5_K>(a, xh, s);
         case XQ_IQ4_XS: return launch_coop_q<XQ_IQ4_XS>(a, xh, s);
@@ -1733,9 +1840,16 @@ hipError_t launch_gemm_f16_prepared(const GemmArgs &a, void *workspace, hipStrea
     }
     // split-K partial sums (or the SwiGLU scratch G) go behind the fp16 X
     float *ps = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(workspace) + ws_x_bytes(a.T, a.k));
-    if (swiglu_via_scratch(a.T, a.epilogue))
-        return a.qtype == Q4_0 ? launch_swiglu_scratch<Q4_0>(a, xh, ps, s) : launch_swiglu_scratch<Q8_0>(a, xh, ps, s);
-    return a.qtype == Q4_0 ? launch_q<Q4_0>(a, xh, s, ps) : launch_q<Q8_0>(a, xh, s, ps);
+    const bool g = swiglu_via_scratch(a.T, a.epilogue);
+    switch (a.qtype) {
+    case Q4_0: return g ? launch_swiglu_scratch<Q4_0>(a, xh, ps, s) : launch_q<Q4_0>(a, xh, s, ps);
+    case Q8_0: return g ? launch_swiglu_scratch<Q8_0>(a, xh, ps, s) : launch_q<Q8_0>(a, xh, s, ps);
+    // further types up to SHORT_T rows (f16_takes_xq)
+    case XQ_Q4_K: return g ? launch_swiglu_scratch<XQ_Q4_K>(a, xh, ps, s) : launch_q<XQ_Q4_K>(a, xh, s, ps);
+    case XQ_Q5_K: return g ? launch_swiglu_scratch<XQ_Q5_K>(a, xh, ps, s) : launch_q<XQ_Q5_K>(a, xh, s, ps);
+    case XQ_IQ4_XS: return g ? launch_swiglu_scratch<XQ_IQ4_XS>(a, xh, ps, s) : launch_q<XQ_IQ4_XS>(a, xh, s, ps);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_gemm_f16_ws(const GemmArgs &a, void *workspace, hipStream_t s) {

@@ -40,10 +40,10 @@ hipError_t launch_gemm_f16_prepared(const GemmArgs &a, void *workspace, hipStrea
 // multiple of 32), and for T >= 256 with a K split, behind it (at the next 256-byte
 // boundary) one [T][n] f32 block of partial sums per split.
 int64_t f16_ws_bytes(int T, int n, int k, int epilogue);
-// The further types the f16 workspace path's cooperative-decode GEMM takes (Q4_K, Q5_K
-// and IQ4_XS from 256 rows; F16, and Q6_K with k % 512 == 0, from 512); the others keep
-// their own GEMM.
-bool f16_coop_takes_xq(int qtype, int T, int k);
+// The further types the f16 workspace path's GEMMs take (Q4_K, Q5_K and IQ4_XS up to
+// 128 rows on the short-chunk tiles and from 256 on the cooperative-decode kernel; F16,
+// and Q6_K with k % 512 == 0, from 512); the others keep their own GEMM.
+bool f16_takes_xq(int qtype, int T, int k);
 // Floats between the [T][n] partial-sum blocks of a K split, and Y = [R +] the `splits`
 // blocks at ps added in split order (PLAIN or RESIDUAL; a.Y, a.ldy, a.T, a.n).
 long part_stride(int T, int n);

@@ -159,20 +159,92 @@ def test_xq_coop_256_rows(gpu, qtype, epi):
     assert ok, "parity failed: metric %.3e" % err
 
 
+KQ = [synth.Q4_K, synth.Q5_K, synth.IQ4_XS]
+
+
+@pytest.mark.parametrize("epi", [PLAIN, RESIDUAL, SWIGLU])
+@pytest.mark.parametrize("T", [9, 32, 33, 64, 65, 128])
+@pytest.mark.parametrize("kind", ["synth", "edge"])
+@pytest.mark.parametrize("qtype", KQ, ids=lambda q: NAMES[q])
+def test_xq_short_tiles_every_output(gpu, qtype, kind, T, epi):
+    """On the f16 leg with a workspace up to 128 rows, Q4_K, Q5_K and IQ4_XS take Q4_0's
+    short-chunk tiles (32, 64 or 128 token rows x 128 weight rows, four waves side by
+    side, each decoding its own B fragments from the staged super-blocks): T = 9 .. 128
+    covers each tile height, full and ragged; n = 150 is two weight tiles, the second
+    ragged; at k = 4096 PLAIN and RESIDUAL split K (partial sums, then their fixed-order
+    sum), and SwiGLU up to 64 rows runs as a split PLAIN GEMM over the 2n rows into G.
+    The workspace is Q4_0's at the same sizes. pf_gemm_noalloc runs the same kernels:
+    same bits."""
+    import torch
+    n, k = 150, 4096
+    rows = 2 * n if epi == SWIGLU else n
+    seed = 760 + 7 * qtype + 3 * epi + T + (kind == "edge")
+    W = _weights(qtype, rows, k, kind, F16, seed)
+    X = synth.activations(T, k, workload_id=seed)
+    R = synth.activations(T, n, workload_id=seed, tensor_id=synth.TENSOR_R) if epi == RESIDUAL else None
+    need = gpu.workspace_bytes(qtype, n, k, T, epi, F16)
+    assert need >= T * k * 2 and need == gpu.workspace_bytes(synth.Q4_0, n, k, T, epi, F16)
+    print("case xq short %s %s T=%d epi=%d" % (NAMES[qtype], kind, T, epi), flush=True)
+    Y = parity.run_gpu(gpu, qtype, W, n, k, X, epi, F16, R=R, workspace=True)
+    ok, err = parity.check(qtype, W, n, k, X, Y, epi, F16, R=R)
+    assert ok, "parity failed: metric %.3e" % err
+    Wd, Xd = parity.to_dev(W), parity.to_dev(X)
+    Yd = parity.to_dev(R) if R is not None else torch.full((T, n), float("nan"), device="cuda")
+    gpu.gemm_noalloc(qtype, Wd, n, k, Xd, Yd, epi, F16)
+    torch.cuda.synchronize()
+    assert np.array_equal(Y.view(np.uint32), Yd.cpu().numpy().view(np.uint32))
+
+
+@pytest.mark.parametrize("qtype", KQ, ids=lambda q: NAMES[q])
+def test_xq_short_tiles_shortest_k(gpu, qtype):
+    """k = 256 (one super-block per row: a single chunk, no split) at T = 20 and 100."""
+    n, k = 70, 256
+    for T, epi in [(20, PLAIN), (100, SWIGLU), (100, RESIDUAL)]:
+        rows = 2 * n if epi == SWIGLU else n
+        seed = 780 + 7 * qtype + T + epi
+        W = _weights(qtype, rows, k, "edge", F16, seed)
+        X = synth.activations(T, k, workload_id=seed)
+        R = synth.activations(T, n, workload_id=seed, tensor_id=synth.TENSOR_R) if epi == RESIDUAL else None
+        print("case xq short k=256 %s T=%d epi=%d" % (NAMES[qtype], T, epi), flush=True)
+        Y = parity.run_gpu(gpu, qtype, W, n, k, X, epi, F16, R=R, workspace=True)
+        ok, err = parity.check(qtype, W, n, k, X, Y, epi, F16, R=R)
+        assert ok, "parity failed: metric %.3e" % err
+
+
+@pytest.mark.parametrize("shape", ["gate_up_T32", "down_T64"])
+@pytest.mark.parametrize("qtype", KQ, ids=lambda q: NAMES[q])
+def test_xq_short_tiles_full_size_sampled(gpu, qtype, shape):
+    """The model shapes on the short-chunk tiles: gate/up 2 x 12288 x 4096 at T = 32 (G
+    route) and the down projection 4096 x 12288 RESIDUAL at T = 64 (sampled outputs)."""
+    if shape == "gate_up_T32":
+        n, k, T, epi = 12288, 4096, 32, SWIGLU
+        W = synth.quantize(qtype, np.concatenate([synth.weights_f32(n, k, workload_id=652),
+                                                  synth.weights_f32(n, k, workload_id=652,
+                                                                    tensor_id=synth.TENSOR_W_UP)]))
+    else:
+        n, k, T, epi = 4096, 12288, 64, RESIDUAL
+        W = synth.quantize(qtype, synth.weights_f32(n, k, workload_id=653))
+    X = synth.activations(T, k, workload_id=654)
+    R = synth.activations(T, n, workload_id=654, tensor_id=synth.TENSOR_R) if epi == RESIDUAL else None
+    print("case xq short full %s %s" % (NAMES[qtype], shape), flush=True)
+    Y = parity.run_gpu(gpu, qtype, W, n, k, X, epi, F16, R=R, workspace=True)
+    ok, err = parity.check(qtype, W, n, k, X, Y, epi, F16, R=R, samples=4096)
+    assert ok, "parity failed: metric %.3e" % err
+
+
 @pytest.mark.parametrize("T", [9, 130, 300])
 @pytest.mark.parametrize("epi", [PLAIN, RESIDUAL])
 @pytest.mark.parametrize("qtype", XQ, ids=lambda q: NAMES[q])
 def test_xq_own_gemm_k_split(gpu, qtype, epi, T):
-    """Where the cooperative kernel does not take them (F16 and Q6_K below 512 rows, the
-    others below 256), the further types' own GEMM splits PLAIN / RESIDUAL K through the
-    workspace when its tiles leave CUs idle: n = 150 is two 128-column tiles, so k = 4096
-    splits 8 ways (512 k each; the cap), and the sum kernel adds R and the splits in order.
-    pf_gemm_noalloc runs the same kernels: same bits."""
+    """Where the f16 GEMMs of Q4_0 do not take them (F16 and Q6_K below 512 rows, the
+    others from 129 to 255), the further types' own GEMM splits PLAIN / RESIDUAL K through
+    the workspace when its tiles leave CUs idle: n = 150 is two 128-column tiles, so k =
+    4096 splits 8 ways (512 k each; the cap), and the sum kernel adds R and the splits in
+    order. pf_gemm_noalloc runs the same kernels: same bits."""
     import torch
     n, k = 150, 4096
-    coop = T >= 256 and qtype in (synth.Q4_K, synth.Q5_K, synth.IQ4_XS)
-    if coop:
-        pytest.skip("the cooperative kernel's range")
+    if qtype in KQ and (T <= 128 or T >= 256):
+        pytest.skip("the short-chunk tiles' or the cooperative kernel's range")
     seed = 700 + 7 * qtype + 3 * epi + T
     W = _weights(qtype, n, k, "edge", F16, seed)
     X = synth.activations(T, k, workload_id=seed)
@@ -192,11 +264,14 @@ def test_xq_own_gemm_k_split(gpu, qtype, epi, T):
 @pytest.mark.parametrize("T", [9, 64])
 @pytest.mark.parametrize("qtype", XQ, ids=lambda q: NAMES[q])
 def test_xq_own_gemm_swiglu_scratch(gpu, qtype, T):
-    """SwiGLU on the f16 leg with a workspace up to 64 rows: the gate and up rows run as one
-    PLAIN GEMM over the 2n rows, split 8 ways along k = 4096 into G, then silu(g) * u sums
-    each half in split order. pf_gemm_noalloc runs the same kernels: same bits."""
+    """SwiGLU on the f16 leg with a workspace up to 64 rows (F16 and Q6_K; the others take
+    the short-chunk tiles there): the gate and up rows run as one PLAIN GEMM over the 2n
+    rows, split 8 ways along k = 4096 into G, then silu(g) * u sums each half in split
+    order. pf_gemm_noalloc runs the same kernels: same bits."""
     import torch
     n, k = 150, 4096
+    if qtype in KQ:
+        pytest.skip("the short-chunk tiles' range")
     seed = 720 + 7 * qtype + T
     W = _weights(qtype, 2 * n, k, "edge", F16, seed)
     X = synth.activations(T, k, workload_id=seed)
@@ -217,9 +292,10 @@ def test_xq_own_gemm_swiglu_scratch(gpu, qtype, T):
 @pytest.mark.parametrize("qtype", XQ, ids=lambda q: NAMES[q])
 def test_xq_strided_y_workspace(gpu, qtype, T, epi):
     """pf_gemm_ex with a workspace into a strided Y: the further types' own GEMM split
-    through the workspace (T = 40, SwiGLU through G; T = 300 for F16 and Q6_K, whose SwiGLU
-    there takes no workspace), and the cooperative kernel (T = 300 for Q4_K, Q5_K and
-    IQ4_XS; T = 520 for all); the columns between Y's rows keep their bits."""
+    through the workspace (T = 40 for F16 and Q6_K, SwiGLU through G; T = 300 for F16 and
+    Q6_K, whose SwiGLU there takes no workspace), the short-chunk tiles (T = 40 for Q4_K,
+    Q5_K and IQ4_XS) and the cooperative kernel (T = 300 for Q4_K, Q5_K and IQ4_XS; T = 520
+    for all); the columns between Y's rows keep their bits."""
     from tests.test_gpu_strided import check_gaps, run_strided
     n, k = 200, 2048
     rows = 2 * n if epi == SWIGLU else n
