@@ -71,12 +71,13 @@ extern "C" {
 #endif
 
 /* Block types. F16 .. IQ4_XS run their own kernels on both legs and need no
- * workspace, except on the f16 leg: from 256 rows (Q4_K, Q5_K, IQ4_XS) or 512 (F16, and
- * Q6_K with k % 512 == 0) pf_gemm_ws runs them on Q4_0's cooperative-decode GEMM, which
- * takes the same workspace as Q4_0 at those sizes; below, their own GEMM splits K
- * through the workspace where its tiles leave CUs idle (pf_gemm, and
- * pf_gemm_noalloc where the workspace exceeds the static scratch, keep their own GEMM
- * unsplit). pf_prepare_x and pf_gemm_prepared take Q4_0 and Q8_0 only. */
+ * workspace, except on the f16 leg, where pf_gemm_ws runs Q4_K, Q5_K and IQ4_XS at
+ * every T above the GEMV, and F16 and Q6_K (k % 512 == 0) from 512 rows, on Q4_0's
+ * matrix-core GEMMs (the 4-wave tiles below 256 rows, the cooperative-decode kernel
+ * from 256), with that GEMM's workspace; elsewhere their own GEMM splits K through the
+ * workspace where its tiles leave CUs idle (pf_gemm, and pf_gemm_noalloc where the
+ * workspace exceeds the static scratch, keep their own GEMM unsplit). pf_prepare_x and
+ * pf_gemm_prepared take Q4_0 and Q8_0 only. */
 enum { PF_Q4_0 = 0, PF_Q8_0 = 1, PF_F16 = 2, PF_Q4_K = 3, PF_Q5_K = 4, PF_Q6_K = 5, PF_IQ4_XS = 6 };
 
 /* Epilogues.
@@ -154,14 +155,15 @@ int pf_gemm_path(int qtype, const void *W_blocks, int64_t n, int64_t k, const fl
 /* Workspace bytes pf_gemm_ws needs for these sizes, or -PF_E_* for arguments pf_gemm
  * would refuse. Host-only; touches no GPU state.
  *  - 0 when pf_gemm_ws runs a kernel that needs none (the f32 leg, the GEMV, T == 0);
- *  - the further types' own GEMM (where the cooperative-decode GEMM does not take them):
+ *  - the further types' own GEMM (where Q4_0's matrix-core GEMMs do not take them):
  *    S * ceil(T * n / 4) * 16 for a K split of PLAIN / RESIDUAL (S > 1), and
  *    S * ceil(T * 2n / 4) * 16 for SwiGLU on up to 64 rows split as a PLAIN GEMM over the
  *    2n gate and up rows; else 0;
  *  - the f16 leg's matrix-core GEMM: X_b = ceil(T / 32) * 32 * k * 2 (X rounded to
  *    binary16, T padded to whole 32-row tiles);
  *  - and where that GEMM splits k across S workgroups (PLAIN or RESIDUAL with too few
- *    output tiles to fill the chip; S is the largest count either block type takes):
+ *    output tiles to fill the chip; S is the largest count Q4_0 and Q8_0 take, and for
+ *    Q4_K, Q5_K and IQ4_XS their own count):
  *    ceil(X_b / 256) * 256 + S * ceil(T * n / 4) * 16, room for S blocks of [T][n] f32
  *    partial sums;
  *  - the SwiGLU epilogue on up to 64 rows, which runs as a split PLAIN GEMM over the 2n

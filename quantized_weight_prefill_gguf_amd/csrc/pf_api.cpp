@@ -90,7 +90,7 @@ hipError_t launch_gemv_q(const pf::GemmArgs &a, int leg, hipStream_t s) {
 int64_t ws_need(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int leg, int use) {
     if (use != PF_PATH_GEMM || leg != PF_LEG_F16) return 0;
     if (!is_xq(qtype) || pf::f16_takes_xq(qtype, (int)T, (int)k))
-        return pf::f16_ws_bytes((int)T, (int)n, (int)k, epilogue);
+        return pf::f16_ws_bytes(qtype, (int)T, (int)n, (int)k, epilogue);
     return pf::xq_ws_bytes((int)T, (int)n, (int)k, epilogue, true);  // their own GEMM's K split
 }
 
@@ -164,7 +164,7 @@ int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
 int64_t rms_ws_need(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int leg, int use) {
     if (T == 0) return 0;
     const int64_t tail = (use == PF_PATH_GEMM && leg == PF_LEG_F16 && !is_xq(qtype))
-                             ? pf::f16_ws_bytes((int)T, (int)n, (int)k, epilogue)
+                             ? pf::f16_ws_bytes(qtype, (int)T, (int)n, (int)k, epilogue)
                              : T * k * 4;
     return round256(T * 4) + tail;
 }
@@ -341,7 +341,7 @@ int pf_gemm_prepared(int qtype, const void *W_blocks, int64_t n, int64_t k, int6
     if (!aligned16(W_blocks) || !aligned16(Y)) return PF_E_ALIGN;
     const int64_t w_bytes = w_bytes_of(qtype, n_w, k), y_bytes = ((T - 1) * ldy + n) * 4;
     if (overlap(Y, y_bytes, W_blocks, w_bytes)) return PF_E_ALIAS;
-    const int64_t need = pf::f16_ws_bytes((int)T, (int)n, (int)k, epilogue);
+    const int64_t need = pf::f16_ws_bytes(qtype, (int)T, (int)n, (int)k, epilogue);
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PF_E_WORKSPACE;
     if (overlap(workspace, need, W_blocks, w_bytes) || overlap(workspace, need, Y, y_bytes))
         return PF_E_WORKSPACE;

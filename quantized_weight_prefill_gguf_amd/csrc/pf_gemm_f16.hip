@@ -116,16 +116,19 @@ template <int QT> __device__ __forceinline__ u2_t x_pack(f4_t v) {
 
 }  // namespace
 
-// Global weight row of local tile row lr, or -1 past the weight.
+// Up to this many token rows the GEMM below 256 rows takes one row tile.
+constexpr int SHORT_T = 128;
 // Workgroups of a one-row-of-waves tile (MT x 128, waves 1 x 4) resident per CU
 // (waves per SIMD), as its LDS (Q4_0: 41 KB at 32 rows, 45 KB at 64, 53 KB at 128;
-// Q8_0: 74 KB and up) and registers allow.
-// Up to this many token rows the GEMM below 256 rows takes one such row tile.
-constexpr int SHORT_T = 128;
+// Q8_0: 74 KB and up; Q4_K / Q5_K / IQ4_XS: 41 / 49 / 39 KB at 32 rows) and registers
+// allow. Three at 32 rows hold the further types in 148-164 registers: gate/up 2 x
+// 12288 x 4096 at T = 16 took 30-33 us against 34-39 with two (the down projection
+// 4096 x 12288 gave up 0.5-1 us to its larger split).
 constexpr int short_tile_waves(int qt, int mt) {
-    return mt > 64 ? 1 : (qt == Q4_0 && mt <= 32) ? 3 : 2;
+    return mt > 64 ? 1 : ((qt == Q4_0 || qt == XQ_Q4_K || qt == XQ_Q5_K || qt == XQ_IQ4_XS) && mt <= 32) ? 3 : 2;
 }
 
+// Global weight row of local tile row lr, or -1 past the weight.
 template <int EPI, int NW>
 __device__ __forceinline__ int f16_weight_row(int tile_n, int lr, int n) {
     if constexpr (EPI == EPI_SWIGLU) {
@@ -150,7 +153,7 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
     // Further types (Q4_K, Q5_K, IQ4_XS): short-chunk tiles on the fp16 X copy only; a
     // row's 256-k chunk is one super-block, and step blk its sub-block blk.
     constexpr bool XQ = coop_xq<QT>();
-    static_assert(!XQ || (XH && ROW1 && QT != XQ_F16 && QT != XQ_Q6_K), "further types: short-chunk tiles");
+    static_assert(!XQ || (XH && QT != XQ_F16 && QT != XQ_Q6_K), "further types: fp16 X, Q4_K / Q5_K / IQ4_XS");
     // Waves: WVM x WVN over the tile. ROW1 tiles (few token rows) put all four side
     // by side along the weight rows, so that no two decode the same columns.
     constexpr int WVM = ROW1 ? 1 : 2;
@@ -1416,7 +1419,10 @@ TileChoice choose_tiles(const GemmArgs &a, bool allow_split) {
     }
     TileChoice best{3, 1};
     float best_t = 1e30f;
-    for (int cfg = 0; cfg < 4; ++cfg) {
+    // The further types' 256 x 192 tile (three B columns per lane, each with its
+    // super-block header and code words in flight) spills registers: not taken.
+    const bool xq = a.qtype == XQ_Q4_K || a.qtype == XQ_Q5_K || a.qtype == XQ_IQ4_XS;
+    for (int cfg = xq ? 1 : 0; cfg < 4; ++cfg) {
         const int MT = CFG_MT[cfg], NW = CFG_NW[cfg];
         const long out_per_tile = swiglu ? NW / 2 : NW;
         const long tm = (a.T + MT - 1) / MT;
@@ -1462,15 +1468,7 @@ hipError_t launch_cfg(const GemmArgs &a, int splits, const uint16_t *xh, long ps
 template <int QT, int EPI, bool SPLIT>
 hipError_t launch_split(const GemmArgs &a, TileChoice tc, const uint16_t *xh, hipStream_t s,
                         long pstride = 0) {
-    if constexpr (coop_xq<QT>()) {
-        // further types: the short-chunk tiles only (T <= SHORT_T)
-        switch (tc.cfg) {
-        case 4: return launch_cfg<QT, EPI, 32, 128, SPLIT, true>(a, tc.splits, xh, pstride, s);
-        case 5: return launch_cfg<QT, EPI, 64, 128, SPLIT, true>(a, tc.splits, xh, pstride, s);
-        case 6: return launch_cfg<QT, EPI, 128, 128, SPLIT, true>(a, tc.splits, xh, pstride, s);
-        default: return hipErrorInvalidValue;
-        }
-    } else {
+    {
         switch (tc.cfg) {
         case 0: return launch_cfg<QT, EPI, 256, 192, SPLIT>(a, tc.splits, xh, pstride, s);
         case 1: return launch_cfg<QT, EPI, 256, 128, SPLIT>(a, tc.splits, xh, pstride, s);
@@ -1540,11 +1538,14 @@ hipError_t launch_swiglu_scratch(const GemmArgs &a, const uint16_t *xh, float *G
     return hipGetLastError();
 }
 
-// Most K splits the GEMM below 256 rows takes for these sizes, over both block types
-// (the workspace size does not depend on the block type).
-int small_t_splits(int T, int n, int k, int epilogue) {
+// Most K splits the GEMM below 256 rows takes for these sizes: over Q4_0 and Q8_0
+// (their workspace size does not depend on which), or the further types' own choice
+// (they all choose as Q4_K does).
+int small_t_splits(int qtype, int T, int n, int k, int epilogue) {
+    const bool xq = qtype == XQ_Q4_K || qtype == XQ_Q5_K || qtype == XQ_IQ4_XS;
     int m = 1;
-    for (int q : {Q4_0, Q8_0}) {
+    for (int q : {(int)Q4_0, (int)Q8_0, (int)XQ_Q4_K}) {
+        if ((q == XQ_Q4_K) != xq) continue;
         GemmArgs g;
         g.qtype = q;
         g.epilogue = epilogue;
@@ -1694,11 +1695,11 @@ static int coop_splits(int T, int n, int k, int epilogue) {
 }
 
 // The further types this file's GEMMs take on the workspace path: Q4_K, Q5_K and
-// IQ4_XS up to SHORT_T rows (the short-chunk tiles) and from 256 (the cooperative
-// kernel, both tiles); F16 and Q6_K (k % 512 == 0) from COOP_T512 (their 256 x 192
-// tile's staging would need more than one piece per thread).
+// IQ4_XS at every T (the 4-wave kernel below 256 rows, the cooperative kernel from
+// 256); F16 and Q6_K (k % 512 == 0) from COOP_T512 (their 256 x 192 tile's staging
+// would need more than one piece per thread).
 bool f16_takes_xq(int qtype, int T, int k) {
-    if (qtype == XQ_Q4_K || qtype == XQ_Q5_K || qtype == XQ_IQ4_XS) return T <= SHORT_T || T >= 256;
+    if (qtype == XQ_Q4_K || qtype == XQ_Q5_K || qtype == XQ_IQ4_XS) return true;
     return T >= COOP_T512 && (qtype == XQ_F16 || (qtype == XQ_Q6_K && k % 512 == 0));
 }
 
@@ -1716,12 +1717,12 @@ static int64_t ws_pstride(int T, int n) { return part_stride(T, n); }
 constexpr int SWIGLU_SCRATCH_T = 64;
 static bool swiglu_via_scratch(int T, int epilogue) { return epilogue == EPI_SWIGLU && T <= SWIGLU_SCRATCH_T; }
 
-int64_t f16_ws_bytes(int T, int n, int k, int epilogue) {
+int64_t f16_ws_bytes(int qtype, int T, int n, int k, int epilogue) {
     const int64_t xb = (int64_t)(T + 31) / 32 * 32 * k * 2;
     if (swiglu_via_scratch(T, epilogue))
-        return ws_x_bytes(T, k) + (int64_t)small_t_splits(T, 2 * n, k, EPI_PLAIN) * ws_pstride(T, 2 * n) * 4;
+        return ws_x_bytes(T, k) + (int64_t)small_t_splits(qtype, T, 2 * n, k, EPI_PLAIN) * ws_pstride(T, 2 * n) * 4;
     if (T < 256) {
-        const int splits = small_t_splits(T, n, k, epilogue);
+        const int splits = small_t_splits(qtype, T, n, k, epilogue);
         return splits > 1 ? ws_x_bytes(T, k) + (int64_t)splits * ws_pstride(T, n) * 4 : xb;
     }
     const int splits = coop_splits(T, n, k, epilogue);
@@ -1844,7 +1845,7 @@ hipError_t launch_gemm_f16_prepared(const GemmArgs &a, void *workspace, hipStrea
     switch (a.qtype) {
     case Q4_0: return g ? launch_swiglu_scratch<Q4_0>(a, xh, ps, s) : launch_q<Q4_0>(a, xh, s, ps);
     case Q8_0: return g ? launch_swiglu_scratch<Q8_0>(a, xh, ps, s) : launch_q<Q8_0>(a, xh, s, ps);
-    // further types up to SHORT_T rows (f16_takes_xq)
+    // further types below 256 rows (f16_takes_xq)
     case XQ_Q4_K: return g ? launch_swiglu_scratch<XQ_Q4_K>(a, xh, ps, s) : launch_q<XQ_Q4_K>(a, xh, s, ps);
     case XQ_Q5_K: return g ? launch_swiglu_scratch<XQ_Q5_K>(a, xh, ps, s) : launch_q<XQ_Q5_K>(a, xh, s, ps);
     case XQ_IQ4_XS: return g ? launch_swiglu_scratch<XQ_IQ4_XS>(a, xh, ps, s) : launch_q<XQ_IQ4_XS>(a, xh, s, ps);

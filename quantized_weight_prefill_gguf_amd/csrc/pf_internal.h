@@ -36,13 +36,13 @@ hipError_t launch_gemm_f16_ws(const GemmArgs &a, void *workspace, hipStream_t s)
 // GEMM on that copy.
 hipError_t launch_prepare_x_f16(const GemmArgs &a, void *workspace, hipStream_t s);
 hipError_t launch_gemm_f16_prepared(const GemmArgs &a, void *workspace, hipStream_t s);
-// Workspace bytes launch_gemm_f16_ws takes: X as binary16 (T rounded up to a
-// multiple of 32), and for T >= 256 with a K split, behind it (at the next 256-byte
-// boundary) one [T][n] f32 block of partial sums per split.
-int64_t f16_ws_bytes(int T, int n, int k, int epilogue);
-// The further types the f16 workspace path's GEMMs take (Q4_K, Q5_K and IQ4_XS up to
-// 128 rows on the short-chunk tiles and from 256 on the cooperative-decode kernel; F16,
-// and Q6_K with k % 512 == 0, from 512); the others keep their own GEMM.
+// Workspace bytes launch_gemm_f16_ws takes for qtype: X as binary16 (T rounded up to a
+// multiple of 32), and with a K split, behind it (at the next 256-byte boundary) one
+// [T][n] f32 block of partial sums per split (or G's blocks for SwiGLU up to 64 rows).
+int64_t f16_ws_bytes(int qtype, int T, int n, int k, int epilogue);
+// The further types the f16 workspace path's GEMMs take (Q4_K, Q5_K and IQ4_XS at every
+// T: the 4-wave kernel below 256 rows, the cooperative-decode kernel from 256; F16, and
+// Q6_K with k % 512 == 0, from 512); the others keep their own GEMM.
 bool f16_takes_xq(int qtype, int T, int k);
 // Floats between the [T][n] partial-sum blocks of a K split, and Y = [R +] the `splits`
 // blocks at ps added in split order (PLAIN or RESIDUAL; a.Y, a.ldy, a.T, a.n).

@@ -186,9 +186,9 @@ def test_workspace_bytes(lib):
     assert wb(pf.PF_Q4_0, 17, 1280, 290, pf.PF_RESIDUAL, pf.PF_LEG_F16) == 320 * 1280 * 2
     assert wb(pf.PF_Q4_0, 4096, 4096, 512, pf.PF_PLAIN, pf.PF_LEG_F32) == 0
     # the further types take no workspace on the f32 leg; on the f16 leg Q4_K, Q5_K and
-    # IQ4_XS from 9 to 128 rows (the short-chunk tiles) and from 256 (the cooperative
-    # kernel), and F16 and Q6_K (k % 512 == 0: rows a multiple of 4 bytes) from 512, take
-    # Q4_0's workspace at the same sizes.
+    # IQ4_XS from 9 rows (the 4-wave tiles below 256, the cooperative kernel from 256),
+    # and F16 and Q6_K (k % 512 == 0: rows a multiple of 4 bytes) from 512, take Q4_0's
+    # GEMMs and their workspace layout (X, then the split count these types take).
     # Elsewhere on the f16 leg their own GEMM (64- or 128-row x 128-column tiles) splits K
     # through the workspace when the tiles leave the resident slots (3 per CU) idle:
     # 768 / tiles splits, each at least 512 k, at most 16, one [T][rows] f32 block each;
@@ -204,7 +204,7 @@ def test_workspace_bytes(lib):
         for T in (1, 8, 9, 300, 511, 512, 2048):
             for epi in (pf.PF_PLAIN, pf.PF_RESIDUAL, pf.PF_GATE_UP_SWIGLU):
                 kq = qt in (pf.PF_Q4_K, pf.PF_Q5_K, pf.PF_IQ4_XS)
-                coop = T >= 512 or (kq and (9 <= T <= 128 or T >= 256))
+                coop = T >= 512 or (kq and T >= 9)
                 sp = own_splits(T, 4096, 4096, epi)
                 rows = 8192 if epi == pf.PF_GATE_UP_SWIGLU else 4096
                 want = wb(pf.PF_Q4_0, 4096, 4096, T, epi, pf.PF_LEG_F16) if coop else \
@@ -212,11 +212,22 @@ def test_workspace_bytes(lib):
                 assert wb(qt, 4096, 4096, T, epi, pf.PF_LEG_F16) == want
                 assert wb(qt, 4096, 4096, T, epi, pf.PF_LEG_F32) == 0
     # the narrow down projection at T = 32 on Q6_K's own GEMM: 32 tiles, 16 splits; Q4_K
-    # gate/up at T = 32 on the short-chunk tiles: X, then G [32][24576] in Q4_0's 4
-    # splits (192 tiles of 32 x 128 over 768 resident slots)
+    # gate/up at T = 32 on the short-chunk tiles: X, then G [32][24576] in 4 splits (192
+    # tiles of 32 x 128 over 768 resident slots, three workgroups per CU, as Q4_0); at
+    # 64 rows two workgroups per CU (512 slots): 2 splits
     assert wb(pf.PF_Q6_K, 4096, 12288, 32, pf.PF_RESIDUAL, pf.PF_LEG_F16) == 16 * 32 * 4096 * 4
-    assert wb(pf.PF_Q4_K, 12288, 4096, 32, pf.PF_GATE_UP_SWIGLU, pf.PF_LEG_F16) == \
-        32 * 4096 * 2 + 4 * 32 * 24576 * 4
+    for qt in (pf.PF_Q4_0, pf.PF_Q4_K):
+        assert wb(qt, 12288, 4096, 32, pf.PF_GATE_UP_SWIGLU, pf.PF_LEG_F16) == \
+            32 * 4096 * 2 + 4 * 32 * 24576 * 4
+    assert wb(pf.PF_IQ4_XS, 12288, 4096, 64, pf.PF_GATE_UP_SWIGLU, pf.PF_LEG_F16) == \
+        64 * 4096 * 2 + 2 * 64 * 24576 * 4
+    # from 129 rows they choose among the 4-wave kernel's tiles without its 256 x 192
+    # one: PLAIN 12288 x 4096 at T = 200 takes 256 x 128 tiles split 8 ways where Q4_0
+    # and Q8_0 take 256 x 192 split 4 ways
+    assert wb(pf.PF_Q4_0, 12288, 4096, 200, pf.PF_PLAIN, pf.PF_LEG_F16) == \
+        224 * 4096 * 2 + 4 * 200 * 12288 * 4
+    assert wb(pf.PF_Q4_K, 12288, 4096, 200, pf.PF_PLAIN, pf.PF_LEG_F16) == \
+        224 * 4096 * 2 + 8 * 200 * 12288 * 4
     # Q6_K rows of an odd number of super-blocks (2-byte aligned rows) keep its own GEMM
     # (512 rows, 4096 columns: 256 tiles, 3 splits)
     assert own_splits(512, 4096, 4352, pf.PF_PLAIN) == 3

@@ -163,18 +163,18 @@ KQ = [synth.Q4_K, synth.Q5_K, synth.IQ4_XS]
 
 
 @pytest.mark.parametrize("epi", [PLAIN, RESIDUAL, SWIGLU])
-@pytest.mark.parametrize("T", [9, 32, 33, 64, 65, 128])
+@pytest.mark.parametrize("T", [9, 32, 33, 64, 65, 128, 130, 255])
 @pytest.mark.parametrize("kind", ["synth", "edge"])
 @pytest.mark.parametrize("qtype", KQ, ids=lambda q: NAMES[q])
-def test_xq_short_tiles_every_output(gpu, qtype, kind, T, epi):
-    """On the f16 leg with a workspace up to 128 rows, Q4_K, Q5_K and IQ4_XS take Q4_0's
-    short-chunk tiles (32, 64 or 128 token rows x 128 weight rows, four waves side by
-    side, each decoding its own B fragments from the staged super-blocks): T = 9 .. 128
-    covers each tile height, full and ragged; n = 150 is two weight tiles, the second
+def test_xq_4wave_every_output(gpu, qtype, kind, T, epi):
+    """On the f16 leg with a workspace below 256 rows, Q4_K, Q5_K and IQ4_XS take Q4_0's
+    4-wave GEMM, each lane decoding its own B fragments from the staged super-blocks: up
+    to 128 rows its short-chunk tiles (32, 64 or 128 token rows x 128 weight rows, the
+    four waves side by side), T = 9 .. 128 covering each tile height, full and ragged;
+    at 130 and 255 the cost model's 64 x 64 tiles. n = 150 leaves the last weight tile
     ragged; at k = 4096 PLAIN and RESIDUAL split K (partial sums, then their fixed-order
     sum), and SwiGLU up to 64 rows runs as a split PLAIN GEMM over the 2n rows into G.
-    The workspace is Q4_0's at the same sizes. pf_gemm_noalloc runs the same kernels:
-    same bits."""
+    pf_gemm_noalloc runs the same kernels: same bits."""
     import torch
     n, k = 150, 4096
     rows = 2 * n if epi == SWIGLU else n
@@ -182,9 +182,8 @@ def test_xq_short_tiles_every_output(gpu, qtype, kind, T, epi):
     W = _weights(qtype, rows, k, kind, F16, seed)
     X = synth.activations(T, k, workload_id=seed)
     R = synth.activations(T, n, workload_id=seed, tensor_id=synth.TENSOR_R) if epi == RESIDUAL else None
-    need = gpu.workspace_bytes(qtype, n, k, T, epi, F16)
-    assert need >= T * k * 2 and need == gpu.workspace_bytes(synth.Q4_0, n, k, T, epi, F16)
-    print("case xq short %s %s T=%d epi=%d" % (NAMES[qtype], kind, T, epi), flush=True)
+    assert gpu.workspace_bytes(qtype, n, k, T, epi, F16) >= T * k * 2
+    print("case xq 4-wave %s %s T=%d epi=%d" % (NAMES[qtype], kind, T, epi), flush=True)
     Y = parity.run_gpu(gpu, qtype, W, n, k, X, epi, F16, R=R, workspace=True)
     ok, err = parity.check(qtype, W, n, k, X, Y, epi, F16, R=R)
     assert ok, "parity failed: metric %.3e" % err
@@ -193,6 +192,24 @@ def test_xq_short_tiles_every_output(gpu, qtype, kind, T, epi):
     gpu.gemm_noalloc(qtype, Wd, n, k, Xd, Yd, epi, F16)
     torch.cuda.synchronize()
     assert np.array_equal(Y.view(np.uint32), Yd.cpu().numpy().view(np.uint32))
+
+
+@pytest.mark.parametrize("n,T,epi", [(2000, 200, PLAIN), (4096, 200, RESIDUAL), (4096, 160, SWIGLU)])
+@pytest.mark.parametrize("qtype", KQ, ids=lambda q: NAMES[q])
+def test_xq_4wave_wide_tiles(gpu, qtype, n, T, epi):
+    """The cost model's larger tiles between 129 and 255 rows (k = 4096): 128 x 128 split 8
+    ways (n = 2000), 256 x 128 split 8 ways (n = 4096), and 128 x 128 unsplit for SwiGLU
+    (the fused epilogue), on every output."""
+    k = 4096
+    rows = 2 * n if epi == SWIGLU else n
+    seed = 790 + 7 * qtype + T + epi
+    W = _weights(qtype, rows, k, "edge", F16, seed)
+    X = synth.activations(T, k, workload_id=seed)
+    R = synth.activations(T, n, workload_id=seed, tensor_id=synth.TENSOR_R) if epi == RESIDUAL else None
+    print("case xq 4-wave wide %s n=%d T=%d epi=%d" % (NAMES[qtype], n, T, epi), flush=True)
+    Y = parity.run_gpu(gpu, qtype, W, n, k, X, epi, F16, R=R, workspace=True)
+    ok, err = parity.check(qtype, W, n, k, X, Y, epi, F16, R=R)
+    assert ok, "parity failed: metric %.3e" % err
 
 
 @pytest.mark.parametrize("qtype", KQ, ids=lambda q: NAMES[q])
@@ -211,13 +228,14 @@ def test_xq_short_tiles_shortest_k(gpu, qtype):
         assert ok, "parity failed: metric %.3e" % err
 
 
-@pytest.mark.parametrize("shape", ["gate_up_T32", "down_T64"])
+@pytest.mark.parametrize("shape", ["gate_up_T32", "gate_up_T200", "down_T64"])
 @pytest.mark.parametrize("qtype", KQ, ids=lambda q: NAMES[q])
-def test_xq_short_tiles_full_size_sampled(gpu, qtype, shape):
-    """The model shapes on the short-chunk tiles: gate/up 2 x 12288 x 4096 at T = 32 (G
-    route) and the down projection 4096 x 12288 RESIDUAL at T = 64 (sampled outputs)."""
-    if shape == "gate_up_T32":
-        n, k, T, epi = 12288, 4096, 32, SWIGLU
+def test_xq_4wave_full_size_sampled(gpu, qtype, shape):
+    """The model shapes on the 4-wave GEMM: gate/up 2 x 12288 x 4096 at T = 32 (short-chunk
+    tiles, G route) and 200 (256 x 128 tiles, fused epilogue), and the down projection
+    4096 x 12288 RESIDUAL at T = 64 (sampled outputs)."""
+    if shape.startswith("gate_up"):
+        n, k, T, epi = 12288, 4096, int(shape.split("_T")[1]), SWIGLU
         W = synth.quantize(qtype, np.concatenate([synth.weights_f32(n, k, workload_id=652),
                                                   synth.weights_f32(n, k, workload_id=652,
                                                                     tensor_id=synth.TENSOR_W_UP)]))
@@ -236,15 +254,15 @@ def test_xq_short_tiles_full_size_sampled(gpu, qtype, shape):
 @pytest.mark.parametrize("epi", [PLAIN, RESIDUAL])
 @pytest.mark.parametrize("qtype", XQ, ids=lambda q: NAMES[q])
 def test_xq_own_gemm_k_split(gpu, qtype, epi, T):
-    """Where the f16 GEMMs of Q4_0 do not take them (F16 and Q6_K below 512 rows, the
-    others from 129 to 255), the further types' own GEMM splits PLAIN / RESIDUAL K through
-    the workspace when its tiles leave CUs idle: n = 150 is two 128-column tiles, so k =
-    4096 splits 8 ways (512 k each; the cap), and the sum kernel adds R and the splits in
-    order. pf_gemm_noalloc runs the same kernels: same bits."""
+    """Where Q4_0's f16 GEMMs do not take them (F16 and Q6_K below 512 rows), the further
+    types' own GEMM splits PLAIN / RESIDUAL K through the workspace when its tiles leave
+    CUs idle: n = 150 is two 128-column tiles, so k = 4096 splits 8 ways (512 k each; the
+    cap), and the sum kernel adds R and the splits in order. pf_gemm_noalloc runs the
+    same kernels: same bits."""
     import torch
     n, k = 150, 4096
-    if qtype in KQ and (T <= 128 or T >= 256):
-        pytest.skip("the short-chunk tiles' or the cooperative kernel's range")
+    if qtype in KQ:
+        pytest.skip("Q4_0's f16 GEMMs take this type")
     seed = 700 + 7 * qtype + 3 * epi + T
     W = _weights(qtype, n, k, "edge", F16, seed)
     X = synth.activations(T, k, workload_id=seed)
@@ -265,13 +283,13 @@ def test_xq_own_gemm_k_split(gpu, qtype, epi, T):
 @pytest.mark.parametrize("qtype", XQ, ids=lambda q: NAMES[q])
 def test_xq_own_gemm_swiglu_scratch(gpu, qtype, T):
     """SwiGLU on the f16 leg with a workspace up to 64 rows (F16 and Q6_K; the others take
-    the short-chunk tiles there): the gate and up rows run as one PLAIN GEMM over the 2n
+    Q4_0's short-chunk tiles there): the gate and up rows run as one PLAIN GEMM over the 2n
     rows, split 8 ways along k = 4096 into G, then silu(g) * u sums each half in split
     order. pf_gemm_noalloc runs the same kernels: same bits."""
     import torch
     n, k = 150, 4096
     if qtype in KQ:
-        pytest.skip("the short-chunk tiles' range")
+        pytest.skip("Q4_0's f16 GEMMs take this type")
     seed = 720 + 7 * qtype + T
     W = _weights(qtype, 2 * n, k, "edge", F16, seed)
     X = synth.activations(T, k, workload_id=seed)
