@@ -150,10 +150,10 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
                      int splits, long pstride) {
     using CT = ChunkTraits<QT>;
     constexpr int BB = CT::BB;
-    // Further types (Q4_K, Q5_K, IQ4_XS): short-chunk tiles on the fp16 X copy only; a
-    // row's 256-k chunk is one super-block, and step blk its sub-block blk.
+    // Further types (Q4_K, Q5_K, IQ4_XS, Q6_K with k % 512 == 0): on the fp16 X copy
+    // only; a row's 256-k chunk is one super-block, and step blk its sub-block blk.
     constexpr bool XQ = coop_xq<QT>();
-    static_assert(!XQ || (XH && QT != XQ_F16 && QT != XQ_Q6_K), "further types: fp16 X, Q4_K / Q5_K / IQ4_XS");
+    static_assert(!XQ || (XH && QT != XQ_F16), "further types: fp16 X, not F16");
     // Waves: WVM x WVN over the tile. ROW1 tiles (few token rows) put all four side
     // by side along the weight rows, so that no two decode the same columns.
     constexpr int WVM = ROW1 ? 1 : 2;
@@ -170,7 +170,9 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
     constexpr int WROW = CT::ROW;
     constexpr int WBUF = NW * WROW + 16;            // +16: decode reads a dword past a row
     constexpr int NW32 = (QT == Q4_0) ? 2 : 4;      // qs words per lane per block
-    typedef typename std::conditional<PIECE == 16, u4_t, u2_t>::type piece_t;
+    constexpr int GROW = chunk_grow<QT>();          // bytes per row chunk in the weight
+    // a piece in flight: 16 bytes, 8 (IQ4_XS), or Q6_K's 8 and two halfwords
+    typedef typename std::conditional<PIECE == 16 || QT == XQ_Q6_K, u4_t, u2_t>::type piece_t;
 
     // One LDS block: the K loop's two X buffers and two weight chunks; after the
     // loop, the SwiGLU epilogue reuses its start as 4 per-wave 32 x 36 float slots.
@@ -211,7 +213,7 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
     const int nch = c_end - c_begin;
     if (nch <= 0) return;  // cannot happen (splits <= chunks); keeps the loop simple
     const int nsteps = 8 * nch;
-    const uint32_t row_bytes = XQ ? (uint32_t)(k >> 8) * WROW : (uint32_t)(k >> 5) * BB;
+    const uint32_t row_bytes = XQ ? (uint32_t)(k >> 8) * GROW : (uint32_t)(k >> 5) * BB;
 
     // ---- staging assignments (fixed over the K loop), as 32-bit byte offsets
     // from uniform bases. Global loads are all unconditional so that the wait
@@ -248,18 +250,25 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
         xdst = (tid >> 3) * 32 + ((((tid & 7) >> 1) ^ ((tid >> 5) & 3)) << 3) + 4 * (tid & 1);
     }
     // Weight staging. Slice S of a chunk is its rows S RS .. S RS + RS - 1 (RS = NW
-    // / 8), whole: RS * U4 pieces (16 bytes, IQ4_XS 8), which the threads take in order, piece
-    // f = tid + 256 i being piece f % U4 of slice row f / U4. Consecutive lanes thus
-    // read consecutive bytes of a row. Since RS * U4 is the same for every slice,
-    // a thread's (row in slice, piece) is fixed; only the weight row of slice row
+    // / 8), whole: RS * U4 pieces (16 bytes, IQ4_XS and Q6_K 8), which the threads take in
+    // order, piece f = tid + 256 i being piece f % U4 of slice row f / U4. Consecutive
+    // lanes thus read consecutive bytes of a row. Since RS * U4 is the same for every
+    // slice, a thread's (row in slice, piece) is fixed; only the weight row of slice row
     // rr, i.e. its global offset, depends on S.
+    // Q6_K (210-byte super-blocks, rows a multiple of 4 bytes): chunk c starts sh = 2 (c
+    // % 2) bytes past a dword boundary in every row, and its 216-byte LDS row holds the
+    // bytes from that boundary: pieces 0 .. 25 are 8-byte loads from there, and the 27th
+    // (chunk bytes 208 - sh .. 211 - sh) is assembled from two halfword loads when stored,
+    // so that no load passes the chunk's end.
     constexpr int RS = NW / 8;
     constexpr int SP = RS * U4;                      // pieces per slice
     constexpr int NPT = (SP + 255) / 256;            // pieces per thread per slice
     uint32_t wsrc[8][NPT];                           // [slice][piece]: row offset + piece
     int wdst[NPT];                                   // LDS offset within slice 0
     bool wvalid[NPT];
-    const uint8_t *wbase = W + (size_t)c_begin * WROW;
+    int wpo[NPT];                                    // Q6_K: the piece's offset past the boundary
+    bool wlast[NPT];                                 // Q6_K: the 27th piece
+    const uint8_t *wbase = W + (size_t)c_begin * GROW;
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
         const int f = tid + 256 * i;
@@ -267,11 +276,13 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
         const int ff = wvalid[i] ? f : 0;
         const int rr = ff / U4, pp = ff % U4;
         wdst[i] = rr * WROW + PIECE * pp;
+        wlast[i] = pp == U4 - 1;
+        wpo[i] = wlast[i] ? 200 : PIECE * pp;
 #pragma unroll
         for (int S = 0; S < 8; ++S) {
             int gr = f16_weight_row<EPI, NW>(tn, S * RS + rr, n);
             gr = gr < 0 ? 0 : gr;
-            wsrc[S][i] = (uint32_t)gr * row_bytes + PIECE * pp;
+            wsrc[S][i] = (uint32_t)gr * row_bytes + (QT == XQ_Q6_K ? 0 : PIECE * pp);
         }
     }
 
@@ -313,17 +324,39 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
     // and 16 + 8 h .. 16 + 8 h + 7 of sub-block blk (Q4_K / Q5_K: the qs bytes, nibble
     // half blk % 2; IQ4_XS: one 8-byte run whose low nibbles are the first eight and
     // high nibbles the second), and for Q5_K the qh dwords of the same k.
-    constexpr int NRAW = QT == XQ_Q5_K ? 12 : QT == XQ_Q4_K ? 8 : QT == XQ_IQ4_XS ? 4 : (QT == Q4_0) ? 3 : 6;
-    auto read_b = [&](const uint8_t *wb, auto blk_c, uint32_t (&d16)[JT], uint32_t (&raw)[JT][NRAW])
+    // Q6_K (sub-block blk = 4 H + C): its ql bytes 64 H + 32 (C % 2) + 8 h .. and 16 bytes
+    // on, and its qh bytes 128 + 32 H + 8 h .. and 16 on, each 8-byte run as the three
+    // dwords around it (the chunk sits sh bytes into its LDS row); then the halfword of the
+    // two scales (bytes 192 + 8 H + 2 C and one on: l < 16 and l >= 16), d, and sh.
+    constexpr int NRAW = QT == XQ_Q6_K ? 15 : QT == XQ_Q5_K ? 12 : QT == XQ_Q4_K ? 8 : QT == XQ_IQ4_XS ? 4
+                                                                                   : (QT == Q4_0) ? 3 : 6;
+    auto read_b = [&](int wbuf, auto blk_c, uint32_t (&d16)[JT], uint32_t (&raw)[JT][NRAW])
         __attribute__((always_inline)) {
         constexpr int blk = decltype(blk_c)::value;
         constexpr int SH = (blk * BB + 2) & 3;
+        const uint8_t *wb = wsm[wbuf];
         if constexpr (XQ) {
             (void)d16;
 #pragma unroll
             for (int j = 0; j < JT; ++j) {
                 const uint8_t *rb = wb + bbase + j * 32 * WROW;  // the column's super-block
-                if constexpr (QT == XQ_IQ4_XS) {
+                if constexpr (QT == XQ_Q6_K) {
+                    constexpr int H = blk >> 2, C = blk & 3;
+                    const uint32_t sh = ((c_begin ^ wbuf) & 1) * 2;
+                    auto run = [&](int off, int at) __attribute__((always_inline)) {
+                        const u2_t a = *reinterpret_cast<const u2_t *>(rb + off);
+                        raw[j][at] = a[0];
+                        raw[j][at + 1] = a[1];
+                        raw[j][at + 2] = *reinterpret_cast<const uint32_t *>(rb + off + 8);
+                    };
+                    run(64 * H + 32 * (C & 1) + 8 * h, 0);
+                    run(64 * H + 32 * (C & 1) + 16 + 8 * h, 3);
+                    run(128 + 32 * H + 8 * h, 6);
+                    run(128 + 32 * H + 16 + 8 * h, 9);
+                    raw[j][12] = *reinterpret_cast<const uint16_t *>(rb + sh + 192 + 8 * H + 2 * C);
+                    raw[j][13] = *reinterpret_cast<const uint16_t *>(rb + sh + 208);
+                    raw[j][14] = sh;
+                } else if constexpr (QT == XQ_IQ4_XS) {
                     const u2_t hd = *reinterpret_cast<const u2_t *>(rb);
                     const u2_t cw = *reinterpret_cast<const u2_t *>(rb + 8 + 16 * blk + 8 * h);
                     raw[j][0] = hd[0]; raw[j][1] = hd[1];
@@ -377,7 +410,34 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
 #pragma unroll
             for (int j = 0; j < JT; ++j) {
                 uint32_t p[8];
-                if constexpr (QT == XQ_IQ4_XS) {
+                if constexpr (QT == XQ_Q6_K) {
+                    // (d sc) (q - 32): d sc is exact, the product rounds once in f32. q: 4
+                    // low bits from ql (high nibble for C >= 2), 2 high bits from qh bits
+                    // 2 C, 2 C + 1.
+                    constexpr int C = blk & 3;
+                    const uint32_t sh = raw[j][14];
+                    auto al = [&](int a) __attribute__((always_inline)) {
+                        return __builtin_amdgcn_alignbyte(raw[j][a + 1], raw[j][a], sh);
+                    };
+                    const uint32_t ql[4] = {al(0), al(1), al(3), al(4)};
+                    const uint32_t qh[4] = {al(6), al(7), al(9), al(10)};
+                    const float d = fp16_bits_to_f32(raw[j][13]);
+                    const float ds[2] = {d * (float)(int8_t)(uint8_t)(raw[j][12] & 0xFFu),
+                                         d * (float)(int8_t)(uint8_t)(raw[j][12] >> 8)};
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        const uint32_t q = ((ql[w] >> (4 * (C >> 1))) & 0x0F0F0F0Fu) |
+                                           (((qh[w] >> (2 * C)) & 0x03030303u) << 4);
+                        float v[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            v[e] = ds[w >> 1] * (float)((int)((q >> (8 * e)) & 0xFFu) - 32);
+                            asm("" : "+v"(v[e]));
+                        }
+                        p[2 * w] = h2_bits(h2_t{(_Float16)v[0], (_Float16)v[1]});
+                        p[2 * w + 1] = h2_bits(h2_t{(_Float16)v[2], (_Float16)v[3]});
+                    }
+                } else if constexpr (QT == XQ_IQ4_XS) {
                     const uint32_t h0 = raw[j][0], sl = raw[j][1];
                     const uint32_t ls = ((sl >> (4 * blk)) & 15u) | (((h0 >> (16 + 2 * blk)) & 3u) << 4);
                     const float dl = fp16_bits_to_f32(h0 & 0xFFFFu) * (float)((int)ls - 32);
@@ -469,15 +529,41 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
     // Slice S (compile-time) of chunk `chunk`: load to registers / store to LDS.
     auto fetch_slice = [&](int chunk, auto s_c, piece_t (&dst)[NPT]) __attribute__((always_inline)) {
         constexpr int S = decltype(s_c)::value;
-        const uint8_t *src = wbase + (size_t)min(chunk, nch - 1) * WROW;
+        const int cc = min(chunk, nch - 1);
+        const uint8_t *src = wbase + (size_t)cc * GROW;
 #pragma unroll
-        for (int i = 0; i < NPT; ++i) dst[i] = *reinterpret_cast<const piece_t *>(src + wsrc[S][i]);
+        for (int i = 0; i < NPT; ++i) {
+            if constexpr (QT == XQ_Q6_K) {
+                // every lane issues the same three loads (see the staging note)
+                const int sh = ((c_begin + cc) & 1) * 2;
+                const uint8_t *row = src + wsrc[S][i];
+                const u2a4_t v = *reinterpret_cast<const u2a4_t *>(row - sh + wpo[i]);
+                const uint32_t s0 = *reinterpret_cast<const uint16_t *>(row + 206);
+                const uint32_t s1 = *reinterpret_cast<const uint16_t *>(row + 208);
+                dst[i] = u4_t{v[0], v[1], s0, s1};
+            } else {
+                dst[i] = *reinterpret_cast<const piece_t *>(src + wsrc[S][i]);
+            }
+        }
     };
-    auto store_slice = [&](uint8_t *buf, auto s_c, const piece_t (&src)[NPT]) __attribute__((always_inline)) {
+    // into chunk buffer wbuf, which holds local chunks of its parity
+    auto store_slice = [&](int wbuf, auto s_c, const piece_t (&src)[NPT]) __attribute__((always_inline)) {
         constexpr int S = decltype(s_c)::value;
+        uint8_t *buf = wsm[wbuf];
 #pragma unroll
-        for (int i = 0; i < NPT; ++i)
-            if (wvalid[i]) *reinterpret_cast<piece_t *>(buf + S * RS * WROW + wdst[i]) = src[i];
+        for (int i = 0; i < NPT; ++i) {
+            if constexpr (QT == XQ_Q6_K) {
+                // the 27th piece: halfwords 206 and 208 (sh = 2), or 208 then two bytes
+                // never read (sh = 0)
+                const bool odd = ((c_begin ^ wbuf) & 1) != 0;
+                const uint32_t tail = __builtin_amdgcn_perm(src[i][3], src[i][2], odd ? 0x05040100u : 0x05040504u);
+                if (wvalid[i])
+                    *reinterpret_cast<u2_t *>(buf + S * RS * WROW + wdst[i]) =
+                        wlast[i] ? u2_t{tail, 0u} : u2_t{src[i][0], src[i][1]};
+            } else {
+                if (wvalid[i]) *reinterpret_cast<piece_t *>(buf + S * RS * WROW + wdst[i]) = src[i];
+            }
+        }
     };
 
     // ---- prologue. LDS: chunk 0, slices 0 and 1 of chunk 1, X(0), X(1).
@@ -498,17 +584,17 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
         fetch_slice(0, std::integral_constant<int, 7>{}, tmp[7]);
         fetch_slice(1, std::integral_constant<int, 0>{}, tmp[8]);
         fetch_slice(1, std::integral_constant<int, 1>{}, tmp[9]);
-        store_slice(wsm[0], std::integral_constant<int, 0>{}, tmp[0]);
-        store_slice(wsm[0], std::integral_constant<int, 1>{}, tmp[1]);
-        store_slice(wsm[0], std::integral_constant<int, 2>{}, tmp[2]);
-        store_slice(wsm[0], std::integral_constant<int, 3>{}, tmp[3]);
-        store_slice(wsm[0], std::integral_constant<int, 4>{}, tmp[4]);
-        store_slice(wsm[0], std::integral_constant<int, 5>{}, tmp[5]);
-        store_slice(wsm[0], std::integral_constant<int, 6>{}, tmp[6]);
-        store_slice(wsm[0], std::integral_constant<int, 7>{}, tmp[7]);
+        store_slice(0, std::integral_constant<int, 0>{}, tmp[0]);
+        store_slice(0, std::integral_constant<int, 1>{}, tmp[1]);
+        store_slice(0, std::integral_constant<int, 2>{}, tmp[2]);
+        store_slice(0, std::integral_constant<int, 3>{}, tmp[3]);
+        store_slice(0, std::integral_constant<int, 4>{}, tmp[4]);
+        store_slice(0, std::integral_constant<int, 5>{}, tmp[5]);
+        store_slice(0, std::integral_constant<int, 6>{}, tmp[6]);
+        store_slice(0, std::integral_constant<int, 7>{}, tmp[7]);
         if (nch > 1) {
-            store_slice(wsm[1], std::integral_constant<int, 0>{}, tmp[8]);
-            store_slice(wsm[1], std::integral_constant<int, 1>{}, tmp[9]);
+            store_slice(1, std::integral_constant<int, 0>{}, tmp[8]);
+            store_slice(1, std::integral_constant<int, 1>{}, tmp[9]);
         }
         fetch_slice(1, std::integral_constant<int, 2>{}, wr[0]);
         fetch_slice(1, std::integral_constant<int, 3>{}, wr[1]);
@@ -534,8 +620,8 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
     // raw weight words of steps s and s+1 (rwd/rwq[s & 1]), read two steps ahead
     uint32_t rwd[2][JT], rwq[2][JT][NRAW];
     load_a(0, afr[0]);
-    read_b(wsm[0], std::integral_constant<int, 0>{}, rwd[0], rwq[0]);
-    read_b(wsm[0], std::integral_constant<int, 1>{}, rwd[1], rwq[1]);
+    read_b(0, std::integral_constant<int, 0>{}, rwd[0], rwq[0]);
+    read_b(0, std::integral_constant<int, 1>{}, rwd[1], rwq[1]);
     decode_b(std::integral_constant<int, 0>{}, rwd[0], rwq[0], bfr[0]);
     // Step 0 writes X(2) into xs[0]: every wave's read of X(0) from it must be done
     // first (in the loop the step-end barrier separates a buffer's reads from its
@@ -560,7 +646,7 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
             // (1) LDS reads first, so that their latency is spent under the MFMAs:
             // A fragments of step s+1, raw weight words of step s+2.
             load_a(P ^ 1, afr[P ^ 1]);
-            read_b(wsm[(ch + ((blk + 2) >> 3)) & 1], std::integral_constant<int, B2>{}, rwd[P],
+            read_b((ch + ((blk + 2) >> 3)) & 1, std::integral_constant<int, B2>{}, rwd[P],
                    rwq[P]);
             // (2) staging: X(s+2) -> xs[P] (X(s) was read during step s-1), then
             // fetch the X that step s+PD writes (s+3 for f32 X, one step ahead);
@@ -574,7 +660,7 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
             }
             {
                 const int wc = ch + 1 + ((blk + 2) >> 3);  // chunk receiving the slice
-                if (wc < nch) store_slice(wsm[wc & 1], std::integral_constant<int, B2>{}, wr[RG]);
+                if (wc < nch) store_slice(wc & 1, std::integral_constant<int, B2>{}, wr[RG]);
                 fetch_slice(ch + 1 + ((blk + PD + 2) >> 3),
                             std::integral_constant<int, (blk + PD + 2) & 7>{}, wr[RG]);
             }
@@ -1393,16 +1479,19 @@ TileChoice choose_tiles(const GemmArgs &a, bool allow_split) {
     const bool swiglu = a.epilogue == EPI_SWIGLU;
     const int nchunks = a.k / 256;
     const int cus = 256;
-    if (a.T <= SHORT_T) {
+    if (a.T <= SHORT_T || a.qtype == XQ_Q6_K) {
         // One row tile: the matrix-core work is small and the time is the weight
         // stream and its decode. MT x 128 tiles with the waves side by side (no
         // column decoded twice), split along K to fill the resident slots: the
         // split count minimises rounds of workgroups x (chunks per workgroup + one
         // chunk's worth of fixed cost). SwiGLU cannot split: its epilogue is not
-        // linear in the partial sums.
+        // linear in the partial sums. Q6_K keeps these tiles (several of 128 rows)
+        // up to 511 rows: its decode is the heaviest, and the cost model's tiles
+        // decode each column in two waves (gate/up 2 x 12288 x 4096 at T = 300: 220 us
+        // against 303 on 128 x 128; Q4_K there: 108 against 86 at T = 200).
         const int mt = a.T <= 32 ? 32 : a.T <= 64 ? 64 : 128;
         const int cfg = mt == 32 ? 4 : mt == 64 ? 5 : 6;
-        const int tn = (a.n + 127) / 128;
+        const int tn = (a.n + 127) / 128 * ((a.T + mt - 1) / mt);
         if (swiglu || !allow_split) return TileChoice{cfg, 1};
         const long slots = (long)cus * short_tile_waves(a.qtype, mt);
         int best_s = 1;
@@ -1538,14 +1627,13 @@ hipError_t launch_swiglu_scratch(const GemmArgs &a, const uint16_t *xh, float *G
     return hipGetLastError();
 }
 
-// Most K splits the GEMM below 256 rows takes for these sizes: over Q4_0 and Q8_0
-// (their workspace size does not depend on which), or the further types' own choice
-// (they all choose as Q4_K does).
+// Most K splits the 4-wave GEMM takes for these sizes: over Q4_0 and Q8_0 (their
+// workspace size does not depend on which), or a further type's own choice.
 int small_t_splits(int qtype, int T, int n, int k, int epilogue) {
-    const bool xq = qtype == XQ_Q4_K || qtype == XQ_Q5_K || qtype == XQ_IQ4_XS;
+    const bool xq = qtype == XQ_Q4_K || qtype == XQ_Q5_K || qtype == XQ_IQ4_XS || qtype == XQ_Q6_K;
     int m = 1;
-    for (int q : {(int)Q4_0, (int)Q8_0, (int)XQ_Q4_K}) {
-        if ((q == XQ_Q4_K) != xq) continue;
+    const int types[2] = {xq ? qtype : (int)Q4_0, xq ? qtype : (int)Q8_0};
+    for (int q : types) {
         GemmArgs g;
         g.qtype = q;
         g.epilogue = epilogue;
@@ -1696,12 +1784,19 @@ static int coop_splits(int T, int n, int k, int epilogue) {
 
 // The further types this file's GEMMs take on the workspace path: Q4_K, Q5_K and
 // IQ4_XS at every T (the 4-wave kernel below 256 rows, the cooperative kernel from
-// 256); F16 and Q6_K (k % 512 == 0) from COOP_T512 (their 256 x 192 tile's staging
-// would need more than one piece per thread).
+// 256); Q6_K with k % 512 == 0 at every T (the 4-wave kernel below COOP_T512); F16
+// from COOP_T512 (its staging on the other tiles would need more than one piece per
+// thread).
 bool f16_takes_xq(int qtype, int T, int k) {
     if (qtype == XQ_Q4_K || qtype == XQ_Q5_K || qtype == XQ_IQ4_XS) return true;
-    return T >= COOP_T512 && (qtype == XQ_F16 || (qtype == XQ_Q6_K && k % 512 == 0));
+    if (qtype == XQ_Q6_K) return k % 512 == 0;
+    return qtype == XQ_F16 && T >= COOP_T512;
 }
+
+// Which f16 GEMM runs: the 4-wave kernel (X copied as [T][k]) below 256 rows, and for
+// Q6_K below COOP_T512 (it has no 256 x 192 cooperative tile); else the cooperative
+// kernel (X in A-fragment order).
+static bool f16_four_wave(int qtype, int T) { return T < 256 || (qtype == XQ_Q6_K && T < COOP_T512); }
 
 // Byte offset of the partial sums in the workspace, and the floats between splits.
 static int64_t ws_x_bytes(int T, int k) { return ((int64_t)(T + 31) / 32 * 32 * k * 2 + 255) / 256 * 256; }
@@ -1721,7 +1816,7 @@ int64_t f16_ws_bytes(int qtype, int T, int n, int k, int epilogue) {
     const int64_t xb = (int64_t)(T + 31) / 32 * 32 * k * 2;
     if (swiglu_via_scratch(T, epilogue))
         return ws_x_bytes(T, k) + (int64_t)small_t_splits(qtype, T, 2 * n, k, EPI_PLAIN) * ws_pstride(T, 2 * n) * 4;
-    if (T < 256) {
+    if (f16_four_wave(qtype, T)) {
         const int splits = small_t_splits(qtype, T, n, k, epilogue);
         return splits > 1 ? ws_x_bytes(T, k) + (int64_t)splits * ws_pstride(T, n) * 4 : xb;
     }
@@ -1781,10 +1876,10 @@ hipError_t launch_coop_q(const GemmArgs &a, uint16_t *xh, hipStream_t s) {
 }
 
 // X -> binary16 into the workspace, in the layout the GEMM for (qtype, T) reads: A-fragment
-// order for T >= 256 (the cooperative kernel), [T][k] below.
+// order for the cooperative kernel, [T][k] for the 4-wave kernel (f16_four_wave).
 hipError_t launch_prepare_x_f16(const GemmArgs &a, void *workspace, hipStream_t s) {
     uint16_t *xh = static_cast<uint16_t *>(workspace);
-    if (a.T >= 256) {
+    if (!f16_four_wave(a.qtype, a.T)) {
         const int count = (a.T + 31) / 32 * 32 * (a.k / 16);  // (row, 16-k slice) pairs
         const dim3 g((count + 255) / 256);
         if (a.norm_inv) {
@@ -1826,7 +1921,7 @@ hipError_t launch_prepare_x_f16(const GemmArgs &a, void *workspace, hipStream_t 
 // qtype, k and T); any split-K partial sums (or the SwiGLU scratch G) go behind it.
 hipError_t launch_gemm_f16_prepared(const GemmArgs &a, void *workspace, hipStream_t s) {
     uint16_t *xh = static_cast<uint16_t *>(workspace);
-    if (a.T >= 256) {
+    if (!f16_four_wave(a.qtype, a.T)) {
         switch (a.qtype) {
         case Q4_0: return launch_coop_q<Q4_0>(a, xh, s);
         case Q8_0: return launch_coop_q<Q8_0>(a, xh, s);
@@ -1845,10 +1940,11 @@ hipError_t launch_gemm_f16_prepared(const GemmArgs &a, void *workspace, hipStrea
     switch (a.qtype) {
     case Q4_0: return g ? launch_swiglu_scratch<Q4_0>(a, xh, ps, s) : launch_q<Q4_0>(a, xh, s, ps);
     case Q8_0: return g ? launch_swiglu_scratch<Q8_0>(a, xh, ps, s) : launch_q<Q8_0>(a, xh, s, ps);
-    // further types below 256 rows (f16_takes_xq)
+    // further types on the 4-wave kernel (f16_takes_xq)
     case XQ_Q4_K: return g ? launch_swiglu_scratch<XQ_Q4_K>(a, xh, ps, s) : launch_q<XQ_Q4_K>(a, xh, s, ps);
     case XQ_Q5_K: return g ? launch_swiglu_scratch<XQ_Q5_K>(a, xh, ps, s) : launch_q<XQ_Q5_K>(a, xh, s, ps);
     case XQ_IQ4_XS: return g ? launch_swiglu_scratch<XQ_IQ4_XS>(a, xh, ps, s) : launch_q<XQ_IQ4_XS>(a, xh, s, ps);
+    case XQ_Q6_K: return g ? launch_swiglu_scratch<XQ_Q6_K>(a, xh, ps, s) : launch_q<XQ_Q6_K>(a, xh, s, ps);
     default: return hipErrorInvalidValue;
     }
 }

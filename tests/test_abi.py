@@ -185,10 +185,11 @@ def test_workspace_bytes(lib):
     # 5 chunks of k are too few to split in two
     assert wb(pf.PF_Q4_0, 17, 1280, 290, pf.PF_RESIDUAL, pf.PF_LEG_F16) == 320 * 1280 * 2
     assert wb(pf.PF_Q4_0, 4096, 4096, 512, pf.PF_PLAIN, pf.PF_LEG_F32) == 0
-    # the further types take no workspace on the f32 leg; on the f16 leg Q4_K, Q5_K and
-    # IQ4_XS from 9 rows (the 4-wave tiles below 256, the cooperative kernel from 256),
-    # and F16 and Q6_K (k % 512 == 0: rows a multiple of 4 bytes) from 512, take Q4_0's
-    # GEMMs and their workspace layout (X, then the split count these types take).
+    # the further types take no workspace on the f32 leg; on the f16 leg Q4_K, Q5_K,
+    # IQ4_XS and Q6_K (k % 512 == 0: rows a multiple of 4 bytes) from 9 rows (the 4-wave
+    # tiles below 256, or 512 for Q6_K; the cooperative kernel above), and F16 from 512,
+    # take Q4_0's GEMMs and their workspace layout (X, then the split count these types
+    # take).
     # Elsewhere on the f16 leg their own GEMM (64- or 128-row x 128-column tiles) splits K
     # through the workspace when the tiles leave the resident slots (3 per CU) idle:
     # 768 / tiles splits, each at least 512 k, at most 16, one [T][rows] f32 block each;
@@ -203,19 +204,27 @@ def test_workspace_bytes(lib):
     for qt in (pf.PF_F16, pf.PF_Q4_K, pf.PF_Q5_K, pf.PF_Q6_K, pf.PF_IQ4_XS):
         for T in (1, 8, 9, 300, 511, 512, 2048):
             for epi in (pf.PF_PLAIN, pf.PF_RESIDUAL, pf.PF_GATE_UP_SWIGLU):
-                kq = qt in (pf.PF_Q4_K, pf.PF_Q5_K, pf.PF_IQ4_XS)
+                kq = qt in (pf.PF_Q4_K, pf.PF_Q5_K, pf.PF_IQ4_XS, pf.PF_Q6_K)
                 coop = T >= 512 or (kq and T >= 9)
                 sp = own_splits(T, 4096, 4096, epi)
                 rows = 8192 if epi == pf.PF_GATE_UP_SWIGLU else 4096
                 want = wb(pf.PF_Q4_0, 4096, 4096, T, epi, pf.PF_LEG_F16) if coop else \
                     (sp * ((T * rows + 3) // 4 * 4) * 4 if sp > 1 else 0)
+                if qt == pf.PF_Q6_K and 256 <= T < 512:
+                    # Q6_K's 4-wave tiles where Q4_0 runs the cooperative kernel
+                    want = wb(qt, 4096, 4096, T, epi, pf.PF_LEG_F16)
+                    assert want >= -(-T // 32) * 32 * 4096 * 2
                 assert wb(qt, 4096, 4096, T, epi, pf.PF_LEG_F16) == want
                 assert wb(qt, 4096, 4096, T, epi, pf.PF_LEG_F32) == 0
-    # the narrow down projection at T = 32 on Q6_K's own GEMM: 32 tiles, 16 splits; Q4_K
-    # gate/up at T = 32 on the short-chunk tiles: X, then G [32][24576] in 4 splits (192
-    # tiles of 32 x 128 over 768 resident slots, three workgroups per CU, as Q4_0); at
-    # 64 rows two workgroups per CU (512 slots): 2 splits
-    assert wb(pf.PF_Q6_K, 4096, 12288, 32, pf.PF_RESIDUAL, pf.PF_LEG_F16) == 16 * 32 * 4096 * 4
+    # the narrow down projection at T = 32: on Q6_K's own GEMM (k = 12544, 49 super-blocks
+    # a row) 32 tiles, 16 splits; on the short-chunk tiles (k = 12288) X, then 32 tiles
+    # over 512 slots (two workgroups per CU), 16 splits. Q4_K gate/up at T = 32 on the
+    # short-chunk tiles: X, then G [32][24576] in 4 splits (192 tiles of 32 x 128 over 768
+    # resident slots, three workgroups per CU, as Q4_0); at 64 rows two workgroups per
+    # CU (512 slots): 2 splits
+    assert wb(pf.PF_Q6_K, 4096, 12544, 32, pf.PF_RESIDUAL, pf.PF_LEG_F16) == 16 * 32 * 4096 * 4
+    assert wb(pf.PF_Q6_K, 4096, 12288, 32, pf.PF_RESIDUAL, pf.PF_LEG_F16) == \
+        32 * 12288 * 2 + 16 * 32 * 4096 * 4
     for qt in (pf.PF_Q4_0, pf.PF_Q4_K):
         assert wb(qt, 12288, 4096, 32, pf.PF_GATE_UP_SWIGLU, pf.PF_LEG_F16) == \
             32 * 4096 * 2 + 4 * 32 * 24576 * 4
@@ -228,6 +237,10 @@ def test_workspace_bytes(lib):
         224 * 4096 * 2 + 4 * 200 * 12288 * 4
     assert wb(pf.PF_Q4_K, 12288, 4096, 200, pf.PF_PLAIN, pf.PF_LEG_F16) == \
         224 * 4096 * 2 + 8 * 200 * 12288 * 4
+    # Q6_K up to 511 rows keeps the short-chunk tiles, several of 128 rows: 3 x 32 tiles at
+    # T = 300 over 256 slots (one workgroup per CU), 2 splits
+    assert wb(pf.PF_Q6_K, 4096, 4096, 300, pf.PF_PLAIN, pf.PF_LEG_F16) == \
+        320 * 4096 * 2 + 2 * 300 * 4096 * 4
     # Q6_K rows of an odd number of super-blocks (2-byte aligned rows) keep its own GEMM
     # (512 rows, 4096 columns: 256 tiles, 3 splits)
     assert own_splits(512, 4096, 4352, pf.PF_PLAIN) == 3

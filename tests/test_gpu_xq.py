@@ -159,7 +159,8 @@ def test_xq_coop_256_rows(gpu, qtype, epi):
     assert ok, "parity failed: metric %.3e" % err
 
 
-KQ = [synth.Q4_K, synth.Q5_K, synth.IQ4_XS]
+# the types Q4_0's 4-wave GEMM takes below 256 rows (Q6_K: k % 512 == 0, and up to 511)
+KQ = [synth.Q4_K, synth.Q5_K, synth.IQ4_XS, synth.Q6_K]
 
 
 @pytest.mark.parametrize("epi", [PLAIN, RESIDUAL, SWIGLU])
@@ -167,8 +168,9 @@ KQ = [synth.Q4_K, synth.Q5_K, synth.IQ4_XS]
 @pytest.mark.parametrize("kind", ["synth", "edge"])
 @pytest.mark.parametrize("qtype", KQ, ids=lambda q: NAMES[q])
 def test_xq_4wave_every_output(gpu, qtype, kind, T, epi):
-    """On the f16 leg with a workspace below 256 rows, Q4_K, Q5_K and IQ4_XS take Q4_0's
-    4-wave GEMM, each lane decoding its own B fragments from the staged super-blocks: up
+    """On the f16 leg with a workspace below 256 rows, Q4_K, Q5_K, IQ4_XS and Q6_K take
+    Q4_0's 4-wave GEMM, each lane decoding its own B fragments from the staged super-blocks
+    (Q6_K's odd chunks two bytes past a dword boundary): up
     to 128 rows its short-chunk tiles (32, 64 or 128 token rows x 128 weight rows, the
     four waves side by side), T = 9 .. 128 covering each tile height, full and ragged;
     at 130 and 255 the cost model's 64 x 64 tiles. n = 150 leaves the last weight tile
@@ -199,7 +201,7 @@ def test_xq_4wave_every_output(gpu, qtype, kind, T, epi):
 def test_xq_4wave_wide_tiles(gpu, qtype, n, T, epi):
     """The cost model's larger tiles between 129 and 255 rows (k = 4096): 128 x 128 split 8
     ways (n = 2000), 256 x 128 split 8 ways (n = 4096), and 128 x 128 unsplit for SwiGLU
-    (the fused epilogue), on every output."""
+    (the fused epilogue), on every output; Q6_K keeps two 128-row short-chunk tiles."""
     k = 4096
     rows = 2 * n if epi == SWIGLU else n
     seed = 790 + 7 * qtype + T + epi
@@ -212,10 +214,29 @@ def test_xq_4wave_wide_tiles(gpu, qtype, n, T, epi):
     assert ok, "parity failed: metric %.3e" % err
 
 
+@pytest.mark.parametrize("n,T,epi", [(150, 300, PLAIN), (150, 300, SWIGLU), (2000, 511, RESIDUAL)])
+def test_xq_q6_k_4wave_below_512(gpu, n, T, epi):
+    """Q6_K from 256 to 511 rows stays on the 4-wave GEMM (128-row short-chunk tiles, three
+    or four of them; its cooperative kernel has only the 512-row tile): ragged tiles both
+    ways, every output."""
+    qtype, k = synth.Q6_K, 2048
+    rows = 2 * n if epi == SWIGLU else n
+    seed = 800 + T + epi
+    W = _weights(qtype, rows, k, "edge", F16, seed)
+    X = synth.activations(T, k, workload_id=seed)
+    R = synth.activations(T, n, workload_id=seed, tensor_id=synth.TENSOR_R) if epi == RESIDUAL else None
+    print("case xq q6_k 4-wave n=%d T=%d epi=%d" % (n, T, epi), flush=True)
+    Y = parity.run_gpu(gpu, qtype, W, n, k, X, epi, F16, R=R, workspace=True)
+    ok, err = parity.check(qtype, W, n, k, X, Y, epi, F16, R=R)
+    assert ok, "parity failed: metric %.3e" % err
+
+
 @pytest.mark.parametrize("qtype", KQ, ids=lambda q: NAMES[q])
 def test_xq_short_tiles_shortest_k(gpu, qtype):
-    """k = 256 (one super-block per row: a single chunk, no split) at T = 20 and 100."""
-    n, k = 70, 256
+    """The shortest rows the 4-wave GEMM takes at T = 20 and 100: one super-block (k =
+    256: a single chunk, no split), for Q6_K two (k = 512, the second chunk two bytes past
+    a dword boundary)."""
+    n, k = 70, 512 if qtype == synth.Q6_K else 256
     for T, epi in [(20, PLAIN), (100, SWIGLU), (100, RESIDUAL)]:
         rows = 2 * n if epi == SWIGLU else n
         seed = 780 + 7 * qtype + T + epi
@@ -254,14 +275,14 @@ def test_xq_4wave_full_size_sampled(gpu, qtype, shape):
 @pytest.mark.parametrize("epi", [PLAIN, RESIDUAL])
 @pytest.mark.parametrize("qtype", XQ, ids=lambda q: NAMES[q])
 def test_xq_own_gemm_k_split(gpu, qtype, epi, T):
-    """Where Q4_0's f16 GEMMs do not take them (F16 and Q6_K below 512 rows), the further
-    types' own GEMM splits PLAIN / RESIDUAL K through the workspace when its tiles leave
-    CUs idle: n = 150 is two 128-column tiles, so k = 4096 splits 8 ways (512 k each; the
-    cap), and the sum kernel adds R and the splits in order. pf_gemm_noalloc runs the
-    same kernels: same bits."""
+    """Where Q4_0's f16 GEMMs do not take them (F16 below 512 rows, Q6_K rows of an odd
+    number of super-blocks), the further types' own GEMM splits PLAIN / RESIDUAL K through
+    the workspace when its tiles leave CUs idle: n = 150 is two 128-column tiles, so k =
+    4096 (Q6_K 4352) splits 8 ways (at least 512 k each; the cap), and the sum kernel adds
+    R and the splits in order. pf_gemm_noalloc runs the same kernels: same bits."""
     import torch
-    n, k = 150, 4096
-    if qtype in KQ:
+    n, k = 150, 4352 if qtype == synth.Q6_K else 4096
+    if qtype in KQ and qtype != synth.Q6_K:
         pytest.skip("Q4_0's f16 GEMMs take this type")
     seed = 700 + 7 * qtype + 3 * epi + T
     W = _weights(qtype, n, k, "edge", F16, seed)
@@ -282,13 +303,13 @@ def test_xq_own_gemm_k_split(gpu, qtype, epi, T):
 @pytest.mark.parametrize("T", [9, 64])
 @pytest.mark.parametrize("qtype", XQ, ids=lambda q: NAMES[q])
 def test_xq_own_gemm_swiglu_scratch(gpu, qtype, T):
-    """SwiGLU on the f16 leg with a workspace up to 64 rows (F16 and Q6_K; the others take
-    Q4_0's short-chunk tiles there): the gate and up rows run as one PLAIN GEMM over the 2n
-    rows, split 8 ways along k = 4096 into G, then silu(g) * u sums each half in split
-    order. pf_gemm_noalloc runs the same kernels: same bits."""
+    """SwiGLU on the f16 leg with a workspace up to 64 rows on the own GEMM (F16, and Q6_K
+    with k = 4352; the others take Q4_0's short-chunk tiles there): the gate and up rows
+    run as one PLAIN GEMM over the 2n rows, split 8 ways along k into G, then silu(g) * u
+    sums each half in split order. pf_gemm_noalloc runs the same kernels: same bits."""
     import torch
-    n, k = 150, 4096
-    if qtype in KQ:
+    n, k = 150, 4352 if qtype == synth.Q6_K else 4096
+    if qtype in KQ and qtype != synth.Q6_K:
         pytest.skip("Q4_0's f16 GEMMs take this type")
     seed = 720 + 7 * qtype + T
     W = _weights(qtype, 2 * n, k, "edge", F16, seed)
@@ -309,11 +330,11 @@ def test_xq_own_gemm_swiglu_scratch(gpu, qtype, T):
 @pytest.mark.parametrize("T", [40, 300, 520])
 @pytest.mark.parametrize("qtype", XQ, ids=lambda q: NAMES[q])
 def test_xq_strided_y_workspace(gpu, qtype, T, epi):
-    """pf_gemm_ex with a workspace into a strided Y: the further types' own GEMM split
-    through the workspace (T = 40 for F16 and Q6_K, SwiGLU through G; T = 300 for F16 and
-    Q6_K, whose SwiGLU there takes no workspace), the short-chunk tiles (T = 40 for Q4_K,
-    Q5_K and IQ4_XS) and the cooperative kernel (T = 300 for Q4_K, Q5_K and IQ4_XS; T = 520
-    for all); the columns between Y's rows keep their bits."""
+    """pf_gemm_ex with a workspace into a strided Y: F16's own GEMM split through the
+    workspace (T = 40, SwiGLU through G; T = 300, whose SwiGLU there takes no workspace),
+    the 4-wave GEMM (T = 40 for the others, T = 300 for Q6_K) and the cooperative kernel
+    (T = 300 for Q4_K, Q5_K and IQ4_XS; T = 520 for all); the columns between Y's rows keep
+    their bits."""
     from tests.test_gpu_strided import check_gaps, run_strided
     n, k = 200, 2048
     rows = 2 * n if epi == SWIGLU else n
