@@ -72,10 +72,10 @@ KERNEL_SOURCES = {
 
 def kernel_family(T, leg, qtype=0):
     if qtype not in (Q4_0, Q8_0):
-        # the further types take the cooperative-decode GEMM through a workspace from 512
-        # rows on the f16 leg (Q6_K with k % 512 == 0, as every workload here has; Q4_K,
-        # Q5_K and IQ4_XS already from 256)
-        return "gemm_f16" if leg == 1 and T >= 512 else "xq"
+        # on the f16 leg above the GEMV the further types take Q4_0's matrix-core GEMMs
+        # (Q4_K, Q5_K, IQ4_XS and Q6_K with k % 512 == 0, as every workload here has, at
+        # every T; F16 from 512 rows)
+        return "gemm_f16" if leg == 1 and T > 8 and (qtype != F16W or T >= 512) else "xq"
     return "gemv" if T <= 8 else ("gemm_f16" if leg == 1 else "gemm_f32")
 
 
@@ -140,6 +140,12 @@ def workloads():
         "gate_up_q5_k_T512_f16": (512, 1, [("gate_up_swiglu_q5_k", Q5_K, INTER, HIDDEN, SWIGLU, "x", "act")], 1),
         "gate_up_f16w_T512_f16": (512, 1, [("gate_up_swiglu_f16w", F16W, INTER, HIDDEN, SWIGLU, "x", "act")], 1),
         "down_q6_k_T512_f16": (512, 1, [("down_residual_q6_k", Q6_K, HIDDEN, INTER, RESIDUAL, "act", "res")], 1),
+        # the K-quant mix of a typical 4-bit file (gate/up Q4_K, down Q6_K) as the FFN at
+        # 32 rows (the 4-wave GEMM's short-chunk tiles) and 512 (the cooperative kernel)
+        "ffn_q4_k_q6_k_T32_f16": (32, 1, [("gate_up_swiglu_q4_k", Q4_K, INTER, HIDDEN, SWIGLU, "x", "act"),
+                                          ("down_residual_q6_k", Q6_K, HIDDEN, INTER, RESIDUAL, "act", "res")], 2),
+        "ffn_q4_k_q6_k_T512_f16": (512, 1, [("gate_up_swiglu_q4_k", Q4_K, INTER, HIDDEN, SWIGLU, "x", "act"),
+                                            ("down_residual_q6_k", Q6_K, HIDDEN, INTER, RESIDUAL, "act", "res")], 2),
         "gemv_q4_k_12288x4096_T1": (1, 0, [("gemv_q4_k", Q4_K, INTER, HIDDEN, PLAIN, "x", "out")], 1),
         "gemv_q5_k_12288x4096_T1": (1, 0, [("gemv_q5_k", Q5_K, INTER, HIDDEN, PLAIN, "x", "out")], 1),
         "gemv_q6_k_4096x12288_T1": (1, 0, [("gemv_q6_k", Q6_K, HIDDEN, INTER, PLAIN, "x12288", "out")], 1),

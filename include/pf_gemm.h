@@ -71,13 +71,14 @@ extern "C" {
 #endif
 
 /* Block types. F16 .. IQ4_XS run their own kernels on both legs and need no
- * workspace, except on the f16 leg, where pf_gemm_ws runs Q4_K, Q5_K and IQ4_XS at
- * every T above the GEMV, and F16 and Q6_K (k % 512 == 0) from 512 rows, on Q4_0's
- * matrix-core GEMMs (the 4-wave tiles below 256 rows, the cooperative-decode kernel
- * from 256), with that GEMM's workspace; elsewhere their own GEMM splits K through the
- * workspace where its tiles leave CUs idle (pf_gemm, and pf_gemm_noalloc where the
- * workspace exceeds the static scratch, keep their own GEMM unsplit). pf_prepare_x and
- * pf_gemm_prepared take Q4_0 and Q8_0 only. */
+ * workspace, except on the f16 leg's GEMM: there pf_gemm_ws runs Q4_K, Q5_K, IQ4_XS and
+ * Q6_K (k % 512 == 0) at every T, and F16 from 512 rows, on Q4_0's matrix-core GEMMs
+ * (the 4-wave tiles below 256 rows, 512 for Q6_K; the cooperative-decode kernel above),
+ * with that GEMM's workspace, and elsewhere their own GEMM splits K through the
+ * workspace where its tiles leave CUs idle. Without a workspace (pf_gemm, and
+ * pf_gemm_noalloc where the workspace exceeds the static scratch) Q4_K, Q5_K, IQ4_XS
+ * and Q6_K (k % 512 == 0) run the 4-wave GEMM unsplit, F16 and the other Q6_K rows
+ * their own GEMM unsplit. pf_prepare_x and pf_gemm_prepared take Q4_0 and Q8_0 only. */
 enum { PF_Q4_0 = 0, PF_Q8_0 = 1, PF_F16 = 2, PF_Q4_K = 3, PF_Q5_K = 4, PF_Q6_K = 5, PF_IQ4_XS = 6 };
 
 /* Epilogues.

@@ -142,7 +142,11 @@ int gemm_impl(int qtype, const void *W, int64_t n, int64_t k, const float *X, in
     a.k = (int)k;
     a.T = (int)T;
     hipError_t err;
-    if (is_xq(qtype) && (need == 0 || !pf::f16_takes_xq(qtype, (int)T, (int)k)))
+    // The further types on the f16 leg's matrix-core GEMMs, where those take them (with
+    // the workspace, or without it on the 4-wave kernel); else their own kernels.
+    const bool xq_f16 = use == PF_PATH_GEMM && leg == PF_LEG_F16 &&
+                        (need > 0 ? pf::f16_takes_xq(qtype, (int)T, (int)k) : pf::f16_direct_takes_xq(qtype, (int)k));
+    if (is_xq(qtype) && !xq_f16)
         err = use == PF_PATH_GEMV ? pf::launch_xq_gemv(a, s)
                                   : pf::launch_xq_gemm(a, leg == PF_LEG_F16, need > 0 ? ws : nullptr, s);
     else if (use == PF_PATH_GEMV)

@@ -150,10 +150,10 @@ void gemm_f16_kernel(const uint8_t *__restrict__ W, const void *__restrict__ Xv,
                      int splits, long pstride) {
     using CT = ChunkTraits<QT>;
     constexpr int BB = CT::BB;
-    // Further types (Q4_K, Q5_K, IQ4_XS, Q6_K with k % 512 == 0): on the fp16 X copy
-    // only; a row's 256-k chunk is one super-block, and step blk its sub-block blk.
+    // Further types (Q4_K, Q5_K, IQ4_XS, Q6_K with k % 512 == 0): a row's 256-k chunk is
+    // one super-block, and step blk its sub-block blk.
     constexpr bool XQ = coop_xq<QT>();
-    static_assert(!XQ || (XH && QT != XQ_F16), "further types: fp16 X, not F16");
+    static_assert(!XQ || QT != XQ_F16, "further types: not F16");
     // Waves: WVM x WVN over the tile. ROW1 tiles (few token rows) put all four side
     // by side along the weight rows, so that no two decode the same columns.
     constexpr int WVM = ROW1 ? 1 : 2;
@@ -1539,12 +1539,7 @@ hipError_t launch_cfg(const GemmArgs &a, int splits, const uint16_t *xh, long ps
     const int tm = (a.T + MT - 1) / MT;
     const int tn = (a.n + OUT - 1) / OUT;
     const int total = tm * tn * splits;
-    if constexpr (coop_xq<QT>()) {
-        // further types: the fp16 X copy only
-        if (!xh) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((gemm_f16_kernel<QT, EPI, MT, NW, SPLIT, true, ROW1>), dim3(total), dim3(256), 0,
-                           s, a.W, (const void *)xh, a.Y, a.n, a.ldy, a.k, a.T, tm, tn, splits, pstride);
-    } else if (xh) {
+    if (xh) {
         hipLaunchKernelGGL((gemm_f16_kernel<QT, EPI, MT, NW, SPLIT, true, ROW1>), dim3(total), dim3(256), 0,
                            s, a.W, (const void *)xh, a.Y, a.n, a.ldy, a.k, a.T, tm, tn, splits, pstride);
     } else {
@@ -1793,6 +1788,12 @@ bool f16_takes_xq(int qtype, int T, int k) {
     return qtype == XQ_F16 && T >= COOP_T512;
 }
 
+// The further types the f16 GEMM without a workspace (the 4-wave kernel, X rounded in
+// each tile, unsplit) takes: Q4_K, Q5_K, IQ4_XS, and Q6_K with k % 512 == 0.
+bool f16_direct_takes_xq(int qtype, int k) {
+    return qtype == XQ_Q4_K || qtype == XQ_Q5_K || qtype == XQ_IQ4_XS || (qtype == XQ_Q6_K && k % 512 == 0);
+}
+
 // Which f16 GEMM runs: the 4-wave kernel (X copied as [T][k]) below 256 rows, and for
 // Q6_K below COOP_T512 (it has no 256 x 192 cooperative tile); else the cooperative
 // kernel (X in A-fragment order).
@@ -1956,7 +1957,16 @@ hipError_t launch_gemm_f16_ws(const GemmArgs &a, void *workspace, hipStream_t s)
 }
 
 hipError_t launch_gemm_f16(const GemmArgs &a, hipStream_t s) {
-    return a.qtype == Q4_0 ? launch_q<Q4_0>(a, nullptr, s) : launch_q<Q8_0>(a, nullptr, s);
+    switch (a.qtype) {
+    case Q4_0: return launch_q<Q4_0>(a, nullptr, s);
+    case Q8_0: return launch_q<Q8_0>(a, nullptr, s);
+    // further types (f16_direct_takes_xq)
+    case XQ_Q4_K: return launch_q<XQ_Q4_K>(a, nullptr, s);
+    case XQ_Q5_K: return launch_q<XQ_Q5_K>(a, nullptr, s);
+    case XQ_IQ4_XS: return launch_q<XQ_IQ4_XS>(a, nullptr, s);
+    case XQ_Q6_K: return launch_q<XQ_Q6_K>(a, nullptr, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace pf

@@ -44,6 +44,9 @@ int64_t f16_ws_bytes(int qtype, int T, int n, int k, int epilogue);
 // T: the 4-wave kernel below 256 rows, the cooperative-decode kernel from 256; F16, and
 // Q6_K with k % 512 == 0, from 512); the others keep their own GEMM.
 bool f16_takes_xq(int qtype, int T, int k);
+// The further types the f16 GEMM without a workspace takes (launch_gemm_f16: Q4_K, Q5_K,
+// IQ4_XS, and Q6_K with k % 512 == 0); the others keep their own GEMM there.
+bool f16_direct_takes_xq(int qtype, int k);
 // Floats between the [T][n] partial-sum blocks of a K split, and Y = [R +] the `splits`
 // blocks at ps added in split order (PLAIN or RESIDUAL; a.Y, a.ldy, a.T, a.n).
 long part_stride(int T, int n);

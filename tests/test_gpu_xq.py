@@ -194,6 +194,11 @@ def test_xq_4wave_every_output(gpu, qtype, kind, T, epi):
     gpu.gemm_noalloc(qtype, Wd, n, k, Xd, Yd, epi, F16)
     torch.cuda.synchronize()
     assert np.array_equal(Y.view(np.uint32), Yd.cpu().numpy().view(np.uint32))
+    if epi == SWIGLU and T > 64:
+        # unsplit (the fused epilogue): pf_gemm, which rounds X to binary16 inside each
+        # tile, runs the same tiles on the same operands: the same bits
+        Y0 = parity.run_gpu(gpu, qtype, W, n, k, X, epi, F16, Wd=Wd, Xd=Xd)
+        assert np.array_equal(Y.view(np.uint32), Y0.view(np.uint32))
 
 
 @pytest.mark.parametrize("n,T,epi", [(2000, 200, PLAIN), (4096, 200, RESIDUAL), (4096, 160, SWIGLU)])
