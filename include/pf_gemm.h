@@ -103,11 +103,11 @@ enum { PF_PLAIN = 0, PF_RESIDUAL = 1, PF_GATE_UP_SWIGLU = 2 };
 enum { PF_LEG_F32 = 0, PF_LEG_F16 = 1 };
 
 /* Kernel family. PF_PATH_AUTO picks the GEMV for 1 <= T <= PF_GEMV_MAX_T and the
- * tiled matrix-core GEMM otherwise, except that for Q4_0 and Q8_0 the f16 leg takes
- * the GEMM from T = 3 for PLAIN and RESIDUAL and from T = 5 for SwiGLU (faster there
- * through a workspace, whose K split spreads the weight stream over every CU). The
- * other two force a family (tests compare them); PF_PATH_GEMV requires T <=
- * PF_GEMV_MAX_T. */
+ * tiled matrix-core GEMM otherwise, except that for Q4_0, Q8_0, Q4_K, Q5_K, IQ4_XS and
+ * Q6_K (k % 512 == 0) the f16 leg takes the GEMM from T = 3 for PLAIN and RESIDUAL and
+ * from T = 5 for SwiGLU (faster there through a workspace, whose K split spreads the
+ * weight stream over every CU). The other two force a family (tests compare them);
+ * PF_PATH_GEMV requires T <= PF_GEMV_MAX_T. */
 enum { PF_PATH_AUTO = 0, PF_PATH_GEMM = 1, PF_PATH_GEMV = 2 };
 #define PF_GEMV_MAX_T 8
 
@@ -232,9 +232,10 @@ int pf_gemm_rmsnorm(int qtype, const void *W_blocks, int64_t n, int64_t k, const
                     void *workspace, int64_t workspace_bytes, void *stream);
 
 /* Workspace bytes pf_gemm_rmsnorm needs, or -PF_E_* for sizes pf_gemm would refuse.
- * 0 for T == 0; else ceil(T * 4 / 256) * 256 (the rows' 1 / rms) plus, on the f16
- * leg's matrix-core GEMM (the family PF_PATH_AUTO picks), pf_workspace_bytes() for the same
- * sizes, otherwise T * k * 4 (Xn in f32). Host-only. */
+ * 0 for T == 0; else ceil(T * 4 / 256) * 256 (the rows' 1 / rms) plus, where
+ * pf_gemm_ws would run the f16 leg's matrix-core GEMMs with a workspace (the family
+ * PF_PATH_AUTO picks; for the further types where those GEMMs take them),
+ * pf_workspace_bytes() for the same sizes, otherwise T * k * 4 (Xn in f32). Host-only. */
 int64_t pf_rmsnorm_workspace_bytes(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int leg);
 
 /* pf_gemm_ws without a caller workspace and without any allocation, for callers that

@@ -65,10 +65,15 @@ int check_sizes(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int le
 // weights faster than the GEMV (whose time grows with each pair of rows). SwiGLU
 // splits K only through a workspace, so its crossing comes later (gate/up 2 x 12288 x
 // 4096: GEMV 36 us at 4 rows and 54 at 6, GEMM 43 unsplit or 28 through a workspace).
-// The further types take the GEMV up to PF_GEMV_MAX_T rows on both legs.
-int auto_path(int qtype, int64_t T, int epilogue, int leg) {
+// The further types that the f16 leg's 4-wave GEMM takes (Q4_K, Q5_K, IQ4_XS, Q6_K with
+// k % 512 == 0) cross over at the same row counts (their GEMVs are slower than Q4_0's:
+// down 4096 x 12288 Q4_K at T = 4 through a workspace 56.8 -> 20.0 us, gate/up T = 8
+// 70.1 -> 29.6; PLAIN 12288 x 4096 at T = 3 gives up 2 us, Q6_K's 12 at T = 3 and 8 at
+// T = 4); F16 and the other Q6_K rows take the GEMV up to PF_GEMV_MAX_T rows on both legs.
+int auto_path(int qtype, int64_t k, int64_t T, int epilogue, int leg) {
     if (T > PF_GEMV_MAX_T) return PF_PATH_GEMM;
-    if (!is_xq(qtype) && leg == PF_LEG_F16 && T >= (epilogue == PF_GATE_UP_SWIGLU ? 5 : 3))
+    if ((!is_xq(qtype) || pf::f16_direct_takes_xq(qtype, (int)k)) && leg == PF_LEG_F16 &&
+        T >= (epilogue == PF_GATE_UP_SWIGLU ? 5 : 3))
         return PF_PATH_GEMM;
     return PF_PATH_GEMV;
 }
@@ -113,7 +118,7 @@ int gemm_impl(int qtype, const void *W, int64_t n, int64_t k, const float *X, in
     const int64_t w_bytes = w_bytes_of(qtype, n_w, k);
     const int64_t x_bytes = T * k * 4, y_bytes = ((T - 1) * ldy + n) * 4;  // Y's rows and gaps
     if (overlap(Y, y_bytes, X, x_bytes) || overlap(Y, y_bytes, W, w_bytes)) return PF_E_ALIAS;
-    const int use = path == PF_PATH_AUTO ? auto_path(qtype, T, epilogue, leg) : path;
+    const int use = path == PF_PATH_AUTO ? auto_path(qtype, k, T, epilogue, leg) : path;
     int64_t need = ws_mode != WS_NONE ? ws_need(qtype, n, k, T, epilogue, leg, use) : 0;
     // A further type whose workspace would not fit the static scratch runs its own GEMM,
     // which needs none (as it does without a workspace).
@@ -165,11 +170,17 @@ int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
 // Workspace of the RMSNorm entry point: inv[T] (rounded up to 256 bytes), then the
 // f16 GEMM's own workspace (X rounded to binary16 with the norm applied, and any
 // split-K partial sums), or, for the kernels that read f32 X, Xn [T][k] f32.
+// Whether the RMSNorm entry point applies the norm inside the f16 leg GEMM's conversion
+// of X to binary16 (Q4_0, Q8_0 and the further types those GEMMs take), rather than
+// materialising Xn for a kernel that reads f32 X.
+bool rms_fused(int qtype, int64_t k, int64_t T, int leg, int use) {
+    return use == PF_PATH_GEMM && leg == PF_LEG_F16 && (!is_xq(qtype) || pf::f16_takes_xq(qtype, (int)T, (int)k));
+}
+
 int64_t rms_ws_need(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int leg, int use) {
     if (T == 0) return 0;
-    const int64_t tail = (use == PF_PATH_GEMM && leg == PF_LEG_F16 && !is_xq(qtype))
-                             ? pf::f16_ws_bytes(qtype, (int)T, (int)n, (int)k, epilogue)
-                             : T * k * 4;
+    const int64_t tail = rms_fused(qtype, k, T, leg, use) ? pf::f16_ws_bytes(qtype, (int)T, (int)n, (int)k, epilogue)
+                                                          : T * k * 4;
     return round256(T * 4) + tail;
 }
 
@@ -189,7 +200,7 @@ int rms_impl(int qtype, const void *W, int64_t n, int64_t k, const float *X, int
     if (overlap(Y, y_bytes, X, x_bytes) || overlap(Y, y_bytes, W, w_bytes) ||
         overlap(Y, y_bytes, norm_w, nw_bytes))
         return PF_E_ALIAS;
-    const int use = auto_path(qtype, T, epilogue, leg);
+    const int use = auto_path(qtype, k, T, epilogue, leg);
     const int64_t need = rms_ws_need(qtype, n, k, T, epilogue, leg, use);
     if (!ws || ws_bytes < need || !aligned16(ws)) return PF_E_WORKSPACE;
     if (overlap(ws, need, W, w_bytes) || overlap(ws, need, X, x_bytes) || overlap(ws, need, Y, y_bytes) ||
@@ -211,7 +222,7 @@ int rms_impl(int qtype, const void *W, int64_t n, int64_t k, const float *X, int
     uint8_t *rest = static_cast<uint8_t *>(ws) + round256(T * 4);
     hipError_t err = pf::launch_rms_inv(X, a.T, a.k, eps, inv, s);
     if (err != hipSuccess) return PF_E_LAUNCH;
-    if (use == PF_PATH_GEMM && leg == PF_LEG_F16 && !is_xq(qtype)) {
+    if (rms_fused(qtype, k, T, leg, use)) {
         a.norm_inv = inv;
         a.norm_w = norm_w;
         err = pf::launch_gemm_f16_ws(a, rest, s);
@@ -339,7 +350,7 @@ int pf_gemm_prepared(int qtype, const void *W_blocks, int64_t n, int64_t k, int6
     if (st != PF_OK) return st;
     if (ldy < n || (T > 0 && ldy > kMax31 / T)) return PF_E_SHAPE;
     // where pf_gemm_ws would run the GEMV (which reads f32 X) there is no prepared form
-    if (T > 0 && auto_path(qtype, T, epilogue, PF_LEG_F16) != PF_PATH_GEMM) return PF_E_PATH;
+    if (T > 0 && auto_path(qtype, k, T, epilogue, PF_LEG_F16) != PF_PATH_GEMM) return PF_E_PATH;
     if (T == 0) return PF_OK;
     if (!W_blocks || !Y) return PF_E_NULL;
     if (!aligned16(W_blocks) || !aligned16(Y)) return PF_E_ALIGN;
@@ -368,7 +379,7 @@ int64_t pf_rmsnorm_workspace_bytes(int qtype, int64_t n, int64_t k, int64_t T, i
     int64_t n_w = 0;
     const int st = check_sizes(qtype, n, k, T, epilogue, leg, &n_w);
     if (st != PF_OK) return -st;
-    return rms_ws_need(qtype, n, k, T, epilogue, leg, auto_path(qtype, T, epilogue, leg));
+    return rms_ws_need(qtype, n, k, T, epilogue, leg, auto_path(qtype, k, T, epilogue, leg));
 }
 
 int64_t pf_workspace_bytes(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int leg) {
@@ -376,7 +387,7 @@ int64_t pf_workspace_bytes(int qtype, int64_t n, int64_t k, int64_t T, int epilo
     const int st = check_sizes(qtype, n, k, T, epilogue, leg, &n_w);
     if (st != PF_OK) return -st;
     if (T == 0) return 0;
-    return ws_need(qtype, n, k, T, epilogue, leg, auto_path(qtype, T, epilogue, leg));
+    return ws_need(qtype, n, k, T, epilogue, leg, auto_path(qtype, k, T, epilogue, leg));
 }
 
 int pf_gemm_path(int qtype, const void *W_blocks, int64_t n, int64_t k, const float *X,
@@ -389,7 +400,7 @@ int pf_select_path(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int
     const int st = check_sizes(qtype, n, k, T, epilogue, leg, &n_w);
     if (st != PF_OK) return -st;
     if (T == 0) return 0;
-    return auto_path(qtype, T, epilogue, leg);
+    return auto_path(qtype, k, T, epilogue, leg);
 }
 
 int pf_dequant_f32(int qtype, const void *W_blocks, int64_t rows, int64_t k, float *out,

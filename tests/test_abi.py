@@ -89,12 +89,18 @@ def test_select_path(lib):
         assert sel(pf.PF_Q8_0, 4096, 4096, T, pf.PF_RESIDUAL, pf.PF_LEG_F16) == want
     for T in (9, 16, 512, 2048):
         assert sel(pf.PF_Q8_0, 4096, 12288, T, pf.PF_RESIDUAL, pf.PF_LEG_F16) == pf.PF_PATH_GEMM
-    # the further types: the GEMV up to 8 rows on both legs, then the GEMM
+    # the further types: the GEMV up to 8 rows, then the GEMM; on the f16 leg those the
+    # 4-wave GEMM takes (Q4_K, Q5_K, IQ4_XS, Q6_K with k % 512 == 0) cross over as Q4_0
     for qt in (pf.PF_F16, pf.PF_Q4_K, pf.PF_Q5_K, pf.PF_Q6_K, pf.PF_IQ4_XS):
-        for leg in (pf.PF_LEG_F32, pf.PF_LEG_F16):
-            for epi in (pf.PF_PLAIN, pf.PF_GATE_UP_SWIGLU):
-                assert sel(qt, 4096, 4096, 8, epi, leg) == pf.PF_PATH_GEMV
-                assert sel(qt, 4096, 4096, 9, epi, leg) == pf.PF_PATH_GEMM
+        for k in (4096, 4352):
+            f16_gemm = qt != pf.PF_F16 and (qt != pf.PF_Q6_K or k % 512 == 0)
+            for leg in (pf.PF_LEG_F32, pf.PF_LEG_F16):
+                for epi in (pf.PF_PLAIN, pf.PF_RESIDUAL, pf.PF_GATE_UP_SWIGLU):
+                    first = 5 if epi == pf.PF_GATE_UP_SWIGLU else 3
+                    for T in (1, 2, 3, 4, 5, 8, 9):
+                        early = leg == pf.PF_LEG_F16 and f16_gemm and T >= first
+                        want = pf.PF_PATH_GEMM if T > 8 or early else pf.PF_PATH_GEMV
+                        assert sel(qt, 4096, k, T, epi, leg) == want, (qt, k, leg, epi, T)
     assert sel(7, 1, 256, 1, 0, 0) == -pf.PF_E_QTYPE
     assert sel(-1, 1, 256, 1, 0, 0) == -pf.PF_E_QTYPE
     assert sel(0, 1, 256, 1, 3, 0) == -pf.PF_E_EPILOGUE
@@ -186,10 +192,10 @@ def test_workspace_bytes(lib):
     assert wb(pf.PF_Q4_0, 17, 1280, 290, pf.PF_RESIDUAL, pf.PF_LEG_F16) == 320 * 1280 * 2
     assert wb(pf.PF_Q4_0, 4096, 4096, 512, pf.PF_PLAIN, pf.PF_LEG_F32) == 0
     # the further types take no workspace on the f32 leg; on the f16 leg Q4_K, Q5_K,
-    # IQ4_XS and Q6_K (k % 512 == 0: rows a multiple of 4 bytes) from 9 rows (the 4-wave
-    # tiles below 256, or 512 for Q6_K; the cooperative kernel above), and F16 from 512,
-    # take Q4_0's GEMMs and their workspace layout (X, then the split count these types
-    # take).
+    # IQ4_XS and Q6_K (k % 512 == 0: rows a multiple of 4 bytes) wherever the GEMM runs
+    # (from 3 rows, 5 for SwiGLU; the 4-wave tiles below 256, or 512 for Q6_K; the
+    # cooperative kernel above), and F16 from 512, take Q4_0's GEMMs and their workspace
+    # layout (X, then the split count these types take).
     # Elsewhere on the f16 leg their own GEMM (64- or 128-row x 128-column tiles) splits K
     # through the workspace when the tiles leave the resident slots (3 per CU) idle:
     # 768 / tiles splits, each at least 512 k, at most 16, one [T][rows] f32 block each;
@@ -205,7 +211,7 @@ def test_workspace_bytes(lib):
         for T in (1, 8, 9, 300, 511, 512, 2048):
             for epi in (pf.PF_PLAIN, pf.PF_RESIDUAL, pf.PF_GATE_UP_SWIGLU):
                 kq = qt in (pf.PF_Q4_K, pf.PF_Q5_K, pf.PF_IQ4_XS, pf.PF_Q6_K)
-                coop = T >= 512 or (kq and T >= 9)
+                coop = T >= 512 or (kq and T >= (5 if epi == pf.PF_GATE_UP_SWIGLU else 3))
                 sp = own_splits(T, 4096, 4096, epi)
                 rows = 8192 if epi == pf.PF_GATE_UP_SWIGLU else 4096
                 want = wb(pf.PF_Q4_0, 4096, 4096, T, epi, pf.PF_LEG_F16) if coop else \

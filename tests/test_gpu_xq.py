@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import oracle
-from quantized_weight_prefill_gguf_amd import synth
+from quantized_weight_prefill_gguf_amd import PF_PATH_GEMM as PATH_GEMM, PF_PATH_GEMV as PATH_GEMV, synth
 from tests import parity, xq_blocks
 
 pytestmark = pytest.mark.gpu
@@ -24,6 +24,15 @@ def _weights(qtype, rows, k, kind, leg, seed):
     if kind == "synth":
         return synth.quantize(qtype, synth.weights_f32(rows, k, workload_id=seed))
     return xq_blocks.weight(qtype, rows, k, seed, xq_blocks.TOP["f16" if leg == F16 else "f32"][qtype])
+
+
+def _auto_path(qtype, k, T, epi, leg):
+    """The family PF_PATH_AUTO picks: the GEMV up to 8 rows, except that on the f16 leg
+    the types Q4_0's 4-wave GEMM takes (Q4_K, Q5_K, IQ4_XS, Q6_K with k % 512 == 0) take
+    the GEMM from 3 rows (5 with SwiGLU)."""
+    f16_gemm = leg == F16 and qtype != synth.F16 and (qtype != synth.Q6_K or k % 512 == 0)
+    early = f16_gemm and T >= (5 if epi == SWIGLU else 3)
+    return PATH_GEMM if T > 8 or early else PATH_GEMV
 
 
 @pytest.mark.parametrize("kind", ["synth", "edge"])
@@ -56,8 +65,7 @@ def test_xq_gemm_every_output(gpu, qtype, kind, T, epi, leg):
     W = _weights(qtype, rows, k, kind, leg, seed)
     X = synth.activations(T, k, workload_id=seed)
     R = synth.activations(T, n, workload_id=seed, tensor_id=synth.TENSOR_R) if epi == RESIDUAL else None
-    want_path = gpu.PF_PATH_GEMV if T <= 8 else gpu.PF_PATH_GEMM
-    assert gpu.select_path(qtype, n, k, T, epi, leg) == want_path
+    assert gpu.select_path(qtype, n, k, T, epi, leg) == _auto_path(qtype, k, T, epi, leg)
     print("case xq %s %s T=%d epi=%d leg=%d" % (NAMES[qtype], kind, T, epi, leg), flush=True)
     Y = parity.run_gpu(gpu, qtype, W, n, k, X, epi, leg, R=R)
     ok, err = parity.check(qtype, W, n, k, X, Y, epi, leg, R=R)
@@ -84,8 +92,10 @@ def test_xq_gemm_shortest_k(gpu, qtype, epi, leg):
 
 @pytest.mark.parametrize("qtype", XQ, ids=lambda q: NAMES[q])
 def test_xq_forced_families_and_noalloc(gpu, qtype):
-    """For T <= 8 the forced GEMM meets the bar too; pf_gemm_ws and pf_gemm_noalloc
-    need no workspace for these types and give pf_gemm's bits."""
+    """For T <= 8 both forced families meet the bar. Where the GEMV runs, pf_gemm_ws and
+    pf_gemm_noalloc need no workspace and give pf_gemm's bits; where the f16 leg takes the
+    GEMM (SwiGLU at 5 rows for the types the 4-wave GEMM takes) pf_gemm_ws splits through
+    its workspace and pf_gemm_noalloc gives its bits."""
     import torch
     n, k = 96, 1024
     for T, epi, leg in [(5, SWIGLU, F16), (7, RESIDUAL, F32), (2, PLAIN, F16)]:
@@ -97,15 +107,20 @@ def test_xq_forced_families_and_noalloc(gpu, qtype):
             Y = parity.run_gpu(gpu, qtype, W, n, k, X, epi, leg, R=R, path=path)
             ok, err = parity.check(qtype, W, n, k, X, Y, epi, leg, R=R)
             assert ok, (path, err)
-        assert gpu.workspace_bytes(qtype, n, k, T, epi, leg) == 0
+        gemm = _auto_path(qtype, k, T, epi, leg) == PATH_GEMM
+        assert (gpu.workspace_bytes(qtype, n, k, T, epi, leg) > 0) == gemm
         y0 = parity.run_gpu(gpu, qtype, W, n, k, X, epi, leg, R=R)
         y1 = parity.run_gpu(gpu, qtype, W, n, k, X, epi, leg, R=R, workspace=True)
         Wd, Xd = parity.to_dev(W), parity.to_dev(X)
         Yd = parity.to_dev(R) if R is not None else torch.full((T, n), float("nan"), device="cuda")
         gpu.gemm_noalloc(qtype, Wd, n, k, Xd, Yd, epi, leg)
         torch.cuda.synchronize()
-        assert np.array_equal(y0.view(np.uint32), y1.view(np.uint32))
-        assert np.array_equal(y0.view(np.uint32), Yd.cpu().numpy().view(np.uint32))
+        for y in (y0, y1):
+            ok, err = parity.check(qtype, W, n, k, X, y, epi, leg, R=R)
+            assert ok, err
+        if not gemm:
+            assert np.array_equal(y0.view(np.uint32), y1.view(np.uint32))
+        assert np.array_equal(y1.view(np.uint32), Yd.cpu().numpy().view(np.uint32))
 
 
 COOP = [synth.F16, synth.Q4_K, synth.Q5_K, synth.Q6_K, synth.IQ4_XS]
