@@ -370,6 +370,48 @@ def test_xq_strided_y_workspace(gpu, qtype, T, epi):
     check_gaps(host, left, n)
 
 
+@pytest.mark.parametrize("epi", [PLAIN, RESIDUAL, SWIGLU])
+@pytest.mark.parametrize("T", [40, 300])
+@pytest.mark.parametrize("qtype", KQ, ids=lambda q: NAMES[q])
+def test_xq_strided_y_no_workspace(gpu, qtype, T, epi):
+    """pf_gemm_ex without a workspace into a strided Y: the 4-wave GEMM unsplit, X rounded
+    inside each tile (short-chunk tiles at T = 40; at 300 the cost model's, Q6_K's row
+    tiles); the columns between Y's rows keep their bits."""
+    from tests.test_gpu_strided import check_gaps, run_strided
+    n, k = 200, 2048
+    rows = 2 * n if epi == SWIGLU else n
+    seed = 820 + 7 * qtype + 3 * epi + T
+    W = _weights(qtype, rows, k, "edge", F16, seed)
+    X = synth.activations(T, k, workload_id=seed)
+    R = synth.activations(T, n, workload_id=seed, tensor_id=synth.TENSOR_R) if epi == RESIDUAL else None
+    print("case xq strided no-ws %s T=%d epi=%d" % (NAMES[qtype], T, epi), flush=True)
+    Y, host, ldy, left = run_strided(gpu, qtype, W, n, k, X, epi, F16, R=R, pad_left=4, pad_right=3)
+    ok, err = parity.check(qtype, W, n, k, X, Y, epi, F16, R=R)
+    assert ok, "parity failed: metric %.3e" % err
+    check_gaps(host, left, n)
+
+
+def test_xq_noalloc_beyond_the_scratch(gpu):
+    """A K-quant call whose workspace exceeds pf_gemm_noalloc's static scratch (X alone
+    takes T * k * 2 bytes: 64 MiB here) runs the 4-wave GEMM without one, as pf_gemm does:
+    the same bits, and the bar on sampled outputs."""
+    import torch
+    qtype, n, k, T = synth.Q4_K, 160, 16384, 2100
+    assert gpu.workspace_bytes(qtype, n, k, T, RESIDUAL, F16) > gpu.PF_NOALLOC_SCRATCH_BYTES
+    W = _weights(qtype, n, k, "synth", F16, 830)
+    X = synth.activations(T, k, workload_id=830)
+    R = synth.activations(T, n, workload_id=830, tensor_id=synth.TENSOR_R)
+    print("case xq noalloc beyond the scratch", flush=True)
+    Wd, Xd = parity.to_dev(W), parity.to_dev(X)
+    Y = parity.run_gpu(gpu, qtype, W, n, k, X, RESIDUAL, F16, R=R, Wd=Wd, Xd=Xd)
+    Yd = parity.to_dev(R)
+    gpu.gemm_noalloc(qtype, Wd, n, k, Xd, Yd, RESIDUAL, F16)
+    torch.cuda.synchronize()
+    assert np.array_equal(Y.view(np.uint32), Yd.cpu().numpy().view(np.uint32))
+    ok, err = parity.check(qtype, W, n, k, X, Y, RESIDUAL, F16, R=R, samples=2048)
+    assert ok, "parity failed: metric %.3e" % err
+
+
 @pytest.mark.parametrize("qtype", COOP, ids=lambda q: NAMES[q])
 def test_xq_coop_full_size_sampled(gpu, qtype):
     """The gate/up shape at T = 512 through the workspace (sampled outputs)."""
