@@ -291,9 +291,14 @@ def test_xq_4wave_full_size_sampled(gpu, qtype, shape):
     assert ok, "parity failed: metric %.3e" % err
 
 
+# the types that keep their own GEMM on the f16 leg with a workspace below 512 rows: F16,
+# and Q6_K rows of an odd number of super-blocks
+OWN = [synth.F16, synth.Q6_K]
+
+
 @pytest.mark.parametrize("T", [9, 130, 300])
 @pytest.mark.parametrize("epi", [PLAIN, RESIDUAL])
-@pytest.mark.parametrize("qtype", XQ, ids=lambda q: NAMES[q])
+@pytest.mark.parametrize("qtype", OWN, ids=lambda q: NAMES[q])
 def test_xq_own_gemm_k_split(gpu, qtype, epi, T):
     """Where Q4_0's f16 GEMMs do not take them (F16 below 512 rows, Q6_K rows of an odd
     number of super-blocks), the further types' own GEMM splits PLAIN / RESIDUAL K through
@@ -302,8 +307,6 @@ def test_xq_own_gemm_k_split(gpu, qtype, epi, T):
     R and the splits in order. pf_gemm_noalloc runs the same kernels: same bits."""
     import torch
     n, k = 150, 4352 if qtype == synth.Q6_K else 4096
-    if qtype in KQ and qtype != synth.Q6_K:
-        pytest.skip("Q4_0's f16 GEMMs take this type")
     seed = 700 + 7 * qtype + 3 * epi + T
     W = _weights(qtype, n, k, "edge", F16, seed)
     X = synth.activations(T, k, workload_id=seed)
@@ -321,7 +324,7 @@ def test_xq_own_gemm_k_split(gpu, qtype, epi, T):
 
 
 @pytest.mark.parametrize("T", [9, 64])
-@pytest.mark.parametrize("qtype", XQ, ids=lambda q: NAMES[q])
+@pytest.mark.parametrize("qtype", OWN, ids=lambda q: NAMES[q])
 def test_xq_own_gemm_swiglu_scratch(gpu, qtype, T):
     """SwiGLU on the f16 leg with a workspace up to 64 rows on the own GEMM (F16, and Q6_K
     with k = 4352; the others take Q4_0's short-chunk tiles there): the gate and up rows
@@ -329,8 +332,6 @@ def test_xq_own_gemm_swiglu_scratch(gpu, qtype, T):
     sums each half in split order. pf_gemm_noalloc runs the same kernels: same bits."""
     import torch
     n, k = 150, 4352 if qtype == synth.Q6_K else 4096
-    if qtype in KQ and qtype != synth.Q6_K:
-        pytest.skip("Q4_0's f16 GEMMs take this type")
     seed = 720 + 7 * qtype + T
     W = _weights(qtype, 2 * n, k, "edge", F16, seed)
     X = synth.activations(T, k, workload_id=seed)
