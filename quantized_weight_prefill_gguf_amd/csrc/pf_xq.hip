@@ -262,14 +262,34 @@ __global__ __launch_bounds__(256) void xq_dequant_kernel(const uint8_t *__restri
 // take 16-weight runs 64 apart; the R rows' raw bytes are all loaded before any is
 // decoded. R = 4 where that still leaves at least 8 waves per CU, else 1 (2 for
 // SwiGLU): memory latency wants the waves more than x wants the reuse.
-template <int QT, int EPI, int TT, int R>
-__global__ __launch_bounds__(256) void xq_gemv_kernel(const uint8_t *__restrict__ W,
-                                                      const float *__restrict__ X, float *__restrict__ Y,
-                                                      int n, int ldy, int k) {
+// XL: x staged once per workgroup of WV waves in LDS (dynamic, xtok float4 per token),
+// lane-transposed: float4 i of run `lane + 64 it` at (4 it + i) 64 + lane, so that a
+// wave's read of one i is 1 KB of consecutive bytes. Each run's 64 bytes of x per token
+// would otherwise come from L2 for every row: four times the weight bytes of Q6_K.
+template <int QT, int EPI, int TT, int R, bool XL = false, int WV = 4>
+__global__ __launch_bounds__(64 * WV) void xq_gemv_kernel(const uint8_t *__restrict__ W,
+                                                          const float *__restrict__ X, float *__restrict__ Y,
+                                                          int n, int ldy, int k, int xtok) {
     using TR = XqTraits<QT>;
     constexpr int OUTW = EPI == EPI_SWIGLU ? R / 2 : R;
     const int lane = threadIdx.x & 63;
-    const int g = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int g = blockIdx.x * WV + (threadIdx.x >> 6);
+    extern __shared__ __attribute__((aligned(16))) uint8_t xsm[];
+    f4_t *xs = reinterpret_cast<f4_t *>(xsm);
+    if constexpr (XL) {
+        // every thread of the workgroup stages, before any wave leaves
+        const int q4 = k / 4;
+        for (int j = threadIdx.x; j < TT * q4; j += 64 * WV) {
+            const int t = j / q4, jj = j - t * q4;
+            const int run = jj >> 2, it = run >> 6;
+            xs[t * xtok + (4 * it + (jj & 3)) * 64 + (run & 63)] =
+                *reinterpret_cast<const f4_t *>(X + (size_t)t * k + 4 * jj);
+        }
+        __syncthreads();
+    } else {
+        (void)xs;
+        (void)xtok;
+    }
     if (g * OUTW >= n) return;  // whole waves leave
     const size_t row_bytes = (size_t)(k / TR::ELEMS) * TR::BYTES;
     const uint8_t *rows[R];
@@ -287,7 +307,7 @@ __global__ __launch_bounds__(256) void xq_gemv_kernel(const uint8_t *__restrict_
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int t = 0; t < TT; ++t) acc[r][t] = 0.f;
-    for (int e = 16 * lane; e < k; e += 16 * 64) {
+    for (int e = 16 * lane, it = 0; e < k; e += 16 * 64, ++it) {
         Raw16<QT> raw[R];
         const size_t boff = (size_t)(e / TR::ELEMS) * TR::BYTES;
 #pragma unroll
@@ -295,9 +315,14 @@ __global__ __launch_bounds__(256) void xq_gemv_kernel(const uint8_t *__restrict_
         f4_t xv[TT][4];
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
-            const f4_t *xp = reinterpret_cast<const f4_t *>(X + (size_t)t * k + e);
+            if constexpr (XL) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xv[t][i] = xp[i];
+                for (int i = 0; i < 4; ++i) xv[t][i] = xs[t * xtok + (4 * it + i) * 64 + lane];
+            } else {
+                const f4_t *xp = reinterpret_cast<const f4_t *>(X + (size_t)t * k + e);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xv[t][i] = xp[i];
+            }
         }
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -538,19 +563,43 @@ __global__ __launch_bounds__(256) void xq_gemm_kernel(const uint8_t *__restrict_
     }
 }
 
+// x staged in LDS (xq_gemv_kernel's XL) for the one-row waves (n < 8192) where a
+// launch's tokens take at most 64 KB of it, eight waves sharing it: 4096 x 12288 at T = 1
+// Q4_K 17.1 -> 13.0 us, Q5_K 20.0 -> 14.2, Q6_K 22.8 -> 17.3. The four-row waves of the
+// wider weights already share x among their rows, and workgroups of eight such waves
+// (384 for 12288 rows) leave the CUs unevenly loaded: Q4_K 12288 x 4096 at T = 1 10.5
+// -> 17.7 us with it.
+constexpr int XQ_GEMV_XL_BYTES = 64 * 1024;
+constexpr int XQ_GEMV_XL_WV = 8;  // waves per workgroup sharing the staged x
+
+template <int QT, int EPI, int R, int TT>
+void launch_gemv_tt(const GemmArgs &a, const float *x, float *y, hipStream_t s) {
+    constexpr int OUTW = EPI == EPI_SWIGLU ? R / 2 : R;  // outputs per wave
+    // x per token in LDS: the transposed layout fills whole 1024-k rounds
+    const int xtok = (a.k + 1023) / 1024 * 256;  // float4
+    const int xl_bytes = TT * xtok * 16;
+    if (R <= 2 && xl_bytes <= XQ_GEMV_XL_BYTES) {
+        constexpr int WV = XQ_GEMV_XL_WV;
+        const dim3 grid((a.n + WV * OUTW - 1) / (WV * OUTW));
+        hipLaunchKernelGGL((xq_gemv_kernel<QT, EPI, TT, R, true, WV>), grid, dim3(64 * WV), xl_bytes, s, a.W, x, y,
+                           a.n, a.ldy, a.k, xtok);
+    } else {
+        const dim3 grid((a.n + 4 * OUTW - 1) / (4 * OUTW));
+        hipLaunchKernelGGL((xq_gemv_kernel<QT, EPI, TT, R>), grid, dim3(256), 0, s, a.W, x, y, a.n, a.ldy, a.k, 0);
+    }
+}
+
 template <int QT, int EPI, int R>
 hipError_t launch_gemv_r(const GemmArgs &a, hipStream_t s) {
-    constexpr int OUTW = EPI == EPI_SWIGLU ? R / 2 : R;  // outputs per wave
-    const dim3 grid((a.n + 4 * OUTW - 1) / (4 * OUTW));
     for (int t0 = 0; t0 < a.T; t0 += 4) {
         const int tt = min(4, a.T - t0);
         const float *x = a.X + (size_t)t0 * a.k;
         float *y = a.Y + (size_t)t0 * a.ldy;
         switch (tt) {
-        case 1: hipLaunchKernelGGL((xq_gemv_kernel<QT, EPI, 1, R>), grid, dim3(256), 0, s, a.W, x, y, a.n, a.ldy, a.k); break;
-        case 2: hipLaunchKernelGGL((xq_gemv_kernel<QT, EPI, 2, R>), grid, dim3(256), 0, s, a.W, x, y, a.n, a.ldy, a.k); break;
-        case 3: hipLaunchKernelGGL((xq_gemv_kernel<QT, EPI, 3, R>), grid, dim3(256), 0, s, a.W, x, y, a.n, a.ldy, a.k); break;
-        default: hipLaunchKernelGGL((xq_gemv_kernel<QT, EPI, 4, R>), grid, dim3(256), 0, s, a.W, x, y, a.n, a.ldy, a.k); break;
+        case 1: launch_gemv_tt<QT, EPI, R, 1>(a, x, y, s); break;
+        case 2: launch_gemv_tt<QT, EPI, R, 2>(a, x, y, s); break;
+        case 3: launch_gemv_tt<QT, EPI, R, 3>(a, x, y, s); break;
+        default: launch_gemv_tt<QT, EPI, R, 4>(a, x, y, s); break;
         }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
