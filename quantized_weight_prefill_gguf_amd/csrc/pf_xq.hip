@@ -571,18 +571,28 @@ __global__ __launch_bounds__(256) void xq_gemm_kernel(const uint8_t *__restrict_
 // -> 17.7 us with it.
 constexpr int XQ_GEMV_XL_BYTES = 64 * 1024;
 constexpr int XQ_GEMV_XL_WV = 8;  // waves per workgroup sharing the staged x
+// Up to 128 KB of x (two tokens at k = 12288) sixteen waves share it, one workgroup per
+// CU; the launch's tokens are chunked so that x fits.
+constexpr int XQ_GEMV_XL_MAX = 128 * 1024;
+
+// x per token in LDS: the transposed layout fills whole 1024-k rounds (float4 units)
+inline int xq_gemv_xtok(int k) { return (k + 1023) / 1024 * 256; }
 
 template <int QT, int EPI, int R, int TT>
 void launch_gemv_tt(const GemmArgs &a, const float *x, float *y, hipStream_t s) {
     constexpr int OUTW = EPI == EPI_SWIGLU ? R / 2 : R;  // outputs per wave
-    // x per token in LDS: the transposed layout fills whole 1024-k rounds
-    const int xtok = (a.k + 1023) / 1024 * 256;  // float4
+    const int xtok = xq_gemv_xtok(a.k);
     const int xl_bytes = TT * xtok * 16;
     if (R <= 2 && xl_bytes <= XQ_GEMV_XL_BYTES) {
         constexpr int WV = XQ_GEMV_XL_WV;
         const dim3 grid((a.n + WV * OUTW - 1) / (WV * OUTW));
         hipLaunchKernelGGL((xq_gemv_kernel<QT, EPI, TT, R, true, WV>), grid, dim3(64 * WV), xl_bytes, s, a.W, x, y,
                            a.n, a.ldy, a.k, xtok);
+    } else if (R <= 2 && TT <= 2 && xl_bytes <= XQ_GEMV_XL_MAX) {
+        constexpr int WV = 16;
+        const dim3 grid((a.n + WV * OUTW - 1) / (WV * OUTW));
+        hipLaunchKernelGGL((xq_gemv_kernel<QT, EPI, TT <= 2 ? TT : 2, R, true, WV>), grid, dim3(64 * WV), xl_bytes, s,
+                           a.W, x, y, a.n, a.ldy, a.k, xtok);
     } else {
         const dim3 grid((a.n + 4 * OUTW - 1) / (4 * OUTW));
         hipLaunchKernelGGL((xq_gemv_kernel<QT, EPI, TT, R>), grid, dim3(256), 0, s, a.W, x, y, a.n, a.ldy, a.k, 0);
@@ -591,8 +601,11 @@ void launch_gemv_tt(const GemmArgs &a, const float *x, float *y, hipStream_t s) 
 
 template <int QT, int EPI, int R>
 hipError_t launch_gemv_r(const GemmArgs &a, hipStream_t s) {
-    for (int t0 = 0; t0 < a.T; t0 += 4) {
-        const int tt = min(4, a.T - t0);
+    // tokens per launch: four, or fewer where that keeps one-row waves' x in LDS
+    const int xb = xq_gemv_xtok(a.k) * 16;
+    const int per = (R <= 2 && xb <= XQ_GEMV_XL_MAX) ? min(4, XQ_GEMV_XL_MAX / xb) : 4;
+    for (int t0 = 0; t0 < a.T; t0 += per) {
+        const int tt = min(per, a.T - t0);
         const float *x = a.X + (size_t)t0 * a.k;
         float *y = a.Y + (size_t)t0 * a.ldy;
         switch (tt) {

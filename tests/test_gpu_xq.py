@@ -72,6 +72,26 @@ def test_xq_gemm_every_output(gpu, qtype, kind, T, epi, leg):
     assert ok, "parity failed: metric %.3e" % err
 
 
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("epi", [PLAIN, RESIDUAL, SWIGLU])
+@pytest.mark.parametrize("qtype", XQ, ids=lambda q: NAMES[q])
+def test_xq_gemv_long_rows(gpu, qtype, epi, T):
+    """The GEMV (f32 leg) on rows of k = 12288 with one row per wave (n < 8192): x staged in
+    LDS, 48 KB a token, for two tokens per launch in sixteen-wave workgroups (T = 2, 3, 5
+    and 8 take chunks of two and a last one), every output."""
+    n, k = 300, 12288
+    rows = 2 * n if epi == SWIGLU else n
+    seed = 840 + 7 * qtype + 3 * epi + T
+    W = _weights(qtype, rows, k, "edge", F32, seed)
+    X = synth.activations(T, k, workload_id=seed)
+    R = synth.activations(T, n, workload_id=seed, tensor_id=synth.TENSOR_R) if epi == RESIDUAL else None
+    assert gpu.select_path(qtype, n, k, T, epi, F32) == gpu.PF_PATH_GEMV
+    print("case xq gemv long rows %s T=%d epi=%d" % (NAMES[qtype], T, epi), flush=True)
+    Y = parity.run_gpu(gpu, qtype, W, n, k, X, epi, F32, R=R)
+    ok, err = parity.check(qtype, W, n, k, X, Y, epi, F32, R=R)
+    assert ok, "parity failed: metric %.3e" % err
+
+
 @pytest.mark.parametrize("leg", [F32, F16])
 @pytest.mark.parametrize("epi", [PLAIN, SWIGLU])
 @pytest.mark.parametrize("qtype", XQ, ids=lambda q: NAMES[q])
