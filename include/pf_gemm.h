@@ -78,7 +78,8 @@ extern "C" {
  * workspace where its tiles leave CUs idle. Without a workspace (pf_gemm, and
  * pf_gemm_noalloc where the workspace exceeds the static scratch) Q4_K, Q5_K, IQ4_XS
  * and Q6_K (k % 512 == 0) run the 4-wave GEMM unsplit, F16 and the other Q6_K rows
- * their own GEMM unsplit. pf_prepare_x and pf_gemm_prepared take Q4_0 and Q8_0 only. */
+ * their own GEMM unsplit. pf_prepare_x and pf_gemm_prepared take Q4_0, Q8_0 and, where
+ * pf_gemm_ws runs them on those GEMMs, the further types (else PF_E_QTYPE). */
 enum { PF_Q4_0 = 0, PF_Q8_0 = 1, PF_F16 = 2, PF_Q4_K = 3, PF_Q5_K = 4, PF_Q6_K = 5, PF_IQ4_XS = 6 };
 
 /* Epilogues.

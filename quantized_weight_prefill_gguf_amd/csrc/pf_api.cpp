@@ -32,8 +32,9 @@ int block_bytes(int qtype) {
 }
 int block_elems(int qtype) { return (qtype >= PF_Q4_K && qtype <= PF_IQ4_XS) ? 256 : 32; }
 // The further types (F16, Q4_K, Q5_K, Q6_K, IQ4_XS) run their own kernels (pf_xq.hip), except
-// where the f16 leg's workspace GEMM decodes them (pf::f16_takes_xq); on the f16 leg
-// their own GEMM splits K through the workspace where its tiles leave CUs idle.
+// where the f16 leg's matrix-core GEMMs decode them (pf::f16_takes_xq with a workspace,
+// pf::f16_direct_takes_xq without); on the f16 leg their own GEMM splits K through the
+// workspace where its tiles leave CUs idle.
 bool is_xq(int qtype) { return qtype >= PF_F16 && qtype <= PF_IQ4_XS; }
 int64_t w_bytes_of(int qtype, int64_t rows, int64_t k) { return rows * (k / block_elems(qtype)) * block_bytes(qtype); }
 
@@ -120,8 +121,8 @@ int gemm_impl(int qtype, const void *W, int64_t n, int64_t k, const float *X, in
     if (overlap(Y, y_bytes, X, x_bytes) || overlap(Y, y_bytes, W, w_bytes)) return PF_E_ALIAS;
     const int use = path == PF_PATH_AUTO ? auto_path(qtype, k, T, epilogue, leg) : path;
     int64_t need = ws_mode != WS_NONE ? ws_need(qtype, n, k, T, epilogue, leg, use) : 0;
-    // A further type whose workspace would not fit the static scratch runs its own GEMM,
-    // which needs none (as it does without a workspace).
+    // A further type whose workspace would not fit the static scratch runs as it does
+    // without a workspace (the 4-wave GEMM unsplit, or its own GEMM), which needs none.
     if (ws_mode == WS_STATIC && is_xq(qtype) && need > pf::kNoallocScratchBytes) need = 0;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (need > 0 && ws_mode == WS_STATIC) {
@@ -167,9 +168,6 @@ int gemm_impl(int qtype, const void *W, int64_t n, int64_t k, const float *X, in
 
 int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
 
-// Workspace of the RMSNorm entry point: inv[T] (rounded up to 256 bytes), then the
-// f16 GEMM's own workspace (X rounded to binary16 with the norm applied, and any
-// split-K partial sums), or, for the kernels that read f32 X, Xn [T][k] f32.
 // Whether the RMSNorm entry point applies the norm inside the f16 leg GEMM's conversion
 // of X to binary16 (Q4_0, Q8_0 and the further types those GEMMs take), rather than
 // materialising Xn for a kernel that reads f32 X.
@@ -177,6 +175,9 @@ bool rms_fused(int qtype, int64_t k, int64_t T, int leg, int use) {
     return use == PF_PATH_GEMM && leg == PF_LEG_F16 && (!is_xq(qtype) || pf::f16_takes_xq(qtype, (int)T, (int)k));
 }
 
+// Workspace of the RMSNorm entry point: inv[T] (rounded up to 256 bytes), then the
+// f16 GEMM's own workspace (X rounded to binary16 with the norm applied, and any
+// split-K partial sums), or, for the kernels that read f32 X, Xn [T][k] f32.
 int64_t rms_ws_need(int qtype, int64_t n, int64_t k, int64_t T, int epilogue, int leg, int use) {
     if (T == 0) return 0;
     const int64_t tail = rms_fused(qtype, k, T, leg, use) ? pf::f16_ws_bytes(qtype, (int)T, (int)n, (int)k, epilogue)
@@ -319,8 +320,10 @@ int pf_lm_head_argmax(int qtype, const void *W_blocks, int64_t n, int64_t k, con
 
 int pf_prepare_x(int qtype, int64_t k, const float *X, int64_t T, void *workspace, int64_t workspace_bytes,
                  void *stream) {
-    if (block_bytes(qtype) < 0 || is_xq(qtype)) return PF_E_QTYPE;
+    if (block_bytes(qtype) < 0) return PF_E_QTYPE;
     if (T < 0 || k < 256 || k % 256 != 0 || (T > 0 && k > kMax31 / T)) return PF_E_SHAPE;
+    // the further types have a prepared form where the f16 GEMMs take them
+    if (is_xq(qtype) && T > 0 && !pf::f16_takes_xq(qtype, (int)T, (int)k)) return PF_E_QTYPE;
     if (T == 0) return PF_OK;
     if (!X) return PF_E_NULL;
     if (!aligned16(X)) return PF_E_ALIGN;
@@ -345,9 +348,11 @@ int pf_prepare_x(int qtype, int64_t k, const float *X, int64_t T, void *workspac
 int pf_gemm_prepared(int qtype, const void *W_blocks, int64_t n, int64_t k, int64_t T, float *Y, int64_t ldy,
                      int epilogue, void *workspace, int64_t workspace_bytes, void *stream) {
     int64_t n_w = 0;
-    if (is_xq(qtype)) return PF_E_QTYPE;  // their GEMM reads f32 X: no prepared form
     const int st = check_sizes(qtype, n, k, T, epilogue, PF_LEG_F16, &n_w);
     if (st != PF_OK) return st;
+    // the further types' own GEMM reads f32 X: a prepared form only where the f16 GEMMs
+    // take them
+    if (is_xq(qtype) && T > 0 && !pf::f16_takes_xq(qtype, (int)T, (int)k)) return PF_E_QTYPE;
     if (ldy < n || (T > 0 && ldy > kMax31 / T)) return PF_E_SHAPE;
     // where pf_gemm_ws would run the GEMV (which reads f32 X) there is no prepared form
     if (T > 0 && auto_path(qtype, k, T, epilogue, PF_LEG_F16) != PF_PATH_GEMM) return PF_E_PATH;

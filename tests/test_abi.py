@@ -402,9 +402,14 @@ def test_prepared_argument_checks(lib):
     px = lambda **kw: lib.pf_prepare_x(kw.get("qtype", 0), kw.get("k", k), P(kw.get("X", X)), kw.get("T", T),
                                        P(kw.get("ws", WS)), kw.get("wsb", xneed), None)
     assert px(qtype=7) == pf.PF_E_QTYPE
-    # the further types' GEMM reads f32 X: no prepared form
-    for qt in (pf.PF_F16, pf.PF_Q4_K, pf.PF_Q5_K, pf.PF_Q6_K, pf.PF_IQ4_XS):
-        assert px(qtype=qt) == pf.PF_E_QTYPE
+    # the further types have a prepared form where the f16 GEMMs take them (their own
+    # GEMM reads f32 X): Q4_K, Q5_K, IQ4_XS, Q6_K with k % 512 == 0, F16 from 512 rows
+    for qt in (pf.PF_Q4_K, pf.PF_Q5_K, pf.PF_Q6_K, pf.PF_IQ4_XS):
+        assert px(qtype=qt, k=512, X=0) == pf.PF_E_NULL  # past the type check
+    assert px(qtype=pf.PF_Q6_K, k=768) == pf.PF_E_QTYPE  # rows of an odd number of super-blocks
+    assert px(qtype=pf.PF_F16) == pf.PF_E_QTYPE  # F16 below 512 rows
+    assert px(qtype=pf.PF_F16, T=512, X=0) == pf.PF_E_NULL
+    assert px(qtype=pf.PF_F16, T=0) == pf.PF_OK
     assert px(k=300) == pf.PF_E_SHAPE
     assert px(T=0) == pf.PF_OK
     assert px(X=0) == pf.PF_E_NULL
@@ -415,6 +420,9 @@ def test_prepared_argument_checks(lib):
     gp = lambda **kw: lib.pf_gemm_prepared(kw.get("qtype", 0), P(kw.get("W", W)), kw.get("n", n), k,
                                            kw.get("T", T), P(kw.get("Y", Y)), kw.get("ldy", n), kw.get("epi", 0),
                                            P(kw.get("ws", WS)), kw.get("wsb", need), None)
+    for qt in (pf.PF_Q4_K, pf.PF_Q5_K, pf.PF_IQ4_XS):
+        assert gp(qtype=qt, W=0) == pf.PF_E_NULL  # past the type check
+    assert gp(qtype=pf.PF_F16) == pf.PF_E_QTYPE
     # where pf_gemm_ws runs the GEMV (which reads f32 X) there is no prepared GEMM
     assert gp(T=2) == pf.PF_E_PATH
     assert gp(T=4, epi=pf.PF_GATE_UP_SWIGLU) == pf.PF_E_PATH

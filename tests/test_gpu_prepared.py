@@ -49,6 +49,35 @@ def check(qtype, Wd, n, k, X, Y, Y0, epi, R=None):
     assert np.array_equal(Y.view(np.uint32), Y0.view(np.uint32))
 
 
+# F16 below 512 rows keeps its own GEMM, which has no prepared form
+FURTHER = [(q, T, n) for q in (synth.Q4_K, synth.Q5_K, synth.IQ4_XS, synth.Q6_K, synth.F16)
+           for T, n in ((40, 200), (300, 200), (520, 150)) if q != synth.F16 or T >= 512]
+
+
+@pytest.mark.parametrize("epi", [PLAIN, RESIDUAL, SWIGLU])
+@pytest.mark.parametrize("qtype,T,n", FURTHER)
+def test_prepared_equals_ws_further_types(gpu, qtype, T, n, epi):
+    """The further types where pf_gemm_ws runs them on the f16 GEMMs (the 4-wave kernel at
+    40 rows, and at 300 for Q6_K; the cooperative kernel from 256 or 512 rows; F16 from
+    512): the prepared form gives pf_gemm_ws's bits."""
+    import torch
+    k = 1024
+    wid = 630 + T + epi + 7 * qtype
+    rows = 2 * n if epi == SWIGLU else n
+    W = parity.to_dev(synth.quantize(qtype, synth.weights_f32(rows, k, workload_id=wid)))
+    X = acts(T, k, wid)
+    R = acts(T, n, wid, synth.TENSOR_R) if epi == RESIDUAL else None
+    print("case prepared further qtype=%d n=%d T=%d epi=%d" % (qtype, n, T, epi), flush=True)
+    Y0 = parity.run_gpu(gpu, qtype, None, n, k, X, epi, F16, R=R, Wd=W, workspace=True)
+    ws = ws_for(gpu, qtype, n, k, T, epi)
+    Y = torch.from_numpy(R.copy()).cuda() if R is not None else \
+        torch.full((T, n), float("nan"), dtype=torch.float32, device="cuda")
+    gpu.prepare_x(qtype, k, parity.to_dev(X), ws)
+    gpu.gemm_prepared(qtype, W, n, k, T, Y, epi, ws)
+    torch.cuda.synchronize()
+    check(qtype, W, n, k, X, Y.cpu().numpy(), Y0, epi, R)
+
+
 @pytest.mark.parametrize("qtype", [Q4_0, Q8_0])
 @pytest.mark.parametrize("T", [64, 512])
 def test_one_copy_many_projections(gpu, qtype, T):
