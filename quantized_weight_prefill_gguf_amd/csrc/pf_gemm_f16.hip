@@ -1486,9 +1486,9 @@ TileChoice choose_tiles(const GemmArgs &a, bool allow_split) {
         // split count minimises rounds of workgroups x (chunks per workgroup + one
         // chunk's worth of fixed cost). SwiGLU cannot split: its epilogue is not
         // linear in the partial sums. Q6_K keeps these tiles (several of 128 rows)
-        // up to 511 rows: its decode is the heaviest, and the cost model's tiles
-        // decode each column in two waves (gate/up 2 x 12288 x 4096 at T = 300: 220 us
-        // against 303 on 128 x 128; Q4_K there: 108 against 86 at T = 200).
+        // above 128 rows: its decode is the heaviest, and the cost model's tiles
+        // decode each column in two waves (gate/up 2 x 12288 x 4096 at T = 200: 149 us
+        // against 203 on 128 x 128; Q4_K there: 108 against 86).
         const int mt = a.T <= 32 ? 32 : a.T <= 64 ? 64 : 128;
         const int cfg = mt == 32 ? 4 : mt == 64 ? 5 : 6;
         const int tn = (a.n + 127) / 128 * ((a.T + mt - 1) / mt);
@@ -1763,9 +1763,8 @@ constexpr int COOP_T512 = PF_COOP_T512;  // smallest T that takes the 512 x 96 t
 // least 5 chunks per split (3 splits), 34.0 with 4 (4 splits), 45.1 with 8; the
 // Q8_0 down projection (k = 12288, 5 splits under any of these) does not change.
 // SwiGLU never splits.
-static int coop_splits(int T, int n, int k, int epilogue) {
+static int coop_splits(int MT, int T, int n, int k, int epilogue) {
     if (epilogue == EPI_SWIGLU) return 1;
-    const int MT = T >= COOP_T512 ? 512 : 256;
     const int NW = MT == 256 ? 192 : 96;
     const int tiles = ((T + MT - 1) / MT) * ((n + NW - 1) / NW);
     if (tiles >= 256) return 1;
@@ -1779,13 +1778,22 @@ static int coop_splits(int T, int n, int k, int epilogue) {
 
 // The further types this file's GEMMs take on the workspace path: Q4_K, Q5_K and
 // IQ4_XS at every T (the 4-wave kernel below 256 rows, the cooperative kernel from
-// 256); Q6_K with k % 512 == 0 at every T (the 4-wave kernel below COOP_T512); F16
-// from COOP_T512 (its staging on the other tiles would need more than one piece per
-// thread).
+// 256); Q6_K with k % 512 == 0 at every T (the 4-wave kernel up to SHORT_T rows); F16
+// above SHORT_T rows. The cooperative kernel takes Q6_K and F16 on its 512-row tile
+// only (their 256 x 192 tile's staging would need more than one piece per thread),
+// part empty below 512 rows, yet faster there than two or more of the 4-wave kernel's
+// row tiles for Q6_K, or F16's own GEMM (gate/up 2 x 12288 x 4096 at T = 300: Q6_K
+// 220 -> 104 us, F16 164 -> 93; at T = 200 the 4-wave kernel took 150 us for Q6_K).
 bool f16_takes_xq(int qtype, int T, int k) {
     if (qtype == XQ_Q4_K || qtype == XQ_Q5_K || qtype == XQ_IQ4_XS) return true;
     if (qtype == XQ_Q6_K) return k % 512 == 0;
-    return qtype == XQ_F16 && T >= COOP_T512;
+    return qtype == XQ_F16 && T > SHORT_T;
+}
+
+// Rows of the cooperative kernel's tile for (qtype, T): 512 from COOP_T512, and for Q6_K
+// and F16 (which have no 256-row tile); else 256.
+static int coop_mt(int qtype, int T) {
+    return (T >= COOP_T512 || qtype == XQ_Q6_K || qtype == XQ_F16) ? 512 : 256;
 }
 
 // The further types the f16 GEMM without a workspace (the 4-wave kernel, X rounded in
@@ -1794,10 +1802,11 @@ bool f16_direct_takes_xq(int qtype, int k) {
     return qtype == XQ_Q4_K || qtype == XQ_Q5_K || qtype == XQ_IQ4_XS || (qtype == XQ_Q6_K && k % 512 == 0);
 }
 
-// Which f16 GEMM runs: the 4-wave kernel (X copied as [T][k]) below 256 rows, and for
-// Q6_K below COOP_T512 (it has no 256 x 192 cooperative tile); else the cooperative
-// kernel (X in A-fragment order).
-static bool f16_four_wave(int qtype, int T) { return T < 256 || (qtype == XQ_Q6_K && T < COOP_T512); }
+// Which f16 GEMM runs: the 4-wave kernel (X copied as [T][k]) below 256 rows (Q6_K and
+// F16: up to SHORT_T), else the cooperative kernel (X in A-fragment order).
+static bool f16_four_wave(int qtype, int T) {
+    return (qtype == XQ_Q6_K || qtype == XQ_F16) ? T <= SHORT_T : T < 256;
+}
 
 // Byte offset of the partial sums in the workspace, and the floats between splits.
 static int64_t ws_x_bytes(int T, int k) { return ((int64_t)(T + 31) / 32 * 32 * k * 2 + 255) / 256 * 256; }
@@ -1821,7 +1830,7 @@ int64_t f16_ws_bytes(int qtype, int T, int n, int k, int epilogue) {
         const int splits = small_t_splits(qtype, T, n, k, epilogue);
         return splits > 1 ? ws_x_bytes(T, k) + (int64_t)splits * ws_pstride(T, n) * 4 : xb;
     }
-    const int splits = coop_splits(T, n, k, epilogue);
+    const int splits = coop_splits(coop_mt(qtype, T), T, n, k, epilogue);
     return splits > 1 ? ws_x_bytes(T, k) + (int64_t)splits * ws_pstride(T, n) * 4 : xb;
 }
 
@@ -1835,7 +1844,7 @@ hipError_t launch_coop(const GemmArgs &a, uint16_t *xh, hipStream_t s) {
     const int tm = (a.T + MT - 1) / MT;
     const int out_per_tile = EPI == EPI_SWIGLU ? NW / 2 : NW;
     const int tn = (a.n + out_per_tile - 1) / out_per_tile;
-    const int splits = coop_splits(a.T, a.n, a.k, EPI);
+    const int splits = coop_splits(MT, a.T, a.n, a.k, EPI);
     const int total = tm * tn * splits;
     if (splits > 1) {
         if constexpr (EPI != EPI_SWIGLU) {

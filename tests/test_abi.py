@@ -193,9 +193,9 @@ def test_workspace_bytes(lib):
     assert wb(pf.PF_Q4_0, 4096, 4096, 512, pf.PF_PLAIN, pf.PF_LEG_F32) == 0
     # the further types take no workspace on the f32 leg; on the f16 leg Q4_K, Q5_K,
     # IQ4_XS and Q6_K (k % 512 == 0: rows a multiple of 4 bytes) wherever the GEMM runs
-    # (from 3 rows, 5 for SwiGLU; the 4-wave tiles below 256, or 512 for Q6_K; the
-    # cooperative kernel above), and F16 from 512, take Q4_0's GEMMs and their workspace
-    # layout (X, then the split count these types take).
+    # (from 3 rows, 5 for SwiGLU; the 4-wave tiles below 256, or up to 128 for Q6_K;
+    # the cooperative kernel above), and F16 above 128 rows, take Q4_0's GEMMs and their
+    # workspace layout (X, then the split count these types take).
     # Elsewhere on the f16 leg their own GEMM (64- or 128-row x 128-column tiles) splits K
     # through the workspace when the tiles leave the resident slots (3 per CU) idle:
     # 768 / tiles splits, each at least 512 k, at most 16, one [T][rows] f32 block each;
@@ -211,13 +211,13 @@ def test_workspace_bytes(lib):
         for T in (1, 8, 9, 300, 511, 512, 2048):
             for epi in (pf.PF_PLAIN, pf.PF_RESIDUAL, pf.PF_GATE_UP_SWIGLU):
                 kq = qt in (pf.PF_Q4_K, pf.PF_Q5_K, pf.PF_IQ4_XS, pf.PF_Q6_K)
-                coop = T >= 512 or (kq and T >= (5 if epi == pf.PF_GATE_UP_SWIGLU else 3))
+                coop = T > 128 if qt == pf.PF_F16 else (T >= 512 or (kq and T >= (5 if epi == pf.PF_GATE_UP_SWIGLU else 3)))
                 sp = own_splits(T, 4096, 4096, epi)
                 rows = 8192 if epi == pf.PF_GATE_UP_SWIGLU else 4096
                 want = wb(pf.PF_Q4_0, 4096, 4096, T, epi, pf.PF_LEG_F16) if coop else \
                     (sp * ((T * rows + 3) // 4 * 4) * 4 if sp > 1 else 0)
-                if qt == pf.PF_Q6_K and 256 <= T < 512:
-                    # Q6_K's 4-wave tiles where Q4_0 runs the cooperative kernel
+                if qt in (pf.PF_Q6_K, pf.PF_F16) and 256 <= T < 512:
+                    # the cooperative kernel's 512-row tile, where Q4_0 takes its 256 x 192
                     want = wb(qt, 4096, 4096, T, epi, pf.PF_LEG_F16)
                     assert want >= -(-T // 32) * 32 * 4096 * 2
                 assert wb(qt, 4096, 4096, T, epi, pf.PF_LEG_F16) == want
@@ -243,10 +243,10 @@ def test_workspace_bytes(lib):
         224 * 4096 * 2 + 4 * 200 * 12288 * 4
     assert wb(pf.PF_Q4_K, 12288, 4096, 200, pf.PF_PLAIN, pf.PF_LEG_F16) == \
         224 * 4096 * 2 + 8 * 200 * 12288 * 4
-    # Q6_K up to 511 rows keeps the short-chunk tiles, several of 128 rows: 3 x 32 tiles at
-    # T = 300 over 256 slots (one workgroup per CU), 2 splits
-    assert wb(pf.PF_Q6_K, 4096, 4096, 300, pf.PF_PLAIN, pf.PF_LEG_F16) == \
-        320 * 4096 * 2 + 2 * 300 * 4096 * 4
+    # Q6_K and F16 above 128 rows take the cooperative kernel's 512-row tile: 43 tiles of
+    # 512 x 96 at T = 300, 4 splits (at least 4 chunks each)
+    for qt in (pf.PF_Q6_K, pf.PF_F16):
+        assert wb(qt, 4096, 4096, 300, pf.PF_PLAIN, pf.PF_LEG_F16) == 320 * 4096 * 2 + 4 * 300 * 4096 * 4
     # Q6_K rows of an odd number of super-blocks (2-byte aligned rows) keep its own GEMM
     # (512 rows, 4096 columns: 256 tiles, 3 splits)
     assert own_splits(512, 4096, 4352, pf.PF_PLAIN) == 3
@@ -403,12 +403,13 @@ def test_prepared_argument_checks(lib):
                                        P(kw.get("ws", WS)), kw.get("wsb", xneed), None)
     assert px(qtype=7) == pf.PF_E_QTYPE
     # the further types have a prepared form where the f16 GEMMs take them (their own
-    # GEMM reads f32 X): Q4_K, Q5_K, IQ4_XS, Q6_K with k % 512 == 0, F16 from 512 rows
+    # GEMM reads f32 X): Q4_K, Q5_K, IQ4_XS, Q6_K with k % 512 == 0, F16 above 128 rows
     for qt in (pf.PF_Q4_K, pf.PF_Q5_K, pf.PF_Q6_K, pf.PF_IQ4_XS):
         assert px(qtype=qt, k=512, X=0) == pf.PF_E_NULL  # past the type check
     assert px(qtype=pf.PF_Q6_K, k=768) == pf.PF_E_QTYPE  # rows of an odd number of super-blocks
-    assert px(qtype=pf.PF_F16) == pf.PF_E_QTYPE  # F16 below 512 rows
-    assert px(qtype=pf.PF_F16, T=512, X=0) == pf.PF_E_NULL
+    assert px(qtype=pf.PF_F16) == pf.PF_E_QTYPE  # F16 up to 128 rows
+    assert px(qtype=pf.PF_F16, T=128) == pf.PF_E_QTYPE
+    assert px(qtype=pf.PF_F16, T=129, X=0) == pf.PF_E_NULL
     assert px(qtype=pf.PF_F16, T=0) == pf.PF_OK
     assert px(k=300) == pf.PF_E_SHAPE
     assert px(T=0) == pf.PF_OK

@@ -49,17 +49,17 @@ def check(qtype, Wd, n, k, X, Y, Y0, epi, R=None):
     assert np.array_equal(Y.view(np.uint32), Y0.view(np.uint32))
 
 
-# F16 below 512 rows keeps its own GEMM, which has no prepared form
+# F16 up to 128 rows keeps its own GEMM, which has no prepared form
 FURTHER = [(q, T, n) for q in (synth.Q4_K, synth.Q5_K, synth.IQ4_XS, synth.Q6_K, synth.F16)
-           for T, n in ((40, 200), (300, 200), (520, 150)) if q != synth.F16 or T >= 512]
+           for T, n in ((40, 200), (300, 200), (520, 150)) if q != synth.F16 or T > 128]
 
 
 @pytest.mark.parametrize("epi", [PLAIN, RESIDUAL, SWIGLU])
 @pytest.mark.parametrize("qtype,T,n", FURTHER)
 def test_prepared_equals_ws_further_types(gpu, qtype, T, n, epi):
     """The further types where pf_gemm_ws runs them on the f16 GEMMs (the 4-wave kernel at
-    40 rows, and at 300 for Q6_K; the cooperative kernel from 256 or 512 rows; F16 from
-    512): the prepared form gives pf_gemm_ws's bits."""
+    40 rows; the cooperative kernel above, F16 only there): the prepared form gives
+    pf_gemm_ws's bits."""
     import torch
     k = 1024
     wid = 630 + T + epi + 7 * qtype

@@ -208,7 +208,8 @@ def test_xq_4wave_every_output(gpu, qtype, kind, T, epi):
     (Q6_K's odd chunks two bytes past a dword boundary): up
     to 128 rows its short-chunk tiles (32, 64 or 128 token rows x 128 weight rows, the
     four waves side by side), T = 9 .. 128 covering each tile height, full and ragged;
-    at 130 and 255 the cost model's 64 x 64 tiles. n = 150 leaves the last weight tile
+    at 130 and 255 the cost model's 64 x 64 tiles (Q6_K there takes the cooperative
+    kernel's 512-row tile). n = 150 leaves the last weight tile
     ragged; at k = 4096 PLAIN and RESIDUAL split K (partial sums, then their fixed-order
     sum), and SwiGLU up to 64 rows runs as a split PLAIN GEMM over the 2n rows into G.
     pf_gemm_noalloc runs the same kernels: same bits."""
@@ -241,7 +242,8 @@ def test_xq_4wave_every_output(gpu, qtype, kind, T, epi):
 def test_xq_4wave_wide_tiles(gpu, qtype, n, T, epi):
     """The cost model's larger tiles between 129 and 255 rows (k = 4096): 128 x 128 split 8
     ways (n = 2000), 256 x 128 split 8 ways (n = 4096), and 128 x 128 unsplit for SwiGLU
-    (the fused epilogue), on every output; Q6_K keeps two 128-row short-chunk tiles."""
+    (the fused epilogue), on every output; Q6_K there takes the cooperative kernel's
+    512-row tile."""
     k = 4096
     rows = 2 * n if epi == SWIGLU else n
     seed = 790 + 7 * qtype + T + epi
@@ -254,18 +256,20 @@ def test_xq_4wave_wide_tiles(gpu, qtype, n, T, epi):
     assert ok, "parity failed: metric %.3e" % err
 
 
-@pytest.mark.parametrize("n,T,epi", [(150, 300, PLAIN), (150, 300, SWIGLU), (2000, 511, RESIDUAL)])
-def test_xq_q6_k_4wave_below_512(gpu, n, T, epi):
-    """Q6_K from 256 to 511 rows stays on the 4-wave GEMM (128-row short-chunk tiles, three
-    or four of them; its cooperative kernel has only the 512-row tile): ragged tiles both
-    ways, every output."""
-    qtype, k = synth.Q6_K, 2048
+@pytest.mark.parametrize("n,T,epi", [(150, 129, PLAIN), (150, 200, RESIDUAL), (150, 256, PLAIN),
+                                     (150, 300, SWIGLU), (2000, 511, RESIDUAL)])
+@pytest.mark.parametrize("qtype", [synth.Q6_K, synth.F16], ids=lambda q: NAMES[q])
+def test_xq_coop_512_tile_below_512(gpu, qtype, n, T, epi):
+    """Q6_K and F16 from 129 to 511 rows take the cooperative kernel's 512-row tile (they
+    have no 256-row one), part empty: rows past T are never stored; ragged weight tiles,
+    every output."""
+    k = 2048
     rows = 2 * n if epi == SWIGLU else n
-    seed = 800 + T + epi
+    seed = 800 + T + epi + qtype
     W = _weights(qtype, rows, k, "edge", F16, seed)
     X = synth.activations(T, k, workload_id=seed)
     R = synth.activations(T, n, workload_id=seed, tensor_id=synth.TENSOR_R) if epi == RESIDUAL else None
-    print("case xq q6_k 4-wave n=%d T=%d epi=%d" % (n, T, epi), flush=True)
+    print("case xq %s coop 512 n=%d T=%d epi=%d" % (NAMES[qtype], n, T, epi), flush=True)
     Y = parity.run_gpu(gpu, qtype, W, n, k, X, epi, F16, R=R, workspace=True)
     ok, err = parity.check(qtype, W, n, k, X, Y, epi, F16, R=R)
     assert ok, "parity failed: metric %.3e" % err
@@ -311,16 +315,16 @@ def test_xq_4wave_full_size_sampled(gpu, qtype, shape):
     assert ok, "parity failed: metric %.3e" % err
 
 
-# the types that keep their own GEMM on the f16 leg with a workspace below 512 rows: F16,
+# the types that keep their own GEMM on the f16 leg with a workspace: F16 up to 128 rows,
 # and Q6_K rows of an odd number of super-blocks
 OWN = [synth.F16, synth.Q6_K]
 
 
-@pytest.mark.parametrize("T", [9, 130, 300])
+@pytest.mark.parametrize("qtype,T", [(synth.F16, 9), (synth.F16, 100), (synth.Q6_K, 9), (synth.Q6_K, 130),
+                                     (synth.Q6_K, 300)])
 @pytest.mark.parametrize("epi", [PLAIN, RESIDUAL])
-@pytest.mark.parametrize("qtype", OWN, ids=lambda q: NAMES[q])
 def test_xq_own_gemm_k_split(gpu, qtype, epi, T):
-    """Where Q4_0's f16 GEMMs do not take them (F16 below 512 rows, Q6_K rows of an odd
+    """Where Q4_0's f16 GEMMs do not take them (F16 up to 128 rows, Q6_K rows of an odd
     number of super-blocks), the further types' own GEMM splits PLAIN / RESIDUAL K through
     the workspace when its tiles leave CUs idle: n = 150 is two 128-column tiles, so k =
     4096 (Q6_K 4352) splits 8 ways (at least 512 k each; the cap), and the sum kernel adds
@@ -372,10 +376,9 @@ def test_xq_own_gemm_swiglu_scratch(gpu, qtype, T):
 @pytest.mark.parametrize("qtype", XQ, ids=lambda q: NAMES[q])
 def test_xq_strided_y_workspace(gpu, qtype, T, epi):
     """pf_gemm_ex with a workspace into a strided Y: F16's own GEMM split through the
-    workspace (T = 40, SwiGLU through G; T = 300, whose SwiGLU there takes no workspace),
-    the 4-wave GEMM (T = 40 for the others, T = 300 for Q6_K) and the cooperative kernel
-    (T = 300 for Q4_K, Q5_K and IQ4_XS; T = 520 for all); the columns between Y's rows keep
-    their bits."""
+    workspace (T = 40, SwiGLU through G), the 4-wave GEMM (T = 40 for the others) and the
+    cooperative kernel (T = 300: the 256 x 192 tile for Q4_K, Q5_K and IQ4_XS, the 512-row
+    one for Q6_K and F16; T = 520 for all); the columns between Y's rows keep their bits."""
     from tests.test_gpu_strided import check_gaps, run_strided
     n, k = 200, 2048
     rows = 2 * n if epi == SWIGLU else n
