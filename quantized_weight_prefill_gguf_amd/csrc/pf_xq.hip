@@ -307,6 +307,53 @@ __global__ __launch_bounds__(64 * WV) void xq_gemv_kernel(const uint8_t *__restr
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int t = 0; t < TT; ++t) acc[r][t] = 0.f;
+    if constexpr (QT == XQ_Q6_K && !XL) {
+        // Q6_K: sub-blocks c and c + 2 of a half take the low and high nibbles of the same
+        // ql bytes and other bits of the same qh bytes, so a lane takes weights l0 ..
+        // l0 + 15 of both (32 weights, x read from global memory as two runs): one set of
+        // ql, qh and d loads, and the two scale bytes, serves both.
+        for (int u = lane; u < k / 32; u += 64) {
+            const int j = u & 7;
+            const int ea = (u >> 3) * 256 + (j >> 2) * 128 + ((j >> 1) & 1) * 32 + (j & 1) * 16;
+            const size_t boff = (size_t)(ea / TR::ELEMS) * TR::BYTES;
+            const int e0a = ea % TR::ELEMS, e0b = e0a + 64;
+            Raw16<QT> ra[R];
+            uint32_t scb[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                load_raw16<QT>(rows[r] + boff, e0a, ra[r]);
+                const int sib = 192 + 8 * (e0b >> 7) + ((e0b & 31) >> 4) + 2 * ((e0b & 127) >> 5);
+                scb[r] = *reinterpret_cast<const uint16_t *>(rows[r] + boff + (sib & ~1));
+            }
+            f4_t xa[TT][4], xb[TT][4];
+#pragma unroll
+            for (int t = 0; t < TT; ++t) {
+                const f4_t *xp = reinterpret_cast<const f4_t *>(X + (size_t)t * k + ea);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    xa[t][i] = xp[i];
+                    xb[t][i] = xp[16 + i];
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    Raw16<QT> rr = ra[r];
+                    if (half) rr.sc = scb[r];
+                    float w[16];
+                    decode_raw16<QT>(rr, half ? e0b : e0a, w);
+#pragma unroll
+                    for (int t = 0; t < TT; ++t) {
+                        float a = acc[r][t];
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) a = fmaf(w[i], (half ? xb : xa)[t][i >> 2][i & 3], a);
+                        acc[r][t] = a;
+                    }
+                }
+            }
+        }
+    } else
     for (int e = 16 * lane, it = 0; e < k; e += 16 * 64, ++it) {
         Raw16<QT> raw[R];
         const size_t boff = (size_t)(e / TR::ELEMS) * TR::BYTES;

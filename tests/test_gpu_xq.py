@@ -92,6 +92,27 @@ def test_xq_gemv_long_rows(gpu, qtype, epi, T):
     assert ok, "parity failed: metric %.3e" % err
 
 
+@pytest.mark.parametrize("T", [1, 3, 8])
+@pytest.mark.parametrize("epi", [PLAIN, RESIDUAL, SWIGLU])
+@pytest.mark.parametrize("qtype", XQ, ids=lambda q: NAMES[q])
+def test_xq_gemv_four_row_waves(gpu, qtype, epi, T):
+    """The GEMV (f32 leg) where n >= 8192 gives each wave four weight rows (SwiGLU: two
+    outputs' gate and up rows), x read from global memory; Q6_K there takes 32 weights a
+    lane, sub-blocks c and c + 2 from one set of loads. n = 8200 leaves the last wave
+    ragged; k = 1280 is five super-blocks a row (Q6_K's rows 2-byte aligned). Every output."""
+    n, k = 8200, 1280
+    rows = 2 * n if epi == SWIGLU else n
+    seed = 860 + 7 * qtype + 3 * epi + T
+    W = _weights(qtype, rows, k, "edge", F32, seed)
+    X = synth.activations(T, k, workload_id=seed)
+    R = synth.activations(T, n, workload_id=seed, tensor_id=synth.TENSOR_R) if epi == RESIDUAL else None
+    assert gpu.select_path(qtype, n, k, T, epi, F32) == gpu.PF_PATH_GEMV
+    print("case xq gemv four-row %s T=%d epi=%d" % (NAMES[qtype], T, epi), flush=True)
+    Y = parity.run_gpu(gpu, qtype, W, n, k, X, epi, F32, R=R)
+    ok, err = parity.check(qtype, W, n, k, X, Y, epi, F32, R=R)
+    assert ok, "parity failed: metric %.3e" % err
+
+
 @pytest.mark.parametrize("leg", [F32, F16])
 @pytest.mark.parametrize("epi", [PLAIN, SWIGLU])
 @pytest.mark.parametrize("qtype", XQ, ids=lambda q: NAMES[q])
