@@ -281,9 +281,19 @@ __global__ __launch_bounds__(64 * WV) void xq_gemv_kernel(const uint8_t *__restr
         const int q4 = k / 4;
         for (int j = threadIdx.x; j < TT * q4; j += 64 * WV) {
             const int t = j / q4, jj = j - t * q4;
-            const int run = jj >> 2, it = run >> 6;
-            xs[t * xtok + (4 * it + (jj & 3)) * 64 + (run & 63)] =
-                *reinterpret_cast<const f4_t *>(X + (size_t)t * k + 4 * jj);
+            int slot;
+            if constexpr (QT == XQ_Q6_K) {
+                // the paired loop's order: unit u (32 weights: 16 at ea, 16 at ea + 64)
+                // reads float4 i of run `hi` (0: ea, 1: ea + 64) from slot
+                // ((u / 64 * 2 + hi) * 4 + i) * 64 + u % 64
+                const int w = (4 * jj) & 255;
+                const int u = (jj >> 6) * 8 + (w >> 7) * 4 + ((w >> 5) & 1) * 2 + ((w >> 4) & 1);
+                slot = (((u >> 6) * 2 + ((w >> 6) & 1)) * 4 + ((w >> 2) & 3)) * 64 + (u & 63);
+            } else {
+                const int run = jj >> 2, it = run >> 6;
+                slot = (4 * it + (jj & 3)) * 64 + (run & 63);
+            }
+            xs[t * xtok + slot] = *reinterpret_cast<const f4_t *>(X + (size_t)t * k + 4 * jj);
         }
         __syncthreads();
     } else {
@@ -307,12 +317,12 @@ __global__ __launch_bounds__(64 * WV) void xq_gemv_kernel(const uint8_t *__restr
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int t = 0; t < TT; ++t) acc[r][t] = 0.f;
-    if constexpr (QT == XQ_Q6_K && !XL) {
+    if constexpr (QT == XQ_Q6_K) {
         // Q6_K: sub-blocks c and c + 2 of a half take the low and high nibbles of the same
         // ql bytes and other bits of the same qh bytes, so a lane takes weights l0 ..
-        // l0 + 15 of both (32 weights, x read from global memory as two runs): one set of
-        // ql, qh and d loads, and the two scale bytes, serves both.
-        for (int u = lane; u < k / 32; u += 64) {
+        // l0 + 15 of both (32 weights, x read as two runs of 16): one set of ql, qh and d
+        // loads, and the two scale bytes, serves both.
+        for (int u = lane, it = 0; u < k / 32; u += 64, ++it) {
             const int j = u & 7;
             const int ea = (u >> 3) * 256 + (j >> 2) * 128 + ((j >> 1) & 1) * 32 + (j & 1) * 16;
             const size_t boff = (size_t)(ea / TR::ELEMS) * TR::BYTES;
@@ -328,11 +338,19 @@ __global__ __launch_bounds__(64 * WV) void xq_gemv_kernel(const uint8_t *__restr
             f4_t xa[TT][4], xb[TT][4];
 #pragma unroll
             for (int t = 0; t < TT; ++t) {
-                const f4_t *xp = reinterpret_cast<const f4_t *>(X + (size_t)t * k + ea);
+                if constexpr (XL) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    xa[t][i] = xp[i];
-                    xb[t][i] = xp[16 + i];
+                    for (int i = 0; i < 4; ++i) {
+                        xa[t][i] = xs[t * xtok + ((2 * it) * 4 + i) * 64 + lane];
+                        xb[t][i] = xs[t * xtok + ((2 * it + 1) * 4 + i) * 64 + lane];
+                    }
+                } else {
+                    const f4_t *xp = reinterpret_cast<const f4_t *>(X + (size_t)t * k + ea);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        xa[t][i] = xp[i];
+                        xb[t][i] = xp[16 + i];
+                    }
                 }
             }
 #pragma unroll
@@ -622,13 +640,16 @@ constexpr int XQ_GEMV_XL_WV = 8;  // waves per workgroup sharing the staged x
 // CU; the launch's tokens are chunked so that x fits.
 constexpr int XQ_GEMV_XL_MAX = 128 * 1024;
 
-// x per token in LDS: the transposed layout fills whole 1024-k rounds (float4 units)
-inline int xq_gemv_xtok(int k) { return (k + 1023) / 1024 * 256; }
+// x per token in LDS (float4 units): the transposed layout fills whole rounds of the
+// wave's loop, 1024 k (Q6_K's paired loop: 2048 k)
+inline int xq_gemv_xtok(int qt, int k) {
+    return qt == XQ_Q6_K ? (k + 2047) / 2048 * 512 : (k + 1023) / 1024 * 256;
+}
 
 template <int QT, int EPI, int R, int TT>
 void launch_gemv_tt(const GemmArgs &a, const float *x, float *y, hipStream_t s) {
     constexpr int OUTW = EPI == EPI_SWIGLU ? R / 2 : R;  // outputs per wave
-    const int xtok = xq_gemv_xtok(a.k);
+    const int xtok = xq_gemv_xtok(QT, a.k);
     const int xl_bytes = TT * xtok * 16;
     if (R <= 2 && xl_bytes <= XQ_GEMV_XL_BYTES) {
         constexpr int WV = XQ_GEMV_XL_WV;
@@ -649,7 +670,7 @@ void launch_gemv_tt(const GemmArgs &a, const float *x, float *y, hipStream_t s) 
 template <int QT, int EPI, int R>
 hipError_t launch_gemv_r(const GemmArgs &a, hipStream_t s) {
     // tokens per launch: four, or fewer where that keeps one-row waves' x in LDS
-    const int xb = xq_gemv_xtok(a.k) * 16;
+    const int xb = xq_gemv_xtok(QT, a.k) * 16;
     const int per = (R <= 2 && xb <= XQ_GEMV_XL_MAX) ? min(4, XQ_GEMV_XL_MAX / xb) : 4;
     for (int t0 = 0; t0 < a.T; t0 += per) {
         const int tt = min(per, a.T - t0);
