@@ -149,6 +149,7 @@ def workloads():
         "gemv_q4_k_12288x4096_T1": (1, 0, [("gemv_q4_k", Q4_K, INTER, HIDDEN, PLAIN, "x", "out")], 1),
         "gemv_q5_k_12288x4096_T1": (1, 0, [("gemv_q5_k", Q5_K, INTER, HIDDEN, PLAIN, "x", "out")], 1),
         "gemv_q6_k_4096x12288_T1": (1, 0, [("gemv_q6_k", Q6_K, HIDDEN, INTER, PLAIN, "x12288", "out")], 1),
+        "gemv_q6_k_12288x4096_T1": (1, 0, [("gemv_q6_k", Q6_K, INTER, HIDDEN, PLAIN, "x", "out")], 1),
         "gemv_f16w_4096x12288_T1": (1, 0, [("gemv_f16w", F16W, HIDDEN, INTER, PLAIN, "x12288", "out")], 1),
         # the plain-read floor: one launch that only streams the same weight bytes as the
         # T = 1 GEMV of that shape (include/pf_probe.h)
