@@ -92,6 +92,26 @@ def test_xq_gemv_long_rows(gpu, qtype, epi, T):
     assert ok, "parity failed: metric %.3e" % err
 
 
+@pytest.mark.parametrize("T", [1, 4, 5, 8])
+@pytest.mark.parametrize("epi", [PLAIN, SWIGLU])
+@pytest.mark.parametrize("qtype", XQ, ids=lambda q: NAMES[q])
+def test_xq_gemv_staged_x_ragged_rounds(gpu, qtype, epi, T):
+    """The one-row-wave GEMV with x staged in LDS where the wave's loop ends in a partial
+    round: k = 2304 is 144 runs of 16 weights (two rounds of 64 lanes and 16 more) and,
+    for Q6_K's paired loop, 72 units of 32 (one round and 8 more), so a token's staged x
+    has unused slots. T = 5 takes a launch of four tokens and one of one. Every output."""
+    n, k = 100, 2304
+    rows = 2 * n if epi == SWIGLU else n
+    seed = 880 + 7 * qtype + 3 * epi + T
+    W = _weights(qtype, rows, k, "edge", F32, seed)
+    X = synth.activations(T, k, workload_id=seed)
+    assert gpu.select_path(qtype, n, k, T, epi, F32) == gpu.PF_PATH_GEMV
+    print("case xq gemv staged ragged %s T=%d epi=%d" % (NAMES[qtype], T, epi), flush=True)
+    Y = parity.run_gpu(gpu, qtype, W, n, k, X, epi, F32)
+    ok, err = parity.check(qtype, W, n, k, X, Y, epi, F32)
+    assert ok, "parity failed: metric %.3e" % err
+
+
 @pytest.mark.parametrize("T", [1, 3, 8])
 @pytest.mark.parametrize("epi", [PLAIN, RESIDUAL, SWIGLU])
 @pytest.mark.parametrize("qtype", XQ, ids=lambda q: NAMES[q])
