@@ -72,8 +72,9 @@ extern "C" {
 
 /* Block types. F16 .. IQ4_XS run their own kernels on both legs and need no
  * workspace, except on the f16 leg's GEMM: there pf_gemm_ws runs Q4_K, Q5_K, IQ4_XS and
- * Q6_K (k % 512 == 0) at every T, and F16 from 256 rows, on Q4_0's matrix-core GEMMs
- * (the 4-wave tiles below 256 rows, the cooperative-decode kernel above),
+ * Q6_K (k % 512 == 0) at every T, and F16 above 128 rows, on Q4_0's matrix-core GEMMs
+ * (the 4-wave tiles below 256 rows, for Q6_K up to 128, the cooperative-decode kernel
+ * from there),
  * with that GEMM's workspace, and elsewhere their own GEMM splits K through the
  * workspace where its tiles leave CUs idle. Without a workspace (pf_gemm, and
  * pf_gemm_noalloc where the workspace exceeds the static scratch) Q4_K, Q5_K, IQ4_XS
