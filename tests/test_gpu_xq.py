@@ -112,6 +112,26 @@ def test_xq_gemv_staged_x_ragged_rounds(gpu, qtype, epi, T):
     assert ok, "parity failed: metric %.3e" % err
 
 
+@pytest.mark.parametrize("T", [1, 2, 5])
+@pytest.mark.parametrize("epi", [PLAIN, SWIGLU])
+@pytest.mark.parametrize("qtype", XQ, ids=lambda q: NAMES[q])
+def test_xq_gemv_sixteen_wave_staged_x(gpu, qtype, epi, T):
+    """One-row waves where sixteen-wave workgroups still number 256 or more (n = 4100: 257,
+    the last one ragged) take up to two tokens a launch in them, x staged once per
+    workgroup; T = 5 runs four tokens on eight-wave workgroups and then one on sixteen.
+    Every output."""
+    n, k = 4100, 4096
+    rows = 2 * n if epi == SWIGLU else n
+    seed = 900 + 7 * qtype + 3 * epi + T
+    W = _weights(qtype, rows, k, "edge", F32, seed)
+    X = synth.activations(T, k, workload_id=seed)
+    assert gpu.select_path(qtype, n, k, T, epi, F32) == gpu.PF_PATH_GEMV
+    print("case xq gemv sixteen-wave %s T=%d epi=%d" % (NAMES[qtype], T, epi), flush=True)
+    Y = parity.run_gpu(gpu, qtype, W, n, k, X, epi, F32)
+    ok, err = parity.check(qtype, W, n, k, X, Y, epi, F32)
+    assert ok, "parity failed: metric %.3e" % err
+
+
 @pytest.mark.parametrize("T", [1, 3, 8])
 @pytest.mark.parametrize("epi", [PLAIN, RESIDUAL, SWIGLU])
 @pytest.mark.parametrize("qtype", XQ, ids=lambda q: NAMES[q])
